@@ -1,0 +1,161 @@
+"""ctypes wrapper around the fp64 CPU oracle (``lstm_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY.  The tests, the smoke check and the CPU-baseline
+leg of ``bench.py`` are the only callers.  Nothing here imports the HIP
+library or its Python binding, and the HIP path never imports this module.
+
+The oracle follows the forward table and the backward recursion of the
+"SingleLayerLstmGrad" operator page (Ascend CANN ops-nn); see the header of
+``lstm_oracle.c`` for the conventions (gate order i,f,g,o in W's row blocks,
+columns [h | x], time-major tensors, the forget factor applied once in the
+cell carry).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "lstm_oracle.c")
+_LIB = os.path.join(_HERE, "liblstm_oracle.so")
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, no fast-math)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(["gcc", "-O2", "-fopenmp", "-std=c99", "-shared", "-fPIC",
+                               "-Wall", _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _bind(path):
+    lib = ctypes.CDLL(path)
+    L, P = ctypes.c_long, ctypes.c_void_p
+    lib.oracle_lstm_fwd.argtypes = [L, L, L, L] + [P] * 9
+    lib.oracle_lstm_fwd.restype = ctypes.c_int
+    lib.oracle_lstm_bwd.argtypes = [L, L, L, L] + [P] * 17
+    lib.oracle_lstm_bwd.restype = ctypes.c_int
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_set_threads.argtypes = [ctypes.c_int]
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        _lib = _bind(_LIB)
+    return _lib
+
+
+def use_library(path):
+    """Point this module at another build of the oracle source (the mutation
+    test builds deliberately broken copies); returns the previous handle so
+    that the caller can restore it with ``restore_library``."""
+    global _lib
+    prev = _load()
+    _lib = _bind(path)
+    return prev
+
+
+def restore_library(handle):
+    global _lib
+    _lib = handle
+
+
+def num_threads() -> int:
+    return _load().oracle_num_threads()
+
+
+def set_threads(n: int) -> None:
+    _load().oracle_set_threads(int(n))
+
+
+def _f64(a, shape=None):
+    if a is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    if shape is not None and a.shape != tuple(shape):
+        raise ValueError(f"expected shape {tuple(shape)}, got {a.shape}")
+    return a
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def fwd(x, W, b=None, h0=None, c0=None):
+    """Forward pass.  Returns dict(y, hT, cT, gates, cell) as fp64 arrays.
+
+    x [T,B,I], W [4H,H+I], b [4H] or None, h0/c0 [B,H] or None (zero state).
+    gates is [T,B,4H] (activated i,f,g,o blocks), cell is c_t, [T,B,H].
+    """
+    x = _f64(x)
+    T, B, I = x.shape
+    H = W.shape[0] // 4
+    W = _f64(W, (4 * H, H + I))
+    b = _f64(b, (4 * H,))
+    h0 = _f64(h0, (B, H))
+    c0 = _f64(c0, (B, H))
+    y = np.empty((T, B, H))
+    hT = np.empty((B, H))
+    cT = np.empty((B, H))
+    gates = np.empty((T, B, 4 * H))
+    cell = np.empty((T, B, H))
+    rc = _load().oracle_lstm_fwd(T, B, I, H, _p(x), _p(W), _p(b), _p(h0), _p(c0),
+                                 _p(y), _p(hT), _p(cT), _p(gates), _p(cell))
+    if rc != 0:
+        raise RuntimeError(f"oracle_lstm_fwd failed ({rc})")
+    return dict(y=y, hT=hT, cT=cT, gates=gates, cell=cell)
+
+
+def bwd(x, W, h0, c0, fw, dy, dhT=None, dcT=None, want_debug=False):
+    """Backward pass from the forward record ``fw`` (the dict ``fwd`` returns).
+
+    Returns dict(dx, dW, db, dh0, dc0) and, with want_debug, also dgates
+    [T,B,4H] (gate deltas) and dcell [T,B,H] (cell gradient per step).
+    """
+    x = _f64(x)
+    T, B, I = x.shape
+    H = W.shape[0] // 4
+    W = _f64(W, (4 * H, H + I))
+    h0 = _f64(h0, (B, H))
+    c0 = _f64(c0, (B, H))
+    dy = _f64(dy, (T, B, H))
+    dhT = _f64(dhT, (B, H))
+    dcT = _f64(dcT, (B, H))
+    y, gates, cell = (_f64(fw[k]) for k in ("y", "gates", "cell"))
+    dx = np.empty((T, B, I))
+    dW = np.empty((4 * H, H + I))
+    db = np.empty((4 * H,))
+    dh0 = np.empty((B, H))
+    dc0 = np.empty((B, H))
+    dgates = np.empty((T, B, 4 * H)) if want_debug else None
+    dcell = np.empty((T, B, H)) if want_debug else None
+    rc = _load().oracle_lstm_bwd(T, B, I, H, _p(x), _p(W), _p(h0), _p(c0),
+                                 _p(y), _p(gates), _p(cell), _p(dy), _p(dhT), _p(dcT),
+                                 _p(dx), _p(dW), _p(db), _p(dh0), _p(dc0),
+                                 _p(dgates), _p(dcell))
+    if rc != 0:
+        raise RuntimeError(f"oracle_lstm_bwd failed ({rc})")
+    out = dict(dx=dx, dW=dW, db=db, dh0=dh0, dc0=dc0)
+    if want_debug:
+        out.update(dgates=dgates, dcell=dcell)
+    return out
+
+
+def fwd_bwd(inp: dict) -> dict:
+    """Run forward then backward on an input dict with keys
+    x, W, b, h0, c0, dy, dhT, dcT (values may be None where optional)."""
+    fw = fwd(inp["x"], inp["W"], inp.get("b"), inp.get("h0"), inp.get("c0"))
+    bw = bwd(inp["x"], inp["W"], inp.get("h0"), inp.get("c0"), fw, inp["dy"],
+             inp.get("dhT"), inp.get("dcT"))
+    out = {k: fw[k] for k in ("y", "hT", "cT")}
+    out.update(bw)
+    return out

@@ -1,0 +1,290 @@
+"""Pins of the fp64 CPU oracle against facts that do not come from the oracle.
+
+Each test names what it pins and the passage of the "SingleLayerLstmGrad"
+operator page (Ascend CANN ops-nn) -- or the mathematics -- that fixes the
+expected value.  All of these run on the CPU.
+
+ * central finite differences of the loss (the Darknet walkthrough's gradient
+   check recipe) pin every backward output against the forward;
+ * the zero-weight closed forms and the T=1 closed form pin the forward
+   recursion and one backward step;
+ * the forget-gate product law of "LSTM梯度流动特性" pins the cell carry and the
+   reading that f enters it once;
+ * segment composition and linearity pin the carry-in / carry-out contract;
+ * PyTorch's CPU nn.LSTM in fp64 with autograd is an independent library
+   implementation of the same cell (gate order i,f,g,o and the two weight
+   blocks are its documented layout) -- licensed by the MXNet page's remark
+   that autodiff of the unrolled graph is equivalent to BPTT.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import oracle
+from layer_lstm_amd import synth
+
+
+def sig(u):
+    return 1.0 / (1.0 + np.exp(-u))
+
+
+def loss(inp, fw):
+    """L = sum_t <dy_t, h_t> + <dhT, h_{T-1}> + <dcT, c_{T-1}>: the scalar
+    whose gradient the backward computes (dy, dhT, dcT are its cotangents)."""
+    L = float(np.sum(inp["dy"] * fw["y"]))
+    if inp.get("dhT") is not None:
+        L += float(np.sum(inp["dhT"] * fw["hT"]))
+    if inp.get("dcT") is not None:
+        L += float(np.sum(inp["dcT"] * fw["cT"]))
+    return L
+
+
+def run_loss(inp):
+    fw = oracle.fwd(inp["x"], inp["W"], inp.get("b"), inp.get("h0"), inp.get("c0"))
+    return loss(inp, fw)
+
+
+def full_inputs(T, B, I, H, seed=0, scale_w=None):
+    """Inputs with every optional tensor present (so FD can perturb it)."""
+    k = 1.0 / math.sqrt(H) if scale_w is None else scale_w
+    dist = dict(W=("u", k), b=("u", k), x=("n", 1.0), h0=("n", 0.5), c0=("n", 0.5),
+                dy=("n", 1.0), dhT=("n", 1.0), dcT=("n", 1.0))
+    return synth.make_inputs(T, B, I, H, "f32", seed, dist)
+
+
+GRAD_OF = dict(x="dx", W="dW", b="db", h0="dh0", c0="dc0")
+
+
+def fd_check(inp, eps_rel=1e-6, tol=1e-7):
+    g = oracle.fwd_bwd(inp)
+    worst = 0.0
+    for p, gname in GRAD_OF.items():
+        base = inp[p]
+        flat = base.reshape(-1)
+        gflat = g[gname].reshape(-1)
+        for idx in range(flat.size):
+            th = flat[idx]
+            eps = eps_rel * max(1.0, abs(th))
+            flat[idx] = th + eps
+            lp = run_loss(inp)
+            flat[idx] = th - eps
+            lm = run_loss(inp)
+            flat[idx] = th
+            fd = (lp - lm) / (2 * eps)
+            err = abs(fd - gflat[idx]) / (1.0 + abs(gflat[idx]))
+            worst = max(worst, err)
+            assert err <= tol, f"{p}[{idx}] FD {fd!r} vs analytic {gflat[idx]!r}"
+    return worst
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _single_thread():
+    oracle.set_threads(1)
+    yield
+    oracle.set_threads(0)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3])
+@pytest.mark.parametrize("B", [1, 2])
+@pytest.mark.parametrize("I", [1, 3])
+@pytest.mark.parametrize("H", [1, 2, 4])
+def test_fd_tiny(T, B, I, H):
+    inp = full_inputs(T, B, I, H, seed=T * 100 + B * 10 + I + H * 1000, scale_w=0.9)
+    fd_check(inp)
+
+
+def test_fd_small_workload_shape():
+    """Every element of x, W, b, h0, c0 at the smallest workload's shape
+    (T=8, B=4, I=16, H=32; 7040 scalars)."""
+    inp = full_inputs(8, 4, 16, 32, seed=7)
+    fd_check(inp)
+
+
+def test_directional_fd_headline_shape():
+    """Directional derivative along a random direction over all inputs at
+    T=64, B=32, I=256, H=256."""
+    oracle.set_threads(0)
+    inp = full_inputs(64, 32, 256, 256, seed=3)
+    g = oracle.fwd_bwd(inp)
+    rng = np.random.default_rng(11)
+    dirs = {p: rng.standard_normal(inp[p].shape) for p in GRAD_OF}
+    nrm = math.sqrt(sum(float(np.sum(v * v)) for v in dirs.values()))
+    # directional derivative <grad L, v> from the backward
+    dd = sum(float(np.sum(g[GRAD_OF[p]] * dirs[p])) for p in GRAD_OF) / nrm
+    eps = 1e-4
+    def shifted(s):
+        j = dict(inp)
+        for p in GRAD_OF:
+            j[p] = inp[p] + s * eps * dirs[p] / nrm
+        return run_loss(j)
+    fd = (shifted(1) - shifted(-1)) / (2 * eps)
+    assert abs(fd - dd) <= 1e-7 * max(1.0, abs(dd)), (fd, dd)
+
+
+def test_zero_weights_closed_form():
+    """W=0, b=0: i=f=o=1/2 and g=0, so c_t = c0 / 2^(t+1) and
+    h_t = tanh(c_t)/2 (forward table with constant gates)."""
+    T, B, I, H = 6, 3, 5, 4
+    inp = full_inputs(T, B, I, H, seed=5)
+    W = np.zeros((4 * H, H + I))
+    fw = oracle.fwd(inp["x"], W, np.zeros(4 * H), inp["h0"], inp["c0"])
+    for t in range(T):
+        c = inp["c0"] / 2.0 ** (t + 1)
+        np.testing.assert_allclose(fw["cell"][t], c, rtol=1e-15, atol=0)
+        np.testing.assert_allclose(fw["y"][t], 0.5 * np.tanh(c), rtol=1e-15, atol=1e-300)
+
+
+def test_zero_weights_bias_geometric_series():
+    """W=0, b!=0: the gates are constant, so the cell recursion
+    c_t = f c_{t-1} + i g is a geometric series:
+    c_t = f^(t+1) c0 + i g (1 - f^(t+1)) / (1 - f)."""
+    T, B, I, H = 9, 2, 3, 5
+    inp = full_inputs(T, B, I, H, seed=6)
+    rng = np.random.default_rng(1)
+    b = rng.uniform(-2, 2, 4 * H)
+    fw = oracle.fwd(inp["x"], np.zeros((4 * H, H + I)), b, inp["h0"], inp["c0"])
+    i, f, g, o = sig(b[:H]), sig(b[H:2 * H]), np.tanh(b[2 * H:3 * H]), sig(b[3 * H:])
+    for t in range(T):
+        c = f ** (t + 1) * inp["c0"] + i * g * (1 - f ** (t + 1)) / (1 - f)
+        np.testing.assert_allclose(fw["cell"][t], c, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(fw["y"][t], o * np.tanh(c), rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(fw["gates"][:, :, H:2 * H], np.broadcast_to(f, (T, B, H)), rtol=1e-15)
+
+
+def test_forget_product_law():
+    """"LSTM梯度流动特性": with no recurrent weights and no gradient reaching
+    any h, the cell gradient flows back only through the forget gates, so
+    dc0 = dcT * prod_t f_t (elementwise) and dh0 = 0.  The forget gates are
+    computed here straight from x and W's input block.  Applying f twice per
+    step in the cell carry would give prod f^2 and fail this."""
+    T, B, I, H = 7, 3, 4, 5
+    inp = full_inputs(T, B, I, H, seed=8, scale_w=1.5)
+    inp["W"][:, :H] = 0.0
+    inp["dy"] = np.zeros_like(inp["dy"])
+    inp["dhT"] = np.zeros_like(inp["dhT"])
+    g = oracle.fwd_bwd(inp)
+    Wf_x = inp["W"][H:2 * H, H:]
+    prod = np.ones((B, H))
+    for t in range(T):
+        prod = prod * sig(inp["x"][t] @ Wf_x.T + inp["b"][H:2 * H])
+    np.testing.assert_allclose(g["dc0"], inp["dcT"] * prod, rtol=1e-13, atol=0)
+    assert np.all(g["dh0"] == 0.0)
+    assert np.all(g["dx"][:, :, :] != 0.0)  # input gradients flow through f
+
+
+def test_dc0_is_first_cell_delta_times_f0():
+    """Step 5 ("传播到前一时刻"): the carry handed to t-1 is delta-c_t . f_t, so
+    the initial-cell gradient is delta-c_0 . f_0."""
+    inp = full_inputs(5, 3, 4, 6, seed=9)
+    fw = oracle.fwd(inp["x"], inp["W"], inp["b"], inp["h0"], inp["c0"])
+    bw = oracle.bwd(inp["x"], inp["W"], inp["h0"], inp["c0"], fw, inp["dy"], inp["dhT"],
+                    inp["dcT"], want_debug=True)
+    H = 6
+    np.testing.assert_array_equal(bw["dc0"], bw["dcell"][0] * fw["gates"][0][:, H:2 * H])
+
+
+def test_t1_closed_form():
+    """One step written out without loops: gates from a = W[h0;x0] + b, the
+    cell and hidden update, then the backward step and all parameter
+    gradients of a single time step."""
+    T, B, I, H = 1, 3, 4, 5
+    inp = full_inputs(T, B, I, H, seed=10)
+    W, b, x0, h0, c0 = inp["W"], inp["b"], inp["x"][0], inp["h0"], inp["c0"]
+    z = np.concatenate([h0, x0], axis=1)  # [B, H+I]
+    a = z @ W.T + b
+    i, f, g, o = sig(a[:, :H]), sig(a[:, H:2 * H]), np.tanh(a[:, 2 * H:3 * H]), sig(a[:, 3 * H:])
+    c1 = f * c0 + i * g
+    h1 = o * np.tanh(c1)
+    dh = inp["dy"][0] + inp["dhT"]
+    dc = dh * o * (1 - np.tanh(c1) ** 2) + inp["dcT"]
+    dG = np.concatenate([dc * g * i * (1 - i), dc * c0 * f * (1 - f), dc * i * (1 - g ** 2),
+                         dh * np.tanh(c1) * o * (1 - o)], axis=1)
+    out = oracle.fwd_bwd(inp)
+    r = dict(y=h1[None], hT=h1, cT=c1, dW=dG.T @ z, db=dG.sum(0), dx=(dG @ W[:, H:])[None],
+             dh0=dG @ W[:, :H], dc0=dc * f)
+    for k, v in r.items():
+        np.testing.assert_allclose(out[k], v, rtol=1e-13, atol=1e-15, err_msg=k)
+
+
+def test_segment_composition():
+    """Running T1 steps, then T2 steps from the returned state, equals
+    running T1+T2 steps (the Darknet walkthrough: state is carried only
+    within one stream); and the backward of the second segment, its
+    dh0/dc0 fed as dhT/dcT of the first, equals the full backward, with dW
+    and db the sum of the two segments'."""
+    T1, T2, B, I, H = 3, 4, 2, 3, 4
+    inp = full_inputs(T1 + T2, B, I, H, seed=12)
+    full = oracle.fwd_bwd(inp)
+    s1 = dict(inp, x=inp["x"][:T1], dy=inp["dy"][:T1])
+    fw1 = oracle.fwd(s1["x"], inp["W"], inp["b"], inp["h0"], inp["c0"])
+    s2 = dict(inp, x=inp["x"][T1:], dy=inp["dy"][T1:], h0=fw1["hT"], c0=fw1["cT"])
+    g2 = oracle.fwd_bwd(s2)
+    s1.update(dhT=g2["dh0"], dcT=g2["dc0"])
+    g1 = oracle.fwd_bwd(s1)
+    rt = dict(rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(np.concatenate([g1["y"], g2["y"]]), full["y"], **rt)
+    np.testing.assert_allclose(g2["hT"], full["hT"], **rt)
+    np.testing.assert_allclose(g2["cT"], full["cT"], **rt)
+    np.testing.assert_allclose(np.concatenate([g1["dx"], g2["dx"]]), full["dx"], **rt)
+    np.testing.assert_allclose(g1["dh0"], full["dh0"], **rt)
+    np.testing.assert_allclose(g1["dc0"], full["dc0"], **rt)
+    np.testing.assert_allclose(g1["dW"] + g2["dW"], full["dW"], **rt)
+    np.testing.assert_allclose(g1["db"] + g2["db"], full["db"], **rt)
+
+
+def test_backward_linear_in_cotangents():
+    """The backward is a vector-Jacobian product: linear in (dy, dhT, dcT)."""
+    T, B, I, H = 4, 3, 5, 6
+    a = full_inputs(T, B, I, H, seed=13)
+    b_ = full_inputs(T, B, I, H, seed=14)
+    al, be = 0.75, -1.5
+    mix = dict(a, dy=al * a["dy"] + be * b_["dy"], dhT=al * a["dhT"] + be * b_["dhT"],
+               dcT=al * a["dcT"] + be * b_["dcT"])
+    gb = oracle.fwd_bwd(dict(a, dy=b_["dy"], dhT=b_["dhT"], dcT=b_["dcT"]))
+    ga = oracle.fwd_bwd(a)
+    gm = oracle.fwd_bwd(mix)
+    for k in ("dx", "dW", "db", "dh0", "dc0"):
+        np.testing.assert_allclose(gm[k], al * ga[k] + be * gb[k], rtol=1e-12, atol=1e-13, err_msg=k)
+
+
+def test_empty_sequence():
+    """T=0: no step runs; the final state is the initial state and the
+    backward hands dhT/dcT straight to dh0/dc0 with zero parameter
+    gradients."""
+    inp = full_inputs(0, 2, 3, 4, seed=15)
+    out = oracle.fwd_bwd(inp)
+    np.testing.assert_array_equal(out["hT"], inp["h0"])
+    np.testing.assert_array_equal(out["cT"], inp["c0"])
+    np.testing.assert_array_equal(out["dh0"], inp["dhT"])
+    np.testing.assert_array_equal(out["dc0"], inp["dcT"])
+    assert np.all(out["dW"] == 0) and np.all(out["db"] == 0) and out["dx"].size == 0
+
+
+@pytest.mark.parametrize("T,B,I,H", [(5, 3, 4, 6), (8, 4, 16, 32), (3, 1, 1, 1)])
+def test_against_torch_nn_lstm_fp64(T, B, I, H):
+    """Independent library implementation: torch.nn.LSTM on the CPU in fp64
+    with weight_hh = W[:, :H], weight_ih = W[:, H:], bias_ih = b,
+    bias_hh = 0; gradients by autograd of the same scalar loss."""
+    torch = pytest.importorskip("torch")
+    inp = full_inputs(T, B, I, H, seed=16)
+    m = torch.nn.LSTM(I, H, num_layers=1, bias=True, batch_first=False).double()
+    with torch.no_grad():
+        m.weight_hh_l0.copy_(torch.from_numpy(inp["W"][:, :H]))
+        m.weight_ih_l0.copy_(torch.from_numpy(inp["W"][:, H:]))
+        m.bias_ih_l0.copy_(torch.from_numpy(inp["b"]))
+        m.bias_hh_l0.zero_()
+    x = torch.from_numpy(inp["x"]).requires_grad_(True)
+    h0 = torch.from_numpy(inp["h0"])[None].clone().requires_grad_(True)
+    c0 = torch.from_numpy(inp["c0"])[None].clone().requires_grad_(True)
+    y, (hn, cn) = m(x, (h0, c0))
+    L = (y * torch.from_numpy(inp["dy"])).sum() + (hn[0] * torch.from_numpy(inp["dhT"])).sum() \
+        + (cn[0] * torch.from_numpy(inp["dcT"])).sum()
+    L.backward()
+    ref = dict(y=y.detach().numpy(), hT=hn[0].detach().numpy(), cT=cn[0].detach().numpy(),
+               dx=x.grad.numpy(), dh0=h0.grad[0].numpy(), dc0=c0.grad[0].numpy(),
+               dW=np.concatenate([m.weight_hh_l0.grad.numpy(), m.weight_ih_l0.grad.numpy()], axis=1),
+               db=m.bias_ih_l0.grad.numpy())
+    out = oracle.fwd_bwd(inp)
+    for k, v in ref.items():
+        np.testing.assert_allclose(out[k], v, rtol=1e-11, atol=1e-13, err_msg=k)
