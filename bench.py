@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Benchmark of the single-layer LSTM forward + BPTT on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = lstm_fwd_train + lstm_bwd on one batch of seeded synthetic input
+(every kernel of the path: input projection, forward recurrence, backward
+recurrence, dW, dx, db).  Inputs, weights and outputs are resident in HBM
+before the timed region starts.  Prints one JSON line with the metric
+(sequences/s; effective TFLOP/s = 24*T*B*H*(H+I) per step / time, and its
+fraction of the MFMA peak of the storage type), a roofline record of the
+kernel that takes the most time, and the fp64 CPU oracle timed on the host
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from layer_lstm_amd import synth  # noqa: E402
+
+METRIC = "LSTM fwd+bwd sequences/s and effective TFLOP/s (fraction of MFMA peak)"
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}  # MI355X dense matrix peaks
+HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "input_projection": "gemm.hip", "dW_product": "gemm.hip", "dx_product": "gemm.hip",
+    "db_colsum": "gemm.hip", "forward_recurrence": "recurrent.hip",
+    "backward_recurrence": "recurrent.hip", "clear_copy": "gemm.hip",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_work(w, kind):
+    """Algorithmic work of one launch: (amount, unit, bound)."""
+    T, B, I, H = w.T, w.B, w.I, w.H
+    TB = T * B
+    e = 4 if w.dtype == "f32" else 2
+    if kind == "input_projection":
+        return 2.0 * TB * 4 * H * I, "flop", "mfma"
+    if kind in ("forward_recurrence", "backward_recurrence"):
+        return 2.0 * TB * 4 * H * H, "flop", "mfma"
+    if kind == "dW_product":
+        return 2.0 * TB * 4 * H * (H + I), "flop", "mfma"
+    if kind == "dx_product":
+        return 2.0 * TB * 4 * H * I, "flop", "mfma"
+    if kind == "db_colsum":
+        return float(TB * 4 * H * e + 4 * H * e), "byte", "hbm"
+    return 0.0, "byte", "hbm"
+
+
+def source_sha(kind):
+    src = os.path.join(ROOT, "layer_lstm_amd", "csrc", KERNEL_SOURCES[kind])
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def traffic_for(workload, kind):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, or
+    None when there are none for this kernel or its source has changed."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))[workload][kind]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha") != source_sha(kind):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, inp, budget_s):
+    """Time the fp64 oracle (as it stands) on a bounded sample: whole
+    sequences (batch rows) of the same workload, as many as fit in about
+    `budget_s` seconds, from a one-row probe."""
+    import numpy as np
+    from oracle import oracle
+
+    def rows(n):
+        sub = dict(inp, B=n)
+        for k in ("x", "dy"):
+            sub[k] = inp[k][:, :n]
+        for k in ("h0", "c0", "dhT", "dcT"):
+            sub[k] = None if inp[k] is None else inp[k][:n]
+        return sub
+
+    t0 = time.perf_counter()
+    oracle.fwd_bwd(rows(1))
+    t1 = time.perf_counter() - t0
+    n = int(max(1, min(w.B, budget_s / max(t1, 1e-6))))
+    t0 = time.perf_counter()
+    oracle.fwd_bwd(rows(n))
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "sequences/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n} of {w.B} sequences (batch rows) of {w.name}, one fwd+bwd, fp64, "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=synth.HEADLINE, choices=sorted(synth.WORKLOADS))
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the data-parallel split over the batch is described in DESIGN.md); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from layer_lstm_amd import lstm
+
+    w = synth.WORKLOADS[args.workload]
+    inp = synth.workload_inputs(w.name)
+    code = lstm.F32 if w.dtype == "f32" else lstm.BF16
+    td = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    dev = torch.device("cuda:0")
+
+    def put(a):
+        return None if a is None else torch.from_numpy(np.asarray(a, dtype=np.float32)).to(dev).to(td)
+
+    d = {k: put(inp[k]) for k in ("x", "W", "b", "h0", "c0", "dy", "dhT", "dcT")}
+    m = lstm.Lstm(w.T, w.B, w.I, w.H, code)
+
+    def step():
+        m.forward(d["x"], d["W"], d["b"], d["h0"], d["c0"])
+        m.backward(d["dy"], d["dhT"], d["dcT"], d["x"], d["W"], d["h0"], d["c0"])
+
+    log(f"workload {w.name}: warmup {args.warmup}, steps {args.steps}")
+    for _ in range(args.warmup):
+        step()
+    m.check()
+    torch.cuda.synchronize()
+
+    # timed region: events on the stream every kernel is launched on
+    stream = torch.cuda.current_stream()
+    lstm.timing_enable(False)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    m.check()
+
+    # per-kernel HIP-event timing over a second pass of the same steps
+    lstm.timing_enable(True)
+    torch.cuda.synchronize()
+    e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e2.record(stream)
+    for _ in range(args.steps):
+        step()
+    e3.record(stream)
+    torch.cuda.synchronize()
+    ms_timed = e2.elapsed_time(e3) / args.steps
+    kt = lstm.timing_read()
+    lstm.timing_enable(False)
+    log(f"step {ms * 1e3:.1f} us (with per-kernel events {ms_timed * 1e3:.1f} us)")
+    for k, (tot, n) in kt.items():
+        if n:
+            log(f"  {k:22s} {tot / n * 1e3:10.1f} us/launch  x{n // args.steps}/step")
+
+    kinds = [k for k in kt if kt[k][1] > 0 and k != "clear_copy"]
+    dom = max(kinds, key=lambda k: kt[k][0])
+    tot, n = kt[dom]
+    avg_s = tot / n / 1e3
+    work, unit, bound = kernel_work(w, dom)
+    if unit == "flop":
+        achieved = work / avg_s / 1e12
+        peak, runit = PEAK_TFLOPS[w.dtype], "TFLOP/s"
+    else:
+        achieved = work / avg_s / 1e9
+        peak, runit = HBM_GBS, "GB/s"
+    roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": runit,
+                "frac": round(achieved / peak, 5), "traffic": traffic_for(w.name, dom),
+                "kernel": dom, "avg_launch_us": round(avg_s * 1e6, 2)}
+
+    flops = w.flops
+    value = w.B / (ms / 1e3)
+    eff_tflops = flops / (ms / 1e3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "sequences/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded; see layer_lstm_amd/synth.py)",
+        "config": {"workload": w.name, "T": w.T, "B": w.B, "I": w.I, "H": w.H, "storage": w.dtype,
+                   "parallelism": "single GPU"},
+        "effective_tflops": round(eff_tflops, 3),
+        "fraction_of_peak": round(eff_tflops / PEAK_TFLOPS[w.dtype], 5),
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,149 @@
+/*
+ * lstm.h -- C ABI of liblstm.so: forward pass and backpropagation through
+ * time of a single-layer, unidirectional LSTM on one AMD Instinct MI355X
+ * (gfx950), written in HIP.
+ *
+ * What is computed (the "SingleLayerLstmGrad" operator page, Ascend CANN
+ * ops-nn: forward-formula table "前向传播公式" and the backward recursion
+ * "反向传播算法" steps 1-6):
+ *
+ *   z_t = [h_{t-1}; x_t]                    h_{-1} = h0, c_{-1} = c0
+ *   i,f,o = sigmoid(W_{i,f,o} z_t + b),     g = tanh(W_g z_t + b)
+ *   c_t = f*c_{t-1} + i*g,                  h_t = o*tanh(c_t) = y_t
+ *
+ * and, given the cotangents dy (of every h_t), dhT (of the last h) and dcT
+ * (of the last c), the exact gradients dx, dW, db, dh0, dc0 of the scalar
+ * sum_t <dy_t,h_t> + <dhT,h_{T-1}> + <dcT,c_{T-1}>, by the page's step-by-
+ * step recursion (the forget gate enters the cell carry once, as its cell-
+ * gradient derivation requires).
+ *
+ * Layouts (all dense, row-major, time-major as in the page's parameter
+ * table):
+ *   x  [T,B,I]      y, dy [T,B,H]      h0, c0, hT, cT, dhT, dcT, dh0, dc0 [B,H]
+ *   W  [4H, H+I]    row block k (rows [kH,(k+1)H)) is gate LSTM_GATE_* = k,
+ *                   i.e. order i, f, g, o ("ifjo", j being the candidate g);
+ *                   columns [0,H) multiply h_{t-1}, columns [H,H+I) multiply
+ *                   x_t (the order of z_t)
+ *   b, db [4H]      same gate order (the page's db shape [4,H] is the same
+ *                   memory)
+ *   dW [4H, H+I]
+ * Element type: all of the above are LSTM_F32 (float) or all LSTM_BF16
+ * (bfloat16 storage).  Every dot product accumulates in fp32; the cell state
+ * is carried in fp32.
+ *
+ * Ownership and execution: the caller allocates every buffer (device
+ * memory).  The library never allocates device memory, keeps no pointer
+ * after a call returns, and launches asynchronously on the given stream
+ * (a hipStream_t passed as void*; NULL = the default stream) without any
+ * host synchronisation.  Buffers must stay alive until the stream has
+ * drained.  Outputs are overwritten, never accumulated into.
+ *
+ * Workspace: opaque device memory of lstm_query() bytes, 256-byte aligned.
+ * lstm_fwd_train() writes the forward record into it (activated gates and
+ * cell states of every step -- the page's i/j/f/o/c inputs of the backward
+ * operator); lstm_bwd() reads that record and must see it unmodified.
+ * lstm_bwd() does not destroy the record, so it may be repeated.  Calls that
+ * share one workspace must not overlap in time.
+ *
+ * Errors: every entry point returns LSTM_OK (0) or a negative LSTM_ERR_*
+ * code.  All argument checks happen before any launch; on error nothing is
+ * launched and no output is touched.  No C++ exception crosses the ABI.
+ */
+#ifndef LAYER_LSTM_AMD_LSTM_H
+#define LAYER_LSTM_AMD_LSTM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LSTM_ABI_VERSION 1
+
+/* Gate row blocks of W, b, dW, db (the "ifjo" order of the page's
+ * gate_order attribute). */
+enum { LSTM_GATE_I = 0, LSTM_GATE_F = 1, LSTM_GATE_G = 2, LSTM_GATE_O = 3 };
+
+/* Element type of every ABI tensor. */
+enum { LSTM_F32 = 0, LSTM_BF16 = 1 };
+
+/* Status codes. */
+enum {
+  LSTM_OK = 0,
+  LSTM_ERR_NULL = -1,        /* a required pointer is NULL */
+  LSTM_ERR_DIMS = -2,        /* T, B or I < 0, or H <= 0 */
+  LSTM_ERR_DTYPE = -3,       /* dtype is not LSTM_F32 / LSTM_BF16 */
+  LSTM_ERR_ALIGN = -4,       /* a tensor is not aligned to its element size, or the workspace to 256 B */
+  LSTM_ERR_WORKSPACE = -5,   /* workspace_bytes < lstm_query() */
+  LSTM_ERR_UNSUPPORTED = -6, /* shape outside the kernels' envelope (see lstm_query) */
+  LSTM_ERR_COOP = -7,        /* the persistent grid cannot be co-resident on this device */
+  LSTM_ERR_LAUNCH = -8,      /* a HIP launch failed */
+  LSTM_ERR_TIMEOUT = -9,     /* a per-step wait of the recurrent kernels hit its time bound */
+  LSTM_ERR_DEVICE = -10      /* the current device is not gfx950 or could not be queried */
+};
+
+/* Problem shape.  dtype is LSTM_F32 or LSTM_BF16. */
+typedef struct {
+  int64_t T; /* time steps, >= 0 */
+  int64_t B; /* batch, >= 0 */
+  int64_t I; /* input size, >= 0 */
+  int64_t H; /* hidden size, >= 1 */
+  int32_t dtype;
+  int32_t reserved; /* must be 0 */
+} lstm_shape;
+
+/* LSTM_ABI_VERSION of the library. */
+int lstm_abi_version(void);
+
+/* Human-readable text of a status code (static storage; never NULL). */
+const char* lstm_status_string(int status);
+
+/* Workspace size in bytes for `shape` on the current device.
+ * Envelope: H <= 2048, I <= 65536, T*B <= 2^31/4H.  Returns LSTM_OK and sets
+ * *workspace_bytes, or an error code (workspace_bytes untouched). */
+int lstm_query(const lstm_shape* shape, size_t* workspace_bytes);
+
+/* Forward pass for training ("前向传播公式").
+ *   x [T,B,I], W [4H,H+I]: required (x may be NULL only if T*B*I == 0)
+ *   b [4H], h0 [B,H], c0 [B,H]: optional, NULL = zero
+ *   y [T,B,H], hT [B,H], cT [B,H]: outputs (y may be NULL only if T*B == 0)
+ *   workspace: receives the forward record for lstm_bwd. */
+int lstm_fwd_train(const lstm_shape* shape, const void* x, const void* W, const void* b,
+                   const void* h0, const void* c0, void* y, void* hT, void* cT,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backpropagation through time ("反向传播算法" steps 1-6).
+ *   dy [T,B,H]: required; dhT, dcT [B,H]: optional, NULL = zero
+ *   x, W, h0, c0, y: the same tensors the forward saw (h0 NULL = zero;
+ *   c0 NULL = zero); the forward record in `workspace`
+ *   dx [T,B,I], dW [4H,H+I], dh0 [B,H], dc0 [B,H]: outputs
+ *   db [4H]: output, optional (NULL = not computed). */
+int lstm_bwd(const lstm_shape* shape, const void* dy, const void* dhT, const void* dcT,
+             const void* x, const void* W, const void* h0, const void* c0, const void* y,
+             void* workspace, size_t workspace_bytes,
+             void* dx, void* dW, void* db, void* dh0, void* dc0, void* stream);
+
+/* Waits for `stream`, then reports (and clears) a time-out that a
+ * recurrent kernel recorded in `workspace`: LSTM_ERR_TIMEOUT, else LSTM_OK
+ * (or LSTM_ERR_LAUNCH if the stream itself reports an error). */
+int lstm_check_workspace(void* workspace, size_t workspace_bytes, void* stream);
+
+/* Per-kernel timing, for measurement.  While enabled (on != 0), every
+ * kernel the library launches is bracketed by HIP events recorded on the
+ * call's stream, and the elapsed time is added to the total of its kind:
+ *   0 input projection   1 forward recurrence   2 backward recurrence
+ *   3 dW product (with its split-K sum)   4 dx product   5 db column sum
+ *   6 buffer clears and state copies
+ * lstm_timing_enable(1) also resets the totals.  lstm_timing_read() waits for
+ * the recorded events and returns the total milliseconds and the launch
+ * count of one kind.  Not thread-safe; timing adds a few microseconds per
+ * launch. */
+int lstm_timing_enable(int on);
+int lstm_timing_read(int kind, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* LAYER_LSTM_AMD_LSTM_H */

@@ -1,0 +1,90 @@
+// device_common.hpp -- element types, bf16 rounding, activations, MFMA
+// wrappers and the tagged-word exchange used by the gfx950 kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lstm {
+
+typedef uint16_t bf16_t;  // bfloat16 bit pattern in memory
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+
+// Round fp32 to the nearest bf16, ties to even; NaN -> quiet NaN.
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// Storage element <-> fp32.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int kBytes = 4;
+  __device__ __forceinline__ static float load(const float* p) { return *p; }
+  __device__ __forceinline__ static float to_f(float v) { return v; }
+  __device__ __forceinline__ static float from_f(float v) { return v; }
+};
+template <> struct Elem<bf16_t> {
+  static constexpr int kBytes = 2;
+  __device__ __forceinline__ static float load(const bf16_t* p) { return bf2f(*p); }
+  __device__ __forceinline__ static float to_f(bf16_t v) { return bf2f(v); }
+  __device__ __forceinline__ static bf16_t from_f(float v) { return f2bf(v); }
+};
+
+// Logistic sigmoid 1/(1+e^-u) and tanh, from the device math library in
+// full fp32 precision.  Saturate to 0/1/+-1 for large |u|, never NaN.
+__device__ __forceinline__ float sigmoidf(float u) { return 1.0f / (1.0f + expf(-u)); }
+__device__ __forceinline__ float tanh_f(float u) { return tanhf(u); }
+
+// One MFMA k-block: 16 bytes per lane of each operand.
+//  fp32: 4 k-values per lane -> four v_mfma_f32_16x16x4f32 (k-slot s of the
+//        lane group q holds k = 4q + s of a 16-wide k-block);
+//  bf16: 8 k-values per lane -> one v_mfma_f32_16x16x32_bf16.
+// Lane layout of both operands: row (A) / column (B) = lane % 16, k-group =
+// lane / 16.  Result: lane holds C[4*(lane/16)+i][lane%16], i = 0..3.
+template <typename T> struct Mfma;
+template <> struct Mfma<float> {
+  static constexpr int kBlock = 16;  // k elements per 16-byte fragment group
+  __device__ __forceinline__ static f32x4_t mac(u32x4_t a, u32x4_t b, f32x4_t c) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[0]), __uint_as_float(b[0]), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[1]), __uint_as_float(b[1]), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[2]), __uint_as_float(b[2]), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[3]), __uint_as_float(b[3]), c, 0, 0, 0);
+    return c;
+  }
+};
+template <> struct Mfma<bf16_t> {
+  static constexpr int kBlock = 32;
+  __device__ __forceinline__ static f32x4_t mac(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Tagged-word exchange between the work-groups of a persistent kernel.
+// A word is 8 bytes: low 32 bits = an fp32 value, high 32 bits = the step
+// tag.  Words are written and read with relaxed agent-scope 64-bit atomics,
+// so a reader that sees the expected tag sees the value written with it: no
+// fence and no separate barrier are needed.  Exchange buffers are cleared
+// (tag 0) before every launch and tags are 1-based.
+__device__ __forceinline__ void xstore(uint64_t* p, float v, uint32_t tag) {
+  uint64_t w = ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v);
+  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t xload(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t xtag(uint64_t w) { return (uint32_t)(w >> 32); }
+__device__ __forceinline__ float xval(uint64_t w) { return __uint_as_float((uint32_t)w); }
+
+// Time bound of one wait: s_memrealtime runs at 100 MHz.
+constexpr uint64_t kWaitTicks = 200000000ull;  // 2 s
+__device__ __forceinline__ uint64_t now_ticks() { return __builtin_amdgcn_s_memrealtime(); }
+
+}  // namespace lstm

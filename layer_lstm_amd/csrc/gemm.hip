@@ -1,0 +1,431 @@
+// gemm.hip -- MFMA GEMMs of the LSTM path (gfx950) and the small helpers.
+//
+// One tiled core serves the three products of the method:
+//   input projection  P  = X  . W_x^T + b   (M=T*B, N=4H, K=I)
+//   input gradient    dX = dG . W_x         (M=T*B, N=I,  K=4H)
+//   weight gradient   dW = dG^T . Z         (M=4H,  N=H+I, K=T*B), Z=[h_{t-1}|x_t]
+// ("SingleLayerLstmGrad" page: pre-activations W z_t + b of the forward
+// table; parameter gradient sum_t delta_t z_t^T of step 4; delta-z = W^T
+// delta of step 5, whose input block is dx.)
+//
+// Gate rows are handled in an interleaved order inside the path: column
+// n = 4j + g of P / dG is gate g of hidden unit j (row gH + j of W), so that
+// the recurrent kernels find the four gates of one unit next to each other.
+//
+// Tiles: 128 x 128 per 256-thread work-group (4 waves, 2 x 2, 64 x 64 each),
+// 128 bytes of k per stage (32 fp32 or 64 bf16), double-buffered in LDS.
+// Both operands sit in LDS as [row][k] with a 16-byte row pad; an operand
+// whose contiguous dimension is M or N is transposed in registers on its way
+// into LDS.  Accumulation is fp32 (v_mfma_f32_16x16x4f32 for fp32 storage,
+// v_mfma_f32_16x16x32_bf16 for bf16 storage).  Split-K partials are summed
+// by a second kernel in a fixed order, so results are run-to-run identical.
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace lstm {
+
+constexpr int kBM = 128, kBN = 128, kThreads = 256;
+constexpr int kRowBytes = 128;            // k bytes per stage and row
+constexpr int kLdsRow = kRowBytes + 16;   // padded LDS row
+constexpr int kTileBytes = kBM * kLdsRow;  // one operand, one stage
+
+__device__ __forceinline__ int64_t gate_row(int64_t n, int64_t H) { return (n & 3) * H + (n >> 2); }
+
+// ---------------------------------------------------------------------------
+// Operand accessors.  VEC = elements per 16 bytes.
+//
+// KRows: element (r, k) at row_ptr(r)[k] (k contiguous).
+// MNRows: element (k, r) at krow_ptr(k)[r] (r contiguous).
+template <typename T>
+struct KRowsX {  // plain row-major [R][ld], rows r, k in [0,K)
+  const T* p; int64_t ld; int64_t R, K; bool vec_ok;
+  __device__ __forceinline__ const T* row(int64_t r) const { return p + r * ld; }
+};
+template <typename T>
+struct KRowsWx {  // row r (interleaved gate row) of W's input block
+  const T* W; int64_t H, ld, R, K; bool vec_ok;
+  __device__ __forceinline__ const T* row(int64_t r) const { return W + gate_row(r, H) * ld + H; }
+};
+template <typename T>
+struct MNRowsWx {  // k-row = interleaved gate row of W's input block, r = input column
+  const T* W; int64_t H, ld, R, K; bool vec_ok;
+  __device__ __forceinline__ const T* krow(int64_t k, int64_t r) const { return W + gate_row(k, H) * ld + H + r; }
+  __device__ __forceinline__ bool same_seg(int64_t, int64_t) const { return true; }
+};
+template <typename T>
+struct MNRowsPlain {  // [K][ld], r contiguous
+  const T* p; int64_t ld, R, K; bool vec_ok;
+  __device__ __forceinline__ const T* krow(int64_t k, int64_t r) const { return p + k * ld + r; }
+  __device__ __forceinline__ bool same_seg(int64_t, int64_t) const { return true; }
+};
+template <typename T>
+struct MNRowsZ {  // Z[tb][r] = r < H ? h_{t-1}[b][r] : x[tb][r-H]
+  const T* x; const T* h0; const T* y; int64_t B, H, I, R, K; bool vec_ok;
+  __device__ __forceinline__ const T* krow(int64_t tb, int64_t r) const {
+    if (r < H) {
+      if (tb >= B) return y + (tb - B) * H + r;
+      return h0 ? h0 + tb * H + r : nullptr;  // nullptr = zero initial state
+    }
+    return x + tb * I + (r - H);
+  }
+  // r..r+n-1 do not straddle the h/x boundary
+  __device__ __forceinline__ bool same_seg(int64_t r, int64_t n) const { return (r >= H) || (r + n <= H); }
+};
+
+template <typename T>
+__device__ __forceinline__ u32x4_t load_krow_vec(const T* rowp, int64_t k, int64_t K, bool vec_ok) {
+  constexpr int VEC = 16 / sizeof(T);
+  u32x4_t v = {0, 0, 0, 0};
+  if (rowp == nullptr) return v;
+  if (vec_ok && k + VEC <= K) {
+    v = *reinterpret_cast<const u32x4_t*>(rowp + k);
+  } else {
+    T tmp[VEC];
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) tmp[i] = (k + i < K) ? rowp[k + i] : T(0);
+    v = __builtin_bit_cast(u32x4_t, tmp);
+  }
+  return v;
+}
+
+// 16 bytes along r at fixed k; zero outside [0,R) x [0,K)
+template <typename T, class Op>
+__device__ __forceinline__ u32x4_t load_mn_vec(const Op& op, int64_t k, int64_t r) {
+  constexpr int VEC = 16 / sizeof(T);
+  u32x4_t v = {0, 0, 0, 0};
+  if (k >= op.K || r >= op.R) return v;
+  if (op.vec_ok && r + VEC <= op.R && op.same_seg(r, VEC)) {
+    const T* p = op.krow(k, r);
+    if (p) v = *reinterpret_cast<const u32x4_t*>(p);
+    return v;
+  }
+  T tmp[VEC];
+#pragma unroll
+  for (int i = 0; i < VEC; ++i) {
+    T e = T(0);
+    if (r + i < op.R) {
+      const T* p = op.krow(k, r + i);
+      if (p) e = *p;
+    }
+    tmp[i] = e;
+  }
+  return __builtin_bit_cast(u32x4_t, tmp);
+}
+
+// ---------------------------------------------------------------------------
+// Stage loaders: fetch one 128 x (128 bytes of k) tile into registers, then
+// write it to LDS as [row][k].
+template <typename T, class Op, bool MN>
+struct Stager;
+
+// k-contiguous source: 128 rows x 8 vectors = 1024 vectors, 4 per thread
+template <typename T, class Op>
+struct Stager<T, Op, false> {
+  static constexpr int VEC = 16 / sizeof(T);
+  u32x4_t v[4];
+  __device__ __forceinline__ void fetch(const Op& op, int64_t row0, int64_t k0, int tid) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int id = tid + s * kThreads;
+      const int r = id >> 3, kv = id & 7;
+      const int64_t gr = row0 + r;
+      v[s] = (gr < op.R) ? load_krow_vec<T>(op.row(gr), k0 + kv * VEC, op.K, op.vec_ok) : u32x4_t{0, 0, 0, 0};
+    }
+  }
+  __device__ __forceinline__ void store(char* lds, int tid) const {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int id = tid + s * kThreads;
+      const int r = id >> 3, kv = id & 7;
+      *reinterpret_cast<u32x4_t*>(lds + r * kLdsRow + kv * 16) = v[s];
+    }
+  }
+};
+
+// r-contiguous source: blocks of 2 k-rows x (16 bytes of r), 2 per thread;
+// transposed into pairs (k, k+1) per r
+template <typename T, class Op>
+struct Stager<T, Op, true> {
+  static constexpr int VEC = 16 / sizeof(T);        // r per vector
+  static constexpr int KPAIRS = kRowBytes / sizeof(T) / 2;  // k pairs per stage
+  static constexpr int RVECS = kBM / VEC;           // vectors along r
+  u32x4_t v0[2], v1[2];
+  __device__ __forceinline__ void fetch(const Op& op, int64_t row0, int64_t k0, int tid) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int id = tid + s * kThreads;
+      const int rv = id / KPAIRS, kp = id % KPAIRS;
+      const int64_t k = k0 + 2 * kp, r = row0 + rv * VEC;
+      v0[s] = load_mn_vec<T>(op, k, r);
+      v1[s] = load_mn_vec<T>(op, k + 1, r);
+    }
+  }
+  __device__ __forceinline__ void store(char* lds, int tid) const {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int id = tid + s * kThreads;
+      const int rv = id / KPAIRS, kp = id % KPAIRS;
+      const T* a = reinterpret_cast<const T*>(&v0[s]);
+      const T* b = reinterpret_cast<const T*>(&v1[s]);
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        T pair[2] = {a[i], b[i]};
+        char* dst = lds + (rv * VEC + i) * kLdsRow + kp * 2 * (int)sizeof(T);
+        if constexpr (sizeof(T) == 2)
+          *reinterpret_cast<uint32_t*>(dst) = __builtin_bit_cast(uint32_t, pair);
+        else
+          *reinterpret_cast<uint64_t*>(dst) = __builtin_bit_cast(uint64_t, pair);
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Epilogues: called per output element (m < M, n < N).
+struct EpiP {  // fp32 P with bias in the interleaved column order
+  float* P; const void* bias; int64_t H, ldp; int dtype;
+  __device__ __forceinline__ void operator()(int64_t m, int64_t n, int, float v) const {
+    if (bias) {
+      const int64_t r = gate_row(n, H);
+      v += dtype ? bf2f(((const bf16_t*)bias)[r]) : ((const float*)bias)[r];
+    }
+    P[m * ldp + n] = v;
+  }
+};
+template <typename T>
+struct EpiStore {  // plain row-major output of the storage type
+  T* out; int64_t ld;
+  __device__ __forceinline__ void operator()(int64_t m, int64_t n, int, float v) const {
+    out[m * ld + n] = Elem<T>::from_f(v);
+  }
+};
+template <typename T>
+struct EpiDW {  // dW rows in gate-block order, or fp32 split-K partials
+  T* dW; float* part; int64_t H, M, N; int splits;
+  __device__ __forceinline__ void operator()(int64_t m, int64_t n, int split, float v) const {
+    if (splits > 1)
+      part[((int64_t)split * M + m) * N + n] = v;
+    else
+      dW[gate_row(m, H) * N + n] = Elem<T>::from_f(v);
+  }
+};
+
+// ---------------------------------------------------------------------------
+template <typename T, class AOp, bool AMN, class BOp, bool BMN, class Epi>
+__global__ void __launch_bounds__(kThreads)
+gemm_kernel(int64_t M, int64_t N, int64_t K, int ktiles_per_split, AOp aop, BOp bop, Epi epi) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* As = smem;                      // [2][kBM][kLdsRow]
+  char* Bs = smem + 2 * kTileBytes;     // [2][kBN][kLdsRow]
+  constexpr int KSTAGE = kRowBytes / sizeof(T);  // k elements per stage
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;
+  const int split = blockIdx.z;
+  const int64_t ktiles = (K + KSTAGE - 1) / KSTAGE;
+  const int64_t kt_begin = (int64_t)split * ktiles_per_split;
+  const int64_t kt_end = kt_begin + ktiles_per_split < ktiles ? kt_begin + ktiles_per_split : ktiles;
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  Stager<T, AOp, AMN> sa;
+  Stager<T, BOp, BMN> sb;
+  if (kt_begin < kt_end) {
+    sa.fetch(aop, m0, kt_begin * KSTAGE, tid);
+    sb.fetch(bop, n0, kt_begin * KSTAGE, tid);
+    sa.store(As, tid);
+    sb.store(Bs, tid);
+  }
+  __syncthreads();
+
+  const int fr = lane & 15, fq = lane >> 4;
+  for (int64_t kt = kt_begin; kt < kt_end; ++kt) {
+    const int st = (int)((kt - kt_begin) & 1);
+    const bool more = kt + 1 < kt_end;
+    if (more) {
+      sa.fetch(aop, m0, (kt + 1) * KSTAGE, tid);
+      sb.fetch(bop, n0, (kt + 1) * KSTAGE, tid);
+    }
+    const char* a_st = As + st * kTileBytes + (wm * 64 + fr) * kLdsRow + fq * 16;
+    const char* b_st = Bs + st * kTileBytes + (wn * 64 + fr) * kLdsRow + fq * 16;
+#pragma unroll
+    for (int kb = 0; kb < kRowBytes / 64; ++kb) {
+      u32x4_t af[4], bfv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const u32x4_t*>(a_st + i * 16 * kLdsRow + kb * 64);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bfv[j] = *reinterpret_cast<const u32x4_t*>(b_st + j * 16 * kLdsRow + kb * 64);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = Mfma<T>::mac(af[i], bfv[j], acc[i][j]);
+    }
+    if (more) {
+      sa.store(As + (st ^ 1) * kTileBytes, tid);
+      sb.store(Bs + (st ^ 1) * kTileBytes, tid);
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t n = n0 + wn * 64 + j * 16 + fr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t m = m0 + wm * 64 + i * 16 + fq * 4 + e;
+        if (m < M && n < N) epi(m, n, split, acc[i][j][e]);
+      }
+    }
+}
+
+template <typename T, class AOp, bool AMN, class BOp, bool BMN, class Epi>
+static hipError_t run_gemm(int64_t M, int64_t N, int64_t K, int splits, const AOp& a, const BOp& b,
+                           const Epi& e, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  constexpr int KSTAGE = kRowBytes / sizeof(T);
+  const int64_t ktiles = (K + KSTAGE - 1) / KSTAGE;
+  int ktps = (int)((ktiles + splits - 1) / splits);
+  if (ktps < 1) ktps = 1;
+  dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM), (unsigned)splits);
+  const size_t lds = 4 * (size_t)kTileBytes;
+  auto fn = gemm_kernel<T, AOp, AMN, BOp, BMN, Epi>;
+  hipError_t err = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(fn, grid, dim3(kThreads), lds, s, M, N, K, ktps, a, b, e);
+  return hipGetLastError();
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+template <typename T>
+static hipError_t inproj_t(const Plan& p, const void* x, const void* W, const void* b, float* P, hipStream_t s) {
+  constexpr int VEC = 16 / sizeof(T);
+  KRowsX<T> a{(const T*)x, p.I, p.TB, p.I, aligned16(x) && p.I % VEC == 0};
+  KRowsWx<T> bw{(const T*)W, p.H, p.Z, p.G4, p.I, aligned16(W) && p.Z % VEC == 0 && p.H % VEC == 0};
+  EpiP e{P, b, p.H, p.G4, p.dtype};
+  return run_gemm<T, KRowsX<T>, false, KRowsWx<T>, false, EpiP>(p.TB, p.G4, p.I, 1, a, bw, e, s);
+}
+
+template <typename T>
+static hipError_t dx_t(const Plan& p, const void* dG, const void* W, void* dx, hipStream_t s) {
+  constexpr int VEC = 16 / sizeof(T);
+  KRowsX<T> a{(const T*)dG, p.G4, p.TB, p.G4, aligned16(dG) && p.G4 % VEC == 0};
+  MNRowsWx<T> bw{(const T*)W, p.H, p.Z, p.I, p.G4, aligned16(W) && p.Z % VEC == 0 && p.H % VEC == 0};
+  EpiStore<T> e{(T*)dx, p.I};
+  return run_gemm<T, KRowsX<T>, false, MNRowsWx<T>, true, EpiStore<T>>(p.TB, p.I, p.G4, 1, a, bw, e, s);
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) splitk_reduce(const float* part, T* dW, int64_t M, int64_t N, int64_t H, int splits) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= M * N) return;
+  const int64_t m = idx / N, n = idx % N;
+  float acc = 0.f;
+  for (int sp = 0; sp < splits; ++sp) acc += part[(int64_t)sp * M * N + idx];
+  dW[gate_row(m, H) * N + n] = Elem<T>::from_f(acc);
+}
+
+template <typename T>
+static hipError_t dw_t(const Plan& p, const void* dG, const void* x, const void* h0, const void* y, void* dW,
+                       float* part, hipStream_t s) {
+  constexpr int VEC = 16 / sizeof(T);
+  MNRowsPlain<T> a{(const T*)dG, p.G4, p.G4, p.TB, aligned16(dG) && p.G4 % VEC == 0};
+  MNRowsZ<T> bz{(const T*)x, (const T*)h0, (const T*)y, p.B, p.H, p.I, p.Z, p.TB,
+                aligned16(x) && aligned16(y) && (h0 == nullptr || aligned16(h0)) && p.H % VEC == 0 && p.I % VEC == 0};
+  EpiDW<T> e{(T*)dW, part, p.H, p.G4, p.Z, p.dw_splits};
+  hipError_t err = run_gemm<T, MNRowsPlain<T>, true, MNRowsZ<T>, true, EpiDW<T>>(p.G4, p.Z, p.TB, p.dw_splits, a, bz, e, s);
+  if (err != hipSuccess || p.dw_splits <= 1) return err;
+  const int64_t n = p.G4 * p.Z;
+  hipLaunchKernelGGL(splitk_reduce<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, (T*)dW, p.G4, p.Z,
+                     p.H, p.dw_splits);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_inproj(const Plan& p, const void* x, const void* W, const void* b, float* P, hipStream_t s) {
+  return p.dtype ? inproj_t<bf16_t>(p, x, W, b, P, s) : inproj_t<float>(p, x, W, b, P, s);
+}
+hipError_t launch_gemm_dx(const Plan& p, const void* dG, const void* W, void* dx, hipStream_t s) {
+  return p.dtype ? dx_t<bf16_t>(p, dG, W, dx, s) : dx_t<float>(p, dG, W, dx, s);
+}
+hipError_t launch_gemm_dw(const Plan& p, const void* dG, const void* x, const void* h0, const void* y, void* dW,
+                          float* part, hipStream_t s) {
+  return p.dtype ? dw_t<bf16_t>(p, dG, x, h0, y, dW, part, s) : dw_t<float>(p, dG, x, h0, y, dW, part, s);
+}
+
+// ---------------------------------------------------------------------------
+// db: column sums of dG [TB][4H] (interleaved columns).  Pass 1: work-group
+// (column block of 64, row chunk) sums its rows in order into part[chunk];
+// pass 2 sums the chunks in order and writes db in gate-block order.
+template <typename T>
+__global__ void __launch_bounds__(256) colsum_pass1(const T* dG, float* part, int64_t TB, int64_t G4, int64_t rows_per_chunk) {
+  __shared__ float red[4][64];
+  const int c = threadIdx.x & 63, rg = threadIdx.x >> 6;
+  const int64_t col = (int64_t)blockIdx.x * 64 + c;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per_chunk;
+  int64_t r1 = r0 + rows_per_chunk;
+  if (r1 > TB) r1 = TB;
+  float acc = 0.f;
+  if (col < G4)
+    for (int64_t r = r0 + rg; r < r1; r += 4) acc += Elem<T>::to_f(dG[r * G4 + col]);
+  red[rg][c] = acc;
+  __syncthreads();
+  if (rg == 0 && col < G4) part[(int64_t)blockIdx.y * G4 + col] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
+}
+
+template <typename T>
+__global__ void __launch_bounds__(256) colsum_pass2(const float* part, T* db, int64_t G4, int64_t H, int chunks) {
+  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (n >= G4) return;
+  float acc = 0.f;
+  for (int c = 0; c < chunks; ++c) acc += part[(int64_t)c * G4 + n];
+  db[gate_row(n, H)] = Elem<T>::from_f(acc);
+}
+
+hipError_t launch_colsum_db(const Plan& p, const void* dG, void* db, float* part, hipStream_t s) {
+  const int64_t rpc = (p.TB + p.col_chunks - 1) / p.col_chunks;
+  dim3 g1((unsigned)((p.G4 + 63) / 64), (unsigned)p.col_chunks);
+  dim3 g2((unsigned)((p.G4 + 255) / 256));
+  if (p.dtype) {
+    hipLaunchKernelGGL(colsum_pass1<bf16_t>, g1, dim3(256), 0, s, (const bf16_t*)dG, part, p.TB, p.G4, rpc);
+    hipLaunchKernelGGL(colsum_pass2<bf16_t>, g2, dim3(256), 0, s, part, (bf16_t*)db, p.G4, p.H, p.col_chunks);
+  } else {
+    hipLaunchKernelGGL(colsum_pass1<float>, g1, dim3(256), 0, s, (const float*)dG, part, p.TB, p.G4, rpc);
+    hipLaunchKernelGGL(colsum_pass2<float>, g2, dim3(256), 0, s, part, (float*)db, p.G4, p.H, p.col_chunks);
+  }
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) fill_zero_kernel(uint32_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
+  if (bytes == 0) return hipSuccess;
+  const int64_t n = (int64_t)(bytes / 4);
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t*)p, n);
+  return hipGetLastError();
+}
+
+// dst = src (n elements of esize bytes), or dst = 0 when src is NULL
+__global__ void __launch_bounds__(256) copy_state_kernel(const uint8_t* src, uint8_t* dst, int64_t nbytes) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < nbytes) dst[i] = src ? src[i] : (uint8_t)0;
+}
+hipError_t launch_copy_state(const void* src, void* dst, size_t n, int esize, hipStream_t s) {
+  const int64_t nb = (int64_t)n * esize;
+  if (nb == 0) return hipSuccess;
+  hipLaunchKernelGGL(copy_state_kernel, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s, (const uint8_t*)src,
+                     (uint8_t*)dst, nb);
+  return hipGetLastError();
+}
+
+}  // namespace lstm

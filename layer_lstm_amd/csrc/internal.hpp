@@ -1,0 +1,62 @@
+// internal.hpp -- host-side plan and launcher declarations shared by the
+// C-ABI layer and the kernel translation units (not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lstm {
+
+// Bit of the error word (first 4 bytes of the workspace) that a recurrent
+// kernel sets when one of its per-step waits hits the time bound.
+constexpr uint32_t kErrTimeout = 1u;
+
+// Work partition and workspace layout of one problem shape.
+struct Plan {
+  int64_t T, B, I, H;
+  int dtype;   // 0 = fp32, 1 = bf16
+  int esize;   // bytes per storage element
+  int64_t TB, G4, Z;  // T*B, 4H, H+I
+
+  // persistent recurrent kernels: a grid of nBG x nJG work-groups; group
+  // (bg, jg) owns batch rows [bg*NB, (bg+1)*NB) and hidden units
+  // [jg*NJ, (jg+1)*NJ)
+  int NB, NJ, nBG, nJG, grid;
+  int Hp;       // H rounded up to the MFMA k-block
+  int Bp;       // nBG * NB
+  size_t lds_fwd, lds_bwd;
+
+  // workspace (byte offsets, 256-aligned)
+  size_t off_ctrl, off_P, off_G, off_C, off_HX, off_PX, off_dWp, off_col, total;
+  size_t bytes_HX, bytes_PX;
+  int dw_splits;    // split-K factor of the dW product
+  int col_chunks;   // row chunks of the db column sum
+};
+
+// Fill the plan for a shape; returns 0 or an LSTM_ERR_* code.
+int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p);
+
+// ---- launchers (return hipError_t) ----
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+hipError_t launch_copy_state(const void* src, void* dst, size_t n, int esize, hipStream_t s);
+
+// P[tb][4j+g] = sum_k x[tb][k] W[gH+j][H+k] + b[gH+j]   (fp32 out)
+hipError_t launch_gemm_inproj(const Plan& p, const void* x, const void* W, const void* b,
+                              float* P, hipStream_t s);
+// dx[tb][i] = sum_n dG[tb][n] W[row(n)][H+i]
+hipError_t launch_gemm_dx(const Plan& p, const void* dG, const void* W, void* dx, hipStream_t s);
+// dW[row(m)][n] = sum_tb dG[tb][m] Z[tb][n],  Z = [h_{t-1} | x_t]
+hipError_t launch_gemm_dw(const Plan& p, const void* dG, const void* x, const void* h0,
+                          const void* y, void* dW, float* part, hipStream_t s);
+// db[row(n)] = sum_tb dG[tb][n]
+hipError_t launch_colsum_db(const Plan& p, const void* dG, void* db, float* part, hipStream_t s);
+
+hipError_t launch_fwd_recurrent(const Plan& p, const float* P, const void* W, const void* h0,
+                                const void* c0, void* y, void* hT, void* cT, void* Gs, float* Cs,
+                                uint64_t* HX, uint32_t* err, hipStream_t s);
+hipError_t launch_bwd_recurrent(const Plan& p, const void* W, const void* c0, const void* dy,
+                                const void* dhT, const void* dcT, const void* Gs, const float* Cs,
+                                void* dG, uint64_t* PX, void* dh0, void* dc0, uint32_t* err,
+                                hipStream_t s);
+
+}  // namespace lstm

@@ -1,0 +1,336 @@
+// lstm_api.hip -- the extern "C" entry points declared in include/lstm.h:
+// argument checks, the work partition and workspace layout, and the launch
+// sequence of each pass.  No device memory is allocated here.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <vector>
+
+#include "internal.hpp"
+#include "lstm.h"
+
+namespace lstm {
+
+static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+static int device_cus(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return LSTM_ERR_DEVICE;
+  static int cached_dev = -1, cached_cus = 0, cached_ok = 0;
+  if (dev != cached_dev) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return LSTM_ERR_DEVICE;
+    cached_ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    cached_cus = prop.multiProcessorCount;
+    cached_dev = dev;
+  }
+  if (!cached_ok) return LSTM_ERR_DEVICE;
+  *cus = cached_cus;
+  return LSTM_OK;
+}
+
+int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
+  if (T < 0 || B < 0 || I < 0 || H <= 0) return LSTM_ERR_DIMS;
+  if (dtype != LSTM_F32 && dtype != LSTM_BF16) return LSTM_ERR_DTYPE;
+  if (H > 2048 || I > 65536) return LSTM_ERR_UNSUPPORTED;
+  if (T > 0 && B > 0 && T * B > ((int64_t)1 << 31) / (4 * H)) return LSTM_ERR_UNSUPPORTED;
+  int cus = 0;
+  const int dev = device_cus(&cus);
+  if (dev != LSTM_OK) return dev;
+
+  memset(p, 0, sizeof(*p));
+  p->T = T; p->B = B; p->I = I; p->H = H; p->dtype = dtype;
+  p->esize = dtype ? 2 : 4;
+  p->TB = T * B; p->G4 = 4 * H; p->Z = H + I;
+  const int e = p->esize;
+  const int KB = dtype ? 32 : 16;                       // MFMA k-block (elements)
+  p->Hp = (int)((H + 4 * KB - 1) / (4 * KB) * (4 * KB));
+
+  // Partition of the persistent kernels: smallest per-step exchange first
+  // (fewest batch rows per group), then the most work-groups.
+  const int nb_opts[3] = {16, 32, 64};
+  const int nj_opts[2] = {8, 16};
+  bool found = false;
+  for (int a = 0; a < 3 && !found; ++a) {
+    for (int c = 0; c < 2 && !found; ++c) {
+      const int NB = nb_opts[a], NJ = nj_opts[c];
+      const int64_t nBG = B > 0 ? (B + NB - 1) / NB : 1;
+      const int64_t nJG = (H + NJ - 1) / NJ;
+      if (nBG * nJG > cus) continue;
+      const int KS = 4 / (NJ / 4);
+      if (p->Hp / KB / KS > 32) continue;                 // forward W_h fragments per wave
+      const int nkbr = 4 * NJ * e / 64;
+      if ((p->Hp / 16 + 3) / 4 > 32 / nkbr) continue;     // backward W_h^T fragments per wave
+      if (NB * NJ > 1024) continue;
+      const size_t lds_f = (size_t)NB * (p->Hp * e + 16) + 16384;
+      if (lds_f > 160 * 1024) continue;
+      p->NB = NB; p->NJ = NJ; p->nBG = (int)nBG; p->nJG = (int)nJG; p->grid = (int)(nBG * nJG);
+      p->lds_fwd = lds_f;
+      p->lds_bwd = (size_t)NB * (4 * NJ * e + 16);
+      found = true;
+    }
+  }
+  if (!found) return LSTM_ERR_UNSUPPORTED;
+  p->Bp = p->nBG * p->NB;
+
+  // split-K of dW: enough work-groups to fill the chip, >= 8 k-tiles each
+  const int64_t kstage = 128 / e;
+  const int64_t tiles = ((p->G4 + 127) / 128) * ((p->Z + 127) / 128);
+  const int64_t ktiles = (p->TB + kstage - 1) / kstage;
+  int splits = 1;
+  while (splits < 16 && tiles * splits < cus && ktiles / (splits * 2) >= 8) splits *= 2;
+  p->dw_splits = splits;
+  int64_t chunks = p->TB / 128;
+  p->col_chunks = (int)(chunks < 1 ? 1 : (chunks > 64 ? 64 : chunks));
+
+  const size_t HW = dtype ? (size_t)p->Hp / 2 : (size_t)p->Hp;
+  size_t off = 0;
+  p->off_ctrl = off; off += 256;
+  p->off_HX = off; p->bytes_HX = align256(2 * (size_t)p->Bp * HW * 8); off += p->bytes_HX;
+  p->off_PX = off; p->bytes_PX = align256(2 * (size_t)p->nJG * p->Hp * p->Bp * 8); off += p->bytes_PX;
+  p->off_P = off; off += align256((size_t)p->TB * p->G4 * 4);
+  p->off_G = off; off += align256((size_t)p->TB * p->G4 * e);
+  p->off_C = off; off += align256((size_t)p->TB * H * 4);
+  p->off_dWp = off; off += splits > 1 ? align256((size_t)splits * p->G4 * p->Z * 4) : 0;
+  p->off_col = off; off += align256((size_t)p->col_chunks * p->G4 * 4);
+  p->total = off;
+  return LSTM_OK;
+}
+
+static int status_of(hipError_t e) {
+  if (e == hipSuccess) return LSTM_OK;
+  if (e == hipErrorCooperativeLaunchTooLarge) return LSTM_ERR_COOP;
+  return LSTM_ERR_LAUNCH;
+}
+
+static bool misaligned(const void* ptr, int esize) { return ptr && ((uintptr_t)ptr % (uintptr_t)esize) != 0; }
+
+// ---- per-kernel event timing (lstm_timing_enable / lstm_timing_read) ----
+enum { kKinds = 7 };
+struct Pending { int kind; hipEvent_t a, b; };
+static bool g_timing_on = false;
+static std::vector<Pending> g_pending;
+static std::vector<hipEvent_t> g_pool;
+static double g_total_ms[kKinds];
+static int64_t g_launches[kKinds];
+
+static hipEvent_t take_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets the launches made during its lifetime with two events.
+struct Timed {
+  int kind;
+  hipStream_t s;
+  hipEvent_t a = nullptr;
+  Timed(int k, hipStream_t st) : kind(k), s(st) {
+    if (g_timing_on && (a = take_event()) != nullptr && hipEventRecord(a, s) != hipSuccess) {
+      g_pool.push_back(a);
+      a = nullptr;
+    }
+  }
+  ~Timed() {
+    if (!a) return;
+    hipEvent_t b = take_event();
+    if (b && hipEventRecord(b, s) == hipSuccess) {
+      g_pending.push_back({kind, a, b});
+    } else {
+      g_pool.push_back(a);
+      if (b) g_pool.push_back(b);
+    }
+  }
+};
+
+static void flush_timing() {
+  for (const Pending& p : g_pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(p.b) == hipSuccess && hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
+      g_total_ms[p.kind] += ms;
+      g_launches[p.kind] += 1;
+    }
+    g_pool.push_back(p.a);
+    g_pool.push_back(p.b);
+  }
+  g_pending.clear();
+}
+
+}  // namespace lstm
+
+using namespace lstm;
+
+extern "C" {
+
+int lstm_abi_version(void) { return LSTM_ABI_VERSION; }
+
+const char* lstm_status_string(int status) {
+  switch (status) {
+    case LSTM_OK: return "ok";
+    case LSTM_ERR_NULL: return "a required pointer is NULL";
+    case LSTM_ERR_DIMS: return "invalid dimensions (T, B, I < 0 or H <= 0)";
+    case LSTM_ERR_DTYPE: return "unsupported dtype";
+    case LSTM_ERR_ALIGN: return "misaligned pointer";
+    case LSTM_ERR_WORKSPACE: return "workspace too small";
+    case LSTM_ERR_UNSUPPORTED: return "shape outside the supported envelope";
+    case LSTM_ERR_COOP: return "persistent grid cannot be co-resident";
+    case LSTM_ERR_LAUNCH: return "HIP launch failed";
+    case LSTM_ERR_TIMEOUT: return "a recurrent step wait timed out";
+    case LSTM_ERR_DEVICE: return "current device is not gfx950";
+    default: return "unknown status";
+  }
+}
+
+int lstm_query(const lstm_shape* shape, size_t* workspace_bytes) {
+  if (!shape || !workspace_bytes) return LSTM_ERR_NULL;
+  if (shape->reserved != 0) return LSTM_ERR_DTYPE;
+  Plan p;
+  const int rc = make_plan(shape->T, shape->B, shape->I, shape->H, shape->dtype, &p);
+  if (rc != LSTM_OK) return rc;
+  *workspace_bytes = p.total;
+  return LSTM_OK;
+}
+
+int lstm_fwd_train(const lstm_shape* shape, const void* x, const void* W, const void* b, const void* h0,
+                   const void* c0, void* y, void* hT, void* cT, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  if (!shape) return LSTM_ERR_NULL;
+  if (shape->reserved != 0) return LSTM_ERR_DTYPE;
+  Plan p;
+  int rc = make_plan(shape->T, shape->B, shape->I, shape->H, shape->dtype, &p);
+  if (rc != LSTM_OK) return rc;
+  const int e = p.esize;
+  if (!W || !workspace) return LSTM_ERR_NULL;
+  if (p.TB * p.I > 0 && !x) return LSTM_ERR_NULL;
+  if (p.TB > 0 && !y) return LSTM_ERR_NULL;
+  if (p.B > 0 && (!hT || !cT)) return LSTM_ERR_NULL;
+  if (misaligned(x, e) || misaligned(W, e) || misaligned(b, e) || misaligned(h0, e) || misaligned(c0, e) ||
+      misaligned(y, e) || misaligned(hT, e) || misaligned(cT, e) || ((uintptr_t)workspace & 255u))
+    return LSTM_ERR_ALIGN;
+  if (workspace_bytes < p.total) return LSTM_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  hipError_t err = hipSuccess;
+
+  if (p.B == 0) return LSTM_OK;
+  if (p.T == 0) {
+    Timed tm(6, s);
+    err = launch_copy_state(h0, hT, (size_t)(p.B * p.H), e, s);
+    if (err == hipSuccess) err = launch_copy_state(c0, cT, (size_t)(p.B * p.H), e, s);
+    return status_of(err);
+  }
+  // control word + step-exchange buffers start cleared (tags 0)
+  {
+    Timed tm(6, s);
+    err = launch_fill_zero(ws + p.off_ctrl, p.off_HX + p.bytes_HX - p.off_ctrl, s);
+  }
+  float* P = (float*)(ws + p.off_P);
+  if (err == hipSuccess) {
+    Timed tm(0, s);
+    err = launch_gemm_inproj(p, x, W, b, P, s);
+  }
+  if (err == hipSuccess) {
+    Timed tm(1, s);
+    err = launch_fwd_recurrent(p, P, W, h0, c0, y, hT, cT, ws + p.off_G, (float*)(ws + p.off_C),
+                               (uint64_t*)(ws + p.off_HX), (uint32_t*)(ws + p.off_ctrl), s);
+  }
+  return status_of(err);
+}
+
+int lstm_bwd(const lstm_shape* shape, const void* dy, const void* dhT, const void* dcT, const void* x,
+             const void* W, const void* h0, const void* c0, const void* y, void* workspace, size_t workspace_bytes,
+             void* dx, void* dW, void* db, void* dh0, void* dc0, void* stream) {
+  if (!shape) return LSTM_ERR_NULL;
+  if (shape->reserved != 0) return LSTM_ERR_DTYPE;
+  Plan p;
+  int rc = make_plan(shape->T, shape->B, shape->I, shape->H, shape->dtype, &p);
+  if (rc != LSTM_OK) return rc;
+  const int e = p.esize;
+  if (!W || !dW || !workspace) return LSTM_ERR_NULL;
+  if (p.TB > 0 && (!dy || !y)) return LSTM_ERR_NULL;
+  if (p.TB * p.I > 0 && (!x || !dx)) return LSTM_ERR_NULL;
+  if (p.B > 0 && (!dh0 || !dc0)) return LSTM_ERR_NULL;
+  if (misaligned(dy, e) || misaligned(dhT, e) || misaligned(dcT, e) || misaligned(x, e) || misaligned(W, e) ||
+      misaligned(h0, e) || misaligned(c0, e) || misaligned(y, e) || misaligned(dx, e) || misaligned(dW, e) ||
+      misaligned(db, e) || misaligned(dh0, e) || misaligned(dc0, e) || ((uintptr_t)workspace & 255u))
+    return LSTM_ERR_ALIGN;
+  if (workspace_bytes < p.total) return LSTM_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  hipError_t err = hipSuccess;
+
+  if (p.T == 0 || p.B == 0) {
+    Timed tm(6, s);
+    err = launch_fill_zero(dW, (size_t)(p.G4 * p.Z) * e, s);
+    if (err == hipSuccess && db) err = launch_fill_zero(db, (size_t)p.G4 * e, s);
+    if (err == hipSuccess && p.B > 0) err = launch_copy_state(dhT, dh0, (size_t)(p.B * p.H), e, s);
+    if (err == hipSuccess && p.B > 0) err = launch_copy_state(dcT, dc0, (size_t)(p.B * p.H), e, s);
+    return status_of(err);
+  }
+  // control word + exchange buffers start cleared
+  {
+    Timed tm(6, s);
+    err = launch_fill_zero(ws + p.off_ctrl, p.off_PX + p.bytes_PX - p.off_ctrl, s);
+  }
+  void* dG = ws + p.off_P;  // the input projection is dead after the forward
+  if (err == hipSuccess) {
+    Timed tm(2, s);
+    err = launch_bwd_recurrent(p, W, c0, dy, dhT, dcT, ws + p.off_G, (const float*)(ws + p.off_C), dG,
+                               (uint64_t*)(ws + p.off_PX), dh0, dc0, (uint32_t*)(ws + p.off_ctrl), s);
+  }
+  if (err == hipSuccess) {
+    Timed tm(3, s);
+    err = launch_gemm_dw(p, dG, x, h0, y, dW, (float*)(ws + p.off_dWp), s);
+  }
+  if (err == hipSuccess && p.I > 0) {
+    Timed tm(4, s);
+    err = launch_gemm_dx(p, dG, W, dx, s);
+  }
+  if (err == hipSuccess && db) {
+    Timed tm(5, s);
+    err = launch_colsum_db(p, dG, db, (float*)(ws + p.off_col), s);
+  }
+  return status_of(err);
+}
+
+int lstm_check_workspace(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return LSTM_ERR_NULL;
+  if (workspace_bytes < 256) return LSTM_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  if (hipStreamSynchronize(s) != hipSuccess) return LSTM_ERR_LAUNCH;
+  uint32_t word = 0;
+  if (hipMemcpy(&word, workspace, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess) return LSTM_ERR_LAUNCH;
+  if (word & kErrTimeout) {
+    const uint32_t zero = 0;
+    if (hipMemcpy(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return LSTM_ERR_LAUNCH;
+    return LSTM_ERR_TIMEOUT;
+  }
+  return LSTM_OK;
+}
+
+int lstm_timing_enable(int on) {
+  flush_timing();
+  g_timing_on = on != 0;
+  if (g_timing_on)
+    for (int k = 0; k < kKinds; ++k) {
+      g_total_ms[k] = 0.0;
+      g_launches[k] = 0;
+    }
+  return LSTM_OK;
+}
+
+int lstm_timing_read(int kind, double* total_ms, int64_t* launches) {
+  if (!total_ms || !launches) return LSTM_ERR_NULL;
+  if (kind < 0 || kind >= kKinds) return LSTM_ERR_DIMS;
+  flush_timing();
+  *total_ms = g_total_ms[kind];
+  *launches = g_launches[kind];
+  return LSTM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,188 @@
+"""Thin ctypes binding of liblstm.so (include/lstm.h).
+
+Argument marshalling only: every step of the forward and backward pass runs
+in the library's HIP kernels.  torch is used for device memory and streams
+(it is imported before the library so that both share one HIP runtime).
+There is no fallback: if liblstm.so is missing or cannot be loaded, importing
+this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liblstm.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m layer_lstm_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+# --- constants restated from include/lstm.h ---------------------------------
+ABI_VERSION = 1
+GATE_I, GATE_F, GATE_G, GATE_O = 0, 1, 2, 3
+F32, BF16 = 0, 1
+OK = 0
+STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_DIMS", -3: "ERR_DTYPE", -4: "ERR_ALIGN",
+          -5: "ERR_WORKSPACE", -6: "ERR_UNSUPPORTED", -7: "ERR_COOP", -8: "ERR_LAUNCH",
+          -9: "ERR_TIMEOUT", -10: "ERR_DEVICE"}
+EXPORTS = ("lstm_abi_version", "lstm_status_string", "lstm_query", "lstm_fwd_train", "lstm_bwd",
+           "lstm_check_workspace", "lstm_timing_enable", "lstm_timing_read")
+KERNEL_KINDS = ("input_projection", "forward_recurrence", "backward_recurrence", "dW_product",
+                "dx_product", "db_colsum", "clear_copy")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("B", ctypes.c_int64), ("I", ctypes.c_int64),
+                ("H", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+_P = ctypes.c_void_p
+_lib.lstm_abi_version.restype = ctypes.c_int
+_lib.lstm_status_string.restype = ctypes.c_char_p
+_lib.lstm_status_string.argtypes = [ctypes.c_int]
+_lib.lstm_query.restype = ctypes.c_int
+_lib.lstm_query.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_size_t)]
+_lib.lstm_fwd_train.restype = ctypes.c_int
+_lib.lstm_fwd_train.argtypes = [ctypes.POINTER(Shape)] + [_P] * 8 + [_P, ctypes.c_size_t, _P]
+_lib.lstm_bwd.restype = ctypes.c_int
+_lib.lstm_bwd.argtypes = [ctypes.POINTER(Shape)] + [_P] * 8 + [_P, ctypes.c_size_t] + [_P] * 5 + [_P]
+_lib.lstm_check_workspace.restype = ctypes.c_int
+_lib.lstm_check_workspace.argtypes = [_P, ctypes.c_size_t, _P]
+_lib.lstm_timing_enable.restype = ctypes.c_int
+_lib.lstm_timing_enable.argtypes = [ctypes.c_int]
+_lib.lstm_timing_read.restype = ctypes.c_int
+_lib.lstm_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+
+
+class LstmError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = _lib.lstm_status_string(code).decode()
+        super().__init__(f"{where}: {STATUS.get(code, code)} ({msg})")
+
+
+def lib():
+    return _lib
+
+
+def abi_version() -> int:
+    return _lib.lstm_abi_version()
+
+
+def status_string(code: int) -> str:
+    return _lib.lstm_status_string(code).decode()
+
+
+def torch_dtype(dtype: int):
+    return torch.float32 if dtype == F32 else torch.bfloat16
+
+
+def make_shape(T, B, I, H, dtype) -> Shape:
+    return Shape(int(T), int(B), int(I), int(H), int(dtype), 0)
+
+
+def query(shape: Shape) -> int:
+    n = ctypes.c_size_t(0)
+    rc = _lib.lstm_query(ctypes.byref(shape), ctypes.byref(n))
+    if rc != OK:
+        raise LstmError(rc, "lstm_query")
+    return n.value
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def fwd_train(shape, x, W, b, h0, c0, y, hT, cT, workspace, ws_bytes=None, stream=None, check=True):
+    """lstm_fwd_train on torch tensors (None = NULL).  Returns the status."""
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    rc = _lib.lstm_fwd_train(ctypes.byref(shape), _ptr(x), _ptr(W), _ptr(b), _ptr(h0), _ptr(c0),
+                             _ptr(y), _ptr(hT), _ptr(cT), _ptr(workspace), ws_bytes, _stream(stream))
+    if check and rc != OK:
+        raise LstmError(rc, "lstm_fwd_train")
+    return rc
+
+
+def bwd(shape, dy, dhT, dcT, x, W, h0, c0, y, workspace, dx, dW, db, dh0, dc0, ws_bytes=None,
+        stream=None, check=True):
+    """lstm_bwd on torch tensors (None = NULL).  Returns the status."""
+    if ws_bytes is None:
+        ws_bytes = workspace.numel() * workspace.element_size()
+    rc = _lib.lstm_bwd(ctypes.byref(shape), _ptr(dy), _ptr(dhT), _ptr(dcT), _ptr(x), _ptr(W),
+                       _ptr(h0), _ptr(c0), _ptr(y), _ptr(workspace), ws_bytes, _ptr(dx), _ptr(dW),
+                       _ptr(db), _ptr(dh0), _ptr(dc0), _stream(stream))
+    if check and rc != OK:
+        raise LstmError(rc, "lstm_bwd")
+    return rc
+
+
+def check_workspace(workspace, stream=None) -> int:
+    return _lib.lstm_check_workspace(_ptr(workspace), workspace.numel() * workspace.element_size(),
+                                     _stream(stream))
+
+
+def timing_enable(on: bool) -> None:
+    _lib.lstm_timing_enable(1 if on else 0)
+
+
+def timing_read() -> dict:
+    """{kind name: (total ms, launches)} of the per-kernel event timing."""
+    out = {}
+    for k, name in enumerate(KERNEL_KINDS):
+        ms, n = ctypes.c_double(0), ctypes.c_int64(0)
+        rc = _lib.lstm_timing_read(k, ctypes.byref(ms), ctypes.byref(n))
+        if rc != OK:
+            raise LstmError(rc, "lstm_timing_read")
+        out[name] = (ms.value, n.value)
+    return out
+
+
+class Lstm:
+    """One problem shape with its workspace and output buffers on the current
+    device.  ``forward``/``backward`` take device tensors and return device
+    tensors; nothing is synchronised."""
+
+    def __init__(self, T, B, I, H, dtype=F32, device="cuda"):
+        self.shape = make_shape(T, B, I, H, dtype)
+        self.T, self.B, self.I, self.H, self.dtype = T, B, I, H, dtype
+        self.tdtype = torch_dtype(dtype)
+        self.ws_bytes = query(self.shape)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        dev, td = device, self.tdtype
+        self.y = torch.empty((T, B, H), dtype=td, device=dev)
+        self.hT = torch.empty((B, H), dtype=td, device=dev)
+        self.cT = torch.empty((B, H), dtype=td, device=dev)
+        self.dx = torch.empty((T, B, I), dtype=td, device=dev)
+        self.dW = torch.empty((4 * H, H + I), dtype=td, device=dev)
+        self.db = torch.empty((4 * H,), dtype=td, device=dev)
+        self.dh0 = torch.empty((B, H), dtype=td, device=dev)
+        self.dc0 = torch.empty((B, H), dtype=td, device=dev)
+
+    def forward(self, x, W, b=None, h0=None, c0=None, stream=None):
+        fwd_train(self.shape, x, W, b, h0, c0, self.y, self.hT, self.cT, self.workspace,
+                  self.ws_bytes, stream)
+        return self.y, self.hT, self.cT
+
+    def backward(self, dy, dhT, dcT, x, W, h0=None, c0=None, want_db=True, stream=None):
+        bwd(self.shape, dy, dhT, dcT, x, W, h0, c0, self.y, self.workspace, self.dx, self.dW,
+            self.db if want_db else None, self.dh0, self.dc0, self.ws_bytes, stream)
+        return self.dx, self.dW, self.db, self.dh0, self.dc0
+
+    def check(self, stream=None):
+        rc = check_workspace(self.workspace, stream)
+        if rc != OK:
+            raise LstmError(rc, "lstm_check_workspace")
