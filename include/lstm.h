@@ -100,7 +100,8 @@ int lstm_abi_version(void);
 const char* lstm_status_string(int status);
 
 /* Workspace size in bytes for `shape` on the current device.
- * Envelope: H <= 2048, I <= 65536, T*B <= 2^31/4H.  Returns LSTM_OK and sets
+ * Envelope: H <= 1024 (fp32) or 2048 (bf16), I <= 65536, T*B <= 2^31/4H,
+ * T <= 2^30.  Returns LSTM_OK and sets
  * *workspace_bytes, or an error code (workspace_bytes untouched). */
 int lstm_query(const lstm_shape* shape, size_t* workspace_bytes);
 
@@ -141,6 +142,17 @@ int lstm_check_workspace(void* workspace, size_t workspace_bytes, void* stream);
  * launch. */
 int lstm_timing_enable(int on);
 int lstm_timing_read(int kind, double* total_ms, int64_t* launches);
+
+/* Step-phase stamps of the recurrent kernels, for measurement.  With a
+ * device buffer of at least 2*8*T*5 uint64 values set, each later call whose
+ * sequence length is at most T makes thread 0 of work-groups 0..7 write the
+ * 100 MHz real-time clock (s_memrealtime) at five points of every step: forward -- step
+ * start, its h_{t-1} words read, all threads past the wait, product done,
+ * outputs written; backward -- step start, dh carry gathered, deltas
+ * written, partial products sent, step end.  Layout: [pass (0 forward,
+ * 1 backward)][work-group][step in execution order][point].  NULL disables.
+ * Returns LSTM_ERR_WORKSPACE if the buffer is too small for T. */
+int lstm_stamps_set(void* device_buffer, size_t bytes, int64_t T);
 
 #ifdef __cplusplus
 } /* extern "C" */

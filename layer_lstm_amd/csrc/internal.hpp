@@ -11,6 +11,9 @@ namespace lstm {
 // kernel sets when one of its per-step waits hits the time bound.
 constexpr uint32_t kErrTimeout = 1u;
 
+// Phase stamps of the recurrent kernels (see lstm_stamps_set in lstm.h).
+constexpr int kStampWGs = 8, kPhases = 5;
+
 // Work partition and workspace layout of one problem shape.
 struct Plan {
   int64_t T, B, I, H;
@@ -22,7 +25,10 @@ struct Plan {
   // (bg, jg) owns batch rows [bg*NB, (bg+1)*NB) and hidden units
   // [jg*NJ, (jg+1)*NJ)
   int NB, NJ, nBG, nJG, grid;
-  int Hp;       // H rounded up to the MFMA k-block
+  int Hp;       // H rounded up to a power of two (>= 4 MFMA k-blocks)
+  int fwd_nkbw; // forward: W_h k-blocks per wave
+  int bwd_mtw;  // backward: 16-column tiles of W_h^T per wave
+  int words_per_thread;  // exchange words a thread reads per step (NB*H / 256, rounded up)
   int Bp;       // nBG * NB
   size_t lds_fwd, lds_bwd;
 
@@ -53,10 +59,10 @@ hipError_t launch_colsum_db(const Plan& p, const void* dG, void* db, float* part
 
 hipError_t launch_fwd_recurrent(const Plan& p, const float* P, const void* W, const void* h0,
                                 const void* c0, void* y, void* hT, void* cT, void* Gs, float* Cs,
-                                uint64_t* HX, uint32_t* err, hipStream_t s);
+                                uint64_t* HX, uint32_t* err, uint64_t* stamps, hipStream_t s);
 hipError_t launch_bwd_recurrent(const Plan& p, const void* W, const void* c0, const void* dy,
                                 const void* dhT, const void* dcT, const void* Gs, const float* Cs,
                                 void* dG, uint64_t* PX, void* dh0, void* dc0, uint32_t* err,
-                                hipStream_t s);
+                                uint64_t* stamps, hipStream_t s);
 
 }  // namespace lstm

@@ -32,7 +32,7 @@ static int device_cus(int* cus) {
 int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
   if (T < 0 || B < 0 || I < 0 || H <= 0) return LSTM_ERR_DIMS;
   if (dtype != LSTM_F32 && dtype != LSTM_BF16) return LSTM_ERR_DTYPE;
-  if (H > 2048 || I > 65536) return LSTM_ERR_UNSUPPORTED;
+  if (H > 2048 || I > 65536 || T > ((int64_t)1 << 30)) return LSTM_ERR_UNSUPPORTED;
   if (T > 0 && B > 0 && T * B > ((int64_t)1 << 31) / (4 * H)) return LSTM_ERR_UNSUPPORTED;
   int cus = 0;
   const int dev = device_cus(&cus);
@@ -44,34 +44,49 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
   p->TB = T * B; p->G4 = 4 * H; p->Z = H + I;
   const int e = p->esize;
   const int KB = dtype ? 32 : 16;                       // MFMA k-block (elements)
-  p->Hp = (int)((H + 4 * KB - 1) / (4 * KB) * (4 * KB));
+  // H padded to a power of two, at least one k-block per wave
+  int Hp = 4 * KB;
+  while (Hp < H) Hp *= 2;
+  p->Hp = Hp;
 
-  // Partition of the persistent kernels: smallest per-step exchange first
-  // (fewest batch rows per group), then the most work-groups.
-  const int nb_opts[3] = {16, 32, 64};
+  // Partition of the persistent kernels.  Every work-group reads NB*H
+  // exchanged values per step, so the fewest batch rows per group that still
+  // fit the grid come first, then the most work-groups.  Fewer than 16 rows
+  // leave part of the 16-row MFMA batch tile empty, which costs little next
+  // to the exchange.
+  const int nb_opts[5] = {4, 8, 16, 32, 64};
   const int nj_opts[2] = {8, 16};
   bool found = false;
-  for (int a = 0; a < 3 && !found; ++a) {
+  for (int a = 0; a < 5 && !found; ++a) {
     for (int c = 0; c < 2 && !found; ++c) {
       const int NB = nb_opts[a], NJ = nj_opts[c];
       const int64_t nBG = B > 0 ? (B + NB - 1) / NB : 1;
       const int64_t nJG = (H + NJ - 1) / NJ;
       if (nBG * nJG > cus) continue;
       const int KS = 4 / (NJ / 4);
-      if (p->Hp / KB / KS > 32) continue;                 // forward W_h fragments per wave
-      const int nkbr = 4 * NJ * e / 64;
-      if ((p->Hp / 16 + 3) / 4 > 32 / nkbr) continue;     // backward W_h^T fragments per wave
-      if (NB * NJ > 1024) continue;
-      const size_t lds_f = (size_t)NB * (p->Hp * e + 16) + 16384;
+      const int nkbw = Hp / (KS * KB);                    // forward W_h fragments per wave
+      if (nkbw < 2 || nkbw > 32) continue;
+      const int nkbr = 4 * NJ * e / 64, mtw = Hp / 64;    // backward W_h^T fragments per wave
+      if (mtw * nkbr > 32) continue;
+      const int NBr = NB < 16 ? 16 : NB;
+      const size_t lds_f = (size_t)NBr * (Hp * e + 16) + (size_t)4096 * (NBr / 16);
       if (lds_f > 160 * 1024) continue;
       p->NB = NB; p->NJ = NJ; p->nBG = (int)nBG; p->nJG = (int)nJG; p->grid = (int)(nBG * nJG);
+      p->fwd_nkbw = nkbw;
+      p->bwd_mtw = mtw;
       p->lds_fwd = lds_f;
-      p->lds_bwd = (size_t)NB * (4 * NJ * e + 16);
+      p->lds_bwd = (size_t)NBr * (4 * NJ * e + 16) + 4096;
       found = true;
     }
   }
   if (!found) return LSTM_ERR_UNSUPPORTED;
   p->Bp = p->nBG * p->NB;
+  {
+    const int64_t fw = (int64_t)p->NB * (dtype ? Hp / 2 : Hp);         // forward words per work-group
+    const int64_t bw = (int64_t)p->nJG * p->NB * p->NJ;                // backward words per work-group
+    const int64_t mx = fw > bw ? fw : bw;
+    p->words_per_thread = (int)((mx + 255) / 256);
+  }
 
   // split-K of dW: enough work-groups to fill the chip, >= 8 k-tiles each
   const int64_t kstage = 128 / e;
@@ -112,6 +127,9 @@ static bool g_timing_on = false;
 static std::vector<Pending> g_pending;
 static std::vector<hipEvent_t> g_pool;
 static double g_total_ms[kKinds];
+static uint64_t* g_stamps_fwd = nullptr;
+static uint64_t* g_stamps_bwd = nullptr;
+static size_t g_stamps_bytes = 0;
 static int64_t g_launches[kKinds];
 
 static hipEvent_t take_event() {
@@ -147,6 +165,11 @@ struct Timed {
     }
   }
 };
+
+// the stamp buffer holds [2 passes][kStampWGs][T][kPhases] clock values
+static bool stamps_fit(const Plan& p) {
+  return g_stamps_fwd && (size_t)2 * kStampWGs * p.T * kPhases * sizeof(uint64_t) <= g_stamps_bytes;
+}
 
 static void flush_timing() {
   for (const Pending& p : g_pending) {
@@ -237,7 +260,8 @@ int lstm_fwd_train(const lstm_shape* shape, const void* x, const void* W, const 
   if (err == hipSuccess) {
     Timed tm(1, s);
     err = launch_fwd_recurrent(p, P, W, h0, c0, y, hT, cT, ws + p.off_G, (float*)(ws + p.off_C),
-                               (uint64_t*)(ws + p.off_HX), (uint32_t*)(ws + p.off_ctrl), s);
+                               (uint64_t*)(ws + p.off_HX), (uint32_t*)(ws + p.off_ctrl),
+                               stamps_fit(p) ? g_stamps_fwd : nullptr, s);
   }
   return status_of(err);
 }
@@ -281,7 +305,8 @@ int lstm_bwd(const lstm_shape* shape, const void* dy, const void* dhT, const voi
   if (err == hipSuccess) {
     Timed tm(2, s);
     err = launch_bwd_recurrent(p, W, c0, dy, dhT, dcT, ws + p.off_G, (const float*)(ws + p.off_C), dG,
-                               (uint64_t*)(ws + p.off_PX), dh0, dc0, (uint32_t*)(ws + p.off_ctrl), s);
+                               (uint64_t*)(ws + p.off_PX), dh0, dc0, (uint32_t*)(ws + p.off_ctrl),
+                               stamps_fit(p) ? g_stamps_bwd : nullptr, s);
   }
   if (err == hipSuccess) {
     Timed tm(3, s);
@@ -321,6 +346,22 @@ int lstm_timing_enable(int on) {
       g_total_ms[k] = 0.0;
       g_launches[k] = 0;
     }
+  return LSTM_OK;
+}
+
+int lstm_stamps_set(void* device_buffer, size_t bytes, int64_t T) {
+  if (!device_buffer || bytes == 0) {
+    g_stamps_fwd = g_stamps_bwd = nullptr;
+    g_stamps_bytes = 0;
+    return LSTM_OK;
+  }
+  if (T <= 0) return LSTM_ERR_DIMS;
+  if ((uintptr_t)device_buffer & 7u) return LSTM_ERR_ALIGN;
+  const size_t half = (size_t)kStampWGs * T * kPhases * sizeof(uint64_t);
+  if (bytes < 2 * half) return LSTM_ERR_WORKSPACE;
+  g_stamps_fwd = (uint64_t*)device_buffer;
+  g_stamps_bwd = (uint64_t*)((char*)device_buffer + half);
+  g_stamps_bytes = bytes;
   return LSTM_OK;
 }
 

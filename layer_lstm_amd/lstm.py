@@ -29,7 +29,8 @@ STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_DIMS", -3: "ERR_DTYPE", -4: "ERR_ALI
           -5: "ERR_WORKSPACE", -6: "ERR_UNSUPPORTED", -7: "ERR_COOP", -8: "ERR_LAUNCH",
           -9: "ERR_TIMEOUT", -10: "ERR_DEVICE"}
 EXPORTS = ("lstm_abi_version", "lstm_status_string", "lstm_query", "lstm_fwd_train", "lstm_bwd",
-           "lstm_check_workspace", "lstm_timing_enable", "lstm_timing_read")
+           "lstm_check_workspace", "lstm_timing_enable", "lstm_timing_read", "lstm_stamps_set")
+STAMP_WGS, STAMP_POINTS = 8, 5
 KERNEL_KINDS = ("input_projection", "forward_recurrence", "backward_recurrence", "dW_product",
                 "dx_product", "db_colsum", "clear_copy")
 
@@ -55,6 +56,8 @@ _lib.lstm_timing_enable.restype = ctypes.c_int
 _lib.lstm_timing_enable.argtypes = [ctypes.c_int]
 _lib.lstm_timing_read.restype = ctypes.c_int
 _lib.lstm_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+_lib.lstm_stamps_set.restype = ctypes.c_int
+_lib.lstm_stamps_set.argtypes = [_P, ctypes.c_size_t, ctypes.c_int64]
 
 
 class LstmError(RuntimeError):
@@ -149,6 +152,17 @@ def timing_read() -> dict:
             raise LstmError(rc, "lstm_timing_read")
         out[name] = (ms.value, n.value)
     return out
+
+
+def stamps_set(buf, T) -> None:
+    """Point the recurrent kernels' phase stamps at a device tensor of at
+    least 2*8*T*5 int64 values (None disables)."""
+    if buf is None:
+        _lib.lstm_stamps_set(None, 0, 0)
+        return
+    rc = _lib.lstm_stamps_set(_ptr(buf), buf.numel() * buf.element_size(), int(T))
+    if rc != OK:
+        raise LstmError(rc, "lstm_stamps_set")
 
 
 class Lstm:
