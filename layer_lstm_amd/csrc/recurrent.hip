@@ -128,6 +128,44 @@ __device__ __forceinline__ void complete_tagged(uint64_t (&wv)[C], const uint64_
   }
 }
 
+// Forward round plan: word idx = base + c*256 + tid of the group's rows
+// (idx = row * HW + word, HW a power of two); a word is wanted if it lies
+// in [0, total) and carries data (word < HWv).  Unwanted slots point at
+// `doff`, a word of the group, so that no two slots of a wave hit one line.
+template <int C>
+__device__ __forceinline__ uint32_t plan_h_round(uint32_t (&off)[C], int base, int tid, int total, int hw_mask,
+                                                 int hwv, uint32_t doff) {
+  uint32_t live = 0;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int idx = base + c * 256 + tid;
+    const bool lv = idx < total && (idx & hw_mask) < hwv;
+    off[c] = lv ? (uint32_t)idx : doff;
+    live |= (lv ? 1u : 0u) << c;
+  }
+  return live;
+}
+
+// Backward round plan: word idx = jg' * nel + e, e = jj * NB + bl; the word
+// is partial[jg'][unit j0 + jj][row b0 + bl] of the exchange layout
+// [nJG][Hp][Bp].
+template <int C>
+__device__ __forceinline__ uint32_t plan_dh_round(uint32_t (&off)[C], int base, int tid, int gtotal, int nel, int lg_nel,
+                                                  int NB, int lg_nb, int j0, int b0, int B, int H, int Hp, int Bp,
+                                                  uint32_t doff) {
+  uint32_t live = 0;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int idx = base + c * 256 + tid;
+    const int e = idx & (nel - 1), g2 = idx >> lg_nel;
+    const int bl = e & (NB - 1), uu = j0 + (e >> lg_nb);
+    const bool lv = idx < gtotal && b0 + bl < B && uu < H;
+    off[c] = lv ? (uint32_t)(((uint32_t)g2 * (uint32_t)Hp + (uint32_t)uu) * (uint32_t)Bp + (uint32_t)(b0 + bl)) : doff;
+    live |= (lv ? 1u : 0u) << c;
+  }
+  return live;
+}
+
 template <typename T>
 __device__ __forceinline__ float ldf(const void* p, int64_t i) {
   return Elem<T>::to_f(((const T*)p)[i]);
@@ -196,18 +234,8 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_rec_kernel(FwdArgs a) {
     uint32_t off[C];
     uint32_t live = 0;
     uint64_t wv[C];
-    auto plan_round = [&](int base) {
-      live = 0;
-#pragma unroll
-      for (int c = 0; c < C; ++c) {
-        const int idx = base + c * kRecThreads + tid;
-        const bool lv = idx < total && (idx & (a.HW - 1)) < HWv;
-        off[c] = lv ? (uint32_t)idx : doff;
-        live |= (lv ? 1u : 0u) << c;
-      }
-    };
     if (t > 0) {
-      plan_round(0);
+      live = plan_h_round<C>(off, 0, tid, total, a.HW - 1, HWv, doff);
       issue_tagged<C>(wv, src, off);
     }
     // prefetch the input projection of this lane's elements (after the
@@ -241,7 +269,7 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_rec_kernel(FwdArgs a) {
         }
         base += kRecThreads * C;
         if (base >= total) break;
-        plan_round(base);
+        live = plan_h_round<C>(off, base, tid, total, a.HW - 1, HWv, doff);
         issue_tagged<C>(wv, src, off);
       }
     }
@@ -400,20 +428,8 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
     uint32_t off[C];
     uint32_t live = 0;
     uint64_t wv[C];
-    auto plan_round = [&](int base) {
-      live = 0;
-#pragma unroll
-      for (int c = 0; c < C; ++c) {
-        const int idx = base + c * kRecThreads + tid;
-        const int e = idx & (nel - 1), g2 = idx >> lgNel;
-        const int bl = e & (a.NB - 1), uu = j0 + (e >> lgNB);
-        const bool lv = idx < gtotal && b0 + bl < a.B && uu < a.H;
-        off[c] = lv ? (uint32_t)(((int64_t)g2 * a.Hp + uu) * a.Bp + b0 + bl) : doff;
-        live |= (lv ? 1u : 0u) << c;
-      }
-    };
     if (gather) {
-      plan_round(0);
+      live = plan_dh_round<C>(off, 0, tid, gtotal, nel, lgNel, a.NB, lgNB, j0, b0, a.B, a.H, a.Hp, a.Bp, doff);
       issue_tagged<C>(wv, src, off);
     }
     // prefetch this step's elementwise operands (after the exchange loads)
@@ -455,7 +471,7 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
         }
         base += kRecThreads * C;
         if (base >= gtotal) break;
-        plan_round(base);
+        live = plan_dh_round<C>(off, base, tid, gtotal, nel, lgNel, a.NB, lgNB, j0, b0, a.B, a.H, a.Hp, a.Bp, doff);
         issue_tagged<C>(wv, src, off);
       }
       // sums[s][tid] holds this thread's part of element tid + 256*s (EPT > 1),
@@ -579,7 +595,7 @@ static hipError_t fwd_dispatch_c(const Plan& p, FwdArgs& a, hipStream_t s) {
 template <typename T, int NBT>
 static hipError_t fwd_dispatch(const Plan& p, FwdArgs& a, hipStream_t s) {
   if (p.words_per_thread <= 4) return fwd_dispatch_c<T, NBT, 4>(p, a, s);
-  return fwd_dispatch_c<T, NBT, 32>(p, a, s);
+  return fwd_dispatch_c<T, NBT, 16>(p, a, s);
 }
 
 hipError_t launch_fwd_recurrent(const Plan& p, const float* P, const void* W, const void* h0, const void* c0,
@@ -622,7 +638,7 @@ static hipError_t bwd_dispatch_c(const Plan& p, BwdArgs& a, hipStream_t s) {
 template <typename T, int NKBR>
 static hipError_t bwd_dispatch(const Plan& p, BwdArgs& a, hipStream_t s) {
   if (p.words_per_thread <= 4) return bwd_dispatch_c<T, NKBR, 4>(p, a, s);
-  return bwd_dispatch_c<T, NKBR, 32>(p, a, s);
+  return bwd_dispatch_c<T, NKBR, 16>(p, a, s);
 }
 
 hipError_t launch_bwd_recurrent(const Plan& p, const void* W, const void* c0, const void* dy, const void* dhT,
