@@ -127,7 +127,11 @@ int lstm_bwd(const lstm_shape* shape, const void* dy, const void* dhT, const voi
 
 /* Waits for `stream`, then reports (and clears) a time-out that a
  * recurrent kernel recorded in `workspace`: LSTM_ERR_TIMEOUT, else LSTM_OK
- * (or LSTM_ERR_LAUNCH if the stream itself reports an error). */
+ * (or LSTM_ERR_LAUNCH if the stream itself reports an error).  The time-out
+ * mark is set by the kernels themselves (a per-step wait that exceeded its
+ * bound); it stays set, and the outputs of later calls on the workspace are
+ * undefined, until lstm_fwd_train() runs again on it.  After any error,
+ * run lstm_fwd_train() before the next lstm_bwd() on the same workspace. */
 int lstm_check_workspace(void* workspace, size_t workspace_bytes, void* stream);
 
 /* Per-kernel timing, for measurement.  While enabled (on != 0), every

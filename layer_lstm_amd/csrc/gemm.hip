@@ -12,8 +12,10 @@
 // n = 4j + g of P / dG is gate g of hidden unit j (row gH + j of W), so that
 // the recurrent kernels find the four gates of one unit next to each other.
 //
-// Tiles: 128 x 128 per 256-thread work-group (4 waves, 2 x 2, 64 x 64 each),
-// 128 bytes of k per stage (32 fp32 or 64 bf16), double-buffered in LDS.
+// Tiles: 128 x 128 (or 64 x 64 when 128-wide tiles would leave compute units
+// idle) per 256-thread work-group, 4 waves in 2 x 2, 128 bytes of k per
+// stage (32 fp32 or 64 bf16), double-buffered in LDS; K is split when even
+// the smaller tiles cannot give every compute unit a tile.
 // Both operands sit in LDS as [row][k] with a 16-byte row pad; an operand
 // whose contiguous dimension is M or N is transposed in registers on its way
 // into LDS.  Accumulation is fp32 (v_mfma_f32_16x16x4f32 for fp32 storage,
@@ -24,10 +26,11 @@
 
 namespace lstm {
 
-constexpr int kBM = 128, kBN = 128, kThreads = 256;
+constexpr int kThreads = 256;
 constexpr int kRowBytes = 128;            // k bytes per stage and row
 constexpr int kLdsRow = kRowBytes + 16;   // padded LDS row
-constexpr int kTileBytes = kBM * kLdsRow;  // one operand, one stage
+
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
 __device__ __forceinline__ int64_t gate_row(int64_t n, int64_t H) { return (n & 3) * H + (n >> 2); }
 
@@ -113,19 +116,20 @@ __device__ __forceinline__ u32x4_t load_mn_vec(const Op& op, int64_t k, int64_t 
 }
 
 // ---------------------------------------------------------------------------
-// Stage loaders: fetch one 128 x (128 bytes of k) tile into registers, then
+// Stage loaders: fetch one ROWS x (128 bytes of k) tile into registers, then
 // write it to LDS as [row][k].
-template <typename T, class Op, bool MN>
+template <int ROWS, typename T, class Op, bool MN>
 struct Stager;
 
-// k-contiguous source: 128 rows x 8 vectors = 1024 vectors, 4 per thread
-template <typename T, class Op>
-struct Stager<T, Op, false> {
+// k-contiguous source: ROWS rows x 8 vectors, ROWS/32 per thread
+template <int ROWS, typename T, class Op>
+struct Stager<ROWS, T, Op, false> {
   static constexpr int VEC = 16 / sizeof(T);
-  u32x4_t v[4];
+  static constexpr int NV = ROWS * 8 / kThreads;
+  u32x4_t v[NV];
   __device__ __forceinline__ void fetch(const Op& op, int64_t row0, int64_t k0, int tid) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < NV; ++s) {
       const int id = tid + s * kThreads;
       const int r = id >> 3, kv = id & 7;
       const int64_t gr = row0 + r;
@@ -134,7 +138,7 @@ struct Stager<T, Op, false> {
   }
   __device__ __forceinline__ void store(char* lds, int tid) const {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < NV; ++s) {
       const int id = tid + s * kThreads;
       const int r = id >> 3, kv = id & 7;
       *reinterpret_cast<u32x4_t*>(lds + r * kLdsRow + kv * 16) = v[s];
@@ -142,17 +146,17 @@ struct Stager<T, Op, false> {
   }
 };
 
-// r-contiguous source: blocks of 2 k-rows x (16 bytes of r), 2 per thread;
-// transposed into pairs (k, k+1) per r
-template <typename T, class Op>
-struct Stager<T, Op, true> {
-  static constexpr int VEC = 16 / sizeof(T);        // r per vector
+// r-contiguous source: blocks of 2 k-rows x (16 bytes of r), ROWS/64 per
+// thread; transposed into pairs (k, k+1) per r
+template <int ROWS, typename T, class Op>
+struct Stager<ROWS, T, Op, true> {
+  static constexpr int VEC = 16 / sizeof(T);                // r per vector
   static constexpr int KPAIRS = kRowBytes / sizeof(T) / 2;  // k pairs per stage
-  static constexpr int RVECS = kBM / VEC;           // vectors along r
-  u32x4_t v0[2], v1[2];
+  static constexpr int NB = ROWS * 4 / kThreads;            // blocks per thread
+  u32x4_t v0[NB], v1[NB];
   __device__ __forceinline__ void fetch(const Op& op, int64_t row0, int64_t k0, int tid) {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < NB; ++s) {
       const int id = tid + s * kThreads;
       const int rv = id / KPAIRS, kp = id % KPAIRS;
       const int64_t k = k0 + 2 * kp, r = row0 + rv * VEC;
@@ -162,7 +166,7 @@ struct Stager<T, Op, true> {
   }
   __device__ __forceinline__ void store(char* lds, int tid) const {
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < NB; ++s) {
       const int id = tid + s * kThreads;
       const int rv = id / KPAIRS, kp = id % KPAIRS;
       const T* a = reinterpret_cast<const T*>(&v0[s]);
@@ -181,10 +185,11 @@ struct Stager<T, Op, true> {
 };
 
 // ---------------------------------------------------------------------------
-// Epilogues: called per output element (m < M, n < N).
+// Epilogues: called once per output element (m < M, n < N) with the full
+// dot product (after the split-K sum when the product is split).
 struct EpiP {  // fp32 P with bias in the interleaved column order
   float* P; const void* bias; int64_t H, ldp; int dtype;
-  __device__ __forceinline__ void operator()(int64_t m, int64_t n, int, float v) const {
+  __device__ __forceinline__ void operator()(int64_t m, int64_t n, float v) const {
     if (bias) {
       const int64_t r = gate_row(n, H);
       v += dtype ? bf2f(((const bf16_t*)bias)[r]) : ((const float*)bias)[r];
@@ -195,49 +200,67 @@ struct EpiP {  // fp32 P with bias in the interleaved column order
 template <typename T>
 struct EpiStore {  // plain row-major output of the storage type
   T* out; int64_t ld;
-  __device__ __forceinline__ void operator()(int64_t m, int64_t n, int, float v) const {
+  __device__ __forceinline__ void operator()(int64_t m, int64_t n, float v) const {
     out[m * ld + n] = Elem<T>::from_f(v);
   }
 };
 template <typename T>
-struct EpiDW {  // dW rows in gate-block order, or fp32 split-K partials
-  T* dW; float* part; int64_t H, M, N; int splits;
-  __device__ __forceinline__ void operator()(int64_t m, int64_t n, int split, float v) const {
-    if (splits > 1)
-      part[((int64_t)split * M + m) * N + n] = v;
-    else
-      dW[gate_row(m, H) * N + n] = Elem<T>::from_f(v);
+struct EpiDW {  // dW rows back in gate-block order
+  T* dW; int64_t H, N;
+  __device__ __forceinline__ void operator()(int64_t m, int64_t n, float v) const {
+    dW[gate_row(m, H) * N + n] = Elem<T>::from_f(v);
   }
 };
 
+template <class AOp, class BOp, class Epi>
+struct GemmArgs {
+  int64_t M, N, K;
+  int ktiles_per_split, splits;
+  AOp a;
+  BOp b;
+  Epi epi;
+  float* part;        // [splits][M][N] fp32 partial products when splits > 1
+  uint32_t* zero;     // extra duty: clear `zero_words` words here (may be null)
+  int64_t zero_words;
+};
+
 // ---------------------------------------------------------------------------
-template <typename T, class AOp, bool AMN, class BOp, bool BMN, class Epi>
-__global__ void __launch_bounds__(kThreads)
-gemm_kernel(int64_t M, int64_t N, int64_t K, int ktiles_per_split, AOp aop, BOp bop, Epi epi) {
+// Tile BM x BN = (32*WM) x (32*WN): 4 waves in 2 x 2, each (16*WM) x (16*WN).
+// grid = (N tiles, M tiles, splits [+ 1 slab of clearing blocks]).
+template <typename T, int WM, int WN, class AOp, bool AMN, class BOp, bool BMN, class Epi>
+__global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs<AOp, BOp, Epi> g) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* As = smem;                      // [2][kBM][kLdsRow]
-  char* Bs = smem + 2 * kTileBytes;     // [2][kBN][kLdsRow]
+  constexpr int BM = 32 * WM, BN = 32 * WN;
+  constexpr int ATILE = BM * kLdsRow, BTILE = BN * kLdsRow;
+  char* As = smem;                 // [2][BM][kLdsRow]
+  char* Bs = smem + 2 * ATILE;     // [2][BN][kLdsRow]
   constexpr int KSTAGE = kRowBytes / sizeof(T);  // k elements per stage
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if ((int)blockIdx.z == g.splits) {  // clearing blocks
+    const int64_t nblk = (int64_t)gridDim.x * gridDim.y;
+    const int64_t blk = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    for (int64_t i = blk * kThreads + tid; i < g.zero_words; i += nblk * kThreads) g.zero[i] = 0u;
+    return;
+  }
   const int wm = w >> 1, wn = w & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;
+  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
   const int split = blockIdx.z;
-  const int64_t ktiles = (K + KSTAGE - 1) / KSTAGE;
-  const int64_t kt_begin = (int64_t)split * ktiles_per_split;
-  const int64_t kt_end = kt_begin + ktiles_per_split < ktiles ? kt_begin + ktiles_per_split : ktiles;
+  const int64_t ktiles = (g.K + KSTAGE - 1) / KSTAGE;
+  const int64_t kt_begin = (int64_t)split * g.ktiles_per_split;
+  const int64_t kt_end = kt_begin + g.ktiles_per_split < ktiles ? kt_begin + g.ktiles_per_split : ktiles;
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[WM][WN];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < WN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  Stager<T, AOp, AMN> sa;
-  Stager<T, BOp, BMN> sb;
+  Stager<BM, T, AOp, AMN> sa;
+  Stager<BN, T, BOp, BMN> sb;
   if (kt_begin < kt_end) {
-    sa.fetch(aop, m0, kt_begin * KSTAGE, tid);
-    sb.fetch(bop, n0, kt_begin * KSTAGE, tid);
+    sa.fetch(g.a, m0, kt_begin * KSTAGE, tid);
+    sb.fetch(g.b, n0, kt_begin * KSTAGE, tid);
     sa.store(As, tid);
     sb.store(Bs, tid);
   }
@@ -248,115 +271,175 @@ gemm_kernel(int64_t M, int64_t N, int64_t K, int ktiles_per_split, AOp aop, BOp 
     const int st = (int)((kt - kt_begin) & 1);
     const bool more = kt + 1 < kt_end;
     if (more) {
-      sa.fetch(aop, m0, (kt + 1) * KSTAGE, tid);
-      sb.fetch(bop, n0, (kt + 1) * KSTAGE, tid);
+      sa.fetch(g.a, m0, (kt + 1) * KSTAGE, tid);
+      sb.fetch(g.b, n0, (kt + 1) * KSTAGE, tid);
     }
-    const char* a_st = As + st * kTileBytes + (wm * 64 + fr) * kLdsRow + fq * 16;
-    const char* b_st = Bs + st * kTileBytes + (wn * 64 + fr) * kLdsRow + fq * 16;
+    const char* a_st = As + st * ATILE + (wm * 16 * WM + fr) * kLdsRow + fq * 16;
+    const char* b_st = Bs + st * BTILE + (wn * 16 * WN + fr) * kLdsRow + fq * 16;
 #pragma unroll
     for (int kb = 0; kb < kRowBytes / 64; ++kb) {
-      u32x4_t af[4], bfv[4];
+      u32x4_t af[WM], bfv[WN];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const u32x4_t*>(a_st + i * 16 * kLdsRow + kb * 64);
+      for (int i = 0; i < WM; ++i) af[i] = *reinterpret_cast<const u32x4_t*>(a_st + i * 16 * kLdsRow + kb * 64);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bfv[j] = *reinterpret_cast<const u32x4_t*>(b_st + j * 16 * kLdsRow + kb * 64);
+      for (int j = 0; j < WN; ++j) bfv[j] = *reinterpret_cast<const u32x4_t*>(b_st + j * 16 * kLdsRow + kb * 64);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < WM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = Mfma<T>::mac(af[i], bfv[j], acc[i][j]);
+        for (int j = 0; j < WN; ++j) acc[i][j] = Mfma<T>::mac(af[i], bfv[j], acc[i][j]);
     }
     if (more) {
-      sa.store(As + (st ^ 1) * kTileBytes, tid);
-      sb.store(Bs + (st ^ 1) * kTileBytes, tid);
+      sa.store(As + (st ^ 1) * ATILE, tid);
+      sb.store(Bs + (st ^ 1) * BTILE, tid);
     }
     __syncthreads();
   }
 
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < WM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t n = n0 + wn * 64 + j * 16 + fr;
+    for (int j = 0; j < WN; ++j) {
+      const int64_t n = n0 + wn * 16 * WN + j * 16 + fr;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t m = m0 + wm * 64 + i * 16 + fq * 4 + e;
-        if (m < M && n < N) epi(m, n, split, acc[i][j][e]);
+        const int64_t m = m0 + wm * 16 * WM + i * 16 + fq * 4 + e;
+        if (m < g.M && n < g.N) {
+          if (g.splits > 1)
+            g.part[((int64_t)split * g.M + m) * g.N + n] = acc[i][j][e];
+          else
+            g.epi(m, n, acc[i][j][e]);
+        }
       }
     }
 }
 
-template <typename T, class AOp, bool AMN, class BOp, bool BMN, class Epi>
-static hipError_t run_gemm(int64_t M, int64_t N, int64_t K, int splits, const AOp& a, const BOp& b,
-                           const Epi& e, hipStream_t s) {
-  if (M <= 0 || N <= 0) return hipSuccess;
-  constexpr int KSTAGE = kRowBytes / sizeof(T);
-  const int64_t ktiles = (K + KSTAGE - 1) / KSTAGE;
-  int ktps = (int)((ktiles + splits - 1) / splits);
-  if (ktps < 1) ktps = 1;
-  dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + kBM - 1) / kBM), (unsigned)splits);
-  const size_t lds = 4 * (size_t)kTileBytes;
-  auto fn = gemm_kernel<T, AOp, AMN, BOp, BMN, Epi>;
+// Split-K sum in a fixed order (split 0, 1, ...), then the epilogue.
+template <class Epi>
+__global__ void __launch_bounds__(256) splitk_reduce(const float* part, int64_t M, int64_t N, int splits, Epi epi) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= M * N) return;
+  float acc = 0.f;
+  for (int sp = 0; sp < splits; ++sp) acc += part[(int64_t)sp * M * N + idx];
+  epi(idx / N, idx % N, acc);
+}
+
+// Tile and split choice for a product of M x N outputs with K-depth K on
+// `cus` compute units: 128 x 128 tiles when they already give one per CU,
+// else 64 x 64; then split K (powers of two, >= 4 stages per split) until
+// tiles x splits covers the CUs.
+struct GemmShape { int tile; int splits; };
+static GemmShape choose_shape(int64_t M, int64_t N, int64_t K, int esize, int cus, int max_splits) {
+  const int64_t kstage = kRowBytes / esize;
+  const int64_t ktiles = (K + kstage - 1) / kstage;
+  const int64_t t128 = ((M + 127) / 128) * ((N + 127) / 128);
+  const int64_t t64 = ((M + 63) / 64) * ((N + 63) / 64);
+  GemmShape gs{t128 >= cus ? 128 : 64, 1};
+  const int64_t tiles = gs.tile == 128 ? t128 : t64;
+  while (gs.splits < max_splits && tiles * gs.splits < cus && ktiles / (gs.splits * 2) >= 4) gs.splits *= 2;
+  return gs;
+}
+
+template <typename T, int WM, int WN, class AOp, bool AMN, class BOp, bool BMN, class Epi>
+static hipError_t launch_tile(GemmArgs<AOp, BOp, Epi>& g, hipStream_t s) {
+  constexpr int BM = 32 * WM, BN = 32 * WN;
+  const unsigned gz = (unsigned)g.splits + (g.zero_words > 0 ? 1u : 0u);
+  dim3 grid((unsigned)((g.N + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM), gz);
+  const size_t lds = 2 * (size_t)(BM + BN) * kLdsRow;
+  auto fn = gemm_kernel<T, WM, WN, AOp, AMN, BOp, BMN, Epi>;
   hipError_t err = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(fn, grid, dim3(kThreads), lds, s, M, N, K, ktps, a, b, e);
+  hipLaunchKernelGGL(fn, grid, dim3(kThreads), lds, s, g);
+  return hipGetLastError();
+}
+
+// Runs C = A . B through the epilogue; `part` must hold splits*M*N floats
+// when the shape splits K.  Optionally clears `zero_bytes` at `zero` in the
+// same launch (extra blocks), so that a buffer clear costs no launch.
+template <typename T, class AOp, bool AMN, class BOp, bool BMN, class Epi>
+static hipError_t run_gemm(const Plan& p, int64_t M, int64_t N, int64_t K, const AOp& a, const BOp& b,
+                           const Epi& e, float* part, void* zero, size_t zero_bytes, hipStream_t s) {
+  if (M <= 0 || N <= 0) {
+    if (zero_bytes) return launch_fill_zero(zero, zero_bytes, s);
+    return hipSuccess;
+  }
+  const GemmShape gs = choose_shape(M, N, K, (int)sizeof(T), p.cus, part ? p.max_splits : 1);
+  constexpr int KSTAGE = kRowBytes / sizeof(T);
+  const int64_t ktiles = (K + KSTAGE - 1) / KSTAGE;
+  int ktps = (int)((ktiles + gs.splits - 1) / gs.splits);
+  if (ktps < 1) ktps = 1;
+  GemmArgs<AOp, BOp, Epi> g{M, N, K, ktps, gs.splits, a, b, e, part, (uint32_t*)zero, (int64_t)(zero_bytes / 4)};
+  hipError_t err = gs.tile == 128 ? launch_tile<T, 4, 4, AOp, AMN, BOp, BMN, Epi>(g, s)
+                                  : launch_tile<T, 2, 2, AOp, AMN, BOp, BMN, Epi>(g, s);
+  if (err != hipSuccess || gs.splits == 1) return err;
+  const int64_t n = M * N;
+  hipLaunchKernelGGL(splitk_reduce<Epi>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, M, N, gs.splits, e);
   return hipGetLastError();
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 template <typename T>
-static hipError_t inproj_t(const Plan& p, const void* x, const void* W, const void* b, float* P, hipStream_t s) {
+static hipError_t inproj_t(const Plan& p, const void* x, const void* W, const void* b, float* P, float* part,
+                           void* zero, size_t zero_bytes, hipStream_t s) {
   constexpr int VEC = 16 / sizeof(T);
   KRowsX<T> a{(const T*)x, p.I, p.TB, p.I, aligned16(x) && p.I % VEC == 0};
   KRowsWx<T> bw{(const T*)W, p.H, p.Z, p.G4, p.I, aligned16(W) && p.Z % VEC == 0 && p.H % VEC == 0};
   EpiP e{P, b, p.H, p.G4, p.dtype};
-  return run_gemm<T, KRowsX<T>, false, KRowsWx<T>, false, EpiP>(p.TB, p.G4, p.I, 1, a, bw, e, s);
+  return run_gemm<T, KRowsX<T>, false, KRowsWx<T>, false, EpiP>(p, p.TB, p.G4, p.I, a, bw, e, part, zero, zero_bytes, s);
 }
 
 template <typename T>
-static hipError_t dx_t(const Plan& p, const void* dG, const void* W, void* dx, hipStream_t s) {
+static hipError_t dx_t(const Plan& p, const void* dG, const void* W, void* dx, float* part, void* zero,
+                       size_t zero_bytes, hipStream_t s) {
   constexpr int VEC = 16 / sizeof(T);
   KRowsX<T> a{(const T*)dG, p.G4, p.TB, p.G4, aligned16(dG) && p.G4 % VEC == 0};
   MNRowsWx<T> bw{(const T*)W, p.H, p.Z, p.I, p.G4, aligned16(W) && p.Z % VEC == 0 && p.H % VEC == 0};
   EpiStore<T> e{(T*)dx, p.I};
-  return run_gemm<T, KRowsX<T>, false, MNRowsWx<T>, true, EpiStore<T>>(p.TB, p.I, p.G4, 1, a, bw, e, s);
-}
-
-template <typename T>
-__global__ void __launch_bounds__(256) splitk_reduce(const float* part, T* dW, int64_t M, int64_t N, int64_t H, int splits) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= M * N) return;
-  const int64_t m = idx / N, n = idx % N;
-  float acc = 0.f;
-  for (int sp = 0; sp < splits; ++sp) acc += part[(int64_t)sp * M * N + idx];
-  dW[gate_row(m, H) * N + n] = Elem<T>::from_f(acc);
+  return run_gemm<T, KRowsX<T>, false, MNRowsWx<T>, true, EpiStore<T>>(p, p.TB, p.I, p.G4, a, bw, e, part, zero,
+                                                                       zero_bytes, s);
 }
 
 template <typename T>
 static hipError_t dw_t(const Plan& p, const void* dG, const void* x, const void* h0, const void* y, void* dW,
-                       float* part, hipStream_t s) {
+                       float* part, void* zero, size_t zero_bytes, hipStream_t s) {
   constexpr int VEC = 16 / sizeof(T);
   MNRowsPlain<T> a{(const T*)dG, p.G4, p.G4, p.TB, aligned16(dG) && p.G4 % VEC == 0};
   MNRowsZ<T> bz{(const T*)x, (const T*)h0, (const T*)y, p.B, p.H, p.I, p.Z, p.TB,
                 aligned16(x) && aligned16(y) && (h0 == nullptr || aligned16(h0)) && p.H % VEC == 0 && p.I % VEC == 0};
-  EpiDW<T> e{(T*)dW, part, p.H, p.G4, p.Z, p.dw_splits};
-  hipError_t err = run_gemm<T, MNRowsPlain<T>, true, MNRowsZ<T>, true, EpiDW<T>>(p.G4, p.Z, p.TB, p.dw_splits, a, bz, e, s);
-  if (err != hipSuccess || p.dw_splits <= 1) return err;
-  const int64_t n = p.G4 * p.Z;
-  hipLaunchKernelGGL(splitk_reduce<T>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, (T*)dW, p.G4, p.Z,
-                     p.H, p.dw_splits);
-  return hipGetLastError();
+  EpiDW<T> e{(T*)dW, p.H, p.Z};
+  return run_gemm<T, MNRowsPlain<T>, true, MNRowsZ<T>, true, EpiDW<T>>(p, p.G4, p.Z, p.TB, a, bz, e, part, zero,
+                                                                       zero_bytes, s);
 }
 
-hipError_t launch_gemm_inproj(const Plan& p, const void* x, const void* W, const void* b, float* P, hipStream_t s) {
-  return p.dtype ? inproj_t<bf16_t>(p, x, W, b, P, s) : inproj_t<float>(p, x, W, b, P, s);
+hipError_t launch_gemm_inproj(const Plan& p, const void* x, const void* W, const void* b, float* P, float* part,
+                              void* zero, size_t zero_bytes, hipStream_t s) {
+  return p.dtype ? inproj_t<bf16_t>(p, x, W, b, P, part, zero, zero_bytes, s)
+                 : inproj_t<float>(p, x, W, b, P, part, zero, zero_bytes, s);
 }
-hipError_t launch_gemm_dx(const Plan& p, const void* dG, const void* W, void* dx, hipStream_t s) {
-  return p.dtype ? dx_t<bf16_t>(p, dG, W, dx, s) : dx_t<float>(p, dG, W, dx, s);
+hipError_t launch_gemm_dx(const Plan& p, const void* dG, const void* W, void* dx, float* part, void* zero,
+                          size_t zero_bytes, hipStream_t s) {
+  return p.dtype ? dx_t<bf16_t>(p, dG, W, dx, part, zero, zero_bytes, s)
+                 : dx_t<float>(p, dG, W, dx, part, zero, zero_bytes, s);
 }
 hipError_t launch_gemm_dw(const Plan& p, const void* dG, const void* x, const void* h0, const void* y, void* dW,
-                          float* part, hipStream_t s) {
-  return p.dtype ? dw_t<bf16_t>(p, dG, x, h0, y, dW, part, s) : dw_t<float>(p, dG, x, h0, y, dW, part, s);
+                          float* part, void* zero, size_t zero_bytes, hipStream_t s) {
+  return p.dtype ? dw_t<bf16_t>(p, dG, x, h0, y, dW, part, zero, zero_bytes, s)
+                 : dw_t<float>(p, dG, x, h0, y, dW, part, zero, zero_bytes, s);
+}
+
+// Bytes of fp32 split-K partials the three products need for this plan.
+size_t gemm_partial_bytes(const Plan& p, int cus) {
+  size_t mx = 0;
+  const int64_t shapes[3][3] = {{p.TB, p.G4, p.I}, {p.TB, p.I, p.G4}, {p.G4, p.Z, p.TB}};
+  for (const auto& sh : shapes) {
+    if (sh[0] <= 0 || sh[1] <= 0) continue;
+    const GemmShape gs = choose_shape(sh[0], sh[1], sh[2], p.esize, cus, p.max_splits);
+    if (gs.splits > 1) {
+      const size_t b = (size_t)gs.splits * sh[0] * sh[1] * 4;
+      if (b > mx) mx = b;
+    }
+  }
+  return mx;
 }
 
 // ---------------------------------------------------------------------------

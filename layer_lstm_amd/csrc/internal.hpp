@@ -33,9 +33,11 @@ struct Plan {
   size_t lds_fwd, lds_bwd;
 
   // workspace (byte offsets, 256-aligned)
-  size_t off_ctrl, off_P, off_G, off_C, off_HX, off_PX, off_dWp, off_col, total;
+  size_t off_ctrl, off_P, off_G, off_C, off_HX, off_PX, off_col, total;
   size_t bytes_HX, bytes_PX;
-  int dw_splits;    // split-K factor of the dW product
+  int cus;          // compute units of the device
+  int max_splits;   // largest split-K factor of the three products
+  size_t off_gp;    // fp32 split-K partials of the products
   int col_chunks;   // row chunks of the db column sum
 };
 
@@ -46,14 +48,18 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p);
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 hipError_t launch_copy_state(const void* src, void* dst, size_t n, int esize, hipStream_t s);
 
+// The three products.  `part` holds the fp32 split-K partials (null = do not
+// split); the launch also clears `zero_bytes` at `zero` (may be 0).
 // P[tb][4j+g] = sum_k x[tb][k] W[gH+j][H+k] + b[gH+j]   (fp32 out)
-hipError_t launch_gemm_inproj(const Plan& p, const void* x, const void* W, const void* b,
-                              float* P, hipStream_t s);
+hipError_t launch_gemm_inproj(const Plan& p, const void* x, const void* W, const void* b, float* P, float* part,
+                              void* zero, size_t zero_bytes, hipStream_t s);
 // dx[tb][i] = sum_n dG[tb][n] W[row(n)][H+i]
-hipError_t launch_gemm_dx(const Plan& p, const void* dG, const void* W, void* dx, hipStream_t s);
+hipError_t launch_gemm_dx(const Plan& p, const void* dG, const void* W, void* dx, float* part, void* zero,
+                          size_t zero_bytes, hipStream_t s);
 // dW[row(m)][n] = sum_tb dG[tb][m] Z[tb][n],  Z = [h_{t-1} | x_t]
-hipError_t launch_gemm_dw(const Plan& p, const void* dG, const void* x, const void* h0,
-                          const void* y, void* dW, float* part, hipStream_t s);
+hipError_t launch_gemm_dw(const Plan& p, const void* dG, const void* x, const void* h0, const void* y, void* dW,
+                          float* part, void* zero, size_t zero_bytes, hipStream_t s);
+size_t gemm_partial_bytes(const Plan& p, int cus);
 // db[row(n)] = sum_tb dG[tb][n]
 hipError_t launch_colsum_db(const Plan& p, const void* dG, void* db, float* part, hipStream_t s);
 

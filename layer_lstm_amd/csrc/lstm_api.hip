@@ -88,13 +88,8 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
     p->words_per_thread = (int)((mx + 255) / 256);
   }
 
-  // split-K of dW: enough work-groups to fill the chip, >= 8 k-tiles each
-  const int64_t kstage = 128 / e;
-  const int64_t tiles = ((p->G4 + 127) / 128) * ((p->Z + 127) / 128);
-  const int64_t ktiles = (p->TB + kstage - 1) / kstage;
-  int splits = 1;
-  while (splits < 16 && tiles * splits < cus && ktiles / (splits * 2) >= 8) splits *= 2;
-  p->dw_splits = splits;
+  p->cus = cus;
+  p->max_splits = 8;
   int64_t chunks = p->TB / 128;
   p->col_chunks = (int)(chunks < 1 ? 1 : (chunks > 64 ? 64 : chunks));
 
@@ -106,7 +101,7 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
   p->off_P = off; off += align256((size_t)p->TB * p->G4 * 4);
   p->off_G = off; off += align256((size_t)p->TB * p->G4 * e);
   p->off_C = off; off += align256((size_t)p->TB * H * 4);
-  p->off_dWp = off; off += splits > 1 ? align256((size_t)splits * p->G4 * p->Z * 4) : 0;
+  p->off_gp = off; off += align256(gemm_partial_bytes(*p, cus));
   p->off_col = off; off += align256((size_t)p->col_chunks * p->G4 * 4);
   p->total = off;
   return LSTM_OK;
@@ -247,15 +242,13 @@ int lstm_fwd_train(const lstm_shape* shape, const void* x, const void* W, const 
     if (err == hipSuccess) err = launch_copy_state(c0, cT, (size_t)(p.B * p.H), e, s);
     return status_of(err);
   }
-  // control word + step-exchange buffers start cleared (tags 0)
-  {
-    Timed tm(6, s);
-    err = launch_fill_zero(ws + p.off_ctrl, p.off_HX + p.bytes_HX - p.off_ctrl, s);
-  }
+  // the input projection's launch also clears the error word and both
+  // step-exchange buffers (tags 0) for the recurrences that follow
   float* P = (float*)(ws + p.off_P);
-  if (err == hipSuccess) {
+  {
     Timed tm(0, s);
-    err = launch_gemm_inproj(p, x, W, b, P, s);
+    err = launch_gemm_inproj(p, x, W, b, P, (float*)(ws + p.off_gp), ws + p.off_ctrl,
+                             p.off_PX + p.bytes_PX - p.off_ctrl, s);
   }
   if (err == hipSuccess) {
     Timed tm(1, s);
@@ -296,13 +289,11 @@ int lstm_bwd(const lstm_shape* shape, const void* dy, const void* dhT, const voi
     if (err == hipSuccess && p.B > 0) err = launch_copy_state(dcT, dc0, (size_t)(p.B * p.H), e, s);
     return status_of(err);
   }
-  // control word + exchange buffers start cleared
-  {
-    Timed tm(6, s);
-    err = launch_fill_zero(ws + p.off_ctrl, p.off_PX + p.bytes_PX - p.off_ctrl, s);
-  }
+  // The backward exchange buffer starts cleared: the forward clears it, and
+  // every backward clears it again once its recurrence is done (in the dW
+  // launch), so that a repeated backward finds it clean too.
   void* dG = ws + p.off_P;  // the input projection is dead after the forward
-  if (err == hipSuccess) {
+  {
     Timed tm(2, s);
     err = launch_bwd_recurrent(p, W, c0, dy, dhT, dcT, ws + p.off_G, (const float*)(ws + p.off_C), dG,
                                (uint64_t*)(ws + p.off_PX), dh0, dc0, (uint32_t*)(ws + p.off_ctrl),
@@ -310,11 +301,11 @@ int lstm_bwd(const lstm_shape* shape, const void* dy, const void* dhT, const voi
   }
   if (err == hipSuccess) {
     Timed tm(3, s);
-    err = launch_gemm_dw(p, dG, x, h0, y, dW, (float*)(ws + p.off_dWp), s);
+    err = launch_gemm_dw(p, dG, x, h0, y, dW, (float*)(ws + p.off_gp), ws + p.off_PX, p.bytes_PX, s);
   }
   if (err == hipSuccess && p.I > 0) {
     Timed tm(4, s);
-    err = launch_gemm_dx(p, dG, W, dx, s);
+    err = launch_gemm_dx(p, dG, W, dx, (float*)(ws + p.off_gp), nullptr, 0, s);
   }
   if (err == hipSuccess && db) {
     Timed tm(5, s);
