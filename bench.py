@@ -32,8 +32,7 @@ HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "input_projection": "gemm.hip", "dW_product": "gemm.hip", "dx_product": "gemm.hip",
-    "db_colsum": "gemm.hip", "forward_recurrence": "recurrent.hip",
-    "backward_recurrence": "recurrent.hip", "clear_copy": "gemm.hip",
+    "forward_recurrence": "recurrent.hip", "backward_recurrence": "recurrent.hip", "state_copy": "gemm.hip",
 }
 
 
@@ -54,8 +53,6 @@ def kernel_work(w, kind):
         return 2.0 * TB * 4 * H * (H + I), "flop", "mfma"
     if kind == "dx_product":
         return 2.0 * TB * 4 * H * I, "flop", "mfma"
-    if kind == "db_colsum":
-        return float(TB * 4 * H * e + 4 * H * e), "byte", "hbm"
     return 0.0, "byte", "hbm"
 
 
@@ -176,7 +173,7 @@ def main():
         if n:
             log(f"  {k:22s} {tot / n * 1e3:10.1f} us/launch  x{n // args.steps}/step")
 
-    kinds = [k for k in kt if kt[k][1] > 0 and k != "clear_copy"]
+    kinds = [k for k in kt if kt[k][1] > 0 and k != "state_copy"]
     dom = max(kinds, key=lambda k: kt[k][0])
     tot, n = kt[dom]
     avg_s = tot / n / 1e3

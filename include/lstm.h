@@ -138,8 +138,8 @@ int lstm_check_workspace(void* workspace, size_t workspace_bytes, void* stream);
  * kernel the library launches is bracketed by HIP events recorded on the
  * call's stream, and the elapsed time is added to the total of its kind:
  *   0 input projection   1 forward recurrence   2 backward recurrence
- *   3 dW product (with its split-K sum)   4 dx product   5 db column sum
- *   6 buffer clears and state copies
+ *   3 dW product (with its split-K sum and the final db sum)   4 dx product
+ *   5 (not used)   6 state copies of the T = 0 / B = 0 cases
  * lstm_timing_enable(1) also resets the totals.  lstm_timing_read() waits for
  * the recorded events and returns the total milliseconds and the launch
  * count of one kind.  Not thread-safe; timing adds a few microseconds per
@@ -148,14 +148,15 @@ int lstm_timing_enable(int on);
 int lstm_timing_read(int kind, double* total_ms, int64_t* launches);
 
 /* Step-phase stamps of the recurrent kernels, for measurement.  With a
- * device buffer of at least 2*8*T*5 uint64 values set, each later call whose
+ * device buffer of at least 2*8*T*6 uint64 values set, each later call whose
  * sequence length is at most T makes thread 0 of work-groups 0..7 write the
- * 100 MHz real-time clock (s_memrealtime) at five points of every step: forward -- step
- * start, its h_{t-1} words read, all threads past the wait, product done,
- * outputs written; backward -- step start, dh carry gathered, deltas
- * written, partial products sent, step end.  Layout: [pass (0 forward,
- * 1 backward)][work-group][step in execution order][point].  NULL disables.
- * Returns LSTM_ERR_WORKSPACE if the buffer is too small for T. */
+ * 100 MHz real-time clock (s_memrealtime) at six points of every step:
+ * forward -- step start, its h_{t-1} words read, all threads past the wait,
+ * own product done, cross-wave sum done, outputs written; backward -- step
+ * start, dh carry gathered, deltas written, partial products sent, next
+ * operands requested, step end.  Layout: [pass (0 forward, 1 backward)]
+ * [work-group][step in execution order][point].  NULL disables.  Returns
+ * LSTM_ERR_WORKSPACE if the buffer is too small for T. */
 int lstm_stamps_set(void* device_buffer, size_t bytes, int64_t T);
 
 #ifdef __cplusplus

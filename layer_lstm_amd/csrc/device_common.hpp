@@ -36,10 +36,15 @@ template <> struct Elem<bf16_t> {
   __device__ __forceinline__ static bf16_t from_f(float v) { return f2bf(v); }
 };
 
-// Logistic sigmoid 1/(1+e^-u) and tanh, from the device math library in
-// full fp32 precision.  Saturate to 0/1/+-1 for large |u|, never NaN.
-__device__ __forceinline__ float sigmoidf(float u) { return 1.0f / (1.0f + expf(-u)); }
-__device__ __forceinline__ float tanh_f(float u) { return tanhf(u); }
+// Logistic sigmoid s(u) = 1/(1+e^-u) from its definition on the hardware
+// base-2 exponential and reciprocal (v_exp_f32, v_rcp_f32; about 1 ulp
+// each): e^-u = 2^(-u*log2(e)).  For u -> -inf, 2^(..) -> +inf and the
+// reciprocal gives 0; for u -> +inf it gives 1; never NaN for finite u.
+// tanh(u) = 2 s(2u) - 1 (absolute error about 1e-7, saturates to +-1).
+__device__ __forceinline__ float sigmoidf(float u) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(u * -1.4426950408889634f));
+}
+__device__ __forceinline__ float tanh_f(float u) { return 2.0f * sigmoidf(2.0f * u) - 1.0f; }
 
 // One MFMA k-block: 16 bytes per lane of each operand.
 //  fp32: 4 k-values per lane -> four v_mfma_f32_16x16x4f32 (k-slot s of the

@@ -222,6 +222,11 @@ struct GemmArgs {
   float* part;        // [splits][M][N] fp32 partial products when splits > 1
   uint32_t* zero;     // extra duty: clear `zero_words` words here (may be null)
   int64_t zero_words;
+  const float* dsum;  // extra duty: dsum_out[row(n)] = sum_r dsum[r][n] (r < dsum_rows)
+  void* dsum_out;     // (null = none); row(n) = gate-block order, storage type dsum_bf16
+  int dsum_rows;
+  int dsum_bf16;
+  int64_t dsum_cols, dsum_H;
 };
 
 // ---------------------------------------------------------------------------
@@ -237,10 +242,19 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs<AOp, BOp, Epi> 
   constexpr int KSTAGE = kRowBytes / sizeof(T);  // k elements per stage
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if ((int)blockIdx.z == g.splits) {  // clearing blocks
+  if ((int)blockIdx.z == g.splits) {  // extra duties: clearing, db sum
     const int64_t nblk = (int64_t)gridDim.x * gridDim.y;
     const int64_t blk = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
     for (int64_t i = blk * kThreads + tid; i < g.zero_words; i += nblk * kThreads) g.zero[i] = 0u;
+    if (g.dsum_out) {
+      for (int64_t n = blk * kThreads + tid; n < g.dsum_cols; n += nblk * kThreads) {
+        float v = 0.f;
+        for (int r = 0; r < g.dsum_rows; ++r) v += g.dsum[(int64_t)r * g.dsum_cols + n];
+        const int64_t row = gate_row(n, g.dsum_H);
+        if (g.dsum_bf16) ((bf16_t*)g.dsum_out)[row] = f2bf(v);
+        else ((float*)g.dsum_out)[row] = v;
+      }
+    }
     return;
   }
   const int wm = w >> 1, wn = w & 1;
@@ -342,7 +356,7 @@ static GemmShape choose_shape(int64_t M, int64_t N, int64_t K, int esize, int cu
 template <typename T, int WM, int WN, class AOp, bool AMN, class BOp, bool BMN, class Epi>
 static hipError_t launch_tile(GemmArgs<AOp, BOp, Epi>& g, hipStream_t s) {
   constexpr int BM = 32 * WM, BN = 32 * WN;
-  const unsigned gz = (unsigned)g.splits + (g.zero_words > 0 ? 1u : 0u);
+  const unsigned gz = (unsigned)g.splits + ((g.zero_words > 0 || g.dsum_out) ? 1u : 0u);
   dim3 grid((unsigned)((g.N + BN - 1) / BN), (unsigned)((g.M + BM - 1) / BM), gz);
   const size_t lds = 2 * (size_t)(BM + BN) * kLdsRow;
   auto fn = gemm_kernel<T, WM, WN, AOp, AMN, BOp, BMN, Epi>;
@@ -355,9 +369,12 @@ static hipError_t launch_tile(GemmArgs<AOp, BOp, Epi>& g, hipStream_t s) {
 // Runs C = A . B through the epilogue; `part` must hold splits*M*N floats
 // when the shape splits K.  Optionally clears `zero_bytes` at `zero` in the
 // same launch (extra blocks), so that a buffer clear costs no launch.
+struct DbDuty { const float* src; void* out; int rows; int64_t cols, H; int bf16; };
+
 template <typename T, class AOp, bool AMN, class BOp, bool BMN, class Epi>
 static hipError_t run_gemm(const Plan& p, int64_t M, int64_t N, int64_t K, const AOp& a, const BOp& b,
-                           const Epi& e, float* part, void* zero, size_t zero_bytes, hipStream_t s) {
+                           const Epi& e, float* part, void* zero, size_t zero_bytes, hipStream_t s,
+                           DbDuty db = DbDuty{nullptr, nullptr, 0, 0, 0, 0}) {
   if (M <= 0 || N <= 0) {
     if (zero_bytes) return launch_fill_zero(zero, zero_bytes, s);
     return hipSuccess;
@@ -367,7 +384,8 @@ static hipError_t run_gemm(const Plan& p, int64_t M, int64_t N, int64_t K, const
   const int64_t ktiles = (K + KSTAGE - 1) / KSTAGE;
   int ktps = (int)((ktiles + gs.splits - 1) / gs.splits);
   if (ktps < 1) ktps = 1;
-  GemmArgs<AOp, BOp, Epi> g{M, N, K, ktps, gs.splits, a, b, e, part, (uint32_t*)zero, (int64_t)(zero_bytes / 4)};
+  GemmArgs<AOp, BOp, Epi> g{M, N, K, ktps, gs.splits, a, b, e, part, (uint32_t*)zero, (int64_t)(zero_bytes / 4),
+                            db.src, db.out, db.rows, db.bf16, db.cols, db.H};
   hipError_t err = gs.tile == 128 ? launch_tile<T, 4, 4, AOp, AMN, BOp, BMN, Epi>(g, s)
                                   : launch_tile<T, 2, 2, AOp, AMN, BOp, BMN, Epi>(g, s);
   if (err != hipSuccess || gs.splits == 1) return err;
@@ -401,14 +419,15 @@ static hipError_t dx_t(const Plan& p, const void* dG, const void* W, void* dx, f
 
 template <typename T>
 static hipError_t dw_t(const Plan& p, const void* dG, const void* x, const void* h0, const void* y, void* dW,
-                       float* part, void* zero, size_t zero_bytes, hipStream_t s) {
+                       float* part, void* zero, size_t zero_bytes, const float* DBP, void* db, hipStream_t s) {
   constexpr int VEC = 16 / sizeof(T);
   MNRowsPlain<T> a{(const T*)dG, p.G4, p.G4, p.TB, aligned16(dG) && p.G4 % VEC == 0};
   MNRowsZ<T> bz{(const T*)x, (const T*)h0, (const T*)y, p.B, p.H, p.I, p.Z, p.TB,
                 aligned16(x) && aligned16(y) && (h0 == nullptr || aligned16(h0)) && p.H % VEC == 0 && p.I % VEC == 0};
   EpiDW<T> e{(T*)dW, p.H, p.Z};
+  const DbDuty dd{DBP, db, p.nBG, p.G4, p.H, p.dtype};
   return run_gemm<T, MNRowsPlain<T>, true, MNRowsZ<T>, true, EpiDW<T>>(p, p.G4, p.Z, p.TB, a, bz, e, part, zero,
-                                                                       zero_bytes, s);
+                                                                       zero_bytes, s, dd);
 }
 
 hipError_t launch_gemm_inproj(const Plan& p, const void* x, const void* W, const void* b, float* P, float* part,
@@ -422,9 +441,9 @@ hipError_t launch_gemm_dx(const Plan& p, const void* dG, const void* W, void* dx
                  : dx_t<float>(p, dG, W, dx, part, zero, zero_bytes, s);
 }
 hipError_t launch_gemm_dw(const Plan& p, const void* dG, const void* x, const void* h0, const void* y, void* dW,
-                          float* part, void* zero, size_t zero_bytes, hipStream_t s) {
-  return p.dtype ? dw_t<bf16_t>(p, dG, x, h0, y, dW, part, zero, zero_bytes, s)
-                 : dw_t<float>(p, dG, x, h0, y, dW, part, zero, zero_bytes, s);
+                          float* part, void* zero, size_t zero_bytes, const float* DBP, void* db, hipStream_t s) {
+  return p.dtype ? dw_t<bf16_t>(p, dG, x, h0, y, dW, part, zero, zero_bytes, DBP, db, s)
+                 : dw_t<float>(p, dG, x, h0, y, dW, part, zero, zero_bytes, DBP, db, s);
 }
 
 // Bytes of fp32 split-K partials the three products need for this plan.
@@ -440,49 +459,6 @@ size_t gemm_partial_bytes(const Plan& p, int cus) {
     }
   }
   return mx;
-}
-
-// ---------------------------------------------------------------------------
-// db: column sums of dG [TB][4H] (interleaved columns).  Pass 1: work-group
-// (column block of 64, row chunk) sums its rows in order into part[chunk];
-// pass 2 sums the chunks in order and writes db in gate-block order.
-template <typename T>
-__global__ void __launch_bounds__(256) colsum_pass1(const T* dG, float* part, int64_t TB, int64_t G4, int64_t rows_per_chunk) {
-  __shared__ float red[4][64];
-  const int c = threadIdx.x & 63, rg = threadIdx.x >> 6;
-  const int64_t col = (int64_t)blockIdx.x * 64 + c;
-  const int64_t r0 = (int64_t)blockIdx.y * rows_per_chunk;
-  int64_t r1 = r0 + rows_per_chunk;
-  if (r1 > TB) r1 = TB;
-  float acc = 0.f;
-  if (col < G4)
-    for (int64_t r = r0 + rg; r < r1; r += 4) acc += Elem<T>::to_f(dG[r * G4 + col]);
-  red[rg][c] = acc;
-  __syncthreads();
-  if (rg == 0 && col < G4) part[(int64_t)blockIdx.y * G4 + col] = ((red[0][c] + red[1][c]) + red[2][c]) + red[3][c];
-}
-
-template <typename T>
-__global__ void __launch_bounds__(256) colsum_pass2(const float* part, T* db, int64_t G4, int64_t H, int chunks) {
-  const int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (n >= G4) return;
-  float acc = 0.f;
-  for (int c = 0; c < chunks; ++c) acc += part[(int64_t)c * G4 + n];
-  db[gate_row(n, H)] = Elem<T>::from_f(acc);
-}
-
-hipError_t launch_colsum_db(const Plan& p, const void* dG, void* db, float* part, hipStream_t s) {
-  const int64_t rpc = (p.TB + p.col_chunks - 1) / p.col_chunks;
-  dim3 g1((unsigned)((p.G4 + 63) / 64), (unsigned)p.col_chunks);
-  dim3 g2((unsigned)((p.G4 + 255) / 256));
-  if (p.dtype) {
-    hipLaunchKernelGGL(colsum_pass1<bf16_t>, g1, dim3(256), 0, s, (const bf16_t*)dG, part, p.TB, p.G4, rpc);
-    hipLaunchKernelGGL(colsum_pass2<bf16_t>, g2, dim3(256), 0, s, part, (bf16_t*)db, p.G4, p.H, p.col_chunks);
-  } else {
-    hipLaunchKernelGGL(colsum_pass1<float>, g1, dim3(256), 0, s, (const float*)dG, part, p.TB, p.G4, rpc);
-    hipLaunchKernelGGL(colsum_pass2<float>, g2, dim3(256), 0, s, part, (float*)db, p.G4, p.H, p.col_chunks);
-  }
-  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------

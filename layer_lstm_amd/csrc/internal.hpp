@@ -12,7 +12,7 @@ namespace lstm {
 constexpr uint32_t kErrTimeout = 1u;
 
 // Phase stamps of the recurrent kernels (see lstm_stamps_set in lstm.h).
-constexpr int kStampWGs = 8, kPhases = 5;
+constexpr int kStampWGs = 8, kPhases = 6;
 
 // Work partition and workspace layout of one problem shape.
 struct Plan {
@@ -33,12 +33,11 @@ struct Plan {
   size_t lds_fwd, lds_bwd;
 
   // workspace (byte offsets, 256-aligned)
-  size_t off_ctrl, off_P, off_G, off_C, off_HX, off_PX, off_col, total;
+  size_t off_ctrl, off_P, off_G, off_C, off_HX, off_PX, off_dbp, total;
   size_t bytes_HX, bytes_PX;
   int cus;          // compute units of the device
   int max_splits;   // largest split-K factor of the three products
   size_t off_gp;    // fp32 split-K partials of the products
-  int col_chunks;   // row chunks of the db column sum
 };
 
 // Fill the plan for a shape; returns 0 or an LSTM_ERR_* code.
@@ -57,18 +56,18 @@ hipError_t launch_gemm_inproj(const Plan& p, const void* x, const void* W, const
 hipError_t launch_gemm_dx(const Plan& p, const void* dG, const void* W, void* dx, float* part, void* zero,
                           size_t zero_bytes, hipStream_t s);
 // dW[row(m)][n] = sum_tb dG[tb][m] Z[tb][n],  Z = [h_{t-1} | x_t]
+// The dW launch also writes db[row(n)] = sum_bg DBP[bg][n] (in bg order) when
+// db is not null.
 hipError_t launch_gemm_dw(const Plan& p, const void* dG, const void* x, const void* h0, const void* y, void* dW,
-                          float* part, void* zero, size_t zero_bytes, hipStream_t s);
+                          float* part, void* zero, size_t zero_bytes, const float* DBP, void* db, hipStream_t s);
 size_t gemm_partial_bytes(const Plan& p, int cus);
-// db[row(n)] = sum_tb dG[tb][n]
-hipError_t launch_colsum_db(const Plan& p, const void* dG, void* db, float* part, hipStream_t s);
 
 hipError_t launch_fwd_recurrent(const Plan& p, const float* P, const void* W, const void* h0,
                                 const void* c0, void* y, void* hT, void* cT, void* Gs, float* Cs,
                                 uint64_t* HX, uint32_t* err, uint64_t* stamps, hipStream_t s);
 hipError_t launch_bwd_recurrent(const Plan& p, const void* W, const void* c0, const void* dy,
                                 const void* dhT, const void* dcT, const void* Gs, const float* Cs,
-                                void* dG, uint64_t* PX, void* dh0, void* dc0, uint32_t* err,
+                                void* dG, uint64_t* PX, float* DBP, void* dh0, void* dc0, uint32_t* err,
                                 uint64_t* stamps, hipStream_t s);
 
 }  // namespace lstm

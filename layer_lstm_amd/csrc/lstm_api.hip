@@ -63,19 +63,20 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
       const int64_t nBG = B > 0 ? (B + NB - 1) / NB : 1;
       const int64_t nJG = (H + NJ - 1) / NJ;
       if (nBG * nJG > cus) continue;
-      const int KS = 4 / (NJ / 4);
+      const int KS = 4 / (NJ / 4);                        // 4 waves: M-tiles x k parts
       const int nkbw = Hp / (KS * KB);                    // forward W_h fragments per wave
-      if (nkbw < 2 || nkbw > 32) continue;
-      const int nkbr = 4 * NJ * e / 64, mtw = Hp / 64;    // backward W_h^T fragments per wave
+      if (nkbw < 1 || nkbw > 32) continue;
+      const int nkbr = 4 * NJ * e / 64;                   // backward: k-blocks of the 4*NJ rows
+      const int mtw = Hp / 64;                            // backward: W_h^T column tiles per wave
       if (mtw * nkbr > 32) continue;
       const int NBr = NB < 16 ? 16 : NB;
-      const size_t lds_f = (size_t)NBr * (Hp * e + 16) + (size_t)4096 * (NBr / 16);
+      const size_t lds_f = (size_t)NBr * (Hp * e + 16) + (size_t)(4 - NJ / 4) * (NBr / 16) * 1024;
       if (lds_f > 160 * 1024) continue;
       p->NB = NB; p->NJ = NJ; p->nBG = (int)nBG; p->nJG = (int)nJG; p->grid = (int)(nBG * nJG);
       p->fwd_nkbw = nkbw;
       p->bwd_mtw = mtw;
       p->lds_fwd = lds_f;
-      p->lds_bwd = (size_t)NBr * (4 * NJ * e + 16) + 4096;
+      p->lds_bwd = (size_t)NBr * (4 * NJ * e + 16) + 4096 + (size_t)NB * NJ * 16;
       found = true;
     }
   }
@@ -90,8 +91,6 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
 
   p->cus = cus;
   p->max_splits = 8;
-  int64_t chunks = p->TB / 128;
-  p->col_chunks = (int)(chunks < 1 ? 1 : (chunks > 64 ? 64 : chunks));
 
   const size_t HW = dtype ? (size_t)p->Hp / 2 : (size_t)p->Hp;
   size_t off = 0;
@@ -102,7 +101,7 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
   p->off_G = off; off += align256((size_t)p->TB * p->G4 * e);
   p->off_C = off; off += align256((size_t)p->TB * H * 4);
   p->off_gp = off; off += align256(gemm_partial_bytes(*p, cus));
-  p->off_col = off; off += align256((size_t)p->col_chunks * p->G4 * 4);
+  p->off_dbp = off; off += align256((size_t)p->nBG * p->G4 * 4);
   p->total = off;
   return LSTM_OK;
 }
@@ -296,20 +295,18 @@ int lstm_bwd(const lstm_shape* shape, const void* dy, const void* dhT, const voi
   {
     Timed tm(2, s);
     err = launch_bwd_recurrent(p, W, c0, dy, dhT, dcT, ws + p.off_G, (const float*)(ws + p.off_C), dG,
-                               (uint64_t*)(ws + p.off_PX), dh0, dc0, (uint32_t*)(ws + p.off_ctrl),
+                               (uint64_t*)(ws + p.off_PX), db ? (float*)(ws + p.off_dbp) : nullptr, dh0, dc0,
+                               (uint32_t*)(ws + p.off_ctrl),
                                stamps_fit(p) ? g_stamps_bwd : nullptr, s);
   }
   if (err == hipSuccess) {
     Timed tm(3, s);
-    err = launch_gemm_dw(p, dG, x, h0, y, dW, (float*)(ws + p.off_gp), ws + p.off_PX, p.bytes_PX, s);
+    err = launch_gemm_dw(p, dG, x, h0, y, dW, (float*)(ws + p.off_gp), ws + p.off_PX, p.bytes_PX,
+                         (const float*)(ws + p.off_dbp), db, s);
   }
   if (err == hipSuccess && p.I > 0) {
     Timed tm(4, s);
     err = launch_gemm_dx(p, dG, W, dx, (float*)(ws + p.off_gp), nullptr, 0, s);
-  }
-  if (err == hipSuccess && db) {
-    Timed tm(5, s);
-    err = launch_colsum_db(p, dG, db, (float*)(ws + p.off_col), s);
   }
   return status_of(err);
 }

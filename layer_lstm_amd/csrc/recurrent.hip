@@ -27,7 +27,9 @@
 //   backward: each work-group writes the fp32 partial product
 //             W_h[rows of its units]^T dG_t for all H columns, and every
 //             work-group sums, in a fixed order, the partials of its own
-//             units from all work-groups of the group.
+//             units from all work-groups of the group.  The words of one
+//             batch group are contiguous ([group][producer][unit][row]),
+//             so a reader fetches only lines that it uses.
 // No other grid-wide synchronisation is used.  A thread issues all of its
 // exchange loads of a round at once (up to C in flight) and re-polls only
 // the words whose tag is not there yet, so a step costs about one memory
@@ -41,7 +43,8 @@
 
 namespace lstm {
 
-constexpr int kRecThreads = 256;
+constexpr int kWaves = 4;                 // waves per work-group
+constexpr int kRecThreads = 64 * kWaves;
 
 struct FwdArgs {
   const float* P;   // [TB][4H] fp32, interleaved gates, bias included
@@ -68,7 +71,8 @@ struct BwdArgs {
   const void* Gs;
   const float* Cs;
   void* dG;         // [TB][4H] gate deltas, interleaved
-  uint64_t* PX;     // [2][nJG][Hp][Bp] exchange words (fp32 partials)
+  uint64_t* PX;     // [2][nBG][nJG][Hp][NB] exchange words (fp32 partials)
+  float* DBP;       // [nBG][4H] per-batch-group db partials, interleaved gates
   void* dh0;
   void* dc0;
   uint32_t* err;
@@ -138,7 +142,7 @@ __device__ __forceinline__ uint32_t plan_h_round(uint32_t (&off)[C], int base, i
   uint32_t live = 0;
 #pragma unroll
   for (int c = 0; c < C; ++c) {
-    const int idx = base + c * 256 + tid;
+    const int idx = base + c * kRecThreads + tid;
     const bool lv = idx < total && (idx & hw_mask) < hwv;
     off[c] = lv ? (uint32_t)idx : doff;
     live |= (lv ? 1u : 0u) << c;
@@ -147,20 +151,20 @@ __device__ __forceinline__ uint32_t plan_h_round(uint32_t (&off)[C], int base, i
 }
 
 // Backward round plan: word idx = jg' * nel + e, e = jj * NB + bl; the word
-// is partial[jg'][unit j0 + jj][row b0 + bl] of the exchange layout
-// [nJG][Hp][Bp].
+// is partial[jg'][unit j0 + jj][row bl] of the group's exchange block
+// [nJG][Hp][NB], i.e. at jg' * Hp * NB + j0 * NB + e.
 template <int C>
 __device__ __forceinline__ uint32_t plan_dh_round(uint32_t (&off)[C], int base, int tid, int gtotal, int nel, int lg_nel,
-                                                  int NB, int lg_nb, int j0, int b0, int B, int H, int Hp, int Bp,
+                                                  int NB, int lg_nb, int j0, int b0, int B, int H, int HpNB,
                                                   uint32_t doff) {
   uint32_t live = 0;
 #pragma unroll
   for (int c = 0; c < C; ++c) {
-    const int idx = base + c * 256 + tid;
+    const int idx = base + c * kRecThreads + tid;
     const int e = idx & (nel - 1), g2 = idx >> lg_nel;
     const int bl = e & (NB - 1), uu = j0 + (e >> lg_nb);
     const bool lv = idx < gtotal && b0 + bl < B && uu < H;
-    off[c] = lv ? (uint32_t)(((uint32_t)g2 * (uint32_t)Hp + (uint32_t)uu) * (uint32_t)Bp + (uint32_t)(b0 + bl)) : doff;
+    off[c] = lv ? (uint32_t)g2 * (uint32_t)HpNB + (uint32_t)(j0 * NB + e) : doff;
     live |= (lv ? 1u : 0u) << c;
   }
   return live;
@@ -182,13 +186,13 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_rec_kernel(FwdArgs a) {
   const int bg = blockIdx.x / a.nJG, jg = blockIdx.x % a.nJG;
   const int b0 = bg * a.NB, j0 = jg * a.NJ;
   const int MT = a.NJ / 4;                   // M-tiles (16 interleaved gate rows = 4 units)
-  const int KS = 4 / MT;                     // waves splitting k per M-tile
+  const int KS = kWaves / MT;                // waves splitting k per M-tile
   const int mt = w / KS, wk = w % KS;        // this wave's M-tile and k part
   const int kb0 = wk * NKBW;
   const int strideH = a.Hp * E + 16;         // LDS row of h_{t-1}
   const int NBr = a.NB < 16 ? 16 : a.NB;     // rows of the batch tiles (rows >= NB stay zero)
   char* Hl = smem;                           // [NBr][strideH]
-  float* red = (float*)(smem + NBr * strideH);  // [4 waves][NBT][64][4]
+  float* red = (float*)(smem + NBr * strideH);  // [MT*(KS-1) partial slots][NBT][64][4]
   const int64_t G4 = 4 * (int64_t)a.H;
   const int u = j0 + 4 * mt + fq;            // unit of this lane's elementwise results
   bool dead = false;
@@ -226,6 +230,21 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_rec_kernel(FwdArgs a) {
   const int total = NBv << lgHW;                         // exchange words read per step
   const uint32_t doff = (uint32_t)(tid % total);         // target of unused load slots
 
+  // The input projection of this lane's elements is prefetched one step
+  // ahead (at the end of the previous step), so that no wait of a step on its
+  // exchange words or its product also waits for this load.
+  f32x4_t pf[NBT];
+  auto load_p = [&](int tt) {
+#pragma unroll
+    for (int nt = 0; nt < NBT; ++nt) {
+      const int b = b0 + 16 * nt + fr;
+      pf[nt] = (wk == 0 && tt < a.T && u < a.H && 16 * nt + fr < NBv)
+                   ? *(const f32x4_t*)(a.P + ((int64_t)tt * a.B + b) * G4 + 4 * (int64_t)u)
+                   : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  load_p(0);
+
   for (int t = 0; t < a.T; ++t) {
     stamp(a.stamps, a.T, t, 0);
     // h_{t-1} words: word idx = bl * HW + kw of this group's rows (HW a power
@@ -237,17 +256,6 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_rec_kernel(FwdArgs a) {
     if (t > 0) {
       live = plan_h_round<C>(off, 0, tid, total, a.HW - 1, HWv, doff);
       issue_tagged<C>(wv, src, off);
-    }
-    // prefetch the input projection of this lane's elements (after the
-    // exchange loads, so that their check does not wait for it)
-    f32x4_t pf[NBT];
-    if (wk == 0) {
-#pragma unroll
-      for (int nt = 0; nt < NBT; ++nt) {
-        const int b = b0 + 16 * nt + fr;
-        pf[nt] = (u < a.H && 16 * nt + fr < NBv) ? *(const f32x4_t*)(a.P + ((int64_t)t * a.B + b) * G4 + 4 * (int64_t)u)
-                                      : f32x4_t{0.f, 0.f, 0.f, 0.f};
-      }
     }
     __syncthreads();  // previous step's readers of Hl are done
     // h_{t-1} -> LDS
@@ -300,21 +308,24 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_rec_kernel(FwdArgs a) {
 #pragma unroll
       for (int ch = 1; ch < CH; ++ch) acc[nt] += part[nt][ch];
     }
+    stamp(a.stamps, a.T, t, 3);
     if (KS > 1) {
       if (wk != 0) {
 #pragma unroll
-        for (int nt = 0; nt < NBT; ++nt) *(f32x4_t*)(red + ((w * NBT + nt) * 64 + lane) * 4) = acc[nt];
+        for (int nt = 0; nt < NBT; ++nt)
+          *(f32x4_t*)(red + (((mt * (KS - 1) + wk - 1) * NBT + nt) * 64 + lane) * 4) = acc[nt];
       }
       __syncthreads();
       if (wk == 0) {
         for (int k2 = 1; k2 < KS; ++k2) {
 #pragma unroll
-          for (int nt = 0; nt < NBT; ++nt) acc[nt] += *(const f32x4_t*)(red + (((w + k2) * NBT + nt) * 64 + lane) * 4);
+          for (int nt = 0; nt < NBT; ++nt)
+            acc[nt] += *(const f32x4_t*)(red + (((mt * (KS - 1) + k2 - 1) * NBT + nt) * 64 + lane) * 4);
         }
       }
     }
 
-    stamp(a.stamps, a.T, t, 3);
+    stamp(a.stamps, a.T, t, 4);
     // elementwise: gates, cell, hidden; outputs and the exchange word
     if (wk == 0) {
       uint64_t* dst = a.HX + (int64_t)(t & 1) * a.Bp * a.HW;
@@ -356,7 +367,8 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_rec_kernel(FwdArgs a) {
         }
       }
     }
-    stamp(a.stamps, a.T, t, 4);
+    load_p(t + 1);
+    stamp(a.stamps, a.T, t, 5);
   }
   // T == 0 is handled on the host
 }
@@ -379,21 +391,25 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
   const int TPE = nel < kRecThreads ? kRecThreads / nel : 1;  // threads per element (1..8)
   const int strideD = 4 * a.NJ * E + 16;
   char* Dl = smem;                                     // [NBr][strideD] gate deltas (B operand)
-  float* sums = (float*)(smem + NBr * strideD);        // [4][256] partial sums of the gather
+  float* sums = (float*)(smem + NBr * strideD);        // [4][kRecThreads] gather sums
+  float* dba = sums + 4 * kRecThreads;                 // [nel][4] db: gate deltas summed over time
+  for (int idx = tid; idx < 4 * nel; idx += kRecThreads) dba[idx] = 0.f;
   for (int idx = tid; idx < NBr * strideD / 4; idx += kRecThreads) ((uint32_t*)Dl)[idx] = 0u;
   const int64_t G4 = 4 * (int64_t)a.H;
   const int gtotal = a.nJG * nel;                      // exchange words read per step
+  const int nBG = a.Bp / a.NB;
+  const int HpNB = a.Hp * a.NB;                        // words of one producer's block
   const uint32_t doff = (uint32_t)(tid % gtotal);      // target of unused load slots
   bool dead = false;
 
   // --- resident fragments of W_h^T: A[m = column k][kslot = row r], column
-  // tile of fragment i is w + 4*i
+  // tile of fragment i is w + kWaves*i
   u32x4_t wreg[MTW * NKBR];
 #pragma unroll
   for (int i = 0; i < MTW; ++i) {
 #pragma unroll
     for (int kb = 0; kb < NKBR; ++kb) {
-      const int k = 16 * (w + 4 * i) + fr;  // column of W_h
+      const int k = 16 * (w + kWaves * i) + fr;  // column of W_h
       T tmp[16 / E];
 #pragma unroll
       for (int e = 0; e < 16 / E; ++e) {
@@ -416,24 +432,10 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
     dhc[s] = (valid && a.dhT) ? ldf<T>(a.dhT, (int64_t)b * a.H + uu) : 0.f;
   }
 
-  for (int t = a.T - 1; t >= -1; --t) {
-    const int step = a.T - 1 - (t < 0 ? 0 : t);
-    if (t >= 0) stamp(a.stamps, a.T, step, 0);
-    // 1. gather dh_carry: sum over work-groups of the partials produced at
-    //    step t+1.  Word idx = jg' * nel + e (e = jj * NB + bl): a thread
-    //    always meets the same element slot(s), in increasing jg' order, and
-    //    the TPE threads sharing an element are then added in a fixed order.
-    const bool gather = t < a.T - 1;
-    const uint64_t* src = a.PX + (int64_t)((t + 1) & 1) * a.nJG * a.Hp * a.Bp;
-    uint32_t off[C];
-    uint32_t live = 0;
-    uint64_t wv[C];
-    if (gather) {
-      live = plan_dh_round<C>(off, 0, tid, gtotal, nel, lgNel, a.NB, lgNB, j0, b0, a.B, a.H, a.Hp, a.Bp, doff);
-      issue_tagged<C>(wv, src, off);
-    }
-    // prefetch this step's elementwise operands (after the exchange loads)
-    float pg[4][4], pc[4], pcp[4], pdy[4];
+  // Elementwise operands of a step (activated gates, c_t, c_{t-1}, dy_t) are
+  // prefetched one step ahead, at the end of the step before.
+  float pg[4][4], pc[4], pcp[4], pdy[4];
+  auto load_ops = [&](int tt) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int e = tid + kRecThreads * s;
@@ -441,8 +443,8 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
       const int b = b0 + bl;
       pg[s][0] = pg[s][1] = pg[s][2] = pg[s][3] = 0.f;
       pc[s] = pcp[s] = pdy[s] = 0.f;
-      if (t >= 0 && s < EPT && e < nel && b < a.B && uu < a.H) {
-        const int64_t o = (int64_t)t * a.B + b;
+      if (tt >= 0 && s < EPT && e < nel && b < a.B && uu < a.H) {
+        const int64_t o = (int64_t)tt * a.B + b;
         if constexpr (E == 4) {
           const f32x4_t gv = *(const f32x4_t*)((const T*)a.Gs + o * G4 + 4 * (int64_t)uu);
           pg[s][0] = gv[0]; pg[s][1] = gv[1]; pg[s][2] = gv[2]; pg[s][3] = gv[3];
@@ -452,9 +454,28 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
           pg[s][2] = bf2f((bf16_t)(raw >> 32)); pg[s][3] = bf2f((bf16_t)(raw >> 48));
         }
         pc[s] = a.Cs[o * a.H + uu];
-        pcp[s] = t > 0 ? a.Cs[(o - a.B) * a.H + uu] : (a.c0 ? ldf<T>(a.c0, (int64_t)b * a.H + uu) : 0.f);
+        pcp[s] = tt > 0 ? a.Cs[(o - a.B) * a.H + uu] : (a.c0 ? ldf<T>(a.c0, (int64_t)b * a.H + uu) : 0.f);
         pdy[s] = ldf<T>(a.dy, o * a.H + uu);
       }
+    }
+  };
+  load_ops(a.T - 1);
+
+  for (int t = a.T - 1; t >= -1; --t) {
+    const int step = a.T - 1 - (t < 0 ? 0 : t);
+    if (t >= 0) stamp(a.stamps, a.T, step, 0);
+    // 1. gather dh_carry: sum over work-groups of the partials produced at
+    //    step t+1.  Word idx = jg' * nel + e (e = jj * NB + bl): a thread
+    //    always meets the same element slot(s), in increasing jg' order, and
+    //    the TPE threads sharing an element are then added in a fixed order.
+    const bool gather = t < a.T - 1;
+    const uint64_t* src = a.PX + ((int64_t)((t + 1) & 1) * nBG + bg) * a.nJG * HpNB;
+    uint32_t off[C];
+    uint32_t live = 0;
+    uint64_t wv[C];
+    if (gather) {
+      live = plan_dh_round<C>(off, 0, tid, gtotal, nel, lgNel, a.NB, lgNB, j0, b0, a.B, a.H, HpNB, doff);
+      issue_tagged<C>(wv, src, off);
     }
     if (gather) {
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -471,7 +492,7 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
         }
         base += kRecThreads * C;
         if (base >= gtotal) break;
-        live = plan_dh_round<C>(off, base, tid, gtotal, nel, lgNel, a.NB, lgNB, j0, b0, a.B, a.H, a.Hp, a.Bp, doff);
+        live = plan_dh_round<C>(off, base, tid, gtotal, nel, lgNel, a.NB, lgNB, j0, b0, a.B, a.H, HpNB, doff);
         issue_tagged<C>(wv, src, off);
       }
       // sums[s][tid] holds this thread's part of element tid + 256*s (EPT > 1),
@@ -513,6 +534,7 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
           const float d_i = dc * gg * gi * (1.f - gi);
           const float d_f = dc * cprev * gf * (1.f - gf);
           dcc[s] = dc * gf;
+          *(f32x4_t*)(dba + 4 * e) += f32x4_t{d_i, d_f, d_g, d_o};
           dq[0] = Elem<T>::from_f(d_i); dq[1] = Elem<T>::from_f(d_f);
           dq[2] = Elem<T>::from_f(d_g); dq[3] = Elem<T>::from_f(d_o);
           if constexpr (E == 4)
@@ -530,14 +552,14 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
     stamp(a.stamps, a.T, step, 2);
 
     // 3. partial[k][b] = sum_{r in my rows} W_h[r][k] dG[b][r], all k < H
-    uint64_t* dst = a.PX + ((int64_t)(t & 1) * a.nJG + jg) * a.Hp * a.Bp;
+    uint64_t* dst = a.PX + (((int64_t)(t & 1) * nBG + bg) * a.nJG + jg) * HpNB;
     for (int nt = 0; nt < NBT; ++nt) {
       u32x4_t breg[NKBR];
 #pragma unroll
       for (int kb = 0; kb < NKBR; ++kb)
         breg[kb] = *(const u32x4_t*)(Dl + (16 * nt + fr) * strideD + kb * 64 + fq * 16);
-      const int b = b0 + 16 * nt + fr;
-      const bool bvalid = 16 * nt + fr < a.NB && b < a.B;
+      const int bl = 16 * nt + fr, b = b0 + bl;
+      const bool bvalid = bl < a.NB && b < a.B;
 #pragma unroll
       for (int i = 0; i < MTW; ++i) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -546,15 +568,29 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
         if (bvalid) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int k = 16 * (w + 4 * i) + 4 * fq + e;
-            if (k < a.H) xstore(dst + (int64_t)k * a.Bp + b, acc[e], (uint32_t)(t + 1));
+            const int k = 16 * (w + kWaves * i) + 4 * fq + e;
+            if (k < a.H) xstore(dst + (int64_t)k * a.NB + bl, acc[e], (uint32_t)(t + 1));
           }
         }
       }
     }
     stamp(a.stamps, a.T, step, 3);
-    __syncthreads();  // Dl is rewritten next step
+    load_ops(t - 1);
     stamp(a.stamps, a.T, step, 4);
+    __syncthreads();  // Dl is rewritten next step
+    stamp(a.stamps, a.T, step, 5);
+  }
+
+  // db partial of this work-group: for each (unit, gate), the sum over its
+  // batch rows (in row order) of the per-element sums over time
+  if (a.DBP) {
+    __syncthreads();
+    for (int r = tid; r < 4 * a.NJ; r += kRecThreads) {
+      const int jj = r >> 2, g = r & 3;
+      float v = 0.f;
+      for (int bl = 0; bl < a.NB; ++bl) v += dba[4 * ((jj << lgNB) + bl) + g];
+      if (j0 + jj < a.H) a.DBP[(int64_t)bg * G4 + 4 * (j0 + jj) + g] = v;
+    }
   }
 
   // dh0 / dc0
@@ -581,6 +617,7 @@ static hipError_t coop_launch(K kernel, int grid, size_t lds, void* arg, hipStre
 template <typename T, int NBT, int C>
 static hipError_t fwd_dispatch_c(const Plan& p, FwdArgs& a, hipStream_t s) {
   switch (p.fwd_nkbw) {
+    case 1: return coop_launch(fwd_rec_kernel<T, NBT, 1, C>, p.grid, p.lds_fwd, &a, s);
     case 2: return coop_launch(fwd_rec_kernel<T, NBT, 2, C>, p.grid, p.lds_fwd, &a, s);
     case 4: return coop_launch(fwd_rec_kernel<T, NBT, 4, C>, p.grid, p.lds_fwd, &a, s);
     case 8: return coop_launch(fwd_rec_kernel<T, NBT, 8, C>, p.grid, p.lds_fwd, &a, s);
@@ -642,9 +679,9 @@ static hipError_t bwd_dispatch(const Plan& p, BwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_bwd_recurrent(const Plan& p, const void* W, const void* c0, const void* dy, const void* dhT,
-                                const void* dcT, const void* Gs, const float* Cs, void* dG, uint64_t* PX, void* dh0,
-                                void* dc0, uint32_t* err, uint64_t* stamps, hipStream_t s) {
-  BwdArgs a{W, c0, dy, dhT, dcT, Gs, Cs, dG, PX, dh0, dc0, err, stamps, (int)p.T, (int)p.B, (int)p.H, (int)p.Z,
+                                const void* dcT, const void* Gs, const float* Cs, void* dG, uint64_t* PX, float* DBP,
+                                void* dh0, void* dc0, uint32_t* err, uint64_t* stamps, hipStream_t s) {
+  BwdArgs a{W, c0, dy, dhT, dcT, Gs, Cs, dG, PX, DBP, dh0, dc0, err, stamps, (int)p.T, (int)p.B, (int)p.H, (int)p.Z,
             p.NB, p.NJ, p.nJG, p.Hp, p.Bp};
   const int nkbr = 4 * p.NJ * p.esize / 64;
   if (p.dtype) {

@@ -30,9 +30,9 @@ STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_DIMS", -3: "ERR_DTYPE", -4: "ERR_ALI
           -9: "ERR_TIMEOUT", -10: "ERR_DEVICE"}
 EXPORTS = ("lstm_abi_version", "lstm_status_string", "lstm_query", "lstm_fwd_train", "lstm_bwd",
            "lstm_check_workspace", "lstm_timing_enable", "lstm_timing_read", "lstm_stamps_set")
-STAMP_WGS, STAMP_POINTS = 8, 5
+STAMP_WGS, STAMP_POINTS = 8, 6
 KERNEL_KINDS = ("input_projection", "forward_recurrence", "backward_recurrence", "dW_product",
-                "dx_product", "db_colsum", "clear_copy")
+                "dx_product", "unused", "state_copy")
 
 
 class Shape(ctypes.Structure):
@@ -156,7 +156,7 @@ def timing_read() -> dict:
 
 def stamps_set(buf, T) -> None:
     """Point the recurrent kernels' phase stamps at a device tensor of at
-    least 2*8*T*5 int64 values (None disables)."""
+    least 2*8*T*6 int64 values (None disables)."""
     if buf is None:
         _lib.lstm_stamps_set(None, 0, 0)
         return
