@@ -11,7 +11,7 @@
 // left after t = 0.
 //
 // One launch per direction of time; the grid (nBG x nJG work-groups, one
-// per CU, co-resident by cooperative launch) runs every step.  Work-group
+// per CU, all resident at once) runs every step.  Work-group
 // (bg, jg) owns batch rows [bg*NB, +NB) and hidden units [jg*NJ, +NJ); it
 // keeps the 4*NJ rows of W_h that belong to its units (gates i,f,g,o of each
 // unit) in VGPRs as MFMA fragments for the whole launch.  Batch groups never
@@ -606,12 +606,25 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// The persistent kernels need every work-group of the grid resident at
+// once.  The grid never exceeds the CU count and each work-group fits a CU
+// on its own; the occupancy query confirms that the device can hold the
+// whole grid before the kernel is dispatched as an ordinary launch (a
+// cooperative launch would guarantee the same but costs about 15 us more per
+// dispatch).  If other work holds CUs, the waiting work-groups spin until it
+// drains; every wait is bounded (kWaitTicks) and reports LSTM_ERR_TIMEOUT.
 template <typename K>
 static hipError_t coop_launch(K kernel, int grid, size_t lds, void* arg, hipStream_t s) {
   hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   void* args[] = {arg};
-  return hipLaunchCooperativeKernel((const void*)kernel, dim3(grid), dim3(kRecThreads), args, (unsigned)lds, s);
+  int per_cu = 0, dev = 0, cus = 0;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kernel, kRecThreads, lds)) != hipSuccess)
+    return e;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  if (per_cu < 1 || (int64_t)per_cu * cus < grid) return hipErrorCooperativeLaunchTooLarge;
+  return hipLaunchKernel((const void*)kernel, dim3(grid), dim3(kRecThreads), args, lds, s);
 }
 
 template <typename T, int NBT, int C>

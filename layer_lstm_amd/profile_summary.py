@@ -1,0 +1,148 @@
+"""Turn rocprofv3 CSV output into the short text summaries kept under
+profiles/ and the per-kernel HBM traffic record that bench.py reports.
+
+    python -m layer_lstm_amd.profile_summary stats DIR OUT.txt --command "..."
+    python -m layer_lstm_amd.profile_summary traffic --workload NAME \
+        --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \
+        --copy-bytes N --out-json profiles/traffic.json --out-txt OUT.txt \
+        --command "..." [--command "..."]
+
+`stats` reads <DIR>/*kernel_stats.csv (rocprofv3 --kernel-trace --stats
+--output-format csv) and writes the per-kernel table with the command that
+produced it.  `traffic` reads the counter_collection.csv of four
+rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, each for the LSTM step and
+for a plain copy of --copy-bytes bytes), scales each counter by what it reads
+for the copy (known bytes / counted bytes), and records HBM bytes per
+launch for each kernel kind of the path, with the hash of the kernel's
+source so that a record goes stale when the kernel changes.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "layer_lstm_amd", "csrc")
+
+# kernel kind -> (source file, predicate on the demangled kernel name)
+KINDS = {
+    "input_projection": ("gemm.hip", lambda n: "gemm_kernel" in n and "EpiP" in n),
+    "forward_recurrence": ("recurrent.hip", lambda n: "fwd_rec_kernel" in n),
+    "backward_recurrence": ("recurrent.hip", lambda n: "bwd_rec_kernel" in n),
+    "dW_product": ("gemm.hip", lambda n: "EpiDW" in n),
+    "dx_product": ("gemm.hip", lambda n: "EpiStore" in n),
+}
+
+
+def source_sha(fname: str) -> str:
+    return hashlib.sha256(open(os.path.join(CSRC, fname), "rb").read()).hexdigest()[:16]
+
+
+def kind_of(name: str):
+    for k, (_, pred) in KINDS.items():
+        if pred(name):
+            return k
+    return None
+
+
+def find_csv(d: str, suffix: str) -> str:
+    hits = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def cmd_stats(a):
+    rows = list(csv.DictReader(open(find_csv(a.dir, "kernel_stats.csv"))))
+    lines = [f"# rocprofv3 kernel statistics", "", "command:", ""]
+    lines += [f"    {c}" for c in a.command] + [""]
+    lines.append(f"{'kernel':96s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'pct':>6s}")
+    for r in rows:
+        name = r["Name"]
+        if len(name) > 96:
+            name = name[:93] + "..."
+        lines.append(f"{name:96s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                     f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):6.2f}")
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def counter_rows(d: str, counter: str):
+    """Per-dispatch (kernel name, value) of one counter."""
+    out = []
+    for r in csv.DictReader(open(find_csv(d, "counter_collection.csv"))):
+        if r.get("Counter_Name") == counter:
+            out.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    if not out:
+        raise SystemExit(f"counter {counter} not found under {d}")
+    return out
+
+
+def copy_factor(d: str, counter: str, nbytes: int):
+    """Known bytes / counted bytes for the largest dispatch of the copy run
+    (the copy itself; torch's small set-up kernels are smaller)."""
+    rows = counter_rows(d, counter)
+    name, kib = max(rows, key=lambda r: r[1])
+    return nbytes / (kib * 1024.0), name, kib
+
+
+def cmd_traffic(a):
+    ff, fname, fkib = copy_factor(a.copy_fetch, "FETCH_SIZE", a.copy_bytes)
+    wf, wname, wkib = copy_factor(a.copy_write, "WRITE_SIZE", a.copy_bytes)
+    per = {}
+    for counter, d, fac in (("FETCH_SIZE", a.fetch, ff), ("WRITE_SIZE", a.write, wf)):
+        for name, kib in counter_rows(d, counter):
+            k = kind_of(name)
+            if k is None:
+                continue
+            per.setdefault(k, {}).setdefault(counter, []).append(kib * 1024.0 * fac)
+    try:
+        rec = json.load(open(a.out_json))
+    except (OSError, ValueError):
+        rec = {}
+    wrec = rec.setdefault(a.workload, {})
+    lines = ["# HBM traffic per launch from rocprofv3 counters", "", "commands:", ""]
+    lines += [f"    {c}" for c in a.command] + [""]
+    lines.append(f"copy calibration: {a.copy_bytes} bytes copied; FETCH_SIZE read {fkib:.0f} KiB "
+                 f"(factor {ff:.4f}), WRITE_SIZE read {wkib:.0f} KiB (factor {wf:.4f})")
+    lines.append(f"workload {a.workload}")
+    lines.append(f"{'kernel kind':22s} {'launches':>8s} {'fetch MB':>10s} {'write MB':>10s} {'total MB':>10s}")
+    for k, v in per.items():
+        fetch = statistics.median(v.get("FETCH_SIZE", [0.0]))
+        write = statistics.median(v.get("WRITE_SIZE", [0.0]))
+        n = len(v.get("FETCH_SIZE", []))
+        wrec[k] = {"bytes_per_launch": round(fetch + write), "fetch_bytes": round(fetch), "write_bytes": round(write),
+                   "source_sha": source_sha(KINDS[k][0]), "copy_factor_fetch": round(ff, 5),
+                   "copy_factor_write": round(wf, 5)}
+        lines.append(f"{k:22s} {n:8d} {fetch / 1e6:10.3f} {write / 1e6:10.3f} {(fetch + write) / 1e6:10.3f}")
+    json.dump(rec, open(a.out_json, "w"), indent=1, sort_keys=True)
+    open(a.out_txt, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("out")
+    s.add_argument("--command", action="append", default=[])
+    t = sub.add_parser("traffic")
+    t.add_argument("--workload", required=True)
+    for k in ("fetch", "write", "copy_fetch", "copy_write"):
+        t.add_argument("--" + k.replace("_", "-"), dest=k, required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--out-json", required=True)
+    t.add_argument("--out-txt", required=True)
+    t.add_argument("--command", action="append", default=[])
+    a = ap.parse_args()
+    cmd_stats(a) if a.cmd == "stats" else cmd_traffic(a)
+
+
+if __name__ == "__main__":
+    main()
