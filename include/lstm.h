@@ -129,7 +129,9 @@ int lstm_bwd(const lstm_shape* shape, const void* dy, const void* dhT, const voi
  * recurrent kernel recorded in `workspace`: LSTM_ERR_TIMEOUT, else LSTM_OK
  * (or LSTM_ERR_LAUNCH if the stream itself reports an error).  The time-out
  * mark is set by the kernels themselves (a per-step wait that exceeded its
- * bound); it stays set, and the outputs of later calls on the workspace are
+ * bound, e.g. because other work held the device's compute units for
+ * seconds, or the device did not deal work-groups to its XCDs round robin
+ * as the XCD-local layout relies on); it stays set, and the outputs of later calls on the workspace are
  * undefined, until lstm_fwd_train() runs again on it.  After any error,
  * run lstm_fwd_train() before the next lstm_bwd() on the same workspace. */
 int lstm_check_workspace(void* workspace, size_t workspace_bytes, void* stream);

@@ -7,6 +7,7 @@ layer_lstm_amd/liblstm.so next to this file.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -16,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblstm.so")
-SOURCES = ["lstm_api.hip", "gemm.hip", "recurrent.hip"]
+SOURCES = ["lstm_api.hip", "gemm.hip", "recurrent.hip", "recurrent_vec.hip"]
 ARCH = "gfx950"
 
 
@@ -37,17 +38,24 @@ def flags() -> list[str]:
 def build(verbose: bool = False) -> str:
     """Compile all sources into liblstm.so (always recompiles)."""
     cc = hipcc()
-    objs = []
     bdir = os.path.join(HERE, "_build")
     os.makedirs(bdir, exist_ok=True)
-    for src in SOURCES:
+
+    def compile_one(src):
         obj = os.path.join(bdir, src.replace(".hip", ".o"))
         cmd = [cc, *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
         r = subprocess.run(cmd, capture_output=True, text=True)
         err = "\n".join(l for l in r.stderr.splitlines() if "packed-fp32-ops" not in l)
-        if r.returncode != 0:
+        return src, obj, " ".join(cmd), r.returncode, err
+
+    # the sources compile independently; hipcc is single-threaded per file
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        results = list(ex.map(compile_one, SOURCES))
+    objs = []
+    for src, obj, cmd, rc, err in results:
+        if verbose:
+            print(cmd, flush=True)
+        if rc != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{err}")
         if err.strip() and verbose:
             print(err)

@@ -78,15 +78,43 @@ template <> struct Mfma<bf16_t> {
 // so a reader that sees the expected tag sees the value written with it: no
 // fence and no separate barrier are needed.  Exchange buffers are cleared
 // (tag 0) before every launch and tags are 1-based.
-__device__ __forceinline__ void xstore(uint64_t* p, float v, uint32_t tag) {
-  uint64_t w = ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v);
-  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+//
+// XCD-local groups (all readers of a word on the writer's XCD): the word is
+// stored with a plain (work-group scope) store, which stays in that XCD's
+// L2, and the device-coherent load of a reader on the same XCD finds it
+// there; this saves the write-through to memory on every step.  Readers on
+// other XCDs would not see such a word, so callers use it only after
+// checking that the work-group runs where the layout assumes (xcc_id()).
+// (The plain store is one aligned 8-byte global store, so a reader sees
+// either the old or the new word whole.)
+__device__ __forceinline__ void xstore_word(uint64_t* p, uint64_t w, bool local) {
+  if (local)
+    *p = w;
+  else
+    __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void xstore(uint64_t* p, float v, uint32_t tag, bool local) {
+  xstore_word(p, ((uint64_t)tag << 32) | (uint64_t)__float_as_uint(v), local);
+}
+// Index of the XCD (accelerator complex die) this wave runs on.
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 15u;
 }
 __device__ __forceinline__ uint64_t xload(const uint64_t* p) {
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint32_t xtag(uint64_t w) { return (uint32_t)(w >> 32); }
 __device__ __forceinline__ float xval(uint64_t w) { return __uint_as_float((uint32_t)w); }
+
+// Wait until every vector memory operation of this wave has completed
+// (s_waitcnt vmcnt(0); expcnt and lgkmcnt left alone).  Used on the rare
+// paths of a step (the first step, a dead wait) so that every path reaching
+// the next step has no loads or stores outstanding; otherwise the compiler
+// must assume some are and waits for all stores before reusing their
+// registers on the common path.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Time bound of one wait: s_memrealtime runs at 100 MHz.
 constexpr uint64_t kWaitTicks = 200000000ull;  // 2 s

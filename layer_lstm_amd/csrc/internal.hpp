@@ -31,6 +31,12 @@ struct Plan {
   int words_per_thread;  // exchange words a thread reads per step (NB*H / 256, rounded up)
   int Bp;       // nBG * NB
   size_t lds_fwd, lds_bwd;
+  // XCD-local exchange: when the batch groups divide evenly over the XCDs
+  // (nBG a multiple of nxcd), each batch group lives on one XCD and its
+  // exchange words stay in that XCD's L2 (plain stores, device-coherent
+  // loads).
+  int nxcd;     // XCDs of the device (compute units / 32 on gfx950)
+  int xcd_local;
 
   // workspace (byte offsets, 256-aligned)
   size_t off_ctrl, off_P, off_G, off_C, off_HX, off_PX, off_dbp, total;

@@ -91,6 +91,8 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
 
   p->cus = cus;
   p->max_splits = 8;
+  p->nxcd = (cus % 32 == 0 && cus >= 32) ? cus / 32 : 1;
+  p->xcd_local = p->nxcd > 1 && p->nBG % p->nxcd == 0;
 
   const size_t HW = dtype ? (size_t)p->Hp / 2 : (size_t)p->Hp;
   size_t off = 0;

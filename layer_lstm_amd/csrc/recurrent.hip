@@ -38,142 +38,9 @@
 // Compile-time shapes (H is padded to Hp, a power of two): NKBW k-blocks of
 // W_h per wave in the forward, MTW 16-column tiles of W_h^T per wave and
 // NKBR k-blocks of the 4*NJ rows in the backward; NBT 16-row batch tiles.
-#include "device_common.hpp"
-#include "internal.hpp"
+#include "recurrent_common.hpp"
 
 namespace lstm {
-
-constexpr int kWaves = 4;                 // waves per work-group
-constexpr int kRecThreads = 64 * kWaves;
-
-struct FwdArgs {
-  const float* P;   // [TB][4H] fp32, interleaved gates, bias included
-  const void* W;    // [4H][H+I]
-  const void* h0;   // [B][H] or null
-  const void* c0;   // [B][H] or null
-  void* y;          // [T][B][H]
-  void* hT;         // [B][H]
-  void* cT;         // [B][H]
-  void* Gs;         // [TB][4H] activated gates, interleaved
-  float* Cs;        // [TB][H] cell states
-  uint64_t* HX;     // [2][Bp][HW] exchange words
-  uint32_t* err;
-  uint64_t* stamps; // optional [kStampWGs][T][kPhases] clock stamps
-  int T, B, H, Z, NB, NJ, nJG, Hp, Bp, HW;
-};
-
-struct BwdArgs {
-  const void* W;
-  const void* c0;
-  const void* dy;   // [T][B][H]
-  const void* dhT;  // [B][H] or null
-  const void* dcT;  // [B][H] or null
-  const void* Gs;
-  const float* Cs;
-  void* dG;         // [TB][4H] gate deltas, interleaved
-  uint64_t* PX;     // [2][nBG][nJG][Hp][NB] exchange words (fp32 partials)
-  float* DBP;       // [nBG][4H] per-batch-group db partials, interleaved gates
-  void* dh0;
-  void* dc0;
-  uint32_t* err;
-  uint64_t* stamps;
-  int T, B, H, Z, NB, NJ, nJG, Hp, Bp;
-};
-
-// Phase stamps: thread 0 of the first kStampWGs work-groups records the
-// 100 MHz real-time clock (s_memrealtime) at kPhases points of every step when
-// a stamp buffer is given; slot layout [wg][step][phase], steps in execution
-// order.
-__device__ __forceinline__ void stamp(uint64_t* buf, int T, int step, int phase) {
-  if (buf && threadIdx.x == 0 && blockIdx.x < kStampWGs)
-    buf[((int64_t)blockIdx.x * T + step) * kPhases + phase] = __builtin_amdgcn_s_memrealtime();
-}
-
-__device__ __forceinline__ bool err_set(uint32_t* err) {
-  return __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
-}
-
-// Tagged-word reads, in two halves so that independent loads can be issued
-// between them: issue_tagged() sends the C loads of a thread at once;
-// complete_tagged() waits until every wanted word (bit c of `live`) carries
-// `tag`, re-polling all still-missing words once per round trip.  Loads
-// retire in order, so anything issued after issue_tagged() does not delay
-// the check.  The wait is bounded: past kWaitTicks (or once another thread
-// has recorded an error) the error word is set and `dead` makes this and
-// every later wait of the thread return at once.
-template <int C>
-__device__ __forceinline__ void issue_tagged(uint64_t (&wv)[C], const uint64_t* base, const uint32_t (&off)[C]) {
-#pragma unroll
-  for (int c = 0; c < C; ++c) wv[c] = xload(base + off[c]);
-}
-
-template <int C>
-__device__ __forceinline__ void complete_tagged(uint64_t (&wv)[C], const uint64_t* base, const uint32_t (&off)[C],
-                                                uint32_t live, uint32_t tag, uint32_t* err, bool& dead) {
-  if (dead) return;
-  uint64_t t0 = 0;
-  uint32_t rounds = 0;
-  while (true) {
-    uint32_t pending = 0;
-#pragma unroll
-    for (int c = 0; c < C; ++c)
-      if (((live >> c) & 1u) && xtag(wv[c]) != tag) pending |= 1u << c;
-    if (!pending) return;
-    if (t0 == 0) {
-      t0 = now_ticks();
-    } else if ((++rounds & 15u) == 0 && (now_ticks() - t0 > kWaitTicks || err_set(err))) {
-      atomicOr(err, kErrTimeout);
-      dead = true;
-      return;
-    }
-#pragma unroll
-    for (int c = 0; c < C; ++c)
-      if ((pending >> c) & 1u) wv[c] = xload(base + off[c]);
-  }
-}
-
-// Forward round plan: word idx = base + c*256 + tid of the group's rows
-// (idx = row * HW + word, HW a power of two); a word is wanted if it lies
-// in [0, total) and carries data (word < HWv).  Unwanted slots point at
-// `doff`, a word of the group, so that no two slots of a wave hit one line.
-template <int C>
-__device__ __forceinline__ uint32_t plan_h_round(uint32_t (&off)[C], int base, int tid, int total, int hw_mask,
-                                                 int hwv, uint32_t doff) {
-  uint32_t live = 0;
-#pragma unroll
-  for (int c = 0; c < C; ++c) {
-    const int idx = base + c * kRecThreads + tid;
-    const bool lv = idx < total && (idx & hw_mask) < hwv;
-    off[c] = lv ? (uint32_t)idx : doff;
-    live |= (lv ? 1u : 0u) << c;
-  }
-  return live;
-}
-
-// Backward round plan: word idx = jg' * nel + e, e = jj * NB + bl; the word
-// is partial[jg'][unit j0 + jj][row bl] of the group's exchange block
-// [nJG][Hp][NB], i.e. at jg' * Hp * NB + j0 * NB + e.
-template <int C>
-__device__ __forceinline__ uint32_t plan_dh_round(uint32_t (&off)[C], int base, int tid, int gtotal, int nel, int lg_nel,
-                                                  int NB, int lg_nb, int j0, int b0, int B, int H, int HpNB,
-                                                  uint32_t doff) {
-  uint32_t live = 0;
-#pragma unroll
-  for (int c = 0; c < C; ++c) {
-    const int idx = base + c * kRecThreads + tid;
-    const int e = idx & (nel - 1), g2 = idx >> lg_nel;
-    const int bl = e & (NB - 1), uu = j0 + (e >> lg_nb);
-    const bool lv = idx < gtotal && b0 + bl < B && uu < H;
-    off[c] = lv ? (uint32_t)g2 * (uint32_t)HpNB + (uint32_t)(j0 * NB + e) : doff;
-    live |= (lv ? 1u : 0u) << c;
-  }
-  return live;
-}
-
-template <typename T>
-__device__ __forceinline__ float ldf(const void* p, int64_t i) {
-  return Elem<T>::to_f(((const T*)p)[i]);
-}
 
 // ---------------------------------------------------------------------------
 template <typename T, int NBT, int NKBW, int C>
@@ -183,7 +50,9 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_rec_kernel(FwdArgs a) {
   constexpr int KB = Mfma<T>::kBlock;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int fr = lane & 15, fq = lane >> 4;
-  const int bg = blockIdx.x / a.nJG, jg = blockIdx.x % a.nJG;
+  int bg, jg;
+  take_role(a.nBG, a.nJG, a.nxcd, a.local, bg, jg);
+  const bool local = a.local != 0;
   const int b0 = bg * a.NB, j0 = jg * a.NJ;
   const int MT = a.NJ / 4;                   // M-tiles (16 interleaved gate rows = 4 units)
   const int KS = kWaves / MT;                // waves splitting k per M-tile
@@ -260,6 +129,7 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_rec_kernel(FwdArgs a) {
     __syncthreads();  // previous step's readers of Hl are done
     // h_{t-1} -> LDS
     if (t == 0) {
+      wait_vmem();
       for (int idx = tid; idx < NBv * a.H; idx += kRecThreads) {
         const int bl = idx / a.H, k = idx % a.H;
         const T v = a.h0 ? ((const T*)a.h0)[(int64_t)(b0 + bl) * a.H + k] : T(0);
@@ -281,6 +151,10 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_rec_kernel(FwdArgs a) {
         issue_tagged<C>(wv, src, off);
       }
     }
+    // Everything this wave issued before (last step's stores, the input
+    // prefetch) has completed by now; saying so keeps the compiler from
+    // waiting for stores before it reuses their registers below.
+    wait_vmem();
     stamp(a.stamps, a.T, t, 1);
     __syncthreads();
     stamp(a.stamps, a.T, t, 2);
@@ -345,11 +219,10 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_rec_kernel(FwdArgs a) {
           const uint32_t next = (uint32_t)__shfl_down((int)mine, 16, 64);
           if ((fq & 1) == 0 && valid) {
             const uint32_t both = mine | ((u + 1 < a.H) ? (next << 16) : 0u);
-            __hip_atomic_store(dst + (int64_t)b * a.HW + u / 2, ((uint64_t)(t + 1) << 32) | both,
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            xstore_word(dst + (int64_t)b * a.HW + u / 2, ((uint64_t)(t + 1) << 32) | both, local);
           }
         } else {
-          if (valid) xstore(dst + (int64_t)b * a.HW + u, h, (uint32_t)(t + 1));
+          if (valid) xstore(dst + (int64_t)b * a.HW + u, h, (uint32_t)(t + 1), local);
         }
         if (valid) {
           const int64_t o = (int64_t)t * a.B + b;
@@ -374,14 +247,25 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_rec_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-template <typename T, int NKBR, int MTW, int C>
+// VNCT > 0 selects the VALU form of the partial product (fp32, batch groups
+// of 4 rows; a 16x16 MFMA tile would leave 12 of its 16 batch columns empty
+// there): lane quad qd = t/4 owns the W_h columns 256*i + 4*qd + {0..3}
+// (i < VNCT), lane p = t%4 of the quad the row chunk [p*VR/4, (p+1)*VR/4)
+// of the VR = 4*NJ rows of the work-group's units, kept in VGPRs.  Each lane
+// forms the 16 (column, batch row) pieces of its chunk with fp32 FMAs --
+// one LDS value of dG feeds four columns -- and a reduce-scatter across the
+// quad (DPP) leaves lane p with the four batch-row sums of column
+// 256*i + 4*qd + p, stored as 32 contiguous bytes.
+template <typename T, int NKBR, int MTW, int C, int VNCT = 0, int VR = 0>
 __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int E = sizeof(T);
   constexpr int KB = Mfma<T>::kBlock;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int fr = lane & 15, fq = lane >> 4;
-  const int bg = blockIdx.x / a.nJG, jg = blockIdx.x % a.nJG;
+  int bg, jg;
+  take_role(a.nBG, a.nJG, a.nxcd, a.local, bg, jg);
+  const bool local = a.local != 0;
   const int b0 = bg * a.NB, j0 = jg * a.NJ;
   const int NBT = a.NB < 16 ? 1 : a.NB / 16;
   const int NBr = a.NB < 16 ? 16 : a.NB;     // rows of the batch tiles (rows >= NB stay zero)
@@ -397,14 +281,31 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
   for (int idx = tid; idx < NBr * strideD / 4; idx += kRecThreads) ((uint32_t*)Dl)[idx] = 0u;
   const int64_t G4 = 4 * (int64_t)a.H;
   const int gtotal = a.nJG * nel;                      // exchange words read per step
-  const int nBG = a.Bp / a.NB;
+  const int nBG = a.nBG;
   const int HpNB = a.Hp * a.NB;                        // words of one producer's block
   const uint32_t doff = (uint32_t)(tid % gtotal);      // target of unused load slots
   bool dead = false;
 
   // --- resident fragments of W_h^T: A[m = column k][kslot = row r], column
   // tile of fragment i is w + kWaves*i
-  u32x4_t wreg[MTW * NKBR];
+  u32x4_t wreg[VNCT ? 1 : MTW * NKBR];
+  constexpr int VRC = VNCT ? VR / 4 : 1;  // rows per quad lane
+  float wq[VNCT ? VNCT : 1][4][VRC];
+  const int qd = tid >> 2, qp = tid & 3;
+  if constexpr (VNCT > 0) {
+#pragma unroll
+    for (int i = 0; i < VNCT; ++i)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) {
+        const int k = kRecThreads * i + 4 * qd + cc;
+#pragma unroll
+        for (int rr = 0; rr < VRC; ++rr) {
+          const int r = qp * VRC + rr, ur = j0 + (r >> 2), g = r & 3;
+          wq[i][cc][rr] = (k < a.H && ur < a.H) ? ldf<T>(a.W, ((int64_t)g * a.H + ur) * a.Z + k) : 0.f;
+        }
+      }
+  }
+  if constexpr (VNCT == 0)
 #pragma unroll
   for (int i = 0; i < MTW; ++i) {
 #pragma unroll
@@ -422,9 +323,12 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
   }
 
   // --- elementwise ownership: elements e = tid + 256*s (s < EPT), batch fastest
-  float dcc[4], dhc[4];
+  // (EPTM bounds EPT at compile time: batch groups of 4 rows have at most 64
+  // elements per work-group)
+  constexpr int EPTM = VNCT ? 1 : 4;
+  float dcc[EPTM], dhc[EPTM];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < EPTM; ++s) {
     const int e = tid + kRecThreads * s;
     const int b = b0 + (e & (a.NB - 1)), uu = j0 + (e >> lgNB);
     const bool valid = s < EPT && e < nel && b < a.B && uu < a.H;
@@ -434,28 +338,36 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
 
   // Elementwise operands of a step (activated gates, c_t, c_{t-1}, dy_t) are
   // prefetched one step ahead, at the end of the step before.
-  float pg[4][4], pc[4], pcp[4], pdy[4];
-  auto load_ops = [&](int tt) {
+  float pg[EPTM][4], pc[EPTM], pcp[EPTM], pdy[EPTM];
+  bool own[EPTM];
+  int64_t g_off[EPTM], c_off[EPTM];  // element offsets in Gs and in [B][H] tensors
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int e = tid + kRecThreads * s;
-      const int bl = e & (a.NB - 1), uu = j0 + (e >> lgNB);
-      const int b = b0 + bl;
+  for (int s = 0; s < EPTM; ++s) {
+    const int e = tid + kRecThreads * s;
+    const int b = b0 + (e & (a.NB - 1)), uu = j0 + (e >> lgNB);
+    own[s] = s < EPT && e < nel && b < a.B && uu < a.H;
+    g_off[s] = (int64_t)b * G4 + 4 * (int64_t)uu;
+    c_off[s] = (int64_t)b * a.H + uu;
+  }
+  const int64_t stepG = (int64_t)a.B * G4, stepC = (int64_t)a.B * a.H;
+  auto load_ops = [&](int tt) {
+    const int64_t oG = (int64_t)tt * stepG, oC = (int64_t)tt * stepC;
+#pragma unroll
+    for (int s = 0; s < EPTM; ++s) {
       pg[s][0] = pg[s][1] = pg[s][2] = pg[s][3] = 0.f;
       pc[s] = pcp[s] = pdy[s] = 0.f;
-      if (tt >= 0 && s < EPT && e < nel && b < a.B && uu < a.H) {
-        const int64_t o = (int64_t)tt * a.B + b;
+      if (tt >= 0 && own[s]) {
         if constexpr (E == 4) {
-          const f32x4_t gv = *(const f32x4_t*)((const T*)a.Gs + o * G4 + 4 * (int64_t)uu);
+          const f32x4_t gv = *(const f32x4_t*)((const T*)a.Gs + oG + g_off[s]);
           pg[s][0] = gv[0]; pg[s][1] = gv[1]; pg[s][2] = gv[2]; pg[s][3] = gv[3];
         } else {
-          const uint64_t raw = *(const uint64_t*)((const T*)a.Gs + o * G4 + 4 * (int64_t)uu);
+          const uint64_t raw = *(const uint64_t*)((const T*)a.Gs + oG + g_off[s]);
           pg[s][0] = bf2f((bf16_t)raw); pg[s][1] = bf2f((bf16_t)(raw >> 16));
           pg[s][2] = bf2f((bf16_t)(raw >> 32)); pg[s][3] = bf2f((bf16_t)(raw >> 48));
         }
-        pc[s] = a.Cs[o * a.H + uu];
-        pcp[s] = tt > 0 ? a.Cs[(o - a.B) * a.H + uu] : (a.c0 ? ldf<T>(a.c0, (int64_t)b * a.H + uu) : 0.f);
-        pdy[s] = ldf<T>(a.dy, o * a.H + uu);
+        pc[s] = a.Cs[oC + c_off[s]];
+        pcp[s] = tt > 0 ? a.Cs[oC - stepC + c_off[s]] : (a.c0 ? ldf<T>(a.c0, c_off[s]) : 0.f);
+        pdy[s] = ldf<T>(a.dy, oC + c_off[s]);
       }
     }
   };
@@ -477,6 +389,7 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
       live = plan_dh_round<C>(off, 0, tid, gtotal, nel, lgNel, a.NB, lgNB, j0, b0, a.B, a.H, HpNB, doff);
       issue_tagged<C>(wv, src, off);
     }
+    if (!gather) wait_vmem();
     if (gather) {
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
       for (int base = 0;;) {
@@ -484,11 +397,15 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
 #pragma unroll
         for (int c = 0; c < C; ++c) {
           const float v = ((live >> c) & 1u) ? xval(wv[c]) : 0.f;
-          const int slot = ((base / kRecThreads) + c) & (EPT - 1);
-          acc[0] += slot == 0 ? v : 0.f;
-          acc[1] += slot == 1 ? v : 0.f;
-          acc[2] += slot == 2 ? v : 0.f;
-          acc[3] += slot == 3 ? v : 0.f;
+          if constexpr (EPTM == 1) {
+            acc[0] += v;
+          } else {
+            const int slot = ((base / kRecThreads) + c) & (EPT - 1);
+            acc[0] += slot == 0 ? v : 0.f;
+            acc[1] += slot == 1 ? v : 0.f;
+            acc[2] += slot == 2 ? v : 0.f;
+            acc[3] += slot == 3 ? v : 0.f;
+          }
         }
         base += kRecThreads * C;
         if (base >= gtotal) break;
@@ -498,10 +415,10 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
       // sums[s][tid] holds this thread's part of element tid + 256*s (EPT > 1),
       // or of element tid % nel (TPE > 1)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) sums[kRecThreads * s + tid] = acc[s];
+      for (int s = 0; s < EPTM; ++s) sums[kRecThreads * s + tid] = acc[s];
       __syncthreads();
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
+      for (int s = 0; s < EPTM; ++s) {
         const int e = tid + kRecThreads * s;
         if (s < EPT && e < nel) {
           float v = 0.f;
@@ -512,11 +429,12 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
       __syncthreads();
     }
     if (t < 0) break;
+    wait_vmem();  // as in the forward: nothing of the last step is outstanding
     stamp(a.stamps, a.T, step, 1);
 
     // 2. gate deltas of this step
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < EPTM; ++s) {
       const int e = tid + kRecThreads * s;
       if (s < EPT && e < nel) {
         const int bl = e & (a.NB - 1), jj = e >> lgNB;
@@ -553,7 +471,66 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
 
     // 3. partial[k][b] = sum_{r in my rows} W_h[r][k] dG[b][r], all k < H
     uint64_t* dst = a.PX + (((int64_t)(t & 1) * nBG + bg) * a.nJG + jg) * HpNB;
-    for (int nt = 0; nt < NBT; ++nt) {
+    if constexpr (VNCT > 0) {
+      // NB == 4: pieces acc[i][column cc][batch row] over this lane's rows
+      float acc[VNCT][4][4];
+#pragma unroll
+      for (int i = 0; i < VNCT; ++i)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) acc[i][cc][0] = acc[i][cc][1] = acc[i][cc][2] = acc[i][cc][3] = 0.f;
+#pragma unroll
+      for (int r4 = 0; r4 < VRC / 4; ++r4) {
+        f32x4_t dv[4];
+#pragma unroll
+        for (int bl = 0; bl < 4; ++bl) dv[bl] = *(const f32x4_t*)(Dl + bl * strideD + (qp * VRC + 4 * r4) * 4);
+#pragma unroll
+        for (int i = 0; i < VNCT; ++i)
+#pragma unroll
+          for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+            for (int bl = 0; bl < 4; ++bl)
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) acc[i][cc][bl] = fmaf(wq[i][cc][4 * r4 + rr], dv[bl][rr], acc[i][cc][bl]);
+      }
+      const uint64_t tg = (uint64_t)(t + 1) << 32;
+      const int qb1 = (qp >> 1) & 1, qb0 = qp & 1;
+#pragma unroll
+      for (int i = 0; i < VNCT; ++i) {
+        // quad bit 1: keep columns 2*qb1 + {0,1}; bit 0: keep column qp
+        float fin[4];
+#pragma unroll
+        for (int bl = 0; bl < 4; ++bl) {
+          float k2[2];
+#pragma unroll
+          for (int cl = 0; cl < 2; ++cl) {
+            const float keep = qb1 ? acc[i][2 + cl][bl] : acc[i][cl][bl];
+            const float send = qb1 ? acc[i][cl][bl] : acc[i][2 + cl][bl];
+            k2[cl] = keep + quad_dpp<0x4E>(send);  // quad_perm [2,3,0,1]
+          }
+          const float keep = qb0 ? k2[1] : k2[0];
+          const float send = qb0 ? k2[0] : k2[1];
+          fin[bl] = keep + quad_dpp<0xB1>(send);  // quad_perm [1,0,3,2]
+        }
+        const int k = kRecThreads * i + 4 * qd + qp;
+        if (k < a.H) {
+          uint64_t* q = dst + (int64_t)k * 4;
+          const uint64_t w0 = tg | __float_as_uint(fin[0]), w1 = tg | __float_as_uint(fin[1]);
+          const uint64_t w2 = tg | __float_as_uint(fin[2]), w3 = tg | __float_as_uint(fin[3]);
+          if (local) {
+            // two 16-byte stores; each 8-byte word lands whole
+            typedef __attribute__((__vector_size__(2 * sizeof(uint64_t)))) uint64_t u64x2_t;
+            *(u64x2_t*)q = u64x2_t{w0, w1};
+            *(u64x2_t*)(q + 2) = u64x2_t{w2, w3};
+          } else {
+            xstore_word(q, w0, false);
+            xstore_word(q + 1, w1, false);
+            xstore_word(q + 2, w2, false);
+            xstore_word(q + 3, w3, false);
+          }
+        }
+      }
+    }
+    if constexpr (VNCT == 0) for (int nt = 0; nt < NBT; ++nt) {
       u32x4_t breg[NKBR];
 #pragma unroll
       for (int kb = 0; kb < NKBR; ++kb)
@@ -569,7 +546,7 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int k = 16 * (w + kWaves * i) + 4 * fq + e;
-            if (k < a.H) xstore(dst + (int64_t)k * a.NB + bl, acc[e], (uint32_t)(t + 1));
+            if (k < a.H) xstore(dst + (int64_t)k * a.NB + bl, acc[e], (uint32_t)(t + 1), local);
           }
         }
       }
@@ -595,7 +572,7 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
 
   // dh0 / dc0
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
+  for (int s = 0; s < EPTM; ++s) {
     const int e = tid + kRecThreads * s;
     const int b = b0 + (e & (a.NB - 1)), uu = j0 + (e >> lgNB);
     if (s < EPT && e < nel && b < a.B && uu < a.H) {
@@ -606,27 +583,6 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// The persistent kernels need every work-group of the grid resident at
-// once.  The grid never exceeds the CU count and each work-group fits a CU
-// on its own; the occupancy query confirms that the device can hold the
-// whole grid before the kernel is dispatched as an ordinary launch (a
-// cooperative launch would guarantee the same but costs about 15 us more per
-// dispatch).  If other work holds CUs, the waiting work-groups spin until it
-// drains; every wait is bounded (kWaitTicks) and reports LSTM_ERR_TIMEOUT.
-template <typename K>
-static hipError_t coop_launch(K kernel, int grid, size_t lds, void* arg, hipStream_t s) {
-  hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  void* args[] = {arg};
-  int per_cu = 0, dev = 0, cus = 0;
-  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kernel, kRecThreads, lds)) != hipSuccess)
-    return e;
-  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-  if (per_cu < 1 || (int64_t)per_cu * cus < grid) return hipErrorCooperativeLaunchTooLarge;
-  return hipLaunchKernel((const void*)kernel, dim3(grid), dim3(kRecThreads), args, lds, s);
-}
-
 template <typename T, int NBT, int C>
 static hipError_t fwd_dispatch_c(const Plan& p, FwdArgs& a, hipStream_t s) {
   switch (p.fwd_nkbw) {
@@ -652,7 +608,8 @@ hipError_t launch_fwd_recurrent(const Plan& p, const float* P, const void* W, co
                                 void* y, void* hT, void* cT, void* Gs, float* Cs, uint64_t* HX, uint32_t* err,
                                 uint64_t* stamps, hipStream_t s) {
   FwdArgs a{P, W, h0, c0, y, hT, cT, Gs, Cs, HX, err, stamps, (int)p.T, (int)p.B, (int)p.H, (int)p.Z, p.NB, p.NJ,
-            p.nJG, p.Hp, p.Bp, p.dtype ? (p.Hp / 2) : p.Hp};
+            p.nJG, p.Hp, p.Bp, p.dtype ? (p.Hp / 2) : p.Hp, p.nBG, p.nxcd, p.xcd_local};
+  if (fwd_vec_ok(p)) return launch_fwd_vec(p, a, s);
   const int nbt = p.NB < 16 ? 1 : p.NB / 16;
   if (p.dtype) {
     if (nbt == 1) return fwd_dispatch<bf16_t, 1>(p, a, s);
@@ -695,8 +652,28 @@ hipError_t launch_bwd_recurrent(const Plan& p, const void* W, const void* c0, co
                                 const void* dcT, const void* Gs, const float* Cs, void* dG, uint64_t* PX, float* DBP,
                                 void* dh0, void* dc0, uint32_t* err, uint64_t* stamps, hipStream_t s) {
   BwdArgs a{W, c0, dy, dhT, dcT, Gs, Cs, dG, PX, DBP, dh0, dc0, err, stamps, (int)p.T, (int)p.B, (int)p.H, (int)p.Z,
-            p.NB, p.NJ, p.nJG, p.Hp, p.Bp};
+            p.NB, p.NJ, p.nJG, p.Hp, p.Bp, p.nBG, p.nxcd, p.xcd_local};
   const int nkbr = 4 * p.NJ * p.esize / 64;
+  if (p.dtype == 0 && p.NB == 4) {
+    // VALU partial product: columns per thread x rows <= 128 resident floats
+    // (spill-free instantiations only; other shapes take the MFMA form)
+    const int vnct = p.Hp <= kRecThreads ? 1 : p.Hp / kRecThreads;
+    const int C = p.words_per_thread <= 4 ? 4 : 16;
+    if (p.NJ == 8 && C == 4) {
+      if (vnct == 1) return coop_launch(bwd_rec_kernel<float, 1, 1, 4, 1, 32>, p.grid, p.lds_bwd, &a, s);
+      if (vnct == 2) return coop_launch(bwd_rec_kernel<float, 1, 1, 4, 2, 32>, p.grid, p.lds_bwd, &a, s);
+      if (vnct == 4) return coop_launch(bwd_rec_kernel<float, 1, 1, 4, 4, 32>, p.grid, p.lds_bwd, &a, s);
+    }
+    if (p.NJ == 8 && C == 16) {
+      if (vnct == 1) return coop_launch(bwd_rec_kernel<float, 1, 1, 16, 1, 32>, p.grid, p.lds_bwd, &a, s);
+      if (vnct == 2) return coop_launch(bwd_rec_kernel<float, 1, 1, 16, 2, 32>, p.grid, p.lds_bwd, &a, s);
+      if (vnct == 4) return coop_launch(bwd_rec_kernel<float, 1, 1, 16, 4, 32>, p.grid, p.lds_bwd, &a, s);
+    }
+    if (p.NJ == 16 && vnct == 1) {
+      if (C == 4) return coop_launch(bwd_rec_kernel<float, 1, 1, 4, 1, 64>, p.grid, p.lds_bwd, &a, s);
+      return coop_launch(bwd_rec_kernel<float, 1, 1, 16, 1, 64>, p.grid, p.lds_bwd, &a, s);
+    }
+  }
   if (p.dtype) {
     if (nkbr == 1) return bwd_dispatch<bf16_t, 1>(p, a, s);
     if (nkbr == 2) return bwd_dispatch<bf16_t, 2>(p, a, s);

@@ -1,0 +1,206 @@
+// recurrent_common.hpp -- pieces shared by the persistent recurrent kernels
+// (recurrent.hip: MFMA products; recurrent_vec.hip: VALU products for
+// small batch groups): launch arguments, the work-group roles, the bounded
+// tagged-word waits and the exchange round plans.
+#pragma once
+#include "device_common.hpp"
+#include "internal.hpp"
+
+namespace lstm {
+
+constexpr int kWaves = 4;                 // waves per work-group
+constexpr int kRecThreads = 64 * kWaves;
+
+struct FwdArgs {
+  const float* P;   // [TB][4H] fp32, interleaved gates, bias included
+  const void* W;    // [4H][H+I]
+  const void* h0;   // [B][H] or null
+  const void* c0;   // [B][H] or null
+  void* y;          // [T][B][H]
+  void* hT;         // [B][H]
+  void* cT;         // [B][H]
+  void* Gs;         // [TB][4H] activated gates, interleaved
+  float* Cs;        // [TB][H] cell states
+  uint64_t* HX;     // [2][Bp][HW] exchange words
+  uint32_t* err;
+  uint64_t* stamps; // optional [kStampWGs][T][kPhases] clock stamps
+  int T, B, H, Z, NB, NJ, nJG, Hp, Bp, HW;
+  int nBG, nxcd, local;
+};
+
+struct BwdArgs {
+  const void* W;
+  const void* c0;
+  const void* dy;   // [T][B][H]
+  const void* dhT;  // [B][H] or null
+  const void* dcT;  // [B][H] or null
+  const void* Gs;
+  const float* Cs;
+  void* dG;         // [TB][4H] gate deltas, interleaved
+  uint64_t* PX;     // [2][nBG][nJG][Hp][NB] exchange words (fp32 partials)
+  float* DBP;       // [nBG][4H] per-batch-group db partials, interleaved gates
+  void* dh0;
+  void* dc0;
+  uint32_t* err;
+  uint64_t* stamps;
+  int T, B, H, Z, NB, NJ, nJG, Hp, Bp;
+  int nBG, nxcd, local;
+};
+
+// Phase stamps: thread 0 of the first kStampWGs work-groups records the
+// 100 MHz real-time clock (s_memrealtime) at kPhases points of every step when
+// a stamp buffer is given; slot layout [wg][step][phase], steps in execution
+// order.
+__device__ __forceinline__ void stamp(uint64_t* buf, int T, int step, int phase) {
+  if (buf && threadIdx.x == 0 && blockIdx.x < kStampWGs)
+    buf[((int64_t)blockIdx.x * T + step) * kPhases + phase] = __builtin_amdgcn_s_memrealtime();
+}
+
+__device__ __forceinline__ bool err_set(uint32_t* err) {
+  return __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
+}
+
+// Role of this work-group: (batch group, unit group).  In the XCD-local
+// layout, XCD x holds batch groups [x*nBG/nxcd, (x+1)*nBG/nxcd) whole.  The
+// device deals the work-groups of a dispatch to its XCDs round robin from a
+// starting XCD that varies between dispatches, so work-group i runs on XCD
+// (s + i) % nxcd and i / nxcd numbers the work-groups of one XCD without
+// repeats; the XCD itself is read from the hardware.  (Were the dealing
+// ever different, two work-groups could take one role -- they would compute
+// and write the same values -- and another role would stay empty, which
+// the bounded waits report as a time-out; results are never mixed.)
+__device__ __forceinline__ void take_role(int nBG, int nJG, int nxcd, int local, int& bg, int& jg) {
+  const int i = blockIdx.x;
+  if (!local) {
+    bg = i / nJG;
+    jg = i % nJG;
+    return;
+  }
+  const int x = (int)(xcc_id() % (uint32_t)nxcd), k = i / nxcd;
+  bg = x * (nBG / nxcd) + k / nJG;
+  jg = k % nJG;
+}
+
+// Tagged-word reads, in two halves so that independent loads can be issued
+// between them: issue_tagged() sends the C loads of a thread at once;
+// complete_tagged() waits until every wanted word (bit c of `live`) carries
+// `tag`, re-polling all still-missing words once per round trip.  Loads
+// retire in order, so anything issued after issue_tagged() does not delay
+// the check.  The wait is bounded: past kWaitTicks (or once another thread
+// has recorded an error) the error word is set and `dead` makes this and
+// every later wait of the thread return at once.
+template <int C>
+__device__ __forceinline__ void issue_tagged(uint64_t (&wv)[C], const uint64_t* base, const uint32_t (&off)[C]) {
+#pragma unroll
+  for (int c = 0; c < C; ++c) wv[c] = xload(base + off[c]);
+}
+
+template <int C>
+__device__ __forceinline__ void complete_tagged(uint64_t (&wv)[C], const uint64_t* base, const uint32_t (&off)[C],
+                                                uint32_t live, uint32_t tag, uint32_t* err, bool& dead) {
+  if (dead) {
+    wait_vmem();
+    return;
+  }
+  uint64_t t0 = 0;
+  uint32_t rounds = 0;
+  while (true) {
+    uint32_t pending = 0;
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+      if (((live >> c) & 1u) && xtag(wv[c]) != tag) pending |= 1u << c;
+    if (!pending) return;
+    if (t0 == 0) {
+      t0 = now_ticks();
+    } else if ((++rounds & 15u) == 0 && (now_ticks() - t0 > kWaitTicks || err_set(err))) {
+      atomicOr(err, kErrTimeout);
+      dead = true;
+      wait_vmem();
+      return;
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+      if ((pending >> c) & 1u) wv[c] = xload(base + off[c]);
+  }
+}
+
+// Forward round plan: word idx = base + c*256 + tid of the group's rows
+// (idx = row * HW + word, HW a power of two); a word is wanted if it lies
+// in [0, total) and carries data (word < HWv).  Unwanted slots point at
+// `doff`, a word of the group, so that no two slots of a wave hit one line.
+template <int C>
+__device__ __forceinline__ uint32_t plan_h_round(uint32_t (&off)[C], int base, int tid, int total, int hw_mask,
+                                                 int hwv, uint32_t doff) {
+  uint32_t live = 0;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int idx = base + c * kRecThreads + tid;
+    const bool lv = idx < total && (idx & hw_mask) < hwv;
+    off[c] = lv ? (uint32_t)idx : doff;
+    live |= (lv ? 1u : 0u) << c;
+  }
+  return live;
+}
+
+// Backward round plan: word idx = jg' * nel + e, e = jj * NB + bl; the word
+// is partial[jg'][unit j0 + jj][row bl] of the group's exchange block
+// [nJG][Hp][NB], i.e. at jg' * Hp * NB + j0 * NB + e.
+template <int C>
+__device__ __forceinline__ uint32_t plan_dh_round(uint32_t (&off)[C], int base, int tid, int gtotal, int nel, int lg_nel,
+                                                  int NB, int lg_nb, int j0, int b0, int B, int H, int HpNB,
+                                                  uint32_t doff) {
+  uint32_t live = 0;
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int idx = base + c * kRecThreads + tid;
+    const int e = idx & (nel - 1), g2 = idx >> lg_nel;
+    const int bl = e & (NB - 1), uu = j0 + (e >> lg_nb);
+    const bool lv = idx < gtotal && b0 + bl < B && uu < H;
+    off[c] = lv ? (uint32_t)g2 * (uint32_t)HpNB + (uint32_t)(j0 * NB + e) : doff;
+    live |= (lv ? 1u : 0u) << c;
+  }
+  return live;
+}
+
+template <typename T>
+__device__ __forceinline__ float ldf(const void* p, int64_t i) {
+  return Elem<T>::to_f(((const T*)p)[i]);
+}
+
+// The persistent kernels need every work-group of the grid resident at
+// once.  The grid never exceeds the CU count and each work-group fits a CU
+// on its own; the occupancy query confirms that the device can hold the
+// whole grid before the kernel is dispatched as an ordinary launch (a
+// cooperative launch would guarantee the same but costs about 15 us more per
+// dispatch).  If other work holds CUs, the waiting work-groups spin until it
+// drains; every wait is bounded (kWaitTicks) and reports LSTM_ERR_TIMEOUT.
+// The LDS request is raised to at least kOneGroupLds, more than half a CU's
+// LDS, so that two work-groups never share a CU (they would share its SIMDs
+// and serialise each other's steps).
+constexpr size_t kOneGroupLds = 82 * 1024;
+template <typename K>
+inline hipError_t coop_launch(K kernel, int grid, size_t lds, void* arg, hipStream_t s) {
+  if (lds < kOneGroupLds) lds = kOneGroupLds;
+  hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  void* args[] = {arg};
+  int per_cu = 0, dev = 0, cus = 0;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kernel, kRecThreads, lds)) != hipSuccess)
+    return e;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  if (per_cu < 1 || (int64_t)per_cu * cus < grid) return hipErrorCooperativeLaunchTooLarge;
+  return hipLaunchKernel((const void*)kernel, dim3(grid), dim3(kRecThreads), args, lds, s);
+}
+
+// v of another lane of the quad (DPP quad_perm control CTRL).
+template <int CTRL>
+__device__ __forceinline__ float quad_dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// VALU forward for fp32 batch groups of 4 rows (recurrent_vec.hip)
+bool fwd_vec_ok(const Plan& p);
+hipError_t launch_fwd_vec(const Plan& p, FwdArgs& a, hipStream_t s);
+
+}  // namespace lstm
