@@ -41,6 +41,9 @@ struct Plan {
   // workspace (byte offsets, 256-aligned)
   size_t off_ctrl, off_P, off_G, off_C, off_HX, off_PX, off_dbp, total;
   size_t bytes_HX, bytes_PX;
+  // flag exchange (MFMA kernels): packed payload at the start of the HX / PX
+  // region, step flags at these byte offsets inside it
+  size_t off_hflags, off_pflags;
   int cus;          // compute units of the device
   int max_splits;   // largest split-K factor of the three products
   size_t off_gp;    // fp32 split-K partials of the products

@@ -95,10 +95,19 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
   p->xcd_local = p->nxcd > 1 && p->nBG % p->nxcd == 0;
 
   const size_t HW = dtype ? (size_t)p->Hp / 2 : (size_t)p->Hp;
+  // HX: tagged words [2][Bp][HW], or packed h [2][Bp][Hp] + flags [nBG][nJG];
+  // PX: tagged words [2][nBG][nJG][Hp][NB], or packed fp32 partials
+  // [2][nBG][nJG][NB][Hp] + flags [nBG][nJG]
+  p->off_hflags = align256(2 * (size_t)p->Bp * p->Hp * e);
+  p->off_pflags = align256(2 * (size_t)p->nBG * p->nJG * p->NB * p->Hp * 4);
+  const size_t nflag = align256((size_t)p->nBG * p->nJG * 4);
+  size_t hx = 2 * (size_t)p->Bp * HW * 8, px = 2 * (size_t)p->nJG * p->Hp * p->Bp * 8;
+  if (hx < p->off_hflags + nflag) hx = p->off_hflags + nflag;
+  if (px < p->off_pflags + nflag) px = p->off_pflags + nflag;
   size_t off = 0;
   p->off_ctrl = off; off += 256;
-  p->off_HX = off; p->bytes_HX = align256(2 * (size_t)p->Bp * HW * 8); off += p->bytes_HX;
-  p->off_PX = off; p->bytes_PX = align256(2 * (size_t)p->nJG * p->Hp * p->Bp * 8); off += p->bytes_PX;
+  p->off_HX = off; p->bytes_HX = align256(hx); off += p->bytes_HX;
+  p->off_PX = off; p->bytes_PX = align256(px); off += p->bytes_PX;
   p->off_P = off; off += align256((size_t)p->TB * p->G4 * 4);
   p->off_G = off; off += align256((size_t)p->TB * p->G4 * e);
   p->off_C = off; off += align256((size_t)p->TB * H * 4);

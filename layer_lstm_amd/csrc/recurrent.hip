@@ -93,11 +93,13 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_rec_kernel(FwdArgs a) {
     const int b = b0 + 16 * nt + fr;
     cst[nt] = (a.c0 && u < a.H && 16 * nt + fr < NBv) ? ldf<T>(a.c0, (int64_t)b * a.H + u) : 0.f;
   }
-  constexpr int vpw = (E == 2) ? 2 : 1;                  // values per exchange word
-  const int HWv = (a.H + vpw - 1) / vpw;                 // words per row carrying data
-  const int lgHW = 31 - __builtin_clz(a.HW);             // HW is a power of two
-  const int total = NBv << lgHW;                         // exchange words read per step
-  const uint32_t doff = (uint32_t)(tid % total);         // target of unused load slots
+  // packed h ring: row b of slot s at byte ((s * Bp + b) * Hp) * E; the chunks
+  // covering [0, H) of the group's valid rows are read each step
+  const int rowB = a.Hp * E;                              // bytes per row
+  const int cpr = (a.H * E + 15) / 16;                    // 16-byte chunks per row with data
+  const int nchunk = NBv * cpr;
+  const __amdgpu_buffer_rsrc_t hd_rsrc = make_rsrc(a.HD, a.hd_bytes);
+  T* HDt = (T*)a.HD;
 
   // The input projection of this lane's elements is prefetched one step
   // ahead (at the end of the previous step), so that no wait of a step on its
@@ -116,17 +118,9 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_rec_kernel(FwdArgs a) {
 
   for (int t = 0; t < a.T; ++t) {
     stamp(a.stamps, a.T, t, 0);
-    // h_{t-1} words: word idx = bl * HW + kw of this group's rows (HW a power
-    // of two); slots past the data point at a harmless word of the group
-    const uint64_t* src = a.HX + ((int64_t)((t - 1) & 1) * a.Bp + b0) * a.HW;
-    uint32_t off[C];
-    uint32_t live = 0;
-    uint64_t wv[C];
-    if (t > 0) {
-      live = plan_h_round<C>(off, 0, tid, total, a.HW - 1, HWv, doff);
-      issue_tagged<C>(wv, src, off);
-    }
-    __syncthreads();  // previous step's readers of Hl are done
+    // wait until every work-group of the batch group has published h_{t-1}
+    if (t > 0 && tid < a.nJG) wait_flag(a.HF + bg * a.nJG + tid, (uint32_t)t, a.err, dead);
+    __syncthreads();  // flags seen; the previous step's readers of Hl are done
     // h_{t-1} -> LDS
     if (t == 0) {
       wait_vmem();
@@ -136,19 +130,21 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_rec_kernel(FwdArgs a) {
         *(T*)(Hl + bl * strideH + k * E) = v;
       }
     } else {
-      for (int base = 0;;) {
-        complete_tagged<C>(wv, src, off, live, (uint32_t)t, a.err, dead);
+      const uint32_t slot0 = (uint32_t)(((t - 1) & 1) * a.Bp + b0) * (uint32_t)rowB;
+      for (int q0 = 0; q0 < nchunk; q0 += kRecThreads * C) {
+        u32x4_t v[C];
 #pragma unroll
         for (int c = 0; c < C; ++c) {
-          if ((live >> c) & 1u) {
-            const int bl = off[c] >> lgHW, kw = off[c] & (a.HW - 1);
-            *(uint32_t*)(Hl + bl * strideH + kw * 4) = (uint32_t)wv[c];  // one fp32 or two bf16
-          }
+          const int q = q0 + c * kRecThreads + tid;
+          const int bl = q / cpr, cc = q - bl * cpr;
+          v[c] = q < nchunk ? load16_coherent(hd_rsrc, slot0 + (uint32_t)(bl * rowB + cc * 16)) : u32x4_t{0, 0, 0, 0};
         }
-        base += kRecThreads * C;
-        if (base >= total) break;
-        live = plan_h_round<C>(off, base, tid, total, a.HW - 1, HWv, doff);
-        issue_tagged<C>(wv, src, off);
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          const int q = q0 + c * kRecThreads + tid;
+          const int bl = q / cpr, cc = q - bl * cpr;
+          if (q < nchunk) *(u32x4_t*)(Hl + bl * strideH + cc * 16) = v[c];
+        }
       }
     }
     // Everything this wave issued before (last step's stores, the input
@@ -200,30 +196,40 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_rec_kernel(FwdArgs a) {
     }
 
     stamp(a.stamps, a.T, t, 4);
-    // elementwise: gates, cell, hidden; outputs and the exchange word
+    // elementwise: gates, cell, hidden; h_t is published first (stores, their
+    // completion, then the flag), the other outputs after
+    float gv[NBT][4], cv[NBT];
+    T hv[NBT];
     if (wk == 0) {
-      uint64_t* dst = a.HX + (int64_t)(t & 1) * a.Bp * a.HW;
+      T* dst = HDt + (int64_t)(t & 1) * a.Bp * a.Hp;
 #pragma unroll
       for (int nt = 0; nt < NBT; ++nt) {
         const int b = b0 + 16 * nt + fr;
         const bool valid = u < a.H && 16 * nt + fr < NBv;
         const f32x4_t z = acc[nt] + pf[nt];
-        const float ig = sigmoidf(z[0]), fg = sigmoidf(z[1]), gg = tanh_f(z[2]), og = sigmoidf(z[3]);
-        const float c = fg * cst[nt] + ig * gg;
-        const float h = og * tanh_f(c);
+        gv[nt][0] = sigmoidf(z[0]);
+        gv[nt][1] = sigmoidf(z[1]);
+        gv[nt][2] = tanh_f(z[2]);
+        gv[nt][3] = sigmoidf(z[3]);
+        const float c = gv[nt][1] * cst[nt] + gv[nt][0] * gv[nt][2];
+        const float h = gv[nt][3] * tanh_f(c);
         cst[nt] = c;
-        const T hq = Elem<T>::from_f(h);
-        if constexpr (E == 2) {
-          // pack units u (even lane group) and u+1 (next lane group) into one word
-          const uint32_t mine = (uint32_t)__builtin_bit_cast(uint16_t, hq);
-          const uint32_t next = (uint32_t)__shfl_down((int)mine, 16, 64);
-          if ((fq & 1) == 0 && valid) {
-            const uint32_t both = mine | ((u + 1 < a.H) ? (next << 16) : 0u);
-            xstore_word(dst + (int64_t)b * a.HW + u / 2, ((uint64_t)(t + 1) << 32) | both, local);
-          }
-        } else {
-          if (valid) xstore(dst + (int64_t)b * a.HW + u, h, (uint32_t)(t + 1), local);
-        }
+        cv[nt] = c;
+        hv[nt] = Elem<T>::from_f(h);
+        if (valid) store_elem<T>(dst + (int64_t)b * a.Hp + u, hv[nt], local);
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+    if (tid == 0) store_flag(a.HF + bg * a.nJG + jg, (uint32_t)(t + 1), local);
+    if (wk == 0) {
+#pragma unroll
+      for (int nt = 0; nt < NBT; ++nt) {
+        const int b = b0 + 16 * nt + fr;
+        const bool valid = u < a.H && 16 * nt + fr < NBv;
+        const float ig = gv[nt][0], fg = gv[nt][1], gg = gv[nt][2], og = gv[nt][3];
+        const float c = cv[nt];
+        const T hq = hv[nt];
         if (valid) {
           const int64_t o = (int64_t)t * a.B + b;
           ((T*)a.y)[o * a.H + u] = hq;
@@ -281,6 +287,11 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
   for (int idx = tid; idx < NBr * strideD / 4; idx += kRecThreads) ((uint32_t*)Dl)[idx] = 0u;
   const int64_t G4 = 4 * (int64_t)a.H;
   const int gtotal = a.nJG * nel;                      // exchange words read per step
+  // flag exchange: 16-byte chunks (row, 4 units) of this work-group's units,
+  // TPC threads per chunk (nel <= 1024, so the sums fit the 4 KB LDS area)
+  const int nchk = nel / 4;
+  const int tpc = nchk >= kRecThreads ? 1 : kRecThreads / nchk;
+  const __amdgpu_buffer_rsrc_t pd_rsrc = make_rsrc(a.PD, a.pd_bytes);
   const int nBG = a.nBG;
   const int HpNB = a.Hp * a.NB;                        // words of one producer's block
   const uint32_t doff = (uint32_t)(tid % gtotal);      // target of unused load slots
@@ -381,16 +392,58 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
     //    always meets the same element slot(s), in increasing jg' order, and
     //    the TPE threads sharing an element are then added in a fixed order.
     const bool gather = t < a.T - 1;
+    if (!gather) wait_vmem();
+    if constexpr (VNCT == 0) {
+      // Flag exchange: the partials of step t+1 sit packed as [producer][row
+      // bl][column k] fp32; the NB*NJ/4 16-byte chunks (bl, 4 units) of this
+      // work-group's units are summed over producers jg' = r, r+TPC, ... by
+      // the TPC threads of a chunk, then over r in LDS, in that fixed order.
+      if (gather) {
+        if (tid < a.nJG) wait_flag(a.PF + bg * a.nJG + tid, (uint32_t)(a.T - t - 1), a.err, dead);
+        __syncthreads();
+        const uint32_t base0 = (uint32_t)((((t + 1) & 1) * nBG + bg) * a.nJG) * (uint32_t)(a.NB * a.Hp * 4);
+        const uint32_t pstride = (uint32_t)(a.NB * a.Hp * 4);  // bytes per producer block
+        for (int qq = tid; qq < tpc * nchk; qq += kRecThreads) {
+          const int q = qq % nchk, r = qq / nchk;     // chunk, producer residue
+          const int bl = q / (a.NJ / 4), jq = q % (a.NJ / 4);
+          const uint32_t off0 = base0 + (uint32_t)((bl * a.Hp + j0 + 4 * jq) * 4);
+          f32x4_t sum = {0.f, 0.f, 0.f, 0.f};
+          for (int g0 = r; g0 < a.nJG; g0 += tpc * C) {
+            u32x4_t v[C];
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+              const int g2 = g0 + c * tpc;
+              v[c] = g2 < a.nJG ? load16_coherent(pd_rsrc, off0 + (uint32_t)g2 * pstride) : u32x4_t{0, 0, 0, 0};
+            }
+#pragma unroll
+            for (int c = 0; c < C; ++c) sum += __builtin_bit_cast(f32x4_t, v[c]);
+          }
+          *(f32x4_t*)(sums + 4 * (r * nchk + q)) = sum;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < EPTM; ++s) {
+          const int e = tid + kRecThreads * s;
+          if (s < EPT && e < nel) {
+            const int bl = e & (a.NB - 1), jj = e >> lgNB;
+            const int q = bl * (a.NJ / 4) + (jj >> 2);
+            float v = 0.f;
+            for (int r = 0; r < tpc; ++r) v += sums[4 * (r * nchk + q) + (jj & 3)];
+            dhc[s] = v;
+          }
+        }
+        __syncthreads();
+      }
+    }
     const uint64_t* src = a.PX + ((int64_t)((t + 1) & 1) * nBG + bg) * a.nJG * HpNB;
     uint32_t off[C];
     uint32_t live = 0;
     uint64_t wv[C];
-    if (gather) {
+    if (VNCT > 0 && gather) {
       live = plan_dh_round<C>(off, 0, tid, gtotal, nel, lgNel, a.NB, lgNB, j0, b0, a.B, a.H, HpNB, doff);
       issue_tagged<C>(wv, src, off);
     }
-    if (!gather) wait_vmem();
-    if (gather) {
+    if (VNCT > 0 && gather) {
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
       for (int base = 0;;) {
         complete_tagged<C>(wv, src, off, live, (uint32_t)(t + 2), a.err, dead);
@@ -535,21 +588,32 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_rec_kernel(BwdArgs a) {
 #pragma unroll
       for (int kb = 0; kb < NKBR; ++kb)
         breg[kb] = *(const u32x4_t*)(Dl + (16 * nt + fr) * strideD + kb * 64 + fq * 16);
-      const int bl = 16 * nt + fr, b = b0 + bl;
-      const bool bvalid = bl < a.NB && b < a.B;
+      const int bl = 16 * nt + fr;
 #pragma unroll
       for (int i = 0; i < MTW; ++i) {
         f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < NKBR; ++kb) acc = Mfma<T>::mac(wreg[i * NKBR + kb], breg[kb], acc);
-        if (bvalid) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int k = 16 * (w + kWaves * i) + 4 * fq + e;
-            if (k < a.H) xstore(dst + (int64_t)k * a.NB + bl, acc[e], (uint32_t)(t + 1), local);
+        if (bl < a.NB) {
+          // 16 bytes: columns k0..k0+3 of row bl, packed
+          const int k0 = 16 * (w + kWaves * i) + 4 * fq;
+          float* q = a.PD + ((((int64_t)(t & 1) * nBG + bg) * a.nJG + jg) * a.NB + bl) * a.Hp + k0;
+          if (local) {
+            *(f32x4_t*)q = acc;
+          } else {
+            const uint64_t lo = (uint64_t)__float_as_uint(acc[0]) | ((uint64_t)__float_as_uint(acc[1]) << 32);
+            const uint64_t hi = (uint64_t)__float_as_uint(acc[2]) | ((uint64_t)__float_as_uint(acc[3]) << 32);
+            __hip_atomic_store((uint64_t*)q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store((uint64_t*)q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
         }
       }
+    }
+    if constexpr (VNCT == 0) {
+      // publish: every partial of this work-group is stored, then the flag
+      wait_vmem();
+      __syncthreads();
+      if (tid == 0) store_flag(a.PF + bg * a.nJG + jg, (uint32_t)(a.T - t), local);
     }
     stamp(a.stamps, a.T, step, 3);
     load_ops(t - 1);
@@ -607,7 +671,9 @@ static hipError_t fwd_dispatch(const Plan& p, FwdArgs& a, hipStream_t s) {
 hipError_t launch_fwd_recurrent(const Plan& p, const float* P, const void* W, const void* h0, const void* c0,
                                 void* y, void* hT, void* cT, void* Gs, float* Cs, uint64_t* HX, uint32_t* err,
                                 uint64_t* stamps, hipStream_t s) {
-  FwdArgs a{P, W, h0, c0, y, hT, cT, Gs, Cs, HX, err, stamps, (int)p.T, (int)p.B, (int)p.H, (int)p.Z, p.NB, p.NJ,
+  char* hd = (char*)HX;  // the packed ring and its flags share the tagged-word region
+  FwdArgs a{P, W, h0, c0, y, hT, cT, Gs, Cs, HX, hd, (uint32_t*)(hd + p.off_hflags), (uint32_t)p.off_hflags, err,
+            stamps, (int)p.T, (int)p.B, (int)p.H, (int)p.Z, p.NB, p.NJ,
             p.nJG, p.Hp, p.Bp, p.dtype ? (p.Hp / 2) : p.Hp, p.nBG, p.nxcd, p.xcd_local};
   if (fwd_vec_ok(p)) return launch_fwd_vec(p, a, s);
   const int nbt = p.NB < 16 ? 1 : p.NB / 16;
@@ -651,7 +717,9 @@ static hipError_t bwd_dispatch(const Plan& p, BwdArgs& a, hipStream_t s) {
 hipError_t launch_bwd_recurrent(const Plan& p, const void* W, const void* c0, const void* dy, const void* dhT,
                                 const void* dcT, const void* Gs, const float* Cs, void* dG, uint64_t* PX, float* DBP,
                                 void* dh0, void* dc0, uint32_t* err, uint64_t* stamps, hipStream_t s) {
-  BwdArgs a{W, c0, dy, dhT, dcT, Gs, Cs, dG, PX, DBP, dh0, dc0, err, stamps, (int)p.T, (int)p.B, (int)p.H, (int)p.Z,
+  char* pd = (char*)PX;
+  BwdArgs a{W, c0, dy, dhT, dcT, Gs, Cs, dG, PX, (float*)pd, (uint32_t*)(pd + p.off_pflags), (uint32_t)p.off_pflags,
+            DBP, dh0, dc0, err, stamps, (int)p.T, (int)p.B, (int)p.H, (int)p.Z,
             p.NB, p.NJ, p.nJG, p.Hp, p.Bp, p.nBG, p.nxcd, p.xcd_local};
   const int nkbr = 4 * p.NJ * p.esize / 64;
   if (p.dtype == 0 && p.NB == 4) {

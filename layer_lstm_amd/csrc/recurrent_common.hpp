@@ -21,7 +21,10 @@ struct FwdArgs {
   void* cT;         // [B][H]
   void* Gs;         // [TB][4H] activated gates, interleaved
   float* Cs;        // [TB][H] cell states
-  uint64_t* HX;     // [2][Bp][HW] exchange words
+  uint64_t* HX;     // [2][Bp][HW] exchange words (tagged-word kernels)
+  void* HD;         // [2][Bp][Hp] packed h ring (flag kernels), T elements
+  uint32_t* HF;     // [nBG][nJG] step flags of the flag kernels
+  uint32_t hd_bytes;
   uint32_t* err;
   uint64_t* stamps; // optional [kStampWGs][T][kPhases] clock stamps
   int T, B, H, Z, NB, NJ, nJG, Hp, Bp, HW;
@@ -37,7 +40,10 @@ struct BwdArgs {
   const void* Gs;
   const float* Cs;
   void* dG;         // [TB][4H] gate deltas, interleaved
-  uint64_t* PX;     // [2][nBG][nJG][Hp][NB] exchange words (fp32 partials)
+  uint64_t* PX;     // [2][nBG][nJG][Hp][NB] exchange words (fp32 partials; tagged-word kernels)
+  float* PD;        // [2][nBG][nJG][NB][Hp] packed fp32 partials (flag kernels)
+  uint32_t* PF;     // [nBG][nJG] step flags of the flag kernels
+  uint32_t pd_bytes;
   float* DBP;       // [nBG][4H] per-batch-group db partials, interleaved gates
   void* dh0;
   void* dc0;
@@ -121,6 +127,60 @@ __device__ __forceinline__ void complete_tagged(uint64_t (&wv)[C], const uint64_
 #pragma unroll
     for (int c = 0; c < C; ++c)
       if ((pending >> c) & 1u) wv[c] = xload(base + off[c]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Flag exchange (the MFMA kernels): a producer writes its payload packed,
+// waits until those stores have completed, and then sets its step flag; a
+// consumer polls the flags of every producer it needs (one thread each) and
+// then reads the payload with 16-byte loads.  Stores and loads are
+// device-coherent (write-through stores, loads that do not hit a stale line)
+// or, in the XCD-local layout, plain stores that stay in the shared L2 --
+// the same pairing as the tagged words.
+__device__ __forceinline__ void store_flag(uint32_t* f, uint32_t v, bool local) {
+  if (local)
+    *f = v;
+  else
+    __hip_atomic_store(f, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Bounded wait until *f >= want; false (and the error word set) past
+// kWaitTicks or once another thread has recorded an error.
+__device__ __forceinline__ bool wait_flag(const uint32_t* f, uint32_t want, uint32_t* err, bool& dead) {
+  if (dead) return false;
+  uint64_t t0 = 0;
+  uint32_t rounds = 0;
+  while (__hip_atomic_load(const_cast<uint32_t*>(f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
+    if (t0 == 0) {
+      t0 = now_ticks();
+    } else if ((++rounds & 15u) == 0 && (now_ticks() - t0 > kWaitTicks || err_set(err))) {
+      atomicOr(err, kErrTimeout);
+      dead = true;
+      return false;
+    }
+  }
+  return true;
+}
+
+// 16 bytes at byte offset `off` of a buffer, read device-coherently (sc1).
+__device__ __forceinline__ u32x4_t load16_coherent(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 16));
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Element store of a packed payload: plain in the XCD-local layout, else
+// device-coherent.
+template <typename T>
+__device__ __forceinline__ void store_elem(T* p, T v, bool local) {
+  if (local) {
+    *p = v;
+  } else if constexpr (sizeof(T) == 2) {
+    __hip_atomic_store((uint16_t*)p, __builtin_bit_cast(uint16_t, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    __hip_atomic_store((uint32_t*)p, __builtin_bit_cast(uint32_t, v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
