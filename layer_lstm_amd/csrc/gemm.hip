@@ -350,30 +350,42 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs<AOp, BOp, Epi> 
 }
 
 // ---------------------------------------------------------------------------
-// bf16 products with K a multiple of 32: 256 x 256 tiles per work-group of
-// 8 waves (2 x 4 of 128 x 64, two waves per SIMD), 32 k per stage, every
-// operand loaded straight into LDS (global_load_lds_dwordx4, no register
-// staging) through a ring of kStages stages -- three stages of loads in
-// flight while one is multiplied.  The large tile halves the bytes loaded
-// per MFMA against 128 x 128 tiles, which is what bounds those (the vector
-// memory path, not the MFMA).
+// Pipelined products (K a multiple of one stage): every operand is loaded
+// straight into LDS (global_load_lds_dwordx4, no register staging) through a
+// ring of kStages stages -- three stages of loads in flight while one is
+// multiplied -- in stages of 64 bytes of k per tile row:
+//   bf16: 256 x 256 tiles, 8 waves (2 x 4 of 128 x 64, two per SIMD), 32 k
+//         per stage; the large tile halves the bytes loaded per MFMA against
+//         128 x 128 tiles, which is what bounds those (the vector memory
+//         path, not the MFMA);
+//   fp32: 128 x 128 tiles, 4 waves (2 x 2 of 64 x 64), 16 k per stage (the
+//         fp32 MFMA needs 16 times fewer bytes per cycle).
+// Both shapes give 512-byte k-rows for r-contiguous operands and two loads
+// per wave per operand and stage.
 //   k-contiguous operand (rows of 64 bytes per stage): 16-byte chunk c of
 //     tile row r sits at position c ^ krow_swz(r), so the rows of an MFMA
 //     fragment read spread over the banks;
-//   r-contiguous operand (k-rows of 256 elements = 512 bytes): chunk c of
-//     k-row kr sits at position c ^ mnrow_swz(kr); an MFMA fragment (16 rows x
-//     8 consecutive k per lane) is assembled by two ds_read_b64_tr_b16 from
-//     this [k][r] layout -- lane L of each 16-lane group points at k-row
-//     kb + L/4, columns 4*(L%4)..+3, and receives row L's four k values --
-//     so both layouts feed the same fragments.
+//   r-contiguous operand (512-byte k-rows): chunk c of k-row kr sits at
+//     position c ^ mnrow_swz(kr); a fragment (16 rows x 16 bytes of
+//     consecutive k per lane) is assembled from this [k][r] layout -- bf16:
+//     two ds_read_b64_tr_b16, lane L of each 16-lane group pointing at
+//     k-row kb + L/4, columns 4*(L%4)..+3, and receiving row L's four k
+//     values; fp32: four 4-byte reads -- so both layouts feed the same
+//     fragments.
 // Tile rows or columns past the operand are loaded from its last valid rows
 // (their outputs are never stored); an absent operand block (zero initial
 // state) is loaded from a 16-byte zero word.
 constexpr int kStages = 4;
-constexpr int kLdsThreads = 512;
 static_assert(kStages == 4, "the stage waits in gemm_lds_kernel assume a 4-stage ring");
-constexpr int kLdsTile = 256;
-constexpr int kStageBytes = 2 * kLdsTile * 64;  // A and B tiles of one stage (32 k of bf16)
+
+template <typename T> struct LdsCfg;
+template <> struct LdsCfg<bf16_t> {
+  static constexpr int kTile = 256, kWaves = 8, kThreads = 512, kKStage = 32;
+};
+template <> struct LdsCfg<float> {
+  static constexpr int kTile = 128, kWaves = 4, kThreads = 256, kKStage = 16;
+};
+template <typename T> constexpr int lds_stage_bytes() { return 2 * LdsCfg<T>::kTile * 64; }
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
@@ -387,29 +399,31 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 __device__ __forceinline__ int krow_swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int mnrow_swz(int kr) { return ((kr & 3) | (((kr >> 3) & 1) << 2)) << 1; }
 
-// 256 rows x 64 bytes: 16 loads of 16 rows, 2 per wave
-template <class Op>
+// kTile rows x 64 bytes: loads of 16 rows, 2 per wave
+template <typename T, class Op>
 __device__ __forceinline__ void dma_krows(const Op& op, char* lds, int64_t row0, int64_t k0, int w, int lane) {
+  constexpr int VEC = 16 / sizeof(T);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int r = 32 * w + 16 * j + (lane >> 2), c = (lane & 3) ^ krow_swz(r);
     int64_t gr = row0 + r;
     gr = gr < op.R ? gr : op.R - 1;
-    const bf16_t* src = op.row(gr) + k0 + c * 8;
+    const T* src = op.row(gr) + k0 + c * VEC;
     __builtin_amdgcn_global_load_lds((const void*)src, (void*)(lds + (32 * w + 16 * j) * 64), 16, 0, 0);
   }
 }
 
-// 32 k-rows x 512 bytes: 16 loads of 2 k-rows, 2 per wave
-template <class Op>
+// kKStage k-rows x 512 bytes: loads of 2 k-rows, 2 per wave
+template <typename T, class Op>
 __device__ __forceinline__ void dma_mnrows(const Op& op, char* lds, int64_t r0, int64_t k0, int w, int lane,
                                            const void* zero16) {
+  constexpr int VEC = 16 / sizeof(T);
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int kr = 4 * w + 2 * j + (lane >> 5), c = (lane & 31) ^ mnrow_swz(kr);
-    int64_t r = r0 + c * 8;
-    r = r + 8 <= op.R ? r : op.R - 8;
-    const bf16_t* src = op.krow(k0 + kr, r);
+    int64_t r = r0 + c * VEC;
+    r = r + VEC <= op.R ? r : op.R - VEC;
+    const T* src = op.krow(k0 + kr, r);
     __builtin_amdgcn_global_load_lds(src ? (const void*)src : zero16, (void*)(lds + (4 * w + 2 * j) * 512), 16, 0,
                                      0);
   }
@@ -419,32 +433,48 @@ __device__ __forceinline__ u32x4_t frag_krows(const char* lds, int row, int c) {
   return *(const u32x4_t*)(lds + row * 64 + ((c ^ krow_swz(row)) << 4));
 }
 
+template <typename T>
 __device__ __forceinline__ u32x4_t frag_mnrows(const char* lds, int rbase, int lane) {
-  const int grp = lane >> 4, L = lane & 15;
-  const int m = rbase + 4 * (L & 3), c = m >> 3;
   u32x4_t out;
+  if constexpr (sizeof(T) == 2) {
+    const int grp = lane >> 4, L = lane & 15;
+    const int m = rbase + 4 * (L & 3), c = m >> 3;
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    const int kr = 8 * grp + 4 * hh + (L >> 2);
-    const char* p = lds + kr * 512 + ((c ^ mnrow_swz(kr)) << 4) + ((m & 7) << 1);
-    const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
-    const uint2 u = __builtin_bit_cast(uint2, v);
-    out[2 * hh] = u.x;
-    out[2 * hh + 1] = u.y;
+    for (int hh = 0; hh < 2; ++hh) {
+      const int kr = 8 * grp + 4 * hh + (L >> 2);
+      const char* p = lds + kr * 512 + ((c ^ mnrow_swz(kr)) << 4) + ((m & 7) << 1);
+      const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+      const uint2 u = __builtin_bit_cast(uint2, v);
+      out[2 * hh] = u.x;
+      out[2 * hh + 1] = u.y;
+    }
+  } else {
+    // lane (fr, fq): row rbase + fr, k = 4 fq + s for s = 0..3
+    const int m = rbase + (lane & 15), c = m >> 2, fq = lane >> 4;
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      const int kr = 4 * fq + sl;
+      out[sl] = *(const uint32_t*)(lds + kr * 512 + ((c ^ mnrow_swz(kr)) << 4) + ((m & 3) << 2));
+    }
   }
   return out;
 }
 
-template <int AMN, int BMN, class AOp, class BOp, class Epi>
-__global__ void __launch_bounds__(kLdsThreads, 1) gemm_lds_kernel(GemmArgs<AOp, BOp, Epi> g, const void* zero16) {
+template <typename T, int AMN, int BMN, class AOp, class BOp, class Epi>
+__global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_kernel(GemmArgs<AOp, BOp, Epi> g,
+                                                                         const void* zero16) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  constexpr int TILE = LdsCfg<T>::kTile, NT = LdsCfg<T>::kThreads, KST = LdsCfg<T>::kKStage;
+  constexpr int STAGE = lds_stage_bytes<T>();
+  constexpr int WGN = LdsCfg<T>::kWaves / 2;  // waves along n (2 along m)
+  constexpr int WM = TILE / 2 / 16, WN = TILE / WGN / 16;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   if ((int)blockIdx.z == g.splits) {  // extra duties: clearing, db sum
     const int64_t nblk = (int64_t)gridDim.x * gridDim.y;
     const int64_t blk = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-    for (int64_t i = blk * kLdsThreads + tid; i < g.zero_words; i += nblk * kLdsThreads) g.zero[i] = 0u;
+    for (int64_t i = blk * NT + tid; i < g.zero_words; i += nblk * NT) g.zero[i] = 0u;
     if (g.dsum_out) {
-      for (int64_t n = blk * kLdsThreads + tid; n < g.dsum_cols; n += nblk * kLdsThreads) {
+      for (int64_t n = blk * NT + tid; n < g.dsum_cols; n += nblk * NT) {
         float v = 0.f;
         for (int r = 0; r < g.dsum_rows; ++r) v += g.dsum[(int64_t)r * g.dsum_cols + n];
         const int64_t row = gate_row(n, g.dsum_H);
@@ -454,31 +484,31 @@ __global__ void __launch_bounds__(kLdsThreads, 1) gemm_lds_kernel(GemmArgs<AOp, 
     }
     return;
   }
-  const int wm = w >> 2, wn = w & 3, fr = lane & 15, fq = lane >> 4;
-  const int64_t m0 = (int64_t)blockIdx.y * kLdsTile, n0 = (int64_t)blockIdx.x * kLdsTile;
+  const int wm = w / WGN, wn = w % WGN, fr = lane & 15, fq = lane >> 4;
+  const int64_t m0 = (int64_t)blockIdx.y * TILE, n0 = (int64_t)blockIdx.x * TILE;
   const int split = blockIdx.z;
-  const int64_t ktiles = g.K / 32;
+  const int64_t ktiles = g.K / KST;
   const int64_t kt_begin = (int64_t)split * g.ktiles_per_split;
   const int64_t kt_end = kt_begin + g.ktiles_per_split < ktiles ? kt_begin + g.ktiles_per_split : ktiles;
 
   auto issue = [&](int64_t kt) {
-    char* st = smem + (int)((kt - kt_begin) % kStages) * kStageBytes;
-    if constexpr (AMN) dma_mnrows(g.a, st, m0, kt * 32, w, lane, zero16);
-    else dma_krows(g.a, st, m0, kt * 32, w, lane);
-    if constexpr (BMN) dma_mnrows(g.b, st + kStageBytes / 2, n0, kt * 32, w, lane, zero16);
-    else dma_krows(g.b, st + kStageBytes / 2, n0, kt * 32, w, lane);
+    char* st = smem + (int)((kt - kt_begin) % kStages) * STAGE;
+    if constexpr (AMN) dma_mnrows<T>(g.a, st, m0, kt * KST, w, lane, zero16);
+    else dma_krows<T>(g.a, st, m0, kt * KST, w, lane);
+    if constexpr (BMN) dma_mnrows<T>(g.b, st + STAGE / 2, n0, kt * KST, w, lane, zero16);
+    else dma_krows<T>(g.b, st + STAGE / 2, n0, kt * KST, w, lane);
   };
 
-  f32x4_t acc[8][4];
+  f32x4_t acc[WM][WN];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < WM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < WN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   // column terms of this lane's output columns, fetched while the tile runs
-  f32x4_t colt[4];
+  f32x4_t colt[WN];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t n = n0 + wn * 64 + j * 16 + 4 * fq;
+  for (int j = 0; j < WN; ++j) {
+    const int64_t n = n0 + wn * 16 * WN + j * 16 + 4 * fq;
     colt[j] = (g.splits == 1 && (g.N & 3) == 0 && n + 3 < g.N) ? g.epi.col4(n) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
@@ -498,34 +528,34 @@ __global__ void __launch_bounds__(kLdsThreads, 1) gemm_lds_kernel(GemmArgs<AOp, 
     else __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0)
     __builtin_amdgcn_s_barrier();  // also: every wave is done with the stage about to be refilled
     if (kt + kStages - 1 < kt_end) issue(kt + kStages - 1);
-    const char* sa = smem + (int)((kt - kt_begin) % kStages) * kStageBytes;
-    const char* sb = sa + kStageBytes / 2;
-    u32x4_t bfv[4];
+    const char* sa = smem + (int)((kt - kt_begin) % kStages) * STAGE;
+    const char* sb = sa + STAGE / 2;
+    u32x4_t bfv[WN];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if constexpr (BMN) bfv[j] = frag_mnrows(sb, wn * 64 + 16 * j, lane);
-      else bfv[j] = frag_krows(sb, wn * 64 + 16 * j + fr, fq);
+    for (int j = 0; j < WN; ++j) {
+      if constexpr (BMN) bfv[j] = frag_mnrows<T>(sb, wn * 16 * WN + 16 * j, lane);
+      else bfv[j] = frag_krows(sb, wn * 16 * WN + 16 * j + fr, fq);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < WM; ++i) {
       u32x4_t af;
-      if constexpr (AMN) af = frag_mnrows(sa, wm * 128 + 16 * i, lane);
-      else af = frag_krows(sa, wm * 128 + 16 * i + fr, fq);
+      if constexpr (AMN) af = frag_mnrows<T>(sa, wm * 16 * WM + 16 * i, lane);
+      else af = frag_krows(sa, wm * 16 * WM + 16 * i + fr, fq);
       // B as the MFMA's first operand: the tile comes out transposed, lane
       // (fr, fq) holding C[m = .. + fr][n = .. + 4 fq + e], four
       // consecutive columns for one row -- one 16-byte store per tile
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = Mfma<bf16_t>::mac(bfv[j], af, acc[i][j]);
+      for (int j = 0; j < WN; ++j) acc[i][j] = Mfma<T>::mac(bfv[j], af, acc[i][j]);
     }
   }
 
   const bool vec_n = (g.N & 3) == 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < WM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t m = m0 + wm * 128 + i * 16 + fr;
-      const int64_t n = n0 + wn * 64 + j * 16 + 4 * fq;
+    for (int j = 0; j < WN; ++j) {
+      const int64_t m = m0 + wm * 16 * WM + i * 16 + fr;
+      const int64_t n = n0 + wn * 16 * WN + j * 16 + 4 * fq;
       if (m >= g.M || n >= g.N) continue;
       if (vec_n && n + 3 < g.N) {
         if (g.splits > 1) *(f32x4_t*)(g.part + ((int64_t)split * g.M + m) * g.N + n) = acc[i][j];
@@ -610,34 +640,40 @@ static hipError_t run_gemm(const Plan& p, int64_t M, int64_t N, int64_t K, const
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-// Pipelined bf16 path (gemm_lds_kernel): 256 x 256 tiles, 32 k per stage;
-// K is split (powers of two) while the tiles do not cover the CUs and every
-// split keeps at least 16 stages.
+// Pipelined path (gemm_lds_kernel): K is split (powers of two) while the
+// tiles do not cover the CUs and every split keeps at least 8 stages.
+// fp32 products take it only for deep K (>= 1024): with a short K the
+// 64 x 64 tiles of gemm_kernel cover the CUs without a split-K pass.
+template <typename T>
+static bool lds_depth_ok(int64_t K) { return sizeof(T) == 2 || K >= 1024; }
+template <typename T>
 static GemmShape choose_shape_lds(int64_t M, int64_t N, int64_t K, int cus, int max_splits) {
-  const int64_t tiles = ((M + kLdsTile - 1) / kLdsTile) * ((N + kLdsTile - 1) / kLdsTile);
-  const int64_t ktiles = K / 32;
-  GemmShape gs{kLdsTile, 1};
-  while (gs.splits < max_splits && tiles * gs.splits < cus && ktiles / (gs.splits * 2) >= 16) gs.splits *= 2;
+  constexpr int TILE = LdsCfg<T>::kTile;
+  const int64_t tiles = ((M + TILE - 1) / TILE) * ((N + TILE - 1) / TILE);
+  const int64_t ktiles = K / LdsCfg<T>::kKStage;
+  GemmShape gs{TILE, 1};
+  while (gs.splits < max_splits && tiles * gs.splits < cus && ktiles / (gs.splits * 2) >= 8) gs.splits *= 2;
   return gs;
 }
 
-template <int AMN, int BMN, class AOp, class BOp, class Epi>
+template <typename T, int AMN, int BMN, class AOp, class BOp, class Epi>
 static hipError_t run_gemm_lds(const Plan& p, int64_t M, int64_t N, int64_t K, const AOp& a, const BOp& b,
                                const Epi& e, float* part, void* zero, size_t zero_bytes, const void* zero16,
                                hipStream_t s, DbDuty db = DbDuty{nullptr, nullptr, 0, 0, 0, 0}) {
-  const GemmShape gs = choose_shape_lds(M, N, K, p.cus, part ? p.max_splits : 1);
-  const int64_t ktiles = K / 32;
+  constexpr int TILE = LdsCfg<T>::kTile;
+  const GemmShape gs = choose_shape_lds<T>(M, N, K, p.cus, part ? p.max_splits : 1);
+  const int64_t ktiles = K / LdsCfg<T>::kKStage;
   int ktps = (int)((ktiles + gs.splits - 1) / gs.splits);
   if (ktps < 1) ktps = 1;
   GemmArgs<AOp, BOp, Epi> g{M, N, K, ktps, gs.splits, a, b, e, part, (uint32_t*)zero, (int64_t)(zero_bytes / 4),
                             db.src, db.out, db.rows, db.bf16, db.cols, db.H};
   const unsigned gz = (unsigned)gs.splits + ((g.zero_words > 0 || g.dsum_out) ? 1u : 0u);
-  dim3 grid((unsigned)((N + kLdsTile - 1) / kLdsTile), (unsigned)((M + kLdsTile - 1) / kLdsTile), gz);
-  const size_t lds = (size_t)kStages * kStageBytes;
-  auto fn = gemm_lds_kernel<AMN, BMN, AOp, BOp, Epi>;
+  dim3 grid((unsigned)((N + TILE - 1) / TILE), (unsigned)((M + TILE - 1) / TILE), gz);
+  const size_t lds = (size_t)kStages * lds_stage_bytes<T>();
+  auto fn = gemm_lds_kernel<T, AMN, BMN, AOp, BOp, Epi>;
   hipError_t err = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(fn, grid, dim3(kLdsThreads), lds, s, g, zero16);
+  hipLaunchKernelGGL(fn, grid, dim3(LdsCfg<T>::kThreads), lds, s, g, zero16);
   err = hipGetLastError();
   if (err != hipSuccess || gs.splits == 1) return err;
   const int64_t n = M * N;
@@ -652,10 +688,8 @@ static hipError_t inproj_t(const Plan& p, const void* x, const void* W, const vo
   KRowsX<T> a{(const T*)x, p.I, p.TB, p.I, aligned16(x) && p.I % VEC == 0};
   KRowsWx<T> bw{(const T*)W, p.H, p.Z, p.G4, p.I, aligned16(W) && p.Z % VEC == 0 && p.H % VEC == 0};
   EpiP e{P, b, p.H, p.G4, p.dtype};
-  if constexpr (sizeof(T) == 2) {
-    if (p.I % 32 == 0 && p.I > 0 && a.vec_ok && bw.vec_ok && p.TB > 0)
-      return run_gemm_lds<0, 0>(p, p.TB, p.G4, p.I, a, bw, e, part, zero, zero_bytes, zero, s);
-  }
+  if (p.I % LdsCfg<T>::kKStage == 0 && lds_depth_ok<T>(p.I) && a.vec_ok && bw.vec_ok && p.TB > 0)
+    return run_gemm_lds<T, 0, 0>(p, p.TB, p.G4, p.I, a, bw, e, part, zero, zero_bytes, zero, s);
   return run_gemm<T, KRowsX<T>, false, KRowsWx<T>, false, EpiP>(p, p.TB, p.G4, p.I, a, bw, e, part, zero, zero_bytes, s);
 }
 
@@ -666,10 +700,8 @@ static hipError_t dx_t(const Plan& p, const void* dG, const void* W, void* dx, f
   KRowsX<T> a{(const T*)dG, p.G4, p.TB, p.G4, aligned16(dG) && p.G4 % VEC == 0};
   MNRowsWx<T> bw{(const T*)W, p.H, p.Z, p.I, p.G4, aligned16(W) && p.Z % VEC == 0 && p.H % VEC == 0};
   EpiStore<T> e{(T*)dx, p.I};
-  if constexpr (sizeof(T) == 2) {
-    if (p.G4 % 32 == 0 && p.I >= 8 && p.I % 8 == 0 && a.vec_ok && bw.vec_ok && p.TB > 0)
-      return run_gemm_lds<0, 1>(p, p.TB, p.I, p.G4, a, bw, e, part, zero, zero_bytes, zero, s);
-  }
+  if (p.G4 % LdsCfg<T>::kKStage == 0 && lds_depth_ok<T>(p.G4) && p.I >= VEC && a.vec_ok && bw.vec_ok && p.TB > 0)
+    return run_gemm_lds<T, 0, 1>(p, p.TB, p.I, p.G4, a, bw, e, part, zero, zero_bytes, zero, s);
   return run_gemm<T, KRowsX<T>, false, MNRowsWx<T>, true, EpiStore<T>>(p, p.TB, p.I, p.G4, a, bw, e, part, zero,
                                                                        zero_bytes, s);
 }
@@ -684,10 +716,9 @@ static hipError_t dw_t(const Plan& p, const void* dG, const void* x, const void*
                 aligned16(x) && aligned16(y) && (h0 == nullptr || aligned16(h0)) && p.H % VEC == 0 && p.I % VEC == 0};
   EpiDW<T> e{(T*)dW, p.H, p.Z};
   const DbDuty dd{DBP, db, p.nBG, p.G4, p.H, p.dtype};
-  if constexpr (sizeof(T) == 2) {
-    if (p.TB % 32 == 0 && p.TB > 0 && p.Z >= 8 && a.vec_ok && bz.vec_ok && aligned16(zero16))
-      return run_gemm_lds<1, 1>(p, p.G4, p.Z, p.TB, a, bz, e, part, zero, zero_bytes, zero16, s, dd);
-  }
+  if (p.TB % LdsCfg<T>::kKStage == 0 && lds_depth_ok<T>(p.TB) && p.Z >= VEC && a.vec_ok && bz.vec_ok &&
+      aligned16(zero16))
+    return run_gemm_lds<T, 1, 1>(p, p.G4, p.Z, p.TB, a, bz, e, part, zero, zero_bytes, zero16, s, dd);
   return run_gemm<T, MNRowsPlain<T>, true, MNRowsZ<T>, true, EpiDW<T>>(p, p.G4, p.Z, p.TB, a, bz, e, part, zero,
                                                                        zero_bytes, s, dd);
 }
@@ -716,10 +747,9 @@ size_t gemm_partial_bytes(const Plan& p, int cus) {
   for (const auto& sh : shapes) {
     if (sh[0] <= 0 || sh[1] <= 0) continue;
     GemmShape gs = choose_shape(sh[0], sh[1], sh[2], p.esize, cus, p.max_splits);
-    if (p.dtype && sh[2] % 32 == 0) {
-      const GemmShape gl = choose_shape_lds(sh[0], sh[1], sh[2], cus, p.max_splits);
-      if (gl.splits > gs.splits) gs = gl;
-    }
+    const GemmShape gl = p.dtype ? choose_shape_lds<bf16_t>(sh[0], sh[1], sh[2], cus, p.max_splits)
+                                 : choose_shape_lds<float>(sh[0], sh[1], sh[2], cus, p.max_splits);
+    if (gl.splits > gs.splits) gs = gl;
     if (gs.splits > 1) {
       const size_t b = (size_t)gs.splits * sh[0] * sh[1] * 4;
       if (b > mx) mx = b;
