@@ -29,18 +29,24 @@ import statistics
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "layer_lstm_amd", "csrc")
 
-# kernel kind -> (source file, predicate on the demangled kernel name)
+# kernel kind -> (source files the kernel is built from, predicate on the
+# demangled kernel name)
+_REC = ("recurrent.hip", "recurrent_vec.hip", "recurrent_common.hpp", "device_common.hpp", "internal.hpp")
+_GEMM = ("gemm.hip", "device_common.hpp", "internal.hpp")
 KINDS = {
-    "input_projection": ("gemm.hip", lambda n: "gemm_kernel" in n and "EpiP" in n),
-    "forward_recurrence": ("recurrent.hip", lambda n: "fwd_rec_kernel" in n),
-    "backward_recurrence": ("recurrent.hip", lambda n: "bwd_rec_kernel" in n),
-    "dW_product": ("gemm.hip", lambda n: "EpiDW" in n),
-    "dx_product": ("gemm.hip", lambda n: "EpiStore" in n),
+    "input_projection": (_GEMM, lambda n: "gemm" in n and "EpiP" in n),
+    "forward_recurrence": (_REC, lambda n: "fwd_rec_kernel" in n or "fwd_vec_kernel" in n),
+    "backward_recurrence": (_REC, lambda n: "bwd_rec_kernel" in n),
+    "dW_product": (_GEMM, lambda n: "EpiDW" in n and "splitk" not in n),
+    "dx_product": (_GEMM, lambda n: "EpiStore" in n and "splitk" not in n),
 }
 
 
-def source_sha(fname: str) -> str:
-    return hashlib.sha256(open(os.path.join(CSRC, fname), "rb").read()).hexdigest()[:16]
+def source_sha(fnames) -> str:
+    h = hashlib.sha256()
+    for f in fnames:
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def kind_of(name: str):
