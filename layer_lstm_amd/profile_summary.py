@@ -6,6 +6,8 @@ profiles/ and the per-kernel HBM traffic record that bench.py reports.
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \
         --copy-bytes N --out-json profiles/traffic.json --out-txt OUT.txt \
         --command "..." [--command "..."]
+    python -m layer_lstm_amd.profile_summary mfma DIR OUT.txt --workload NAME \
+        --command "..."
 
 `stats` reads <DIR>/*kernel_stats.csv (rocprofv3 --kernel-trace --stats
 --output-format csv) and writes the per-kernel table with the command that
@@ -14,7 +16,9 @@ rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, each for the LSTM step and
 for a plain copy of --copy-bytes bytes), scales each counter by what it reads
 for the copy (known bytes / counted bytes), and records HBM bytes per
 launch for each kernel kind of the path, with the hash of the kernel's
-source so that a record goes stale when the kernel changes.
+source so that a record goes stale when the kernel changes.  `mfma` reads
+one --pmc run of SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE and reports
+the MFMA utilisation of each kernel kind.
 """
 from __future__ import annotations
 
@@ -131,9 +135,45 @@ def cmd_traffic(a):
     print("\n".join(lines))
 
 
+def cmd_mfma(a):
+    """MFMA utilisation per kernel kind from one rocprofv3 --pmc run with
+    SQ_VALU_MFMA_BUSY_CYCLES (busy cycles summed over SIMDs) and
+    GRBM_GUI_ACTIVE (active cycles summed over the XCDs):
+    utilisation = busy / (active / xcds * simds)."""
+    rows = list(csv.DictReader(open(find_csv(a.dir, "counter_collection.csv"))))
+    per = {}
+    for r in rows:
+        k = kind_of(r["Kernel_Name"])
+        if k is None:
+            continue
+        key = (k, r["Dispatch_Id"])
+        per.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    agg = {}
+    for (k, _), d in per.items():
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in d and "GRBM_GUI_ACTIVE" in d and d["GRBM_GUI_ACTIVE"] > 0:
+            u = d["SQ_VALU_MFMA_BUSY_CYCLES"] / (d["GRBM_GUI_ACTIVE"] / a.xcds * a.simds)
+            agg.setdefault(k, []).append(u)
+    lines = ["# MFMA utilisation per kernel from rocprofv3 counters", "", "command:", ""]
+    lines += [f"    {c}" for c in a.command] + [""]
+    lines.append(f"utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / {a.xcds} XCDs x {a.simds} SIMDs)")
+    lines.append(f"workload {a.workload}")
+    lines.append(f"{'kernel kind':22s} {'launches':>8s} {'MFMA busy':>10s}")
+    for k, v in agg.items():
+        lines.append(f"{k:22s} {len(v):8d} {100 * statistics.median(v):9.1f}%")
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
+    mm = sub.add_parser("mfma")
+    mm.add_argument("dir")
+    mm.add_argument("out")
+    mm.add_argument("--workload", required=True)
+    mm.add_argument("--xcds", type=int, default=8)
+    mm.add_argument("--simds", type=int, default=1024)
+    mm.add_argument("--command", action="append", default=[])
     s = sub.add_parser("stats")
     s.add_argument("dir")
     s.add_argument("out")
@@ -147,7 +187,7 @@ def main():
     t.add_argument("--out-txt", required=True)
     t.add_argument("--command", action="append", default=[])
     a = ap.parse_args()
-    cmd_stats(a) if a.cmd == "stats" else cmd_traffic(a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "mfma": cmd_mfma}[a.cmd](a)
 
 
 if __name__ == "__main__":
