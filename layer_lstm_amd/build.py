@@ -17,7 +17,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblstm.so")
-SOURCES = ["lstm_api.hip", "gemm.hip", "recurrent.hip", "recurrent_vec.hip"]
+SOURCES = ["lstm_api.hip", "gemm.hip", "recurrent.hip", "recurrent_vec.hip", "recurrent_bwd.hip"]
 ARCH = "gfx950"
 
 

@@ -26,8 +26,11 @@ struct Plan {
   // [jg*NJ, (jg+1)*NJ)
   int NB, NJ, nBG, nJG, grid;
   int Hp;       // H rounded up to a power of two (>= 4 MFMA k-blocks)
+  int waves;    // waves per work-group of the MFMA recurrences (4 or 8)
   int fwd_nkbw; // forward: W_h k-blocks per wave
-  int bwd_mtw;  // backward: 16-column tiles of W_h^T per wave
+  int bwd_mt;   // backward (MFMA): 16-unit tiles of W_h^T per work-group
+  int bwd_nkb;  // backward (MFMA): k-blocks of the 4H gate rows per wave
+  int bwd_valu; // backward runs the VALU kernel (fp32, batch groups of 4 rows)
   int words_per_thread;  // exchange words a thread reads per step (NB*H / 256, rounded up)
   int Bp;       // nBG * NB
   size_t lds_fwd, lds_bwd;
@@ -42,15 +45,26 @@ struct Plan {
   size_t off_ctrl, off_P, off_G, off_C, off_HX, off_PX, off_dbp, total;
   size_t bytes_HX, bytes_PX;
   // flag exchange (MFMA kernels): packed payload at the start of the HX / PX
-  // region, step flags at these byte offsets inside it
+  // region (h ring, gate-delta ring), step flags at these byte offsets
+  // inside it
   size_t off_hflags, off_pflags;
   int cus;          // compute units of the device
   int max_splits;   // largest split-K factor of the three products
   size_t off_gp;    // fp32 split-K partials of the products
 };
 
+// LDS through which the MFMA backward gathers its W_h^T fragments at start.
+constexpr size_t kColStageLds = 80 * 1024;
+
+// Waves of the VALU recurrences and of the 4-wave MFMA ones.
+constexpr int kWaves = 4;
+constexpr int kRecThreads = 64 * kWaves;
+
 // Fill the plan for a shape; returns 0 or an LSTM_ERR_* code.
 int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p);
+
+// The plan runs the VALU forward (fp32 batch groups of 4 rows).
+bool fwd_vec_ok(const Plan& p);
 
 // ---- launchers (return hipError_t) ----
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);

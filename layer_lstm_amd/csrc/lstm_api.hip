@@ -49,35 +49,67 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
   while (Hp < H) Hp *= 2;
   p->Hp = Hp;
 
+  p->cus = cus;
+  p->nxcd = (cus % 32 == 0 && cus >= 32) ? cus / 32 : 1;
+
   // Partition of the persistent kernels.  Every work-group reads NB*H
-  // exchanged values per step, so the fewest batch rows per group that still
-  // fit the grid come first, then the most work-groups.  Fewer than 16 rows
-  // leave part of the 16-row MFMA batch tile empty, which costs little next
-  // to the exchange.
+  // values of h (forward) and NB*4H gate deltas (backward) per step, so the
+  // fewest batch rows per group that still fit the grid come first, then
+  // the most work-groups, then 4 waves before 8 (8 waves -- bf16 only -- hold
+  // twice the W_h slice).  A first pass takes only partitions whose batch
+  // groups divide evenly over the XCDs, so that each group's exchange stays
+  // in one XCD's L2.  Fewer than 16 rows leave part of the 16-row MFMA batch
+  // tile empty, which costs little next to the exchange.
   const int nb_opts[5] = {4, 8, 16, 32, 64};
-  const int nj_opts[2] = {8, 16};
+  const int nj_opts[3] = {8, 16, 32};
+  const int nw_opts[2] = {4, 8};
   bool found = false;
-  for (int a = 0; a < 5 && !found; ++a) {
-    for (int c = 0; c < 2 && !found; ++c) {
-      const int NB = nb_opts[a], NJ = nj_opts[c];
-      const int64_t nBG = B > 0 ? (B + NB - 1) / NB : 1;
-      const int64_t nJG = (H + NJ - 1) / NJ;
-      if (nBG * nJG > cus) continue;
-      const int KS = 4 / (NJ / 4);                        // 4 waves: M-tiles x k parts
-      const int nkbw = Hp / (KS * KB);                    // forward W_h fragments per wave
-      if (nkbw < 1 || nkbw > 32) continue;
-      const int nkbr = 4 * NJ * e / 64;                   // backward: k-blocks of the 4*NJ rows
-      const int mtw = Hp / 64;                            // backward: W_h^T column tiles per wave
-      if (mtw * nkbr > 32) continue;
-      const int NBr = NB < 16 ? 16 : NB;
-      const size_t lds_f = (size_t)NBr * (Hp * e + 16) + (size_t)(4 - NJ / 4) * (NBr / 16) * 1024;
-      if (lds_f > 160 * 1024) continue;
-      p->NB = NB; p->NJ = NJ; p->nBG = (int)nBG; p->nJG = (int)nJG; p->grid = (int)(nBG * nJG);
-      p->fwd_nkbw = nkbw;
-      p->bwd_mtw = mtw;
-      p->lds_fwd = lds_f;
-      p->lds_bwd = (size_t)NBr * (4 * NJ * e + 16) + 4096 + (size_t)NB * NJ * 16;
-      found = true;
+  for (int pass = 0; pass < 2 && !found; ++pass) {
+    for (int a = 0; a < 5 && !found; ++a) {
+      for (int c = 0; c < 3 && !found; ++c) {
+        for (int d = 0; d < 2 && !found; ++d) {
+          const int NB = nb_opts[a], NJ = nj_opts[c], NW = nw_opts[d];
+          if (NW == 8 && !dtype) continue;
+          const int64_t nBG = B > 0 ? (B + NB - 1) / NB : 1;
+          const int64_t nJG = (H + NJ - 1) / NJ;
+          if (nBG * nJG > cus) continue;
+          if (pass == 0 && !(p->nxcd > 1 && nBG % p->nxcd == 0)) continue;
+          const int NBr = NB < 16 ? 16 : NB;
+          // forward: NJ/4 M-tiles of 16 interleaved gate rows, the waves of
+          // an M-tile splitting k
+          const int MTf = NJ / 4;
+          if (MTf > NW) continue;
+          const int KS = NW / MTf;
+          const int nkbw = Hp / (KS * KB);
+          if (nkbw < 1 || nkbw > 32) continue;
+          const size_t lds_f = (size_t)NBr * (Hp * e + 16) + (size_t)MTf * (KS - 1) * (NBr / 16) * 1024;
+          if (lds_f > 160 * 1024) continue;
+          // backward: the VALU kernel (fp32, 4-row groups, <= 128 resident
+          // W_h values per lane) or the MFMA kernel: 16-unit tiles of W_h^T,
+          // the waves splitting the 4H gate rows
+          const int vnct = Hp <= kRecThreads ? 1 : Hp / kRecThreads;
+          const bool valu = !dtype && NB == 4 && NW == 4 && ((NJ == 8 && vnct <= 4) || (NJ == 16 && vnct == 1));
+          const int MTb = NJ < 16 ? 1 : NJ / 16;
+          const int nkb = Hp * e / (16 * NW);
+          size_t lds_b;
+          if (valu) {
+            lds_b = (size_t)NBr * (4 * NJ * e + 16) + 4096 + (size_t)NB * NJ * 16;
+          } else {
+            if (nkb < 1 || MTb * nkb > 32 || NB * NJ > 1024) continue;
+            lds_b = (size_t)NW * NBr * (16 * MTb + 4) * 4 + (size_t)NB * NJ * 16;
+            if (lds_b < kColStageLds) lds_b = kColStageLds;
+          }
+          p->NB = NB; p->NJ = NJ; p->nBG = (int)nBG; p->nJG = (int)nJG; p->grid = (int)(nBG * nJG);
+          p->waves = NW;
+          p->fwd_nkbw = nkbw;
+          p->bwd_valu = valu ? 1 : 0;
+          p->bwd_mt = MTb;
+          p->bwd_nkb = nkb;
+          p->lds_fwd = lds_f;
+          p->lds_bwd = lds_b;
+          found = true;
+        }
+      }
     }
   }
   if (!found) return LSTM_ERR_UNSUPPORTED;
@@ -88,22 +120,21 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
     const int64_t mx = fw > bw ? fw : bw;
     p->words_per_thread = (int)((mx + 255) / 256);
   }
+  if (2 * (int64_t)p->Bp * 4 * Hp * e >= ((int64_t)1 << 31)) return LSTM_ERR_UNSUPPORTED;
 
-  p->cus = cus;
   p->max_splits = 8;
-  p->nxcd = (cus % 32 == 0 && cus >= 32) ? cus / 32 : 1;
   p->xcd_local = p->nxcd > 1 && p->nBG % p->nxcd == 0;
 
   const size_t HW = dtype ? (size_t)p->Hp / 2 : (size_t)p->Hp;
-  // HX: tagged words [2][Bp][HW], or packed h [2][Bp][Hp] + flags [nBG][nJG];
-  // PX: tagged words [2][nBG][nJG][Hp][NB], or packed fp32 partials
-  // [2][nBG][nJG][NB][Hp] + flags [nBG][nJG]
+  // HX: tagged words [2][Bp][HW] (VALU forward), or packed h [2][Bp][Hp] +
+  // flags [nBG][nJG]; PX: tagged words [2][nBG][nJG][Hp][NB] (VALU
+  // backward), or packed gate deltas [2][Bp][4Hp] + flags [nBG][nJG]
   p->off_hflags = align256(2 * (size_t)p->Bp * p->Hp * e);
-  p->off_pflags = align256(2 * (size_t)p->nBG * p->nJG * p->NB * p->Hp * 4);
+  p->off_pflags = align256(2 * (size_t)p->Bp * 4 * p->Hp * e);
   const size_t nflag = align256((size_t)p->nBG * p->nJG * 4);
-  size_t hx = 2 * (size_t)p->Bp * HW * 8, px = 2 * (size_t)p->nJG * p->Hp * p->Bp * 8;
-  if (hx < p->off_hflags + nflag) hx = p->off_hflags + nflag;
-  if (px < p->off_pflags + nflag) px = p->off_pflags + nflag;
+  size_t hx = p->off_hflags + nflag, px = p->off_pflags + nflag;
+  if (fwd_vec_ok(*p) && hx < 2 * (size_t)p->Bp * HW * 8) hx = 2 * (size_t)p->Bp * HW * 8;
+  if (p->bwd_valu && px < 2 * (size_t)p->nJG * p->Hp * p->Bp * 8) px = 2 * (size_t)p->nJG * p->Hp * p->Bp * 8;
   size_t off = 0;
   p->off_ctrl = off; off += 256;
   p->off_HX = off; p->bytes_HX = align256(hx); off += p->bytes_HX;

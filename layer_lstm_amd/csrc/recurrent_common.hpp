@@ -8,9 +8,6 @@
 
 namespace lstm {
 
-constexpr int kWaves = 4;                 // waves per work-group
-constexpr int kRecThreads = 64 * kWaves;
-
 struct FwdArgs {
   const float* P;   // [TB][4H] fp32, interleaved gates, bias included
   const void* W;    // [4H][H+I]
@@ -40,10 +37,10 @@ struct BwdArgs {
   const void* Gs;
   const float* Cs;
   void* dG;         // [TB][4H] gate deltas, interleaved
-  uint64_t* PX;     // [2][nBG][nJG][Hp][NB] exchange words (fp32 partials; tagged-word kernels)
-  float* PD;        // [2][nBG][nJG][NB][Hp] packed fp32 partials (flag kernels)
-  uint32_t* PF;     // [nBG][nJG] step flags of the flag kernels
-  uint32_t pd_bytes;
+  uint64_t* PX;     // [2][nBG][nJG][Hp][NB] exchange words (fp32 partials; VALU kernel)
+  void* GD;         // [2][Bp][4Hp] packed gate deltas, interleaved, T elements (MFMA kernel)
+  uint32_t* GF;     // [nBG][nJG] step flags of the MFMA kernel
+  uint32_t gd_bytes;
   float* DBP;       // [nBG][4H] per-batch-group db partials, interleaved gates
   void* dh0;
   void* dc0;
@@ -239,18 +236,18 @@ __device__ __forceinline__ float ldf(const void* p, int64_t i) {
 // and serialise each other's steps).
 constexpr size_t kOneGroupLds = 82 * 1024;
 template <typename K>
-inline hipError_t coop_launch(K kernel, int grid, size_t lds, void* arg, hipStream_t s) {
+inline hipError_t coop_launch(K kernel, int grid, size_t lds, void* arg, hipStream_t s, int threads = kRecThreads) {
   if (lds < kOneGroupLds) lds = kOneGroupLds;
   hipError_t e = hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   void* args[] = {arg};
   int per_cu = 0, dev = 0, cus = 0;
-  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kernel, kRecThreads, lds)) != hipSuccess)
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void*)kernel, threads, lds)) != hipSuccess)
     return e;
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
   if (per_cu < 1 || (int64_t)per_cu * cus < grid) return hipErrorCooperativeLaunchTooLarge;
-  return hipLaunchKernel((const void*)kernel, dim3(grid), dim3(kRecThreads), args, lds, s);
+  return hipLaunchKernel((const void*)kernel, dim3(grid), dim3(threads), args, lds, s);
 }
 
 // v of another lane of the quad (DPP quad_perm control CTRL).
@@ -259,8 +256,10 @@ __device__ __forceinline__ float quad_dpp(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
 }
 
-// VALU forward for fp32 batch groups of 4 rows (recurrent_vec.hip)
-bool fwd_vec_ok(const Plan& p);
+// VALU recurrences for fp32 batch groups of 4 rows (recurrent_vec.hip)
 hipError_t launch_fwd_vec(const Plan& p, FwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_vec(const Plan& p, BwdArgs& a, hipStream_t s);
+// MFMA backward, column partition (recurrent_bwd.hip)
+hipError_t launch_bwd_col(const Plan& p, BwdArgs& a, hipStream_t s);
 
 }  // namespace lstm

@@ -1,5 +1,5 @@
-// recurrent_vec.hip -- forward recurrence for fp32 storage with batch groups
-// of at most 4 rows, the product on the vector ALUs (gfx950).
+// recurrent_vec.hip -- forward and backward recurrences for fp32 storage
+// with batch groups of 4 rows, the products on the vector ALUs (gfx950).
 //
 // Same step as the MFMA kernel ("SingleLayerLstmGrad" page, forward table:
 // a_t = P_t + W_h h_{t-1}; i,f,o = sigmoid, g = tanh; c_t = f c_{t-1} + i g;
@@ -18,8 +18,10 @@
 //   full sum of gate 2*c[2] + c[1] for batch row 2*c[4] + c[3];
 //   lane c = 8b (b < 4) gathers the four gates of batch row b by DPP and
 //   does the cell update of that (unit, row) element.
-// The exchange (tagged words, XCD-local or device-wide) is the same as in
-// recurrent.hip.
+// Both kernels exchange through tagged 8-byte words (value + step tag,
+// relaxed agent-scope atomics, or plain stores in the XCD-local layout; see
+// device_common.hpp), read with all of a thread's loads of a round in
+// flight at once and only the words whose tag is not there yet polled again.
 #include "recurrent_common.hpp"
 
 namespace lstm {
@@ -241,13 +243,242 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_vec_kernel(FwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Backward ("SingleLayerLstmGrad" page, "反向传播算法" steps 1-6; the step is
+// that of the MFMA kernel in recurrent_bwd.hip) with the partition by gate
+// rows: work-group (bg, jg) forms, for its 4*NJ gate rows, the fp32 partial
+// product W_h[rows]^T dG_t for all H columns and publishes it as tagged words
+// [group][producer][column][row]; every work-group then sums, in a fixed
+// order, the partials of its own units from all producers of the group.  At
+// 4 batch rows the partials are few (nJG*4*NJ words per work-group and
+// step), so this beats gathering the 4H gate deltas of every row.
+//
+// The partial product on the VALUs: lane quad qd = t/4 owns the W_h columns
+// 256*i + 4*qd + {0..3} (i < VNCT), lane p = t%4 of the quad the row chunk
+// [p*VR/4, (p+1)*VR/4) of the VR = 4*NJ rows of the work-group's units,
+// kept in VGPRs.  Each lane forms the 16 (column, batch row) pieces of its
+// chunk with fp32 FMAs -- one LDS value of dG feeds four columns -- and a
+// reduce-scatter across the quad (DPP) leaves lane p with the four
+// batch-row sums of column 256*i + 4*qd + p, stored as 32 contiguous bytes.
+template <int VNCT, int VR, int C>
+__global__ void __launch_bounds__(kRecThreads, 1) bwd_vec_kernel(BwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int tid = threadIdx.x;
+  int bg, jg;
+  take_role(a.nBG, a.nJG, a.nxcd, a.local, bg, jg);
+  const bool local = a.local != 0;
+  const int b0 = bg * a.NB, j0 = jg * a.NJ;
+  const int nel = a.NB * a.NJ;               // (batch row, unit) elements: 32 or 64
+  const int lgNB = 31 - __builtin_clz(a.NB), lgNel = 31 - __builtin_clz(nel);
+  const int TPE = kRecThreads / nel;         // threads per element
+  const int strideD = 4 * a.NJ * 4 + 16;
+  char* Dl = smem;                                     // [4][strideD] gate deltas of the step
+  float* sums = (float*)(smem + 4 * strideD);          // [kRecThreads] gather sums
+  float* dba = sums + kRecThreads;                     // [nel][4] db: gate deltas summed over time
+  for (int idx = tid; idx < 4 * nel; idx += kRecThreads) dba[idx] = 0.f;
+  for (int idx = tid; idx < 4 * strideD / 4; idx += kRecThreads) ((uint32_t*)Dl)[idx] = 0u;
+  const int64_t G4 = 4 * (int64_t)a.H;
+  const int gtotal = a.nJG * nel;                      // exchange words read per step
+  const int nBG = a.nBG;
+  const int HpNB = a.Hp * a.NB;                        // words of one producer's block
+  const uint32_t doff = (uint32_t)(tid % gtotal);      // target of unused load slots
+  bool dead = false;
+
+  constexpr int VRC = VR / 4;  // rows per quad lane
+  float wq[VNCT][4][VRC];
+  const int qd = tid >> 2, qp = tid & 3;
+#pragma unroll
+  for (int i = 0; i < VNCT; ++i)
+#pragma unroll
+    for (int cc = 0; cc < 4; ++cc) {
+      const int k = kRecThreads * i + 4 * qd + cc;
+#pragma unroll
+      for (int rr = 0; rr < VRC; ++rr) {
+        const int r = qp * VRC + rr, ur = j0 + (r >> 2), g = r & 3;
+        wq[i][cc][rr] = (k < a.H && ur < a.H) ? ((const float*)a.W)[((int64_t)g * a.H + ur) * a.Z + k] : 0.f;
+      }
+    }
+
+  // elementwise ownership: thread tid < nel owns element e = tid (batch row
+  // fastest); every thread takes part in the gather
+  const int e = tid;
+  const int bl0 = e & (a.NB - 1), jj0 = e >> lgNB;
+  const int bown = b0 + bl0, uown = j0 + jj0;
+  const bool own = e < nel && bown < a.B && uown < a.H;
+  float dcc = (own && a.dcT) ? ((const float*)a.dcT)[(int64_t)bown * a.H + uown] : 0.f;
+  float dhc = (own && a.dhT) ? ((const float*)a.dhT)[(int64_t)bown * a.H + uown] : 0.f;
+
+  // elementwise operands of a step (activated gates, c_t, c_{t-1}, dy_t),
+  // prefetched one step ahead
+  float pg[4], pc, pcp, pdy;
+  const int64_t g_off = (int64_t)bown * G4 + 4 * (int64_t)uown, c_off = (int64_t)bown * a.H + uown;
+  const int64_t stepG = (int64_t)a.B * G4, stepC = (int64_t)a.B * a.H;
+  auto load_ops = [&](int tt) {
+    pg[0] = pg[1] = pg[2] = pg[3] = 0.f;
+    pc = pcp = pdy = 0.f;
+    if (tt >= 0 && own) {
+      const int64_t oG = (int64_t)tt * stepG, oC = (int64_t)tt * stepC;
+      const f32x4_t gv = *(const f32x4_t*)((const float*)a.Gs + oG + g_off);
+      pg[0] = gv[0]; pg[1] = gv[1]; pg[2] = gv[2]; pg[3] = gv[3];
+      pc = a.Cs[oC + c_off];
+      pcp = tt > 0 ? a.Cs[oC - stepC + c_off] : (a.c0 ? ((const float*)a.c0)[c_off] : 0.f);
+      pdy = ((const float*)a.dy)[oC + c_off];
+    }
+  };
+  load_ops(a.T - 1);
+
+  for (int t = a.T - 1; t >= -1; --t) {
+    const int step = a.T - 1 - (t < 0 ? 0 : t);
+    if (t >= 0) stamp(a.stamps, a.T, step, 0);
+    // 1. gather dh_carry: sum over work-groups of the partials produced at
+    //    step t+1.  Word idx = jg' * nel + e (e = jj * NB + bl): a thread
+    //    always meets the same element, in increasing jg' order, and the TPE
+    //    threads sharing an element are then added in a fixed order.
+    const bool gather = t < a.T - 1;
+    if (!gather) wait_vmem();
+    const uint64_t* src = a.PX + ((int64_t)((t + 1) & 1) * nBG + bg) * a.nJG * HpNB;
+    if (gather) {
+      uint32_t off[C];
+      uint64_t wv[C];
+      uint32_t live = plan_dh_round<C>(off, 0, tid, gtotal, nel, lgNel, a.NB, lgNB, j0, b0, a.B, a.H, HpNB, doff);
+      issue_tagged<C>(wv, src, off);
+      float acc = 0.f;
+      for (int base = 0;;) {
+        complete_tagged<C>(wv, src, off, live, (uint32_t)(t + 2), a.err, dead);
+#pragma unroll
+        for (int c = 0; c < C; ++c) acc += ((live >> c) & 1u) ? xval(wv[c]) : 0.f;
+        base += kRecThreads * C;
+        if (base >= gtotal) break;
+        live = plan_dh_round<C>(off, base, tid, gtotal, nel, lgNel, a.NB, lgNB, j0, b0, a.B, a.H, HpNB, doff);
+        issue_tagged<C>(wv, src, off);
+      }
+      // sums[tid] holds this thread's part of element tid % nel
+      sums[tid] = acc;
+      __syncthreads();
+      if (e < nel) {
+        float v = 0.f;
+        for (int q = 0; q < TPE; ++q) v += sums[tid + q * nel];
+        dhc = v;
+      }
+      __syncthreads();
+    }
+    if (t < 0) break;
+    wait_vmem();  // nothing of the last step is outstanding
+    stamp(a.stamps, a.T, step, 1);
+
+    // 2. gate deltas of this step
+    if (e < nel) {
+      f32x4_t dq = {0.f, 0.f, 0.f, 0.f};
+      if (own) {
+        const int64_t o = (int64_t)t * a.B + bown;
+        const float gi = pg[0], gf = pg[1], gg = pg[2], go = pg[3];
+        const float tc = tanh_f(pc);
+        const float dh = pdy + dhc;
+        const float dc = dh * go * (1.f - tc * tc) + dcc;
+        const float d_o = dh * tc * go * (1.f - go);
+        const float d_g = dc * gi * (1.f - gg * gg);
+        const float d_i = dc * gg * gi * (1.f - gi);
+        const float d_f = dc * pcp * gf * (1.f - gf);
+        dcc = dc * gf;
+        dq = f32x4_t{d_i, d_f, d_g, d_o};
+        *(f32x4_t*)(dba + 4 * e) += dq;
+        *(f32x4_t*)((float*)a.dG + o * G4 + 4 * (int64_t)uown) = dq;
+      }
+      *(f32x4_t*)(Dl + bl0 * strideD + jj0 * 16) = dq;
+    }
+    __syncthreads();
+    stamp(a.stamps, a.T, step, 2);
+
+    // 3. partial[k][b] = sum_{r in my rows} W_h[r][k] dG[b][r], all k < H:
+    //    pieces acc[i][column cc][batch row] over this lane's rows
+    uint64_t* dst = a.PX + (((int64_t)(t & 1) * nBG + bg) * a.nJG + jg) * HpNB;
+    float acc[VNCT][4][4];
+#pragma unroll
+    for (int i = 0; i < VNCT; ++i)
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) acc[i][cc][0] = acc[i][cc][1] = acc[i][cc][2] = acc[i][cc][3] = 0.f;
+#pragma unroll
+    for (int r4 = 0; r4 < VRC / 4; ++r4) {
+      f32x4_t dv[4];
+#pragma unroll
+      for (int bl = 0; bl < 4; ++bl) dv[bl] = *(const f32x4_t*)(Dl + bl * strideD + (qp * VRC + 4 * r4) * 4);
+#pragma unroll
+      for (int i = 0; i < VNCT; ++i)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc)
+#pragma unroll
+          for (int bl = 0; bl < 4; ++bl)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) acc[i][cc][bl] = fmaf(wq[i][cc][4 * r4 + rr], dv[bl][rr], acc[i][cc][bl]);
+    }
+    const uint64_t tg = (uint64_t)(t + 1) << 32;
+    const int qb1 = (qp >> 1) & 1, qb0 = qp & 1;
+#pragma unroll
+    for (int i = 0; i < VNCT; ++i) {
+      // quad bit 1: keep columns 2*qb1 + {0,1}; bit 0: keep column qp
+      float fin[4];
+#pragma unroll
+      for (int bl = 0; bl < 4; ++bl) {
+        float k2[2];
+#pragma unroll
+        for (int cl = 0; cl < 2; ++cl) {
+          const float keep = qb1 ? acc[i][2 + cl][bl] : acc[i][cl][bl];
+          const float send = qb1 ? acc[i][cl][bl] : acc[i][2 + cl][bl];
+          k2[cl] = keep + quad_dpp<kQuadSwap2>(send);
+        }
+        const float keep = qb0 ? k2[1] : k2[0];
+        const float send = qb0 ? k2[0] : k2[1];
+        fin[bl] = keep + quad_dpp<kQuadSwap1>(send);
+      }
+      const int k = kRecThreads * i + 4 * qd + qp;
+      if (k < a.H) {
+        uint64_t* q = dst + (int64_t)k * 4;
+        const uint64_t w0 = tg | __float_as_uint(fin[0]), w1 = tg | __float_as_uint(fin[1]);
+        const uint64_t w2 = tg | __float_as_uint(fin[2]), w3 = tg | __float_as_uint(fin[3]);
+        if (local) {
+          // two 16-byte stores; each 8-byte word lands whole
+          typedef __attribute__((__vector_size__(2 * sizeof(uint64_t)))) uint64_t u64x2_t;
+          *(u64x2_t*)q = u64x2_t{w0, w1};
+          *(u64x2_t*)(q + 2) = u64x2_t{w2, w3};
+        } else {
+          xstore_word(q, w0, false);
+          xstore_word(q + 1, w1, false);
+          xstore_word(q + 2, w2, false);
+          xstore_word(q + 3, w3, false);
+        }
+      }
+    }
+    stamp(a.stamps, a.T, step, 3);
+    load_ops(t - 1);
+    stamp(a.stamps, a.T, step, 4);
+    __syncthreads();  // Dl is rewritten next step
+    stamp(a.stamps, a.T, step, 5);
+  }
+
+  // db partial of this work-group: for each (unit, gate), the sum over its
+  // batch rows (in row order) of the per-element sums over time
+  if (a.DBP) {
+    __syncthreads();
+    for (int r = tid; r < 4 * a.NJ; r += kRecThreads) {
+      const int jj = r >> 2, g = r & 3;
+      float v = 0.f;
+      for (int bl = 0; bl < a.NB; ++bl) v += dba[4 * ((jj << lgNB) + bl) + g];
+      if (j0 + jj < a.H) a.DBP[(int64_t)bg * G4 + 4 * (j0 + jj) + g] = v;
+    }
+  }
+  if (own) {
+    ((float*)a.dh0)[c_off] = dhc;
+    ((float*)a.dc0)[c_off] = dcc;
+  }
+}
+
 // Dispatch: L = max(4, Hp/32) columns per chunk, U2 = NJ/8 units per
 // half-wave; the resident slice 4*U2*L floats per lane is kept at most 64
 // (larger slices spill with the fully unrolled product).
 static int vec_chunk(const Plan& p) { return p.Hp / 32 < 4 ? 4 : p.Hp / 32; }
 
 bool fwd_vec_ok(const Plan& p) {
-  if (p.dtype != 0 || p.NB != 4) return false;
+  if (p.dtype != 0 || p.NB != 4 || p.waves != kWaves) return false;
   const int L = vec_chunk(p), u2 = p.NJ / 8;
   return L <= 16 && (u2 == 1 || u2 == 2) && 4 * u2 * L <= 64;
 }
@@ -271,6 +502,22 @@ hipError_t launch_fwd_vec(const Plan& p, FwdArgs& a, hipStream_t s) {
   const bool wide = p.words_per_thread > 4;
   if (p.NJ == 8) return wide ? fwd_vec_l<1, 16>(p, a, s) : fwd_vec_l<1, 4>(p, a, s);
   return wide ? fwd_vec_l<2, 16>(p, a, s) : fwd_vec_l<2, 4>(p, a, s);
+}
+
+// Backward: VNCT = Hp/256 column groups per thread (at least 1), VR = 4*NJ
+// rows; the make_plan conditions (NJ = 8 with VNCT <= 4, or NJ = 16 with
+// VNCT = 1) keep the resident VNCT*4*VR/4 floats per lane at most 128.
+hipError_t launch_bwd_vec(const Plan& p, BwdArgs& a, hipStream_t s) {
+  const int vnct = p.Hp <= kRecThreads ? 1 : p.Hp / kRecThreads;
+  const bool wide = p.words_per_thread > 4;
+  if (p.NJ == 8) {
+    if (vnct == 1) return coop_launch(wide ? bwd_vec_kernel<1, 32, 16> : bwd_vec_kernel<1, 32, 4>, p.grid, p.lds_bwd, &a, s);
+    if (vnct == 2) return coop_launch(wide ? bwd_vec_kernel<2, 32, 16> : bwd_vec_kernel<2, 32, 4>, p.grid, p.lds_bwd, &a, s);
+    if (vnct == 4) return coop_launch(wide ? bwd_vec_kernel<4, 32, 16> : bwd_vec_kernel<4, 32, 4>, p.grid, p.lds_bwd, &a, s);
+  }
+  if (p.NJ == 16 && vnct == 1)
+    return coop_launch(wide ? bwd_vec_kernel<1, 64, 16> : bwd_vec_kernel<1, 64, 4>, p.grid, p.lds_bwd, &a, s);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace lstm

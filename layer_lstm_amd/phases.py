@@ -18,8 +18,12 @@ import sys
 import numpy as np
 
 FWD_PHASES = ("exchange wait + h load", "barrier", "product", "reduction + gather", "gate math + publish")
-BWD_PHASES = ("exchange wait + dh gather", "gate deltas + barrier", "partial product + publish",
-              "operand prefetch issue", "barrier")
+# backward: the MFMA kernel (column partition, bf16 and most fp32 shapes) and
+# the VALU kernel (fp32 batch groups of 4 rows, the fp32 workloads here)
+BWD_PHASES_MFMA = ("exchange wait (dG flags)", "dG loads + product", "wave reduction", "gate deltas + publish",
+                   "operand prefetch issue")
+BWD_PHASES_VALU = ("exchange wait + dh gather", "gate deltas + barrier", "partial product + publish",
+                   "operand prefetch issue", "barrier")
 
 
 def measure(name: str):
@@ -47,7 +51,8 @@ def measure(name: str):
 def summarize(name, w, s):
     lines = [f"workload {name} (T={w.T} B={w.B} I={w.I} H={w.H} {w.dtype}); microseconds, medians over "
              f"steps 1..T-1 of the stamped work-groups"]
-    for p, (pname, names) in enumerate((("forward", FWD_PHASES), ("backward", BWD_PHASES))):
+    bwd = BWD_PHASES_VALU if w.dtype == "f32" else BWD_PHASES_MFMA
+    for p, (pname, names) in enumerate((("forward", FWD_PHASES), ("backward", bwd))):
         a = s[p]
         valid = [g for g in range(a.shape[0]) if a[g, 0, 0] > 0]
         a = a[valid]

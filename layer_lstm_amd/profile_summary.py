@@ -35,12 +35,13 @@ CSRC = os.path.join(ROOT, "layer_lstm_amd", "csrc")
 
 # kernel kind -> (source files the kernel is built from, predicate on the
 # demangled kernel name)
-_REC = ("recurrent.hip", "recurrent_vec.hip", "recurrent_common.hpp", "device_common.hpp", "internal.hpp")
+_REC = ("recurrent.hip", "recurrent_vec.hip", "recurrent_bwd.hip", "recurrent_common.hpp", "device_common.hpp",
+        "internal.hpp")
 _GEMM = ("gemm.hip", "device_common.hpp", "internal.hpp")
 KINDS = {
     "input_projection": (_GEMM, lambda n: "gemm" in n and "EpiP" in n),
     "forward_recurrence": (_REC, lambda n: "fwd_rec_kernel" in n or "fwd_vec_kernel" in n),
-    "backward_recurrence": (_REC, lambda n: "bwd_rec_kernel" in n),
+    "backward_recurrence": (_REC, lambda n: "bwd_col_kernel" in n or "bwd_vec_kernel" in n),
     "dW_product": (_GEMM, lambda n: "EpiDW" in n and "splitk" not in n),
     "dx_product": (_GEMM, lambda n: "EpiStore" in n and "splitk" not in n),
 }
