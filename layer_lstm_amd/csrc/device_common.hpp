@@ -11,6 +11,9 @@ typedef uint16_t bf16_t;  // bfloat16 bit pattern in memory
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+// operand types of the buffer load / store builtins
+typedef uint32_t v2u32_t __attribute__((ext_vector_type(2)));
+typedef uint32_t v4u32_t __attribute__((ext_vector_type(4)));
 
 // Round fp32 to the nearest bf16, ties to even; NaN -> quiet NaN.
 __device__ __forceinline__ bf16_t f2bf(float f) {
@@ -115,6 +118,11 @@ __device__ __forceinline__ float xval(uint64_t w) { return __uint_as_float((uint
 // must assume some are and waits for all stores before reusing their
 // registers on the common path.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits [3:0] and [15:14],
+// expcnt [6:4], lgkmcnt [11:8]; a field at its maximum does not wait):
+// vmcnt(n) alone, and lgkmcnt(0) alone
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
+constexpr int kLgkm0 = 0xC07F;
 
 // Time bound of one wait: s_memrealtime runs at 100 MHz.
 constexpr uint64_t kWaitTicks = 200000000ull;  // 2 s

@@ -53,7 +53,7 @@ struct Plan {
   size_t off_gp;    // fp32 split-K partials of the products
 };
 
-// LDS through which the MFMA backward gathers its W_h^T fragments at start.
+// LDS through which the MFMA recurrences gather their W_h slices at start.
 constexpr size_t kColStageLds = 80 * 1024;
 
 // Waves of the VALU recurrences and of the 4-wave MFMA ones.

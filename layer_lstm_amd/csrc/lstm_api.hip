@@ -34,6 +34,7 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
   if (dtype != LSTM_F32 && dtype != LSTM_BF16) return LSTM_ERR_DTYPE;
   if (H > 2048 || I > 65536 || T > ((int64_t)1 << 30)) return LSTM_ERR_UNSUPPORTED;
   if (T > 0 && B > 0 && T * B > ((int64_t)1 << 31) / (4 * H)) return LSTM_ERR_UNSUPPORTED;
+  if (B * H >= ((int64_t)1 << 27)) return LSTM_ERR_UNSUPPORTED;  // per-step buffer offsets fit 31 bits
   int cus = 0;
   const int dev = device_cus(&cus);
   if (dev != LSTM_OK) return dev;
@@ -84,6 +85,8 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
           if (nkbw < 1 || nkbw > 32) continue;
           const size_t lds_f = (size_t)NBr * (Hp * e + 16) + (size_t)MTf * (KS - 1) * (NBr / 16) * 1024;
           if (lds_f > 160 * 1024) continue;
+          // the W_h slice is gathered through LDS at the start (recurrent.hip)
+          const size_t lds_fw = lds_f < kColStageLds ? kColStageLds : lds_f;
           // backward: the VALU kernel (fp32, 4-row groups, <= 128 resident
           // W_h values per lane) or the MFMA kernel: 16-unit tiles of W_h^T,
           // the waves splitting the 4H gate rows
@@ -105,7 +108,7 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
           p->bwd_valu = valu ? 1 : 0;
           p->bwd_mt = MTb;
           p->bwd_nkb = nkb;
-          p->lds_fwd = lds_f;
+          p->lds_fwd = lds_fw;
           p->lds_bwd = lds_b;
           found = true;
         }

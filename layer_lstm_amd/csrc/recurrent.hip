@@ -28,8 +28,9 @@
 // recurrent_vec.hip (VALU form for fp32 batch groups of 4 rows).
 //
 // Compile-time shapes (H is padded to Hp, a power of two): NKBW k-blocks of
-// W_h per wave, NBT 16-row batch tiles, C ring chunks in flight per thread,
-// NW waves (8-wave work-groups hold twice the W_h slice of 4-wave ones).
+// W_h per wave, NBT 16-row batch tiles, C ring chunks in flight per thread
+// (0: direct-to-LDS copy), NW waves (8-wave work-groups hold twice the W_h
+// slice of 4-wave ones).
 #include "recurrent_common.hpp"
 
 namespace lstm {
@@ -59,19 +60,40 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
   const int u = j0 + 4 * mt + fq;            // unit of this lane's elementwise results
   bool dead = false;
 
-  // --- resident W_h fragments: rows 16*mt + fr (gate fr&3 of unit 4*mt + fr/4)
+  // --- resident W_h fragments: rows 16*mt + fr (gate fr&3 of unit 4*mt +
+  // fr/4), k-blocks kb0 + i.  Gathered through a wave-private LDS area in
+  // passes of PB k-blocks: the wave reads its 16 rows with consecutive lanes
+  // on consecutive columns, and every lane then takes each of its fragments
+  // with one 16-byte LDS read.
   u32x4_t wreg[NKBW];
   {
-    const int ur = j0 + 4 * mt + (fr >> 2), g = fr & 3;
-    const T* wrow = (const T*)a.W + ((int64_t)g * a.H + ur) * a.Z;
+    constexpr int PB = NKBW < 8 ? NKBW : 8;             // k-blocks per pass (8 KB of LDS per wave)
+    constexpr int CWL = PB * KB;                        // staged columns per row
+    constexpr int RSW = CWL + 16 / E;                   // staged row (elements), padded
+    constexpr int LPT = 16 * CWL / 64;                  // elements each lane loads per pass
+    T* stage = (T*)smem + w * 16 * RSW;
 #pragma unroll
-    for (int i = 0; i < NKBW; ++i) {
-      T tmp[16 / E];
-      const int k = (kb0 + i) * KB + fq * (16 / E);
+    for (int p = 0; p < NKBW / PB; ++p) {
+      T v[LPT];
 #pragma unroll
-      for (int e = 0; e < 16 / E; ++e) tmp[e] = (ur < a.H && k + e < a.H) ? wrow[k + e] : T(0);
-      wreg[i] = __builtin_bit_cast(u32x4_t, tmp);
+      for (int j = 0; j < LPT; ++j) {
+        const int e = lane + 64 * j, row = e / CWL, col = e % CWL;
+        const int ur = j0 + 4 * mt + (row >> 2), g = row & 3;
+        const int k = (kb0 + p * PB) * KB + col;
+        const bool ok = ur < a.H && k < a.H;
+        v[j] = ((const T*)a.W)[ok ? ((int64_t)g * a.H + ur) * a.Z + k : 0];
+        v[j] = ok ? v[j] : T(0);
+      }
+#pragma unroll
+      for (int j = 0; j < LPT; ++j) {
+        const int e = lane + 64 * j;
+        stage[(e / CWL) * RSW + e % CWL] = v[j];
+      }
+#pragma unroll
+      for (int ii = 0; ii < PB; ++ii)
+        wreg[p * PB + ii] = *(const u32x4_t*)(stage + fr * RSW + ii * KB + fq * (16 / E));
     }
+    __syncthreads();  // the staging area is reused below
   }
   const int NBv = (a.B - b0) < a.NB ? (a.B - b0) : a.NB;  // valid rows of this group
   // --- zero the padding of h_{t-1} in LDS once (k >= H, rows past the group or B)
@@ -94,58 +116,118 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
   const __amdgpu_buffer_rsrc_t hd_rsrc = make_rsrc(a.HD, a.hd_bytes);
   T* HDt = (T*)a.HD;
 
-  // The input projection of this lane's elements is prefetched one step
-  // ahead (at the end of the previous step), so that no wait of a step on its
-  // exchange words or its product also waits for this load.
-  f32x4_t pf[NBT];
-  auto load_p = [&](int tt) {
+  // Memory traffic off the exchange path: the input projection P_{t+1} and
+  // the step's record (y_t, the activated gates, c_t) are issued right after
+  // the ring reads of the next step.  A wave's vector-memory operations
+  // complete in issue order, so operations issued before the ring reads
+  // would hold up the wait for them; issued after, they drain while the
+  // product runs.  Each lane of a wk == 0 wave issues exactly kDefer of them
+  // per step, whatever its element's validity (buffer operations out of
+  // range do nothing), which lets the ring wait name the count.
+  constexpr int kDefer = 4 * NBT;
+  const int64_t stepP = (int64_t)a.B * G4 * 4;            // bytes of P per step
+  const int64_t stepY = (int64_t)a.B * a.H;               // elements of y / Cs per step
+  // element (b, u) index in a [B][H] step; lanes without an element address
+  // the first byte past each buffer (reads return zeros, writes are dropped)
+  int eidx[NBT];
+  bool eok[NBT];
+#pragma unroll
+  for (int nt = 0; nt < NBT; ++nt) {
+    const int b = b0 + 16 * nt + fr;
+    eok[nt] = u < a.H && 16 * nt + fr < NBv;
+    eidx[nt] = b * a.H + u;
+  }
+  f32x4_t pf[NBT], pfn[NBT];  // P_t (in use) and P_{t+1} (in flight)
+  auto load_p = [&](f32x4_t (&dst)[NBT], int tt) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.P + (int64_t)(tt < a.T ? tt : 0) * (stepP / 4)), 0, tt < a.T ? (int)stepP : 0, 0x00020000);
+#pragma unroll
+    for (int nt = 0; nt < NBT; ++nt)
+      dst[nt] = __builtin_bit_cast(
+          f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, eok[nt] ? 16 * eidx[nt] : (int)stepP, 0, 0));
+  };
+  T hq[NBT];
+  float cq[NBT];
+  u32x4_t gq[NBT];  // activated gates of the step, packed (E == 2: two words)
+  auto store_record = [&](int tt) {
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((T*)a.y + tt * stepY), 0, (int)(stepY * E), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((T*)a.Gs + tt * stepY * 4), 0, (int)(stepY * 4 * E), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.Cs + tt * stepY), 0, (int)(stepY * 4), 0x00020000);
 #pragma unroll
     for (int nt = 0; nt < NBT; ++nt) {
-      const int b = b0 + 16 * nt + fr;
-      pf[nt] = (wk == 0 && tt < a.T && u < a.H && 16 * nt + fr < NBv)
-                   ? *(const f32x4_t*)(a.P + ((int64_t)tt * a.B + b) * G4 + 4 * (int64_t)u)
-                   : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int o = eok[nt] ? eidx[nt] : (int)stepY;  // stepY: one past the end
+      if constexpr (E == 4) {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, hq[nt]), ry, 4 * o, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, gq[nt]), rg, 16 * o, 0, 0);
+      } else {
+        __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, hq[nt]), ry, 2 * o, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(v2u32_t{gq[nt][0], gq[nt][1]}, rg, 8 * o, 0, 0);
+      }
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(cq[nt]), rc, 4 * o, 0, 0);
     }
   };
-  load_p(0);
+  if (wk == 0) load_p(pf, 0);
 
   for (int t = 0; t < a.T; ++t) {
     stamp(a.stamps, a.T, t, 0);
     // wait until every work-group of the batch group has published h_{t-1}
     if (t > 0 && tid < a.nJG) wait_flag(a.HF + bg * a.nJG + tid, (uint32_t)t, a.err, dead);
     __syncthreads();  // flags seen; the previous step's readers of Hl are done
-    // h_{t-1} -> LDS
+    stamp(a.stamps, a.T, t, 1);
+    // h_{t-1} -> LDS, then the deferred operations
     if (t == 0) {
-      wait_vmem();
       for (int idx = tid; idx < NBv * a.H; idx += NTH) {
         const int bl = idx / a.H, k = idx % a.H;
         const T v = a.h0 ? ((const T*)a.h0)[(int64_t)(b0 + bl) * a.H + k] : T(0);
         *(T*)(Hl + bl * strideH + k * E) = v;
       }
+      if (wk == 0) load_p(pfn, 1);
+      wait_vmem();
+      __syncthreads();
     } else {
       const uint32_t slot0 = (uint32_t)(((t - 1) & 1) * a.Bp + b0) * (uint32_t)rowB;
-      for (int q0 = 0; q0 < nchunk; q0 += NTH * C) {
-        u32x4_t v[C];
-#pragma unroll
-        for (int c = 0; c < C; ++c) {
-          const int q = q0 + c * NTH + tid;
-          const int bl = q / cpr, cc = q - bl * cpr;
-          v[c] = q < nchunk ? load16_coherent(hd_rsrc, slot0 + (uint32_t)(bl * rowB + cc * 16)) : u32x4_t{0, 0, 0, 0};
+      if constexpr (C == 0) {
+        // direct-to-LDS: wave-load j moves chunks [64j, 64j + 64) -- 1 KB of
+        // one row, as every row holds a multiple of 64 chunks here
+        for (int j = w; j * 64 < nchunk; j += NW) {
+          const int bl = (64 * j) / cpr, cc = 64 * j - bl * cpr;
+          const char* src = (const char*)a.HD + slot0 + (uint32_t)(bl * rowB + (cc + lane) * 16);
+          __builtin_amdgcn_global_load_lds((const void*)src, (void*)(Hl + bl * strideH + cc * 16), 16, 0, 16);
         }
+      } else {
+        for (int q0 = 0; q0 < nchunk; q0 += NTH * C) {
+          u32x4_t v[C];
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-          const int q = q0 + c * NTH + tid;
-          const int bl = q / cpr, cc = q - bl * cpr;
-          if (q < nchunk) *(u32x4_t*)(Hl + bl * strideH + cc * 16) = v[c];
+          for (int c = 0; c < C; ++c) {
+            const int q = q0 + c * NTH + tid;
+            const int bl = q / cpr, cc = q - bl * cpr;
+            v[c] = q < nchunk ? load16_coherent(hd_rsrc, slot0 + (uint32_t)(bl * rowB + cc * 16)) : u32x4_t{0, 0, 0, 0};
+          }
+#pragma unroll
+          for (int c = 0; c < C; ++c) {
+            const int q = q0 + c * NTH + tid;
+            const int bl = q / cpr, cc = q - bl * cpr;
+            if (q < nchunk) *(u32x4_t*)(Hl + bl * strideH + cc * 16) = v[c];
+          }
         }
       }
+      asm volatile("" ::: "memory");
+      if (wk == 0) {
+        store_record(t - 1);
+        load_p(pfn, t + 1);
+      }
+      asm volatile("" ::: "memory");
+      // the ring reads of this wave are done once at most the deferred
+      // operations are outstanding; LDS writes (register path) once lgkmcnt
+      // is 0; the barrier then covers the other waves
+      if (C == 0 && wk == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDefer));
+      else if (C == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      else __builtin_amdgcn_s_waitcnt(kLgkm0);
+      __builtin_amdgcn_s_barrier();
     }
-    // Everything this wave issued before (last step's stores, the input
-    // prefetch) has completed by now; saying so keeps the compiler from
-    // waiting for stores before it reuses their registers below.
-    wait_vmem();
-    stamp(a.stamps, a.T, t, 1);
-    __syncthreads();
     stamp(a.stamps, a.T, t, 2);
 
     // MFMA: acc[nt] = W_h[rows of M-tile mt, k part] . h_{t-1}[tile nt]^T,
@@ -178,7 +260,10 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
         for (int nt = 0; nt < NBT; ++nt)
           *(f32x4_t*)(red + (((mt * (KS - 1) + wk - 1) * NBT + nt) * 64 + lane) * 4) = acc[nt];
       }
-      __syncthreads();
+      // LDS writes done, then the barrier (not __syncthreads: that would
+      // also wait for the deferred memory operations)
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      __builtin_amdgcn_s_barrier();
       if (wk == 0) {
         for (int k2 = 1; k2 < KS; ++k2) {
 #pragma unroll
@@ -189,10 +274,8 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
     }
 
     stamp(a.stamps, a.T, t, 4);
-    // elementwise: gates, cell, hidden; h_t is published first (stores, their
-    // completion, then the flag), the other outputs after
-    float gv[NBT][4], cv[NBT];
-    T hv[NBT];
+    // elementwise: gates, cell, hidden; h_t is published (stores, their
+    // completion, then the flag), the record is kept for the next step
     if (wk == 0) {
       T* dst = HDt + (int64_t)(t & 1) * a.Bp * a.Hp;
 #pragma unroll
@@ -200,47 +283,39 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
         const int b = b0 + 16 * nt + fr;
         const bool valid = u < a.H && 16 * nt + fr < NBv;
         const f32x4_t z = acc[nt] + pf[nt];
-        gv[nt][0] = sigmoidf(z[0]);
-        gv[nt][1] = sigmoidf(z[1]);
-        gv[nt][2] = tanh_f(z[2]);
-        gv[nt][3] = sigmoidf(z[3]);
-        const float c = gv[nt][1] * cst[nt] + gv[nt][0] * gv[nt][2];
-        const float h = gv[nt][3] * tanh_f(c);
+        const float ig = sigmoidf(z[0]), fg = sigmoidf(z[1]), gg = tanh_f(z[2]), og = sigmoidf(z[3]);
+        const float c = fg * cst[nt] + ig * gg;
+        const float h = og * tanh_f(c);
         cst[nt] = c;
-        cv[nt] = c;
-        hv[nt] = Elem<T>::from_f(h);
-        if (valid) store_elem<T>(dst + (int64_t)b * a.Hp + u, hv[nt], local);
+        cq[nt] = c;
+        hq[nt] = Elem<T>::from_f(h);
+        T g4[4] = {Elem<T>::from_f(ig), Elem<T>::from_f(fg), Elem<T>::from_f(gg), Elem<T>::from_f(og)};
+        if constexpr (E == 4) {
+          gq[nt] = __builtin_bit_cast(u32x4_t, g4);
+        } else {
+          const uint64_t g64 = __builtin_bit_cast(uint64_t, g4);
+          gq[nt] = u32x4_t{(uint32_t)g64, (uint32_t)(g64 >> 32), 0u, 0u};
+        }
+        if (valid) store_elem<T>(dst + (int64_t)b * a.Hp + u, hq[nt], local);
+        pf[nt] = pfn[nt];
       }
     }
     wait_vmem();
     __syncthreads();
     if (tid == 0) store_flag(a.HF + bg * a.nJG + jg, (uint32_t)(t + 1), local);
-    if (wk == 0) {
+    stamp(a.stamps, a.T, t, 5);
+  }
+  // the last step's record and the final states
+  if (wk == 0) {
+    store_record(a.T - 1);
 #pragma unroll
-      for (int nt = 0; nt < NBT; ++nt) {
-        const int b = b0 + 16 * nt + fr;
-        const bool valid = u < a.H && 16 * nt + fr < NBv;
-        const float ig = gv[nt][0], fg = gv[nt][1], gg = gv[nt][2], og = gv[nt][3];
-        const float c = cv[nt];
-        const T hq = hv[nt];
-        if (valid) {
-          const int64_t o = (int64_t)t * a.B + b;
-          ((T*)a.y)[o * a.H + u] = hq;
-          T gq[4] = {Elem<T>::from_f(ig), Elem<T>::from_f(fg), Elem<T>::from_f(gg), Elem<T>::from_f(og)};
-          if constexpr (E == 4)
-            *(f32x4_t*)((T*)a.Gs + o * G4 + 4 * (int64_t)u) = __builtin_bit_cast(f32x4_t, gq);
-          else
-            *(uint64_t*)((T*)a.Gs + o * G4 + 4 * (int64_t)u) = __builtin_bit_cast(uint64_t, gq);
-          a.Cs[o * a.H + u] = c;
-          if (t == a.T - 1) {
-            ((T*)a.hT)[(int64_t)b * a.H + u] = hq;
-            ((T*)a.cT)[(int64_t)b * a.H + u] = Elem<T>::from_f(c);
-          }
-        }
+    for (int nt = 0; nt < NBT; ++nt) {
+      const int b = b0 + 16 * nt + fr;
+      if (u < a.H && 16 * nt + fr < NBv) {
+        ((T*)a.hT)[(int64_t)b * a.H + u] = hq[nt];
+        ((T*)a.cT)[(int64_t)b * a.H + u] = Elem<T>::from_f(cq[nt]);
       }
     }
-    load_p(t + 1);
-    stamp(a.stamps, a.T, t, 5);
   }
   // T == 0 is handled on the host
 }
@@ -260,16 +335,17 @@ static hipError_t fwd_dispatch_c(const Plan& p, FwdArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-// h chunks in flight per thread: as many as a thread reads per step (4 or
-// 16), so that few load slots go unused; 8-wave work-groups (bf16 only)
-// take 16
+// The ring is copied into LDS by direct-to-LDS loads when every row holds a
+// multiple of 64 16-byte chunks (H * E a multiple of 1 KB), else through
+// registers, 4 chunks in flight per thread and round.  8-wave work-groups
+// are bf16 only.
 template <typename T, int NBT>
 static hipError_t fwd_dispatch(const Plan& p, FwdArgs& a, hipStream_t s) {
+  const bool dma = (p.H * p.esize) % 1024 == 0;
   if constexpr (sizeof(T) == 2)
-    if (p.waves == 8) return fwd_dispatch_c<T, NBT, 16, 8>(p, a, s);
+    if (p.waves == 8) return dma ? fwd_dispatch_c<T, NBT, 0, 8>(p, a, s) : fwd_dispatch_c<T, NBT, 4, 8>(p, a, s);
   if (p.waves != kWaves) return hipErrorInvalidValue;
-  if (p.words_per_thread <= 4) return fwd_dispatch_c<T, NBT, 4, kWaves>(p, a, s);
-  return fwd_dispatch_c<T, NBT, 16, kWaves>(p, a, s);
+  return dma ? fwd_dispatch_c<T, NBT, 0, kWaves>(p, a, s) : fwd_dispatch_c<T, NBT, 4, kWaves>(p, a, s);
 }
 
 hipError_t launch_fwd_recurrent(const Plan& p, const float* P, const void* W, const void* h0, const void* c0,

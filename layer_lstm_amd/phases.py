@@ -17,7 +17,8 @@ import sys
 
 import numpy as np
 
-FWD_PHASES = ("exchange wait + h load", "barrier", "product", "reduction + gather", "gate math + publish")
+FWD_PHASES = ("exchange wait (h flags)", "h load + record issue", "product", "k-part reduction",
+              "gate math + publish")
 # backward: the MFMA kernel (column partition, bf16 and most fp32 shapes) and
 # the VALU kernel (fp32 batch groups of 4 rows, the fp32 workloads here)
 BWD_PHASES_MFMA = ("exchange wait (dG flags)", "dG loads + product", "wave reduction", "gate deltas + publish",
