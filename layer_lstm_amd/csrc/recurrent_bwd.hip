@@ -38,8 +38,9 @@ namespace lstm {
 
 // NBT 16-row batch tiles, MT 16-unit tiles, NKB k-blocks (16 bytes per lane
 // each) of the 4Hp gate rows per wave, NW waves.  EPTM elements (row, unit)
-// per thread at most.
-template <typename T, int NBT, int MT, int NKB, int NW>
+// per thread at most.  DEF selects where the step's other memory traffic
+// goes (see below).
+template <typename T, int NBT, int MT, int NKB, int NW, bool DEF>
 __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
   constexpr int NTH = 64 * NW;
   constexpr int E = sizeof(T);
@@ -136,33 +137,93 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
     if (e < nel) *(f32x4_t*)(dba + 4 * e) = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  // Elementwise operands of a step (activated gates, c_t, c_{t-1}, dy_t),
-  // prefetched one step ahead, at the end of the step before.
-  float pg[EPTM][4], pc[EPTM], pcp[EPTM], pdy[EPTM];
-  const int64_t stepC = (int64_t)a.B * a.H;  // elements of one step in [B][H]
-  auto load_ops = [&](int tt) {
-    const int64_t oC = (int64_t)tt * stepC;
+  // Memory traffic off the exchange path: the operands of a step's
+  // elementwise chain (activated gates, c_t, c_{t-1}, dy_t) are fetched one
+  // step ahead, and the record of a step (dG rows for the dW / dx products)
+  // is written.  A wave's vector-memory operations complete in issue order,
+  // so this traffic delays whichever wait on the exchange comes next after
+  // it is issued; where it goes depends on the exchange:
+  //   DEF (XCD-local groups: the ring sits in L2 and the flag wait is short):
+  //     issued as soon as the product's ring reads are consumed (gates and
+  //     cells direct-to-LDS into one of two slots, dy into registers, the
+  //     record one step late), it drains during the reduction and the gate
+  //     deltas;
+  //   !DEF (groups across XCDs: every flag and ring read goes through memory
+  //     and the flag wait is long): the record is written with the ring and
+  //     the operands are loaded into registers right after the flag, while
+  //     the other work-groups' flags are on their way.
+  constexpr int GSB = 4 * E;                                 // bytes of one element's gates
+  constexpr int SLOT = EPTM * NTH * (GSB + 8);               // bytes of one operand slot
+  char* opl = (char*)(dba + 4 * 1024);                       // [2][SLOT]: per s: gates, c_t, c_{t-1}
+  const int64_t stepC = (int64_t)a.B * a.H;                  // elements of one step in [B][H]
+  T pdy[EPTM], pdyn[EPTM];  // dy_t (in use), dy of the next step: raw, converted at use (a conversion at
+                            // load time would make the load's issue wait for its data)
+  uint32_t dqw[EPTM][GSB / 4];                               // this step's gate deltas, packed
+  uint32_t rgw[EPTM][GSB / 4];                               // !DEF: gates of the next step, raw
+  float rc[EPTM], rcp[EPTM];                                 // !DEF: c_t, c_{t-1} of the next step
+  auto load_regs = [&](int tt) {
+    // !DEF: operands of step tt >= 0 into registers (raw: no conversion at
+    // load time, which would make the issue wait for the data)
+    if (tt < 0) return;
 #pragma unroll
     for (int s = 0; s < EPTM; ++s) {
-      pg[s][0] = pg[s][1] = pg[s][2] = pg[s][3] = 0.f;
-      pc[s] = pcp[s] = pdy[s] = 0.f;
-      if (tt >= 0 && own[s]) {
-        const int64_t o = oC + c_off(s);
-        if constexpr (E == 4) {
-          const f32x4_t gv = *(const f32x4_t*)((const T*)a.Gs + 4 * o);
-          pg[s][0] = gv[0]; pg[s][1] = gv[1]; pg[s][2] = gv[2]; pg[s][3] = gv[3];
-        } else {
-          const uint64_t raw = *(const uint64_t*)((const T*)a.Gs + 4 * o);
-          pg[s][0] = bf2f((bf16_t)raw); pg[s][1] = bf2f((bf16_t)(raw >> 16));
-          pg[s][2] = bf2f((bf16_t)(raw >> 32)); pg[s][3] = bf2f((bf16_t)(raw >> 48));
-        }
-        pc[s] = a.Cs[o];
-        pcp[s] = tt > 0 ? a.Cs[o - stepC] : (a.c0 ? ldf<T>(a.c0, c_off(s)) : 0.f);
-        pdy[s] = ldf<T>(a.dy, o);
+      if (!own[s]) continue;
+      const int64_t o = tt * stepC + c_off(s);
+      if constexpr (E == 4) {
+        const u32x4_t g = *(const u32x4_t*)((const T*)a.Gs + 4 * o);
+        rgw[s][0] = g[0]; rgw[s][1] = g[1]; rgw[s][2] = g[2]; rgw[s][3] = g[3];
+      } else {
+        const uint64_t g = *(const uint64_t*)((const T*)a.Gs + 4 * o);
+        rgw[s][0] = (uint32_t)g; rgw[s][1] = (uint32_t)(g >> 32);
       }
+      rc[s] = a.Cs[o];
+      rcp[s] = tt > 0 ? a.Cs[o - stepC] : 0.f;
+      pdy[s] = ((const T*)a.dy)[o];
     }
   };
-  load_ops(a.T - 1);
+  auto issue_ops = [&](int tt) {
+    // DEF: operands of step tt >= 0 of this thread's elements
+    if (tt < 0) return;
+    char* slot = opl + (tt & 1) * SLOT;
+#pragma unroll
+    for (int s = 0; s < EPTM; ++s) {
+      if (!own[s]) continue;
+      char* ss = slot + s * NTH * (GSB + 8);
+      const int64_t o = tt * stepC + c_off(s);                  // element of step tt
+      const char* gsrc = (const char*)a.Gs + 4 * o * E;
+      if constexpr (E == 4) {
+        __builtin_amdgcn_global_load_lds((const void*)gsrc, (void*)(ss + w * 64 * 16), 16, 0, 0);
+      } else {
+        __builtin_amdgcn_global_load_lds((const void*)gsrc, (void*)(ss + w * 64 * 4), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(gsrc + 4), (void*)(ss + NTH * 4 + w * 64 * 4), 4, 0, 0);
+      }
+      __builtin_amdgcn_global_load_lds((const void*)(a.Cs + o), (void*)(ss + NTH * GSB + w * 64 * 4), 4, 0, 0);
+      if (tt > 0)
+        __builtin_amdgcn_global_load_lds((const void*)(a.Cs + o - stepC), (void*)(ss + NTH * (GSB + 4) + w * 64 * 4),
+                                         4, 0, 0);
+      pdyn[s] = ((const T*)a.dy)[o];
+    }
+  };
+  auto store_record = [&](int tt) {
+    // gate deltas of step tt into the dG record
+#pragma unroll
+    for (int s = 0; s < EPTM; ++s) {
+      if (!own[s]) continue;
+      T* dst = (T*)a.dG + 4 * (tt * stepC + c_off(s));
+      if constexpr (E == 4)
+        *(u32x4_t*)dst = u32x4_t{dqw[s][0], dqw[s][1], dqw[s][2], dqw[s][3]};
+      else
+        *(uint64_t*)dst = (uint64_t)dqw[s][0] | ((uint64_t)dqw[s][1] << 32);
+    }
+  };
+  if constexpr (DEF) {
+    issue_ops(a.T - 1);
+    wait_vmem();
+#pragma unroll
+    for (int s = 0; s < EPTM; ++s) pdy[s] = pdyn[s];
+  } else {
+    load_regs(a.T - 1);
+  }
 
   for (int t = a.T - 1; t >= -1; --t) {
     const int step = a.T - 1 - (t < 0 ? 0 : t);
@@ -188,7 +249,9 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
       };
       // scheduling barriers pin each chunk's loads ahead of the products of
       // the chunk before (the scheduler would otherwise trade loads in
-      // flight for registers)
+      // flight for registers).  The deferred operations wait until every
+      // ring read is consumed: with other kinds of operations outstanding
+      // (stores, direct-to-LDS loads), the compiler can only wait for all.
       issue(0, 0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -203,6 +266,11 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
             for (int mt = 0; mt < MT; ++mt)
               acc[mt][nt] = Mfma<T>::mac(wreg[mt][ch * CK + i], bb[ch & 1][i][nt], acc[mt][nt]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (DEF) {
+        store_record(t + 1);
+        issue_ops(t - 1);
+      }
       // lane holds D[unit 16*mt + 4*fq + q][row 16*nt + fr], q < 4
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
@@ -210,7 +278,10 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
         for (int nt = 0; nt < NBT; ++nt)
           *(f32x4_t*)(red + (w * NBr + 16 * nt + fr) * NJS + 16 * mt + 4 * fq) = acc[mt][nt];
       if (t >= 0) stamp(a.stamps, a.T, step, 2);
-      __syncthreads();
+      // LDS writes done, then the barrier (not __syncthreads: that would also
+      // wait for the deferred memory operations)
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      __builtin_amdgcn_s_barrier();
 #pragma unroll
       for (int s = 0; s < EPTM; ++s) {
         const int e = tid + NTH * s;
@@ -223,48 +294,77 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
         }
       }
     } else {
+      if constexpr (DEF) issue_ops(t - 1);
       stamp(a.stamps, a.T, step, 1);
       stamp(a.stamps, a.T, step, 2);
     }
     if (t < 0) break;
-    // Everything this thread issued before has completed; saying so keeps
-    // the compiler from waiting for stores before it reuses registers below.
-    wait_vmem();
     stamp(a.stamps, a.T, step, 3);
 
-    // 2. gate deltas of this step; dG_t to the record and to the ring
+    // 2. gate deltas of this step; dG_t to the ring (the record follows next
+    //    step)
     T* ring = (T*)a.GD + (size_t)(t & 1) * (size_t)a.Bp * 4 * a.Hp;
+    const char* slot = opl + (t & 1) * SLOT;
 #pragma unroll
     for (int s = 0; s < EPTM; ++s) {
+      const char* ss = slot + s * NTH * (GSB + 8);
+      uint32_t gw[GSB / 4];
+      float c, cprev;
+      if constexpr (DEF) {
+#pragma unroll
+        for (int k = 0; k < GSB / 4; ++k) gw[k] = *(const uint32_t*)(ss + (GSB == 16 ? tid * 16 + 4 * k : k * NTH * 4 + tid * 4));
+        c = *(const float*)(ss + NTH * GSB + tid * 4);
+        cprev = *(const float*)(ss + NTH * (GSB + 4) + tid * 4);
+      } else {
+#pragma unroll
+        for (int k = 0; k < GSB / 4; ++k) gw[k] = rgw[s][k];
+        c = rc[s];
+        cprev = rcp[s];
+      }
+      float gi, gf, gg, go;
+      if constexpr (E == 4) {
+        gi = __uint_as_float(gw[0]); gf = __uint_as_float(gw[1]); gg = __uint_as_float(gw[2]); go = __uint_as_float(gw[3]);
+      } else {
+        gi = bf2f((bf16_t)gw[0]); gf = bf2f((bf16_t)(gw[0] >> 16)); gg = bf2f((bf16_t)gw[1]); go = bf2f((bf16_t)(gw[1] >> 16));
+      }
+      if (t == 0) cprev = (own[s] && a.c0) ? ldf<T>(a.c0, c_off(s)) : 0.f;
+      const float tc = tanh_f(c);
+      const float dh = Elem<T>::to_f(pdy[s]) + dhc[s];
+      const float dc = dh * go * (1.f - tc * tc) + dcc[s];
+      const float d_o = dh * tc * go * (1.f - go);
+      const float d_g = dc * gi * (1.f - gg * gg);
+      const float d_i = dc * gg * gi * (1.f - gi);
+      const float d_f = dc * cprev * gf * (1.f - gf);
+      T dq[4] = {Elem<T>::from_f(d_i), Elem<T>::from_f(d_f), Elem<T>::from_f(d_g), Elem<T>::from_f(d_o)};
+      if constexpr (E == 4) {
+        const u32x4_t v = __builtin_bit_cast(u32x4_t, dq);
+        dqw[s][0] = v[0]; dqw[s][1] = v[1]; dqw[s][2] = v[2]; dqw[s][3] = v[3];
+      } else {
+        const uint64_t v = __builtin_bit_cast(uint64_t, dq);
+        dqw[s][0] = (uint32_t)v; dqw[s][1] = (uint32_t)(v >> 32);
+      }
       if (own[s]) {
-        const int64_t o = 4 * ((int64_t)t * stepC + c_off(s));  // element offset in dG
-        const float gi = pg[s][0], gf = pg[s][1], gg = pg[s][2], go = pg[s][3];
-        const float c = pc[s], cprev = pcp[s];
-        const float tc = tanh_f(c);
-        const float dh = pdy[s] + dhc[s];
-        const float dc = dh * go * (1.f - tc * tc) + dcc[s];
-        const float d_o = dh * tc * go * (1.f - go);
-        const float d_g = dc * gi * (1.f - gg * gg);
-        const float d_i = dc * gg * gi * (1.f - gi);
-        const float d_f = dc * cprev * gf * (1.f - gf);
+        if constexpr (!DEF) {
+          T* dst = (T*)a.dG + 4 * (t * stepC + c_off(s));
+          if constexpr (E == 4)
+            *(u32x4_t*)dst = __builtin_bit_cast(u32x4_t, dq);
+          else
+            *(uint64_t*)dst = __builtin_bit_cast(uint64_t, dq);
+        }
         dcc[s] = dc * gf;
         *(f32x4_t*)(dba + 4 * (tid + NTH * s)) += f32x4_t{d_i, d_f, d_g, d_o};
-        T dq[4] = {Elem<T>::from_f(d_i), Elem<T>::from_f(d_f), Elem<T>::from_f(d_g), Elem<T>::from_f(d_o)};
         T* rp = ring + (uint32_t)elem_b(s) * (uint32_t)(4 * a.Hp) + 4u * (uint32_t)elem_u(s);
         if constexpr (E == 4) {
-          const f32x4_t v = __builtin_bit_cast(f32x4_t, dq);
-          *(f32x4_t*)((T*)a.dG + o) = v;
           if (local) {
-            *(f32x4_t*)rp = v;
+            *(u32x4_t*)rp = __builtin_bit_cast(u32x4_t, dq);
           } else {
-            const uint64_t lo = (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32);
-            const uint64_t hi = (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32);
+            const uint64_t lo = (uint64_t)dqw[s][0] | ((uint64_t)dqw[s][1] << 32);
+            const uint64_t hi = (uint64_t)dqw[s][2] | ((uint64_t)dqw[s][3] << 32);
             __hip_atomic_store((uint64_t*)rp, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store((uint64_t*)rp + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           }
         } else {
           const uint64_t v = __builtin_bit_cast(uint64_t, dq);
-          *(uint64_t*)((T*)a.dG + o) = v;
           if (local)
             *(uint64_t*)rp = v;
           else
@@ -272,12 +372,21 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
         }
       }
     }
-    // publish: every gate delta of this work-group is stored, then the flag
+    // publish: every gate delta of this work-group is in the ring, then the flag
     wait_vmem();
     __syncthreads();
     if (tid == 0) store_flag(a.GF + bg * a.nJG + jg, (uint32_t)(a.T - t), local);
+    if constexpr (DEF) {
+#pragma unroll
+      for (int s = 0; s < EPTM; ++s) pdy[s] = pdyn[s];
+    } else {
+      // loaded to completion here, while the flags of this step travel: in
+      // flight, the loads would hold up the next step's flag polls and ring
+      // reads, which complete only after every earlier load of their wave
+      load_regs(t - 1);
+      wait_vmem();
+    }
     stamp(a.stamps, a.T, step, 4);
-    load_ops(t - 1);
     stamp(a.stamps, a.T, step, 5);
   }
 
@@ -304,42 +413,47 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-template <typename T, int NBT, int MT, int NW>
+template <typename T, int NBT, int MT, int NW, bool DEF>
 static hipError_t bwd_col_nkb(const Plan& p, BwdArgs& a, hipStream_t s) {
   const int nt = 64 * NW;
   switch (p.bwd_nkb) {
-    case 1: return coop_launch(bwd_col_kernel<T, NBT, MT, 1, NW>, p.grid, p.lds_bwd, &a, s, nt);
-    case 2: return coop_launch(bwd_col_kernel<T, NBT, MT, 2, NW>, p.grid, p.lds_bwd, &a, s, nt);
-    case 4: return coop_launch(bwd_col_kernel<T, NBT, MT, 4, NW>, p.grid, p.lds_bwd, &a, s, nt);
-    case 8: return coop_launch(bwd_col_kernel<T, NBT, MT, 8, NW>, p.grid, p.lds_bwd, &a, s, nt);
-    case 16: return coop_launch(bwd_col_kernel<T, NBT, MT, 16, NW>, p.grid, p.lds_bwd, &a, s, nt);
+    case 1: return coop_launch(bwd_col_kernel<T, NBT, MT, 1, NW, DEF>, p.grid, p.lds_bwd, &a, s, nt);
+    case 2: return coop_launch(bwd_col_kernel<T, NBT, MT, 2, NW, DEF>, p.grid, p.lds_bwd, &a, s, nt);
+    case 4: return coop_launch(bwd_col_kernel<T, NBT, MT, 4, NW, DEF>, p.grid, p.lds_bwd, &a, s, nt);
+    case 8: return coop_launch(bwd_col_kernel<T, NBT, MT, 8, NW, DEF>, p.grid, p.lds_bwd, &a, s, nt);
+    case 16: return coop_launch(bwd_col_kernel<T, NBT, MT, 16, NW, DEF>, p.grid, p.lds_bwd, &a, s, nt);
     case 32:
-      if constexpr (MT == 1) return coop_launch(bwd_col_kernel<T, NBT, MT, 32, NW>, p.grid, p.lds_bwd, &a, s, nt);
+      if constexpr (MT == 1) return coop_launch(bwd_col_kernel<T, NBT, MT, 32, NW, DEF>, p.grid, p.lds_bwd, &a, s, nt);
       break;
   }
   return hipErrorInvalidValue;
 }
 
-template <typename T, int NW>
+template <typename T, int NW, bool DEF>
 static hipError_t bwd_col_nw(const Plan& p, BwdArgs& a, hipStream_t s) {
   const int nbt = p.NB < 16 ? 1 : p.NB / 16;
   if (p.bwd_mt == 1) {
-    if (nbt == 1) return bwd_col_nkb<T, 1, 1, NW>(p, a, s);
-    if (nbt == 2) return bwd_col_nkb<T, 2, 1, NW>(p, a, s);
-    if (nbt == 4) return bwd_col_nkb<T, 4, 1, NW>(p, a, s);
+    if (nbt == 1) return bwd_col_nkb<T, 1, 1, NW, DEF>(p, a, s);
+    if (nbt == 2) return bwd_col_nkb<T, 2, 1, NW, DEF>(p, a, s);
+    if (nbt == 4) return bwd_col_nkb<T, 4, 1, NW, DEF>(p, a, s);
   } else if (p.bwd_mt == 2) {
-    if (nbt == 1) return bwd_col_nkb<T, 1, 2, NW>(p, a, s);
-    if (nbt == 2) return bwd_col_nkb<T, 2, 2, NW>(p, a, s);
-    if (nbt == 4) return bwd_col_nkb<T, 4, 2, NW>(p, a, s);
+    if (nbt == 1) return bwd_col_nkb<T, 1, 2, NW, DEF>(p, a, s);
+    if (nbt == 2) return bwd_col_nkb<T, 2, 2, NW, DEF>(p, a, s);
+    if (nbt == 4) return bwd_col_nkb<T, 4, 2, NW, DEF>(p, a, s);
   }
   return hipErrorInvalidValue;
 }
 
+template <typename T, int NW>
+static hipError_t bwd_col_def(const Plan& p, BwdArgs& a, hipStream_t s) {
+  return p.xcd_local ? bwd_col_nw<T, NW, true>(p, a, s) : bwd_col_nw<T, NW, false>(p, a, s);
+}
+
 hipError_t launch_bwd_col(const Plan& p, BwdArgs& a, hipStream_t s) {
   if (p.NB * p.NJ > 1024) return hipErrorInvalidValue;
-  if (p.dtype) return p.waves == 8 ? bwd_col_nw<bf16_t, 8>(p, a, s) : bwd_col_nw<bf16_t, kWaves>(p, a, s);
+  if (p.dtype) return p.waves == 8 ? bwd_col_def<bf16_t, 8>(p, a, s) : bwd_col_def<bf16_t, kWaves>(p, a, s);
   if (p.waves != kWaves) return hipErrorInvalidValue;
-  return bwd_col_nw<float, kWaves>(p, a, s);
+  return bwd_col_def<float, kWaves>(p, a, s);
 }
 
 }  // namespace lstm
