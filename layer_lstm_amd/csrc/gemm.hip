@@ -249,7 +249,33 @@ struct GemmArgs {
   int dsum_rows;
   int dsum_bf16;
   int64_t dsum_cols, dsum_H;
+  int nxcd;           // XCDs of the device (1: no XCD-aware tile order)
 };
+
+// Output tile (n tile, m tile, split) of this work-group.  The device deals
+// the work-groups of a dispatch to its XCDs round robin (from a starting XCD
+// that varies), so work-groups i and i + nxcd share an XCD and its L2.  Each
+// residue class mod nxcd is given one contiguous range of the row-major
+// tile order (n fastest, then m, then split): the tiles an XCD runs at once
+// then share rows of A and columns of B in its L2, instead of every XCD
+// streaming every row-block of A.  Products with few tiles per split keep
+// the plain order (there an XCD would work one K slice with all its CUs).
+struct TileId {
+  int64_t x, y;
+  int z;
+};
+__device__ __forceinline__ TileId tile_of(int nxcd, int splits) {
+  const int64_t gx = gridDim.x, gxy = (int64_t)gridDim.x * gridDim.y;
+  const int64_t nc = gxy * splits;
+  int64_t i = ((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gx + blockIdx.x;
+  if (nxcd > 1 && nc % nxcd == 0 && gxy >= 8 * nxcd) i = (i % nxcd) * (nc / nxcd) + i / nxcd;
+  TileId t;
+  t.z = (int)(i / gxy);
+  const int64_t r = i - t.z * gxy;
+  t.y = r / gx;
+  t.x = r - t.y * gx;
+  return t;
+}
 
 // ---------------------------------------------------------------------------
 // Tile BM x BN = (32*WM) x (32*WN): 4 waves in 2 x 2, each (16*WM) x (16*WN).
@@ -280,8 +306,9 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs<AOp, BOp, Epi> 
     return;
   }
   const int wm = w >> 1, wn = w & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
-  const int split = blockIdx.z;
+  const TileId tl = tile_of(g.nxcd, g.splits);
+  const int64_t m0 = tl.y * BM, n0 = tl.x * BN;
+  const int split = tl.z;
   const int64_t ktiles = (g.K + KSTAGE - 1) / KSTAGE;
   const int64_t kt_begin = (int64_t)split * g.ktiles_per_split;
   const int64_t kt_end = kt_begin + g.ktiles_per_split < ktiles ? kt_begin + g.ktiles_per_split : ktiles;
@@ -485,8 +512,9 @@ __global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_kernel(GemmAr
     return;
   }
   const int wm = w / WGN, wn = w % WGN, fr = lane & 15, fq = lane >> 4;
-  const int64_t m0 = (int64_t)blockIdx.y * TILE, n0 = (int64_t)blockIdx.x * TILE;
-  const int split = blockIdx.z;
+  const TileId tl = tile_of(g.nxcd, g.splits);
+  const int64_t m0 = tl.y * TILE, n0 = tl.x * TILE;
+  const int split = tl.z;
   const int64_t ktiles = g.K / KST;
   const int64_t kt_begin = (int64_t)split * g.ktiles_per_split;
   const int64_t kt_end = kt_begin + g.ktiles_per_split < ktiles ? kt_begin + g.ktiles_per_split : ktiles;
@@ -629,7 +657,7 @@ static hipError_t run_gemm(const Plan& p, int64_t M, int64_t N, int64_t K, const
   int ktps = (int)((ktiles + gs.splits - 1) / gs.splits);
   if (ktps < 1) ktps = 1;
   GemmArgs<AOp, BOp, Epi> g{M, N, K, ktps, gs.splits, a, b, e, part, (uint32_t*)zero, (int64_t)(zero_bytes / 4),
-                            db.src, db.out, db.rows, db.bf16, db.cols, db.H};
+                            db.src, db.out, db.rows, db.bf16, db.cols, db.H, p.nxcd};
   hipError_t err = gs.tile == 128 ? launch_tile<T, 4, 4, AOp, AMN, BOp, BMN, Epi>(g, s)
                                   : launch_tile<T, 2, 2, AOp, AMN, BOp, BMN, Epi>(g, s);
   if (err != hipSuccess || gs.splits == 1) return err;
@@ -666,7 +694,7 @@ static hipError_t run_gemm_lds(const Plan& p, int64_t M, int64_t N, int64_t K, c
   int ktps = (int)((ktiles + gs.splits - 1) / gs.splits);
   if (ktps < 1) ktps = 1;
   GemmArgs<AOp, BOp, Epi> g{M, N, K, ktps, gs.splits, a, b, e, part, (uint32_t*)zero, (int64_t)(zero_bytes / 4),
-                            db.src, db.out, db.rows, db.bf16, db.cols, db.H};
+                            db.src, db.out, db.rows, db.bf16, db.cols, db.H, p.nxcd};
   const unsigned gz = (unsigned)gs.splits + ((g.zero_words > 0 || g.dsum_out) ? 1u : 0u);
   dim3 grid((unsigned)((N + TILE - 1) / TILE), (unsigned)((M + TILE - 1) / TILE), gz);
   const size_t lds = (size_t)kStages * lds_stage_bytes<T>();
