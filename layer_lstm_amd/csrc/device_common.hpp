@@ -118,6 +118,34 @@ __device__ __forceinline__ float xval(uint64_t w) { return __uint_as_float((uint
 // must assume some are and waits for all stores before reusing their
 // registers on the common path.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// 16 bytes per lane from a buffer straight into LDS, to (wave-uniform) lds +
+// 16 * lane; SC1 selects a device-coherent read.  Issued through inline asm
+// so that the compiler does not see an LDS write: for a direct-to-LDS
+// builtin it inserts waits of its own before LDS reads it cannot tell
+// apart from the destination, which empties every pipeline built on these
+// loads.  The caller therefore waits (vmcnt, then a barrier for the other
+// waves) before the data is read.  The instruction writes no register (the
+// hazard of asm loads with register outputs does not arise); M0 carries the
+// LDS address and is declared clobbered.
+typedef __attribute__((address_space(3))) void lds_void_t;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <bool SC1>
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)lds);
+  if constexpr (SC1)
+    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, %3 offen sc1 lds"
+                 :
+                 : "v"(voff), "s"(m0v), "s"(r), "s"(soff)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, %3 offen lds"
+                 :
+                 : "v"(voff), "s"(m0v), "s"(r), "s"(soff)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits [3:0] and [15:14],
 // expcnt [6:4], lgkmcnt [11:8]; a field at its maximum does not wait):
 // vmcnt(n) alone, and lgkmcnt(0) alone

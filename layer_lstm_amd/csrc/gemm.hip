@@ -401,7 +401,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs<AOp, BOp, Epi> 
 //     fragments.
 // Tile rows or columns past the operand are loaded from its last valid rows
 // (their outputs are never stored); an absent operand block (zero initial
-// state) is loaded from a 16-byte zero word.
+// state) is read through an empty buffer descriptor, which returns zeros.
 constexpr int kStages = 4;
 static_assert(kStages == 4, "the stage waits in gemm_lds_kernel assume a 4-stage ring");
 
@@ -426,35 +426,148 @@ typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 __device__ __forceinline__ int krow_swz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ int mnrow_swz(int kr) { return ((kr & 3) | (((kr >> 3) & 1) << 2)) << 1; }
 
-// kTile rows x 64 bytes: loads of 16 rows, 2 per wave
-template <typename T, class Op>
-__device__ __forceinline__ void dma_krows(const Op& op, char* lds, int64_t row0, int64_t k0, int w, int lane) {
-  constexpr int VEC = 16 / sizeof(T);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = 32 * w + 16 * j + (lane >> 2), c = (lane & 3) ^ krow_swz(r);
-    int64_t gr = row0 + r;
-    gr = gr < op.R ? gr : op.R - 1;
-    const T* src = op.row(gr) + k0 + c * VEC;
-    __builtin_amdgcn_global_load_lds((const void*)src, (void*)(lds + (32 * w + 16 * j) * 64), 16, 0, 0);
-  }
+// Direct-to-LDS loaders with launch-constant lane offsets: each of a lane's
+// two 16-byte loads per operand and stage reads one buffer at (a per-lane
+// offset fixed for the launch) + (a per-stage offset, uniform), through
+// lds_dma16 (the stage waits below are the only ones).  The buffers are
+// below 2 GiB (checked on the host).  Rows (krows) or columns (mnrows) past
+// the operand are clamped to its last valid ones (their outputs are never
+// stored).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
 }
-
-// kKStage k-rows x 512 bytes: loads of 2 k-rows, 2 per wave
-template <typename T, class Op>
-__device__ __forceinline__ void dma_mnrows(const Op& op, char* lds, int64_t r0, int64_t k0, int w, int lane,
-                                           const void* zero16) {
-  constexpr int VEC = 16 / sizeof(T);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int kr = 4 * w + 2 * j + (lane >> 5), c = (lane & 31) ^ mnrow_swz(kr);
-    int64_t r = r0 + c * VEC;
-    r = r + VEC <= op.R ? r : op.R - VEC;
-    const T* src = op.krow(k0 + kr, r);
-    __builtin_amdgcn_global_load_lds(src ? (const void*)src : zero16, (void*)(lds + (4 * w + 2 * j) * 512), 16, 0,
-                                     0);
-  }
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t vo, uint32_t so) {
+  lds_dma16<false>(r, lds, vo, so);
 }
+template <typename T, class Op, bool MN> struct Dma;
+template <typename T, class Op>
+struct DmaKRows {  // k-contiguous rows: row(r) = base + (rowidx(r) * ld + col0) elements
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t vo[2];
+  template <class RowIdx>
+  __device__ __forceinline__ void init(const T* base, int64_t rows_total, int64_t ld, int64_t col0, int64_t R,
+                                       int64_t row0, int w, int lane, RowIdx rowidx) {
+    constexpr int VEC = 16 / sizeof(T);
+    r = rsrc_of(base, rows_total * ld * (int64_t)sizeof(T));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int rr = 32 * w + 16 * j + (lane >> 2), c = (lane & 3) ^ krow_swz(rr);
+      int64_t gr = row0 + rr;
+      gr = gr < R ? gr : R - 1;
+      vo[j] = (uint32_t)((rowidx(gr) * ld + col0 + c * VEC) * (int64_t)sizeof(T));
+    }
+  }
+  __device__ __forceinline__ void issue(char* lds, int64_t k0, int w, int) const {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(r, lds + (32 * w + 16 * j) * 64, vo[j], (uint32_t)(k0 * (int64_t)sizeof(T)));
+  }
+};
+template <typename T>
+struct Dma<T, KRowsX<T>, false> : DmaKRows<T, KRowsX<T>> {
+  __device__ __forceinline__ Dma(const KRowsX<T>& op, int64_t row0, int w, int lane) {
+    this->init(op.p, op.R, op.ld, 0, op.R, row0, w, lane, [](int64_t g) { return g; });
+  }
+};
+template <typename T>
+struct Dma<T, KRowsWx<T>, false> : DmaKRows<T, KRowsWx<T>> {
+  __device__ __forceinline__ Dma(const KRowsWx<T>& op, int64_t row0, int w, int lane) {
+    const int64_t H = op.H;
+    this->init(op.W, 4 * H, op.ld, H, op.R, row0, w, lane, [H](int64_t g) { return gate_row(g, H); });
+  }
+};
+// r-contiguous k-rows: lane (kr, chunk c) of a stage, r = r0 + c * VEC
+__device__ __forceinline__ int mn_kr(int w, int j, int lane) { return 4 * w + 2 * j + (lane >> 5); }
+template <typename T>
+__device__ __forceinline__ int64_t mn_r(int64_t r0, int64_t R, int kr, int lane) {
+  constexpr int VEC = 16 / sizeof(T);
+  const int c = (lane & 31) ^ mnrow_swz(kr);
+  const int64_t r = r0 + c * VEC;
+  return r + VEC <= R ? r : R - VEC;
+}
+template <typename T>
+struct Dma<T, MNRowsPlain<T>, true> {  // [K][ld]
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t vo[2];
+  int64_t ldb;
+  __device__ __forceinline__ Dma(const MNRowsPlain<T>& op, int64_t r0, int w, int lane) {
+    r = rsrc_of(op.p, op.K * op.ld * (int64_t)sizeof(T));
+    ldb = op.ld * (int64_t)sizeof(T);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int kr = mn_kr(w, j, lane);
+      vo[j] = (uint32_t)(kr * ldb + mn_r<T>(r0, op.R, kr, lane) * (int64_t)sizeof(T));
+    }
+  }
+  __device__ __forceinline__ void issue(char* lds, int64_t k0, int w, int) const {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(r, lds + (4 * w + 2 * j) * 512, vo[j], (uint32_t)(k0 * ldb));
+  }
+};
+template <typename T>
+struct Dma<T, MNRowsWx<T>, true> {  // k-row = interleaved gate row of W's input block
+  __amdgpu_buffer_rsrc_t r;
+  uint32_t vo[2];
+  int64_t ldb;
+  __device__ __forceinline__ Dma(const MNRowsWx<T>& op, int64_t r0, int w, int lane) {
+    r = rsrc_of(op.W, 4 * op.H * op.ld * (int64_t)sizeof(T));
+    ldb = op.ld * (int64_t)sizeof(T);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int kr = mn_kr(w, j, lane);  // stage k-rows start at a multiple of 4: gate kr & 3, unit + kr / 4
+      vo[j] = (uint32_t)(((kr & 3) * op.H + (kr >> 2)) * ldb + (op.H + mn_r<T>(r0, op.R, kr, lane)) * (int64_t)sizeof(T));
+    }
+  }
+  __device__ __forceinline__ void issue(char* lds, int64_t k0, int w, int) const {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) dma16(r, lds + (4 * w + 2 * j) * 512, vo[j], (uint32_t)((k0 >> 2) * ldb));
+  }
+};
+template <typename T>
+struct Dma<T, MNRowsZ<T>, true> {  // Z[tb] = [h_{t-1}[b] | x[tb]]
+  // three buffers, all addressed as [tb][...] with the stage's first k-row
+  // tb0 = k0 as the uniform offset: h0 for tb < B (absent: an empty buffer,
+  // read as zeros), y shifted back by B rows for tb >= B, and x
+  __amdgpu_buffer_rsrc_t rh, ry, rx;
+  uint32_t vh[2], vx[2];
+  bool seg;  // this lane's columns lie in the h part
+  int64_t B, hb, ib;
+  __device__ __forceinline__ Dma(const MNRowsZ<T>& op, int64_t r0, int w, int lane) {
+    constexpr int64_t E = sizeof(T);
+    B = op.B;
+    hb = op.H * E;
+    ib = op.I * E;
+    rh = rsrc_of(op.h0 ? (const void*)op.h0 : (const void*)op.x, op.h0 ? op.B * hb : 0);
+    ry = rsrc_of((const char*)op.y - op.B * hb, op.K * hb);  // only offsets of rows tb >= B are read
+    rx = rsrc_of(op.x, op.K * ib);
+    seg = mn_r<T>(r0, op.R, mn_kr(w, 0, lane), lane) < op.H;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int kr = mn_kr(w, j, lane);
+      const int64_t rj = mn_r<T>(r0, op.R, kr, lane);
+      vh[j] = (uint32_t)(kr * hb + rj * E);
+      vx[j] = (uint32_t)(kr * ib + (rj - op.H) * E);
+    }
+  }
+  // The branches end in distinct empty asm statements: the compiler would
+  // otherwise merge their loads into one with a per-lane descriptor, which
+  // it can only issue in a loop over the lanes' values.
+  __device__ __forceinline__ void issue(char* lds, int64_t k0, int w, int lane) const {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      char* dst = lds + (4 * w + 2 * j) * 512;
+      if (!seg) {
+        dma16(rx, dst, vx[j], (uint32_t)(k0 * ib));
+        asm volatile("; z: x part" ::: "memory");
+      } else if (k0 + mn_kr(w, j, lane) < B) {
+        dma16(rh, dst, vh[j], (uint32_t)(k0 * hb));
+        asm volatile("; z: h0 part" ::: "memory");
+      } else {
+        dma16(ry, dst, vh[j], (uint32_t)(k0 * hb));
+        asm volatile("; z: y part" ::: "memory");
+      }
+    }
+  }
+};
 
 __device__ __forceinline__ u32x4_t frag_krows(const char* lds, int row, int c) {
   return *(const u32x4_t*)(lds + row * 64 + ((c ^ krow_swz(row)) << 4));
@@ -488,14 +601,15 @@ __device__ __forceinline__ u32x4_t frag_mnrows(const char* lds, int rbase, int l
 }
 
 template <typename T, int AMN, int BMN, class AOp, class BOp, class Epi>
-__global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_kernel(GemmArgs<AOp, BOp, Epi> g,
-                                                                         const void* zero16) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+__global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_kernel(GemmArgs<AOp, BOp, Epi> g) {
   constexpr int TILE = LdsCfg<T>::kTile, NT = LdsCfg<T>::kThreads, KST = LdsCfg<T>::kKStage;
   constexpr int STAGE = lds_stage_bytes<T>();
+  __shared__ __attribute__((aligned(16))) char ring0[STAGE], ring1[STAGE], ring2[STAGE], ring3[STAGE];
   constexpr int WGN = LdsCfg<T>::kWaves / 2;  // waves along n (2 along m)
   constexpr int WM = TILE / 2 / 16, WN = TILE / WGN / 16;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the wave index is uniform: saying so keeps the direct-to-LDS addresses in
+  // scalar registers (a divergent one would be iterated over lane values)
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   if ((int)blockIdx.z == g.splits) {  // extra duties: clearing, db sum
     const int64_t nblk = (int64_t)gridDim.x * gridDim.y;
     const int64_t blk = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
@@ -519,12 +633,11 @@ __global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_kernel(GemmAr
   const int64_t kt_begin = (int64_t)split * g.ktiles_per_split;
   const int64_t kt_end = kt_begin + g.ktiles_per_split < ktiles ? kt_begin + g.ktiles_per_split : ktiles;
 
-  auto issue = [&](int64_t kt) {
-    char* st = smem + (int)((kt - kt_begin) % kStages) * STAGE;
-    if constexpr (AMN) dma_mnrows<T>(g.a, st, m0, kt * KST, w, lane, zero16);
-    else dma_krows<T>(g.a, st, m0, kt * KST, w, lane);
-    if constexpr (BMN) dma_mnrows<T>(g.b, st + STAGE / 2, n0, kt * KST, w, lane, zero16);
-    else dma_krows<T>(g.b, st + STAGE / 2, n0, kt * KST, w, lane);
+  const Dma<T, AOp, (bool)AMN> da(g.a, m0, w, lane);
+  const Dma<T, BOp, (bool)BMN> db(g.b, n0, w, lane);
+  auto issue = [&](int64_t kt, char* st) {
+    da.issue(st, kt * KST, w, lane);
+    db.issue(st + STAGE / 2, kt * KST, w, lane);
   };
 
   f32x4_t acc[WM][WN];
@@ -540,42 +653,54 @@ __global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_kernel(GemmAr
     colt[j] = (g.splits == 1 && (g.N & 3) == 0 && n + 3 < g.N) ? g.epi.col4(n) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-#pragma unroll
-  for (int s = 0; s < kStages - 1; ++s)
-    if (kt_begin + s < kt_end) issue(kt_begin + s);
-
-  for (int64_t kt = kt_begin; kt < kt_end; ++kt) {
-    // stage kt is complete once at most (stages issued after it) x 4 loads
-    // of this wave are outstanding (s_waitcnt immediate: vmcnt bits [3:0]
-    // and [15:14], expcnt and lgkmcnt at their no-wait maxima); the barrier
-    // then covers the other waves -- a bare barrier, since __syncthreads()
-    // would also wait for every load in flight
+  // One stage: stage kt (in `cur`) is complete once at most (stages issued
+  // after it) x 4 loads of this wave are outstanding (s_waitcnt immediate:
+  // vmcnt bits [3:0] and [15:14], expcnt and lgkmcnt at their no-wait
+  // maxima); the barrier then covers the other waves -- a bare barrier,
+  // since __syncthreads() would also wait for every load in flight -- and
+  // also tells that every wave is done with `nxt`, refilled with stage kt+3.
+  auto stage = [&](int64_t kt, const char* cur, char* nxt) {
+    const int ln = lane, lfr = fr, lfq = fq;
     const int64_t after = kt_end - 1 - kt;
     if (after >= kStages - 2) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
     else if (after == 1) __builtin_amdgcn_s_waitcnt(0x0F74);       // vmcnt(4)
     else __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0)
-    __builtin_amdgcn_s_barrier();  // also: every wave is done with the stage about to be refilled
-    if (kt + kStages - 1 < kt_end) issue(kt + kStages - 1);
-    const char* sa = smem + (int)((kt - kt_begin) % kStages) * STAGE;
-    const char* sb = sa + STAGE / 2;
+    __builtin_amdgcn_s_barrier();
+    if (kt + kStages - 1 < kt_end) issue(kt + kStages - 1, nxt);
+    const char* sa = cur;
+    const char* sb = cur + STAGE / 2;
     u32x4_t bfv[WN];
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
-      if constexpr (BMN) bfv[j] = frag_mnrows<T>(sb, wn * 16 * WN + 16 * j, lane);
-      else bfv[j] = frag_krows(sb, wn * 16 * WN + 16 * j + fr, fq);
+      if constexpr (BMN) bfv[j] = frag_mnrows<T>(sb, wn * 16 * WN + 16 * j, ln);
+      else bfv[j] = frag_krows(sb, wn * 16 * WN + 16 * j + lfr, lfq);
     }
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
       u32x4_t af;
-      if constexpr (AMN) af = frag_mnrows<T>(sa, wm * 16 * WM + 16 * i, lane);
-      else af = frag_krows(sa, wm * 16 * WM + 16 * i + fr, fq);
+      if constexpr (AMN) af = frag_mnrows<T>(sa, wm * 16 * WM + 16 * i, ln);
+      else af = frag_krows(sa, wm * 16 * WM + 16 * i + lfr, lfq);
       // B as the MFMA's first operand: the tile comes out transposed, lane
       // (fr, fq) holding C[m = .. + fr][n = .. + 4 fq + e], four
       // consecutive columns for one row -- one 16-byte store per tile
 #pragma unroll
       for (int j = 0; j < WN; ++j) acc[i][j] = Mfma<T>::mac(bfv[j], af, acc[i][j]);
     }
+  };
+
+  if (kt_begin + 0 < kt_end) issue(kt_begin + 0, ring0);
+  if (kt_begin + 1 < kt_end) issue(kt_begin + 1, ring1);
+  if (kt_begin + 2 < kt_end) issue(kt_begin + 2, ring2);
+  int64_t kt = kt_begin;
+  for (; kt + kStages - 1 < kt_end; kt += kStages) {
+    stage(kt, ring0, ring3);
+    stage(kt + 1, ring1, ring0);
+    stage(kt + 2, ring2, ring1);
+    stage(kt + 3, ring3, ring2);
   }
+  if (kt < kt_end) stage(kt, ring0, ring3);
+  if (kt + 1 < kt_end) stage(kt + 1, ring1, ring0);
+  if (kt + 2 < kt_end) stage(kt + 2, ring2, ring1);
 
   const bool vec_n = (g.N & 3) == 0;
 #pragma unroll
@@ -667,6 +792,8 @@ static hipError_t run_gemm(const Plan& p, int64_t M, int64_t N, int64_t K, const
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+// operands of the pipelined path are addressed through buffer descriptors
+static bool small_buf(int64_t elems, int esize) { return elems * esize < ((int64_t)1 << 31); }
 
 // Pipelined path (gemm_lds_kernel): K is split (powers of two) while the
 // tiles do not cover the CUs and every split keeps at least 8 stages.
@@ -686,8 +813,8 @@ static GemmShape choose_shape_lds(int64_t M, int64_t N, int64_t K, int cus, int 
 
 template <typename T, int AMN, int BMN, class AOp, class BOp, class Epi>
 static hipError_t run_gemm_lds(const Plan& p, int64_t M, int64_t N, int64_t K, const AOp& a, const BOp& b,
-                               const Epi& e, float* part, void* zero, size_t zero_bytes, const void* zero16,
-                               hipStream_t s, DbDuty db = DbDuty{nullptr, nullptr, 0, 0, 0, 0}) {
+                               const Epi& e, float* part, void* zero, size_t zero_bytes, hipStream_t s,
+                               DbDuty db = DbDuty{nullptr, nullptr, 0, 0, 0, 0}) {
   constexpr int TILE = LdsCfg<T>::kTile;
   const GemmShape gs = choose_shape_lds<T>(M, N, K, p.cus, part ? p.max_splits : 1);
   const int64_t ktiles = K / LdsCfg<T>::kKStage;
@@ -697,12 +824,9 @@ static hipError_t run_gemm_lds(const Plan& p, int64_t M, int64_t N, int64_t K, c
                             db.src, db.out, db.rows, db.bf16, db.cols, db.H, p.nxcd};
   const unsigned gz = (unsigned)gs.splits + ((g.zero_words > 0 || g.dsum_out) ? 1u : 0u);
   dim3 grid((unsigned)((N + TILE - 1) / TILE), (unsigned)((M + TILE - 1) / TILE), gz);
-  const size_t lds = (size_t)kStages * lds_stage_bytes<T>();
-  auto fn = gemm_lds_kernel<T, AMN, BMN, AOp, BOp, Epi>;
-  hipError_t err = hipFuncSetAttribute((const void*)fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(fn, grid, dim3(LdsCfg<T>::kThreads), lds, s, g, zero16);
-  err = hipGetLastError();
+  auto fn = gemm_lds_kernel<T, AMN, BMN, AOp, BOp, Epi>;  // the ring is static LDS
+  hipLaunchKernelGGL(fn, grid, dim3(LdsCfg<T>::kThreads), 0, s, g);
+  hipError_t err = hipGetLastError();
   if (err != hipSuccess || gs.splits == 1) return err;
   const int64_t n = M * N;
   hipLaunchKernelGGL(splitk_reduce<Epi>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, part, M, N, gs.splits, e);
@@ -716,8 +840,9 @@ static hipError_t inproj_t(const Plan& p, const void* x, const void* W, const vo
   KRowsX<T> a{(const T*)x, p.I, p.TB, p.I, aligned16(x) && p.I % VEC == 0};
   KRowsWx<T> bw{(const T*)W, p.H, p.Z, p.G4, p.I, aligned16(W) && p.Z % VEC == 0 && p.H % VEC == 0};
   EpiP e{P, b, p.H, p.G4, p.dtype};
-  if (p.I % LdsCfg<T>::kKStage == 0 && lds_depth_ok<T>(p.I) && a.vec_ok && bw.vec_ok && p.TB > 0)
-    return run_gemm_lds<T, 0, 0>(p, p.TB, p.G4, p.I, a, bw, e, part, zero, zero_bytes, zero, s);
+  if (p.I % LdsCfg<T>::kKStage == 0 && lds_depth_ok<T>(p.I) && a.vec_ok && bw.vec_ok && p.TB > 0 &&
+      small_buf(p.TB * p.I, p.esize) && small_buf(p.G4 * p.Z, p.esize))
+    return run_gemm_lds<T, 0, 0>(p, p.TB, p.G4, p.I, a, bw, e, part, zero, zero_bytes, s);
   return run_gemm<T, KRowsX<T>, false, KRowsWx<T>, false, EpiP>(p, p.TB, p.G4, p.I, a, bw, e, part, zero, zero_bytes, s);
 }
 
@@ -728,16 +853,16 @@ static hipError_t dx_t(const Plan& p, const void* dG, const void* W, void* dx, f
   KRowsX<T> a{(const T*)dG, p.G4, p.TB, p.G4, aligned16(dG) && p.G4 % VEC == 0};
   MNRowsWx<T> bw{(const T*)W, p.H, p.Z, p.I, p.G4, aligned16(W) && p.Z % VEC == 0 && p.H % VEC == 0};
   EpiStore<T> e{(T*)dx, p.I};
-  if (p.G4 % LdsCfg<T>::kKStage == 0 && lds_depth_ok<T>(p.G4) && p.I >= VEC && a.vec_ok && bw.vec_ok && p.TB > 0)
-    return run_gemm_lds<T, 0, 1>(p, p.TB, p.I, p.G4, a, bw, e, part, zero, zero_bytes, zero, s);
+  if (p.G4 % LdsCfg<T>::kKStage == 0 && lds_depth_ok<T>(p.G4) && p.I >= VEC && a.vec_ok && bw.vec_ok && p.TB > 0 &&
+      small_buf(p.TB * p.G4, p.esize) && small_buf(p.G4 * p.Z, p.esize))
+    return run_gemm_lds<T, 0, 1>(p, p.TB, p.I, p.G4, a, bw, e, part, zero, zero_bytes, s);
   return run_gemm<T, KRowsX<T>, false, MNRowsWx<T>, true, EpiStore<T>>(p, p.TB, p.I, p.G4, a, bw, e, part, zero,
                                                                        zero_bytes, s);
 }
 
 template <typename T>
 static hipError_t dw_t(const Plan& p, const void* dG, const void* x, const void* h0, const void* y, void* dW,
-                       float* part, void* zero, size_t zero_bytes, const float* DBP, void* db, const void* zero16,
-                       hipStream_t s) {
+                       float* part, void* zero, size_t zero_bytes, const float* DBP, void* db, hipStream_t s) {
   constexpr int VEC = 16 / sizeof(T);
   MNRowsPlain<T> a{(const T*)dG, p.G4, p.G4, p.TB, aligned16(dG) && p.G4 % VEC == 0};
   MNRowsZ<T> bz{(const T*)x, (const T*)h0, (const T*)y, p.B, p.H, p.I, p.Z, p.TB,
@@ -745,8 +870,8 @@ static hipError_t dw_t(const Plan& p, const void* dG, const void* x, const void*
   EpiDW<T> e{(T*)dW, p.H, p.Z};
   const DbDuty dd{DBP, db, p.nBG, p.G4, p.H, p.dtype};
   if (p.TB % LdsCfg<T>::kKStage == 0 && lds_depth_ok<T>(p.TB) && p.Z >= VEC && a.vec_ok && bz.vec_ok &&
-      aligned16(zero16))
-    return run_gemm_lds<T, 1, 1>(p, p.G4, p.Z, p.TB, a, bz, e, part, zero, zero_bytes, zero16, s, dd);
+      small_buf(p.TB * p.G4, p.esize) && small_buf(p.TB * p.Z, p.esize))
+    return run_gemm_lds<T, 1, 1>(p, p.G4, p.Z, p.TB, a, bz, e, part, zero, zero_bytes, s, dd);
   return run_gemm<T, MNRowsPlain<T>, true, MNRowsZ<T>, true, EpiDW<T>>(p, p.G4, p.Z, p.TB, a, bz, e, part, zero,
                                                                        zero_bytes, s, dd);
 }
@@ -762,10 +887,9 @@ hipError_t launch_gemm_dx(const Plan& p, const void* dG, const void* W, void* dx
                  : dx_t<float>(p, dG, W, dx, part, zero, zero_bytes, s);
 }
 hipError_t launch_gemm_dw(const Plan& p, const void* dG, const void* x, const void* h0, const void* y, void* dW,
-                          float* part, void* zero, size_t zero_bytes, const float* DBP, void* db, const void* zero16,
-                          hipStream_t s) {
-  return p.dtype ? dw_t<bf16_t>(p, dG, x, h0, y, dW, part, zero, zero_bytes, DBP, db, zero16, s)
-                 : dw_t<float>(p, dG, x, h0, y, dW, part, zero, zero_bytes, DBP, db, zero16, s);
+                          float* part, void* zero, size_t zero_bytes, const float* DBP, void* db, hipStream_t s) {
+  return p.dtype ? dw_t<bf16_t>(p, dG, x, h0, y, dW, part, zero, zero_bytes, DBP, db, s)
+                 : dw_t<float>(p, dG, x, h0, y, dW, part, zero, zero_bytes, DBP, db, s);
 }
 
 // Bytes of fp32 split-K partials the three products need for this plan.

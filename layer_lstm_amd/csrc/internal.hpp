@@ -82,8 +82,7 @@ hipError_t launch_gemm_dx(const Plan& p, const void* dG, const void* W, void* dx
 // The dW launch also writes db[row(n)] = sum_bg DBP[bg][n] (in bg order) when
 // db is not null.
 hipError_t launch_gemm_dw(const Plan& p, const void* dG, const void* x, const void* h0, const void* y, void* dW,
-                          float* part, void* zero, size_t zero_bytes, const float* DBP, void* db, const void* zero16,
-                          hipStream_t s);
+                          float* part, void* zero, size_t zero_bytes, const float* DBP, void* db, hipStream_t s);
 size_t gemm_partial_bytes(const Plan& p, int cus);
 
 hipError_t launch_fwd_recurrent(const Plan& p, const float* P, const void* W, const void* h0,

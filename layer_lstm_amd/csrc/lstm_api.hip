@@ -347,10 +347,8 @@ int lstm_bwd(const lstm_shape* shape, const void* dy, const void* dhT, const voi
   }
   if (err == hipSuccess) {
     Timed tm(3, s);
-    // bytes 128..143 of the control block are a zero word (cleared with it
-    // by every forward), the source of absent initial-state rows
     err = launch_gemm_dw(p, dG, x, h0, y, dW, (float*)(ws + p.off_gp), ws + p.off_PX, p.bytes_PX,
-                         (const float*)(ws + p.off_dbp), db, ws + p.off_ctrl + 128, s);
+                         (const float*)(ws + p.off_dbp), db, s);
   }
   if (err == hipSuccess && p.I > 0) {
     Timed tm(4, s);

@@ -54,7 +54,10 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
   constexpr int NJS = 16 * MT + 4;                    // LDS row of a wave's partial tile (floats)
   static_assert(NKB % CK == 0, "chunks divide the k-blocks");
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the wave index is uniform (said so, it stays in scalar registers and the
+  // branches on it are scalar branches: an s_waitcnt under a divergent branch
+  // would run for every wave)
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, fq = lane >> 4;
   int bg, jg;
   take_role(a.nBG, a.nJG, a.nxcd, a.local, bg, jg);

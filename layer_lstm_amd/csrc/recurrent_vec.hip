@@ -54,7 +54,10 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_vec_kernel(FwdArgs a) {
   constexpr int CS = L + 4;    // chunk stride (floats)
   constexpr int RS = 32 * CS;  // row stride
   constexpr int LG_L = L == 4 ? 2 : L == 8 ? 3 : L == 16 ? 4 : 5;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the wave index is uniform (said so, it stays in scalar registers and the
+  // branches on it are scalar branches: an s_waitcnt under a divergent branch
+  // would run for every wave)
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   int bg, jg;
   take_role(a.nBG, a.nJG, a.nxcd, a.local, bg, jg);
   const bool local = a.local != 0;
