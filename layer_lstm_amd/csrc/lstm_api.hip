@@ -124,7 +124,9 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
     const int64_t mx = fw > bw ? fw : bw;
     p->words_per_thread = (int)((mx + 255) / 256);
   }
-  if (2 * (int64_t)p->Bp * 4 * Hp * e >= ((int64_t)1 << 31)) return LSTM_ERR_UNSUPPORTED;
+  // the gate-delta ring holds whole 16-row tiles per batch group
+  const int64_t ring_rows = (int64_t)p->nBG * (p->NB < 16 ? 16 : p->NB);
+  if (2 * ring_rows * 4 * Hp * e >= ((int64_t)1 << 30)) return LSTM_ERR_UNSUPPORTED;
 
   p->max_splits = 8;
   p->xcd_local = p->nxcd > 1 && p->nBG % p->nxcd == 0;
@@ -132,9 +134,10 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
   const size_t HW = dtype ? (size_t)p->Hp / 2 : (size_t)p->Hp;
   // HX: tagged words [2][Bp][HW] (VALU forward), or packed h [2][Bp][Hp] +
   // flags [nBG][nJG]; PX: tagged words [2][nBG][nJG][Hp][NB] (VALU
-  // backward), or packed gate deltas [2][Bp][4Hp] + flags [nBG][nJG]
+  // backward), or gate deltas in 16-row tiles [2][nBG][max(NB,16)][4Hp] +
+  // flags [nBG][nJG]
   p->off_hflags = align256(2 * (size_t)p->Bp * p->Hp * e);
-  p->off_pflags = align256(2 * (size_t)p->Bp * 4 * p->Hp * e);
+  p->off_pflags = align256(2 * (size_t)ring_rows * 4 * p->Hp * e);
   const size_t nflag = align256((size_t)p->nBG * p->nJG * 4);
   size_t hx = p->off_hflags + nflag, px = p->off_pflags + nflag;
   if (fwd_vec_ok(*p) && hx < 2 * (size_t)p->Bp * HW * 8) hx = 2 * (size_t)p->Bp * HW * 8;

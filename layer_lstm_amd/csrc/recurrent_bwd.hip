@@ -21,17 +21,21 @@
 //      flight), then summing their partial tiles through LDS in a fixed
 //      order;
 //   2. runs the elementwise chain for its (row, unit) elements, writes dG_t
-//      (for the dW / dx products) and publishes it into the ring slot t&1 as
-//      packed rows of 4Hp gate deltas (interleaved gates, 4u + g), then its
-//      step flag.
+//      (for the dW / dx products) and publishes it into the ring slot t&1,
+//      then its step flag.
 // Nothing is summed across work-groups, so every work-group reads only
 // dG values (NB * 4H per step, shared by the nJG readers of a batch group
 // in L2) and writes only its own 4*NJ columns of them.
 //
-// Rows of the ring past B, and the columns past 4H, are never written and
-// stay zero (the ring is cleared before the forward and after every
-// backward); B fragments of tile rows past NB are read out of the buffer's
-// range, which returns zeros.
+// Ring layout, in MFMA fragment order: a slot holds, for each batch group
+// and each of its 16-row batch tiles, the 4Hp gate deltas (interleaved gates,
+// gate row r = 4u + g) of the tile's rows as Hp*E/16 chunks of 1 KB; chunk kc
+// holds the 64 bytes of gate rows [kc*64/E, +64/E) of each row, lane l = 16q
+// + f of the B fragment (tile row f, bytes [16q, +16) of the chunk's rows) at
+// bytes [16l, +16).  A wave's fragment load is one contiguous kilobyte.
+// Gate rows past 4H are never written and stay zero (the ring is cleared
+// before the forward and after every backward); B fragments of tile rows
+// past NB are read out of the buffer's range, which returns zeros.
 #include "recurrent_common.hpp"
 
 namespace lstm {
@@ -69,7 +73,7 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
   float* red = (float*)smem;                          // [NW][NBr][NJS] per-wave partial dh
   float* dba = red + NW * NBr * NJS;                  // [nel][4] db: gate deltas summed over time
   const int64_t G4 = 4 * (int64_t)a.H;
-  const uint32_t rowG = 4u * (uint32_t)a.Hp * E;      // bytes per ring row
+  constexpr uint32_t kTileB = (uint32_t)NW * NKB * 1024; // bytes of one 16-row tile of the ring
   const __amdgpu_buffer_rsrc_t gd_rsrc = make_rsrc(a.GD, a.gd_bytes);
   bool dead = false;
 
@@ -114,14 +118,14 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
     }
     __syncthreads();  // the staging area is reused below
   }
-  // ring byte offset (slot 0) of this lane's B fragments: row b0 + 16*nt + fr,
-  // k-block w*NKB; tile rows past NB point out of the buffer (zeros)
+  // ring byte offset (slot 0) of this lane's B fragments: tile nt of the
+  // batch group, chunk w*NKB; tile rows past NB point out of the buffer (zeros)
   uint32_t boff[NBT];
 #pragma unroll
   for (int nt = 0; nt < NBT; ++nt)
-    boff[nt] = 16 * nt + fr < a.NB ? (uint32_t)(b0 + 16 * nt + fr) * rowG + (uint32_t)(w * NKB * 64 + fq * 16)
+    boff[nt] = 16 * nt + fr < a.NB ? (uint32_t)(bg * NBT + nt) * kTileB + (uint32_t)(w * NKB * 1024 + lane * 16)
                                    : 0xC0000000u;
-  const uint32_t slotB = (uint32_t)a.Bp * rowG;
+  const uint32_t slotB = (uint32_t)a.nBG * NBT * kTileB;
 
   // --- elementwise ownership: element e = tid + NTH*s (s < EPTM), unit fastest
   // (b, u) of element e and its offset in [B][H] tensors; in [B][4H] tensors
@@ -248,7 +252,7 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
         for (int i = 0; i < CK; ++i)
 #pragma unroll
           for (int nt = 0; nt < NBT; ++nt)
-            bb[buf][i][nt] = load16_coherent(gd_rsrc, sb + boff[nt] + (uint32_t)((ch * CK + i) * 64));
+            bb[buf][i][nt] = load16_coherent(gd_rsrc, sb + boff[nt] + (uint32_t)((ch * CK + i) * 1024));
       };
       // scheduling barriers pin each chunk's loads ahead of the products of
       // the chunk before (the scheduler would otherwise trade loads in
@@ -306,7 +310,7 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
 
     // 2. gate deltas of this step; dG_t to the ring (the record follows next
     //    step)
-    T* ring = (T*)a.GD + (size_t)(t & 1) * (size_t)a.Bp * 4 * a.Hp;
+    char* ring = (char*)a.GD + (t & 1) * slotB;
     const char* slot = opl + (t & 1) * SLOT;
 #pragma unroll
     for (int s = 0; s < EPTM; ++s) {
@@ -356,7 +360,11 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
         }
         dcc[s] = dc * gf;
         *(f32x4_t*)(dba + 4 * (tid + NTH * s)) += f32x4_t{d_i, d_f, d_g, d_o};
-        T* rp = ring + (uint32_t)elem_b(s) * (uint32_t)(4 * a.Hp) + 4u * (uint32_t)elem_u(s);
+        // gate rows 4u..4u+3 of row bl: chunk kc, bytes [o, o + 4E) of it
+        const uint32_t bl = (uint32_t)(elem_b(s) - b0), ob = 4u * E * (uint32_t)elem_u(s);
+        const uint32_t kc = ob >> 6, o = ob & 63;
+        T* rp = (T*)(ring + (uint32_t)(bg * NBT + (bl >> 4)) * kTileB + kc * 1024 +
+                     ((o >> 4) * 16 + (bl & 15)) * 16 + (o & 15));
         if constexpr (E == 4) {
           if (local) {
             *(u32x4_t*)rp = __builtin_bit_cast(u32x4_t, dq);

@@ -38,7 +38,7 @@ struct BwdArgs {
   const float* Cs;
   void* dG;         // [TB][4H] gate deltas, interleaved
   uint64_t* PX;     // [2][nBG][nJG][Hp][NB] exchange words (fp32 partials; VALU kernel)
-  void* GD;         // [2][Bp][4Hp] packed gate deltas, interleaved, T elements (MFMA kernel)
+  void* GD;         // [2][nBG][16-row tiles] gate deltas in MFMA fragment order, T elements (MFMA kernel)
   uint32_t* GF;     // [nBG][nJG] step flags of the MFMA kernel
   uint32_t gd_bytes;
   float* DBP;       // [nBG][4H] per-batch-group db partials, interleaved gates
