@@ -76,13 +76,15 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
           if (nBG * nJG > cus) continue;
           if (pass == 0 && !(p->nxcd > 1 && nBG % p->nxcd == 0)) continue;
           const int NBr = NB < 16 ? 16 : NB;
-          // forward: NJ/4 M-tiles of 16 interleaved gate rows, the waves of
-          // an M-tile splitting k
+          // forward: NJ/4 M-tiles of 16 interleaved gate rows in groups of
+          // MW, the waves of a group splitting k; two tiles per wave when k
+          // splits far enough (the same W_h values per wave either way)
           const int MTf = NJ / 4;
           if (MTf > NW) continue;
-          const int KS = NW / MTf;
+          const int MW = (MTf % 2 == 0 && Hp / ((2 * NW / MTf) * KB) >= 1) ? 2 : 1;
+          const int KS = NW * MW / MTf;
           const int nkbw = Hp / (KS * KB);
-          if (nkbw < 1 || nkbw > 32) continue;
+          if (nkbw < 1 || MW * nkbw > 32) continue;
           const size_t lds_f = (size_t)NBr * (Hp * e + 16) + (size_t)MTf * (KS - 1) * (NBr / 16) * 1024;
           if (lds_f > 160 * 1024) continue;
           // the W_h slice is gathered through LDS at the start (recurrent.hip)
@@ -106,6 +108,7 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
           p->NB = NB; p->NJ = NJ; p->nBG = (int)nBG; p->nJG = (int)nJG; p->grid = (int)(nBG * nJG);
           p->waves = NW;
           p->fwd_nkbw = nkbw;
+          p->fwd_mw = MW;
           p->bwd_valu = valu ? 1 : 0;
           p->bwd_mt = MTb;
           p->bwd_nkb = nkb;

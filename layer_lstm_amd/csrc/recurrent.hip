@@ -30,13 +30,20 @@
 // Compile-time shapes (H is padded to Hp, a power of two): NKBW k-blocks of
 // W_h per wave, NBT 16-row batch tiles, C ring chunks in flight per thread
 // (0: direct-to-LDS copy), NW waves (8-wave work-groups hold twice the W_h
-// slice of 4-wave ones).
+// slice of 4-wave ones), MW M-tiles per wave.
+//
+// Waves: the NJ/4 M-tiles (16 interleaved gate rows = 4 units each) form
+// groups of MW; the KS = NW*MW/(NJ/4) waves of a group split k, each taking
+// all MW M-tiles of the group over its k part, so one LDS read of h feeds MW
+// products (the product is bound by LDS reads of h).  Wave wk < MW of a
+// group owns M-tile wk of it: it receives the other waves' partial sums of
+// that tile and runs its elementwise step.
 #include "recurrent_common.hpp"
 
 namespace lstm {
 
 // ---------------------------------------------------------------------------
-template <typename T, int NBT, int NKBW, int C, int NW = kWaves>
+template <typename T, int NBT, int NKBW, int C, int NW, int MW>
 __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
   constexpr int NTH = 64 * NW;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -49,8 +56,10 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
   const bool local = a.local != 0;
   const int b0 = bg * a.NB, j0 = jg * a.NJ;
   const int MT = a.NJ / 4;                   // M-tiles (16 interleaved gate rows = 4 units)
-  const int KS = NW / MT;                // waves splitting k per M-tile
-  const int mt = w / KS, wk = w % KS;        // this wave's M-tile and k part
+  const int KS = NW * MW / MT;               // waves splitting k per group of MW M-tiles
+  const int mg = w / KS, wk = w % KS;        // this wave's M-tile group and k part
+  const bool owner = wk < MW;                // owns M-tile mg*MW + wk
+  const int mt = mg * MW + (owner ? wk : 0); // the owned M-tile
   const int kb0 = wk * NKBW;
   const int strideH = a.Hp * E + 16;         // LDS row of h_{t-1}
   const int NBr = a.NB < 16 ? 16 : a.NB;     // rows of the batch tiles (rows >= NB stay zero)
@@ -60,13 +69,14 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
   const int u = j0 + 4 * mt + fq;            // unit of this lane's elementwise results
   bool dead = false;
 
-  // --- resident W_h fragments: rows 16*mt + fr (gate fr&3 of unit 4*mt +
-  // fr/4), k-blocks kb0 + i.  Gathered through a wave-private LDS area in
-  // passes of PB k-blocks: the wave reads its 16 rows with consecutive lanes
-  // on consecutive columns, and every lane then takes each of its fragments
-  // with one 16-byte LDS read.
-  u32x4_t wreg[NKBW];
-  {
+  // --- resident W_h fragments: rows 16*(mg*MW + mi) + fr (gate fr&3 of unit
+  // 4*(mg*MW + mi) + fr/4), k-blocks kb0 + i.  Gathered through a
+  // wave-private LDS area in passes of PB k-blocks: the wave reads its 16 rows
+  // with consecutive lanes on consecutive columns, and every lane then takes
+  // each of its fragments with one 16-byte LDS read.
+  u32x4_t wreg[MW][NKBW];
+#pragma unroll
+  for (int mi = 0; mi < MW; ++mi) {
     constexpr int PB = NKBW < 8 ? NKBW : 8;             // k-blocks per pass (8 KB of LDS per wave)
     constexpr int CWL = PB * KB;                        // staged columns per row
     constexpr int RSW = CWL + 16 / E;                   // staged row (elements), padded
@@ -78,7 +88,7 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
 #pragma unroll
       for (int j = 0; j < LPT; ++j) {
         const int e = lane + 64 * j, row = e / CWL, col = e % CWL;
-        const int ur = j0 + 4 * mt + (row >> 2), g = row & 3;
+        const int ur = j0 + 4 * (mg * MW + mi) + (row >> 2), g = row & 3;
         const int k = (kb0 + p * PB) * KB + col;
         const bool ok = ur < a.H && k < a.H;
         v[j] = ((const T*)a.W)[ok ? ((int64_t)g * a.H + ur) * a.Z + k : 0];
@@ -91,17 +101,17 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
       }
 #pragma unroll
       for (int ii = 0; ii < PB; ++ii)
-        wreg[p * PB + ii] = *(const u32x4_t*)(stage + fr * RSW + ii * KB + fq * (16 / E));
+        wreg[mi][p * PB + ii] = *(const u32x4_t*)(stage + fr * RSW + ii * KB + fq * (16 / E));
     }
-    __syncthreads();  // the staging area is reused below
   }
+  __syncthreads();  // the staging area is reused below
   const int NBv = (a.B - b0) < a.NB ? (a.B - b0) : a.NB;  // valid rows of this group
   // --- zero the padding of h_{t-1} in LDS once (k >= H, rows past the group or B)
   for (int idx = tid; idx < NBr * a.Hp; idx += NTH) {
     const int bl = idx / a.Hp, k = idx % a.Hp;
     if (k >= a.H || bl >= NBv) *(T*)(Hl + bl * strideH + k * E) = T(0);
   }
-  // --- cell state of this lane's elements (wk == 0 waves own the elementwise)
+  // --- cell state of this lane's elements (owner waves run the elementwise)
   float cst[NBT];
 #pragma unroll
   for (int nt = 0; nt < NBT; ++nt) {
@@ -121,7 +131,7 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
   // the ring reads of the next step.  A wave's vector-memory operations
   // complete in issue order, so operations issued before the ring reads
   // would hold up the wait for them; issued after, they drain while the
-  // product runs.  Each lane of a wk == 0 wave issues exactly kDefer of them
+  // product runs.  Each lane of an owner wave issues exactly kDefer of them
   // per step, whatever its element's validity (buffer operations out of
   // range do nothing), which lets the ring wait name the count.
   constexpr int kDefer = 4 * NBT;
@@ -169,7 +179,7 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(cq[nt]), rc, 4 * o, 0, 0);
     }
   };
-  if (wk == 0) load_p(pf, 0);
+  if (owner) load_p(pf, 0);
 
   for (int t = 0; t < a.T; ++t) {
     stamp(a.stamps, a.T, t, 0);
@@ -184,7 +194,7 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
         const T v = a.h0 ? ((const T*)a.h0)[(int64_t)(b0 + bl) * a.H + k] : T(0);
         *(T*)(Hl + bl * strideH + k * E) = v;
       }
-      if (wk == 0) load_p(pfn, 1);
+      if (owner) load_p(pfn, 1);
       wait_vmem();
       __syncthreads();
     } else {
@@ -215,7 +225,7 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
         }
       }
       asm volatile("" ::: "memory");
-      if (wk == 0) {
+      if (owner) {
         store_record(t - 1);
         load_p(pfn, t + 1);
       }
@@ -223,66 +233,84 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
       // the ring reads of this wave are done once at most the deferred
       // operations are outstanding; LDS writes (register path) once lgkmcnt
       // is 0; the barrier then covers the other waves
-      if (C == 0 && wk == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDefer));
+      if (C == 0 && owner) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDefer));
       else if (C == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       else __builtin_amdgcn_s_waitcnt(kLgkm0);
       __builtin_amdgcn_s_barrier();
     }
     stamp(a.stamps, a.T, t, 2);
 
-    // MFMA: acc[nt] = W_h[rows of M-tile mt, k part] . h_{t-1}[tile nt]^T,
-    // with CH independent accumulator chains per tile (summed in a fixed order)
-    constexpr int CH = NBT == 1 ? (NKBW >= 4 ? 4 : NKBW) : (NBT == 2 && NKBW >= 2 ? 2 : 1);
-    f32x4_t acc[NBT], part[NBT][CH];
+    // MFMA: part[mi][nt] = W_h[rows of M-tile mg*MW + mi, k part] .
+    // h_{t-1}[tile nt]^T, with CH independent accumulator chains per tile
+    // (summed in a fixed order); one LDS read of h feeds the MW tiles
+    constexpr int CH = NBT * MW == 1 ? (NKBW >= 4 ? 4 : NKBW) : (NBT * MW == 2 && NKBW >= 2 ? 2 : 1);
+    f32x4_t acc[MW][NBT], part[MW][NBT][CH];
 #pragma unroll
-    for (int nt = 0; nt < NBT; ++nt)
+    for (int mi = 0; mi < MW; ++mi)
 #pragma unroll
-      for (int ch = 0; ch < CH; ++ch) part[nt][ch] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int nt = 0; nt < NBT; ++nt)
+#pragma unroll
+        for (int ch = 0; ch < CH; ++ch) part[mi][nt][ch] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const char* hb0 = Hl + fr * strideH + kb0 * 64 + fq * 16;
 #pragma unroll
     for (int i = 0; i < NKBW; ++i) {
 #pragma unroll
       for (int nt = 0; nt < NBT; ++nt) {
         const u32x4_t hb = *(const u32x4_t*)(hb0 + 16 * nt * strideH + i * 64);
-        part[nt][i % CH] = Mfma<T>::mac(wreg[i], hb, part[nt][i % CH]);
+#pragma unroll
+        for (int mi = 0; mi < MW; ++mi) part[mi][nt][i % CH] = Mfma<T>::mac(wreg[mi][i], hb, part[mi][nt][i % CH]);
       }
     }
 #pragma unroll
-    for (int nt = 0; nt < NBT; ++nt) {
-      acc[nt] = part[nt][0];
+    for (int mi = 0; mi < MW; ++mi)
 #pragma unroll
-      for (int ch = 1; ch < CH; ++ch) acc[nt] += part[nt][ch];
-    }
+      for (int nt = 0; nt < NBT; ++nt) {
+        acc[mi][nt] = part[mi][nt][0];
+#pragma unroll
+        for (int ch = 1; ch < CH; ++ch) acc[mi][nt] += part[mi][nt][ch];
+      }
     stamp(a.stamps, a.T, t, 3);
+    // k-part reduction: partial tiles go to their owners through LDS; slot
+    // (M-tile m, kk) holds the part of the kk-th non-owner wave of m's group
+    f32x4_t mine[NBT];
+#pragma unroll
+    for (int nt = 0; nt < NBT; ++nt) mine[nt] = acc[0][nt];
+#pragma unroll
+    for (int mi = 1; mi < MW; ++mi)
+      if (wk == mi)
+#pragma unroll
+        for (int nt = 0; nt < NBT; ++nt) mine[nt] = acc[mi][nt];
     if (KS > 1) {
-      if (wk != 0) {
+#pragma unroll
+      for (int mi = 0; mi < MW; ++mi) {
+        if (wk == mi) continue;
+        const int m = mg * MW + mi, kk = wk < mi ? wk : wk - 1;
 #pragma unroll
         for (int nt = 0; nt < NBT; ++nt)
-          *(f32x4_t*)(red + (((mt * (KS - 1) + wk - 1) * NBT + nt) * 64 + lane) * 4) = acc[nt];
+          *(f32x4_t*)(red + (((m * (KS - 1) + kk) * NBT + nt) * 64 + lane) * 4) = acc[mi][nt];
       }
       // LDS writes done, then the barrier (not __syncthreads: that would
       // also wait for the deferred memory operations)
       __builtin_amdgcn_s_waitcnt(kLgkm0);
       __builtin_amdgcn_s_barrier();
-      if (wk == 0) {
-        for (int k2 = 1; k2 < KS; ++k2) {
+      if (owner) {
+        for (int kk = 0; kk < KS - 1; ++kk) {
 #pragma unroll
           for (int nt = 0; nt < NBT; ++nt)
-            acc[nt] += *(const f32x4_t*)(red + (((mt * (KS - 1) + k2 - 1) * NBT + nt) * 64 + lane) * 4);
+            mine[nt] += *(const f32x4_t*)(red + (((mt * (KS - 1) + kk) * NBT + nt) * 64 + lane) * 4);
         }
       }
     }
-
     stamp(a.stamps, a.T, t, 4);
     // elementwise: gates, cell, hidden; h_t is published (stores, their
     // completion, then the flag), the record is kept for the next step
-    if (wk == 0) {
+    if (owner) {
       T* dst = HDt + (int64_t)(t & 1) * a.Bp * a.Hp;
 #pragma unroll
       for (int nt = 0; nt < NBT; ++nt) {
         const int b = b0 + 16 * nt + fr;
         const bool valid = u < a.H && 16 * nt + fr < NBv;
-        const f32x4_t z = acc[nt] + pf[nt];
+        const f32x4_t z = mine[nt] + pf[nt];
         const float ig = sigmoidf(z[0]), fg = sigmoidf(z[1]), gg = tanh_f(z[2]), og = sigmoidf(z[3]);
         const float c = fg * cst[nt] + ig * gg;
         const float h = og * tanh_f(c);
@@ -306,7 +334,7 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
     stamp(a.stamps, a.T, t, 5);
   }
   // the last step's record and the final states
-  if (wk == 0) {
+  if (owner) {
     store_record(a.T - 1);
 #pragma unroll
     for (int nt = 0; nt < NBT; ++nt) {
@@ -321,17 +349,26 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-template <typename T, int NBT, int C, int NW>
-static hipError_t fwd_dispatch_c(const Plan& p, FwdArgs& a, hipStream_t s) {
+template <typename T, int NBT, int C, int NW, int MW>
+static hipError_t fwd_dispatch_mw(const Plan& p, FwdArgs& a, hipStream_t s) {
   const int nt = 64 * NW;
   switch (p.fwd_nkbw) {
-    case 1: return coop_launch(fwd_rec_kernel<T, NBT, 1, C, NW>, p.grid, p.lds_fwd, &a, s, nt);
-    case 2: return coop_launch(fwd_rec_kernel<T, NBT, 2, C, NW>, p.grid, p.lds_fwd, &a, s, nt);
-    case 4: return coop_launch(fwd_rec_kernel<T, NBT, 4, C, NW>, p.grid, p.lds_fwd, &a, s, nt);
-    case 8: return coop_launch(fwd_rec_kernel<T, NBT, 8, C, NW>, p.grid, p.lds_fwd, &a, s, nt);
-    case 16: return coop_launch(fwd_rec_kernel<T, NBT, 16, C, NW>, p.grid, p.lds_fwd, &a, s, nt);
-    case 32: return coop_launch(fwd_rec_kernel<T, NBT, 32, C, NW>, p.grid, p.lds_fwd, &a, s, nt);
+    case 1: return coop_launch(fwd_rec_kernel<T, NBT, 1, C, NW, MW>, p.grid, p.lds_fwd, &a, s, nt);
+    case 2: return coop_launch(fwd_rec_kernel<T, NBT, 2, C, NW, MW>, p.grid, p.lds_fwd, &a, s, nt);
+    case 4: return coop_launch(fwd_rec_kernel<T, NBT, 4, C, NW, MW>, p.grid, p.lds_fwd, &a, s, nt);
+    case 8: return coop_launch(fwd_rec_kernel<T, NBT, 8, C, NW, MW>, p.grid, p.lds_fwd, &a, s, nt);
+    case 16: return coop_launch(fwd_rec_kernel<T, NBT, 16, C, NW, MW>, p.grid, p.lds_fwd, &a, s, nt);
+    case 32:
+      if constexpr (MW == 1) return coop_launch(fwd_rec_kernel<T, NBT, 32, C, NW, MW>, p.grid, p.lds_fwd, &a, s, nt);
+      break;
   }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int NBT, int C, int NW>
+static hipError_t fwd_dispatch_c(const Plan& p, FwdArgs& a, hipStream_t s) {
+  if (p.fwd_mw == 2) return fwd_dispatch_mw<T, NBT, C, NW, 2>(p, a, s);
+  if (p.fwd_mw == 1) return fwd_dispatch_mw<T, NBT, C, NW, 1>(p, a, s);
   return hipErrorInvalidValue;
 }
 
