@@ -130,9 +130,10 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 typedef __attribute__((address_space(3))) void lds_void_t;
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// (lds_addr: the LDS byte address the wave's 1 KB goes to)
 template <bool SC1>
-__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
-  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)lds);
+__device__ __forceinline__ void lds_dma16_at(__amdgpu_buffer_rsrc_t r, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_addr);
   if constexpr (SC1)
     asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, %3 offen sc1 lds"
                  :
@@ -143,6 +144,10 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, u
                  :
                  : "v"(voff), "s"(m0v), "s"(r), "s"(soff)
                  : "memory", "m0");
+}
+template <bool SC1>
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff, uint32_t soff) {
+  lds_dma16_at<SC1>(r, (uint32_t)(uintptr_t)(lds_void_t*)lds, voff, soff);
 }
 #pragma clang diagnostic pop
 

@@ -29,6 +29,7 @@ struct Plan {
   int waves;    // waves per work-group of the MFMA recurrences (4 or 8)
   int fwd_nkbw; // forward: W_h k-blocks per wave
   int fwd_mw;   // forward: M-tiles per wave (1 or 2)
+  int fwd_dma;  // forward: h ring copied by direct-to-LDS loads (rows of whole KB), split ring-read phase
   int bwd_mt;   // backward (MFMA): 16-unit tiles of W_h^T per work-group
   int bwd_nkb;  // backward (MFMA): k-blocks of the 4H gate rows per wave
   int bwd_valu; // backward runs the VALU kernel (fp32, batch groups of 4 rows)

@@ -85,7 +85,11 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
           const int KS = NW * MW / MTf;
           const int nkbw = Hp / (KS * KB);
           if (nkbw < 1 || MW * nkbw > 32) continue;
-          const size_t lds_f = (size_t)NBr * (Hp * e + 16) + (size_t)MTf * (KS - 1) * (NBr / 16) * 1024;
+          const bool fdma = (H * e) % 1024 == 0;
+          // h_{t-1}, partial tiles; direct-to-LDS path: two P buffers and
+          // the record staging area
+          size_t lds_f = (size_t)NBr * (Hp * e + 16) + (size_t)MTf * (KS - 1) * (NBr / 16) * 1024;
+          if (fdma) lds_f += (size_t)2 * NB * NJ * 16 + (size_t)NB * (5 * NJ * e + 4 * NJ + 48);
           if (lds_f > 160 * 1024) continue;
           // the W_h slice is gathered through LDS at the start (recurrent.hip)
           const size_t lds_fw = lds_f < kColStageLds ? kColStageLds : lds_f;
@@ -109,6 +113,7 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
           p->waves = NW;
           p->fwd_nkbw = nkbw;
           p->fwd_mw = MW;
+          p->fwd_dma = fdma ? 1 : 0;
           p->bwd_valu = valu ? 1 : 0;
           p->bwd_mt = MTb;
           p->bwd_nkb = nkb;

@@ -49,7 +49,9 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int E = sizeof(T);
   constexpr int KB = Mfma<T>::kBlock;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the wave index is uniform (branches on it are scalar: an s_waitcnt under
+  // a divergent branch would run for every wave)
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, fq = lane >> 4;
   int bg, jg;
   take_role(a.nBG, a.nJG, a.nxcd, a.local, bg, jg);
@@ -126,15 +128,13 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
   const __amdgpu_buffer_rsrc_t hd_rsrc = make_rsrc(a.HD, a.hd_bytes);
   T* HDt = (T*)a.HD;
 
-  // Memory traffic off the exchange path: the input projection P_{t+1} and
-  // the step's record (y_t, the activated gates, c_t) are issued right after
-  // the ring reads of the next step.  A wave's vector-memory operations
-  // complete in issue order, so operations issued before the ring reads
-  // would hold up the wait for them; issued after, they drain while the
-  // product runs.  Each lane of an owner wave issues exactly kDefer of them
-  // per step, whatever its element's validity (buffer operations out of
-  // range do nothing), which lets the ring wait name the count.
-  constexpr int kDefer = 4 * NBT;
+  // Memory traffic off the exchange path (register-copy path): the input
+  // projection P_{t+1} and the step's record (y_t, the activated gates, c_t)
+  // are issued by the owner lanes right after the ring reads of the next
+  // step.  A wave's vector-memory operations complete in issue order, so
+  // operations issued before the ring reads would hold up the wait for them;
+  // issued after, they drain while the product runs.  Lanes without an
+  // element use offsets out of the buffers' range (nothing is moved).
   const int64_t stepP = (int64_t)a.B * G4 * 4;            // bytes of P per step
   const int64_t stepY = (int64_t)a.B * a.H;               // elements of y / Cs per step
   // element (b, u) index in a [B][H] step; lanes without an element address
@@ -179,7 +179,107 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
       __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(cq[nt]), rc, 4 * o, 0, 0);
     }
   };
-  if (owner) load_p(pf, 0);
+  // Direct-to-LDS path: the ring-read phase moves h_{t-1} alone, and every
+  // wave waits for its part of it.  Right after, when the product (bound by
+  // LDS reads) leaves the memory path idle, the waves start P_{t+1} into one
+  // of two LDS buffers and write the previous step's record (y, activated
+  // gates, c) from an LDS staging area as whole 16-byte pieces of its rows;
+  // these drain during the product and the gate math and are complete at the
+  // publish, which waits for every operation of every wave.  The owners read
+  // P_t from LDS and stage the step's record there.
+  constexpr bool SPLIT = C == 0;
+  const int lgNJ = 31 - __builtin_clz(a.NJ);
+  const int nbj = a.NB * a.NJ;                            // 16-byte P chunks (4 gates) per step
+  char* Pl = (char*)(red + MT * (KS - 1) * NBT * 256);    // [2][NB][NJ] chunks, chunk c of row bl at c ^ (bl % NJ)
+  const int hSr = a.NJ * E + 16, gSr = 4 * a.NJ * E + 16, cSr = 4 * a.NJ + 16;  // padded staging rows (bytes)
+  const uint32_t pl_lds = (uint32_t)(uintptr_t)(lds_void_t*)smem + (uint32_t)(Pl - smem);  // LDS address of Pl
+  char* hS = Pl + 2 * nbj * 16;                           // [NB][NJ] h
+  char* gS = hS + a.NB * hSr;                             // [NB][NJ][4] activated gates
+  char* cS = gS + a.NB * gSr;                             // [NB][NJ] c (fp32)
+  // Per-lane pieces of these copies, fixed for the launch: wave-load j = w +
+  // NW*i of P moves chunk slot 64j + lane; record piece i of a tensor is
+  // piece tid + NTH*i of its NBv rows (16 bytes each), at an LDS source and a
+  // byte offset in the step's slab of the tensor (out of range when the
+  // piece does not exist: the store is dropped)
+  constexpr int RJ = (NBT * 8 + NW - 1) / NW;             // P wave-loads per wave, at most
+  constexpr int RY = (NBT * 64 * E + NTH - 1) / NTH;      // y pieces per lane (NB <= 16*NBT, NJ <= 32)
+  constexpr int RG = (NBT * 256 * E + NTH - 1) / NTH;     // gate pieces
+  constexpr int RC = (NBT * 128 + NTH - 1) / NTH;         // c pieces
+  uint32_t pvo[RJ], yso[RY], yvo[RY], gso[RG], gvo[RG], cso[RC], cvo[RC];
+  if constexpr (SPLIT) {
+#pragma unroll
+    for (int i = 0; i < RJ; ++i) {
+      const int sl = 64 * (w + NW * i) + lane, bl = sl >> lgNJ;
+      const int c = (sl & (a.NJ - 1)) ^ (bl & (a.NJ - 1));
+      pvo[i] = (uint32_t)(((b0 + bl) * G4 + 4 * (j0 + c)) * 4);
+    }
+    const int hC = a.NJ * E / 16, gC = 4 * a.NJ * E / 16, cC = a.NJ / 4;
+    const uint32_t smem_lds = (uint32_t)(uintptr_t)(lds_void_t*)smem;
+#pragma unroll
+    for (int i = 0; i < RY; ++i) {
+      const int q = tid + NTH * i, bl = q / hC, c = q - bl * hC;
+      const bool ok = q < NBv * hC;
+      yso[i] = ok ? smem_lds + (uint32_t)(hS - smem) + bl * hSr + 16 * c : smem_lds;
+      yvo[i] = ok ? (uint32_t)(((b0 + bl) * a.H + j0) * E + 16 * c) : 0x80000000u;
+    }
+#pragma unroll
+    for (int i = 0; i < RG; ++i) {
+      const int q = tid + NTH * i, bl = q / gC, c = q - bl * gC;
+      const bool ok = q < NBv * gC;
+      gso[i] = ok ? smem_lds + (uint32_t)(gS - smem) + bl * gSr + 16 * c : smem_lds;
+      gvo[i] = ok ? (uint32_t)(((b0 + bl) * G4 + 4 * j0) * E + 16 * c) : 0x80000000u;
+    }
+#pragma unroll
+    for (int i = 0; i < RC; ++i) {
+      const int q = tid + NTH * i, bl = q / cC, c = q - bl * cC;
+      const bool ok = q < NBv * cC;
+      cso[i] = ok ? smem_lds + (uint32_t)(cS - smem) + bl * cSr + 16 * c : smem_lds;
+      cvo[i] = ok ? (uint32_t)(((b0 + bl) * a.H + j0) * 4 + 16 * c) : 0x80000000u;
+    }
+  }
+  auto dma_p = [&](int tt) {
+    // P_tt of the group's rows and units into buffer tt & 1; rows past B are
+    // out of the buffer's range (zeros)
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.P + (int64_t)tt * (stepP / 4)), 0, (int)stepP, 0x00020000);
+    const uint32_t dst = pl_lds + (uint32_t)((tt & 1) * nbj * 16);
+#pragma unroll
+    for (int i = 0; i < RJ; ++i) {
+      const int j = w + NW * i;
+      if (64 * j < nbj && 64 * j + lane < nbj) lds_dma16_at<false>(r, dst + 64 * j * 16, pvo[i], 0u);
+    }
+  };
+  auto store_rec = [&](int tt) {
+    // the record of step tt from the staging area: every piece read, then
+    // every piece stored
+    const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((T*)a.y + tt * stepY), 0, (int)(stepY * E), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)((T*)a.Gs + tt * stepY * 4), 0, (int)(stepY * 4 * E), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.Cs + tt * stepY), 0, (int)(stepY * 4), 0x00020000);
+    typedef __attribute__((address_space(3))) const u32x4_t lds_u4;
+    u32x4_t vy[RY], vg[RG], vc[RC];
+#pragma unroll
+    for (int i = 0; i < RY; ++i) vy[i] = *(lds_u4*)(uintptr_t)yso[i];
+#pragma unroll
+    for (int i = 0; i < RG; ++i) vg[i] = *(lds_u4*)(uintptr_t)gso[i];
+#pragma unroll
+    for (int i = 0; i < RC; ++i) vc[i] = *(lds_u4*)(uintptr_t)cso[i];
+#pragma unroll
+    for (int i = 0; i < RY; ++i) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, vy[i]), ry, yvo[i], 0, 0);
+#pragma unroll
+    for (int i = 0; i < RG; ++i) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, vg[i]), rg, gvo[i], 0, 0);
+#pragma unroll
+    for (int i = 0; i < RC; ++i) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, vc[i]), rc, cvo[i], 0, 0);
+  };
+  if (SPLIT) {
+    dma_p(0);
+    wait_vmem();
+    __syncthreads();
+  } else if (owner) {
+    load_p(pf, 0);
+  }
 
   for (int t = 0; t < a.T; ++t) {
     stamp(a.stamps, a.T, t, 0);
@@ -194,7 +294,7 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
         const T v = a.h0 ? ((const T*)a.h0)[(int64_t)(b0 + bl) * a.H + k] : T(0);
         *(T*)(Hl + bl * strideH + k * E) = v;
       }
-      if (owner) load_p(pfn, 1);
+      if (!SPLIT && owner) load_p(pfn, 1);
       wait_vmem();
       __syncthreads();
     } else {
@@ -207,6 +307,7 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
           const char* src = (const char*)a.HD + slot0 + (uint32_t)(bl * rowB + (cc + lane) * 16);
           __builtin_amdgcn_global_load_lds((const void*)src, (void*)(Hl + bl * strideH + cc * 16), 16, 0, 16);
         }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       } else {
         for (int q0 = 0; q0 < nchunk; q0 += NTH * C) {
           u32x4_t v[C];
@@ -224,21 +325,24 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
           }
         }
       }
-      asm volatile("" ::: "memory");
-      if (owner) {
-        store_record(t - 1);
-        load_p(pfn, t + 1);
+      if constexpr (!SPLIT) {
+        asm volatile("" ::: "memory");
+        if (owner) {
+          store_record(t - 1);
+          load_p(pfn, t + 1);
+        }
+        asm volatile("" ::: "memory");
+        // register path: the ring's LDS writes are done once lgkmcnt is 0
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
       }
-      asm volatile("" ::: "memory");
-      // the ring reads of this wave are done once at most the deferred
-      // operations are outstanding; LDS writes (register path) once lgkmcnt
-      // is 0; the barrier then covers the other waves
-      if (C == 0 && owner) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDefer));
-      else if (C == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      else __builtin_amdgcn_s_waitcnt(kLgkm0);
+      // the barrier then covers the other waves
       __builtin_amdgcn_s_barrier();
     }
     stamp(a.stamps, a.T, t, 2);
+    if constexpr (SPLIT) {
+      if (t + 1 < a.T) dma_p(t + 1);
+      if (t > 0) store_rec(t - 1);
+    }
 
     // MFMA: part[mi][nt] = W_h[rows of M-tile mg*MW + mi, k part] .
     // h_{t-1}[tile nt]^T, with CH independent accumulator chains per tile
@@ -251,15 +355,39 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
       for (int nt = 0; nt < NBT; ++nt)
 #pragma unroll
         for (int ch = 0; ch < CH; ++ch) part[mi][nt][ch] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // The B fragments are read in chunks of CKF k-blocks into two register
+    // buffers, the next chunk's reads issued ahead of the current chunk's
+    // products (scheduling barriers keep the compiler from trading the reads
+    // in flight for registers and waiting on every read)
+    constexpr int CKF0 = 4 / NBT > 0 ? 4 / NBT : 1;
+    constexpr int CKF = NKBW < CKF0 ? NKBW : CKF0;
+    constexpr int NCF = NKBW / CKF;
+    static_assert(NKBW % CKF == 0, "chunks divide the k-blocks");
     const char* hb0 = Hl + fr * strideH + kb0 * 64 + fq * 16;
+    u32x4_t hbuf[2][CKF][NBT];
+    auto read_chunk = [&](int cf, int buf) {
 #pragma unroll
-    for (int i = 0; i < NKBW; ++i) {
+      for (int ii = 0; ii < CKF; ++ii)
 #pragma unroll
-      for (int nt = 0; nt < NBT; ++nt) {
-        const u32x4_t hb = *(const u32x4_t*)(hb0 + 16 * nt * strideH + i * 64);
+        for (int nt = 0; nt < NBT; ++nt)
+          hbuf[buf][ii][nt] = *(const u32x4_t*)(hb0 + 16 * nt * strideH + (cf * CKF + ii) * 64);
+    };
+    read_chunk(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int mi = 0; mi < MW; ++mi) part[mi][nt][i % CH] = Mfma<T>::mac(wreg[mi][i], hb, part[mi][nt][i % CH]);
+    for (int cf = 0; cf < NCF; ++cf) {
+      if (cf + 1 < NCF) read_chunk(cf + 1, (cf + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ii = 0; ii < CKF; ++ii) {
+        const int i = cf * CKF + ii;
+#pragma unroll
+        for (int nt = 0; nt < NBT; ++nt)
+#pragma unroll
+          for (int mi = 0; mi < MW; ++mi)
+            part[mi][nt][i % CH] = Mfma<T>::mac(wreg[mi][i], hbuf[cf & 1][ii][nt], part[mi][nt][i % CH]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int mi = 0; mi < MW; ++mi)
@@ -301,6 +429,12 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
         }
       }
     }
+    // without a k-part reduction no barrier separates the record's staging
+    // reads above from the staging writes below
+    if (SPLIT && KS == 1) {
+      __builtin_amdgcn_s_waitcnt(kLgkm0);
+      __builtin_amdgcn_s_barrier();
+    }
     stamp(a.stamps, a.T, t, 4);
     // elementwise: gates, cell, hidden; h_t is published (stores, their
     // completion, then the flag), the record is kept for the next step
@@ -310,7 +444,15 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
       for (int nt = 0; nt < NBT; ++nt) {
         const int b = b0 + 16 * nt + fr;
         const bool valid = u < a.H && 16 * nt + fr < NBv;
-        const f32x4_t z = mine[nt] + pf[nt];
+        f32x4_t pv;
+        if constexpr (SPLIT) {
+          const int bl = 16 * nt + fr, ul = u - j0;
+          pv = bl < a.NB ? *(const f32x4_t*)(Pl + (t & 1) * nbj * 16 + ((bl << lgNJ) + (ul ^ (bl & (a.NJ - 1)))) * 16)
+                         : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        } else {
+          pv = pf[nt];
+        }
+        const f32x4_t z = mine[nt] + pv;
         const float ig = sigmoidf(z[0]), fg = sigmoidf(z[1]), gg = tanh_f(z[2]), og = sigmoidf(z[3]);
         const float c = fg * cst[nt] + ig * gg;
         const float h = og * tanh_f(c);
@@ -325,7 +467,19 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
           gq[nt] = u32x4_t{(uint32_t)g64, (uint32_t)(g64 >> 32), 0u, 0u};
         }
         if (valid) store_elem<T>(dst + (int64_t)b * a.Hp + u, hq[nt], local);
-        pf[nt] = pfn[nt];
+        if constexpr (SPLIT) {
+          const int bl = 16 * nt + fr, ul = u - j0;
+          if (bl < a.NB) {
+            *(T*)(hS + bl * hSr + ul * E) = hq[nt];
+            if constexpr (E == 4)
+              *(u32x4_t*)(gS + bl * gSr + ul * 16) = gq[nt];
+            else
+              *(uint64_t*)(gS + bl * gSr + ul * 8) = (uint64_t)gq[nt][0] | ((uint64_t)gq[nt][1] << 32);
+            *(float*)(cS + bl * cSr + ul * 4) = c;
+          }
+        } else {
+          pf[nt] = pfn[nt];
+        }
       }
     }
     wait_vmem();
@@ -334,8 +488,12 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
     stamp(a.stamps, a.T, t, 5);
   }
   // the last step's record and the final states
-  if (owner) {
+  if (SPLIT) {
+    store_rec(a.T - 1);
+  } else if (owner) {
     store_record(a.T - 1);
+  }
+  if (owner) {
 #pragma unroll
     for (int nt = 0; nt < NBT; ++nt) {
       const int b = b0 + 16 * nt + fr;
@@ -378,7 +536,7 @@ static hipError_t fwd_dispatch_c(const Plan& p, FwdArgs& a, hipStream_t s) {
 // are bf16 only.
 template <typename T, int NBT>
 static hipError_t fwd_dispatch(const Plan& p, FwdArgs& a, hipStream_t s) {
-  const bool dma = (p.H * p.esize) % 1024 == 0;
+  const bool dma = p.fwd_dma != 0;
   if constexpr (sizeof(T) == 2)
     if (p.waves == 8) return dma ? fwd_dispatch_c<T, NBT, 0, 8>(p, a, s) : fwd_dispatch_c<T, NBT, 4, 8>(p, a, s);
   if (p.waves != kWaves) return hipErrorInvalidValue;
