@@ -71,6 +71,12 @@ ALL = dict(W=("u", 0.3), b=("u", 0.3), x=("n", 1.0), h0=("n", 0.5), c0=("n", 0.5
     ("bf16", 4, 19, 40, 72),
     ("bf16", 3, 5, 7, 33),      # odd hidden size
     ("bf16", 2, 33, 24, 130),
+    # rows of whole kilobytes (the forward's direct-to-LDS path, P and the
+    # record staged in LDS), with a last batch group that is not full
+    ("bf16", 3, 5, 24, 512),    # 4-row groups: P of a step is half a wave-load
+    ("f32", 3, 100, 16, 256),   # fp32 through the MFMA forward, 8-row groups
+    ("bf16", 2, 100, 64, 512),  # 8-row groups, 32 units, 8 waves
+    ("bf16", 3, 60, 32, 512),   # 8 batch groups (one per XCD)
 ])
 def test_ragged_shapes(lstm, dt, T, B, I, H):
     say(f"case: ragged {dt} T={T} B={B} I={I} H={H}")
