@@ -27,6 +27,7 @@ from layer_lstm_amd import synth  # noqa: E402
 
 METRIC = "LSTM fwd+bwd sequences/s and effective TFLOP/s (fraction of MFMA peak)"
 PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}  # MI355X dense matrix peaks
+VALU_TFLOPS = 157.3  # MI355X fp32 vector peak (256 CUs x 2.4 GHz)
 HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -35,14 +36,17 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_work(w, kind):
-    """Algorithmic work of one launch: (amount, unit, bound)."""
+def kernel_work(w, kind, plan=None):
+    """Algorithmic work of one launch: (amount, unit, bound).  A recurrence
+    whose product runs on the vector ALUs (plan from lstm_query_plan) is
+    bound by "alu" arithmetic, else by the matrix cores."""
     T, B, I, H = w.T, w.B, w.I, w.H
     TB = T * B
     if kind == "input_projection":
         return 2.0 * TB * 4 * H * I, "flop", "mfma"
     if kind in ("forward_recurrence", "backward_recurrence"):
-        return 2.0 * TB * 4 * H * H, "flop", "mfma"
+        key = "fwd_valu" if kind == "forward_recurrence" else "bwd_valu"
+        return 2.0 * TB * 4 * H * H, "flop", "alu" if plan and plan[key] else "mfma"
     if kind == "dW_product":
         return 2.0 * TB * 4 * H * (H + I), "flop", "mfma"
     if kind == "dx_product":
@@ -191,10 +195,11 @@ def main():
     dom = max(kinds, key=lambda k: kt[k][0])
     tot, n = kt[dom]
     avg_s = tot / n / 1e3
-    work, unit, bound = kernel_work(w, dom)
+    plan = lstm.query_plan(lstm.make_shape(w.T, w.B, w.I, w.H, code))
+    work, unit, bound = kernel_work(w, dom, plan)
     if unit == "flop":
         achieved = work / avg_s / 1e12
-        peak, runit = PEAK_TFLOPS[w.dtype], "TFLOP/s"
+        peak, runit = (VALU_TFLOPS if bound == "alu" else PEAK_TFLOPS[w.dtype]), "TFLOP/s"
     else:
         achieved = work / avg_s / 1e9
         peak, runit = HBM_GBS, "GB/s"
@@ -215,6 +220,7 @@ def main():
         "effective_tflops": round(eff_tflops, 3),
         "fraction_of_peak": round(eff_tflops / PEAK_TFLOPS[w.dtype], 5),
         "roofline": roofline,
+        "recurrence_plan": plan,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

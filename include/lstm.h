@@ -105,6 +105,28 @@ const char* lstm_status_string(int status);
  * *workspace_bytes, or an error code (workspace_bytes untouched). */
 int lstm_query(const lstm_shape* shape, size_t* workspace_bytes);
 
+/* How the persistent recurrences are laid out for `shape` on the current
+ * device, for measurement and reporting (the same choice lstm_fwd_train()
+ * and lstm_bwd() make).  Work-group (bg, jg) of the grid owns batch rows
+ * [bg*rows_per_group, +rows_per_group) and hidden units [jg*units_per_group,
+ * +units_per_group).  A *_valu field is 1 when that recurrence runs its
+ * product on the vector ALUs (fp32, 4-row groups) and 0 when it runs on the
+ * matrix cores.  Returns LSTM_OK and fills *info, or an error code of
+ * lstm_query() (info untouched). */
+typedef struct {
+  int32_t rows_per_group;  /* NB */
+  int32_t units_per_group; /* NJ */
+  int32_t groups;          /* batch groups (nBG) */
+  int32_t units_groups;    /* work-groups per batch group (nJG) */
+  int32_t grid;            /* work-groups of each recurrent launch */
+  int32_t waves;           /* waves per work-group */
+  int32_t xcd_local;       /* 1: every batch group runs on one XCD */
+  int32_t fwd_valu;
+  int32_t bwd_valu;
+  int32_t reserved[7];
+} lstm_plan_info;
+int lstm_query_plan(const lstm_shape* shape, lstm_plan_info* info);
+
 /* Forward pass for training ("前向传播公式").
  *   x [T,B,I], W [4H,H+I]: required (x may be NULL only if T*B*I == 0)
  *   b [4H], h0 [B,H], c0 [B,H]: optional, NULL = zero

@@ -270,6 +270,25 @@ int lstm_query(const lstm_shape* shape, size_t* workspace_bytes) {
   return LSTM_OK;
 }
 
+int lstm_query_plan(const lstm_shape* shape, lstm_plan_info* info) {
+  if (!shape || !info) return LSTM_ERR_NULL;
+  if (shape->reserved != 0) return LSTM_ERR_DTYPE;
+  Plan p;
+  const int rc = make_plan(shape->T, shape->B, shape->I, shape->H, shape->dtype, &p);
+  if (rc != LSTM_OK) return rc;
+  memset(info, 0, sizeof(*info));
+  info->rows_per_group = p.NB;
+  info->units_per_group = p.NJ;
+  info->groups = p.nBG;
+  info->units_groups = p.nJG;
+  info->grid = p.grid;
+  info->waves = p.waves;
+  info->xcd_local = p.xcd_local ? 1 : 0;
+  info->fwd_valu = fwd_vec_ok(p) ? 1 : 0;
+  info->bwd_valu = p.bwd_valu ? 1 : 0;
+  return LSTM_OK;
+}
+
 int lstm_fwd_train(const lstm_shape* shape, const void* x, const void* W, const void* b, const void* h0,
                    const void* c0, void* y, void* hT, void* cT, void* workspace, size_t workspace_bytes,
                    void* stream) {

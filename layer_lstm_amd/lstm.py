@@ -28,8 +28,8 @@ OK = 0
 STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_DIMS", -3: "ERR_DTYPE", -4: "ERR_ALIGN",
           -5: "ERR_WORKSPACE", -6: "ERR_UNSUPPORTED", -7: "ERR_COOP", -8: "ERR_LAUNCH",
           -9: "ERR_TIMEOUT", -10: "ERR_DEVICE"}
-EXPORTS = ("lstm_abi_version", "lstm_status_string", "lstm_query", "lstm_fwd_train", "lstm_bwd",
-           "lstm_check_workspace", "lstm_timing_enable", "lstm_timing_read", "lstm_stamps_set")
+EXPORTS = ("lstm_abi_version", "lstm_status_string", "lstm_query", "lstm_query_plan", "lstm_fwd_train",
+           "lstm_bwd", "lstm_check_workspace", "lstm_timing_enable", "lstm_timing_read", "lstm_stamps_set")
 STAMP_WGS, STAMP_POINTS = 8, 6
 KERNEL_KINDS = ("input_projection", "forward_recurrence", "backward_recurrence", "dW_product",
                 "dx_product", "unused", "state_copy")
@@ -40,12 +40,20 @@ class Shape(ctypes.Structure):
                 ("H", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
+class PlanInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("rows_per_group", "units_per_group", "groups", "units_groups",
+                                               "grid", "waves", "xcd_local", "fwd_valu", "bwd_valu")] + \
+               [("reserved", ctypes.c_int32 * 7)]
+
+
 _P = ctypes.c_void_p
 _lib.lstm_abi_version.restype = ctypes.c_int
 _lib.lstm_status_string.restype = ctypes.c_char_p
 _lib.lstm_status_string.argtypes = [ctypes.c_int]
 _lib.lstm_query.restype = ctypes.c_int
 _lib.lstm_query.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_size_t)]
+_lib.lstm_query_plan.restype = ctypes.c_int
+_lib.lstm_query_plan.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(PlanInfo)]
 _lib.lstm_fwd_train.restype = ctypes.c_int
 _lib.lstm_fwd_train.argtypes = [ctypes.POINTER(Shape)] + [_P] * 8 + [_P, ctypes.c_size_t, _P]
 _lib.lstm_bwd.restype = ctypes.c_int
@@ -93,6 +101,15 @@ def query(shape: Shape) -> int:
     if rc != OK:
         raise LstmError(rc, "lstm_query")
     return n.value
+
+
+def query_plan(shape: Shape) -> dict:
+    """Layout of the persistent recurrences for `shape` (lstm_query_plan)."""
+    info = PlanInfo()
+    rc = _lib.lstm_query_plan(ctypes.byref(shape), ctypes.byref(info))
+    if rc != OK:
+        raise LstmError(rc, "lstm_query_plan")
+    return {n: getattr(info, n) for n, _ in PlanInfo._fields_ if n != "reserved"}
 
 
 def _ptr(t):

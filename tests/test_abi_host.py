@@ -80,5 +80,11 @@ def test_query_rejects_bad_dtype_and_nulls(lstm):
     assert lstm.lib().lstm_query(None, ctypes.byref(n)) == -1
     s = lstm.make_shape(2, 2, 2, 2, 0)
     assert lstm.lib().lstm_query(ctypes.byref(s), None) == -1
+    info = lstm.PlanInfo()
+    assert lstm.lib().lstm_query_plan(None, ctypes.byref(info)) == -1
+    assert lstm.lib().lstm_query_plan(ctypes.byref(s), None) == -1
+    assert lstm.lib().lstm_query_plan(ctypes.byref(lstm.make_shape(2, 2, 2, 2, 7)), ctypes.byref(info)) == -3
+    assert lstm.lib().lstm_query_plan(ctypes.byref(lstm.make_shape(2, -1, 2, 2, 0)), ctypes.byref(info)) == -2
+    assert info.grid == 0  # untouched on error
     assert lstm.lib().lstm_fwd_train(None, *([None] * 9), 0, None) == -1
     assert lstm.lib().lstm_bwd(None, *([None] * 9), 0, *([None] * 6)) == -1

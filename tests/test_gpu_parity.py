@@ -40,12 +40,38 @@ def say(*a):
 
 
 def full_check(inp, lstm, tol=None):
+    code = lstm.F32 if inp["dtype"] == "f32" else lstm.BF16
+    say("plan:", lstm.query_plan(lstm.make_shape(inp["T"], inp["B"], inp["I"], inp["H"], code)))
     ref = oracle.fwd_bwd(inp)
     out, _, _ = run_gpu(inp, lstm, torch)
     errs, bad = compare(out, ref, inp["dtype"], tol=tol)
     say("rel-L2:", {k: f"{v:.2e}" for k, v in errs.items()})
     assert not bad, bad
     return errs
+
+
+# Layouts of the persistent recurrences on one MI355X (256 CUs in 8 XCDs):
+# (rows per group, units per group, waves, XCD-local, forward VALU, backward VALU)
+PLANS = {
+    "f32_T8_B4_I16_H32": (4, 8, 4, 0, 1, 1),
+    "f32_T64_B32_I256_H256": (4, 8, 4, 1, 1, 1),
+    "bf16_T128_B64_I512_H1024": (8, 32, 8, 1, 0, 0),
+    "bf16_T512_B16_I1024_H2048": (8, 16, 8, 0, 0, 0),
+    "bf16_T256_B256_I1024_H1024": (32, 32, 8, 1, 0, 0),
+}
+
+
+@pytest.mark.parametrize("name", list(PLANS))
+def test_workload_plans(lstm, name):
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("layouts are stated for 256 CUs")
+    w = synth.WORKLOADS[name]
+    code = lstm.F32 if w.dtype == "f32" else lstm.BF16
+    p = lstm.query_plan(lstm.make_shape(w.T, w.B, w.I, w.H, code))
+    say(name, p)
+    got = (p["rows_per_group"], p["units_per_group"], p["waves"], p["xcd_local"], p["fwd_valu"], p["bwd_valu"])
+    assert got == PLANS[name]
+    assert p["grid"] == p["groups"] * p["units_groups"] <= 256
 
 
 def test_small_workload(lstm):
