@@ -379,8 +379,9 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs<AOp, BOp, Epi> 
 // ---------------------------------------------------------------------------
 // Pipelined products (K a multiple of one stage): every operand is loaded
 // straight into LDS (global_load_lds_dwordx4, no register staging) through a
-// ring of kStages stages -- three stages of loads in flight while one is
-// multiplied -- in stages of 64 bytes of k per tile row:
+// ring of kStages stages -- four stages of loads in flight while one is
+// multiplied (the bf16 ring fills the 160 KB of LDS) -- in stages of 64
+// bytes of k per tile row:
 //   bf16: 256 x 256 tiles, 8 waves (2 x 4 of 128 x 64, two per SIMD), 32 k
 //         per stage; the large tile halves the bytes loaded per MFMA against
 //         128 x 128 tiles, which is what bounds those (the vector memory
@@ -402,8 +403,8 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs<AOp, BOp, Epi> 
 // Tile rows or columns past the operand are loaded from its last valid rows
 // (their outputs are never stored); an absent operand block (zero initial
 // state) is read through an empty buffer descriptor, which returns zeros.
-constexpr int kStages = 4;
-static_assert(kStages == 4, "the stage waits in gemm_lds_kernel assume a 4-stage ring");
+constexpr int kStages = 5;
+static_assert(kStages == 5, "the stage waits in gemm_lds_kernel assume a 5-stage ring");
 
 template <typename T> struct LdsCfg;
 template <> struct LdsCfg<bf16_t> {
@@ -436,8 +437,9 @@ __device__ __forceinline__ int mnrow_swz(int kr) { return ((kr & 3) | (((kr >> 3
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* p, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, char* lds, uint32_t vo, uint32_t so) {
-  lds_dma16<false>(r, lds, vo, so);
+// (lds: LDS byte address of the wave's kilobyte)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t lds, uint32_t vo, uint32_t so) {
+  lds_dma16_at<false>(r, lds, vo, so);
 }
 template <typename T, class Op, bool MN> struct Dma;
 template <typename T, class Op>
@@ -457,7 +459,7 @@ struct DmaKRows {  // k-contiguous rows: row(r) = base + (rowidx(r) * ld + col0)
       vo[j] = (uint32_t)((rowidx(gr) * ld + col0 + c * VEC) * (int64_t)sizeof(T));
     }
   }
-  __device__ __forceinline__ void issue(char* lds, int64_t k0, int w, int) const {
+  __device__ __forceinline__ void issue(uint32_t lds, int64_t k0, int w, int) const {
 #pragma unroll
     for (int j = 0; j < 2; ++j) dma16(r, lds + (32 * w + 16 * j) * 64, vo[j], (uint32_t)(k0 * (int64_t)sizeof(T)));
   }
@@ -498,7 +500,7 @@ struct Dma<T, MNRowsPlain<T>, true> {  // [K][ld]
       vo[j] = (uint32_t)(kr * ldb + mn_r<T>(r0, op.R, kr, lane) * (int64_t)sizeof(T));
     }
   }
-  __device__ __forceinline__ void issue(char* lds, int64_t k0, int w, int) const {
+  __device__ __forceinline__ void issue(uint32_t lds, int64_t k0, int w, int) const {
 #pragma unroll
     for (int j = 0; j < 2; ++j) dma16(r, lds + (4 * w + 2 * j) * 512, vo[j], (uint32_t)(k0 * ldb));
   }
@@ -517,7 +519,7 @@ struct Dma<T, MNRowsWx<T>, true> {  // k-row = interleaved gate row of W's input
       vo[j] = (uint32_t)(((kr & 3) * op.H + (kr >> 2)) * ldb + (op.H + mn_r<T>(r0, op.R, kr, lane)) * (int64_t)sizeof(T));
     }
   }
-  __device__ __forceinline__ void issue(char* lds, int64_t k0, int w, int) const {
+  __device__ __forceinline__ void issue(uint32_t lds, int64_t k0, int w, int) const {
 #pragma unroll
     for (int j = 0; j < 2; ++j) dma16(r, lds + (4 * w + 2 * j) * 512, vo[j], (uint32_t)((k0 >> 2) * ldb));
   }
@@ -551,10 +553,10 @@ struct Dma<T, MNRowsZ<T>, true> {  // Z[tb] = [h_{t-1}[b] | x[tb]]
   // The branches end in distinct empty asm statements: the compiler would
   // otherwise merge their loads into one with a per-lane descriptor, which
   // it can only issue in a loop over the lanes' values.
-  __device__ __forceinline__ void issue(char* lds, int64_t k0, int w, int lane) const {
+  __device__ __forceinline__ void issue(uint32_t lds, int64_t k0, int w, int lane) const {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      char* dst = lds + (4 * w + 2 * j) * 512;
+      const uint32_t dst = lds + (4 * w + 2 * j) * 512;
       if (!seg) {
         dma16(rx, dst, vx[j], (uint32_t)(k0 * ib));
         asm volatile("; z: x part" ::: "memory");
@@ -604,7 +606,7 @@ template <typename T, int AMN, int BMN, class AOp, class BOp, class Epi>
 __global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_kernel(GemmArgs<AOp, BOp, Epi> g) {
   constexpr int TILE = LdsCfg<T>::kTile, NT = LdsCfg<T>::kThreads, KST = LdsCfg<T>::kKStage;
   constexpr int STAGE = lds_stage_bytes<T>();
-  __shared__ __attribute__((aligned(16))) char ring0[STAGE], ring1[STAGE], ring2[STAGE], ring3[STAGE];
+  __shared__ __attribute__((aligned(16))) char ring0[STAGE], ring1[STAGE], ring2[STAGE], ring3[STAGE], ring4[STAGE];
   constexpr int WGN = LdsCfg<T>::kWaves / 2;  // waves along n (2 along m)
   constexpr int WM = TILE / 2 / 16, WN = TILE / WGN / 16;
   // the wave index is uniform: saying so keeps the direct-to-LDS addresses in
@@ -635,7 +637,11 @@ __global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_kernel(GemmAr
 
   const Dma<T, AOp, (bool)AMN> da(g.a, m0, w, lane);
   const Dma<T, BOp, (bool)BMN> db(g.b, n0, w, lane);
-  auto issue = [&](int64_t kt, char* st) {
+  // LDS byte addresses of the ring slots (taken from the arrays themselves)
+  const uint32_t rl[kStages] = {(uint32_t)(uintptr_t)(lds_void_t*)ring0, (uint32_t)(uintptr_t)(lds_void_t*)ring1,
+                                (uint32_t)(uintptr_t)(lds_void_t*)ring2, (uint32_t)(uintptr_t)(lds_void_t*)ring3,
+                                (uint32_t)(uintptr_t)(lds_void_t*)ring4};
+  auto issue = [&](int64_t kt, uint32_t st) {
     da.issue(st, kt * KST, w, lane);
     db.issue(st + STAGE / 2, kt * KST, w, lane);
   };
@@ -658,13 +664,14 @@ __global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_kernel(GemmAr
   // vmcnt bits [3:0] and [15:14], expcnt and lgkmcnt at their no-wait
   // maxima); the barrier then covers the other waves -- a bare barrier,
   // since __syncthreads() would also wait for every load in flight -- and
-  // also tells that every wave is done with `nxt`, refilled with stage kt+3.
-  auto stage = [&](int64_t kt, const char* cur, char* nxt) {
+  // also tells that every wave is done with `nxt`, refilled with stage kt+4.
+  auto stage = [&](int64_t kt, const char* cur, uint32_t nxt) {
     const int ln = lane, lfr = fr, lfq = fq;
     const int64_t after = kt_end - 1 - kt;
-    if (after >= kStages - 2) __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8)
-    else if (after == 1) __builtin_amdgcn_s_waitcnt(0x0F74);       // vmcnt(4)
-    else __builtin_amdgcn_s_waitcnt(0x0F70);                       // vmcnt(0)
+    if (after >= kStages - 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(12));
+    else if (after == 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+    else if (after == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __builtin_amdgcn_s_barrier();
     if (kt + kStages - 1 < kt_end) issue(kt + kStages - 1, nxt);
     const char* sa = cur;
@@ -688,19 +695,22 @@ __global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_kernel(GemmAr
     }
   };
 
-  if (kt_begin + 0 < kt_end) issue(kt_begin + 0, ring0);
-  if (kt_begin + 1 < kt_end) issue(kt_begin + 1, ring1);
-  if (kt_begin + 2 < kt_end) issue(kt_begin + 2, ring2);
+  if (kt_begin + 0 < kt_end) issue(kt_begin + 0, rl[0]);
+  if (kt_begin + 1 < kt_end) issue(kt_begin + 1, rl[1]);
+  if (kt_begin + 2 < kt_end) issue(kt_begin + 2, rl[2]);
+  if (kt_begin + 3 < kt_end) issue(kt_begin + 3, rl[3]);
   int64_t kt = kt_begin;
   for (; kt + kStages - 1 < kt_end; kt += kStages) {
-    stage(kt, ring0, ring3);
-    stage(kt + 1, ring1, ring0);
-    stage(kt + 2, ring2, ring1);
-    stage(kt + 3, ring3, ring2);
+    stage(kt, ring0, rl[4]);
+    stage(kt + 1, ring1, rl[0]);
+    stage(kt + 2, ring2, rl[1]);
+    stage(kt + 3, ring3, rl[2]);
+    stage(kt + 4, ring4, rl[3]);
   }
-  if (kt < kt_end) stage(kt, ring0, ring3);
-  if (kt + 1 < kt_end) stage(kt + 1, ring1, ring0);
-  if (kt + 2 < kt_end) stage(kt + 2, ring2, ring1);
+  if (kt < kt_end) stage(kt, ring0, rl[4]);
+  if (kt + 1 < kt_end) stage(kt + 1, ring1, rl[0]);
+  if (kt + 2 < kt_end) stage(kt + 2, ring2, rl[1]);
+  if (kt + 3 < kt_end) stage(kt + 3, ring3, rl[2]);
 
   const bool vec_n = (g.N & 3) == 0;
 #pragma unroll
