@@ -676,7 +676,11 @@ __global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_kernel(GemmAr
     if (kt + kStages - 1 < kt_end) issue(kt + kStages - 1, nxt);
     const char* sa = cur;
     const char* sb = cur + STAGE / 2;
-    u32x4_t bfv[WN];
+    // every fragment of the stage is read before the first product (a
+    // scheduling barrier keeps the compiler from interleaving the reads with
+    // the products and waiting on each pair), so one LDS latency per stage
+    // is exposed instead of one per pair of A fragments
+    u32x4_t bfv[WN], afv[WM];
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
       if constexpr (BMN) bfv[j] = frag_mnrows<T>(sb, wn * 16 * WN + 16 * j, ln);
@@ -684,15 +688,18 @@ __global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_kernel(GemmAr
     }
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
-      u32x4_t af;
-      if constexpr (AMN) af = frag_mnrows<T>(sa, wm * 16 * WM + 16 * i, ln);
-      else af = frag_krows(sa, wm * 16 * WM + 16 * i + lfr, lfq);
-      // B as the MFMA's first operand: the tile comes out transposed, lane
-      // (fr, fq) holding C[m = .. + fr][n = .. + 4 fq + e], four
-      // consecutive columns for one row -- one 16-byte store per tile
-#pragma unroll
-      for (int j = 0; j < WN; ++j) acc[i][j] = Mfma<T>::mac(bfv[j], af, acc[i][j]);
+      if constexpr (AMN) afv[i] = frag_mnrows<T>(sa, wm * 16 * WM + 16 * i, ln);
+      else afv[i] = frag_krows(sa, wm * 16 * WM + 16 * i + lfr, lfq);
     }
+    __builtin_amdgcn_sched_barrier(0);
+    // B as the MFMA's first operand: the tile comes out transposed, lane
+    // (fr, fq) holding C[m = .. + fr][n = .. + 4 fq + e], four consecutive
+    // columns for one row -- one 16-byte store per tile
+#pragma unroll
+    for (int i = 0; i < WM; ++i)
+#pragma unroll
+      for (int j = 0; j < WN; ++j) acc[i][j] = Mfma<T>::mac(bfv[j], afv[i], acc[i][j]);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   if (kt_begin + 0 < kt_end) issue(kt_begin + 0, rl[0]);
