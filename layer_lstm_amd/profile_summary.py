@@ -5,7 +5,7 @@ profiles/ and the per-kernel HBM traffic record that bench.py reports.
     python -m layer_lstm_amd.profile_summary traffic --workload NAME \
         --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR \
         --copy-bytes N --out-json profiles/traffic.json --out-txt OUT.txt \
-        --command "..." [--command "..."]
+        [--stats DIR] --command "..." [--command "..."]
     python -m layer_lstm_amd.profile_summary mfma DIR OUT.txt --workload NAME \
         --command "..."
 
@@ -16,7 +16,10 @@ rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, each for the LSTM step and
 for a plain copy of --copy-bytes bytes), scales each counter by what it reads
 for the copy (known bytes / counted bytes), and records HBM bytes per
 launch for each kernel kind of the path, with the hash of the kernel's
-source so that a record goes stale when the kernel changes.  `mfma` reads
+source so that a record goes stale when the kernel changes; with --stats
+(a rocprofv3 --kernel-trace --stats run of the same workload) it also
+reports the achieved HBM GB/s of each kind (bytes per launch / average
+launch duration).  `mfma` reads
 one --pmc run of SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE and reports
 the MFMA utilisation of each kernel kind.
 """
@@ -102,6 +105,18 @@ def copy_factor(d: str, counter: str, nbytes: int):
     return nbytes / (kib * 1024.0), name, kib
 
 
+def kind_durations(d: str):
+    """Average launch duration (ns) of each kernel kind from a kernel_stats.csv."""
+    tot = {}
+    for r in csv.DictReader(open(find_csv(d, "kernel_stats.csv"))):
+        k = kind_of(r["Name"])
+        if k is None:
+            continue
+        ns, n = tot.get(k, (0.0, 0))
+        tot[k] = (ns + float(r["TotalDurationNs"]), n + int(r["Calls"]))
+    return {k: ns / n for k, (ns, n) in tot.items() if n}
+
+
 def cmd_traffic(a):
     ff, fname, fkib = copy_factor(a.copy_fetch, "FETCH_SIZE", a.copy_bytes)
     wf, wname, wkib = copy_factor(a.copy_write, "WRITE_SIZE", a.copy_bytes)
@@ -122,7 +137,9 @@ def cmd_traffic(a):
     lines.append(f"copy calibration: {a.copy_bytes} bytes copied; FETCH_SIZE read {fkib:.0f} KiB "
                  f"(factor {ff:.4f}), WRITE_SIZE read {wkib:.0f} KiB (factor {wf:.4f})")
     lines.append(f"workload {a.workload}")
-    lines.append(f"{'kernel kind':22s} {'launches':>8s} {'fetch MB':>10s} {'write MB':>10s} {'total MB':>10s}")
+    dur = kind_durations(a.stats) if a.stats else {}
+    lines.append(f"{'kernel kind':22s} {'launches':>8s} {'fetch MB':>10s} {'write MB':>10s} {'total MB':>10s}"
+                 + (f" {'avg us':>9s} {'GB/s':>8s}" if dur else ""))
     for k, v in per.items():
         fetch = statistics.median(v.get("FETCH_SIZE", [0.0]))
         write = statistics.median(v.get("WRITE_SIZE", [0.0]))
@@ -130,7 +147,10 @@ def cmd_traffic(a):
         wrec[k] = {"bytes_per_launch": round(fetch + write), "fetch_bytes": round(fetch), "write_bytes": round(write),
                    "source_sha": source_sha(KINDS[k][0]), "copy_factor_fetch": round(ff, 5),
                    "copy_factor_write": round(wf, 5)}
-        lines.append(f"{k:22s} {n:8d} {fetch / 1e6:10.3f} {write / 1e6:10.3f} {(fetch + write) / 1e6:10.3f}")
+        row = f"{k:22s} {n:8d} {fetch / 1e6:10.3f} {write / 1e6:10.3f} {(fetch + write) / 1e6:10.3f}"
+        if k in dur:
+            row += f" {dur[k] / 1e3:9.1f} {(fetch + write) / dur[k]:8.0f}"
+        lines.append(row)
     json.dump(rec, open(a.out_json, "w"), indent=1, sort_keys=True)
     open(a.out_txt, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -186,6 +206,7 @@ def main():
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--out-json", required=True)
     t.add_argument("--out-txt", required=True)
+    t.add_argument("--stats", default=None)
     t.add_argument("--command", action="append", default=[])
     a = ap.parse_args()
     {"stats": cmd_stats, "traffic": cmd_traffic, "mfma": cmd_mfma}[a.cmd](a)
