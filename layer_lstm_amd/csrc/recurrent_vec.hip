@@ -14,7 +14,7 @@
 //   fp32 FMAs -- per FMA one LDS value feeds four gates, which keeps the
 //   LDS reads (not the FMAs) from bounding the step;
 //   the 32 chunks are summed by a reduce-scatter across the half-wave (xor
-//   16 by ds_swizzle; xor 8, 4, 2, 1 by DPP), after which lane c holds the
+//   16 by v_permlane16_swap; xor 8, 4, 2, 1 by DPP), after which lane c holds the
 //   full sum of gate 2*c[2] + c[1] for batch row 2*c[4] + c[3];
 //   lane c = 8b (b < 4) gathers the four gates of batch row b by DPP and
 //   does the cell update of that (unit, row) element.
@@ -30,7 +30,7 @@ namespace lstm {
 constexpr int kQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
 constexpr int kQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
 constexpr int kQuadBcast2 = 0xAA;  // quad_perm [2,2,2,2]
-constexpr int kRowShl4 = 0x104, kRowShl8 = 0x108, kRowShr4 = 0x114, kRowShr8 = 0x118;
+constexpr int kRowShl4 = 0x104, kRowShr4 = 0x114, kRowRor8 = 0x128;
 
 // v from another lane by a DPP move; lanes outside bank_mask keep `old`.
 template <int CTRL, int BANKS = 0xf>
@@ -38,14 +38,19 @@ __device__ __forceinline__ float dpp_f32(float old, float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, v),
                                                                CTRL, 0xf, BANKS, false));
 }
-// v of lane l ^ 8 (inside a 16-lane row): lanes 8..15 take from l - 8,
-// lanes 0..7 from l + 8.
-__device__ __forceinline__ float xor8_f32(float v) { return dpp_f32<kRowShl8, 0x3>(dpp_f32<kRowShr8, 0xC>(0.f, v), v); }
+// v of lane l ^ 8 (inside a 16-lane row): a rotation of the row by 8.
+__device__ __forceinline__ float xor8_f32(float v) { return dpp_f32<kRowRor8>(0.f, v); }
 // v of lane l ^ 4: banks 1, 3 (lane bit 2 set) take from l - 4, banks 0, 2 from l + 4.
 __device__ __forceinline__ float xor4_f32(float v) { return dpp_f32<kRowShl4, 0x5>(dpp_f32<kRowShr4, 0xA>(0.f, v), v); }
-// v of lane l ^ 16 (within each 32-lane half), ds_swizzle bit mode.
-__device__ __forceinline__ float xor16_f32(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
+// One reduce-scatter level over lane bit 4 (within each 32-lane half):
+// lanes with bit 4 clear get lo(l) + lo(l ^ 16), the others hi(l ^ 16) +
+// hi(l).  v_permlane16_swap exchanges the odd 16-lane rows of its first
+// operand with the even rows of its second: (lo, hi) becomes (lo.r0, hi.r0,
+// lo.r2, hi.r2) and (lo.r1, hi.r1, lo.r3, hi.r3), whose sum is the level.
+__device__ __forceinline__ float rs16_f32(float lo, float hi) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi),
+                                                  false, false);
+  return __builtin_bit_cast(float, (unsigned)r[0]) + __builtin_bit_cast(float, (unsigned)r[1]);
 }
 
 template <int L, int U2, int C>
@@ -63,7 +68,7 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_vec_kernel(FwdArgs a) {
   const bool local = a.local != 0;
   const int b0 = bg * a.NB, j0 = jg * a.NJ;  // NB == 4
   const int c = lane & 31, ulb = 2 * w + (lane >> 5);
-  const int bit4 = (c >> 4) & 1, bit3 = (c >> 3) & 1, bit2 = (c >> 2) & 1, bit1 = (c >> 1) & 1;
+  const int bit3 = (c >> 3) & 1, bit2 = (c >> 2) & 1, bit1 = (c >> 1) & 1;  // lane bits of the reduce-scatter
   const int64_t G4 = 4 * (int64_t)a.H;
   bool dead = false;
 
@@ -183,11 +188,7 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_vec_kernel(FwdArgs a) {
 #pragma unroll
       for (int g = 0; g < 4; ++g)
 #pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-          const float keep = bit4 ? acc[q][g][2 + bb] : acc[q][g][bb];
-          const float send = bit4 ? acc[q][g][bb] : acc[q][g][2 + bb];
-          k8[g][bb] = keep + xor16_f32(send);
-        }
+        for (int bb = 0; bb < 2; ++bb) k8[g][bb] = rs16_f32(acc[q][g][bb], acc[q][g][2 + bb]);
       // bit 3: keep row 2*bit4 + bit3
       float k4[4];
 #pragma unroll
