@@ -188,6 +188,7 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
   // publish, which waits for every operation of every wave.  The owners read
   // P_t from LDS and stage the step's record there.
   constexpr bool SPLIT = C == 0;
+  const uint32_t hl_lds = (uint32_t)(uintptr_t)(lds_void_t*)smem;  // LDS address of Hl
   const int lgNJ = 31 - __builtin_clz(a.NJ);
   const int nbj = a.NB * a.NJ;                            // 16-byte P chunks (4 gates) per step
   char* Pl = (char*)(red + MT * (KS - 1) * NBT * 256);    // [2][NB][NJ] chunks, chunk c of row bl at c ^ (bl % NJ)
@@ -301,11 +302,14 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
       const uint32_t slot0 = (uint32_t)(((t - 1) & 1) * a.Bp + b0) * (uint32_t)rowB;
       if constexpr (C == 0) {
         // direct-to-LDS: wave-load j moves chunks [64j, 64j + 64) -- 1 KB of
-        // one row, as every row holds a multiple of 64 chunks here
+        // one row, as every row holds a multiple of 64 chunks here (device-
+        // coherent loads, issued as inline asm and waited for explicitly:
+        // the compiler's own waits for the builtin form measured slower
+        // where the ring is read across XCDs)
         for (int j = w; j * 64 < nchunk; j += NW) {
           const int bl = (64 * j) / cpr, cc = 64 * j - bl * cpr;
-          const char* src = (const char*)a.HD + slot0 + (uint32_t)(bl * rowB + (cc + lane) * 16);
-          __builtin_amdgcn_global_load_lds((const void*)src, (void*)(Hl + bl * strideH + cc * 16), 16, 0, 16);
+          lds_dma16_at<true>(hd_rsrc, hl_lds + (uint32_t)(bl * strideH + cc * 16),
+                             slot0 + (uint32_t)(bl * rowB + lane * 16), (uint32_t)(cc * 16));
         }
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       } else {
@@ -358,37 +362,42 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
     // The B fragments are read in chunks of CKF k-blocks into two register
     // buffers, the next chunk's reads issued ahead of the current chunk's
     // products (scheduling barriers keep the compiler from trading the reads
-    // in flight for registers and waiting on every read)
-    constexpr int CKF0 = 4 / NBT > 0 ? 4 / NBT : 1;
-    constexpr int CKF = NKBW < CKF0 ? NKBW : CKF0;
-    constexpr int NCF = NKBW / CKF;
-    static_assert(NKBW % CKF == 0, "chunks divide the k-blocks");
+    // in flight for registers and waiting on every read).  A pass covers
+    // batch tiles [NT0, NT0 + NTN); one pass covers them all.
     const char* hb0 = Hl + fr * strideH + kb0 * 64 + fq * 16;
-    u32x4_t hbuf[2][CKF][NBT];
-    auto read_chunk = [&](int cf, int buf) {
+    auto product = [&](auto nt0c, auto ntnc) {
+      constexpr int NT0 = decltype(nt0c)::value, NTN = decltype(ntnc)::value;
+      constexpr int CKF0 = 4 / NTN > 0 ? 4 / NTN : 1;
+      constexpr int CKF = NKBW < CKF0 ? NKBW : CKF0;
+      constexpr int NCF = NKBW / CKF;
+      static_assert(NKBW % CKF == 0, "chunks divide the k-blocks");
+      u32x4_t hbuf[2][CKF][NTN];
+      auto read_chunk = [&](int cf, int buf) {
 #pragma unroll
-      for (int ii = 0; ii < CKF; ++ii)
+        for (int ii = 0; ii < CKF; ++ii)
 #pragma unroll
-        for (int nt = 0; nt < NBT; ++nt)
-          hbuf[buf][ii][nt] = *(const u32x4_t*)(hb0 + 16 * nt * strideH + (cf * CKF + ii) * 64);
-    };
-    read_chunk(0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int cf = 0; cf < NCF; ++cf) {
-      if (cf + 1 < NCF) read_chunk(cf + 1, (cf + 1) & 1);
+          for (int n = 0; n < NTN; ++n)
+            hbuf[buf][ii][n] = *(const u32x4_t*)(hb0 + 16 * (NT0 + n) * strideH + (cf * CKF + ii) * 64);
+      };
+      read_chunk(0, 0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int ii = 0; ii < CKF; ++ii) {
-        const int i = cf * CKF + ii;
+      for (int cf = 0; cf < NCF; ++cf) {
+        if (cf + 1 < NCF) read_chunk(cf + 1, (cf + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int nt = 0; nt < NBT; ++nt)
+        for (int ii = 0; ii < CKF; ++ii) {
+          const int i = cf * CKF + ii;
 #pragma unroll
-          for (int mi = 0; mi < MW; ++mi)
-            part[mi][nt][i % CH] = Mfma<T>::mac(wreg[mi][i], hbuf[cf & 1][ii][nt], part[mi][nt][i % CH]);
+          for (int n = 0; n < NTN; ++n)
+#pragma unroll
+            for (int mi = 0; mi < MW; ++mi)
+              part[mi][NT0 + n][i % CH] = Mfma<T>::mac(wreg[mi][i], hbuf[cf & 1][ii][n], part[mi][NT0 + n][i % CH]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    product(std::integral_constant<int, 0>{}, std::integral_constant<int, NBT>{});
 #pragma unroll
     for (int mi = 0; mi < MW; ++mi)
 #pragma unroll
