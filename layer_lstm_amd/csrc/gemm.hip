@@ -378,7 +378,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs<AOp, BOp, Epi> 
 
 // ---------------------------------------------------------------------------
 // Pipelined products (K a multiple of one stage): every operand is loaded
-// straight into LDS (global_load_lds_dwordx4, no register staging) through a
+// straight into LDS (buffer_load_dwordx4 ... lds, no register staging) through a
 // ring of kStages stages -- four stages of loads in flight while one is
 // multiplied (the bf16 ring fills the 160 KB of LDS) -- in stages of 64
 // bytes of k per tile row:
