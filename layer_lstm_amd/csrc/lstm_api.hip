@@ -105,8 +105,8 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
             lds_b = (size_t)NBr * (4 * NJ * e + 16) + 4096 + (size_t)NB * NJ * 16;
           } else {
             if (nkb < 1 || MTb * nkb > 32 || NB * NJ > 1024) continue;
-            // wave partials, db sums (1024 elements at most), two operand slots
-            lds_b = (size_t)NW * NBr * (16 * MTb + 4) * 4 + 16384 + 2 * 1024 * (size_t)(4 * e + 8);
+            // wave partials, db sums (1024 elements at most)
+            lds_b = (size_t)NW * NBr * (16 * MTb + 4) * 4 + 16384;
             if (lds_b < kColStageLds) lds_b = kColStageLds;
           }
           p->NB = NB; p->NJ = NJ; p->nBG = (int)nBG; p->nJG = (int)nJG; p->grid = (int)(nBG * nJG);

@@ -151,26 +151,26 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
   // so this traffic delays whichever wait on the exchange comes next after
   // it is issued; where it goes depends on the exchange:
   //   DEF (XCD-local groups: the ring sits in L2 and the flag wait is short):
-  //     issued as soon as the product's ring reads are consumed (gates and
-  //     cells direct-to-LDS into one of two slots, dy into registers, the
-  //     record one step late), it drains during the reduction and the gate
-  //     deltas;
+  //     issued as soon as the product's ring reads are consumed (into a
+  //     second set of registers, the record one step late), it drains
+  //     during the reduction and the gate deltas.  (Direct-to-LDS loads of
+  //     the same operands held the waves up at the reduction's barrier,
+  //     about a fifth of the step at 32-row groups.);
   //   !DEF (groups across XCDs: every flag and ring read goes through memory
   //     and the flag wait is long): the record is written with the ring and
   //     the operands are loaded into registers right after the flag, while
   //     the other work-groups' flags are on their way.
   constexpr int GSB = 4 * E;                                 // bytes of one element's gates
-  constexpr int SLOT = EPTM * NTH * (GSB + 8);               // bytes of one operand slot
-  char* opl = (char*)(dba + 4 * 1024);                       // [2][SLOT]: per s: gates, c_t, c_{t-1}
   const int64_t stepC = (int64_t)a.B * a.H;                  // elements of one step in [B][H]
   T pdy[EPTM], pdyn[EPTM];  // dy_t (in use), dy of the next step: raw, converted at use (a conversion at
                             // load time would make the load's issue wait for its data)
   uint32_t dqw[EPTM][GSB / 4];                               // this step's gate deltas, packed
-  uint32_t rgw[EPTM][GSB / 4];                               // !DEF: gates of the next step, raw
-  float rc[EPTM], rcp[EPTM];                                 // !DEF: c_t, c_{t-1} of the next step
-  auto load_regs = [&](int tt) {
-    // !DEF: operands of step tt >= 0 into registers (raw: no conversion at
-    // load time, which would make the issue wait for the data)
+  uint32_t rgw[EPTM][GSB / 4], ngw[EPTM][GSB / 4];           // gates of this step and of the next, raw
+  float rc[EPTM], rcp[EPTM], nc[EPTM], ncp[EPTM];            // c_t, c_{t-1} of this step and of the next
+  // operands of step tt >= 0 into registers (raw: no conversion at load
+  // time, which would make the issue wait for the data): !DEF into the set
+  // of this step, DEF into the set of the next
+  auto load_ops = [&](int tt, uint32_t (&gw)[EPTM][GSB / 4], float (&cc)[EPTM], float (&cp)[EPTM], T (&dyv)[EPTM]) {
     if (tt < 0) return;
 #pragma unroll
     for (int s = 0; s < EPTM; ++s) {
@@ -178,37 +178,26 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
       const int64_t o = tt * stepC + c_off(s);
       if constexpr (E == 4) {
         const u32x4_t g = *(const u32x4_t*)((const T*)a.Gs + 4 * o);
-        rgw[s][0] = g[0]; rgw[s][1] = g[1]; rgw[s][2] = g[2]; rgw[s][3] = g[3];
+        gw[s][0] = g[0]; gw[s][1] = g[1]; gw[s][2] = g[2]; gw[s][3] = g[3];
       } else {
         const uint64_t g = *(const uint64_t*)((const T*)a.Gs + 4 * o);
-        rgw[s][0] = (uint32_t)g; rgw[s][1] = (uint32_t)(g >> 32);
+        gw[s][0] = (uint32_t)g; gw[s][1] = (uint32_t)(g >> 32);
       }
-      rc[s] = a.Cs[o];
-      rcp[s] = tt > 0 ? a.Cs[o - stepC] : 0.f;
-      pdy[s] = ((const T*)a.dy)[o];
+      cc[s] = a.Cs[o];
+      cp[s] = tt > 0 ? a.Cs[o - stepC] : 0.f;
+      dyv[s] = ((const T*)a.dy)[o];
     }
   };
-  auto issue_ops = [&](int tt) {
-    // DEF: operands of step tt >= 0 of this thread's elements
-    if (tt < 0) return;
-    char* slot = opl + (tt & 1) * SLOT;
+  auto load_regs = [&](int tt) { load_ops(tt, rgw, rc, rcp, pdy); };
+  auto issue_ops = [&](int tt) { load_ops(tt, ngw, nc, ncp, pdyn); };
+  auto take_next = [&]() {
 #pragma unroll
     for (int s = 0; s < EPTM; ++s) {
-      if (!own[s]) continue;
-      char* ss = slot + s * NTH * (GSB + 8);
-      const int64_t o = tt * stepC + c_off(s);                  // element of step tt
-      const char* gsrc = (const char*)a.Gs + 4 * o * E;
-      if constexpr (E == 4) {
-        __builtin_amdgcn_global_load_lds((const void*)gsrc, (void*)(ss + w * 64 * 16), 16, 0, 0);
-      } else {
-        __builtin_amdgcn_global_load_lds((const void*)gsrc, (void*)(ss + w * 64 * 4), 4, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(gsrc + 4), (void*)(ss + NTH * 4 + w * 64 * 4), 4, 0, 0);
-      }
-      __builtin_amdgcn_global_load_lds((const void*)(a.Cs + o), (void*)(ss + NTH * GSB + w * 64 * 4), 4, 0, 0);
-      if (tt > 0)
-        __builtin_amdgcn_global_load_lds((const void*)(a.Cs + o - stepC), (void*)(ss + NTH * (GSB + 4) + w * 64 * 4),
-                                         4, 0, 0);
-      pdyn[s] = ((const T*)a.dy)[o];
+#pragma unroll
+      for (int k = 0; k < GSB / 4; ++k) rgw[s][k] = ngw[s][k];
+      rc[s] = nc[s];
+      rcp[s] = ncp[s];
+      pdy[s] = pdyn[s];
     }
   };
   auto store_record = [&](int tt) {
@@ -223,14 +212,7 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
         *(uint64_t*)dst = (uint64_t)dqw[s][0] | ((uint64_t)dqw[s][1] << 32);
     }
   };
-  if constexpr (DEF) {
-    issue_ops(a.T - 1);
-    wait_vmem();
-#pragma unroll
-    for (int s = 0; s < EPTM; ++s) pdy[s] = pdyn[s];
-  } else {
-    load_regs(a.T - 1);
-  }
+  load_regs(a.T - 1);
 
   for (int t = a.T - 1; t >= -1; --t) {
     const int step = a.T - 1 - (t < 0 ? 0 : t);
@@ -311,23 +293,12 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
     // 2. gate deltas of this step; dG_t to the ring (the record follows next
     //    step)
     char* ring = (char*)a.GD + (t & 1) * slotB;
-    const char* slot = opl + (t & 1) * SLOT;
 #pragma unroll
     for (int s = 0; s < EPTM; ++s) {
-      const char* ss = slot + s * NTH * (GSB + 8);
       uint32_t gw[GSB / 4];
-      float c, cprev;
-      if constexpr (DEF) {
 #pragma unroll
-        for (int k = 0; k < GSB / 4; ++k) gw[k] = *(const uint32_t*)(ss + (GSB == 16 ? tid * 16 + 4 * k : k * NTH * 4 + tid * 4));
-        c = *(const float*)(ss + NTH * GSB + tid * 4);
-        cprev = *(const float*)(ss + NTH * (GSB + 4) + tid * 4);
-      } else {
-#pragma unroll
-        for (int k = 0; k < GSB / 4; ++k) gw[k] = rgw[s][k];
-        c = rc[s];
-        cprev = rcp[s];
-      }
+      for (int k = 0; k < GSB / 4; ++k) gw[k] = rgw[s][k];
+      float c = rc[s], cprev = rcp[s];
       float gi, gf, gg, go;
       if constexpr (E == 4) {
         gi = __uint_as_float(gw[0]); gf = __uint_as_float(gw[1]); gg = __uint_as_float(gw[2]); go = __uint_as_float(gw[3]);
@@ -388,8 +359,7 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
     __syncthreads();
     if (tid == 0) store_flag(a.GF + bg * a.nJG + jg, (uint32_t)(a.T - t), local);
     if constexpr (DEF) {
-#pragma unroll
-      for (int s = 0; s < EPTM; ++s) pdy[s] = pdyn[s];
+      take_next();
     } else {
       // loaded to completion here, while the flags of this step travel: in
       // flight, the loads would hold up the next step's flag polls and ring
