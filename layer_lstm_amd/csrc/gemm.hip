@@ -250,6 +250,9 @@ struct GemmArgs {
   int dsum_bf16;
   int64_t dsum_cols, dsum_H;
   int nxcd;           // XCDs of the device (1: no XCD-aware tile order)
+  // persistent input projection (gemm_lds_multi_kernel) only:
+  int tiles_x, tiles_y;  // output tiles along n and m
+  int per_wg;            // output tiles per work-group
 };
 
 // Output tile (n tile, m tile, split) of this work-group.  The device deals
@@ -741,6 +744,140 @@ __global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_kernel(GemmAr
     }
 }
 
+// Persistent form for products whose operands are both k-contiguous rows
+// (the input projection): one work-group per CU walks per_wg output tiles,
+// and its loads form one stream over them, so the first stages of a tile
+// are in flight while the previous tile ends and writes its outputs.  Four
+// ring slots, the stages per tile a multiple of four: every tile starts in
+// slot 0 and its loop is unrolled over the ring.  splits == 1; a second
+// slab of work-groups (blockIdx.z == 1) only clears `zero`.  The tiles of an XCD (work-groups i mod nxcd) are one contiguous
+// range of the row-major tile order, walked together, each work-group taking
+// every (work-groups per XCD)-th.
+template <typename T, class AOp, class BOp, class Epi>
+__global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_multi_kernel(GemmArgs<AOp, BOp, Epi> g) {
+  constexpr int TILE = LdsCfg<T>::kTile, KST = LdsCfg<T>::kKStage;
+  constexpr int STAGE = lds_stage_bytes<T>();
+  constexpr int NS = 4;
+  __shared__ __attribute__((aligned(16))) char ring[NS * STAGE];
+  constexpr int WGN = LdsCfg<T>::kWaves / 2;  // waves along n (2 along m)
+  constexpr int WM = TILE / 2 / 16, WN = TILE / WGN / 16;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (blockIdx.z == 1) {
+    const int64_t nt = (int64_t)gridDim.x * LdsCfg<T>::kThreads;
+    for (int64_t i = (int64_t)blockIdx.x * LdsCfg<T>::kThreads + tid; i < g.zero_words; i += nt) g.zero[i] = 0u;
+    return;
+  }
+  const int wm = w / WGN, wn = w % WGN, fr = lane & 15, fq = lane >> 4;
+  const int i = blockIdx.x, per_xcd = g.tiles_x * g.tiles_y / g.nxcd;
+  const int tstep = (int)gridDim.x / g.nxcd;
+  const int tile0 = (i % g.nxcd) * per_xcd + i / g.nxcd;
+  const int nk = (int)(g.K / KST);  // stages per tile
+  const int S = nk * g.per_wg;      // stages of the stream
+
+  int it = tile0, ik = 0;  // tile and stage of the next load
+  Dma<T, AOp, false> da(g.a, (int64_t)(it / g.tiles_x) * TILE, w, lane);
+  Dma<T, BOp, false> db(g.b, (int64_t)(it % g.tiles_x) * TILE, w, lane);
+  const uint32_t rl0 = (uint32_t)(uintptr_t)(lds_void_t*)ring;
+  auto issue_next = [&](uint32_t st) {
+    if (ik == nk) {
+      ik = 0;
+      it += tstep;
+      da = Dma<T, AOp, false>(g.a, (int64_t)(it / g.tiles_x) * TILE, w, lane);
+      db = Dma<T, BOp, false>(g.b, (int64_t)(it % g.tiles_x) * TILE, w, lane);
+    }
+    const int64_t k0 = (int64_t)(ik++) * KST;
+    da.issue(st, k0, w, lane);
+    db.issue(st + STAGE / 2, k0, w, lane);
+  };
+
+  f32x4_t acc[WM][WN];
+  f32x4_t colt[WN];  // column terms of this lane's output columns in the current tile
+  auto tile_start = [&](int t) {
+#pragma unroll
+    for (int a = 0; a < WM; ++a)
+#pragma unroll
+      for (int j = 0; j < WN; ++j) acc[a][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int64_t n0 = (int64_t)(t % g.tiles_x) * TILE;
+#pragma unroll
+    for (int j = 0; j < WN; ++j) {
+      const int64_t n = n0 + wn * 16 * WN + j * 16 + 4 * fq;
+      colt[j] = ((g.N & 3) == 0 && n + 3 < g.N) ? g.epi.col4(n) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    // an explicit wait for these loads (and everything before them), so that
+    // the compiler places none of its own in the epilogue inside the stream,
+    // where it would also wait for the next tile's ring loads
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  };
+  auto epilogue = [&](int t) {
+    const int64_t m0 = (int64_t)(t / g.tiles_x) * TILE, n0 = (int64_t)(t % g.tiles_x) * TILE;
+    const bool vec_n = (g.N & 3) == 0;
+#pragma unroll
+    for (int a = 0; a < WM; ++a)
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const int64_t m = m0 + wm * 16 * WM + a * 16 + fr;
+        const int64_t n = n0 + wn * 16 * WN + j * 16 + 4 * fq;
+        if (m >= g.M || n >= g.N) continue;
+        if (vec_n && n + 3 < g.N) {
+          g.epi.store4(m, n, acc[a][j] + colt[j]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (n + e >= g.N) break;
+            g.epi(m, n + e, acc[a][j][e]);
+          }
+        }
+      }
+  };
+  // One stage, as in gemm_lds_kernel with three stages in flight: stage s
+  // (slot cur) is complete once at most (stages issued after it) x 4 loads
+  // of this wave are outstanding; the bare barrier covers the other waves
+  // and frees the slot refilled here.  The slot's offset goes through an
+  // empty asm statement, so that the compiler adds it to one set of lane
+  // offsets per stage instead of keeping a set of addresses per slot.
+  auto stage = [&](int s, int cur) {
+    const int after = S - 1 - s;
+    if (after >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+    else if (after == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __builtin_amdgcn_s_barrier();
+    if (s + NS - 1 < S) issue_next(rl0 + (uint32_t)((cur == 0 ? NS - 1 : cur - 1) * STAGE));
+    uint32_t off = (uint32_t)(cur * STAGE);
+    asm volatile("" : "+s"(off));
+    const char* sa = ring + off;
+    const char* sb = sa + STAGE / 2;
+    u32x4_t bfv[WN], afv[WM];
+#pragma unroll
+    for (int j = 0; j < WN; ++j) bfv[j] = frag_krows(sb, wn * 16 * WN + 16 * j + fr, fq);
+#pragma unroll
+    for (int a = 0; a < WM; ++a) afv[a] = frag_krows(sa, wm * 16 * WM + 16 * a + fr, fq);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int a = 0; a < WM; ++a)
+#pragma unroll
+      for (int j = 0; j < WN; ++j) acc[a][j] = Mfma<T>::mac(bfv[j], afv[a], acc[a][j]);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  int ct = tile0;  // tile of the products
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (j < S) issue_next(rl0 + (uint32_t)(j * STAGE));
+  tile_start(ct);
+  int s = 0;
+  for (int j = 0; j < g.per_wg; ++j) {
+    for (int k = 0; k < nk; k += NS, s += NS) {
+      stage(s, 0);
+      stage(s + 1, 1);
+      stage(s + 2, 2);
+      stage(s + 3, 3);
+    }
+    epilogue(ct);
+    ct += tstep;
+    if (j + 1 < g.per_wg) tile_start(ct);
+  }
+}
+
 // Split-K sum in a fixed order (split 0, 1, ...), then the epilogue.
 template <class Epi>
 __global__ void __launch_bounds__(256) splitk_reduce(const float* part, int64_t M, int64_t N, int splits, Epi epi) {
@@ -837,10 +974,23 @@ static hipError_t run_gemm_lds(const Plan& p, int64_t M, int64_t N, int64_t K, c
   const int64_t ktiles = K / LdsCfg<T>::kKStage;
   int ktps = (int)((ktiles + gs.splits - 1) / gs.splits);
   if (ktps < 1) ktps = 1;
+  const int64_t tx = (N + TILE - 1) / TILE, ty = (M + TILE - 1) / TILE, tiles = tx * ty;
   GemmArgs<AOp, BOp, Epi> g{M, N, K, ktps, gs.splits, a, b, e, part, (uint32_t*)zero, (int64_t)(zero_bytes / 4),
-                            db.src, db.out, db.rows, db.bf16, db.cols, db.H, p.nxcd};
+                            db.src, db.out, db.rows, db.bf16, db.cols, db.H, p.nxcd, (int)tx, (int)ty, 1};
+  // Persistent form: both operands k-contiguous, no split, no column sum,
+  // the tiles an exact multiple (>= 2) of the CUs, the stages per tile a
+  // multiple of four.
+  if constexpr (AMN == 0 && BMN == 0) {
+    if (gs.splits == 1 && !g.dsum_out && p.cus > 0 && p.cus % p.nxcd == 0 &&
+        tiles % p.cus == 0 && tiles / p.cus >= 2 && ktps % 4 == 0) {
+      g.per_wg = (int)(tiles / p.cus);
+      const dim3 grid_m((unsigned)p.cus, 1u, g.zero_words > 0 ? 2u : 1u);
+      hipLaunchKernelGGL((gemm_lds_multi_kernel<T, AOp, BOp, Epi>), grid_m, dim3(LdsCfg<T>::kThreads), 0, s, g);
+      return hipGetLastError();
+    }
+  }
   const unsigned gz = (unsigned)gs.splits + ((g.zero_words > 0 || g.dsum_out) ? 1u : 0u);
-  dim3 grid((unsigned)((N + TILE - 1) / TILE), (unsigned)((M + TILE - 1) / TILE), gz);
+  dim3 grid((unsigned)tx, (unsigned)ty, gz);
   auto fn = gemm_lds_kernel<T, AMN, BMN, AOp, BOp, Epi>;  // the ring is static LDS
   hipLaunchKernelGGL(fn, grid, dim3(LdsCfg<T>::kThreads), 0, s, g);
   hipError_t err = hipGetLastError();
