@@ -123,7 +123,10 @@ typedef struct {
   int32_t xcd_local;       /* 1: every batch group runs on one XCD */
   int32_t fwd_valu;
   int32_t bwd_valu;
-  int32_t reserved[7];
+  int32_t inproj_tiles_per_wg; /* input projection: output tiles per work-group
+                                  (> 1: persistent work-groups, one per CU;
+                                  16-byte aligned x and W assumed) */
+  int32_t reserved[6];
 } lstm_plan_info;
 int lstm_query_plan(const lstm_shape* shape, lstm_plan_info* info);
 

@@ -965,6 +965,22 @@ static GemmShape choose_shape_lds(int64_t M, int64_t N, int64_t K, int cus, int 
   return gs;
 }
 
+// Tiles per work-group of the persistent form (gemm_lds_multi_kernel) for
+// an M x N x K product with both operands k-contiguous, or 1 where it does
+// not apply: it needs no split of K, the tiles an exact multiple (>= 2) of
+// the CUs, and the stages per tile a multiple of four.
+template <typename T>
+static int multi_tiles_per_wg(const Plan& p, int64_t M, int64_t N, int64_t K) {
+  constexpr int TILE = LdsCfg<T>::kTile;
+  const GemmShape gs = choose_shape_lds<T>(M, N, K, p.cus, 1);
+  const int64_t tiles = ((M + TILE - 1) / TILE) * ((N + TILE - 1) / TILE);
+  const int64_t ktiles = K / LdsCfg<T>::kKStage;
+  if (gs.splits != 1 || p.cus <= 0 || p.cus % p.nxcd != 0 || tiles % p.cus != 0 || tiles / p.cus < 2 ||
+      ktiles % 4 != 0)
+    return 1;
+  return (int)(tiles / p.cus);
+}
+
 template <typename T, int AMN, int BMN, class AOp, class BOp, class Epi>
 static hipError_t run_gemm_lds(const Plan& p, int64_t M, int64_t N, int64_t K, const AOp& a, const BOp& b,
                                const Epi& e, float* part, void* zero, size_t zero_bytes, hipStream_t s,
@@ -974,16 +990,13 @@ static hipError_t run_gemm_lds(const Plan& p, int64_t M, int64_t N, int64_t K, c
   const int64_t ktiles = K / LdsCfg<T>::kKStage;
   int ktps = (int)((ktiles + gs.splits - 1) / gs.splits);
   if (ktps < 1) ktps = 1;
-  const int64_t tx = (N + TILE - 1) / TILE, ty = (M + TILE - 1) / TILE, tiles = tx * ty;
+  const int64_t tx = (N + TILE - 1) / TILE, ty = (M + TILE - 1) / TILE;
   GemmArgs<AOp, BOp, Epi> g{M, N, K, ktps, gs.splits, a, b, e, part, (uint32_t*)zero, (int64_t)(zero_bytes / 4),
                             db.src, db.out, db.rows, db.bf16, db.cols, db.H, p.nxcd, (int)tx, (int)ty, 1};
-  // Persistent form: both operands k-contiguous, no split, no column sum,
-  // the tiles an exact multiple (>= 2) of the CUs, the stages per tile a
-  // multiple of four.
   if constexpr (AMN == 0 && BMN == 0) {
-    if (gs.splits == 1 && !g.dsum_out && p.cus > 0 && p.cus % p.nxcd == 0 &&
-        tiles % p.cus == 0 && tiles / p.cus >= 2 && ktps % 4 == 0) {
-      g.per_wg = (int)(tiles / p.cus);
+    const int per_wg = g.dsum_out ? 1 : multi_tiles_per_wg<T>(p, M, N, K);
+    if (per_wg > 1) {
+      g.per_wg = per_wg;
       const dim3 grid_m((unsigned)p.cus, 1u, g.zero_words > 0 ? 2u : 1u);
       hipLaunchKernelGGL((gemm_lds_multi_kernel<T, AOp, BOp, Epi>), grid_m, dim3(LdsCfg<T>::kThreads), 0, s, g);
       return hipGetLastError();
@@ -1000,6 +1013,14 @@ static hipError_t run_gemm_lds(const Plan& p, int64_t M, int64_t N, int64_t K, c
   return hipGetLastError();
 }
 
+// the input projection takes the pipelined path (operands 16-byte aligned)
+template <typename T>
+static bool inproj_lds_ok(const Plan& p) {
+  constexpr int VEC = 16 / sizeof(T);
+  return p.I % LdsCfg<T>::kKStage == 0 && lds_depth_ok<T>(p.I) && p.I % VEC == 0 && p.Z % VEC == 0 &&
+         p.H % VEC == 0 && p.TB > 0 && small_buf(p.TB * p.I, p.esize) && small_buf(p.G4 * p.Z, p.esize);
+}
+
 template <typename T>
 static hipError_t inproj_t(const Plan& p, const void* x, const void* W, const void* b, float* P, float* part,
                            void* zero, size_t zero_bytes, hipStream_t s) {
@@ -1007,8 +1028,7 @@ static hipError_t inproj_t(const Plan& p, const void* x, const void* W, const vo
   KRowsX<T> a{(const T*)x, p.I, p.TB, p.I, aligned16(x) && p.I % VEC == 0};
   KRowsWx<T> bw{(const T*)W, p.H, p.Z, p.G4, p.I, aligned16(W) && p.Z % VEC == 0 && p.H % VEC == 0};
   EpiP e{P, b, p.H, p.G4, p.dtype};
-  if (p.I % LdsCfg<T>::kKStage == 0 && lds_depth_ok<T>(p.I) && a.vec_ok && bw.vec_ok && p.TB > 0 &&
-      small_buf(p.TB * p.I, p.esize) && small_buf(p.G4 * p.Z, p.esize))
+  if (inproj_lds_ok<T>(p) && a.vec_ok && bw.vec_ok)
     return run_gemm_lds<T, 0, 0>(p, p.TB, p.G4, p.I, a, bw, e, part, zero, zero_bytes, s);
   return run_gemm<T, KRowsX<T>, false, KRowsWx<T>, false, EpiP>(p, p.TB, p.G4, p.I, a, bw, e, part, zero, zero_bytes, s);
 }
@@ -1041,6 +1061,11 @@ static hipError_t dw_t(const Plan& p, const void* dG, const void* x, const void*
     return run_gemm_lds<T, 1, 1>(p, p.G4, p.Z, p.TB, a, bz, e, part, zero, zero_bytes, s, dd);
   return run_gemm<T, MNRowsPlain<T>, true, MNRowsZ<T>, true, EpiDW<T>>(p, p.G4, p.Z, p.TB, a, bz, e, part, zero,
                                                                        zero_bytes, s, dd);
+}
+
+int inproj_tiles_per_wg(const Plan& p) {
+  if (p.dtype) return inproj_lds_ok<bf16_t>(p) ? multi_tiles_per_wg<bf16_t>(p, p.TB, p.G4, p.I) : 1;
+  return inproj_lds_ok<float>(p) ? multi_tiles_per_wg<float>(p, p.TB, p.G4, p.I) : 1;
 }
 
 hipError_t launch_gemm_inproj(const Plan& p, const void* x, const void* W, const void* b, float* P, float* part,

@@ -86,6 +86,9 @@ hipError_t launch_gemm_dx(const Plan& p, const void* dG, const void* W, void* dx
 hipError_t launch_gemm_dw(const Plan& p, const void* dG, const void* x, const void* h0, const void* y, void* dW,
                           float* part, void* zero, size_t zero_bytes, const float* DBP, void* db, hipStream_t s);
 size_t gemm_partial_bytes(const Plan& p, int cus);
+// output tiles per work-group of the input projection (1: one tile each;
+// 16-byte aligned operands assumed)
+int inproj_tiles_per_wg(const Plan& p);
 
 hipError_t launch_fwd_recurrent(const Plan& p, const float* P, const void* W, const void* h0,
                                 const void* c0, void* y, void* hT, void* cT, void* Gs, float* Cs,

@@ -286,6 +286,7 @@ int lstm_query_plan(const lstm_shape* shape, lstm_plan_info* info) {
   info->xcd_local = p.xcd_local ? 1 : 0;
   info->fwd_valu = fwd_vec_ok(p) ? 1 : 0;
   info->bwd_valu = p.bwd_valu ? 1 : 0;
+  info->inproj_tiles_per_wg = inproj_tiles_per_wg(p);
   return LSTM_OK;
 }
 

@@ -42,8 +42,9 @@ class Shape(ctypes.Structure):
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("rows_per_group", "units_per_group", "groups", "units_groups",
-                                               "grid", "waves", "xcd_local", "fwd_valu", "bwd_valu")] + \
-               [("reserved", ctypes.c_int32 * 7)]
+                                               "grid", "waves", "xcd_local", "fwd_valu", "bwd_valu",
+                                               "inproj_tiles_per_wg")] + \
+               [("reserved", ctypes.c_int32 * 6)]
 
 
 _P = ctypes.c_void_p

@@ -13,7 +13,9 @@ same stored values.
    configuration: sampled batch rows against the oracle run on those rows
    (rows of the batch are independent in both passes), dW/db from a second
    backward whose cotangents are zero outside the sampled rows, linearity of
-   the backward in its cotangents, and run-to-run determinism.
+   the backward in its cotangents, and run-to-run determinism;
+ * an fp32 shape whose input projection takes the persistent form (sampled
+   rows and masked dW/db, as above).
 """
 import numpy as np
 import pytest
@@ -51,13 +53,15 @@ def full_check(inp, lstm, tol=None):
 
 
 # Layouts of the persistent recurrences on one MI355X (256 CUs in 8 XCDs):
-# (rows per group, units per group, waves, XCD-local, forward VALU, backward VALU)
+# (rows per group, units per group, waves, XCD-local, forward VALU, backward
+# VALU), and the input projection's output tiles per work-group (> 1: the
+# persistent form; 256 x 256 bf16 tiles, 32-deep stages)
 PLANS = {
-    "f32_T8_B4_I16_H32": (4, 8, 4, 0, 1, 1),
-    "f32_T64_B32_I256_H256": (4, 8, 4, 1, 1, 1),
-    "bf16_T128_B64_I512_H1024": (8, 32, 8, 1, 0, 0),
-    "bf16_T512_B16_I1024_H2048": (8, 16, 8, 0, 0, 0),
-    "bf16_T256_B256_I1024_H1024": (32, 32, 8, 1, 0, 0),
+    "f32_T8_B4_I16_H32": ((4, 8, 4, 0, 1, 1), 1),
+    "f32_T64_B32_I256_H256": ((4, 8, 4, 1, 1, 1), 1),
+    "bf16_T128_B64_I512_H1024": ((8, 32, 8, 1, 0, 0), 2),     # 32 x 16 tiles
+    "bf16_T512_B16_I1024_H2048": ((8, 16, 8, 0, 0, 0), 4),    # 32 x 32 tiles
+    "bf16_T256_B256_I1024_H1024": ((32, 32, 8, 1, 0, 0), 16), # 256 x 16 tiles
 }
 
 
@@ -70,7 +74,8 @@ def test_workload_plans(lstm, name):
     p = lstm.query_plan(lstm.make_shape(w.T, w.B, w.I, w.H, code))
     say(name, p)
     got = (p["rows_per_group"], p["units_per_group"], p["waves"], p["xcd_local"], p["fwd_valu"], p["bwd_valu"])
-    assert got == PLANS[name]
+    assert got == PLANS[name][0]
+    assert p["inproj_tiles_per_wg"] == PLANS[name][1]
     assert p["grid"] == p["groups"] * p["units_groups"] <= 256
 
 
@@ -248,6 +253,43 @@ def test_bf16_backward_linearity_full_size(lstm, big_runs):
     for k in outs[0]:
         e = rel_l2(outs[2][k], outs[0][k] + outs[1][k])
         assert e <= TOL["bf16"], (k, e)
+
+
+def test_f32_persistent_input_projection(lstm):
+    """fp32 through the persistent input projection (128 x 128 tiles, 16-deep
+    stages: 32 x 16 tiles, two per work-group on 256 CUs): sampled batch rows
+    of every output, and dW/db from cotangents zero outside those rows,
+    against the oracle on the rows alone."""
+    T, B, I, H = 16, 256, 1024, 512
+    shape = lstm.make_shape(T, B, I, H, lstm.F32)
+    p = lstm.query_plan(shape)
+    say("case: f32 persistent input projection", p)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert p["inproj_tiles_per_wg"] == 2
+    inp = synth.make_inputs(T, B, I, H, "f32", seed=23, dist=ALL)
+    rows = [0, 97, 255]
+    out, m, d = run_gpu(inp, lstm, torch)
+    ref = oracle.fwd_bwd(rows_of(inp, rows))
+    got = dict(y=out["y"][:, rows], hT=out["hT"][rows], cT=out["cT"][rows], dx=out["dx"][:, rows],
+               dh0=out["dh0"][rows], dc0=out["dc0"][rows])
+    errs, bad = compare(got, ref, "f32", keys=tuple(got))
+    say("rel-L2:", {k: f"{v:.2e}" for k, v in errs.items()})
+    assert not bad, bad
+    mask = np.zeros(B)
+    mask[rows] = 1.0
+    masked = dict(inp)
+    masked["dy"] = inp["dy"] * mask[None, :, None]
+    for k in ("dhT", "dcT"):
+        masked[k] = None if inp[k] is None else inp[k] * mask[:, None]
+    dm = {k: to_dev(masked[k], "f32", torch) for k in ("dy", "dhT", "dcT")}
+    m.forward(d["x"], d["W"], d["b"], d["h0"], d["c0"])
+    m.backward(dm["dy"], dm["dhT"], dm["dcT"], d["x"], d["W"], d["h0"], d["c0"])
+    m.check()
+    torch.cuda.synchronize()
+    refm = oracle.fwd_bwd(rows_of(masked, rows))
+    errs = {"dW": rel_l2(to_host(m.dW), refm["dW"]), "db": rel_l2(to_host(m.db), refm["db"])}
+    say("rel-L2:", errs)
+    assert errs["dW"] <= TOL["f32"] and errs["db"] <= TOL["f32"], errs
 
 
 def test_determinism(lstm):
