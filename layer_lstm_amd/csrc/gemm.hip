@@ -744,6 +744,11 @@ __global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_kernel(GemmAr
     }
 }
 
+// value of lane (lane ^ 8): DPP rotation by 8 within each row of 16 lanes
+__device__ __forceinline__ float lane_xor8(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
+}
+
 // Persistent form for products whose operands are both k-contiguous rows
 // (the input projection): one work-group per CU walks per_wg output tiles,
 // and its loads form one stream over them, so the first stages of a tile
@@ -808,24 +813,47 @@ __global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_multi_kernel(
     // where it would also wait for the next tile's ring loads
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   };
+  // Output blocks are written in pairs of 16 x 16 blocks (j0, j1 = j0 + 1):
+  // lanes of rows 0-7 keep their j0 values and take the j1 values of the
+  // lane 8 rows further (a DPP row rotation by 8), lanes of rows 8-15 the
+  // reverse, so that each store covers 8 whole rows of 32 columns (128
+  // contiguous bytes each) instead of 16 half rows.
+  // one lane's four outputs (m, n..n+3): 16 bytes with the column term
+  // (which tile_start fetched exactly for such columns), else one by one
+  // through the epilogue, which adds it
+  auto store_lane = [&](int64_t m, int64_t n, const f32x4_t& v, const f32x4_t& ct) {
+    if (m >= g.M || n >= g.N) return;
+    if ((g.N & 3) == 0 && n + 3 < g.N) {
+      g.epi.store4(m, n, v + ct);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (n + e >= g.N) break;
+        g.epi(m, n + e, v[e]);
+      }
+    }
+  };
   auto epilogue = [&](int t) {
     const int64_t m0 = (int64_t)(t / g.tiles_x) * TILE, n0 = (int64_t)(t % g.tiles_x) * TILE;
-    const bool vec_n = (g.N & 3) == 0;
+    const bool hi = fr >= 8;
 #pragma unroll
     for (int a = 0; a < WM; ++a)
 #pragma unroll
-      for (int j = 0; j < WN; ++j) {
-        const int64_t m = m0 + wm * 16 * WM + a * 16 + fr;
-        const int64_t n = n0 + wn * 16 * WN + j * 16 + 4 * fq;
-        if (m >= g.M || n >= g.N) continue;
-        if (vec_n && n + 3 < g.N) {
-          g.epi.store4(m, n, acc[a][j] + colt[j]);
-        } else {
+      for (int jj = 0; jj < WN / 2; ++jj) {
+        const int j0 = 2 * jj, j1 = j0 + 1;
+        const int64_t mb = m0 + wm * 16 * WM + a * 16;  // first row of the blocks
+        const int64_t nb = n0 + wn * 16 * WN + j0 * 16;  // first column of the pair
+        if ((g.N & 3) == 0 && nb + 31 < g.N) {
+          const f32x4_t v0 = acc[a][j0] + colt[j0], v1 = acc[a][j1] + colt[j1];
+          f32x4_t p1;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (n + e >= g.N) break;
-            g.epi(m, n + e, acc[a][j][e]);
-          }
+          for (int e = 0; e < 4; ++e) p1[e] = lane_xor8(v1[e]);
+          const int r = fr & 7;
+          if (mb + r < g.M) g.epi.store4(mb + r, nb + (hi ? 16 : 0) + 4 * fq, hi ? p1 : v0);
+          if (mb + 8 + r < g.M) g.epi.store4(mb + 8 + r, nb + (hi ? 0 : 16) + 4 * fq, hi ? v0 : p1);
+        } else {
+          store_lane(mb + fr, nb + 4 * fq, acc[a][j0], colt[j0]);
+          store_lane(mb + fr, nb + 16 + 4 * fq, acc[a][j1], colt[j1]);
         }
       }
   };
