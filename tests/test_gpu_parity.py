@@ -14,8 +14,8 @@ same stored values.
    (rows of the batch are independent in both passes), dW/db from a second
    backward whose cotangents are zero outside the sampled rows, linearity of
    the backward in its cotangents, and run-to-run determinism;
- * an fp32 shape whose input projection takes the persistent form (sampled
-   rows and masked dW/db, as above).
+ * shapes whose input projection takes the persistent form: fp32 (sampled
+   rows and masked dW/db, as above) and bf16 with a partial last row tile.
 """
 import numpy as np
 import pytest
@@ -290,6 +290,32 @@ def test_f32_persistent_input_projection(lstm):
     errs = {"dW": rel_l2(to_host(m.dW), refm["dW"]), "db": rel_l2(to_host(m.db), refm["db"])}
     say("rel-L2:", errs)
     assert errs["dW"] <= TOL["f32"] and errs["db"] <= TOL["f32"], errs
+
+
+def test_persistent_input_projection_ragged_rows(lstm):
+    """bf16 through the persistent input projection with a partial last row
+    tile: T*B = 131070 = 511 full 256-row tiles + 254 rows, one column tile
+    (4H = 256), two tiles per work-group on 256 CUs.  Sampled batch rows
+    against the oracle on those rows; at t = T-1, rows b >= 3 lie in the
+    partial tile."""
+    T, B, I, H = 510, 257, 128, 64
+    p = lstm.query_plan(lstm.make_shape(T, B, I, H, lstm.BF16))
+    say("case: bf16 persistent input projection, ragged rows", p)
+    if torch.cuda.get_device_properties(0).multi_processor_count == 256:
+        assert p["inproj_tiles_per_wg"] == 2
+    inp = synth.make_inputs(T, B, I, H, "bf16", seed=29, dist=ALL)
+    rows = [0, 128, 256]
+    out, _, _ = run_gpu(inp, lstm, torch)
+    ref = oracle.fwd_bwd(rows_of(inp, rows))
+    got = dict(y=out["y"][:, rows], hT=out["hT"][rows], cT=out["cT"][rows], dx=out["dx"][:, rows],
+               dh0=out["dh0"][rows], dc0=out["dc0"][rows])
+    errs, bad = compare(got, ref, "bf16", keys=tuple(got))
+    say("rel-L2:", {k: f"{v:.2e}" for k, v in errs.items()})
+    assert not bad, bad
+    last = dict(y=out["y"][T - 1, rows[1:]])
+    errs, bad = compare(last, dict(y=ref["y"][T - 1, 1:]), "bf16", keys=("y",))
+    say("rel-L2 (last step, partial tile):", errs)
+    assert not bad, bad
 
 
 def test_determinism(lstm):
