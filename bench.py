@@ -127,9 +127,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the data-parallel split over the batch is described in DESIGN.md); "
-              "run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: there is no multi-GPU path (sequences are "
+              "independent, so several GPUs would each take a share of the batch with "
+              "one all-reduce of dW and db); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
