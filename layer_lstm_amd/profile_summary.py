@@ -8,6 +8,8 @@ profiles/ and the per-kernel HBM traffic record that bench.py reports.
         [--stats DIR] --command "..." [--command "..."]
     python -m layer_lstm_amd.profile_summary mfma DIR OUT.txt --workload NAME \
         --command "..."
+    python -m layer_lstm_amd.profile_summary stalls DIR [DIR ...] --out OUT.txt \
+        --workload NAME --command "..."
 
 `stats` reads <DIR>/*kernel_stats.csv (rocprofv3 --kernel-trace --stats
 --output-format csv) and writes the per-kernel table with the command that
@@ -21,7 +23,9 @@ source so that a record goes stale when the kernel changes; with --stats
 reports the achieved HBM GB/s of each kind (bytes per launch / average
 launch duration).  `mfma` reads
 one --pmc run of SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE and reports
-the MFMA utilisation of each kernel kind.
+the MFMA utilisation of each kernel kind.  `stalls` reads --pmc runs that
+each include SQ_WAVE_CYCLES and reports every other SQ counter of them as a
+share of the wave-cycles of each kernel kind (median over launches).
 """
 from __future__ import annotations
 
@@ -185,6 +189,54 @@ def cmd_mfma(a):
     print("\n".join(lines))
 
 
+# per-wave SQ counters that `stalls` reports against SQ_WAVE_CYCLES (the
+# others of a run, counted per SIMD or per CU, are left out)
+WAVE_COUNTERS = ("SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+                 "SQ_ACTIVE_INST_VMEM", "SQ_ACTIVE_INST_SCA", "SQ_ACTIVE_INST_ANY")
+
+
+def cmd_stalls(a):
+    """Each per-wave SQ counter of the runs as a share of SQ_WAVE_CYCLES
+    (both summed over the device for one dispatch), median over the
+    dispatches of a kernel kind."""
+    shares = {}
+    names = []
+    for d in a.dirs:
+        per = {}
+        for r in csv.DictReader(open(find_csv(d, "counter_collection.csv"))):
+            k = kind_of(r["Kernel_Name"])
+            if k is None:
+                continue
+            per.setdefault((k, r["Dispatch_Id"]), {})[r["Counter_Name"]] = float(r["Counter_Value"])
+        for (k, _), c in per.items():
+            wc = c.get("SQ_WAVE_CYCLES", 0.0)
+            if wc <= 0:
+                continue
+            for n, v in c.items():
+                if n not in WAVE_COUNTERS:
+                    continue
+                if n not in names:
+                    names.append(n)
+                shares.setdefault(k, {}).setdefault(n, []).append(v / wc)
+    lines = ["# Wave-cycle shares per kernel from rocprofv3 counters", "", "commands:", ""]
+    lines += [f"    {c}" for c in a.command] + [""]
+    lines.append("share = counter / SQ_WAVE_CYCLES of the same launch (median over launches).  WAIT_ANY: waves")
+    lines.append("waiting on s_waitcnt or a barrier; WAIT_INST_ANY: waves ready but not issuing (dependencies, a")
+    lines.append("busy unit such as the other wave's MFMAs); ACTIVE_INST_*: issuing that kind (VALU includes MFMA)")
+    lines.append(f"workload {a.workload}")
+    short = [n[3:] for n in names]
+    lines.append(f"{'kernel kind':22s} " + " ".join(f"{n:>14s}" for n in short))
+    for k in KINDS:
+        if k not in shares:
+            continue
+        row = f"{k:22s} "
+        row += " ".join(f"{100 * statistics.median(shares[k][n]):13.1f}%" if n in shares[k] else f"{'-':>14s}"
+                        for n in names)
+        lines.append(row)
+    open(a.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -208,8 +260,13 @@ def main():
     t.add_argument("--out-txt", required=True)
     t.add_argument("--stats", default=None)
     t.add_argument("--command", action="append", default=[])
+    st = sub.add_parser("stalls")
+    st.add_argument("dirs", nargs="+")
+    st.add_argument("--out", required=True)
+    st.add_argument("--workload", required=True)
+    st.add_argument("--command", action="append", default=[])
     a = ap.parse_args()
-    {"stats": cmd_stats, "traffic": cmd_traffic, "mfma": cmd_mfma}[a.cmd](a)
+    {"stats": cmd_stats, "traffic": cmd_traffic, "mfma": cmd_mfma, "stalls": cmd_stalls}[a.cmd](a)
 
 
 if __name__ == "__main__":
