@@ -65,6 +65,10 @@ void oracle_set_threads(int n) {
 
 /*
  * Forward pass ("前向传播公式" table).
+ *   reverse: 0, or 1 for the reverse direction of the operator's direction
+ *            attribute ("参数说明"): the steps run from t = T-1 down to 0, so
+ *            the step at time t reads the state of time t+1 and h0/c0 enter
+ *            at t = T-1; hT/cT are the state after the step at t = 0.
  *   x  [T,B,I], W [4H,H+I], b [4H] or NULL, h0/c0 [B,H] or NULL (zero state)
  *   y  [T,B,H]      h_t for every step (the layer output)
  *   hT, cT [B,H]    state after the last step (may be NULL)
@@ -73,7 +77,7 @@ void oracle_set_threads(int n) {
  *   cell  [T,B,H]   c_t per step (same remark)
  * Returns 0, or -1 on a bad size / allocation failure.
  */
-int oracle_lstm_fwd(long T, long B, long I, long H,
+int oracle_lstm_fwd(long T, long B, long I, long H, int reverse,
                     const double* x, const double* W, const double* b,
                     const double* h0, const double* c0,
                     double* y, double* hT, double* cT,
@@ -87,7 +91,8 @@ int oracle_lstm_fwd(long T, long B, long I, long H,
   if (h0) memcpy(hp, h0, (size_t)(B * H) * sizeof(double));
   if (c0) memcpy(cp, c0, (size_t)(B * H) * sizeof(double));
 
-  for (long t = 0; t < T; ++t) {
+  for (long s = 0; s < T; ++s) {
+    const long t = reverse ? T - 1 - s : s; /* time of the s-th step */
     const double* xt = x + t * B * I;
     /* pre-activation a = W z_t + b with z_t = [h_{t-1}; x_t] */
 #pragma omp parallel for schedule(static)
@@ -132,6 +137,8 @@ int oracle_lstm_fwd(long T, long B, long I, long H,
 
 /*
  * Backward pass ("反向传播算法" steps 1-6) from the stored forward values.
+ *   reverse as in the forward (the recursion then runs from t = 0 up to T-1:
+ *   the reverse of the forward's step order, whichever the direction);
  *   x, W, h0, c0 as in the forward; y, gates, cell as the forward wrote them;
  *   dy [T,B,H]; dhT, dcT [B,H] or NULL (zero).
  * Outputs (overwritten, never accumulated into):
@@ -147,7 +154,7 @@ int oracle_lstm_fwd(long T, long B, long I, long H,
  * already holds the factor) is added as it is.  The carries start from the
  * given final-state gradients: delta-h = dhT, delta-c = dcT.
  */
-int oracle_lstm_bwd(long T, long B, long I, long H,
+int oracle_lstm_bwd(long T, long B, long I, long H, int reverse,
                     const double* x, const double* W,
                     const double* h0, const double* c0,
                     const double* y, const double* gates, const double* cell,
@@ -172,7 +179,8 @@ int oracle_lstm_bwd(long T, long B, long I, long H,
   if (dhT) memcpy(dhc, dhT, (size_t)(B * H) * sizeof(double));
   if (dcT) memcpy(dcc, dcT, (size_t)(B * H) * sizeof(double));
 
-  for (long t = T - 1; t >= 0; --t) {
+  for (long s = T - 1; s >= 0; --s) {
+    const long t = reverse ? T - 1 - s : s; /* time of the s-th forward step */
     /* steps 1-3 and the cell carry of step 5 (elementwise per (b, j)) */
     for (long bb = 0; bb < B; ++bb) {
       for (long j = 0; j < H; ++j) {
@@ -182,7 +190,8 @@ int oracle_lstm_bwd(long T, long B, long I, long H,
         const double gg = gates[o * G4 + 2 * H + j];
         const double og = gates[o * G4 + 3 * H + j];
         const double c = cell[o * H + j];
-        const double cprev = t > 0 ? cell[(o - B) * H + j] : (c0 ? c0[bb * H + j] : 0.0);
+        double cprev = t > 0 ? cell[(o - B) * H + j] : (c0 ? c0[bb * H + j] : 0.0);
+        if (reverse) cprev = t < T - 1 ? cell[(o + B) * H + j] : (c0 ? c0[bb * H + j] : 0.0);
         const double tc = tanh(c);
         const double dh = dy[o * H + j] + dhc[bb * H + j];             /* step 1 */
         const double dc = dh * og * (1.0 - tc * tc) + dcc[bb * H + j]; /* step 2 */
@@ -222,6 +231,7 @@ int oracle_lstm_bwd(long T, long B, long I, long H,
       for (long bb = 0; bb < B; ++bb) {
         const double g = dG[(t * B + bb) * G4 + r];
         const double* hprev = t > 0 ? y + ((t - 1) * B + bb) * H : (h0 ? h0 + bb * H : NULL);
+        if (reverse) hprev = t < T - 1 ? y + ((t + 1) * B + bb) * H : (h0 ? h0 + bb * H : NULL);
         const double* xt = x + (t * B + bb) * I;
         for (long k = 0; k < H; ++k) dwr[k] += g * (hprev ? hprev[k] : 0.0);
         for (long k = 0; k < I; ++k) dwr[H + k] += g * xt[k];

@@ -37,9 +37,9 @@ def build(force: bool = False) -> str:
 def _bind(path):
     lib = ctypes.CDLL(path)
     L, P = ctypes.c_long, ctypes.c_void_p
-    lib.oracle_lstm_fwd.argtypes = [L, L, L, L] + [P] * 9
+    lib.oracle_lstm_fwd.argtypes = [L, L, L, L, ctypes.c_int] + [P] * 9
     lib.oracle_lstm_fwd.restype = ctypes.c_int
-    lib.oracle_lstm_bwd.argtypes = [L, L, L, L] + [P] * 17
+    lib.oracle_lstm_bwd.argtypes = [L, L, L, L, ctypes.c_int] + [P] * 17
     lib.oracle_lstm_bwd.restype = ctypes.c_int
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
@@ -90,11 +90,13 @@ def _p(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def fwd(x, W, b=None, h0=None, c0=None):
+def fwd(x, W, b=None, h0=None, c0=None, reverse=False):
     """Forward pass.  Returns dict(y, hT, cT, gates, cell) as fp64 arrays.
 
     x [T,B,I], W [4H,H+I], b [4H] or None, h0/c0 [B,H] or None (zero state).
     gates is [T,B,4H] (activated i,f,g,o blocks), cell is c_t, [T,B,H].
+    reverse: the steps run from t = T-1 down to 0 (the operator's reverse
+    direction); tensors keep their time-major layout.
     """
     x = _f64(x)
     T, B, I = x.shape
@@ -108,15 +110,16 @@ def fwd(x, W, b=None, h0=None, c0=None):
     cT = np.empty((B, H))
     gates = np.empty((T, B, 4 * H))
     cell = np.empty((T, B, H))
-    rc = _load().oracle_lstm_fwd(T, B, I, H, _p(x), _p(W), _p(b), _p(h0), _p(c0),
+    rc = _load().oracle_lstm_fwd(T, B, I, H, int(bool(reverse)), _p(x), _p(W), _p(b), _p(h0), _p(c0),
                                  _p(y), _p(hT), _p(cT), _p(gates), _p(cell))
     if rc != 0:
         raise RuntimeError(f"oracle_lstm_fwd failed ({rc})")
     return dict(y=y, hT=hT, cT=cT, gates=gates, cell=cell)
 
 
-def bwd(x, W, h0, c0, fw, dy, dhT=None, dcT=None, want_debug=False):
-    """Backward pass from the forward record ``fw`` (the dict ``fwd`` returns).
+def bwd(x, W, h0, c0, fw, dy, dhT=None, dcT=None, want_debug=False, reverse=False):
+    """Backward pass from the forward record ``fw`` (the dict ``fwd`` returns,
+    with the same ``reverse``).
 
     Returns dict(dx, dW, db, dh0, dc0) and, with want_debug, also dgates
     [T,B,4H] (gate deltas) and dcell [T,B,H] (cell gradient per step).
@@ -138,7 +141,7 @@ def bwd(x, W, h0, c0, fw, dy, dhT=None, dcT=None, want_debug=False):
     dc0 = np.empty((B, H))
     dgates = np.empty((T, B, 4 * H)) if want_debug else None
     dcell = np.empty((T, B, H)) if want_debug else None
-    rc = _load().oracle_lstm_bwd(T, B, I, H, _p(x), _p(W), _p(h0), _p(c0),
+    rc = _load().oracle_lstm_bwd(T, B, I, H, int(bool(reverse)), _p(x), _p(W), _p(h0), _p(c0),
                                  _p(y), _p(gates), _p(cell), _p(dy), _p(dhT), _p(dcT),
                                  _p(dx), _p(dW), _p(db), _p(dh0), _p(dc0),
                                  _p(dgates), _p(dcell))
@@ -152,10 +155,12 @@ def bwd(x, W, h0, c0, fw, dy, dhT=None, dcT=None, want_debug=False):
 
 def fwd_bwd(inp: dict) -> dict:
     """Run forward then backward on an input dict with keys
-    x, W, b, h0, c0, dy, dhT, dcT (values may be None where optional)."""
-    fw = fwd(inp["x"], inp["W"], inp.get("b"), inp.get("h0"), inp.get("c0"))
+    x, W, b, h0, c0, dy, dhT, dcT (values may be None where optional) and
+    optionally reverse (default False)."""
+    rev = bool(inp.get("reverse", False))
+    fw = fwd(inp["x"], inp["W"], inp.get("b"), inp.get("h0"), inp.get("c0"), reverse=rev)
     bw = bwd(inp["x"], inp["W"], inp.get("h0"), inp.get("c0"), fw, inp["dy"],
-             inp.get("dhT"), inp.get("dcT"))
+             inp.get("dhT"), inp.get("dcT"), reverse=rev)
     out = {k: fw[k] for k in ("y", "hT", "cT")}
     out.update(bw)
     return out

@@ -11,6 +11,9 @@ expected value.  All of these run on the CPU.
  * the forget-gate product law of "LSTM梯度流动特性" pins the cell carry and the
    reading that f enters it once;
  * segment composition and linearity pin the carry-in / carry-out contract;
+ * the reverse direction (the page's direction attribute, "参数说明") equals
+   the forward direction on time-flipped inputs, and passes finite
+   differences of its own loss;
  * PyTorch's CPU nn.LSTM in fp64 with autograd is an independent library
    implementation of the same cell (gate order i,f,g,o and the two weight
    blocks are its documented layout) -- licensed by the MXNet page's remark
@@ -41,7 +44,8 @@ def loss(inp, fw):
 
 
 def run_loss(inp):
-    fw = oracle.fwd(inp["x"], inp["W"], inp.get("b"), inp.get("h0"), inp.get("c0"))
+    fw = oracle.fwd(inp["x"], inp["W"], inp.get("b"), inp.get("h0"), inp.get("c0"),
+                    reverse=bool(inp.get("reverse", False)))
     return loss(inp, fw)
 
 
@@ -92,6 +96,32 @@ def _single_thread():
 def test_fd_tiny(T, B, I, H):
     inp = full_inputs(T, B, I, H, seed=T * 100 + B * 10 + I + H * 1000, scale_w=0.9)
     fd_check(inp)
+
+
+@pytest.mark.parametrize("T,B,I,H", [(3, 2, 3, 2), (4, 1, 2, 3)])
+def test_fd_tiny_reverse(T, B, I, H):
+    """Finite differences of the loss in the reverse direction: every
+    gradient, including dh0 and dc0 of the state that enters at t = T-1."""
+    inp = full_inputs(T, B, I, H, seed=31 + T + 10 * H, scale_w=0.9)
+    inp["reverse"] = True
+    fd_check(inp)
+
+
+def test_reverse_direction_is_the_forward_on_flipped_time():
+    """The reverse direction runs the same cell from t = T-1 down to 0; on
+    time-flipped x and dy that is the forward direction, so y and dx flip
+    back and every other output agrees.  The two runs take different step
+    orders and index the previous step differently."""
+    inp = full_inputs(5, 3, 4, 6, seed=7)
+    rev = oracle.fwd_bwd(dict(inp, reverse=True))
+    fwd = oracle.fwd_bwd(dict(inp, x=inp["x"][::-1].copy(), dy=inp["dy"][::-1].copy()))
+    for k in ("y", "dx"):
+        np.testing.assert_allclose(rev[k], fwd[k][::-1], rtol=1e-12, atol=1e-13)
+    for k in ("hT", "cT", "dW", "db", "dh0", "dc0"):
+        np.testing.assert_allclose(rev[k], fwd[k], rtol=1e-12, atol=1e-13)
+    # and it is not the forward direction on the unflipped inputs
+    same = oracle.fwd_bwd(inp)
+    assert np.max(np.abs(same["y"] - rev["y"])) > 1e-3
 
 
 def test_fd_small_workload_shape():
