@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define LSTM_ABI_VERSION 1
+#define LSTM_ABI_VERSION 2
 
 /* Gate row blocks of W, b, dW, db (the "ifjo" order of the page's
  * gate_order attribute). */
@@ -73,7 +73,7 @@ enum {
   LSTM_OK = 0,
   LSTM_ERR_NULL = -1,        /* a required pointer is NULL */
   LSTM_ERR_DIMS = -2,        /* T, B or I < 0, or H <= 0 */
-  LSTM_ERR_DTYPE = -3,       /* dtype is not LSTM_F32 / LSTM_BF16 */
+  LSTM_ERR_DTYPE = -3,       /* dtype is not LSTM_F32 / LSTM_BF16, or an unknown flag is set */
   LSTM_ERR_ALIGN = -4,       /* a tensor is not aligned to its element size, or the workspace to 256 B */
   LSTM_ERR_WORKSPACE = -5,   /* workspace_bytes < lstm_query() */
   LSTM_ERR_UNSUPPORTED = -6, /* shape outside the kernels' envelope (see lstm_query) */
@@ -83,14 +83,24 @@ enum {
   LSTM_ERR_DEVICE = -10      /* the current device is not gfx950 or could not be queried */
 };
 
-/* Problem shape.  dtype is LSTM_F32 or LSTM_BF16. */
+/* Direction of time (SingleLayerLstmGrad, 参数说明: the direction attribute,
+ * forward or reverse).  The reverse direction runs the same cell from
+ * t = T-1 down to t = 0: the step at time t reads h and c of time t+1, h0
+ * and c0 enter at t = T-1, and hT / cT are the states after the step at
+ * t = 0; dh0 / dc0 are the gradients of h0 / c0 as they enter.  Tensors
+ * keep their [T][B][...] layout in both directions. */
+enum { LSTM_REVERSE = 1 };
+
+/* Problem shape.  dtype is LSTM_F32 or LSTM_BF16; flags is 0 (forward in
+ * time) or LSTM_REVERSE, other bits must be 0 (else LSTM_ERR_DTYPE).  The
+ * forward call and the backward call of one record take the same flags. */
 typedef struct {
   int64_t T; /* time steps, >= 0 */
   int64_t B; /* batch, >= 0 */
   int64_t I; /* input size, >= 0 */
   int64_t H; /* hidden size, >= 1 */
   int32_t dtype;
-  int32_t reserved; /* must be 0 */
+  int32_t flags; /* 0 or LSTM_REVERSE */
 } lstm_shape;
 
 /* LSTM_ABI_VERSION of the library. */

@@ -62,12 +62,16 @@ struct MNRowsPlain {  // [K][ld], r contiguous
   __device__ __forceinline__ bool same_seg(int64_t, int64_t) const { return true; }
 };
 template <typename T>
-struct MNRowsZ {  // Z[tb][r] = r < H ? h_{t-1}[b][r] : x[tb][r-H]
-  const T* x; const T* h0; const T* y; int64_t B, H, I, R, K; bool vec_ok;
+struct MNRowsZ {  // Z[tb][r] = r < H ? h_prev(t)[b][r] : x[tb][r-H]
+  // h_prev(t): the hidden state the step at time t read -- y[t-1] (h0 at
+  // t = 0), or y[t+1] (h0 at t = T-1) in the reverse direction (rev)
+  const T* x; const T* h0; const T* y; int64_t B, H, I, R, K; bool vec_ok; bool rev;
   __device__ __forceinline__ const T* krow(int64_t tb, int64_t r) const {
     if (r < H) {
-      if (tb >= B) return y + (tb - B) * H + r;
-      return h0 ? h0 + tb * H + r : nullptr;  // nullptr = zero initial state
+      if (!rev && tb >= B) return y + (tb - B) * H + r;
+      if (rev && tb < K - B) return y + (tb + B) * H + r;
+      const int64_t b = rev ? tb - (K - B) : tb;
+      return h0 ? h0 + b * H + r : nullptr;  // nullptr = zero initial state
     }
     return x + tb * I + (r - H);
   }
@@ -528,21 +532,26 @@ struct Dma<T, MNRowsWx<T>, true> {  // k-row = interleaved gate row of W's input
   }
 };
 template <typename T>
-struct Dma<T, MNRowsZ<T>, true> {  // Z[tb] = [h_{t-1}[b] | x[tb]]
+struct Dma<T, MNRowsZ<T>, true> {  // Z[tb] = [h_prev(t)[b] | x[tb]]
   // three buffers, all addressed as [tb][...] with the stage's first k-row
-  // tb0 = k0 as the uniform offset: h0 for tb < B (absent: an empty buffer,
-  // read as zeros), y shifted back by B rows for tb >= B, and x
+  // tb0 = k0 as the uniform offset: h0 for the rows tb in [hlo, hhi) -- the
+  // first B rows, or the last B in the reverse direction -- (absent: an empty
+  // buffer, read as zeros), y shifted by B rows (back, or forward in the
+  // reverse direction) for the others, and x
   __amdgpu_buffer_rsrc_t rh, ry, rx;
   uint32_t vh[2], vx[2];
   bool seg;  // this lane's columns lie in the h part
-  int64_t B, hb, ib;
+  int64_t hlo, hhi, hb, ib;
   __device__ __forceinline__ Dma(const MNRowsZ<T>& op, int64_t r0, int w, int lane) {
     constexpr int64_t E = sizeof(T);
-    B = op.B;
     hb = op.H * E;
     ib = op.I * E;
-    rh = rsrc_of(op.h0 ? (const void*)op.h0 : (const void*)op.x, op.h0 ? op.B * hb : 0);
-    ry = rsrc_of((const char*)op.y - op.B * hb, op.K * hb);  // only offsets of rows tb >= B are read
+    hlo = op.rev ? op.K - op.B : 0;
+    hhi = op.rev ? op.K : op.B;
+    rh = op.h0 ? rsrc_of((const char*)op.h0 - hlo * hb, hhi * hb) : rsrc_of(op.x, 0);
+    // only offsets of the y rows are read
+    ry = op.rev ? rsrc_of((const char*)op.y + op.B * hb, (op.K - op.B) * hb)
+                : rsrc_of((const char*)op.y - op.B * hb, op.K * hb);
     rx = rsrc_of(op.x, op.K * ib);
     seg = mn_r<T>(r0, op.R, mn_kr(w, 0, lane), lane) < op.H;
 #pragma unroll
@@ -563,7 +572,7 @@ struct Dma<T, MNRowsZ<T>, true> {  // Z[tb] = [h_{t-1}[b] | x[tb]]
       if (!seg) {
         dma16(rx, dst, vx[j], (uint32_t)(k0 * ib));
         asm volatile("; z: x part" ::: "memory");
-      } else if (k0 + mn_kr(w, j, lane) < B) {
+      } else if (k0 + mn_kr(w, j, lane) >= hlo && k0 + mn_kr(w, j, lane) < hhi) {
         dma16(rh, dst, vh[j], (uint32_t)(k0 * hb));
         asm volatile("; z: h0 part" ::: "memory");
       } else {
@@ -1117,7 +1126,8 @@ static hipError_t dw_t(const Plan& p, const void* dG, const void* x, const void*
   constexpr int VEC = 16 / sizeof(T);
   MNRowsPlain<T> a{(const T*)dG, p.G4, p.G4, p.TB, aligned16(dG) && p.G4 % VEC == 0};
   MNRowsZ<T> bz{(const T*)x, (const T*)h0, (const T*)y, p.B, p.H, p.I, p.Z, p.TB,
-                aligned16(x) && aligned16(y) && (h0 == nullptr || aligned16(h0)) && p.H % VEC == 0 && p.I % VEC == 0};
+                aligned16(x) && aligned16(y) && (h0 == nullptr || aligned16(h0)) && p.H % VEC == 0 && p.I % VEC == 0,
+                p.rev != 0};
   EpiDW<T> e{(T*)dW, p.H, p.Z};
   const DbDuty dd{DBP, db, p.nBG, p.G4, p.H, p.dtype};
   if (p.TB % LdsCfg<T>::kKStage == 0 && lds_depth_ok<T>(p.TB) && p.Z >= VEC && a.vec_ok && bz.vec_ok &&

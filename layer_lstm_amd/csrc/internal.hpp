@@ -50,6 +50,7 @@ struct Plan {
   // region (h ring, gate-delta ring), step flags at these byte offsets
   // inside it
   size_t off_hflags, off_pflags;
+  int rev;          // 1: the reverse direction (steps from t = T-1 down to 0)
   int cus;          // compute units of the device
   int max_splits;   // largest split-K factor of the three products
   size_t off_gp;    // fp32 split-K partials of the products

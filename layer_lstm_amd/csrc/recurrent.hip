@@ -150,7 +150,8 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
   f32x4_t pf[NBT], pfn[NBT];  // P_t (in use) and P_{t+1} (in flight)
   auto load_p = [&](f32x4_t (&dst)[NBT], int tt) {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.P + (int64_t)(tt < a.T ? tt : 0) * (stepP / 4)), 0, tt < a.T ? (int)stepP : 0, 0x00020000);
+        (void*)(a.P + (int64_t)(tt < a.T ? mem_t(tt, a.T, a.rev) : 0) * (stepP / 4)), 0, tt < a.T ? (int)stepP : 0,
+        0x00020000);
 #pragma unroll
     for (int nt = 0; nt < NBT; ++nt)
       dst[nt] = __builtin_bit_cast(
@@ -161,11 +162,11 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
   u32x4_t gq[NBT];  // activated gates of the step, packed (E == 2: two words)
   auto store_record = [&](int tt) {
     const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((T*)a.y + tt * stepY), 0, (int)(stepY * E), 0x00020000);
+        (void*)((T*)a.y + mem_t(tt, a.T, a.rev) * stepY), 0, (int)(stepY * E), 0x00020000);
     const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((T*)a.Gs + tt * stepY * 4), 0, (int)(stepY * 4 * E), 0x00020000);
+        (void*)((T*)a.Gs + mem_t(tt, a.T, a.rev) * stepY * 4), 0, (int)(stepY * 4 * E), 0x00020000);
     const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.Cs + tt * stepY), 0, (int)(stepY * 4), 0x00020000);
+        (void*)(a.Cs + mem_t(tt, a.T, a.rev) * stepY), 0, (int)(stepY * 4), 0x00020000);
 #pragma unroll
     for (int nt = 0; nt < NBT; ++nt) {
       const int o = eok[nt] ? eidx[nt] : (int)stepY;  // stepY: one past the end
@@ -242,7 +243,7 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
     // P_tt of the group's rows and units into buffer tt & 1; rows past B are
     // out of the buffer's range (zeros)
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.P + (int64_t)tt * (stepP / 4)), 0, (int)stepP, 0x00020000);
+        (void*)(a.P + (int64_t)mem_t(tt, a.T, a.rev) * (stepP / 4)), 0, (int)stepP, 0x00020000);
     const uint32_t dst = pl_lds + (uint32_t)((tt & 1) * nbj * 16);
 #pragma unroll
     for (int i = 0; i < RJ; ++i) {
@@ -254,11 +255,11 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
     // the record of step tt from the staging area: every piece read, then
     // every piece stored
     const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((T*)a.y + tt * stepY), 0, (int)(stepY * E), 0x00020000);
+        (void*)((T*)a.y + mem_t(tt, a.T, a.rev) * stepY), 0, (int)(stepY * E), 0x00020000);
     const __amdgpu_buffer_rsrc_t rg = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)((T*)a.Gs + tt * stepY * 4), 0, (int)(stepY * 4 * E), 0x00020000);
+        (void*)((T*)a.Gs + mem_t(tt, a.T, a.rev) * stepY * 4), 0, (int)(stepY * 4 * E), 0x00020000);
     const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.Cs + tt * stepY), 0, (int)(stepY * 4), 0x00020000);
+        (void*)(a.Cs + mem_t(tt, a.T, a.rev) * stepY), 0, (int)(stepY * 4), 0x00020000);
     typedef __attribute__((address_space(3))) const u32x4_t lds_u4;
     u32x4_t vy[RY], vg[RG], vc[RC];
 #pragma unroll
@@ -558,7 +559,7 @@ hipError_t launch_fwd_recurrent(const Plan& p, const float* P, const void* W, co
   char* hd = (char*)HX;  // the packed ring and its flags share the tagged-word region
   FwdArgs a{P, W, h0, c0, y, hT, cT, Gs, Cs, HX, hd, (uint32_t*)(hd + p.off_hflags), (uint32_t)p.off_hflags, err,
             stamps, (int)p.T, (int)p.B, (int)p.H, (int)p.Z, p.NB, p.NJ,
-            p.nJG, p.Hp, p.Bp, p.dtype ? (p.Hp / 2) : p.Hp, p.nBG, p.nxcd, p.xcd_local};
+            p.nJG, p.Hp, p.Bp, p.dtype ? (p.Hp / 2) : p.Hp, p.nBG, p.nxcd, p.xcd_local, p.rev};
   if (fwd_vec_ok(p)) return launch_fwd_vec(p, a, s);
   const int nbt = p.NB < 16 ? 1 : p.NB / 16;
   if (p.dtype) {
@@ -579,7 +580,7 @@ hipError_t launch_bwd_recurrent(const Plan& p, const void* W, const void* c0, co
   char* gd = (char*)PX;  // the gate-delta ring and its flags share the tagged-word region
   BwdArgs a{W, c0, dy, dhT, dcT, Gs, Cs, dG, PX, gd, (uint32_t*)(gd + p.off_pflags), (uint32_t)p.off_pflags,
             DBP, dh0, dc0, err, stamps, (int)p.T, (int)p.B, (int)p.H, (int)p.Z,
-            p.NB, p.NJ, p.nJG, p.Hp, p.Bp, p.nBG, p.nxcd, p.xcd_local};
+            p.NB, p.NJ, p.nJG, p.Hp, p.Bp, p.nBG, p.nxcd, p.xcd_local, p.rev};
   if (p.bwd_valu) return launch_bwd_vec(p, a, s);
   return launch_bwd_col(p, a, s);
 }

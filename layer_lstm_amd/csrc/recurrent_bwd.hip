@@ -175,7 +175,7 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
 #pragma unroll
     for (int s = 0; s < EPTM; ++s) {
       if (!own[s]) continue;
-      const int64_t o = tt * stepC + c_off(s);
+      const int64_t o = (int64_t)mem_t(tt, a.T, a.rev) * stepC + c_off(s);
       if constexpr (E == 4) {
         const u32x4_t g = *(const u32x4_t*)((const T*)a.Gs + 4 * o);
         gw[s][0] = g[0]; gw[s][1] = g[1]; gw[s][2] = g[2]; gw[s][3] = g[3];
@@ -184,7 +184,7 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
         gw[s][0] = (uint32_t)g; gw[s][1] = (uint32_t)(g >> 32);
       }
       cc[s] = a.Cs[o];
-      cp[s] = tt > 0 ? a.Cs[o - stepC] : 0.f;
+      cp[s] = tt > 0 ? a.Cs[(int64_t)mem_t(tt - 1, a.T, a.rev) * stepC + c_off(s)] : 0.f;
       dyv[s] = ((const T*)a.dy)[o];
     }
   };
@@ -205,7 +205,7 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
 #pragma unroll
     for (int s = 0; s < EPTM; ++s) {
       if (!own[s]) continue;
-      T* dst = (T*)a.dG + 4 * (tt * stepC + c_off(s));
+      T* dst = (T*)a.dG + 4 * ((int64_t)mem_t(tt, a.T, a.rev) * stepC + c_off(s));
       if constexpr (E == 4)
         *(u32x4_t*)dst = u32x4_t{dqw[s][0], dqw[s][1], dqw[s][2], dqw[s][3]};
       else
@@ -323,7 +323,7 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
       }
       if (own[s]) {
         if constexpr (!DEF) {
-          T* dst = (T*)a.dG + 4 * (t * stepC + c_off(s));
+          T* dst = (T*)a.dG + 4 * ((int64_t)mem_t(t, a.T, a.rev) * stepC + c_off(s));
           if constexpr (E == 4)
             *(u32x4_t*)dst = __builtin_bit_cast(u32x4_t, dq);
           else

@@ -26,6 +26,7 @@ struct FwdArgs {
   uint64_t* stamps; // optional [kStampWGs][T][kPhases] clock stamps
   int T, B, H, Z, NB, NJ, nJG, Hp, Bp, HW;
   int nBG, nxcd, local;
+  int rev;          // 1: the reverse direction (steps run from t = T-1 down to 0)
 };
 
 struct BwdArgs {
@@ -48,7 +49,14 @@ struct BwdArgs {
   uint64_t* stamps;
   int T, B, H, Z, NB, NJ, nJG, Hp, Bp;
   int nBG, nxcd, local;
+  int rev;          // 1: the reverse direction (the forward ran from t = T-1 down to 0)
 };
+
+// Time index in memory of processing step s (s = 0 is the step that reads
+// the initial state): s itself, or T-1-s in the reverse direction.  Loops,
+// exchange slots and flags count processing steps; every tensor indexed by
+// time (P, y, the record, dy, the gate deltas) is addressed through this.
+__device__ __forceinline__ int mem_t(int s, int T, int rev) { return rev ? T - 1 - s : s; }
 
 // Phase stamps: thread 0 of the first kStampWGs work-groups records the
 // 100 MHz real-time clock (s_memrealtime) at kPhases points of every step when

@@ -105,8 +105,9 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_vec_kernel(FwdArgs a) {
 #pragma unroll
     for (int q = 0; q < U2; ++q) {
       const int u = j0 + ulb + 8 * q;
-      pf[q] = (ew && tt < a.T && u < a.H) ? *(const f32x4_t*)(a.P + ((int64_t)tt * a.B + bme) * G4 + 4 * (int64_t)u)
-                                          : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      pf[q] = (ew && tt < a.T && u < a.H)
+                  ? *(const f32x4_t*)(a.P + ((int64_t)mem_t(tt, a.T, a.rev) * a.B + bme) * G4 + 4 * (int64_t)u)
+                  : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
   };
   load_p(0);
@@ -231,7 +232,7 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_vec_kernel(FwdArgs a) {
           const float h = og * tanh_f(cn);
           cst[q] = cn;
           xstore(dst + (int64_t)bme * a.HW + u, h, (uint32_t)(t + 1), local);
-          const int64_t o = (int64_t)t * a.B + bme;
+          const int64_t o = (int64_t)mem_t(t, a.T, a.rev) * a.B + bme;
           ((float*)a.y)[o * a.H + u] = h;
           *(f32x4_t*)((float*)a.Gs + o * G4 + 4 * (int64_t)u) = f32x4_t{ig, fg, gg, og};
           a.Cs[o * a.H + u] = cn;
@@ -321,11 +322,13 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_vec_kernel(BwdArgs a) {
     pg[0] = pg[1] = pg[2] = pg[3] = 0.f;
     pc = pcp = pdy = 0.f;
     if (tt >= 0 && own) {
-      const int64_t oG = (int64_t)tt * stepG, oC = (int64_t)tt * stepC;
+      const int tm = mem_t(tt, a.T, a.rev);
+      const int64_t oG = (int64_t)tm * stepG, oC = (int64_t)tm * stepC;
       const f32x4_t gv = *(const f32x4_t*)((const float*)a.Gs + oG + g_off);
       pg[0] = gv[0]; pg[1] = gv[1]; pg[2] = gv[2]; pg[3] = gv[3];
       pc = a.Cs[oC + c_off];
-      pcp = tt > 0 ? a.Cs[oC - stepC + c_off] : (a.c0 ? ((const float*)a.c0)[c_off] : 0.f);
+      pcp = tt > 0 ? a.Cs[(int64_t)mem_t(tt - 1, a.T, a.rev) * stepC + c_off]
+                   : (a.c0 ? ((const float*)a.c0)[c_off] : 0.f);
       pdy = ((const float*)a.dy)[oC + c_off];
     }
   };
@@ -374,7 +377,7 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_vec_kernel(BwdArgs a) {
     if (e < nel) {
       f32x4_t dq = {0.f, 0.f, 0.f, 0.f};
       if (own) {
-        const int64_t o = (int64_t)t * a.B + bown;
+        const int64_t o = (int64_t)mem_t(t, a.T, a.rev) * a.B + bown;
         const float gi = pg[0], gf = pg[1], gg = pg[2], go = pg[3];
         const float tc = tanh_f(pc);
         const float dh = pdy + dhc;

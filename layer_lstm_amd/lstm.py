@@ -21,7 +21,8 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 # --- constants restated from include/lstm.h ---------------------------------
-ABI_VERSION = 1
+ABI_VERSION = 2
+REVERSE = 1  # lstm_shape.flags: the reverse direction of time
 GATE_I, GATE_F, GATE_G, GATE_O = 0, 1, 2, 3
 F32, BF16 = 0, 1
 OK = 0
@@ -37,7 +38,7 @@ KERNEL_KINDS = ("input_projection", "forward_recurrence", "backward_recurrence",
 
 class Shape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int64), ("B", ctypes.c_int64), ("I", ctypes.c_int64),
-                ("H", ctypes.c_int64), ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("H", ctypes.c_int64), ("dtype", ctypes.c_int32), ("flags", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -92,8 +93,8 @@ def torch_dtype(dtype: int):
     return torch.float32 if dtype == F32 else torch.bfloat16
 
 
-def make_shape(T, B, I, H, dtype) -> Shape:
-    return Shape(int(T), int(B), int(I), int(H), int(dtype), 0)
+def make_shape(T, B, I, H, dtype, reverse=False) -> Shape:
+    return Shape(int(T), int(B), int(I), int(H), int(dtype), REVERSE if reverse else 0)
 
 
 def query(shape: Shape) -> int:
@@ -188,8 +189,8 @@ class Lstm:
     device.  ``forward``/``backward`` take device tensors and return device
     tensors; nothing is synchronised."""
 
-    def __init__(self, T, B, I, H, dtype=F32, device="cuda"):
-        self.shape = make_shape(T, B, I, H, dtype)
+    def __init__(self, T, B, I, H, dtype=F32, device="cuda", reverse=False):
+        self.shape = make_shape(T, B, I, H, dtype, reverse)
         self.T, self.B, self.I, self.H, self.dtype = T, B, I, H, dtype
         self.tdtype = torch_dtype(dtype)
         self.ws_bytes = query(self.shape)

@@ -43,6 +43,7 @@ def test_constants_match_header(lstm):
     for g, v in (("LSTM_GATE_I", 0), ("LSTM_GATE_F", 1), ("LSTM_GATE_G", 2), ("LSTM_GATE_O", 3)):
         assert header_enum(g) == v
     assert header_enum("LSTM_F32") == lstm.F32 and header_enum("LSTM_BF16") == lstm.BF16
+    assert header_enum("LSTM_REVERSE") == lstm.REVERSE
     for code, name in lstm.STATUS.items():
         if code != 0:
             assert header_enum("LSTM_" + name) == code
@@ -86,5 +87,9 @@ def test_query_rejects_bad_dtype_and_nulls(lstm):
     assert lstm.lib().lstm_query_plan(ctypes.byref(lstm.make_shape(2, 2, 2, 2, 7)), ctypes.byref(info)) == -3
     assert lstm.lib().lstm_query_plan(ctypes.byref(lstm.make_shape(2, -1, 2, 2, 0)), ctypes.byref(info)) == -2
     assert info.grid == 0  # untouched on error
+    s = lstm.make_shape(2, 2, 2, 2, 0)
+    s.flags = 2  # an unknown flag
+    assert lstm.lib().lstm_query(ctypes.byref(s), ctypes.byref(n)) == -3
+    assert lstm.lib().lstm_query_plan(ctypes.byref(s), ctypes.byref(info)) == -3
     assert lstm.lib().lstm_fwd_train(None, *([None] * 9), 0, None) == -1
     assert lstm.lib().lstm_bwd(None, *([None] * 9), 0, *([None] * 6)) == -1

@@ -15,7 +15,9 @@ same stored values.
    backward whose cotangents are zero outside the sampled rows, linearity of
    the backward in its cotangents, and run-to-run determinism;
  * shapes whose input projection takes the persistent form: fp32 (sampled
-   rows and masked dW/db, as above) and bf16 with a partial last row tile.
+   rows and masked dW/db, as above) and bf16 with a partial last row tile;
+ * the reverse direction of time against the oracle through every kernel
+   variant, and against the forward direction on time-flipped inputs.
 """
 import numpy as np
 import pytest
@@ -316,6 +318,44 @@ def test_persistent_input_projection_ragged_rows(lstm):
     errs, bad = compare(last, dict(y=ref["y"][T - 1, 1:]), "bf16", keys=("y",))
     say("rel-L2 (last step, partial tile):", errs)
     assert not bad, bad
+
+
+# The reverse direction (flags = LSTM_REVERSE) through every kernel variant:
+# fp32 VALU recurrences with the register-staged and the pipelined products,
+# the fp32 MFMA forward, and the bf16 MFMA recurrences with and without the
+# forward's direct-to-LDS path.
+@pytest.mark.parametrize("dt,T,B,I,H", [
+    ("f32", 8, 4, 16, 32),
+    ("f32", 64, 32, 256, 256),
+    ("f32", 3, 100, 16, 256),
+    ("bf16", 4, 19, 40, 72),
+    ("bf16", 3, 60, 32, 512),
+    ("bf16", 5, 40, 64, 1024),
+])
+def test_reverse_direction(lstm, dt, T, B, I, H):
+    say(f"case: reverse {dt} T={T} B={B} I={I} H={H}")
+    inp = synth.make_inputs(T, B, I, H, dt, seed=37, dist=ALL)
+    inp["reverse"] = True
+    full_check(inp, lstm)
+
+
+@pytest.mark.parametrize("dt,T,B,I,H", [("f32", 64, 32, 256, 256), ("bf16", 3, 60, 32, 512)])
+def test_reverse_is_forward_on_flipped_time_gpu(lstm, dt, T, B, I, H):
+    """On the GPU, the reverse direction equals the forward direction on
+    time-flipped x and dy: the same arithmetic on the same values, so every
+    output but dW and db (whose sums over t run in another order) matches
+    bit for bit."""
+    say(f"case: reverse vs flipped forward {dt} T={T} B={B} I={I} H={H}")
+    inp = synth.make_inputs(T, B, I, H, dt, seed=41, dist=ALL)
+    rev, _, _ = run_gpu(dict(inp, reverse=True), lstm, torch)
+    fwd, _, _ = run_gpu(dict(inp, x=inp["x"][::-1].copy(), dy=inp["dy"][::-1].copy()), lstm, torch)
+    for k in ("y", "dx"):
+        assert np.array_equal(rev[k], fwd[k][::-1]), k
+    for k in ("hT", "cT", "dh0", "dc0"):
+        assert np.array_equal(rev[k], fwd[k]), k
+    for k in ("dW", "db"):
+        e = rel_l2(rev[k], fwd[k])
+        assert e <= TOL[dt], (k, e)
 
 
 def test_determinism(lstm):
