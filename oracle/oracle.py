@@ -153,10 +153,29 @@ def bwd(x, W, h0, c0, fw, dy, dhT=None, dcT=None, want_debug=False, reverse=Fals
     return out
 
 
+def ifjo_rows(H: int, gate_order: str):
+    """Row index map from the i, f, g, o block order to `gate_order`'s: W in
+    the "ijfo" order (blocks i, g, f, o) is W_ifjo[ifjo_rows(H, "ijfo")].  The
+    two orders are the values of the gate_order attribute of the
+    SingleLayerLstmGrad page (参数说明); the map is its own inverse."""
+    blocks = {"ifjo": (0, 1, 2, 3), "ijfo": (0, 2, 1, 3)}[gate_order]
+    return np.concatenate([np.arange(H) + g * H for g in blocks])
+
+
 def fwd_bwd(inp: dict) -> dict:
     """Run forward then backward on an input dict with keys
     x, W, b, h0, c0, dy, dhT, dcT (values may be None where optional) and
-    optionally reverse (default False)."""
+    optionally reverse (default False) and gate_order ("ifjo", the oracle's
+    own order, or "ijfo": W, b, dW and db with their row blocks relabelled)."""
+    order = inp.get("gate_order", "ifjo")
+    if order != "ifjo":
+        H = inp["W"].shape[0] // 4
+        rows = ifjo_rows(H, order)
+        sub = dict(inp, gate_order="ifjo", W=inp["W"][rows], b=None if inp.get("b") is None else inp["b"][rows])
+        out = fwd_bwd(sub)
+        out["dW"] = out["dW"][rows]
+        out["db"] = out["db"][rows]
+        return out
     rev = bool(inp.get("reverse", False))
     fw = fwd(inp["x"], inp["W"], inp.get("b"), inp.get("h0"), inp.get("c0"), reverse=rev)
     bw = bwd(inp["x"], inp["W"], inp.get("h0"), inp.get("c0"), fw, inp["dy"],

@@ -124,6 +124,29 @@ def test_reverse_direction_is_the_forward_on_flipped_time():
     assert np.max(np.abs(same["y"] - rev["y"])) > 1e-3
 
 
+def test_gate_order_relabelling():
+    """The gate_order attribute ("参数说明": "ifjo" or "ijfo") only relabels
+    the row blocks of W, b, dW and db: the map is its own inverse, and with
+    equal f and g blocks of W and b the two orders give the same forward
+    values and input gradients, and dW / db with those blocks exchanged
+    (the forget and candidate gates still differ, so do their deltas)."""
+    H = 3
+    rows = oracle.ifjo_rows(H, "ijfo")
+    assert np.array_equal(rows[rows], np.arange(4 * H))
+    assert np.array_equal(oracle.ifjo_rows(H, "ifjo"), np.arange(4 * H))
+    inp = full_inputs(3, 2, 2, H, seed=5)
+    W, b = inp["W"].copy(), inp["b"].copy()
+    W[2 * H:3 * H] = W[H:2 * H]
+    b[2 * H:3 * H] = b[H:2 * H]
+    a = oracle.fwd_bwd(dict(inp, W=W, b=b))
+    c = oracle.fwd_bwd(dict(inp, W=W, b=b, gate_order="ijfo"))
+    for k in ("y", "hT", "cT", "dx", "dh0", "dc0"):
+        np.testing.assert_allclose(c[k], a[k], rtol=0, atol=0)
+    np.testing.assert_allclose(c["dW"], a["dW"][rows], rtol=0, atol=0)
+    np.testing.assert_allclose(c["db"], a["db"][rows], rtol=0, atol=0)
+    assert np.max(np.abs(a["dW"][H:2 * H] - a["dW"][2 * H:3 * H])) > 1e-6
+
+
 def test_fd_small_workload_shape():
     """Every element of x, W, b, h0, c0 at the smallest workload's shape
     (T=8, B=4, I=16, H=32; 7040 scalars)."""
