@@ -62,7 +62,7 @@ extern "C" {
 #define LSTM_ABI_VERSION 2
 
 /* Gate row blocks of W, b, dW, db (the "ifjo" order of the page's
- * gate_order attribute). */
+ * gate_order attribute; LSTM_GATES_IJFO below selects "ijfo"). */
 enum { LSTM_GATE_I = 0, LSTM_GATE_F = 1, LSTM_GATE_G = 2, LSTM_GATE_O = 3 };
 
 /* Element type of every ABI tensor. */
@@ -91,16 +91,24 @@ enum {
  * keep their [T][B][...] layout in both directions. */
 enum { LSTM_REVERSE = 1 };
 
-/* Problem shape.  dtype is LSTM_F32 or LSTM_BF16; flags is 0 (forward in
- * time) or LSTM_REVERSE, other bits must be 0 (else LSTM_ERR_DTYPE).  The
- * forward call and the backward call of one record take the same flags. */
+/* Gate order of W's, b's, dW's and db's row blocks (SingleLayerLstmGrad,
+ * 参数说明: the gate_order attribute, "ifjo" or "ijfo").  Without this flag
+ * the blocks are i, f, g, o (LSTM_GATE_I..O below, "ifjo"); with it they
+ * are i, g, f, o ("ijfo", j being the candidate g).  The arithmetic is the
+ * same; only the row blocks are relabelled. */
+enum { LSTM_GATES_IJFO = 2 };
+
+/* Problem shape.  dtype is LSTM_F32 or LSTM_BF16; flags is 0 or an OR of
+ * LSTM_REVERSE and LSTM_GATES_IJFO, other bits must be 0 (else
+ * LSTM_ERR_DTYPE).  The forward call and the backward call of one record
+ * take the same flags. */
 typedef struct {
   int64_t T; /* time steps, >= 0 */
   int64_t B; /* batch, >= 0 */
   int64_t I; /* input size, >= 0 */
   int64_t H; /* hidden size, >= 1 */
   int32_t dtype;
-  int32_t flags; /* 0 or LSTM_REVERSE */
+  int32_t flags; /* 0, LSTM_REVERSE, LSTM_GATES_IJFO or both */
 } lstm_shape;
 
 /* LSTM_ABI_VERSION of the library. */

@@ -128,6 +128,11 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // hazard of asm loads with register outputs does not arise); M0 carries the
 // LDS address and is declared clobbered.
 typedef __attribute__((address_space(3))) void lds_void_t;
+
+// Row block of gate g (0..3 = i, f, g, o) in W, b, dW and db: the gate order
+// "ifjo" (i, f, g, o), or with ijfo "ijfo" (i, g, f, o) -- the two values of
+// the gate_order attribute of the SingleLayerLstmGrad page (参数说明).
+__host__ __device__ __forceinline__ int gate_block(int g, int ijfo) { return (ijfo && (g == 1 || g == 2)) ? 3 - g : g; }
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 // (lds_addr: the LDS byte address the wave's 1 KB goes to)

@@ -32,7 +32,9 @@ constexpr int kLdsRow = kRowBytes + 16;   // padded LDS row
 
 hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
 
-__device__ __forceinline__ int64_t gate_row(int64_t n, int64_t H) { return (n & 3) * H + (n >> 2); }
+__device__ __forceinline__ int64_t gate_row(int64_t n, int64_t H, int ijfo) {
+  return (int64_t)gate_block((int)(n & 3), ijfo) * H + (n >> 2);
+}
 
 // ---------------------------------------------------------------------------
 // Operand accessors.  VEC = elements per 16 bytes.
@@ -46,13 +48,13 @@ struct KRowsX {  // plain row-major [R][ld], rows r, k in [0,K)
 };
 template <typename T>
 struct KRowsWx {  // row r (interleaved gate row) of W's input block
-  const T* W; int64_t H, ld, R, K; bool vec_ok;
-  __device__ __forceinline__ const T* row(int64_t r) const { return W + gate_row(r, H) * ld + H; }
+  const T* W; int64_t H, ld, R, K; bool vec_ok; int ijfo;
+  __device__ __forceinline__ const T* row(int64_t r) const { return W + gate_row(r, H, ijfo) * ld + H; }
 };
 template <typename T>
 struct MNRowsWx {  // k-row = interleaved gate row of W's input block, r = input column
-  const T* W; int64_t H, ld, R, K; bool vec_ok;
-  __device__ __forceinline__ const T* krow(int64_t k, int64_t r) const { return W + gate_row(k, H) * ld + H + r; }
+  const T* W; int64_t H, ld, R, K; bool vec_ok; int ijfo;
+  __device__ __forceinline__ const T* krow(int64_t k, int64_t r) const { return W + gate_row(k, H, ijfo) * ld + H + r; }
   __device__ __forceinline__ bool same_seg(int64_t, int64_t) const { return true; }
 };
 template <typename T>
@@ -201,9 +203,9 @@ __device__ __forceinline__ void store_row4(bf16_t* p, f32x4_t v) {
 __device__ __forceinline__ void store_row4(float* p, f32x4_t v) { *(f32x4_t*)p = v; }
 
 struct EpiP {  // fp32 P with bias in the interleaved column order
-  float* P; const void* bias; int64_t H, ldp; int dtype;
+  float* P; const void* bias; int64_t H, ldp; int dtype; int ijfo;
   __device__ __forceinline__ float bias_at(int64_t n) const {
-    const int64_t r = gate_row(n, H);
+    const int64_t r = gate_row(n, H, ijfo);
     return dtype ? bf2f(((const bf16_t*)bias)[r]) : ((const float*)bias)[r];
   }
   __device__ __forceinline__ void operator()(int64_t m, int64_t n, float v) const {
@@ -228,13 +230,13 @@ struct EpiStore {  // plain row-major output of the storage type
 };
 template <typename T>
 struct EpiDW {  // dW rows back in gate-block order
-  T* dW; int64_t H, N;
+  T* dW; int64_t H, N; int ijfo;
   __device__ __forceinline__ void operator()(int64_t m, int64_t n, float v) const {
-    dW[gate_row(m, H) * N + n] = Elem<T>::from_f(v);
+    dW[gate_row(m, H, ijfo) * N + n] = Elem<T>::from_f(v);
   }
   __device__ __forceinline__ f32x4_t col4(int64_t) const { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
   __device__ __forceinline__ void store4(int64_t m, int64_t n, f32x4_t v) const {
-    store_row4(dW + gate_row(m, H) * N + n, v);
+    store_row4(dW + gate_row(m, H, ijfo) * N + n, v);
   }
 };
 
@@ -253,6 +255,7 @@ struct GemmArgs {
   int dsum_rows;
   int dsum_bf16;
   int64_t dsum_cols, dsum_H;
+  int dsum_ijfo;      // gate-block order of dsum_out (gate_block)
   int nxcd;           // XCDs of the device (1: no XCD-aware tile order)
   // persistent input projection (gemm_lds_multi_kernel) only:
   int tiles_x, tiles_y;  // output tiles along n and m
@@ -305,7 +308,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs<AOp, BOp, Epi> 
       for (int64_t n = blk * kThreads + tid; n < g.dsum_cols; n += nblk * kThreads) {
         float v = 0.f;
         for (int r = 0; r < g.dsum_rows; ++r) v += g.dsum[(int64_t)r * g.dsum_cols + n];
-        const int64_t row = gate_row(n, g.dsum_H);
+        const int64_t row = gate_row(n, g.dsum_H, g.dsum_ijfo);
         if (g.dsum_bf16) ((bf16_t*)g.dsum_out)[row] = f2bf(v);
         else ((float*)g.dsum_out)[row] = v;
       }
@@ -481,7 +484,8 @@ template <typename T>
 struct Dma<T, KRowsWx<T>, false> : DmaKRows<T, KRowsWx<T>> {
   __device__ __forceinline__ Dma(const KRowsWx<T>& op, int64_t row0, int w, int lane) {
     const int64_t H = op.H;
-    this->init(op.W, 4 * H, op.ld, H, op.R, row0, w, lane, [H](int64_t g) { return gate_row(g, H); });
+    const int ijfo = op.ijfo;
+    this->init(op.W, 4 * H, op.ld, H, op.R, row0, w, lane, [H, ijfo](int64_t g) { return gate_row(g, H, ijfo); });
   }
 };
 // r-contiguous k-rows: lane (kr, chunk c) of a stage, r = r0 + c * VEC
@@ -523,7 +527,8 @@ struct Dma<T, MNRowsWx<T>, true> {  // k-row = interleaved gate row of W's input
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int kr = mn_kr(w, j, lane);  // stage k-rows start at a multiple of 4: gate kr & 3, unit + kr / 4
-      vo[j] = (uint32_t)(((kr & 3) * op.H + (kr >> 2)) * ldb + (op.H + mn_r<T>(r0, op.R, kr, lane)) * (int64_t)sizeof(T));
+      vo[j] = (uint32_t)(((int64_t)gate_block(kr & 3, op.ijfo) * op.H + (kr >> 2)) * ldb +
+                         (op.H + mn_r<T>(r0, op.R, kr, lane)) * (int64_t)sizeof(T));
     }
   }
   __device__ __forceinline__ void issue(uint32_t lds, int64_t k0, int w, int) const {
@@ -632,7 +637,7 @@ __global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_kernel(GemmAr
       for (int64_t n = blk * NT + tid; n < g.dsum_cols; n += nblk * NT) {
         float v = 0.f;
         for (int r = 0; r < g.dsum_rows; ++r) v += g.dsum[(int64_t)r * g.dsum_cols + n];
-        const int64_t row = gate_row(n, g.dsum_H);
+        const int64_t row = gate_row(n, g.dsum_H, g.dsum_ijfo);
         if (g.dsum_bf16) ((bf16_t*)g.dsum_out)[row] = f2bf(v);
         else ((float*)g.dsum_out)[row] = v;
       }
@@ -993,12 +998,12 @@ static hipError_t launch_tile(GemmArgs<AOp, BOp, Epi>& g, hipStream_t s) {
 // Runs C = A . B through the epilogue; `part` must hold splits*M*N floats
 // when the shape splits K.  Optionally clears `zero_bytes` at `zero` in the
 // same launch (extra blocks), so that a buffer clear costs no launch.
-struct DbDuty { const float* src; void* out; int rows; int64_t cols, H; int bf16; };
+struct DbDuty { const float* src; void* out; int rows; int64_t cols, H; int bf16; int ijfo; };
 
 template <typename T, class AOp, bool AMN, class BOp, bool BMN, class Epi>
 static hipError_t run_gemm(const Plan& p, int64_t M, int64_t N, int64_t K, const AOp& a, const BOp& b,
                            const Epi& e, float* part, void* zero, size_t zero_bytes, hipStream_t s,
-                           DbDuty db = DbDuty{nullptr, nullptr, 0, 0, 0, 0}) {
+                           DbDuty db = DbDuty{nullptr, nullptr, 0, 0, 0, 0, 0}) {
   if (M <= 0 || N <= 0) {
     if (zero_bytes) return launch_fill_zero(zero, zero_bytes, s);
     return hipSuccess;
@@ -1009,7 +1014,7 @@ static hipError_t run_gemm(const Plan& p, int64_t M, int64_t N, int64_t K, const
   int ktps = (int)((ktiles + gs.splits - 1) / gs.splits);
   if (ktps < 1) ktps = 1;
   GemmArgs<AOp, BOp, Epi> g{M, N, K, ktps, gs.splits, a, b, e, part, (uint32_t*)zero, (int64_t)(zero_bytes / 4),
-                            db.src, db.out, db.rows, db.bf16, db.cols, db.H, p.nxcd};
+                            db.src, db.out, db.rows, db.bf16, db.cols, db.H, db.ijfo, p.nxcd};
   hipError_t err = gs.tile == 128 ? launch_tile<T, 4, 4, AOp, AMN, BOp, BMN, Epi>(g, s)
                                   : launch_tile<T, 2, 2, AOp, AMN, BOp, BMN, Epi>(g, s);
   if (err != hipSuccess || gs.splits == 1) return err;
@@ -1057,7 +1062,7 @@ static int multi_tiles_per_wg(const Plan& p, int64_t M, int64_t N, int64_t K) {
 template <typename T, int AMN, int BMN, class AOp, class BOp, class Epi>
 static hipError_t run_gemm_lds(const Plan& p, int64_t M, int64_t N, int64_t K, const AOp& a, const BOp& b,
                                const Epi& e, float* part, void* zero, size_t zero_bytes, hipStream_t s,
-                               DbDuty db = DbDuty{nullptr, nullptr, 0, 0, 0, 0}) {
+                               DbDuty db = DbDuty{nullptr, nullptr, 0, 0, 0, 0, 0}) {
   constexpr int TILE = LdsCfg<T>::kTile;
   const GemmShape gs = choose_shape_lds<T>(M, N, K, p.cus, part ? p.max_splits : 1);
   const int64_t ktiles = K / LdsCfg<T>::kKStage;
@@ -1065,7 +1070,7 @@ static hipError_t run_gemm_lds(const Plan& p, int64_t M, int64_t N, int64_t K, c
   if (ktps < 1) ktps = 1;
   const int64_t tx = (N + TILE - 1) / TILE, ty = (M + TILE - 1) / TILE;
   GemmArgs<AOp, BOp, Epi> g{M, N, K, ktps, gs.splits, a, b, e, part, (uint32_t*)zero, (int64_t)(zero_bytes / 4),
-                            db.src, db.out, db.rows, db.bf16, db.cols, db.H, p.nxcd, (int)tx, (int)ty, 1};
+                            db.src, db.out, db.rows, db.bf16, db.cols, db.H, db.ijfo, p.nxcd, (int)tx, (int)ty, 1};
   if constexpr (AMN == 0 && BMN == 0) {
     const int per_wg = g.dsum_out ? 1 : multi_tiles_per_wg<T>(p, M, N, K);
     if (per_wg > 1) {
@@ -1099,8 +1104,8 @@ static hipError_t inproj_t(const Plan& p, const void* x, const void* W, const vo
                            void* zero, size_t zero_bytes, hipStream_t s) {
   constexpr int VEC = 16 / sizeof(T);
   KRowsX<T> a{(const T*)x, p.I, p.TB, p.I, aligned16(x) && p.I % VEC == 0};
-  KRowsWx<T> bw{(const T*)W, p.H, p.Z, p.G4, p.I, aligned16(W) && p.Z % VEC == 0 && p.H % VEC == 0};
-  EpiP e{P, b, p.H, p.G4, p.dtype};
+  KRowsWx<T> bw{(const T*)W, p.H, p.Z, p.G4, p.I, aligned16(W) && p.Z % VEC == 0 && p.H % VEC == 0, p.ijfo};
+  EpiP e{P, b, p.H, p.G4, p.dtype, p.ijfo};
   if (inproj_lds_ok<T>(p) && a.vec_ok && bw.vec_ok)
     return run_gemm_lds<T, 0, 0>(p, p.TB, p.G4, p.I, a, bw, e, part, zero, zero_bytes, s);
   return run_gemm<T, KRowsX<T>, false, KRowsWx<T>, false, EpiP>(p, p.TB, p.G4, p.I, a, bw, e, part, zero, zero_bytes, s);
@@ -1111,7 +1116,7 @@ static hipError_t dx_t(const Plan& p, const void* dG, const void* W, void* dx, f
                        size_t zero_bytes, hipStream_t s) {
   constexpr int VEC = 16 / sizeof(T);
   KRowsX<T> a{(const T*)dG, p.G4, p.TB, p.G4, aligned16(dG) && p.G4 % VEC == 0};
-  MNRowsWx<T> bw{(const T*)W, p.H, p.Z, p.I, p.G4, aligned16(W) && p.Z % VEC == 0 && p.H % VEC == 0};
+  MNRowsWx<T> bw{(const T*)W, p.H, p.Z, p.I, p.G4, aligned16(W) && p.Z % VEC == 0 && p.H % VEC == 0, p.ijfo};
   EpiStore<T> e{(T*)dx, p.I};
   if (p.G4 % LdsCfg<T>::kKStage == 0 && lds_depth_ok<T>(p.G4) && p.I >= VEC && a.vec_ok && bw.vec_ok && p.TB > 0 &&
       small_buf(p.TB * p.G4, p.esize) && small_buf(p.G4 * p.Z, p.esize))
@@ -1128,8 +1133,8 @@ static hipError_t dw_t(const Plan& p, const void* dG, const void* x, const void*
   MNRowsZ<T> bz{(const T*)x, (const T*)h0, (const T*)y, p.B, p.H, p.I, p.Z, p.TB,
                 aligned16(x) && aligned16(y) && (h0 == nullptr || aligned16(h0)) && p.H % VEC == 0 && p.I % VEC == 0,
                 p.rev != 0};
-  EpiDW<T> e{(T*)dW, p.H, p.Z};
-  const DbDuty dd{DBP, db, p.nBG, p.G4, p.H, p.dtype};
+  EpiDW<T> e{(T*)dW, p.H, p.Z, p.ijfo};
+  const DbDuty dd{DBP, db, p.nBG, p.G4, p.H, p.dtype, p.ijfo};
   if (p.TB % LdsCfg<T>::kKStage == 0 && lds_depth_ok<T>(p.TB) && p.Z >= VEC && a.vec_ok && bz.vec_ok &&
       small_buf(p.TB * p.G4, p.esize) && small_buf(p.TB * p.Z, p.esize))
     return run_gemm_lds<T, 1, 1>(p, p.G4, p.Z, p.TB, a, bz, e, part, zero, zero_bytes, s, dd);

@@ -51,6 +51,7 @@ struct Plan {
   // inside it
   size_t off_hflags, off_pflags;
   int rev;          // 1: the reverse direction (steps from t = T-1 down to 0)
+  int ijfo;         // 1: W, b, dW, db in the gate order i, g, f, o (gate_block)
   int cus;          // compute units of the device
   int max_splits;   // largest split-K factor of the three products
   size_t off_gp;    // fp32 split-K partials of the products

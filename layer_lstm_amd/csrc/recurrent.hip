@@ -93,7 +93,7 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
         const int ur = j0 + 4 * (mg * MW + mi) + (row >> 2), g = row & 3;
         const int k = (kb0 + p * PB) * KB + col;
         const bool ok = ur < a.H && k < a.H;
-        v[j] = ((const T*)a.W)[ok ? ((int64_t)g * a.H + ur) * a.Z + k : 0];
+        v[j] = ((const T*)a.W)[ok ? ((int64_t)gate_block(g, a.ijfo) * a.H + ur) * a.Z + k : 0];
         v[j] = ok ? v[j] : T(0);
       }
 #pragma unroll
@@ -559,7 +559,7 @@ hipError_t launch_fwd_recurrent(const Plan& p, const float* P, const void* W, co
   char* hd = (char*)HX;  // the packed ring and its flags share the tagged-word region
   FwdArgs a{P, W, h0, c0, y, hT, cT, Gs, Cs, HX, hd, (uint32_t*)(hd + p.off_hflags), (uint32_t)p.off_hflags, err,
             stamps, (int)p.T, (int)p.B, (int)p.H, (int)p.Z, p.NB, p.NJ,
-            p.nJG, p.Hp, p.Bp, p.dtype ? (p.Hp / 2) : p.Hp, p.nBG, p.nxcd, p.xcd_local, p.rev};
+            p.nJG, p.Hp, p.Bp, p.dtype ? (p.Hp / 2) : p.Hp, p.nBG, p.nxcd, p.xcd_local, p.rev, p.ijfo};
   if (fwd_vec_ok(p)) return launch_fwd_vec(p, a, s);
   const int nbt = p.NB < 16 ? 1 : p.NB / 16;
   if (p.dtype) {
@@ -580,7 +580,7 @@ hipError_t launch_bwd_recurrent(const Plan& p, const void* W, const void* c0, co
   char* gd = (char*)PX;  // the gate-delta ring and its flags share the tagged-word region
   BwdArgs a{W, c0, dy, dhT, dcT, Gs, Cs, dG, PX, gd, (uint32_t*)(gd + p.off_pflags), (uint32_t)p.off_pflags,
             DBP, dh0, dc0, err, stamps, (int)p.T, (int)p.B, (int)p.H, (int)p.Z,
-            p.NB, p.NJ, p.nJG, p.Hp, p.Bp, p.nBG, p.nxcd, p.xcd_local, p.rev};
+            p.NB, p.NJ, p.nJG, p.Hp, p.Bp, p.nBG, p.nxcd, p.xcd_local, p.rev, p.ijfo};
   if (p.bwd_valu) return launch_bwd_vec(p, a, s);
   return launch_bwd_col(p, a, s);
 }

@@ -103,7 +103,7 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
         const int r = ((rl / (PB * KB)) * NKB + p * PB) * KB + rl % (PB * KB);
         const int ur = r >> 2, g = r & 3;
         const bool ok = uok && ur < a.H;
-        v[j] = ((const T*)a.W)[ok ? ((int64_t)g * a.H + ur) * a.Z + u : 0];
+        v[j] = ((const T*)a.W)[ok ? ((int64_t)gate_block(g, a.ijfo) * a.H + ur) * a.Z + u : 0];
         v[j] = ok ? v[j] : T(0);
       }
       __syncthreads();  // the previous pass's fragment reads are done

@@ -27,6 +27,7 @@ struct FwdArgs {
   int T, B, H, Z, NB, NJ, nJG, Hp, Bp, HW;
   int nBG, nxcd, local;
   int rev;          // 1: the reverse direction (steps run from t = T-1 down to 0)
+  int ijfo;         // gate-block order of W (gate_block)
 };
 
 struct BwdArgs {
@@ -50,6 +51,7 @@ struct BwdArgs {
   int T, B, H, Z, NB, NJ, nJG, Hp, Bp;
   int nBG, nxcd, local;
   int rev;          // 1: the reverse direction (the forward ran from t = T-1 down to 0)
+  int ijfo;         // gate-block order of W (gate_block)
 };
 
 // Time index in memory of processing step s (s = 0 is the step that reads

@@ -79,7 +79,7 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_vec_kernel(FwdArgs a) {
     const int ur = j0 + ulb + 8 * q;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const float* wrow = (const float*)a.W + ((int64_t)g * a.H + ur) * a.Z;
+      const float* wrow = (const float*)a.W + ((int64_t)gate_block(g, a.ijfo) * a.H + ur) * a.Z;
 #pragma unroll
       for (int i = 0; i < L; ++i) {
         const int k = c * L + i;
@@ -300,7 +300,8 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_vec_kernel(BwdArgs a) {
 #pragma unroll
       for (int rr = 0; rr < VRC; ++rr) {
         const int r = qp * VRC + rr, ur = j0 + (r >> 2), g = r & 3;
-        wq[i][cc][rr] = (k < a.H && ur < a.H) ? ((const float*)a.W)[((int64_t)g * a.H + ur) * a.Z + k] : 0.f;
+        wq[i][cc][rr] =
+            (k < a.H && ur < a.H) ? ((const float*)a.W)[((int64_t)gate_block(g, a.ijfo) * a.H + ur) * a.Z + k] : 0.f;
       }
     }
 

@@ -23,6 +23,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 # --- constants restated from include/lstm.h ---------------------------------
 ABI_VERSION = 2
 REVERSE = 1  # lstm_shape.flags: the reverse direction of time
+GATES_IJFO = 2  # lstm_shape.flags: W/b/dW/db row blocks in the gate order i, g, f, o
 GATE_I, GATE_F, GATE_G, GATE_O = 0, 1, 2, 3
 F32, BF16 = 0, 1
 OK = 0
@@ -93,8 +94,11 @@ def torch_dtype(dtype: int):
     return torch.float32 if dtype == F32 else torch.bfloat16
 
 
-def make_shape(T, B, I, H, dtype, reverse=False) -> Shape:
-    return Shape(int(T), int(B), int(I), int(H), int(dtype), REVERSE if reverse else 0)
+def make_shape(T, B, I, H, dtype, reverse=False, gate_order="ifjo") -> Shape:
+    if gate_order not in ("ifjo", "ijfo"):
+        raise ValueError(f"gate_order {gate_order!r}: 'ifjo' or 'ijfo'")
+    flags = (REVERSE if reverse else 0) | (GATES_IJFO if gate_order == "ijfo" else 0)
+    return Shape(int(T), int(B), int(I), int(H), int(dtype), flags)
 
 
 def query(shape: Shape) -> int:
@@ -189,8 +193,8 @@ class Lstm:
     device.  ``forward``/``backward`` take device tensors and return device
     tensors; nothing is synchronised."""
 
-    def __init__(self, T, B, I, H, dtype=F32, device="cuda", reverse=False):
-        self.shape = make_shape(T, B, I, H, dtype, reverse)
+    def __init__(self, T, B, I, H, dtype=F32, device="cuda", reverse=False, gate_order="ifjo"):
+        self.shape = make_shape(T, B, I, H, dtype, reverse, gate_order)
         self.T, self.B, self.I, self.H, self.dtype = T, B, I, H, dtype
         self.tdtype = torch_dtype(dtype)
         self.ws_bytes = query(self.shape)

@@ -17,7 +17,9 @@ same stored values.
  * shapes whose input projection takes the persistent form: fp32 (sampled
    rows and masked dW/db, as above) and bf16 with a partial last row tile;
  * the reverse direction of time against the oracle through every kernel
-   variant, and against the forward direction on time-flipped inputs.
+   variant, and against the forward direction on time-flipped inputs;
+ * the "ijfo" gate order against the oracle, and against the default order
+   on relabelled weights.
 """
 import numpy as np
 import pytest
@@ -356,6 +358,38 @@ def test_reverse_is_forward_on_flipped_time_gpu(lstm, dt, T, B, I, H):
     for k in ("dW", "db"):
         e = rel_l2(rev[k], fwd[k])
         assert e <= TOL[dt], (k, e)
+
+
+# The "ijfo" gate order (flags = LSTM_GATES_IJFO) through the register-staged
+# and direct-to-LDS products and both recurrence forms; once with the
+# reverse direction as well.
+@pytest.mark.parametrize("dt,T,B,I,H,rev", [
+    ("f32", 8, 4, 16, 32, False),
+    ("f32", 64, 32, 256, 256, False),
+    ("bf16", 4, 19, 40, 72, False),
+    ("bf16", 3, 60, 32, 512, True),
+])
+def test_gate_order_ijfo(lstm, dt, T, B, I, H, rev):
+    say(f"case: ijfo {dt} T={T} B={B} I={I} H={H} reverse={rev}")
+    inp = synth.make_inputs(T, B, I, H, dt, seed=43, dist=ALL)
+    inp["gate_order"] = "ijfo"
+    inp["reverse"] = rev
+    full_check(inp, lstm)
+
+
+@pytest.mark.parametrize("dt,T,B,I,H", [("f32", 16, 256, 1024, 512), ("bf16", 3, 60, 32, 512)])
+def test_gate_order_is_a_relabelling_gpu(lstm, dt, T, B, I, H):
+    """On the GPU, the "ijfo" order on relabelled W and b equals the default
+    order bit for bit (dW and db relabelled back): the same arithmetic.  The
+    fp32 shape takes the persistent input projection."""
+    say(f"case: ijfo relabelling {dt} T={T} B={B} I={I} H={H}")
+    inp = synth.make_inputs(T, B, I, H, dt, seed=47, dist=ALL)
+    rows = oracle.ifjo_rows(H, "ijfo")
+    a, _, _ = run_gpu(inp, lstm, torch)
+    c, _, _ = run_gpu(dict(inp, W=inp["W"][rows], b=inp["b"][rows], gate_order="ijfo"), lstm, torch)
+    for k in ("y", "hT", "cT", "dx", "dh0", "dc0"):
+        assert np.array_equal(c[k], a[k]), k
+    assert np.array_equal(c["dW"], a["dW"][rows]) and np.array_equal(c["db"], a["db"][rows])
 
 
 def test_determinism(lstm):
