@@ -2,6 +2,7 @@
 """Benchmark of the single-layer LSTM forward + BPTT on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--reverse]
+                    [--gate-order ifjo|ijfo]
 
 One step = lstm_fwd_train + lstm_bwd on one batch of seeded synthetic input
 (every kernel of the path: input projection, forward recurrence, backward
@@ -11,7 +12,8 @@ before the timed region starts.  Prints one JSON line with the metric
 fraction of the MFMA peak of the storage type), a roofline record of the
 kernel that takes the most time, and the fp64 CPU oracle timed on the host
 on a bounded sample of the same workload.  --reverse runs the reverse
-direction of time (lstm_shape.flags = LSTM_REVERSE) on the same workload.
+direction of time (lstm_shape.flags = LSTM_REVERSE), --gate-order ijfo the
+other gate order of W's row blocks (LSTM_GATES_IJFO), on the same workload.
 """
 from __future__ import annotations
 
@@ -83,7 +85,7 @@ def copy_calibration(mib):
     print(json.dumps({"copy_bytes": n * 4, "launches": 3}), flush=True)
 
 
-def cpu_baseline(w, inp, budget_s, reverse=False):
+def cpu_baseline(w, inp, budget_s, reverse=False, gate_order="ifjo"):
     """Time the fp64 oracle (as it stands) on a bounded sample of the same
     workload: whole sequences (batch rows), as many as fit in about
     `budget_s` seconds by a one-row probe; when the whole batch takes less,
@@ -91,7 +93,7 @@ def cpu_baseline(w, inp, budget_s, reverse=False):
     from oracle import oracle
 
     def rows(n):
-        sub = dict(inp, B=n, reverse=reverse)
+        sub = dict(inp, B=n, reverse=reverse, gate_order=gate_order)
         for k in ("x", "dy"):
             sub[k] = inp[k][:, :n]
         for k in ("h0", "c0", "dhT", "dcT"):
@@ -123,6 +125,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for the CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--reverse", action="store_true", help="the reverse direction of time")
+    ap.add_argument("--gate-order", default="ifjo", choices=("ifjo", "ijfo"), help="row-block order of W, b, dW, db")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -151,7 +154,7 @@ def main():
         return None if a is None else torch.from_numpy(np.asarray(a, dtype=np.float32)).to(dev).to(td)
 
     d = {k: put(inp[k]) for k in ("x", "W", "b", "h0", "c0", "dy", "dhT", "dcT")}
-    m = lstm.Lstm(w.T, w.B, w.I, w.H, code, reverse=args.reverse)
+    m = lstm.Lstm(w.T, w.B, w.I, w.H, code, reverse=args.reverse, gate_order=args.gate_order)
 
     def step():
         m.forward(d["x"], d["W"], d["b"], d["h0"], d["c0"])
@@ -207,8 +210,8 @@ def main():
         peak, runit = HBM_GBS, "GB/s"
     roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": runit,
                 "frac": round(achieved / peak, 5),
-                # (the counter runs are of the forward direction)
-                "traffic": None if args.reverse else traffic_for(w.name, dom),
+                # (the counter runs are of the forward direction, default gate order)
+                "traffic": None if (args.reverse or args.gate_order != "ifjo") else traffic_for(w.name, dom),
                 "kernel": dom, "avg_launch_us": round(avg_s * 1e6, 2)}
 
     flops = w.flops
@@ -220,7 +223,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded; see layer_lstm_amd/synth.py)",
         "config": {"workload": w.name, "T": w.T, "B": w.B, "I": w.I, "H": w.H, "storage": w.dtype,
-                   "direction": "reverse" if args.reverse else "forward", "parallelism": "single GPU"},
+                   "direction": "reverse" if args.reverse else "forward", "gate_order": args.gate_order,
+                   "parallelism": "single GPU"},
         "effective_tflops": round(eff_tflops, 3),
         "fraction_of_peak": round(eff_tflops / PEAK_TFLOPS[w.dtype], 5),
         "roofline": roofline,
@@ -229,7 +233,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
-        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, args.reverse)
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, args.reverse, args.gate_order)
     print(json.dumps(out), flush=True)
 
 
