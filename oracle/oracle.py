@@ -165,8 +165,16 @@ def ifjo_rows(H: int, gate_order: str):
 def fwd_bwd(inp: dict) -> dict:
     """Run forward then backward on an input dict with keys
     x, W, b, h0, c0, dy, dhT, dcT (values may be None where optional) and
-    optionally reverse (default False) and gate_order ("ifjo", the oracle's
-    own order, or "ijfo": W, b, dW and db with their row blocks relabelled)."""
+    optionally reverse (default False), gate_order ("ifjo", the oracle's
+    own order, or "ijfo": W, b, dW and db with their row blocks relabelled)
+    and two_bias (b and db [2][4H])."""
+    if inp.get("two_bias"):
+        # b = [b_ih; b_hh] enter the pre-activation as their sum (the PyTorch
+        # LSTM page's two biases); both receive the one bias gradient
+        b2 = inp["b"]
+        out = fwd_bwd(dict(inp, two_bias=False, b=None if b2 is None else b2[0] + b2[1]))
+        out["db"] = np.stack([out["db"], out["db"]])
+        return out
     order = inp.get("gate_order", "ifjo")
     if order != "ifjo":
         H = inp["W"].shape[0] // 4

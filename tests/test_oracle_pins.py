@@ -44,7 +44,10 @@ def loss(inp, fw):
 
 
 def run_loss(inp):
-    fw = oracle.fwd(inp["x"], inp["W"], inp.get("b"), inp.get("h0"), inp.get("c0"),
+    b = inp.get("b")
+    if inp.get("two_bias") and b is not None:
+        b = b[0] + b[1]  # the two biases of the PyTorch page enter as their sum
+    fw = oracle.fwd(inp["x"], inp["W"], b, inp.get("h0"), inp.get("c0"),
                     reverse=bool(inp.get("reverse", False)))
     return loss(inp, fw)
 
@@ -122,6 +125,15 @@ def test_reverse_direction_is_the_forward_on_flipped_time():
     # and it is not the forward direction on the unflipped inputs
     same = oracle.fwd_bwd(inp)
     assert np.max(np.abs(same["y"] - rev["y"])) > 1e-3
+
+
+def test_fd_two_biases():
+    """Finite differences with two biases b = [b_ih; b_hh]: each half of db
+    against the loss's change with its own bias."""
+    inp = full_inputs(3, 2, 3, 2, seed=53, scale_w=0.9)
+    inp["b"] = np.stack([inp["b"], np.linspace(-0.3, 0.4, inp["b"].size)])
+    inp["two_bias"] = True
+    fd_check(inp)
 
 
 def test_gate_order_relabelling():
