@@ -98,17 +98,23 @@ enum { LSTM_REVERSE = 1 };
  * same; only the row blocks are relabelled. */
 enum { LSTM_GATES_IJFO = 2 };
 
+/* Two biases (the b_ih, b_hh pair of the PyTorch LSTM page): with this flag
+ * b is [2][4H], the input-side bias then the hidden-side one, and the cell
+ * adds both; db, when given, is [2][4H] and receives the bias gradient in
+ * both halves (the two enter the pre-activation alike). */
+enum { LSTM_TWO_BIAS = 4 };
+
 /* Problem shape.  dtype is LSTM_F32 or LSTM_BF16; flags is 0 or an OR of
- * LSTM_REVERSE and LSTM_GATES_IJFO, other bits must be 0 (else
- * LSTM_ERR_DTYPE).  The forward call and the backward call of one record
- * take the same flags. */
+ * LSTM_REVERSE, LSTM_GATES_IJFO and LSTM_TWO_BIAS, other bits must be 0
+ * (else LSTM_ERR_DTYPE).  The forward call and the backward call of one
+ * record take the same flags. */
 typedef struct {
   int64_t T; /* time steps, >= 0 */
   int64_t B; /* batch, >= 0 */
   int64_t I; /* input size, >= 0 */
   int64_t H; /* hidden size, >= 1 */
   int32_t dtype;
-  int32_t flags; /* 0, LSTM_REVERSE, LSTM_GATES_IJFO or both */
+  int32_t flags; /* an OR of LSTM_REVERSE, LSTM_GATES_IJFO, LSTM_TWO_BIAS, or 0 */
 } lstm_shape;
 
 /* LSTM_ABI_VERSION of the library. */

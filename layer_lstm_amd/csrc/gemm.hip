@@ -203,10 +203,13 @@ __device__ __forceinline__ void store_row4(bf16_t* p, f32x4_t v) {
 __device__ __forceinline__ void store_row4(float* p, f32x4_t v) { *(f32x4_t*)p = v; }
 
 struct EpiP {  // fp32 P with bias in the interleaved column order
-  float* P; const void* bias; int64_t H, ldp; int dtype; int ijfo;
+  // (two: the bias is the sum of two [4H] vectors, bias[r] + bias[ldp + r])
+  float* P; const void* bias; int64_t H, ldp; int dtype; int ijfo; int two;
   __device__ __forceinline__ float bias_at(int64_t n) const {
     const int64_t r = gate_row(n, H, ijfo);
-    return dtype ? bf2f(((const bf16_t*)bias)[r]) : ((const float*)bias)[r];
+    float v = dtype ? bf2f(((const bf16_t*)bias)[r]) : ((const float*)bias)[r];
+    if (two) v += dtype ? bf2f(((const bf16_t*)bias)[ldp + r]) : ((const float*)bias)[ldp + r];
+    return v;
   }
   __device__ __forceinline__ void operator()(int64_t m, int64_t n, float v) const {
     if (bias) v += bias_at(n);
@@ -256,6 +259,7 @@ struct GemmArgs {
   int dsum_bf16;
   int64_t dsum_cols, dsum_H;
   int dsum_ijfo;      // gate-block order of dsum_out (gate_block)
+  int dsum_two;       // dsum_out is [2][dsum_cols]: the sums written to both halves
   int nxcd;           // XCDs of the device (1: no XCD-aware tile order)
   // persistent input projection (gemm_lds_multi_kernel) only:
   int tiles_x, tiles_y;  // output tiles along n and m
@@ -309,8 +313,11 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs<AOp, BOp, Epi> 
         float v = 0.f;
         for (int r = 0; r < g.dsum_rows; ++r) v += g.dsum[(int64_t)r * g.dsum_cols + n];
         const int64_t row = gate_row(n, g.dsum_H, g.dsum_ijfo);
-        if (g.dsum_bf16) ((bf16_t*)g.dsum_out)[row] = f2bf(v);
-        else ((float*)g.dsum_out)[row] = v;
+        for (int h = 0; h <= g.dsum_two; ++h) {
+          const int64_t o = row + h * g.dsum_cols;
+          if (g.dsum_bf16) ((bf16_t*)g.dsum_out)[o] = f2bf(v);
+          else ((float*)g.dsum_out)[o] = v;
+        }
       }
     }
     return;
@@ -638,8 +645,11 @@ __global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_kernel(GemmAr
         float v = 0.f;
         for (int r = 0; r < g.dsum_rows; ++r) v += g.dsum[(int64_t)r * g.dsum_cols + n];
         const int64_t row = gate_row(n, g.dsum_H, g.dsum_ijfo);
-        if (g.dsum_bf16) ((bf16_t*)g.dsum_out)[row] = f2bf(v);
-        else ((float*)g.dsum_out)[row] = v;
+        for (int h = 0; h <= g.dsum_two; ++h) {
+          const int64_t o = row + h * g.dsum_cols;
+          if (g.dsum_bf16) ((bf16_t*)g.dsum_out)[o] = f2bf(v);
+          else ((float*)g.dsum_out)[o] = v;
+        }
       }
     }
     return;
@@ -998,12 +1008,12 @@ static hipError_t launch_tile(GemmArgs<AOp, BOp, Epi>& g, hipStream_t s) {
 // Runs C = A . B through the epilogue; `part` must hold splits*M*N floats
 // when the shape splits K.  Optionally clears `zero_bytes` at `zero` in the
 // same launch (extra blocks), so that a buffer clear costs no launch.
-struct DbDuty { const float* src; void* out; int rows; int64_t cols, H; int bf16; int ijfo; };
+struct DbDuty { const float* src; void* out; int rows; int64_t cols, H; int bf16; int ijfo; int two; };
 
 template <typename T, class AOp, bool AMN, class BOp, bool BMN, class Epi>
 static hipError_t run_gemm(const Plan& p, int64_t M, int64_t N, int64_t K, const AOp& a, const BOp& b,
                            const Epi& e, float* part, void* zero, size_t zero_bytes, hipStream_t s,
-                           DbDuty db = DbDuty{nullptr, nullptr, 0, 0, 0, 0, 0}) {
+                           DbDuty db = DbDuty{nullptr, nullptr, 0, 0, 0, 0, 0, 0}) {
   if (M <= 0 || N <= 0) {
     if (zero_bytes) return launch_fill_zero(zero, zero_bytes, s);
     return hipSuccess;
@@ -1014,7 +1024,7 @@ static hipError_t run_gemm(const Plan& p, int64_t M, int64_t N, int64_t K, const
   int ktps = (int)((ktiles + gs.splits - 1) / gs.splits);
   if (ktps < 1) ktps = 1;
   GemmArgs<AOp, BOp, Epi> g{M, N, K, ktps, gs.splits, a, b, e, part, (uint32_t*)zero, (int64_t)(zero_bytes / 4),
-                            db.src, db.out, db.rows, db.bf16, db.cols, db.H, db.ijfo, p.nxcd};
+                            db.src, db.out, db.rows, db.bf16, db.cols, db.H, db.ijfo, db.two, p.nxcd};
   hipError_t err = gs.tile == 128 ? launch_tile<T, 4, 4, AOp, AMN, BOp, BMN, Epi>(g, s)
                                   : launch_tile<T, 2, 2, AOp, AMN, BOp, BMN, Epi>(g, s);
   if (err != hipSuccess || gs.splits == 1) return err;
@@ -1062,7 +1072,7 @@ static int multi_tiles_per_wg(const Plan& p, int64_t M, int64_t N, int64_t K) {
 template <typename T, int AMN, int BMN, class AOp, class BOp, class Epi>
 static hipError_t run_gemm_lds(const Plan& p, int64_t M, int64_t N, int64_t K, const AOp& a, const BOp& b,
                                const Epi& e, float* part, void* zero, size_t zero_bytes, hipStream_t s,
-                               DbDuty db = DbDuty{nullptr, nullptr, 0, 0, 0, 0, 0}) {
+                               DbDuty db = DbDuty{nullptr, nullptr, 0, 0, 0, 0, 0, 0}) {
   constexpr int TILE = LdsCfg<T>::kTile;
   const GemmShape gs = choose_shape_lds<T>(M, N, K, p.cus, part ? p.max_splits : 1);
   const int64_t ktiles = K / LdsCfg<T>::kKStage;
@@ -1070,7 +1080,7 @@ static hipError_t run_gemm_lds(const Plan& p, int64_t M, int64_t N, int64_t K, c
   if (ktps < 1) ktps = 1;
   const int64_t tx = (N + TILE - 1) / TILE, ty = (M + TILE - 1) / TILE;
   GemmArgs<AOp, BOp, Epi> g{M, N, K, ktps, gs.splits, a, b, e, part, (uint32_t*)zero, (int64_t)(zero_bytes / 4),
-                            db.src, db.out, db.rows, db.bf16, db.cols, db.H, db.ijfo, p.nxcd, (int)tx, (int)ty, 1};
+                            db.src, db.out, db.rows, db.bf16, db.cols, db.H, db.ijfo, db.two, p.nxcd, (int)tx, (int)ty, 1};
   if constexpr (AMN == 0 && BMN == 0) {
     const int per_wg = g.dsum_out ? 1 : multi_tiles_per_wg<T>(p, M, N, K);
     if (per_wg > 1) {
@@ -1105,7 +1115,7 @@ static hipError_t inproj_t(const Plan& p, const void* x, const void* W, const vo
   constexpr int VEC = 16 / sizeof(T);
   KRowsX<T> a{(const T*)x, p.I, p.TB, p.I, aligned16(x) && p.I % VEC == 0};
   KRowsWx<T> bw{(const T*)W, p.H, p.Z, p.G4, p.I, aligned16(W) && p.Z % VEC == 0 && p.H % VEC == 0, p.ijfo};
-  EpiP e{P, b, p.H, p.G4, p.dtype, p.ijfo};
+  EpiP e{P, b, p.H, p.G4, p.dtype, p.ijfo, p.two_bias};
   if (inproj_lds_ok<T>(p) && a.vec_ok && bw.vec_ok)
     return run_gemm_lds<T, 0, 0>(p, p.TB, p.G4, p.I, a, bw, e, part, zero, zero_bytes, s);
   return run_gemm<T, KRowsX<T>, false, KRowsWx<T>, false, EpiP>(p, p.TB, p.G4, p.I, a, bw, e, part, zero, zero_bytes, s);
@@ -1134,7 +1144,7 @@ static hipError_t dw_t(const Plan& p, const void* dG, const void* x, const void*
                 aligned16(x) && aligned16(y) && (h0 == nullptr || aligned16(h0)) && p.H % VEC == 0 && p.I % VEC == 0,
                 p.rev != 0};
   EpiDW<T> e{(T*)dW, p.H, p.Z, p.ijfo};
-  const DbDuty dd{DBP, db, p.nBG, p.G4, p.H, p.dtype, p.ijfo};
+  const DbDuty dd{DBP, db, p.nBG, p.G4, p.H, p.dtype, p.ijfo, p.two_bias};
   if (p.TB % LdsCfg<T>::kKStage == 0 && lds_depth_ok<T>(p.TB) && p.Z >= VEC && a.vec_ok && bz.vec_ok &&
       small_buf(p.TB * p.G4, p.esize) && small_buf(p.TB * p.Z, p.esize))
     return run_gemm_lds<T, 1, 1>(p, p.G4, p.Z, p.TB, a, bz, e, part, zero, zero_bytes, s, dd);

@@ -52,6 +52,7 @@ struct Plan {
   size_t off_hflags, off_pflags;
   int rev;          // 1: the reverse direction (steps from t = T-1 down to 0)
   int ijfo;         // 1: W, b, dW, db in the gate order i, g, f, o (gate_block)
+  int two_bias;     // 1: b and db are [2][4H] (b_ih, b_hh)
   int cus;          // compute units of the device
   int max_splits;   // largest split-K factor of the three products
   size_t off_gp;    // fp32 split-K partials of the products

@@ -262,7 +262,7 @@ const char* lstm_status_string(int status) {
 
 int lstm_query(const lstm_shape* shape, size_t* workspace_bytes) {
   if (!shape || !workspace_bytes) return LSTM_ERR_NULL;
-  if ((shape->flags & ~(LSTM_REVERSE | LSTM_GATES_IJFO)) != 0) return LSTM_ERR_DTYPE;
+  if ((shape->flags & ~(LSTM_REVERSE | LSTM_GATES_IJFO | LSTM_TWO_BIAS)) != 0) return LSTM_ERR_DTYPE;
   Plan p;
   const int rc = make_plan(shape->T, shape->B, shape->I, shape->H, shape->dtype, &p);
   if (rc != LSTM_OK) return rc;
@@ -272,7 +272,7 @@ int lstm_query(const lstm_shape* shape, size_t* workspace_bytes) {
 
 int lstm_query_plan(const lstm_shape* shape, lstm_plan_info* info) {
   if (!shape || !info) return LSTM_ERR_NULL;
-  if ((shape->flags & ~(LSTM_REVERSE | LSTM_GATES_IJFO)) != 0) return LSTM_ERR_DTYPE;
+  if ((shape->flags & ~(LSTM_REVERSE | LSTM_GATES_IJFO | LSTM_TWO_BIAS)) != 0) return LSTM_ERR_DTYPE;
   Plan p;
   const int rc = make_plan(shape->T, shape->B, shape->I, shape->H, shape->dtype, &p);
   if (rc != LSTM_OK) return rc;
@@ -294,12 +294,13 @@ int lstm_fwd_train(const lstm_shape* shape, const void* x, const void* W, const 
                    const void* c0, void* y, void* hT, void* cT, void* workspace, size_t workspace_bytes,
                    void* stream) {
   if (!shape) return LSTM_ERR_NULL;
-  if ((shape->flags & ~(LSTM_REVERSE | LSTM_GATES_IJFO)) != 0) return LSTM_ERR_DTYPE;
+  if ((shape->flags & ~(LSTM_REVERSE | LSTM_GATES_IJFO | LSTM_TWO_BIAS)) != 0) return LSTM_ERR_DTYPE;
   Plan p;
   int rc = make_plan(shape->T, shape->B, shape->I, shape->H, shape->dtype, &p);
   if (rc != LSTM_OK) return rc;
   p.rev = (shape->flags & LSTM_REVERSE) ? 1 : 0;
   p.ijfo = (shape->flags & LSTM_GATES_IJFO) ? 1 : 0;
+  p.two_bias = (shape->flags & LSTM_TWO_BIAS) ? 1 : 0;
   const int e = p.esize;
   if (!W || !workspace) return LSTM_ERR_NULL;
   if (p.TB * p.I > 0 && !x) return LSTM_ERR_NULL;
@@ -341,12 +342,13 @@ int lstm_bwd(const lstm_shape* shape, const void* dy, const void* dhT, const voi
              const void* W, const void* h0, const void* c0, const void* y, void* workspace, size_t workspace_bytes,
              void* dx, void* dW, void* db, void* dh0, void* dc0, void* stream) {
   if (!shape) return LSTM_ERR_NULL;
-  if ((shape->flags & ~(LSTM_REVERSE | LSTM_GATES_IJFO)) != 0) return LSTM_ERR_DTYPE;
+  if ((shape->flags & ~(LSTM_REVERSE | LSTM_GATES_IJFO | LSTM_TWO_BIAS)) != 0) return LSTM_ERR_DTYPE;
   Plan p;
   int rc = make_plan(shape->T, shape->B, shape->I, shape->H, shape->dtype, &p);
   if (rc != LSTM_OK) return rc;
   p.rev = (shape->flags & LSTM_REVERSE) ? 1 : 0;
   p.ijfo = (shape->flags & LSTM_GATES_IJFO) ? 1 : 0;
+  p.two_bias = (shape->flags & LSTM_TWO_BIAS) ? 1 : 0;
   const int e = p.esize;
   if (!W || !dW || !workspace) return LSTM_ERR_NULL;
   if (p.TB > 0 && (!dy || !y)) return LSTM_ERR_NULL;

@@ -24,6 +24,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 ABI_VERSION = 2
 REVERSE = 1  # lstm_shape.flags: the reverse direction of time
 GATES_IJFO = 2  # lstm_shape.flags: W/b/dW/db row blocks in the gate order i, g, f, o
+TWO_BIAS = 4  # lstm_shape.flags: b and db are [2][4H] (b_ih, b_hh)
 GATE_I, GATE_F, GATE_G, GATE_O = 0, 1, 2, 3
 F32, BF16 = 0, 1
 OK = 0
@@ -94,10 +95,10 @@ def torch_dtype(dtype: int):
     return torch.float32 if dtype == F32 else torch.bfloat16
 
 
-def make_shape(T, B, I, H, dtype, reverse=False, gate_order="ifjo") -> Shape:
+def make_shape(T, B, I, H, dtype, reverse=False, gate_order="ifjo", two_bias=False) -> Shape:
     if gate_order not in ("ifjo", "ijfo"):
         raise ValueError(f"gate_order {gate_order!r}: 'ifjo' or 'ijfo'")
-    flags = (REVERSE if reverse else 0) | (GATES_IJFO if gate_order == "ijfo" else 0)
+    flags = (REVERSE if reverse else 0) | (GATES_IJFO if gate_order == "ijfo" else 0) | (TWO_BIAS if two_bias else 0)
     return Shape(int(T), int(B), int(I), int(H), int(dtype), flags)
 
 
@@ -193,8 +194,8 @@ class Lstm:
     device.  ``forward``/``backward`` take device tensors and return device
     tensors; nothing is synchronised."""
 
-    def __init__(self, T, B, I, H, dtype=F32, device="cuda", reverse=False, gate_order="ifjo"):
-        self.shape = make_shape(T, B, I, H, dtype, reverse, gate_order)
+    def __init__(self, T, B, I, H, dtype=F32, device="cuda", reverse=False, gate_order="ifjo", two_bias=False):
+        self.shape = make_shape(T, B, I, H, dtype, reverse, gate_order, two_bias)
         self.T, self.B, self.I, self.H, self.dtype = T, B, I, H, dtype
         self.tdtype = torch_dtype(dtype)
         self.ws_bytes = query(self.shape)
@@ -205,7 +206,7 @@ class Lstm:
         self.cT = torch.empty((B, H), dtype=td, device=dev)
         self.dx = torch.empty((T, B, I), dtype=td, device=dev)
         self.dW = torch.empty((4 * H, H + I), dtype=td, device=dev)
-        self.db = torch.empty((4 * H,), dtype=td, device=dev)
+        self.db = torch.empty((2, 4 * H) if two_bias else (4 * H,), dtype=td, device=dev)
         self.dh0 = torch.empty((B, H), dtype=td, device=dev)
         self.dc0 = torch.empty((B, H), dtype=td, device=dev)
 

@@ -32,7 +32,7 @@ def run_gpu(inp, lstm, torch, want_db=True, stream=None):
     T, B, I, H, dt = inp["T"], inp["B"], inp["I"], inp["H"], inp["dtype"]
     code = lstm.F32 if dt == "f32" else lstm.BF16
     m = lstm.Lstm(T, B, I, H, code, reverse=bool(inp.get("reverse", False)),
-                  gate_order=inp.get("gate_order", "ifjo"))
+                  gate_order=inp.get("gate_order", "ifjo"), two_bias=bool(inp.get("two_bias", False)))
     d = {k: to_dev(inp.get(k), dt, torch) for k in ("x", "W", "b", "h0", "c0", "dy", "dhT", "dcT")}
     m.forward(d["x"], d["W"], d["b"], d["h0"], d["c0"], stream=stream)
     m.backward(d["dy"], d["dhT"], d["dcT"], d["x"], d["W"], d["h0"], d["c0"], want_db=want_db, stream=stream)

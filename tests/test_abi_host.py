@@ -45,6 +45,7 @@ def test_constants_match_header(lstm):
     assert header_enum("LSTM_F32") == lstm.F32 and header_enum("LSTM_BF16") == lstm.BF16
     assert header_enum("LSTM_REVERSE") == lstm.REVERSE
     assert header_enum("LSTM_GATES_IJFO") == lstm.GATES_IJFO
+    assert header_enum("LSTM_TWO_BIAS") == lstm.TWO_BIAS
     for code, name in lstm.STATUS.items():
         if code != 0:
             assert header_enum("LSTM_" + name) == code
@@ -89,7 +90,7 @@ def test_query_rejects_bad_dtype_and_nulls(lstm):
     assert lstm.lib().lstm_query_plan(ctypes.byref(lstm.make_shape(2, -1, 2, 2, 0)), ctypes.byref(info)) == -2
     assert info.grid == 0  # untouched on error
     s = lstm.make_shape(2, 2, 2, 2, 0)
-    s.flags = 4  # an unknown flag
+    s.flags = 8  # an unknown flag
     assert lstm.lib().lstm_query(ctypes.byref(s), ctypes.byref(n)) == -3
     assert lstm.lib().lstm_query_plan(ctypes.byref(s), ctypes.byref(info)) == -3
     assert lstm.lib().lstm_fwd_train(None, *([None] * 9), 0, None) == -1

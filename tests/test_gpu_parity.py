@@ -19,7 +19,9 @@ same stored values.
  * the reverse direction of time against the oracle through every kernel
    variant, and against the forward direction on time-flipped inputs;
  * the "ijfo" gate order against the oracle, and against the default order
-   on relabelled weights.
+   on relabelled weights;
+ * two biases (b_ih, b_hh) against the oracle, and against their sum as one
+   bias.
 """
 import numpy as np
 import pytest
@@ -390,6 +392,43 @@ def test_gate_order_is_a_relabelling_gpu(lstm, dt, T, B, I, H):
     for k in ("y", "hT", "cT", "dx", "dh0", "dc0"):
         assert np.array_equal(c[k], a[k]), k
     assert np.array_equal(c["dW"], a["dW"][rows]) and np.array_equal(c["db"], a["db"][rows])
+
+
+def two_bias_inputs(dt, T, B, I, H, seed):
+    inp = synth.make_inputs(T, B, I, H, dt, seed=seed, dist=ALL)
+    rng = np.random.default_rng(seed + 1)
+    b_hh = synth.round_to_storage(rng.uniform(-0.3, 0.3, 4 * H), dt)
+    return dict(inp, b=np.stack([inp["b"], b_hh]), two_bias=True)
+
+
+# Two biases (flags = LSTM_TWO_BIAS) through the register-staged, the
+# pipelined and the persistent input projection; once with every flag.
+@pytest.mark.parametrize("dt,T,B,I,H,rev,order", [
+    ("f32", 8, 4, 16, 32, False, "ifjo"),
+    ("f32", 64, 32, 256, 256, False, "ifjo"),
+    ("bf16", 4, 19, 40, 72, False, "ifjo"),
+    ("bf16", 3, 60, 32, 512, True, "ijfo"),
+])
+def test_two_biases(lstm, dt, T, B, I, H, rev, order):
+    say(f"case: two biases {dt} T={T} B={B} I={I} H={H} reverse={rev} order={order}")
+    inp = two_bias_inputs(dt, T, B, I, H, 59)
+    inp.update(reverse=rev, gate_order=order)
+    full_check(inp, lstm)
+
+
+def test_two_biases_are_their_sum_gpu(lstm):
+    """fp32: two biases give bit for bit what their fp32 sum gives as one
+    bias (the kernel adds them in fp32 before the product's sum), with db
+    in both halves.  The shape takes the persistent input projection."""
+    T, B, I, H = 16, 256, 1024, 512
+    say(f"case: two biases vs their sum f32 T={T} B={B} I={I} H={H}")
+    two = two_bias_inputs("f32", T, B, I, H, 61)
+    one = dict(two, two_bias=False, b=(two["b"][0].astype(np.float32) + two["b"][1].astype(np.float32)))
+    a, _, _ = run_gpu(two, lstm, torch)
+    c, _, _ = run_gpu(one, lstm, torch)
+    for k in ("y", "hT", "cT", "dx", "dW", "dh0", "dc0"):
+        assert np.array_equal(a[k], c[k]), k
+    assert np.array_equal(a["db"][0], c["db"]) and np.array_equal(a["db"][1], c["db"])
 
 
 def test_determinism(lstm):
