@@ -2,7 +2,7 @@
 """Benchmark of the single-layer LSTM forward + BPTT on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--reverse]
-                    [--gate-order ifjo|ijfo]
+                    [--gate-order ifjo|ijfo] [--two-bias]
 
 One step = lstm_fwd_train + lstm_bwd on one batch of seeded synthetic input
 (every kernel of the path: input projection, forward recurrence, backward
@@ -13,7 +13,9 @@ fraction of the MFMA peak of the storage type), a roofline record of the
 kernel that takes the most time, and the fp64 CPU oracle timed on the host
 on a bounded sample of the same workload.  --reverse runs the reverse
 direction of time (lstm_shape.flags = LSTM_REVERSE), --gate-order ijfo the
-other gate order of W's row blocks (LSTM_GATES_IJFO), on the same workload.
+other gate order of W's row blocks (LSTM_GATES_IJFO), --two-bias two bias
+vectors (LSTM_TWO_BIAS; the second one seeded like the first), on the same
+workload.
 """
 from __future__ import annotations
 
@@ -85,7 +87,7 @@ def copy_calibration(mib):
     print(json.dumps({"copy_bytes": n * 4, "launches": 3}), flush=True)
 
 
-def cpu_baseline(w, inp, budget_s, reverse=False, gate_order="ifjo"):
+def cpu_baseline(w, inp, budget_s, reverse=False, gate_order="ifjo", two_bias=False):
     """Time the fp64 oracle (as it stands) on a bounded sample of the same
     workload: whole sequences (batch rows), as many as fit in about
     `budget_s` seconds by a one-row probe; when the whole batch takes less,
@@ -93,7 +95,7 @@ def cpu_baseline(w, inp, budget_s, reverse=False, gate_order="ifjo"):
     from oracle import oracle
 
     def rows(n):
-        sub = dict(inp, B=n, reverse=reverse, gate_order=gate_order)
+        sub = dict(inp, B=n, reverse=reverse, gate_order=gate_order, two_bias=two_bias)
         for k in ("x", "dy"):
             sub[k] = inp[k][:, :n]
         for k in ("h0", "c0", "dhT", "dcT"):
@@ -126,6 +128,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--reverse", action="store_true", help="the reverse direction of time")
     ap.add_argument("--gate-order", default="ifjo", choices=("ifjo", "ijfo"), help="row-block order of W, b, dW, db")
+    ap.add_argument("--two-bias", action="store_true", help="two bias vectors (b_ih, b_hh)")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -146,6 +149,8 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     inp = synth.workload_inputs(w.name)
+    if args.two_bias:
+        inp["b"] = np.stack([inp["b"], inp["b"][::-1].copy()])
     code = lstm.F32 if w.dtype == "f32" else lstm.BF16
     td = torch.float32 if w.dtype == "f32" else torch.bfloat16
     dev = torch.device("cuda:0")
@@ -154,7 +159,7 @@ def main():
         return None if a is None else torch.from_numpy(np.asarray(a, dtype=np.float32)).to(dev).to(td)
 
     d = {k: put(inp[k]) for k in ("x", "W", "b", "h0", "c0", "dy", "dhT", "dcT")}
-    m = lstm.Lstm(w.T, w.B, w.I, w.H, code, reverse=args.reverse, gate_order=args.gate_order)
+    m = lstm.Lstm(w.T, w.B, w.I, w.H, code, reverse=args.reverse, gate_order=args.gate_order, two_bias=args.two_bias)
 
     def step():
         m.forward(d["x"], d["W"], d["b"], d["h0"], d["c0"])
@@ -210,8 +215,9 @@ def main():
         peak, runit = HBM_GBS, "GB/s"
     roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": runit,
                 "frac": round(achieved / peak, 5),
-                # (the counter runs are of the forward direction, default gate order)
-                "traffic": None if (args.reverse or args.gate_order != "ifjo") else traffic_for(w.name, dom),
+                # (the counter runs are of the forward direction, default gate order, one bias)
+                "traffic": None if (args.reverse or args.gate_order != "ifjo" or args.two_bias)
+                else traffic_for(w.name, dom),
                 "kernel": dom, "avg_launch_us": round(avg_s * 1e6, 2)}
 
     flops = w.flops
@@ -224,6 +230,7 @@ def main():
         "data": "synthetic (seeded; see layer_lstm_amd/synth.py)",
         "config": {"workload": w.name, "T": w.T, "B": w.B, "I": w.I, "H": w.H, "storage": w.dtype,
                    "direction": "reverse" if args.reverse else "forward", "gate_order": args.gate_order,
+                   "biases": 2 if args.two_bias else 1,
                    "parallelism": "single GPU"},
         "effective_tflops": round(eff_tflops, 3),
         "fraction_of_peak": round(eff_tflops / PEAK_TFLOPS[w.dtype], 5),
@@ -233,7 +240,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
-        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, args.reverse, args.gate_order)
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, args.reverse, args.gate_order, args.two_bias)
     print(json.dumps(out), flush=True)
 
 
