@@ -98,7 +98,7 @@ enum { LSTM_REVERSE = 1 };
  * same; only the row blocks are relabelled. */
 enum { LSTM_GATES_IJFO = 2 };
 
-/* Two biases (the b_ih, b_hh pair of the PyTorch LSTM page): with this flag
+/* Two biases (bias_ih and bias_hh of the LSTMCell of the CMU 10-414 HW4 page): with this flag
  * b is [2][4H], the input-side bias then the hidden-side one, and the cell
  * adds both; db, when given, is [2][4H] and receives the bias gradient in
  * both halves (the two enter the pre-activation alike). */

@@ -169,8 +169,9 @@ def fwd_bwd(inp: dict) -> dict:
     own order, or "ijfo": W, b, dW and db with their row blocks relabelled)
     and two_bias (b and db [2][4H])."""
     if inp.get("two_bias"):
-        # b = [b_ih; b_hh] enter the pre-activation as their sum (the PyTorch
-        # LSTM page's two biases); both receive the one bias gradient
+        # b = [b_ih; b_hh] enter the pre-activation as their sum (bias_ih and
+        # bias_hh of the CMU 10-414 HW4 page's LSTMCell); both receive the one
+        # bias gradient
         b2 = inp["b"]
         out = fwd_bwd(dict(inp, two_bias=False, b=None if b2 is None else b2[0] + b2[1]))
         out["db"] = np.stack([out["db"], out["db"]])

@@ -46,7 +46,7 @@ def loss(inp, fw):
 def run_loss(inp):
     b = inp.get("b")
     if inp.get("two_bias") and b is not None:
-        b = b[0] + b[1]  # the two biases of the PyTorch page enter as their sum
+        b = b[0] + b[1]  # bias_ih + bias_hh of the CMU page's LSTMCell, entering as their sum
     fw = oracle.fwd(inp["x"], inp["W"], b, inp.get("h0"), inp.get("c0"),
                     reverse=bool(inp.get("reverse", False)))
     return loss(inp, fw)
