@@ -21,7 +21,8 @@ same stored values.
  * the "ijfo" gate order against the oracle, and against the default order
    on relabelled weights;
  * two biases (b_ih, b_hh) against the oracle, and against their sum as one
-   bias.
+   bias;
+ * every flag at once at full size (T=128 B=64 I=512 H=1024), sampled rows.
 """
 import numpy as np
 import pytest
@@ -429,6 +430,28 @@ def test_two_biases_are_their_sum_gpu(lstm):
     for k in ("y", "hT", "cT", "dx", "dW", "dh0", "dc0"):
         assert np.array_equal(a[k], c[k]), k
     assert np.array_equal(a["db"][0], c["db"]) and np.array_equal(a["db"][1], c["db"])
+
+
+def test_all_flags_full_size_sampled_rows(lstm):
+    """bf16_T128_B64_I512_H1024 at full size, in the benchmark's launch
+    configuration, with every flag: the reverse direction, the "ijfo" gate
+    order and two biases.  Sampled batch rows of every per-row output
+    against the oracle on those rows."""
+    name = "bf16_T128_B64_I512_H1024"
+    w = synth.WORKLOADS[name]
+    say("case: full size, all flags", name)
+    inp = synth.workload_inputs(name)
+    rng = np.random.default_rng(67)
+    b_hh = synth.round_to_storage(rng.uniform(-0.03, 0.03, 4 * w.H), "bf16")
+    inp = dict(inp, b=np.stack([inp["b"], b_hh]), two_bias=True, reverse=True, gate_order="ijfo")
+    out, _, _ = run_gpu(inp, lstm, torch)
+    rows = [1, 40]
+    ref = oracle.fwd_bwd(rows_of(inp, rows))
+    got = dict(y=out["y"][:, rows], hT=out["hT"][rows], cT=out["cT"][rows], dx=out["dx"][:, rows],
+               dh0=out["dh0"][rows], dc0=out["dc0"][rows])
+    errs, bad = compare(got, ref, "bf16", keys=tuple(got))
+    say("rel-L2:", {k: f"{v:.2e}" for k, v in errs.items()})
+    assert not bad, bad
 
 
 def test_determinism(lstm):
