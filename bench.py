@@ -4,6 +4,9 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--reverse]
                     [--gate-order ifjo|ijfo] [--two-bias]
 
+The default workload is the largest one that fits one GPU,
+bf16_T256_B256_I1024_H1024 (T=256, B=256, I=1024, H=1024, bf16 storage with
+fp32 accumulation); --workload picks another of layer_lstm_amd/synth.py.
 One step = lstm_fwd_train + lstm_bwd on one batch of seeded synthetic input
 (every kernel of the path: input projection, forward recurrence, backward
 recurrence, dW, dx, db).  Inputs, weights and outputs are resident in HBM
@@ -87,6 +90,17 @@ def copy_calibration(mib):
     print(json.dumps({"copy_bytes": n * 4, "launches": 3}), flush=True)
 
 
+def cpu_model():
+    """Model name of the host CPU (/proc/cpuinfo), or None."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, inp, budget_s, reverse=False, gate_order="ifjo", two_bias=False):
     """Time the fp64 oracle (as it stands) on a bounded sample of the same
     workload: whole sequences (batch rows), as many as fit in about
@@ -114,6 +128,8 @@ def cpu_baseline(w, inp, budget_s, reverse=False, gate_order="ifjo", two_bias=Fa
         passes += 1
         dt = time.perf_counter() - t0
     return {"value": passes * n / dt, "unit": "sequences/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(), "logical_cpus": os.cpu_count(),
+            "gflops": round(passes * n * w.flops / w.B / dt / 1e9, 3),
             "sample": f"{passes} x {n} of {w.B} sequences (batch rows) of {w.name}, fwd+bwd in fp64, "
                       f"{dt:.2f} s wall"}
 
@@ -220,6 +236,19 @@ def main():
                 else traffic_for(w.name, dom),
                 "kernel": dom, "avg_launch_us": round(avg_s * 1e6, 2)}
 
+    # each batched product against the MFMA peak of the storage type: its
+    # algorithmic FLOPs per launch over its average launch time (the dW
+    # launch includes its split-K sum and the db sum)
+    gemm_frac = {}
+    for kind in ("input_projection", "dW_product", "dx_product"):
+        tot_k, n_k = kt.get(kind, (0.0, 0))
+        if n_k:
+            fl = kernel_work(w, kind, plan)[0]
+            gemm_frac[kind] = {"us": round(tot_k / n_k * 1e3, 2),
+                               "frac": round(fl / (tot_k / n_k / 1e3) / 1e12 / PEAK_TFLOPS[w.dtype], 4)}
+    rec_us = {k: round(kt[k][0] / kt[k][1] * 1e3, 2) for k in ("forward_recurrence", "backward_recurrence")
+              if kt.get(k, (0, 0))[1]}
+
     flops = w.flops
     value = w.B / (ms / 1e3)
     eff_tflops = flops / (ms / 1e3) / 1e12
@@ -235,6 +264,8 @@ def main():
         "effective_tflops": round(eff_tflops, 3),
         "fraction_of_peak": round(eff_tflops / PEAK_TFLOPS[w.dtype], 5),
         "roofline": roofline,
+        "gemm_fraction_of_peak": gemm_frac,
+        "recurrence_us": rec_us,
         "recurrence_plan": plan,
         "cpu_baseline": None,
     }
