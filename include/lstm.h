@@ -36,7 +36,12 @@
  * after a call returns, and launches asynchronously on the given stream
  * (a hipStream_t passed as void*; NULL = the default stream) without any
  * host synchronisation.  Buffers must stay alive until the stream has
- * drained.  Outputs are overwritten, never accumulated into.
+ * drained.  Outputs are overwritten, never accumulated into.  Calls may be
+ * issued on several streams: the persistent recurrent kernels (each holds
+ * every compute unit it uses until its last step) of one device are
+ * ordered by the library -- a launch on another stream than the previous
+ * one first waits for that one -- so two of them never compete for the
+ * compute units; the other kernels overlap freely.
  *
  * Workspace: opaque device memory of lstm_query() bytes, 256-byte aligned.
  * lstm_fwd_train() writes the forward record into it (activated gates and

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "internal.hpp"
@@ -161,6 +162,39 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
   p->off_dbp = off; off += align256((size_t)p->nBG * p->G4 * 4);
   p->total = off;
   return LSTM_OK;
+}
+
+// ---- order of the persistent launches (recurrent_common.hpp) ----
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_persist_mu;
+hipEvent_t g_persist_ev[kMaxDevices];
+hipStream_t g_persist_stream[kMaxDevices];
+bool g_persist_used[kMaxDevices];
+}  // namespace
+
+hipError_t persistent_before(hipStream_t s) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_persist_mu);
+  if (g_persist_used[dev] && g_persist_stream[dev] != s) return hipStreamWaitEvent(s, g_persist_ev[dev], 0);
+  return hipSuccess;
+}
+
+hipError_t persistent_after(hipStream_t s) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_persist_mu);
+  if (!g_persist_ev[dev] && (e = hipEventCreateWithFlags(&g_persist_ev[dev], hipEventDisableTiming)) != hipSuccess)
+    return e;
+  if ((e = hipEventRecord(g_persist_ev[dev], s)) != hipSuccess) return e;
+  g_persist_stream[dev] = s;
+  g_persist_used[dev] = true;
+  return hipSuccess;
 }
 
 static int status_of(hipError_t e) {
@@ -366,7 +400,8 @@ int lstm_bwd(const lstm_shape* shape, const void* dy, const void* dhT, const voi
   if (p.T == 0 || p.B == 0) {
     Timed tm(6, s);
     err = launch_fill_zero(dW, (size_t)(p.G4 * p.Z) * e, s);
-    if (err == hipSuccess && db) err = launch_fill_zero(db, (size_t)p.G4 * e, s);
+    // db is [2][4H] with two biases: both halves are outputs
+    if (err == hipSuccess && db) err = launch_fill_zero(db, (size_t)(p.two_bias ? 2 : 1) * p.G4 * e, s);
     if (err == hipSuccess && p.B > 0) err = launch_copy_state(dhT, dh0, (size_t)(p.B * p.H), e, s);
     if (err == hipSuccess && p.B > 0) err = launch_copy_state(dcT, dc0, (size_t)(p.B * p.H), e, s);
     return status_of(err);

@@ -234,6 +234,15 @@ __device__ __forceinline__ float ldf(const void* p, int64_t i) {
   return Elem<T>::to_f(((const T*)p)[i]);
 }
 
+// Persistent launches of one device run one at a time, whatever stream the
+// caller gives: two such grids resident together could each hold part of
+// the CUs that the other's waiting work-groups need.  persistent_before(s)
+// makes stream s wait for the last persistent launch of the current device
+// when that was on another stream; persistent_after(s) records its end
+// (one event per device, kept for the life of the process).
+hipError_t persistent_before(hipStream_t s);
+hipError_t persistent_after(hipStream_t s);
+
 // The persistent kernels need every work-group of the grid resident at
 // once.  The grid never exceeds the CU count and each work-group fits a CU
 // on its own; the occupancy query confirms that the device can hold the
@@ -257,7 +266,9 @@ inline hipError_t coop_launch(K kernel, int grid, size_t lds, void* arg, hipStre
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
   if (per_cu < 1 || (int64_t)per_cu * cus < grid) return hipErrorCooperativeLaunchTooLarge;
-  return hipLaunchKernel((const void*)kernel, dim3(grid), dim3(threads), args, lds, s);
+  if ((e = persistent_before(s)) != hipSuccess) return e;
+  if ((e = hipLaunchKernel((const void*)kernel, dim3(grid), dim3(threads), args, lds, s)) != hipSuccess) return e;
+  return persistent_after(s);
 }
 
 // v of another lane of the quad (DPP quad_perm control CTRL).
