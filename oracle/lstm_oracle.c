@@ -55,9 +55,10 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* n > 0: that many OpenMP threads; n <= 0: one per available processor */
 void oracle_set_threads(int n) {
 #ifdef _OPENMP
-  if (n > 0) omp_set_num_threads(n);
+  omp_set_num_threads(n > 0 ? n : omp_get_num_procs());
 #else
   (void)n;
 #endif

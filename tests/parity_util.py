@@ -27,12 +27,17 @@ def to_host(t):
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def run_gpu(inp, lstm, torch, want_db=True, stream=None):
-    """Forward + backward on the GPU; returns fp64 host copies of the 8 outputs."""
+def run_gpu(inp, lstm, torch, want_db=True, stream=None, poison=False):
+    """Forward + backward on the GPU; returns fp64 host copies of the 8
+    outputs.  poison: fill every output buffer with NaN first, so that an
+    output the library fails to write shows up."""
     T, B, I, H, dt = inp["T"], inp["B"], inp["I"], inp["H"], inp["dtype"]
     code = lstm.F32 if dt == "f32" else lstm.BF16
     m = lstm.Lstm(T, B, I, H, code, reverse=bool(inp.get("reverse", False)),
                   gate_order=inp.get("gate_order", "ifjo"), two_bias=bool(inp.get("two_bias", False)))
+    if poison:
+        for k in OUTPUTS:
+            getattr(m, k).fill_(float("nan"))
     d = {k: to_dev(inp.get(k), dt, torch) for k in ("x", "W", "b", "h0", "c0", "dy", "dhT", "dcT")}
     m.forward(d["x"], d["W"], d["b"], d["h0"], d["c0"], stream=stream)
     m.backward(d["dy"], d["dhT"], d["dcT"], d["x"], d["W"], d["h0"], d["c0"], want_db=want_db, stream=stream)
@@ -48,3 +53,45 @@ def compare(out, ref, dtype, keys=OUTPUTS, tol=None):
     errs = {k: rel_l2(out[k], ref[k]) for k in keys}
     bad = {k: v for k, v in errs.items() if not (v <= tol)}
     return errs, bad
+
+
+def row_errors(got, ref, row_dims):
+    """Per-row relative error: rows are the slices over the trailing
+    dimensions after the first `row_dims` (a (t, b) row of y or dx, a batch
+    row of hT, a gate row of dW; row_dims = 0: one value per row).  Each
+    row's L2 error is divided by the larger of its own L2 norm and the RMS
+    row norm of the reference, so that a row whose reference is small is
+    not held to a relative bound it cannot meet, while a corrupted or stale
+    row (an error as large as a typical row) stands out.  Returns the array
+    of ratios."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if row_dims == 0:
+        got, ref = got.reshape(-1, 1), ref.reshape(-1, 1)
+    else:
+        n = int(np.prod(ref.shape[:row_dims]))
+        got, ref = got.reshape(n, -1), ref.reshape(n, -1)
+    err = np.linalg.norm(got - ref, axis=1)
+    nrm = np.linalg.norm(ref, axis=1)
+    rms = np.sqrt(np.mean(nrm * nrm)) if nrm.size else 0.0
+    den = np.maximum(nrm, rms)
+    return np.where(den > 0, err / np.where(den > 0, den, 1.0), err)
+
+
+# rows of each output: (t, b) rows of y and dx, batch rows of the [B, H]
+# states, gate rows of dW, single values of db
+ROW_DIMS = dict(y=2, dx=2, hT=1, cT=1, dh0=1, dc0=1, dW=1, db=0)
+
+
+def compare_rows(out, ref, tol, keys=OUTPUTS):
+    """Worst per-row error of each output (row_errors) and the outputs over
+    `tol`."""
+    worst = {}
+    for k in keys:
+        rd = ROW_DIMS[k]
+        if k == "db" and np.ndim(ref[k]) == 2:  # two biases: [2][4H]
+            rd = 0
+        r = row_errors(out[k], ref[k], rd)
+        worst[k] = float(r.max()) if r.size else 0.0
+    bad = {k: v for k, v in worst.items() if not (v <= tol)}
+    return worst, bad

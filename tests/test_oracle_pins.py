@@ -87,9 +87,10 @@ def fd_check(inp, eps_rel=1e-6, tol=1e-7):
 
 @pytest.fixture(autouse=True, scope="module")
 def _single_thread():
+    prev = oracle.num_threads()
     oracle.set_threads(1)
     yield
-    oracle.set_threads(0)
+    oracle.set_threads(prev)
 
 
 @pytest.mark.parametrize("T", [1, 2, 3])
@@ -326,19 +327,18 @@ def test_empty_sequence():
     assert np.all(out["dW"] == 0) and np.all(out["db"] == 0) and out["dx"].size == 0
 
 
-@pytest.mark.parametrize("T,B,I,H", [(5, 3, 4, 6), (8, 4, 16, 32), (3, 1, 1, 1)])
-def test_against_torch_nn_lstm_fp64(T, B, I, H):
-    """Independent library implementation: torch.nn.LSTM on the CPU in fp64
-    with weight_hh = W[:, :H], weight_ih = W[:, H:], bias_ih = b,
-    bias_hh = 0; gradients by autograd of the same scalar loss."""
+def torch_lstm_reference(inp, b_ih, b_hh):
+    """torch.nn.LSTM (CPU, fp64) with weight_hh = W[:, :H], weight_ih =
+    W[:, H:] and the given biases; outputs and autograd gradients of the
+    loss L = sum_t <dy_t, h_t> + <dhT, h_{T-1}> + <dcT, c_{T-1}>."""
     torch = pytest.importorskip("torch")
-    inp = full_inputs(T, B, I, H, seed=16)
+    T, B, I, H = inp["T"], inp["B"], inp["I"], inp["H"]
     m = torch.nn.LSTM(I, H, num_layers=1, bias=True, batch_first=False).double()
     with torch.no_grad():
         m.weight_hh_l0.copy_(torch.from_numpy(inp["W"][:, :H]))
         m.weight_ih_l0.copy_(torch.from_numpy(inp["W"][:, H:]))
-        m.bias_ih_l0.copy_(torch.from_numpy(inp["b"]))
-        m.bias_hh_l0.zero_()
+        m.bias_ih_l0.copy_(torch.from_numpy(b_ih))
+        m.bias_hh_l0.copy_(torch.from_numpy(b_hh))
     x = torch.from_numpy(inp["x"]).requires_grad_(True)
     h0 = torch.from_numpy(inp["h0"])[None].clone().requires_grad_(True)
     c0 = torch.from_numpy(inp["c0"])[None].clone().requires_grad_(True)
@@ -346,10 +346,37 @@ def test_against_torch_nn_lstm_fp64(T, B, I, H):
     L = (y * torch.from_numpy(inp["dy"])).sum() + (hn[0] * torch.from_numpy(inp["dhT"])).sum() \
         + (cn[0] * torch.from_numpy(inp["dcT"])).sum()
     L.backward()
-    ref = dict(y=y.detach().numpy(), hT=hn[0].detach().numpy(), cT=cn[0].detach().numpy(),
-               dx=x.grad.numpy(), dh0=h0.grad[0].numpy(), dc0=c0.grad[0].numpy(),
-               dW=np.concatenate([m.weight_hh_l0.grad.numpy(), m.weight_ih_l0.grad.numpy()], axis=1),
-               db=m.bias_ih_l0.grad.numpy())
+    return dict(y=y.detach().numpy(), hT=hn[0].detach().numpy(), cT=cn[0].detach().numpy(),
+                dx=x.grad.numpy(), dh0=h0.grad[0].numpy(), dc0=c0.grad[0].numpy(),
+                dW=np.concatenate([m.weight_hh_l0.grad.numpy(), m.weight_ih_l0.grad.numpy()], axis=1),
+                db_ih=m.bias_ih_l0.grad.numpy(), db_hh=m.bias_hh_l0.grad.numpy())
+
+
+@pytest.mark.parametrize("T,B,I,H", [(5, 3, 4, 6), (8, 4, 16, 32), (3, 1, 1, 1)])
+def test_against_torch_nn_lstm_fp64(T, B, I, H):
+    """Independent library implementation: torch.nn.LSTM on the CPU in fp64
+    with weight_hh = W[:, :H], weight_ih = W[:, H:], bias_ih = b,
+    bias_hh = 0; gradients by autograd of the same scalar loss."""
+    inp = full_inputs(T, B, I, H, seed=16)
+    ref = torch_lstm_reference(inp, inp["b"], np.zeros_like(inp["b"]))
+    ref["db"] = ref.pop("db_ih")
+    ref.pop("db_hh")
     out = oracle.fwd_bwd(inp)
     for k, v in ref.items():
         np.testing.assert_allclose(out[k], v, rtol=1e-11, atol=1e-13, err_msg=k)
+
+
+@pytest.mark.parametrize("T,B,I,H", [(5, 3, 4, 6), (6, 2, 7, 5)])
+def test_two_biases_against_torch_nn_lstm_fp64(T, B, I, H):
+    """The two-bias path (b = [b_ih; b_hh], both nonzero) against
+    torch.nn.LSTM's bias_ih_l0 / bias_hh_l0: every output, and db[0], db[1]
+    against the two bias gradients autograd returns."""
+    inp = full_inputs(T, B, I, H, seed=17)
+    rng = np.random.default_rng(171)
+    b_hh = synth.round_to_storage(rng.uniform(-0.4, 0.4, 4 * H), "f32")
+    ref = torch_lstm_reference(inp, inp["b"], b_hh)
+    out = oracle.fwd_bwd(dict(inp, b=np.stack([inp["b"], b_hh]), two_bias=True))
+    for k in ("y", "hT", "cT", "dx", "dh0", "dc0", "dW"):
+        np.testing.assert_allclose(out[k], ref[k], rtol=1e-11, atol=1e-13, err_msg=k)
+    np.testing.assert_allclose(out["db"][0], ref["db_ih"], rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(out["db"][1], ref["db_hh"], rtol=1e-11, atol=1e-13)
