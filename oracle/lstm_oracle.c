@@ -71,6 +71,14 @@ void oracle_set_threads(int n) {
  *            the step at time t reads the state of time t+1 and h0/c0 enter
  *            at t = T-1; hT/cT are the state after the step at t = 0.
  *   x  [T,B,I], W [4H,H+I], b [4H] or NULL, h0/c0 [B,H] or NULL (zero state)
+ *   mask [T,B,H] or NULL (all ones): the seq_length input of the parameter
+ *            table ("参数说明"), a mask matrix standing for the actual length
+ *            of each sequence.  Reading: the step's new cell and hidden
+ *            values are blended with the state it read, element by element,
+ *            c_t = m*c_new + (1-m)*c_{t-1} and h_t = m*h_new + (1-m)*h_{t-1},
+ *            so that a step with m = 0 leaves the state as it was (padding
+ *            past a sequence's end changes neither state nor gradient) and
+ *            m = 1 is the plain cell; y_t is the state h_t
  *   y  [T,B,H]      h_t for every step (the layer output)
  *   hT, cT [B,H]    state after the last step (may be NULL)
  *   gates [T,B,4H]  activated gates i,f,g,o per step (kept for the backward;
@@ -80,7 +88,7 @@ void oracle_set_threads(int n) {
  */
 int oracle_lstm_fwd(long T, long B, long I, long H, int reverse,
                     const double* x, const double* W, const double* b,
-                    const double* h0, const double* c0,
+                    const double* h0, const double* c0, const double* mask,
                     double* y, double* hT, double* cT,
                     double* gates, double* cell) {
   if (T < 0 || B < 0 || I < 0 || H <= 0) return -1;
@@ -114,9 +122,12 @@ int oracle_lstm_fwd(long T, long B, long I, long H, int reverse,
         const double fg = sigm(ab[H + j]);      /* forget gate     */
         const double gg = tanh(ab[2 * H + j]);  /* candidate state */
         const double og = sigm(ab[3 * H + j]);  /* output gate     */
-        const double c = fg * cp[bb * H + j] + ig * gg;
-        const double h = og * tanh(c);
         const long o = t * B + bb;
+        const double m = mask ? mask[o * H + j] : 1.0;
+        const double cn = fg * cp[bb * H + j] + ig * gg; /* new cell value     */
+        const double hn = og * tanh(cn);                 /* new hidden value   */
+        const double c = m * cn + (1.0 - m) * cp[bb * H + j];
+        const double h = m * hn + (1.0 - m) * hp[bb * H + j];
         if (gates) {
           gates[o * G4 + j] = ig;
           gates[o * G4 + H + j] = fg;
@@ -140,7 +151,8 @@ int oracle_lstm_fwd(long T, long B, long I, long H, int reverse,
  * Backward pass ("反向传播算法" steps 1-6) from the stored forward values.
  *   reverse as in the forward (the recursion then runs from t = 0 up to T-1:
  *   the reverse of the forward's step order, whichever the direction);
- *   x, W, h0, c0 as in the forward; y, gates, cell as the forward wrote them;
+ *   x, W, h0, c0, mask as in the forward; y, gates, cell as the forward
+ *   wrote them;
  *   dy [T,B,H]; dhT, dcT [B,H] or NULL (zero).
  * Outputs (overwritten, never accumulated into):
  *   dx [T,B,I], dW [4H,H+I], db [4H] (may be NULL), dh0, dc0 [B,H]
@@ -154,10 +166,22 @@ int oracle_lstm_fwd(long T, long B, long I, long H, int reverse,
  * meaning: the forget factor enters once, so the carry delta-c_prev (which
  * already holds the factor) is added as it is.  The carries start from the
  * given final-state gradients: delta-h = dhT, delta-c = dcT.
+ *
+ * Mask (the blend of the forward): with m the step's mask value, the new
+ * hidden and cell values receive m times the step's gradients, and the
+ * state the step read receives the other (1-m) part directly --
+ *   delta-h_new = m.delta-h,  delta-c_new = m.delta-c + delta-h_new.o.(1-tanh^2 c_new),
+ *   carries: delta-c_prev = (1-m).delta-c + delta-c_new.f,
+ *            delta-h_prev = (1-m).delta-h + (W^T delta-gates)[0,H);
+ * the gate deltas are those of steps 2-3 with delta-h_new, delta-c_new in
+ * place of delta-h, delta-c.  c_new = f.c_{t-1} + i.g is formed again from
+ * the stored gates and the stored cell state of the previous step (the same
+ * expression on the same values as in the forward).  With m = 1 this is the
+ * page's recursion unchanged.
  */
 int oracle_lstm_bwd(long T, long B, long I, long H, int reverse,
                     const double* x, const double* W,
-                    const double* h0, const double* c0,
+                    const double* h0, const double* c0, const double* mask,
                     const double* y, const double* gates, const double* cell,
                     const double* dy, const double* dhT, const double* dcT,
                     double* dx, double* dW, double* db,
@@ -167,14 +191,15 @@ int oracle_lstm_bwd(long T, long B, long I, long H, int reverse,
   const long Z = H + I, G4 = 4 * H;
   double* dhc = (double*)calloc((size_t)(B * H) + 1, sizeof(double)); /* delta-h carry */
   double* dcc = (double*)calloc((size_t)(B * H) + 1, sizeof(double)); /* delta-c carry */
+  double* dhp = (double*)calloc((size_t)(B * H) + 1, sizeof(double)); /* (1-m).delta-h of the step */
   double* dG = dgates;
   int own_dG = 0;
   if (!dG) {
     dG = (double*)malloc(((size_t)(T * B * G4) + 1) * sizeof(double));
     own_dG = 1;
   }
-  if (!dhc || !dcc || !dG) {
-    free(dhc); free(dcc); if (own_dG) free(dG);
+  if (!dhc || !dcc || !dhp || !dG) {
+    free(dhc); free(dcc); free(dhp); if (own_dG) free(dG);
     return -1;
   }
   if (dhT) memcpy(dhc, dhT, (size_t)(B * H) * sizeof(double));
@@ -193,10 +218,13 @@ int oracle_lstm_bwd(long T, long B, long I, long H, int reverse,
         const double c = cell[o * H + j];
         double cprev = t > 0 ? cell[(o - B) * H + j] : (c0 ? c0[bb * H + j] : 0.0);
         if (reverse) cprev = t < T - 1 ? cell[(o + B) * H + j] : (c0 ? c0[bb * H + j] : 0.0);
-        const double tc = tanh(c);
+        const double m = mask ? mask[o * H + j] : 1.0;
+        const double cn = mask ? fg * cprev + ig * gg : c;             /* the step's new cell value */
+        const double tc = tanh(cn);
         const double dh = dy[o * H + j] + dhc[bb * H + j];             /* step 1 */
-        const double dc = dh * og * (1.0 - tc * tc) + dcc[bb * H + j]; /* step 2 */
-        const double d_o = dh * tc * og * (1.0 - og);                  /* step 3 */
+        const double dhn = m * dh;
+        const double dc = dhn * og * (1.0 - tc * tc) + m * dcc[bb * H + j]; /* step 2 */
+        const double d_o = dhn * tc * og * (1.0 - og);                 /* step 3 */
         const double d_g = dc * ig * (1.0 - gg * gg);
         const double d_i = dc * gg * ig * (1.0 - ig);
         const double d_f = dc * cprev * fg * (1.0 - fg);
@@ -205,7 +233,8 @@ int oracle_lstm_bwd(long T, long B, long I, long H, int reverse,
         dG[o * G4 + 2 * H + j] = d_g;
         dG[o * G4 + 3 * H + j] = d_o;
         if (dcell) dcell[o * H + j] = dc;
-        dcc[bb * H + j] = dc * fg;                                     /* step 5: delta-c_prev */
+        dcc[bb * H + j] = (1.0 - m) * dcc[bb * H + j] + dc * fg;       /* step 5: delta-c_prev */
+        dhp[bb * H + j] = (1.0 - m) * dh;                              /* the state's own part */
       }
     }
     /* step 5: delta-z = W^T delta-gates; the first H entries go to the
@@ -216,7 +245,7 @@ int oracle_lstm_bwd(long T, long B, long I, long H, int reverse,
       const double* g = dG + (t * B + bb) * G4;
       double s = 0.0;
       for (long r = 0; r < G4; ++r) s += W[r * Z + k] * g[r];
-      if (k < H) dhc[bb * H + k] = s;           /* step 6: delta-h_next */
+      if (k < H) dhc[bb * H + k] = dhp[bb * H + k] + s; /* step 6: delta-h_next */
       else dx[(t * B + bb) * I + (k - H)] = s;
     }
   }
@@ -244,7 +273,7 @@ int oracle_lstm_bwd(long T, long B, long I, long H, int reverse,
 
   if (dh0) memcpy(dh0, dhc, (size_t)(B * H) * sizeof(double));
   if (dc0) memcpy(dc0, dcc, (size_t)(B * H) * sizeof(double));
-  free(dhc); free(dcc);
+  free(dhc); free(dcc); free(dhp);
   if (own_dG) free(dG);
   return 0;
 }

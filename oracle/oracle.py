@@ -37,9 +37,9 @@ def build(force: bool = False) -> str:
 def _bind(path):
     lib = ctypes.CDLL(path)
     L, P = ctypes.c_long, ctypes.c_void_p
-    lib.oracle_lstm_fwd.argtypes = [L, L, L, L, ctypes.c_int] + [P] * 9
+    lib.oracle_lstm_fwd.argtypes = [L, L, L, L, ctypes.c_int] + [P] * 10
     lib.oracle_lstm_fwd.restype = ctypes.c_int
-    lib.oracle_lstm_bwd.argtypes = [L, L, L, L, ctypes.c_int] + [P] * 17
+    lib.oracle_lstm_bwd.argtypes = [L, L, L, L, ctypes.c_int] + [P] * 18
     lib.oracle_lstm_bwd.restype = ctypes.c_int
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_set_threads.argtypes = [ctypes.c_int]
@@ -90,13 +90,15 @@ def _p(a):
     return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
 
-def fwd(x, W, b=None, h0=None, c0=None, reverse=False):
+def fwd(x, W, b=None, h0=None, c0=None, reverse=False, mask=None):
     """Forward pass.  Returns dict(y, hT, cT, gates, cell) as fp64 arrays.
 
     x [T,B,I], W [4H,H+I], b [4H] or None, h0/c0 [B,H] or None (zero state).
     gates is [T,B,4H] (activated i,f,g,o blocks), cell is c_t, [T,B,H].
     reverse: the steps run from t = T-1 down to 0 (the operator's reverse
     direction); tensors keep their time-major layout.
+    mask: [T,B,H] or None, the seq_length mask matrix (see lstm_oracle.c:
+    the state is blended with the step's new values, m = 0 keeps it).
     """
     x = _f64(x)
     T, B, I = x.shape
@@ -105,21 +107,22 @@ def fwd(x, W, b=None, h0=None, c0=None, reverse=False):
     b = _f64(b, (4 * H,))
     h0 = _f64(h0, (B, H))
     c0 = _f64(c0, (B, H))
+    mask = _f64(mask, (T, B, H))
     y = np.empty((T, B, H))
     hT = np.empty((B, H))
     cT = np.empty((B, H))
     gates = np.empty((T, B, 4 * H))
     cell = np.empty((T, B, H))
-    rc = _load().oracle_lstm_fwd(T, B, I, H, int(bool(reverse)), _p(x), _p(W), _p(b), _p(h0), _p(c0),
+    rc = _load().oracle_lstm_fwd(T, B, I, H, int(bool(reverse)), _p(x), _p(W), _p(b), _p(h0), _p(c0), _p(mask),
                                  _p(y), _p(hT), _p(cT), _p(gates), _p(cell))
     if rc != 0:
         raise RuntimeError(f"oracle_lstm_fwd failed ({rc})")
     return dict(y=y, hT=hT, cT=cT, gates=gates, cell=cell)
 
 
-def bwd(x, W, h0, c0, fw, dy, dhT=None, dcT=None, want_debug=False, reverse=False):
+def bwd(x, W, h0, c0, fw, dy, dhT=None, dcT=None, want_debug=False, reverse=False, mask=None):
     """Backward pass from the forward record ``fw`` (the dict ``fwd`` returns,
-    with the same ``reverse``).
+    with the same ``reverse`` and ``mask``).
 
     Returns dict(dx, dW, db, dh0, dc0) and, with want_debug, also dgates
     [T,B,4H] (gate deltas) and dcell [T,B,H] (cell gradient per step).
@@ -133,6 +136,7 @@ def bwd(x, W, h0, c0, fw, dy, dhT=None, dcT=None, want_debug=False, reverse=Fals
     dy = _f64(dy, (T, B, H))
     dhT = _f64(dhT, (B, H))
     dcT = _f64(dcT, (B, H))
+    mask = _f64(mask, (T, B, H))
     y, gates, cell = (_f64(fw[k]) for k in ("y", "gates", "cell"))
     dx = np.empty((T, B, I))
     dW = np.empty((4 * H, H + I))
@@ -141,7 +145,7 @@ def bwd(x, W, h0, c0, fw, dy, dhT=None, dcT=None, want_debug=False, reverse=Fals
     dc0 = np.empty((B, H))
     dgates = np.empty((T, B, 4 * H)) if want_debug else None
     dcell = np.empty((T, B, H)) if want_debug else None
-    rc = _load().oracle_lstm_bwd(T, B, I, H, int(bool(reverse)), _p(x), _p(W), _p(h0), _p(c0),
+    rc = _load().oracle_lstm_bwd(T, B, I, H, int(bool(reverse)), _p(x), _p(W), _p(h0), _p(c0), _p(mask),
                                  _p(y), _p(gates), _p(cell), _p(dy), _p(dhT), _p(dcT),
                                  _p(dx), _p(dW), _p(db), _p(dh0), _p(dc0),
                                  _p(dgates), _p(dcell))
@@ -162,12 +166,48 @@ def ifjo_rows(H: int, gate_order: str):
     return np.concatenate([np.arange(H) + g * H for g in blocks])
 
 
+def length_mask(lengths, T, H):
+    """The seq_length mask matrix [T,B,H] of per-sequence lengths: 1 at the
+    steps t < lengths[b] of sequence b, 0 past its end (lengths outside
+    [0, T] are taken as the nearest end of that range)."""
+    L = np.clip(np.asarray(lengths, dtype=np.int64), 0, T)
+    m = (np.arange(T)[:, None] < L[None, :]).astype(np.float64)
+    return np.repeat(m[:, :, None], H, axis=2)
+
+
 def fwd_bwd(inp: dict) -> dict:
     """Run forward then backward on an input dict with keys
     x, W, b, h0, c0, dy, dhT, dcT (values may be None where optional) and
     optionally reverse (default False), gate_order ("ifjo", the oracle's
-    own order, or "ijfo": W, b, dW and db with their row blocks relabelled)
-    and two_bias (b and db [2][4H])."""
+    own order, or "ijfo": W, b, dW and db with their row blocks relabelled),
+    two_bias (b and db [2][4H]), mask ([T,B,H], the seq_length mask matrix)
+    or lengths ([B], turned into that mask by length_mask), and
+    bidirectional (see below)."""
+    if inp.get("bidirectional"):
+        # Two directions of one layer: direction 0 runs forward in time and
+        # direction 1 in reverse, each with its own W, b and initial state
+        # ([2][...] of the one-direction shapes), on the same x; the output
+        # at time t is the two directions' h_t side by side ([T,B,2H]) and
+        # the final states are [2][B][H] -- the num_directions layout of the
+        # PyTorch recurrent-layer page.  dy [T,B,2H] splits the same way;
+        # dx is the sum of the two directions' input gradients (x feeds
+        # both).
+        H = inp["W"].shape[1] // 4
+        outs = []
+        for d in range(2):
+            sub = dict(inp, bidirectional=False, reverse=bool(d), W=inp["W"][d],
+                       b=None if inp.get("b") is None else inp["b"][d],
+                       dy=inp["dy"][:, :, d * H:(d + 1) * H])
+            for k in ("h0", "c0", "dhT", "dcT"):
+                sub[k] = None if inp.get(k) is None else inp[k][d]
+            outs.append(fwd_bwd(sub))
+        out = {"y": np.concatenate([outs[0]["y"], outs[1]["y"]], axis=2), "dx": outs[0]["dx"] + outs[1]["dx"]}
+        for k in ("hT", "cT", "dW", "db", "dh0", "dc0"):
+            out[k] = np.stack([outs[0][k], outs[1][k]])
+        return out
+    if inp.get("lengths") is not None and inp.get("mask") is None:
+        x = inp["x"]
+        return fwd_bwd(dict(inp, lengths=None, mask=length_mask(inp["lengths"], x.shape[0], inp["W"].shape[0] // 4)))
     if inp.get("two_bias"):
         # b = [b_ih; b_hh] enter the pre-activation as their sum (bias_ih and
         # bias_hh of the CMU 10-414 HW4 page's LSTMCell); both receive the one
@@ -186,9 +226,10 @@ def fwd_bwd(inp: dict) -> dict:
         out["db"] = out["db"][rows]
         return out
     rev = bool(inp.get("reverse", False))
-    fw = fwd(inp["x"], inp["W"], inp.get("b"), inp.get("h0"), inp.get("c0"), reverse=rev)
+    mask = inp.get("mask")
+    fw = fwd(inp["x"], inp["W"], inp.get("b"), inp.get("h0"), inp.get("c0"), reverse=rev, mask=mask)
     bw = bwd(inp["x"], inp["W"], inp.get("h0"), inp.get("c0"), fw, inp["dy"],
-             inp.get("dhT"), inp.get("dcT"), reverse=rev)
+             inp.get("dhT"), inp.get("dcT"), reverse=rev, mask=mask)
     out = {k: fw[k] for k in ("y", "hT", "cT")}
     out.update(bw)
     return out

@@ -12,10 +12,10 @@
 #include <stdlib.h>
 
 int oracle_lstm_fwd(long T, long B, long I, long H, int reverse, const double* x, const double* W,
-                    const double* b, const double* h0, const double* c0, double* y, double* hT, double* cT,
-                    double* gates, double* cell);
+                    const double* b, const double* h0, const double* c0, const double* mask, double* y,
+                    double* hT, double* cT, double* gates, double* cell);
 int oracle_lstm_bwd(long T, long B, long I, long H, int reverse, const double* x, const double* W,
-                    const double* h0, const double* c0, const double* y, const double* gates,
+                    const double* h0, const double* c0, const double* mask, const double* y, const double* gates,
                     const double* cell, const double* dy, const double* dhT, const double* dcT, double* dx,
                     double* dW, double* db, double* dh0, double* dc0, double* dgates, double* dcell);
 
@@ -44,24 +44,25 @@ static int finite_all(const double* p, long n) {
 static int run(long T, long B, long I, long H, int reverse, int opt) {
   const long Z = H + I, G4 = 4 * H;
   double *x = alloc(T * B * I, 1), *W = alloc(G4 * Z, 1), *b = alloc(G4, 1), *h0 = alloc(B * H, 1),
-         *c0 = alloc(B * H, 1);
+         *c0 = alloc(B * H, 1), *mask = alloc(T * B * H, 1);
   double *y = alloc(T * B * H, 0), *hT = alloc(B * H, 0), *cT = alloc(B * H, 0);
   double *gates = alloc(T * B * G4, 0), *cell = alloc(T * B * H, 0);
   double *dy = alloc(T * B * H, 1), *dhT = alloc(B * H, 1), *dcT = alloc(B * H, 1);
   double *dx = alloc(T * B * I, 0), *dW = alloc(G4 * Z, 0), *db = alloc(G4, 0), *dh0 = alloc(B * H, 0),
          *dc0 = alloc(B * H, 0), *dgates = alloc(T * B * G4, 0), *dcell = alloc(T * B * H, 0);
   /* opt: 1 = every optional tensor present, 0 = every one absent (NULL) */
-  int rc = oracle_lstm_fwd(T, B, I, H, reverse, x, W, opt ? b : NULL, opt ? h0 : NULL, opt ? c0 : NULL, y, hT, cT,
-                           gates, cell);
+  int rc = oracle_lstm_fwd(T, B, I, H, reverse, x, W, opt ? b : NULL, opt ? h0 : NULL, opt ? c0 : NULL,
+                           opt ? mask : NULL, y, hT, cT, gates, cell);
   if (rc == 0)
-    rc = oracle_lstm_bwd(T, B, I, H, reverse, x, W, opt ? h0 : NULL, opt ? c0 : NULL, y, gates, cell, dy,
+    rc = oracle_lstm_bwd(T, B, I, H, reverse, x, W, opt ? h0 : NULL, opt ? c0 : NULL, opt ? mask : NULL, y, gates,
+                         cell, dy,
                          opt ? dhT : NULL, opt ? dcT : NULL, dx, dW, opt ? db : NULL, dh0, dc0,
                          opt ? dgates : NULL, opt ? dcell : NULL);
   int ok = rc == 0 && finite_all(y, T * B * H) && finite_all(hT, B * H) && finite_all(cT, B * H) &&
            finite_all(dx, T * B * I) && finite_all(dW, G4 * Z) && finite_all(dh0, B * H) && finite_all(dc0, B * H) &&
            (!opt || finite_all(db, G4));
   if (!ok) fprintf(stderr, "FAILED T=%ld B=%ld I=%ld H=%ld reverse=%d optional=%d rc=%d\n", T, B, I, H, reverse, opt, rc);
-  free(x); free(W); free(b); free(h0); free(c0); free(y); free(hT); free(cT); free(gates); free(cell);
+  free(x); free(W); free(b); free(h0); free(c0); free(mask); free(y); free(hT); free(cT); free(gates); free(cell);
   free(dy); free(dhT); free(dcT); free(dx); free(dW); free(db); free(dh0); free(dc0); free(dgates); free(dcell);
   return ok;
 }
@@ -76,7 +77,7 @@ int main(void) {
         ++n;
       }
   /* an invalid size is rejected, nothing is touched */
-  ok &= oracle_lstm_fwd(1, 1, 1, 0, 0, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == -1;
+  ok &= oracle_lstm_fwd(1, 1, 1, 0, 0, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL) == -1;
   printf("%d oracle runs under the sanitizers: %s\n", n, ok ? "ok" : "FAILED");
   return ok ? 0 : 1;
 }

@@ -5,7 +5,8 @@ at least one pin.  The mistakes are the ones a reading of the
 factor applied twice in the cell carry, a dropped carry, a wrong sign in a
 gate derivative, swapped gate blocks, the [x | h] column order, the cell
 value of the wrong step in the forget-gate delta, the wrong step's hidden
-state in the parameter gradient, and the input block used for delta-h."""
+state in the parameter gradient, the input block used for delta-h, and
+three ways of getting the seq_length mask's blend wrong.""" 
 import os
 import subprocess
 import tempfile
@@ -18,12 +19,12 @@ import test_oracle_pins as pins
 SRC = os.path.join(os.path.dirname(oracle.__file__), "lstm_oracle.c")
 
 MUTANTS = {
-    "forget_twice": ("const double dc = dh * og * (1.0 - tc * tc) + dcc[bb * H + j];",
-                     "const double dc = dh * og * (1.0 - tc * tc) + dcc[bb * H + j] * fg;"),
-    "carry_dropped": ("const double dc = dh * og * (1.0 - tc * tc) + dcc[bb * H + j];",
-                      "const double dc = dh * og * (1.0 - tc * tc);"),
-    "sign_output_gate": ("const double d_o = dh * tc * og * (1.0 - og);",
-                         "const double d_o = dh * tc * og * (og - 1.0);"),
+    "forget_twice": ("const double dc = dhn * og * (1.0 - tc * tc) + m * dcc[bb * H + j];",
+                     "const double dc = dhn * og * (1.0 - tc * tc) + m * dcc[bb * H + j] * fg;"),
+    "carry_dropped": ("const double dc = dhn * og * (1.0 - tc * tc) + m * dcc[bb * H + j];",
+                      "const double dc = dhn * og * (1.0 - tc * tc);"),
+    "sign_output_gate": ("const double d_o = dhn * tc * og * (1.0 - og);",
+                         "const double d_o = dhn * tc * og * (og - 1.0);"),
     "gates_if_swapped": ("const double ig = sigm(ab[j]);          /* input gate      */\n"
                          "        const double fg = sigm(ab[H + j]);      /* forget gate     */",
                          "const double ig = sigm(ab[H + j]);\n        const double fg = sigm(ab[j]);"),
@@ -35,6 +36,15 @@ MUTANTS = {
                               "const double d_f = dc * c * fg * (1.0 - fg);"),
     "dW_uses_h_t": ("const double* hprev = t > 0 ? y + ((t - 1) * B + bb) * H : (h0 ? h0 + bb * H : NULL);",
                     "const double* hprev = y + (t * B + bb) * H;"),
+    # seq_length mask: the state not kept where the mask is 0 (the new
+    # value scaled down instead), the state's own gradient not passed on,
+    # and the cell carry's (1-m) part dropped
+    "mask_state_not_kept": ("const double c = m * cn + (1.0 - m) * cp[bb * H + j];",
+                            "const double c = m * cn;"),
+    "mask_carry_not_passed": ("dhp[bb * H + j] = (1.0 - m) * dh;",
+                              "dhp[bb * H + j] = 0.0;"),
+    "mask_cell_carry_dropped": ("dcc[bb * H + j] = (1.0 - m) * dcc[bb * H + j] + dc * fg;",
+                                "dcc[bb * H + j] = dc * fg;"),
     # delta-h read from the wrong block of delta-z (column k+I instead of k)
     "dh_from_input_block": ("for (long r = 0; r < G4; ++r) s += W[r * Z + k] * g[r];",
                             "for (long r = 0; r < G4; ++r) s += W[r * Z + ((k < H) ? (k + I) % Z : k)] * g[r];"),
@@ -52,6 +62,8 @@ def battery():
         ("forget_product", pins.test_forget_product_law),
         ("t1_closed_form", pins.test_t1_closed_form),
         ("torch", lambda: pins.test_against_torch_nn_lstm_fp64(5, 3, 4, 6)),
+        ("fd_mask", lambda: pins.test_fd_mask(3, 2, 2, 3, False)),
+        ("mask_truncation", lambda: pins.test_mask_is_truncation(False)),
     ]
     for name, fn in checks:
         try:

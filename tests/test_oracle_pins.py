@@ -380,3 +380,189 @@ def test_two_biases_against_torch_nn_lstm_fp64(T, B, I, H):
         np.testing.assert_allclose(out[k], ref[k], rtol=1e-11, atol=1e-13, err_msg=k)
     np.testing.assert_allclose(out["db"][0], ref["db_ih"], rtol=1e-11, atol=1e-13)
     np.testing.assert_allclose(out["db"][1], ref["db_hh"], rtol=1e-11, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# seq_length mask (the parameter table's mask matrix [T, Batch, hidden_size]
+# for the actual sequence lengths) and the bidirectional layer (two
+# directions, outputs side by side: the num_directions layout of the
+# PyTorch recurrent-layer page)
+
+def outputs_loss(inp, out):
+    """The scalar whose gradient the backward computes, from the forward
+    outputs in `out`: sum <dy, y> + <dhT, hT> + <dcT, cT> (any layout)."""
+    L = float(np.sum(inp["dy"] * out["y"]))
+    for c, k in (("dhT", "hT"), ("dcT", "cT")):
+        if inp.get(c) is not None:
+            L += float(np.sum(inp[c] * out[k]))
+    return L
+
+
+def fd_check_general(inp, params=("x", "W", "b", "h0", "c0"), eps_rel=1e-6, tol=1e-7):
+    """Central differences of outputs_loss against the backward, every
+    element of every parameter, through oracle.fwd_bwd (any flags)."""
+    g = oracle.fwd_bwd(inp)
+    for p in params:
+        flat = inp[p].reshape(-1)
+        gflat = g[GRAD_OF[p]].reshape(-1)
+        for idx in range(flat.size):
+            th = flat[idx]
+            eps = eps_rel * max(1.0, abs(th))
+            flat[idx] = th + eps
+            lp = outputs_loss(inp, oracle.fwd_bwd(inp))
+            flat[idx] = th - eps
+            lm = outputs_loss(inp, oracle.fwd_bwd(inp))
+            flat[idx] = th
+            fd = (lp - lm) / (2 * eps)
+            err = abs(fd - gflat[idx]) / (1.0 + abs(gflat[idx]))
+            assert err <= tol, f"{p}[{idx}] FD {fd!r} vs analytic {gflat[idx]!r}"
+
+
+@pytest.mark.parametrize("T,B,I,H,rev", [(3, 2, 2, 3, False), (3, 2, 2, 3, True), (4, 3, 1, 2, False)])
+def test_fd_mask(T, B, I, H, rev):
+    """Finite differences through the mask's blend, with mask values
+    anywhere in [0, 1] (not only 0 and 1), in both directions: the backward
+    is the exact gradient of the blended forward."""
+    inp = full_inputs(T, B, I, H, seed=91)
+    rng = np.random.default_rng(92)
+    mask = rng.uniform(0, 1, (T, B, H))
+    mask[rng.uniform(0, 1, (T, B, H)) < 0.3] = 0.0
+    mask[rng.uniform(0, 1, (T, B, H)) < 0.3] = 1.0
+    fd_check_general(dict(inp, mask=mask, reverse=rev))
+
+
+def test_mask_of_ones_is_the_plain_cell():
+    """A mask of ones gives the unmasked result bit for bit (m = 1 is the
+    page's cell), in both directions."""
+    for rev in (False, True):
+        inp = dict(full_inputs(5, 3, 4, 6, seed=93), reverse=rev)
+        a = oracle.fwd_bwd(inp)
+        b = oracle.fwd_bwd(dict(inp, mask=np.ones((5, 3, 6))))
+        for k in a:
+            np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+@pytest.mark.parametrize("rev", [False, True])
+def test_mask_is_truncation(rev):
+    """Lengths L_b (a 0/1 mask of whole steps): sequence b gives what the
+    unmasked cell gives on its first L_b steps alone -- y at those steps, the
+    final state (hT, cT), dh0, dc0, dx at those steps, and its share of dW,
+    db -- and the padded outputs (t >= L_b) repeat the state they hold: the
+    last state in the forward direction, h0 in the reverse one (whose steps
+    past the end come first), with dx zero there.  In the reverse direction
+    the truncated sequence runs from t = L_b - 1 down to 0.  dy, dhT and dcT
+    are nonzero everywhere: the cotangent of a padded output reaches the
+    state it repeats (the final state, or h0 in reverse)."""
+    T, B, I, H = 6, 4, 3, 5
+    inp = dict(full_inputs(T, B, I, H, seed=94), reverse=rev)
+    lengths = [6, 3, 0, 1]
+    out = oracle.fwd_bwd(dict(inp, lengths=lengths))
+    dW, db = np.zeros_like(out["dW"]), np.zeros_like(out["db"])
+    for b, L in enumerate(lengths):
+        one = {k: (None if inp[k] is None else inp[k][b:b + 1]) for k in ("h0", "c0", "dhT", "dcT")}
+        pad_dy = inp["dy"][L:, b:b + 1].sum(axis=0)
+        dhT = one["dhT"] if rev else one["dhT"] + pad_dy
+        sub = dict(inp, B=1, T=L, x=inp["x"][:L, b:b + 1], dy=inp["dy"][:L, b:b + 1], dhT=dhT, **{
+            k: one[k] for k in ("h0", "c0", "dcT")})
+        ref = oracle.fwd_bwd(sub)
+        if rev:
+            ref["dh0"] = ref["dh0"] + pad_dy
+        np.testing.assert_allclose(out["y"][:L, b], ref["y"][:, 0], rtol=1e-13, atol=1e-15)
+        held = inp["h0"][b] if rev else ref["hT"][0]
+        np.testing.assert_allclose(out["y"][L:, b], np.broadcast_to(held, (T - L, H)), rtol=1e-13, atol=1e-15)
+        for k in ("hT", "cT", "dh0", "dc0"):
+            np.testing.assert_allclose(out[k][b], ref[k][0], rtol=1e-12, atol=1e-14, err_msg=f"{k} b={b}")
+        np.testing.assert_allclose(out["dx"][:L, b], ref["dx"][:, 0], rtol=1e-12, atol=1e-14)
+        assert np.all(out["dx"][L:, b] == 0.0)
+        dW += ref["dW"]
+        db += ref["db"]
+    np.testing.assert_allclose(out["dW"], dW, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(out["db"], db, rtol=1e-12, atol=1e-13)
+
+
+def bidir_inputs(T, B, I, H, seed):
+    """Inputs of a bidirectional layer: W, b, h0, c0, dhT, dcT with a
+    leading direction axis, dy [T,B,2H]."""
+    a = full_inputs(T, B, I, H, seed=seed)
+    c = full_inputs(T, B, I, H, seed=seed + 1000)
+    inp = dict(a, bidirectional=True, dy=np.concatenate([a["dy"], c["dy"]], axis=2))
+    for k in ("W", "b", "h0", "c0", "dhT", "dcT"):
+        inp[k] = np.stack([a[k], c[k]])
+    return inp
+
+
+@pytest.mark.parametrize("T,B,I,H", [(3, 2, 2, 3), (2, 1, 3, 2)])
+def test_fd_bidirectional(T, B, I, H):
+    """Finite differences of the two-direction loss: dx collects both
+    directions' input gradients, and each direction's dW, db, dh0, dc0 are
+    its own."""
+    fd_check_general(bidir_inputs(T, B, I, H, seed=95))
+
+
+def test_fd_bidirectional_masked():
+    """Finite differences with a length mask under both directions."""
+    inp = bidir_inputs(4, 3, 2, 3, seed=96)
+    fd_check_general(dict(inp, lengths=[4, 2, 0]))
+
+
+def torch_bidir_reference(inp, lengths=None):
+    """torch.nn.LSTM(bidirectional=True) on the CPU in fp64, direction d's
+    weights from W[d] ([W_h | W_x] columns), b[d] as bias_ih and a zero
+    bias_hh; with lengths, through a packed sequence (outputs past a
+    sequence's end come back as zeros, h_n / c_n are the states at each
+    sequence's last step).  Returns outputs and autograd gradients of
+    outputs_loss."""
+    torch = pytest.importorskip("torch")
+    T, B, I, H = inp["T"], inp["B"], inp["I"], inp["H"]
+    m = torch.nn.LSTM(I, H, num_layers=1, bias=True, batch_first=False, bidirectional=True).double()
+    with torch.no_grad():
+        for d, sfx in enumerate(("", "_reverse")):
+            getattr(m, "weight_hh_l0" + sfx).copy_(torch.from_numpy(inp["W"][d][:, :H]))
+            getattr(m, "weight_ih_l0" + sfx).copy_(torch.from_numpy(inp["W"][d][:, H:]))
+            getattr(m, "bias_ih_l0" + sfx).copy_(torch.from_numpy(inp["b"][d]))
+            getattr(m, "bias_hh_l0" + sfx).zero_()
+    x = torch.from_numpy(inp["x"]).requires_grad_(True)
+    h0 = torch.from_numpy(inp["h0"]).clone().requires_grad_(True)
+    c0 = torch.from_numpy(inp["c0"]).clone().requires_grad_(True)
+    if lengths is None:
+        y, (hn, cn) = m(x, (h0, c0))
+    else:
+        packed = torch.nn.utils.rnn.pack_padded_sequence(x, torch.tensor(lengths), enforce_sorted=False)
+        yp, (hn, cn) = m(packed, (h0, c0))
+        y, _ = torch.nn.utils.rnn.pad_packed_sequence(yp, total_length=T)
+    L = (y * torch.from_numpy(inp["dy"])).sum() + (hn * torch.from_numpy(inp["dhT"])).sum() \
+        + (cn * torch.from_numpy(inp["dcT"])).sum()
+    L.backward()
+    grads = lambda name: np.stack([getattr(m, name + sfx).grad.numpy() for sfx in ("", "_reverse")])
+    return dict(y=y.detach().numpy(), hT=hn.detach().numpy(), cT=cn.detach().numpy(), dx=x.grad.numpy(),
+                dh0=h0.grad.numpy(), dc0=c0.grad.numpy(),
+                dW=np.concatenate([grads("weight_hh_l0"), grads("weight_ih_l0")], axis=2), db=grads("bias_ih_l0"))
+
+
+def test_bidirectional_against_torch_nn_lstm_fp64():
+    """The two-direction layer against torch.nn.LSTM(bidirectional=True):
+    every output and gradient (this also pins the reverse direction against
+    an independent implementation)."""
+    inp = bidir_inputs(5, 3, 4, 6, seed=97)
+    ref = torch_bidir_reference(inp)
+    out = oracle.fwd_bwd(inp)
+    for k, v in ref.items():
+        np.testing.assert_allclose(out[k], v, rtol=1e-11, atol=1e-13, err_msg=k)
+
+
+def test_masked_bidirectional_against_torch_packed_sequence():
+    """Lengths under both directions against torch's packed sequences.
+    torch returns zeros past each sequence's end where this reading repeats
+    the state, so the comparison takes the outputs at valid steps, the
+    final states, and the gradients with dy zero past each end (then the
+    two readings have the same loss)."""
+    T = 6
+    inp = bidir_inputs(T, 4, 3, 5, seed=98)
+    lengths = [6, 2, 4, 1]
+    valid = (np.arange(T)[:, None] < np.array(lengths)[None, :]).astype(np.float64)
+    inp["dy"] = inp["dy"] * valid[:, :, None]
+    ref = torch_bidir_reference(inp, lengths)
+    out = oracle.fwd_bwd(dict(inp, lengths=lengths))
+    np.testing.assert_allclose(out["y"] * valid[:, :, None], ref["y"], rtol=1e-11, atol=1e-13)
+    for k in ("hT", "cT", "dx", "dh0", "dc0", "dW", "db"):
+        np.testing.assert_allclose(out[k], ref[k], rtol=1e-11, atol=1e-13, err_msg=k)
