@@ -85,7 +85,8 @@ enum {
   LSTM_ERR_COOP = -7,        /* the persistent grid cannot be co-resident on this device */
   LSTM_ERR_LAUNCH = -8,      /* a HIP launch failed */
   LSTM_ERR_TIMEOUT = -9,     /* a per-step wait of the recurrent kernels hit its time bound */
-  LSTM_ERR_DEVICE = -10      /* the current device is not gfx950 or could not be queried */
+  LSTM_ERR_DEVICE = -10,     /* the current device is not gfx950 or could not be queried */
+  LSTM_ERR_SCRATCH = -11     /* lstm_fwd_train_scratch: the shape needs more than LSTM_SCRATCH_BYTES */
 };
 
 /* Direction of time (SingleLayerLstmGrad, 参数说明: the direction attribute,
@@ -167,6 +168,27 @@ int lstm_query_plan(const lstm_shape* shape, lstm_plan_info* info);
 int lstm_fwd_train(const lstm_shape* shape, const void* x, const void* W, const void* b,
                    const void* h0, const void* c0, void* y, void* hT, void* cT,
                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the
+ * forward pass of lstm_fwd_train() with the library's own device array as
+ * its workspace, so that the caller passes only inputs and outputs.  The
+ * array holds LSTM_SCRATCH_BYTES per device; it is set up on the first call
+ * on each device (its address looked up once, the device's ordering event
+ * created) and kept until the process ends.  No call allocates memory.
+ *   Arguments and results as lstm_fwd_train() without the workspace; the
+ *   forward record stays in the array until the next call on the device
+ *   (there is no matching backward: a training step uses lstm_fwd_train()).
+ *   LSTM_ERR_SCRATCH (nothing launched, outputs untouched) when
+ *   lstm_query() of the shape exceeds LSTM_SCRATCH_BYTES.
+ * Every call on a device shares its array: calls that overlap in time on
+ * one device (on different streams, or from several threads) race and give
+ * undefined results; calls on one stream are safe.  A per-step time-out
+ * leaves the outputs undefined and is not reported (the array is not the
+ * caller's to inspect). */
+#define LSTM_SCRATCH_BYTES (64u << 20)
+int lstm_fwd_train_scratch(const lstm_shape* shape, const void* x, const void* W, const void* b,
+                           const void* h0, const void* c0, void* y, void* hT, void* cT, void* stream);
 
 /* Backpropagation through time ("反向传播算法" steps 1-6).
  *   dy [T,B,H]: required; dhT, dcT [B,H]: optional, NULL = zero

@@ -183,14 +183,28 @@ hipError_t persistent_before(hipStream_t s) {
   return hipSuccess;
 }
 
+// the current device's ordering event, created on first use
+static hipError_t persistent_event(int dev) {
+  if (g_persist_ev[dev]) return hipSuccess;
+  return hipEventCreateWithFlags(&g_persist_ev[dev], hipEventDisableTiming);
+}
+
+hipError_t persistent_prepare() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_persist_mu);
+  return persistent_event(dev);
+}
+
 hipError_t persistent_after(hipStream_t s) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lk(g_persist_mu);
-  if (!g_persist_ev[dev] && (e = hipEventCreateWithFlags(&g_persist_ev[dev], hipEventDisableTiming)) != hipSuccess)
-    return e;
+  if ((e = persistent_event(dev)) != hipSuccess) return e;
   if ((e = hipEventRecord(g_persist_ev[dev], s)) != hipSuccess) return e;
   g_persist_stream[dev] = s;
   g_persist_used[dev] = true;
@@ -290,6 +304,7 @@ const char* lstm_status_string(int status) {
     case LSTM_ERR_LAUNCH: return "HIP launch failed";
     case LSTM_ERR_TIMEOUT: return "a recurrent step wait timed out";
     case LSTM_ERR_DEVICE: return "current device is not gfx950";
+    case LSTM_ERR_SCRATCH: return "shape needs more workspace than the library's scratch array holds";
     default: return "unknown status";
   }
 }
@@ -323,6 +338,40 @@ int lstm_query_plan(const lstm_shape* shape, lstm_plan_info* info) {
   info->inproj_tiles_per_wg = inproj_tiles_per_wg(p);
   return LSTM_OK;
 }
+
+}  // extern "C"
+
+namespace lstm {
+
+// Device scratch of lstm_fwd_train_scratch: the workspace of that entry
+// point, one copy per device, held until the process ends.  Host code uses
+// only the device address that hipGetSymbolAddress returns for it (kept per
+// device in g_scratch_ptr), never the array's name.
+constexpr size_t kScratchBytes = LSTM_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Address of the current device's scratch, looked up once per device (with
+// that device current); the ordering event of the persistent launches is
+// created here as well, so that later calls create nothing.
+static int scratch_for_device(void** ptr) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LSTM_ERR_DEVICE;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return LSTM_ERR_DEVICE;
+    if (persistent_prepare() != hipSuccess) return LSTM_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return LSTM_OK;
+}
+
+}  // namespace lstm
+
+extern "C" {
 
 int lstm_fwd_train(const lstm_shape* shape, const void* x, const void* W, const void* b, const void* h0,
                    const void* c0, void* y, void* hT, void* cT, void* workspace, size_t workspace_bytes,
@@ -370,6 +419,19 @@ int lstm_fwd_train(const lstm_shape* shape, const void* x, const void* W, const 
                                stamps_fit(p) ? g_stamps_fwd : nullptr, s);
   }
   return status_of(err);
+}
+
+int lstm_fwd_train_scratch(const lstm_shape* shape, const void* x, const void* W, const void* b, const void* h0,
+                           const void* c0, void* y, void* hT, void* cT, void* stream) {
+  if (!shape) return LSTM_ERR_NULL;
+  size_t need = 0;
+  const int rc = lstm_query(shape, &need);
+  if (rc != LSTM_OK) return rc;
+  if (need > kScratchBytes) return LSTM_ERR_SCRATCH;
+  void* ws = nullptr;
+  const int rs = scratch_for_device(&ws);
+  if (rs != LSTM_OK) return rs;
+  return lstm_fwd_train(shape, x, W, b, h0, c0, y, hT, cT, ws, kScratchBytes, stream);
 }
 
 int lstm_bwd(const lstm_shape* shape, const void* dy, const void* dhT, const void* dcT, const void* x,

@@ -242,6 +242,8 @@ __device__ __forceinline__ float ldf(const void* p, int64_t i) {
 // (one event per device, kept for the life of the process).
 hipError_t persistent_before(hipStream_t s);
 hipError_t persistent_after(hipStream_t s);
+// creates the current device's ordering event ahead of the first launch
+hipError_t persistent_prepare();
 
 // The persistent kernels need every work-group of the grid resident at
 // once.  The grid never exceeds the CU count and each work-group fits a CU

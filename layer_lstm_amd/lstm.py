@@ -30,9 +30,10 @@ F32, BF16 = 0, 1
 OK = 0
 STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_DIMS", -3: "ERR_DTYPE", -4: "ERR_ALIGN",
           -5: "ERR_WORKSPACE", -6: "ERR_UNSUPPORTED", -7: "ERR_COOP", -8: "ERR_LAUNCH",
-          -9: "ERR_TIMEOUT", -10: "ERR_DEVICE"}
+          -9: "ERR_TIMEOUT", -10: "ERR_DEVICE", -11: "ERR_SCRATCH"}
+SCRATCH_BYTES = 64 << 20  # LSTM_SCRATCH_BYTES
 EXPORTS = ("lstm_abi_version", "lstm_status_string", "lstm_query", "lstm_query_plan", "lstm_fwd_train",
-           "lstm_bwd", "lstm_check_workspace", "lstm_timing_enable", "lstm_timing_read", "lstm_stamps_set")
+           "lstm_fwd_train_scratch", "lstm_bwd", "lstm_check_workspace", "lstm_timing_enable", "lstm_timing_read", "lstm_stamps_set")
 STAMP_WGS, STAMP_POINTS = 8, 6
 KERNEL_KINDS = ("input_projection", "forward_recurrence", "backward_recurrence", "dW_product",
                 "dx_product", "unused", "state_copy")
@@ -60,6 +61,8 @@ _lib.lstm_query_plan.restype = ctypes.c_int
 _lib.lstm_query_plan.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(PlanInfo)]
 _lib.lstm_fwd_train.restype = ctypes.c_int
 _lib.lstm_fwd_train.argtypes = [ctypes.POINTER(Shape)] + [_P] * 8 + [_P, ctypes.c_size_t, _P]
+_lib.lstm_fwd_train_scratch.restype = ctypes.c_int
+_lib.lstm_fwd_train_scratch.argtypes = [ctypes.POINTER(Shape)] + [_P] * 8 + [_P]
 _lib.lstm_bwd.restype = ctypes.c_int
 _lib.lstm_bwd.argtypes = [ctypes.POINTER(Shape)] + [_P] * 8 + [_P, ctypes.c_size_t] + [_P] * 5 + [_P]
 _lib.lstm_check_workspace.restype = ctypes.c_int
@@ -141,6 +144,17 @@ def fwd_train(shape, x, W, b, h0, c0, y, hT, cT, workspace, ws_bytes=None, strea
                              _ptr(y), _ptr(hT), _ptr(cT), _ptr(workspace), ws_bytes, _stream(stream))
     if check and rc != OK:
         raise LstmError(rc, "lstm_fwd_train")
+    return rc
+
+
+def fwd_train_scratch(shape, x, W, b, h0, c0, y, hT, cT, stream=None, check=True):
+    """lstm_fwd_train_scratch on torch tensors (None = NULL): the forward
+    pass with the library's own device array as the workspace.  Returns the
+    status."""
+    rc = _lib.lstm_fwd_train_scratch(ctypes.byref(shape), _ptr(x), _ptr(W), _ptr(b), _ptr(h0), _ptr(c0),
+                                     _ptr(y), _ptr(hT), _ptr(cT), _stream(stream))
+    if check and rc != OK:
+        raise LstmError(rc, "lstm_fwd_train_scratch")
     return rc
 
 

@@ -95,3 +95,13 @@ def test_query_rejects_bad_dtype_and_nulls(lstm):
     assert lstm.lib().lstm_query_plan(ctypes.byref(s), ctypes.byref(info)) == -3
     assert lstm.lib().lstm_fwd_train(None, *([None] * 9), 0, None) == -1
     assert lstm.lib().lstm_bwd(None, *([None] * 9), 0, *([None] * 6)) == -1
+
+
+def test_scratch_entry_point_host_checks(lstm):
+    """lstm_fwd_train_scratch: the array size stated in the header matches
+    the binding's, and a NULL shape is refused before any device work."""
+    src = open(HEADER).read()
+    m = re.search(r"#define\s+LSTM_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == lstm.SCRATCH_BYTES
+    assert header_enum("LSTM_ERR_SCRATCH") == -11
+    assert lstm.lib().lstm_fwd_train_scratch(None, *([None] * 8), None) == -1
