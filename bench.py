@@ -34,7 +34,7 @@ sys.path.insert(0, ROOT)
 from layer_lstm_amd import synth  # noqa: E402
 
 METRIC = "LSTM fwd+bwd sequences/s and effective TFLOP/s (fraction of MFMA peak)"
-PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6}  # MI355X dense matrix peaks
+PEAK_TFLOPS = {"f32": 157.3, "bf16": 2516.6, "f16": 2516.6}  # MI355X dense matrix peaks
 VALU_TFLOPS = 157.3  # MI355X fp32 vector peak (256 CUs x 2.4 GHz)
 HBM_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -167,8 +167,8 @@ def main():
     inp = synth.workload_inputs(w.name)
     if args.two_bias:
         inp["b"] = np.stack([inp["b"], inp["b"][::-1].copy()])
-    code = lstm.F32 if w.dtype == "f32" else lstm.BF16
-    td = torch.float32 if w.dtype == "f32" else torch.bfloat16
+    code = {"f32": lstm.F32, "bf16": lstm.BF16, "f16": lstm.F16}[w.dtype]
+    td = lstm.torch_dtype(code)
     dev = torch.device("cuda:0")
 
     def put(a):

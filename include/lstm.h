@@ -27,9 +27,9 @@
  *   b, db [4H]      same gate order (the page's db shape [4,H] is the same
  *                   memory)
  *   dW [4H, H+I]
- * Element type: all of the above are LSTM_F32 (float) or all LSTM_BF16
- * (bfloat16 storage).  Every dot product accumulates in fp32; the cell state
- * is carried in fp32.
+ * Element type: all of the above are LSTM_F32 (float), all LSTM_BF16
+ * (bfloat16 storage) or all LSTM_F16 (IEEE binary16 storage).  Every dot
+ * product accumulates in fp32; the cell state is carried in fp32.
  *
  * Ownership and execution: the caller allocates every buffer (device
  * memory).  The library never allocates device memory, keeps no pointer
@@ -70,15 +70,17 @@ extern "C" {
  * gate_order attribute; LSTM_GATES_IJFO below selects "ijfo"). */
 enum { LSTM_GATE_I = 0, LSTM_GATE_F = 1, LSTM_GATE_G = 2, LSTM_GATE_O = 3 };
 
-/* Element type of every ABI tensor. */
-enum { LSTM_F32 = 0, LSTM_BF16 = 1 };
+/* Element type of every ABI tensor: fp32, or 16-bit storage -- bfloat16 or
+ * IEEE binary16 (the FLOAT16 of the page's dtype column) -- with fp32
+ * accumulation. */
+enum { LSTM_F32 = 0, LSTM_BF16 = 1, LSTM_F16 = 2 };
 
 /* Status codes. */
 enum {
   LSTM_OK = 0,
   LSTM_ERR_NULL = -1,        /* a required pointer is NULL */
   LSTM_ERR_DIMS = -2,        /* T, B or I < 0, or H <= 0 */
-  LSTM_ERR_DTYPE = -3,       /* dtype is not LSTM_F32 / LSTM_BF16, or an unknown flag is set */
+  LSTM_ERR_DTYPE = -3,       /* dtype is not LSTM_F32 / LSTM_BF16 / LSTM_F16, or an unknown flag is set */
   LSTM_ERR_ALIGN = -4,       /* a tensor is not aligned to its element size, or the workspace to 256 B */
   LSTM_ERR_WORKSPACE = -5,   /* workspace_bytes < lstm_query() */
   LSTM_ERR_UNSUPPORTED = -6, /* shape outside the kernels' envelope (see lstm_query) */
@@ -110,7 +112,7 @@ enum { LSTM_GATES_IJFO = 2 };
  * both halves (the two enter the pre-activation alike). */
 enum { LSTM_TWO_BIAS = 4 };
 
-/* Problem shape.  dtype is LSTM_F32 or LSTM_BF16; flags is 0 or an OR of
+/* Problem shape.  dtype is LSTM_F32, LSTM_BF16 or LSTM_F16; flags is 0 or an OR of
  * LSTM_REVERSE, LSTM_GATES_IJFO and LSTM_TWO_BIAS, other bits must be 0
  * (else LSTM_ERR_DTYPE).  The forward call and the backward call of one
  * record take the same flags. */
@@ -130,7 +132,7 @@ int lstm_abi_version(void);
 const char* lstm_status_string(int status);
 
 /* Workspace size in bytes for `shape` on the current device.
- * Envelope: H <= 1024 (fp32) or 2048 (bf16), I <= 65536, T*B <= 2^31/4H,
+ * Envelope: H <= 1024 (fp32) or 2048 (16-bit storage), I <= 65536, T*B <= 2^31/4H,
  * T <= 2^30.  Returns LSTM_OK and sets
  * *workspace_bytes, or an error code (workspace_bytes untouched). */
 int lstm_query(const lstm_shape* shape, size_t* workspace_bytes);

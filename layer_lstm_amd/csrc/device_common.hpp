@@ -8,7 +8,9 @@ namespace lstm {
 
 typedef uint16_t bf16_t;  // bfloat16 bit pattern in memory
 
+typedef _Float16 f16_t;   // IEEE binary16 storage
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(8 * sizeof(_Float16)))) _Float16 f16x8_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 // operand types of the buffer load / store builtins
@@ -39,6 +41,20 @@ template <> struct Elem<bf16_t> {
   __device__ __forceinline__ static bf16_t from_f(float v) { return f2bf(v); }
 };
 
+template <> struct Elem<f16_t> {
+  static constexpr int kBytes = 2;
+  __device__ __forceinline__ static float load(const f16_t* p) { return (float)*p; }
+  __device__ __forceinline__ static float to_f(f16_t v) { return (float)v; }
+  // v_cvt_f16_f32: round to nearest even (the default mode); beyond the
+  // range, +-inf
+  __device__ __forceinline__ static f16_t from_f(float v) { return (f16_t)v; }
+};
+// A 16-bit storage element from the low 16 bits of a word.
+template <typename T>
+__device__ __forceinline__ float f_of_bits16(uint32_t bits) {
+  return Elem<T>::to_f(__builtin_bit_cast(T, (uint16_t)bits));
+}
+
 // Logistic sigmoid s(u) = 1/(1+e^-u) from its definition on the hardware
 // base-2 exponential and reciprocal (v_exp_f32, v_rcp_f32; about 1 ulp
 // each): e^-u = 2^(-u*log2(e)).  For u -> -inf, 2^(..) -> +inf and the
@@ -52,7 +68,7 @@ __device__ __forceinline__ float tanh_f(float u) { return 2.0f * sigmoidf(2.0f *
 // One MFMA k-block: 16 bytes per lane of each operand.
 //  fp32: 4 k-values per lane -> four v_mfma_f32_16x16x4f32 (k-slot s of the
 //        lane group q holds k = 4q + s of a 16-wide k-block);
-//  bf16: 8 k-values per lane -> one v_mfma_f32_16x16x32_bf16.
+//  bf16: 8 k-values per lane -> one v_mfma_f32_16x16x32_bf16;
 // Lane layout of both operands: row (A) / column (B) = lane % 16, k-group =
 // lane / 16.  Result: lane holds C[4*(lane/16)+i][lane%16], i = 0..3.
 template <typename T> struct Mfma;
@@ -73,6 +89,29 @@ template <> struct Mfma<bf16_t> {
                                                    __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
   }
 };
+//  fp16: 8 k-values per lane -> one v_mfma_f32_16x16x32_f16.
+template <> struct Mfma<f16_t> {
+  static constexpr int kBlock = 32;
+  __device__ __forceinline__ static f32x4_t mac(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+};
+
+// Element type of a storage dtype code (0 fp32, 1 bf16, 2 fp16).
+__host__ __device__ __forceinline__ int dtype_bytes(int dtype) { return dtype == 0 ? 4 : 2; }
+// fp32 value of element i of a buffer of storage dtype `dtype`.
+__device__ __forceinline__ float load_as_f(const void* p, int64_t i, int dtype) {
+  if (dtype == 1) return bf2f(((const bf16_t*)p)[i]);
+  if (dtype == 2) return (float)((const f16_t*)p)[i];
+  return ((const float*)p)[i];
+}
+// Store fp32 v as element i of a buffer of storage dtype `dtype`.
+__device__ __forceinline__ void store_from_f(void* p, int64_t i, float v, int dtype) {
+  if (dtype == 1) ((bf16_t*)p)[i] = f2bf(v);
+  else if (dtype == 2) ((f16_t*)p)[i] = (f16_t)v;
+  else ((float*)p)[i] = v;
+}
 
 // ---------------------------------------------------------------------------
 // Tagged-word exchange between the work-groups of a persistent kernel.

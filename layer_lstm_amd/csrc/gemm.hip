@@ -14,12 +14,12 @@
 //
 // Tiles: 128 x 128 (or 64 x 64 when 128-wide tiles would leave compute units
 // idle) per 256-thread work-group, 4 waves in 2 x 2, 128 bytes of k per
-// stage (32 fp32 or 64 bf16), double-buffered in LDS; K is split when even
+// stage (32 fp32 or 64 bf16 / fp16), double-buffered in LDS; K is split when even
 // the smaller tiles cannot give every compute unit a tile.
 // Both operands sit in LDS as [row][k] with a 16-byte row pad; an operand
 // whose contiguous dimension is M or N is transposed in registers on its way
 // into LDS.  Accumulation is fp32 (v_mfma_f32_16x16x4f32 for fp32 storage,
-// v_mfma_f32_16x16x32_bf16 for bf16 storage).  Split-K partials are summed
+// v_mfma_f32_16x16x32_bf16 / _f16 for bf16 / fp16 storage).  Split-K partials are summed
 // by a second kernel in a fixed order, so results are run-to-run identical.
 #include "device_common.hpp"
 #include "internal.hpp"
@@ -200,6 +200,10 @@ __device__ __forceinline__ void store_row4(bf16_t* p, f32x4_t v) {
   const uint32_t hi = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
   *(uint2*)p = uint2{lo, hi};
 }
+__device__ __forceinline__ void store_row4(f16_t* p, f32x4_t v) {
+  const f16_t h[4] = {(f16_t)v[0], (f16_t)v[1], (f16_t)v[2], (f16_t)v[3]};
+  *(uint2*)p = __builtin_bit_cast(uint2, h);
+}
 __device__ __forceinline__ void store_row4(float* p, f32x4_t v) { *(f32x4_t*)p = v; }
 
 struct EpiP {  // fp32 P with bias in the interleaved column order
@@ -207,8 +211,8 @@ struct EpiP {  // fp32 P with bias in the interleaved column order
   float* P; const void* bias; int64_t H, ldp; int dtype; int ijfo; int two;
   __device__ __forceinline__ float bias_at(int64_t n) const {
     const int64_t r = gate_row(n, H, ijfo);
-    float v = dtype ? bf2f(((const bf16_t*)bias)[r]) : ((const float*)bias)[r];
-    if (two) v += dtype ? bf2f(((const bf16_t*)bias)[ldp + r]) : ((const float*)bias)[ldp + r];
+    float v = load_as_f(bias, r, dtype);
+    if (two) v += load_as_f(bias, ldp + r, dtype);
     return v;
   }
   __device__ __forceinline__ void operator()(int64_t m, int64_t n, float v) const {
@@ -254,9 +258,9 @@ struct GemmArgs {
   uint32_t* zero;     // extra duty: clear `zero_words` words here (may be null)
   int64_t zero_words;
   const float* dsum;  // extra duty: dsum_out[row(n)] = sum_r dsum[r][n] (r < dsum_rows)
-  void* dsum_out;     // (null = none); row(n) = gate-block order, storage type dsum_bf16
+  void* dsum_out;     // (null = none); row(n) = gate-block order, storage dtype dsum_dtype
   int dsum_rows;
-  int dsum_bf16;
+  int dsum_dtype;     // 0 fp32, 1 bf16, 2 fp16
   int64_t dsum_cols, dsum_H;
   int dsum_ijfo;      // gate-block order of dsum_out (gate_block)
   int dsum_two;       // dsum_out is [2][dsum_cols]: the sums written to both halves
@@ -315,8 +319,7 @@ __global__ void __launch_bounds__(kThreads) gemm_kernel(GemmArgs<AOp, BOp, Epi> 
         const int64_t row = gate_row(n, g.dsum_H, g.dsum_ijfo);
         for (int h = 0; h <= g.dsum_two; ++h) {
           const int64_t o = row + h * g.dsum_cols;
-          if (g.dsum_bf16) ((bf16_t*)g.dsum_out)[o] = f2bf(v);
-          else ((float*)g.dsum_out)[o] = v;
+          store_from_f(g.dsum_out, o, v, g.dsum_dtype);
         }
       }
     }
@@ -425,6 +428,9 @@ static_assert(kStages == 5, "the stage waits in gemm_lds_kernel assume a 5-stage
 
 template <typename T> struct LdsCfg;
 template <> struct LdsCfg<bf16_t> {
+  static constexpr int kTile = 256, kWaves = 8, kThreads = 512, kKStage = 32;
+};
+template <> struct LdsCfg<f16_t> {
   static constexpr int kTile = 256, kWaves = 8, kThreads = 512, kKStage = 32;
 };
 template <> struct LdsCfg<float> {
@@ -647,8 +653,7 @@ __global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_kernel(GemmAr
         const int64_t row = gate_row(n, g.dsum_H, g.dsum_ijfo);
         for (int h = 0; h <= g.dsum_two; ++h) {
           const int64_t o = row + h * g.dsum_cols;
-          if (g.dsum_bf16) ((bf16_t*)g.dsum_out)[o] = f2bf(v);
-          else ((float*)g.dsum_out)[o] = v;
+          store_from_f(g.dsum_out, o, v, g.dsum_dtype);
         }
       }
     }
@@ -1008,7 +1013,7 @@ static hipError_t launch_tile(GemmArgs<AOp, BOp, Epi>& g, hipStream_t s) {
 // Runs C = A . B through the epilogue; `part` must hold splits*M*N floats
 // when the shape splits K.  Optionally clears `zero_bytes` at `zero` in the
 // same launch (extra blocks), so that a buffer clear costs no launch.
-struct DbDuty { const float* src; void* out; int rows; int64_t cols, H; int bf16; int ijfo; int two; };
+struct DbDuty { const float* src; void* out; int rows; int64_t cols, H; int dtype; int ijfo; int two; };
 
 template <typename T, class AOp, bool AMN, class BOp, bool BMN, class Epi>
 static hipError_t run_gemm(const Plan& p, int64_t M, int64_t N, int64_t K, const AOp& a, const BOp& b,
@@ -1024,7 +1029,7 @@ static hipError_t run_gemm(const Plan& p, int64_t M, int64_t N, int64_t K, const
   int ktps = (int)((ktiles + gs.splits - 1) / gs.splits);
   if (ktps < 1) ktps = 1;
   GemmArgs<AOp, BOp, Epi> g{M, N, K, ktps, gs.splits, a, b, e, part, (uint32_t*)zero, (int64_t)(zero_bytes / 4),
-                            db.src, db.out, db.rows, db.bf16, db.cols, db.H, db.ijfo, db.two, p.nxcd};
+                            db.src, db.out, db.rows, db.dtype, db.cols, db.H, db.ijfo, db.two, p.nxcd};
   hipError_t err = gs.tile == 128 ? launch_tile<T, 4, 4, AOp, AMN, BOp, BMN, Epi>(g, s)
                                   : launch_tile<T, 2, 2, AOp, AMN, BOp, BMN, Epi>(g, s);
   if (err != hipSuccess || gs.splits == 1) return err;
@@ -1080,7 +1085,7 @@ static hipError_t run_gemm_lds(const Plan& p, int64_t M, int64_t N, int64_t K, c
   if (ktps < 1) ktps = 1;
   const int64_t tx = (N + TILE - 1) / TILE, ty = (M + TILE - 1) / TILE;
   GemmArgs<AOp, BOp, Epi> g{M, N, K, ktps, gs.splits, a, b, e, part, (uint32_t*)zero, (int64_t)(zero_bytes / 4),
-                            db.src, db.out, db.rows, db.bf16, db.cols, db.H, db.ijfo, db.two, p.nxcd, (int)tx, (int)ty, 1};
+                            db.src, db.out, db.rows, db.dtype, db.cols, db.H, db.ijfo, db.two, p.nxcd, (int)tx, (int)ty, 1};
   if constexpr (AMN == 0 && BMN == 0) {
     const int per_wg = g.dsum_out ? 1 : multi_tiles_per_wg<T>(p, M, N, K);
     if (per_wg > 1) {
@@ -1153,24 +1158,27 @@ static hipError_t dw_t(const Plan& p, const void* dG, const void* x, const void*
 }
 
 int inproj_tiles_per_wg(const Plan& p) {
-  if (p.dtype) return inproj_lds_ok<bf16_t>(p) ? multi_tiles_per_wg<bf16_t>(p, p.TB, p.G4, p.I) : 1;
+  if (p.esize == 2) return inproj_lds_ok<bf16_t>(p) ? multi_tiles_per_wg<bf16_t>(p, p.TB, p.G4, p.I) : 1;
   return inproj_lds_ok<float>(p) ? multi_tiles_per_wg<float>(p, p.TB, p.G4, p.I) : 1;
 }
 
 hipError_t launch_gemm_inproj(const Plan& p, const void* x, const void* W, const void* b, float* P, float* part,
                               void* zero, size_t zero_bytes, hipStream_t s) {
-  return p.dtype ? inproj_t<bf16_t>(p, x, W, b, P, part, zero, zero_bytes, s)
-                 : inproj_t<float>(p, x, W, b, P, part, zero, zero_bytes, s);
+  if (p.dtype == 1) return inproj_t<bf16_t>(p, x, W, b, P, part, zero, zero_bytes, s);
+  if (p.dtype == 2) return inproj_t<f16_t>(p, x, W, b, P, part, zero, zero_bytes, s);
+  return inproj_t<float>(p, x, W, b, P, part, zero, zero_bytes, s);
 }
 hipError_t launch_gemm_dx(const Plan& p, const void* dG, const void* W, void* dx, float* part, void* zero,
                           size_t zero_bytes, hipStream_t s) {
-  return p.dtype ? dx_t<bf16_t>(p, dG, W, dx, part, zero, zero_bytes, s)
-                 : dx_t<float>(p, dG, W, dx, part, zero, zero_bytes, s);
+  if (p.dtype == 1) return dx_t<bf16_t>(p, dG, W, dx, part, zero, zero_bytes, s);
+  if (p.dtype == 2) return dx_t<f16_t>(p, dG, W, dx, part, zero, zero_bytes, s);
+  return dx_t<float>(p, dG, W, dx, part, zero, zero_bytes, s);
 }
 hipError_t launch_gemm_dw(const Plan& p, const void* dG, const void* x, const void* h0, const void* y, void* dW,
                           float* part, void* zero, size_t zero_bytes, const float* DBP, void* db, hipStream_t s) {
-  return p.dtype ? dw_t<bf16_t>(p, dG, x, h0, y, dW, part, zero, zero_bytes, DBP, db, s)
-                 : dw_t<float>(p, dG, x, h0, y, dW, part, zero, zero_bytes, DBP, db, s);
+  if (p.dtype == 1) return dw_t<bf16_t>(p, dG, x, h0, y, dW, part, zero, zero_bytes, DBP, db, s);
+  if (p.dtype == 2) return dw_t<f16_t>(p, dG, x, h0, y, dW, part, zero, zero_bytes, DBP, db, s);
+  return dw_t<float>(p, dG, x, h0, y, dW, part, zero, zero_bytes, DBP, db, s);
 }
 
 // Bytes of fp32 split-K partials the three products need for this plan.
@@ -1180,7 +1188,7 @@ size_t gemm_partial_bytes(const Plan& p, int cus) {
   for (const auto& sh : shapes) {
     if (sh[0] <= 0 || sh[1] <= 0) continue;
     GemmShape gs = choose_shape(sh[0], sh[1], sh[2], p.esize, cus, p.max_splits);
-    const GemmShape gl = p.dtype ? choose_shape_lds<bf16_t>(sh[0], sh[1], sh[2], cus, p.max_splits)
+    const GemmShape gl = p.esize == 2 ? choose_shape_lds<bf16_t>(sh[0], sh[1], sh[2], cus, p.max_splits)
                                  : choose_shape_lds<float>(sh[0], sh[1], sh[2], cus, p.max_splits);
     if (gl.splits > gs.splits) gs = gl;
     if (gs.splits > 1) {

@@ -17,7 +17,7 @@ constexpr int kStampWGs = 8, kPhases = 6;
 // Work partition and workspace layout of one problem shape.
 struct Plan {
   int64_t T, B, I, H;
-  int dtype;   // 0 = fp32, 1 = bf16
+  int dtype;   // 0 = fp32, 1 = bf16, 2 = fp16 (storage)
   int esize;   // bytes per storage element
   int64_t TB, G4, Z;  // T*B, 4H, H+I
 

@@ -32,7 +32,7 @@ static int device_cus(int* cus) {
 
 int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
   if (T < 0 || B < 0 || I < 0 || H <= 0) return LSTM_ERR_DIMS;
-  if (dtype != LSTM_F32 && dtype != LSTM_BF16) return LSTM_ERR_DTYPE;
+  if (dtype != LSTM_F32 && dtype != LSTM_BF16 && dtype != LSTM_F16) return LSTM_ERR_DTYPE;
   if (H > 2048 || I > 65536 || T > ((int64_t)1 << 30)) return LSTM_ERR_UNSUPPORTED;
   if (T > 0 && B > 0 && T * B > ((int64_t)1 << 31) / (4 * H)) return LSTM_ERR_UNSUPPORTED;
   if (B * H >= ((int64_t)1 << 27)) return LSTM_ERR_UNSUPPORTED;  // per-step buffer offsets fit 31 bits
@@ -42,10 +42,10 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
 
   memset(p, 0, sizeof(*p));
   p->T = T; p->B = B; p->I = I; p->H = H; p->dtype = dtype;
-  p->esize = dtype ? 2 : 4;
+  p->esize = dtype == LSTM_F32 ? 4 : 2;
   p->TB = T * B; p->G4 = 4 * H; p->Z = H + I;
   const int e = p->esize;
-  const int KB = dtype ? 32 : 16;                       // MFMA k-block (elements)
+  const int KB = e == 2 ? 32 : 16;                      // MFMA k-block (elements)
   // H padded to a power of two, at least one k-block per wave
   int Hp = 4 * KB;
   while (Hp < H) Hp *= 2;
@@ -57,7 +57,7 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
   // Partition of the persistent kernels.  Every work-group reads NB*H
   // values of h (forward) and NB*4H gate deltas (backward) per step, so the
   // fewest batch rows per group that still fit the grid come first, then
-  // the most work-groups, then 4 waves before 8 (8 waves -- bf16 only -- hold
+  // the most work-groups, then 4 waves before 8 (8 waves -- 16-bit storage only -- hold
   // twice the W_h slice).  A first pass takes only partitions whose batch
   // groups divide evenly over the XCDs, so that each group's exchange stays
   // in one XCD's L2.  Fewer than 16 rows leave part of the 16-row MFMA batch
@@ -71,7 +71,7 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
       for (int c = 0; c < 3 && !found; ++c) {
         for (int d = 0; d < 2 && !found; ++d) {
           const int NB = nb_opts[a], NJ = nj_opts[c], NW = nw_opts[d];
-          if (NW == 8 && !dtype) continue;
+          if (NW == 8 && e == 4) continue;
           const int64_t nBG = B > 0 ? (B + NB - 1) / NB : 1;
           const int64_t nJG = (H + NJ - 1) / NJ;
           if (nBG * nJG > cus) continue;
@@ -98,7 +98,7 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
           // W_h values per lane) or the MFMA kernel: 16-unit tiles of W_h^T,
           // the waves splitting the 4H gate rows
           const int vnct = Hp <= kRecThreads ? 1 : Hp / kRecThreads;
-          const bool valu = !dtype && NB == 4 && NW == 4 && ((NJ == 8 && vnct <= 4) || (NJ == 16 && vnct == 1));
+          const bool valu = e == 4 && NB == 4 && NW == 4 && ((NJ == 8 && vnct <= 4) || (NJ == 16 && vnct == 1));
           const int MTb = NJ < 16 ? 1 : NJ / 16;
           const int nkb = Hp * e / (16 * NW);
           size_t lds_b;
@@ -128,7 +128,7 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
   if (!found) return LSTM_ERR_UNSUPPORTED;
   p->Bp = p->nBG * p->NB;
   {
-    const int64_t fw = (int64_t)p->NB * (dtype ? Hp / 2 : Hp);         // forward words per work-group
+    const int64_t fw = (int64_t)p->NB * (e == 2 ? Hp / 2 : Hp);        // forward words per work-group
     const int64_t bw = (int64_t)p->nJG * p->NB * p->NJ;                // backward words per work-group
     const int64_t mx = fw > bw ? fw : bw;
     p->words_per_thread = (int)((mx + 255) / 256);
@@ -140,7 +140,7 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
   p->max_splits = 8;
   p->xcd_local = p->nxcd > 1 && p->nBG % p->nxcd == 0;
 
-  const size_t HW = dtype ? (size_t)p->Hp / 2 : (size_t)p->Hp;
+  const size_t HW = e == 2 ? (size_t)p->Hp / 2 : (size_t)p->Hp;
   // HX: tagged words [2][Bp][HW] (VALU forward), or packed h [2][Bp][Hp] +
   // flags [nBG][nJG]; PX: tagged words [2][nBG][nJG][Hp][NB] (VALU
   // backward), or gate deltas in 16-row tiles [2][nBG][max(NB,16)][4Hp] +

@@ -543,7 +543,7 @@ static hipError_t fwd_dispatch_c(const Plan& p, FwdArgs& a, hipStream_t s) {
 // The ring is copied into LDS by direct-to-LDS loads when every row holds a
 // multiple of 64 16-byte chunks (H * E a multiple of 1 KB), else through
 // registers, 4 chunks in flight per thread and round.  8-wave work-groups
-// are bf16 only.
+// have 16-bit storage only.
 template <typename T, int NBT>
 static hipError_t fwd_dispatch(const Plan& p, FwdArgs& a, hipStream_t s) {
   const bool dma = p.fwd_dma != 0;
@@ -559,13 +559,17 @@ hipError_t launch_fwd_recurrent(const Plan& p, const float* P, const void* W, co
   char* hd = (char*)HX;  // the packed ring and its flags share the tagged-word region
   FwdArgs a{P, W, h0, c0, y, hT, cT, Gs, Cs, HX, hd, (uint32_t*)(hd + p.off_hflags), (uint32_t)p.off_hflags, err,
             stamps, (int)p.T, (int)p.B, (int)p.H, (int)p.Z, p.NB, p.NJ,
-            p.nJG, p.Hp, p.Bp, p.dtype ? (p.Hp / 2) : p.Hp, p.nBG, p.nxcd, p.xcd_local, p.rev, p.ijfo};
+            p.nJG, p.Hp, p.Bp, p.esize == 2 ? (p.Hp / 2) : p.Hp, p.nBG, p.nxcd, p.xcd_local, p.rev, p.ijfo};
   if (fwd_vec_ok(p)) return launch_fwd_vec(p, a, s);
   const int nbt = p.NB < 16 ? 1 : p.NB / 16;
-  if (p.dtype) {
+  if (p.dtype == 1) {
     if (nbt == 1) return fwd_dispatch<bf16_t, 1>(p, a, s);
     if (nbt == 2) return fwd_dispatch<bf16_t, 2>(p, a, s);
     if (nbt == 4) return fwd_dispatch<bf16_t, 4>(p, a, s);
+  } else if (p.dtype == 2) {
+    if (nbt == 1) return fwd_dispatch<f16_t, 1>(p, a, s);
+    if (nbt == 2) return fwd_dispatch<f16_t, 2>(p, a, s);
+    if (nbt == 4) return fwd_dispatch<f16_t, 4>(p, a, s);
   } else {
     if (nbt == 1) return fwd_dispatch<float, 1>(p, a, s);
     if (nbt == 2) return fwd_dispatch<float, 2>(p, a, s);

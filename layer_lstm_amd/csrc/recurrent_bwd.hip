@@ -303,7 +303,8 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
       if constexpr (E == 4) {
         gi = __uint_as_float(gw[0]); gf = __uint_as_float(gw[1]); gg = __uint_as_float(gw[2]); go = __uint_as_float(gw[3]);
       } else {
-        gi = bf2f((bf16_t)gw[0]); gf = bf2f((bf16_t)(gw[0] >> 16)); gg = bf2f((bf16_t)gw[1]); go = bf2f((bf16_t)(gw[1] >> 16));
+        gi = f_of_bits16<T>(gw[0]); gf = f_of_bits16<T>(gw[0] >> 16);
+        gg = f_of_bits16<T>(gw[1]); go = f_of_bits16<T>(gw[1] >> 16);
       }
       if (t == 0) cprev = (own[s] && a.c0) ? ldf<T>(a.c0, c_off(s)) : 0.f;
       const float tc = tanh_f(c);
@@ -432,7 +433,8 @@ static hipError_t bwd_col_def(const Plan& p, BwdArgs& a, hipStream_t s) {
 
 hipError_t launch_bwd_col(const Plan& p, BwdArgs& a, hipStream_t s) {
   if (p.NB * p.NJ > 1024) return hipErrorInvalidValue;
-  if (p.dtype) return p.waves == 8 ? bwd_col_def<bf16_t, 8>(p, a, s) : bwd_col_def<bf16_t, kWaves>(p, a, s);
+  if (p.dtype == 1) return p.waves == 8 ? bwd_col_def<bf16_t, 8>(p, a, s) : bwd_col_def<bf16_t, kWaves>(p, a, s);
+  if (p.dtype == 2) return p.waves == 8 ? bwd_col_def<f16_t, 8>(p, a, s) : bwd_col_def<f16_t, kWaves>(p, a, s);
   if (p.waves != kWaves) return hipErrorInvalidValue;
   return bwd_col_def<float, kWaves>(p, a, s);
 }

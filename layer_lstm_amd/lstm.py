@@ -26,7 +26,7 @@ REVERSE = 1  # lstm_shape.flags: the reverse direction of time
 GATES_IJFO = 2  # lstm_shape.flags: W/b/dW/db row blocks in the gate order i, g, f, o
 TWO_BIAS = 4  # lstm_shape.flags: b and db are [2][4H] (b_ih, b_hh)
 GATE_I, GATE_F, GATE_G, GATE_O = 0, 1, 2, 3
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 OK = 0
 STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_DIMS", -3: "ERR_DTYPE", -4: "ERR_ALIGN",
           -5: "ERR_WORKSPACE", -6: "ERR_UNSUPPORTED", -7: "ERR_COOP", -8: "ERR_LAUNCH",
@@ -95,7 +95,7 @@ def status_string(code: int) -> str:
 
 
 def torch_dtype(dtype: int):
-    return torch.float32 if dtype == F32 else torch.bfloat16
+    return {F32: torch.float32, BF16: torch.bfloat16, F16: torch.float16}[dtype]
 
 
 def make_shape(T, B, I, H, dtype, reverse=False, gate_order="ifjo", two_bias=False) -> Shape:

@@ -12,7 +12,8 @@ Recipe
   where ``s`` is the standard deviation;
 * draws are fp64, then rounded to the storage dtype: fp32 by numpy's
   round-to-nearest-even cast, bf16 by rounding that fp32 value to the nearest
-  bf16 (ties to even) with integer arithmetic on the bit pattern.  Both sides
+  bf16 (ties to even) with integer arithmetic on the bit pattern, f16 by
+  numpy's fp32 -> fp16 cast of that fp32 value (nearest, ties to even).  Both sides
   of every comparison consume exactly these stored values (the oracle upcast
   to fp64).
 
@@ -32,7 +33,7 @@ TENSOR_IDS = dict(W=0, b=1, x=2, h0=3, c0=4, dy=5, dhT=6, dcT=7)
 @dataclass(frozen=True)
 class Workload:
     name: str
-    dtype: str  # "f32" or "bf16" (storage); accumulation is always fp32
+    dtype: str  # "f32", "bf16" or "f16" (storage); accumulation is always fp32
     T: int
     B: int
     I: int
@@ -67,6 +68,12 @@ WORKLOADS = {
     "bf16_T256_B256_I1024_H1024": Workload("bf16_T256_B256_I1024_H1024", "bf16", 256, 256, 1024, 1024,
                                            _std(1024, dy="n.1")),
 }
+# fp16 storage (the FLOAT16 of the operator page's dtype column) on the
+# shapes and distributions of the three bf16 workloads
+for _n in [n for n in WORKLOADS if n.startswith("bf16_")]:
+    _w = WORKLOADS[_n]
+    _f = "f16_" + _n[len("bf16_"):]
+    WORKLOADS[_f] = Workload(_f, "f16", _w.T, _w.B, _w.I, _w.H, _w.dist)
 SMALL = "f32_T8_B4_I16_H32"
 # the benchmark's default: the largest workload that fits one GPU
 HEADLINE = "bf16_T256_B256_I1024_H1024"
@@ -96,6 +103,8 @@ def round_to_storage(a64: np.ndarray, dtype: str) -> np.ndarray:
         return a32.astype(np.float64)
     if dtype == "bf16":
         return bf16_bits_to_f32(f32_to_bf16_bits(a32)).astype(np.float64)
+    if dtype == "f16":
+        return a32.astype(np.float16).astype(np.float64)
     raise ValueError(dtype)
 
 

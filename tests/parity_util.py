@@ -3,7 +3,12 @@ the device, run the HIP path through the C-ABI binding, and compare with the
 fp64 oracle by relative L2 norm per output tensor."""
 import numpy as np
 
-TOL = {"f32": 1e-5, "bf16": 2e-2}
+# Relative L2 bounds per storage type: fp32 1e-5 and bf16 (fp32 accumulation)
+# 2e-2 as stated for the method; fp16 takes bf16's bound scaled by the ratio
+# of the two unit roundoffs (2^-11 / 2^-8), since the error comes from
+# rounding the stored operands (inputs, gates, gate deltas, h) to the
+# storage type.
+TOL = {"f32": 1e-5, "bf16": 2e-2, "f16": 2.5e-3}
 OUTPUTS = ("y", "hT", "cT", "dx", "dW", "db", "dh0", "dc0")
 
 
@@ -18,7 +23,7 @@ def rel_l2(got, ref):
 def to_dev(a, dtype, torch):
     if a is None:
         return None
-    td = torch.float32 if dtype == "f32" else torch.bfloat16
+    td = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[dtype]
     # stored values are exactly representable in the storage type
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda").to(td)
 
@@ -32,7 +37,7 @@ def run_gpu(inp, lstm, torch, want_db=True, stream=None, poison=False):
     outputs.  poison: fill every output buffer with NaN first, so that an
     output the library fails to write shows up."""
     T, B, I, H, dt = inp["T"], inp["B"], inp["I"], inp["H"], inp["dtype"]
-    code = lstm.F32 if dt == "f32" else lstm.BF16
+    code = {"f32": lstm.F32, "bf16": lstm.BF16, "f16": lstm.F16}[dt]
     m = lstm.Lstm(T, B, I, H, code, reverse=bool(inp.get("reverse", False)),
                   gate_order=inp.get("gate_order", "ifjo"), two_bias=bool(inp.get("two_bias", False)))
     if poison:

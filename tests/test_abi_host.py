@@ -43,6 +43,7 @@ def test_constants_match_header(lstm):
     for g, v in (("LSTM_GATE_I", 0), ("LSTM_GATE_F", 1), ("LSTM_GATE_G", 2), ("LSTM_GATE_O", 3)):
         assert header_enum(g) == v
     assert header_enum("LSTM_F32") == lstm.F32 and header_enum("LSTM_BF16") == lstm.BF16
+    assert header_enum("LSTM_F16") == lstm.F16
     assert header_enum("LSTM_REVERSE") == lstm.REVERSE
     assert header_enum("LSTM_GATES_IJFO") == lstm.GATES_IJFO
     assert header_enum("LSTM_TWO_BIAS") == lstm.TWO_BIAS

@@ -58,7 +58,7 @@ def say(*a):
 
 
 def full_check(inp, lstm, tol=None):
-    code = lstm.F32 if inp["dtype"] == "f32" else lstm.BF16
+    code = {"f32": lstm.F32, "bf16": lstm.BF16, "f16": lstm.F16}[inp["dtype"]]
     say("plan:", lstm.query_plan(lstm.make_shape(inp["T"], inp["B"], inp["I"], inp["H"], code)))
     ref = oracle.fwd_bwd(inp)
     out, _, _ = run_gpu(inp, lstm, torch, poison=True)
@@ -217,7 +217,7 @@ FULL_PARITY = os.environ.get("LSTM_FULL_PARITY") == "1"
 # H+I columns), so its rounding error spreads wider than the whole tensor's
 # (bf16 rows reach 2-4e-2 where the tensors sit at 5e-3), while a corrupted,
 # stale or unwritten row is off by about its own size (a ratio near 1).
-ROW_TOL = {"f32": 5e-5, "bf16": 1e-1}
+ROW_TOL = {"f32": 5e-5, "bf16": 1e-1, "f16": 1.25e-2}
 
 
 def rows_of(inp, rows):
@@ -286,21 +286,22 @@ def test_bf16_workload_full_batch(lstm, big_runs, name, progress):
     assert not bad_rows, bad_rows
 
 
-def test_bf16_largest_workload_every_group(lstm, big_runs, progress):
-    """T=256 B=256 I=1024 H=1024 at full size: the first and last batch row
-    of each of the eight 32-row batch groups against the oracle on those 16
-    rows (whole and row by row), and dW, db from a second backward whose
-    cotangents are zero outside those rows."""
-    inp, out, m, d = big_runs[LARGEST]
-    nb = lstm.query_plan(lstm.make_shape(inp["T"], inp["B"], inp["I"], inp["H"], lstm.BF16))["rows_per_group"]
+def check_every_group(lstm, inp, out, m, d, progress):
+    """The first and last batch row of each batch group of the recurrences'
+    layout against the oracle on those rows (whole and row by row), and dW,
+    db from a second backward on `m` whose cotangents are zero outside those
+    rows (every other row's gate deltas are then exactly zero)."""
+    dt = inp["dtype"]
+    code = {"f32": lstm.F32, "bf16": lstm.BF16, "f16": lstm.F16}[dt]
+    nb = lstm.query_plan(lstm.make_shape(inp["T"], inp["B"], inp["I"], inp["H"], code))["rows_per_group"]
     rows = sorted({r for g0 in range(0, inp["B"], nb) for r in (g0, min(inp["B"], g0 + nb) - 1)})
-    progress(f"case: every batch group of {LARGEST}, rows {rows}")
+    progress(f"  rows {rows}")
     ref = oracle.fwd_bwd(rows_of(inp, rows))
     keys = ("y", "hT", "cT", "dx", "dh0", "dc0")
     got = dict(y=out["y"][:, rows], hT=out["hT"][rows], cT=out["cT"][rows], dx=out["dx"][:, rows],
                dh0=out["dh0"][rows], dc0=out["dc0"][rows])
-    errs, bad = compare(got, ref, "bf16", keys=keys)
-    worst, bad_rows = compare_rows(got, ref, ROW_TOL["bf16"], keys=keys)
+    errs, bad = compare(got, ref, dt, keys=keys)
+    worst, bad_rows = compare_rows(got, ref, ROW_TOL[dt], keys=keys)
     progress("  rel-L2: " + str({k: f"{v:.2e}" for k, v in errs.items()}))
     progress("  worst row: " + str({k: f"{v:.2e}" for k, v in worst.items()}))
     assert not bad and not bad_rows, (bad, bad_rows)
@@ -309,18 +310,27 @@ def test_bf16_largest_workload_every_group(lstm, big_runs, progress):
     masked = dict(inp, dy=inp["dy"] * mask[None, :, None])
     for k in ("dhT", "dcT"):
         masked[k] = None if inp[k] is None else inp[k] * mask[:, None]
-    dm = {k: to_dev(masked[k], "bf16", torch) for k in ("dy", "dhT", "dcT")}
+    dm = {k: to_dev(masked[k], dt, torch) for k in ("dy", "dhT", "dcT")}
     m.forward(d["x"], d["W"], d["b"], d["h0"], d["c0"])
     m.backward(dm["dy"], dm["dhT"], dm["dcT"], d["x"], d["W"], d["h0"], d["c0"])
     m.check()
     torch.cuda.synchronize()
     refm = oracle.fwd_bwd(rows_of(masked, rows))
     gotm = {"dW": to_host(m.dW), "db": to_host(m.db)}
-    errs, bad = compare(gotm, refm, "bf16", keys=("dW", "db"))
-    worst, bad_rows = compare_rows(gotm, refm, ROW_TOL["bf16"], keys=("dW", "db"))
+    errs, bad = compare(gotm, refm, dt, keys=("dW", "db"))
+    worst, bad_rows = compare_rows(gotm, refm, ROW_TOL[dt], keys=("dW", "db"))
     progress("  masked dW/db rel-L2: " + str({k: f"{v:.2e}" for k, v in errs.items()}) +
              " worst row: " + str({k: f"{v:.2e}" for k, v in worst.items()}))
     assert not bad and not bad_rows, (bad, bad_rows)
+
+
+def test_bf16_largest_workload_every_group(lstm, big_runs, progress):
+    """T=256 B=256 I=1024 H=1024 at full size: the first and last batch row
+    of each of the eight 32-row batch groups, and the masked dW, db
+    (check_every_group)."""
+    inp, out, m, d = big_runs[LARGEST]
+    progress(f"case: every batch group of {LARGEST}")
+    check_every_group(lstm, inp, out, m, d, progress)
 
 
 def test_bf16_determinism_full_size(lstm, big_runs):
@@ -610,3 +620,46 @@ def test_two_streams_concurrent(lstm):
         out = {k: to_host(getattr(m, k)) for k in ("y", "hT", "cT", "dx", "dW", "db", "dh0", "dc0")}
         errs, bad = compare(out, ref, "f32")
         assert not bad, bad
+
+
+# ---------------------------------------------------------------------------
+# fp16 storage (LSTM_F16: the FLOAT16 of the operator page's dtype column)
+# through every kernel variant on ragged shapes, and at the three 16-bit
+# workload shapes at full size, against the oracle on the same fp16-rounded
+# inputs within the fp16 bound (parity_util.TOL).
+
+@pytest.mark.parametrize("T,B,I,H,rev", [
+    (4, 19, 40, 72, False),
+    (3, 5, 7, 33, False),      # odd hidden size
+    (3, 5, 24, 512, False),    # 4-row groups, the forward's direct-to-LDS path
+    (2, 100, 64, 512, True),   # 8-row groups, 32 units, 8 waves; reverse
+    (3, 60, 32, 512, False),   # 8 batch groups (one per XCD)
+    (5, 40, 64, 1024, False),
+])
+def test_f16_ragged_shapes(lstm, T, B, I, H, rev):
+    say(f"case: f16 T={T} B={B} I={I} H={H} reverse={rev}")
+    inp = dict(synth.make_inputs(T, B, I, H, "f16", seed=83, dist=ALL), reverse=rev)
+    full_check(inp, lstm)
+
+
+def test_f16_all_flags(lstm):
+    """fp16 with the "ijfo" gate order and two biases."""
+    say("case: f16 ijfo, two biases")
+    inp = two_bias_inputs("f16", 3, 60, 32, 512, 85)
+    inp.update(gate_order="ijfo")
+    full_check(inp, lstm)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["f16_T128_B64_I512_H1024", "f16_T512_B16_I1024_H2048",
+                                  "f16_T256_B256_I1024_H1024"])
+def test_f16_workload_every_group(lstm, name, progress):
+    """The 16-bit workload shapes in fp16 at full size, in the benchmark's
+    launch configuration: every batch group's first and last row and the
+    masked dW, db against the oracle (check_every_group)."""
+    progress(f"case: fp16 full size {name}")
+    inp = synth.workload_inputs(name)
+    out, m, d = run_gpu(inp, lstm, torch, poison=True)
+    for k, v in out.items():
+        assert np.all(np.isfinite(v)), k
+    check_every_group(lstm, inp, out, m, d, progress)
