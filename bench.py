@@ -2,7 +2,7 @@
 """Benchmark of the single-layer LSTM forward + BPTT on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--reverse]
-                    [--gate-order ifjo|ijfo] [--two-bias]
+                    [--gate-order ifjo|ijfo] [--two-bias] [--bidirectional] [--lengths none|ragged]
 
 The default workload is the largest one that fits one GPU,
 bf16_T256_B256_I1024_H1024 (T=256, B=256, I=1024, H=1024, bf16 storage with
@@ -17,7 +17,10 @@ kernel that takes the most time, and the fp64 CPU oracle timed on the host
 on a bounded sample of the same workload.  --reverse runs the reverse
 direction of time (lstm_shape.flags = LSTM_REVERSE), --gate-order ijfo the
 other gate order of W's row blocks (LSTM_GATES_IJFO), --two-bias two bias
-vectors (LSTM_TWO_BIAS; the second one seeded like the first), on the same
+vectors (LSTM_TWO_BIAS; the second one the first reversed), --bidirectional
+both directions of time (LSTM_BIDIRECTIONAL; effective FLOPs counted for both),
+--lengths ragged seeded sequence lengths (seq_length; the FLOPs counted are
+those of the full T steps, which the products still run), on the same
 workload.
 """
 from __future__ import annotations
@@ -54,7 +57,9 @@ def kernel_work(w, kind, plan=None):
         return 2.0 * TB * 4 * H * I, "flop", "mfma"
     if kind in ("forward_recurrence", "backward_recurrence"):
         key = "fwd_valu" if kind == "forward_recurrence" else "bwd_valu"
-        return 2.0 * TB * 4 * H * H, "flop", "alu" if plan and plan[key] else "mfma"
+        # a bidirectional layer's concurrent launch runs both directions
+        nd = 2 if plan and plan.get("directions_concurrent") else 1
+        return nd * 2.0 * TB * 4 * H * H, "flop", "alu" if plan and plan[key] else "mfma"
     if kind == "dW_product":
         return 2.0 * TB * 4 * H * (H + I), "flop", "mfma"
     if kind == "dx_product":
@@ -101,7 +106,7 @@ def cpu_model():
     return None
 
 
-def cpu_baseline(w, inp, budget_s, reverse=False, gate_order="ifjo", two_bias=False):
+def cpu_baseline(w, inp, budget_s, reverse=False, gate_order="ifjo", two_bias=False, bidirectional=False):
     """Time the fp64 oracle (as it stands) on a bounded sample of the same
     workload: whole sequences (batch rows), as many as fit in about
     `budget_s` seconds by a one-row probe; when the whole batch takes less,
@@ -109,11 +114,13 @@ def cpu_baseline(w, inp, budget_s, reverse=False, gate_order="ifjo", two_bias=Fa
     from oracle import oracle
 
     def rows(n):
-        sub = dict(inp, B=n, reverse=reverse, gate_order=gate_order, two_bias=two_bias)
+        sub = dict(inp, B=n, reverse=reverse, gate_order=gate_order, two_bias=two_bias, bidirectional=bidirectional)
         for k in ("x", "dy"):
             sub[k] = inp[k][:, :n]
         for k in ("h0", "c0", "dhT", "dcT"):
-            sub[k] = None if inp[k] is None else inp[k][:n]
+            sub[k] = None if inp[k] is None else (inp[k][:, :n] if bidirectional else inp[k][:n])
+        if inp.get("lengths") is not None:
+            sub["lengths"] = inp["lengths"][:n]
         return sub
 
     t0 = time.perf_counter()
@@ -145,6 +152,10 @@ def main():
     ap.add_argument("--reverse", action="store_true", help="the reverse direction of time")
     ap.add_argument("--gate-order", default="ifjo", choices=("ifjo", "ijfo"), help="row-block order of W, b, dW, db")
     ap.add_argument("--two-bias", action="store_true", help="two bias vectors (b_ih, b_hh)")
+    ap.add_argument("--bidirectional", action="store_true",
+                    help="both directions of time (the second direction's tensors seeded with seed 1)")
+    ap.add_argument("--lengths", default="none", choices=("none", "ragged"),
+                    help="sequence lengths: none, or ragged (seeded, uniform over 1..T)")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (for scaling rocprofv3 byte counters)")
     args = ap.parse_args()
@@ -165,8 +176,15 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     inp = synth.workload_inputs(w.name)
+    if args.bidirectional:
+        other = synth.workload_inputs(w.name, seed=1)
+        inp["dy"] = np.concatenate([inp["dy"], other["dy"]], axis=2)
+        for k in ("W", "b", "h0", "c0", "dhT", "dcT"):
+            inp[k] = None if inp[k] is None else np.stack([inp[k], other[k]])
     if args.two_bias:
-        inp["b"] = np.stack([inp["b"], inp["b"][::-1].copy()])
+        inp["b"] = np.stack([inp["b"], inp["b"][..., ::-1].copy()], axis=-2)
+    if args.lengths == "ragged":
+        inp["lengths"] = np.random.default_rng([0, 8]).integers(1, w.T + 1, size=w.B).astype(np.int32)
     code = {"f32": lstm.F32, "bf16": lstm.BF16, "f16": lstm.F16}[w.dtype]
     td = lstm.torch_dtype(code)
     dev = torch.device("cuda:0")
@@ -175,11 +193,13 @@ def main():
         return None if a is None else torch.from_numpy(np.asarray(a, dtype=np.float32)).to(dev).to(td)
 
     d = {k: put(inp[k]) for k in ("x", "W", "b", "h0", "c0", "dy", "dhT", "dcT")}
-    m = lstm.Lstm(w.T, w.B, w.I, w.H, code, reverse=args.reverse, gate_order=args.gate_order, two_bias=args.two_bias)
+    lens = None if inp.get("lengths") is None else torch.from_numpy(inp["lengths"]).to(dev)
+    m = lstm.Lstm(w.T, w.B, w.I, w.H, code, reverse=args.reverse, gate_order=args.gate_order, two_bias=args.two_bias,
+                  bidirectional=args.bidirectional)
 
     def step():
-        m.forward(d["x"], d["W"], d["b"], d["h0"], d["c0"])
-        m.backward(d["dy"], d["dhT"], d["dcT"], d["x"], d["W"], d["h0"], d["c0"])
+        m.forward(d["x"], d["W"], d["b"], d["h0"], d["c0"], seq_length=lens)
+        m.backward(d["dy"], d["dhT"], d["dcT"], d["x"], d["W"], d["h0"], d["c0"], seq_length=lens)
 
     log(f"workload {w.name}{' (reverse)' if args.reverse else ''}: warmup {args.warmup}, steps {args.steps}")
     for _ in range(args.warmup):
@@ -221,7 +241,7 @@ def main():
     dom = max(kinds, key=lambda k: kt[k][0])
     tot, n = kt[dom]
     avg_s = tot / n / 1e3
-    plan = lstm.query_plan(lstm.make_shape(w.T, w.B, w.I, w.H, code))
+    plan = lstm.query_plan(lstm.make_shape(w.T, w.B, w.I, w.H, code, bidirectional=args.bidirectional))
     work, unit, bound = kernel_work(w, dom, plan)
     if unit == "flop":
         achieved = work / avg_s / 1e12
@@ -232,7 +252,8 @@ def main():
     roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": runit,
                 "frac": round(achieved / peak, 5),
                 # (the counter runs are of the forward direction, default gate order, one bias)
-                "traffic": None if (args.reverse or args.gate_order != "ifjo" or args.two_bias)
+                "traffic": None if (args.reverse or args.gate_order != "ifjo" or args.two_bias or
+                                    args.bidirectional or args.lengths != "none")
                 else traffic_for(w.name, dom),
                 "kernel": dom, "avg_launch_us": round(avg_s * 1e6, 2)}
 
@@ -249,7 +270,7 @@ def main():
     rec_us = {k: round(kt[k][0] / kt[k][1] * 1e3, 2) for k in ("forward_recurrence", "backward_recurrence")
               if kt.get(k, (0, 0))[1]}
 
-    flops = w.flops
+    flops = w.flops * (2 if args.bidirectional else 1)
     value = w.B / (ms / 1e3)
     eff_tflops = flops / (ms / 1e3) / 1e12
     out = {
@@ -260,6 +281,7 @@ def main():
         "config": {"workload": w.name, "T": w.T, "B": w.B, "I": w.I, "H": w.H, "storage": w.dtype,
                    "direction": "reverse" if args.reverse else "forward", "gate_order": args.gate_order,
                    "biases": 2 if args.two_bias else 1,
+                   "bidirectional": args.bidirectional, "lengths": args.lengths,
                    "parallelism": "single GPU"},
         "effective_tflops": round(eff_tflops, 3),
         "fraction_of_peak": round(eff_tflops / PEAK_TFLOPS[w.dtype], 5),
@@ -271,7 +293,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
-        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, args.reverse, args.gate_order, args.two_bias)
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, args.reverse, args.gate_order, args.two_bias,
+                                           args.bidirectional)
     print(json.dumps(out), flush=True)
 
 

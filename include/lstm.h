@@ -1,7 +1,7 @@
 /*
  * lstm.h -- C ABI of liblstm.so: forward pass and backpropagation through
- * time of a single-layer, unidirectional LSTM on one AMD Instinct MI355X
- * (gfx950), written in HIP.
+ * time of a single-layer LSTM (one direction of time, either one, or both:
+ * LSTM_BIDIRECTIONAL) on one AMD Instinct MI355X (gfx950), written in HIP.
  *
  * What is computed (the "SingleLayerLstmGrad" operator page, Ascend CANN
  * ops-nn: forward-formula table "前向传播公式" and the backward recursion
@@ -64,7 +64,7 @@
 extern "C" {
 #endif
 
-#define LSTM_ABI_VERSION 2
+#define LSTM_ABI_VERSION 3
 
 /* Gate row blocks of W, b, dW, db (the "ifjo" order of the page's
  * gate_order attribute; LSTM_GATES_IJFO below selects "ijfo"). */
@@ -112,17 +112,31 @@ enum { LSTM_GATES_IJFO = 2 };
  * both halves (the two enter the pre-activation alike). */
 enum { LSTM_TWO_BIAS = 4 };
 
-/* Problem shape.  dtype is LSTM_F32, LSTM_BF16 or LSTM_F16; flags is 0 or an OR of
- * LSTM_REVERSE, LSTM_GATES_IJFO and LSTM_TWO_BIAS, other bits must be 0
- * (else LSTM_ERR_DTYPE).  The forward call and the backward call of one
- * record take the same flags. */
+/* Bidirectional layer (the bidirectional recurrent layer of the PyTorch
+ * recurrent-layer page; num_directions = 2): direction 0 runs forward in
+ * time and direction 1 in reverse, each with its own weights and initial
+ * state, on the same x.  With this flag
+ *   W, dW [2][4H][H+I]    b, db [2][4H] (or [2][2][4H] with LSTM_TWO_BIAS)
+ *   h0, c0, hT, cT, dhT, dcT, dh0, dc0 [2][B][H]   (direction-major)
+ *   y, dy [T][B][2H]      (h_t of direction 0, then of direction 1)
+ *   x, dx [T][B][I]       (dx: the sum of both directions' input gradients)
+ * Not combinable with LSTM_REVERSE (else LSTM_ERR_DTYPE).  The two
+ * recurrences run in one launch on half the compute units each when the
+ * shape's layout fits that, else one after the other
+ * (lstm_plan_info.directions_concurrent). */
+enum { LSTM_BIDIRECTIONAL = 8 };
+
+/* Problem shape.  dtype is LSTM_F32, LSTM_BF16 or LSTM_F16; flags is 0 or an
+ * OR of LSTM_REVERSE, LSTM_GATES_IJFO, LSTM_TWO_BIAS and LSTM_BIDIRECTIONAL,
+ * other bits must be 0 (else LSTM_ERR_DTYPE).  The forward call and the
+ * backward call of one record take the same flags. */
 typedef struct {
   int64_t T; /* time steps, >= 0 */
   int64_t B; /* batch, >= 0 */
   int64_t I; /* input size, >= 0 */
   int64_t H; /* hidden size, >= 1 */
   int32_t dtype;
-  int32_t flags; /* an OR of LSTM_REVERSE, LSTM_GATES_IJFO, LSTM_TWO_BIAS, or 0 */
+  int32_t flags; /* an OR of the LSTM_REVERSE .. LSTM_BIDIRECTIONAL flags, or 0 */
 } lstm_shape;
 
 /* LSTM_ABI_VERSION of the library. */
@@ -158,17 +172,33 @@ typedef struct {
   int32_t inproj_tiles_per_wg; /* input projection: output tiles per work-group
                                   (> 1: persistent work-groups, one per CU;
                                   16-byte aligned x and W assumed) */
-  int32_t reserved[6];
+  int32_t directions_concurrent; /* LSTM_BIDIRECTIONAL: 1 when both recurrences
+                                    run in one launch (grid above is per direction) */
+  int32_t reserved[5];
 } lstm_plan_info;
 int lstm_query_plan(const lstm_shape* shape, lstm_plan_info* info);
+
+/* seq_length (SingleLayerLstmGrad, 参数说明: the optional mask matrix
+ * [T, Batch, hidden_size] for the actual length of each sequence), taken in
+ * its per-sequence form: a device array of B int32 lengths, or NULL (every
+ * step of every sequence is real).  Length L_b stands for the mask that is 1
+ * at the steps t < L_b of sequence b and 0 past them.  A step with mask 0
+ * holds the state: c_t = c_{t-1} and h_t = h_{t-1} (y_t = h_t repeats it),
+ * so a sequence's final state is that after its last real step (in the
+ * reverse direction its steps past L_b come first and leave h0, c0 as they
+ * are), and such a step gets no gate deltas: its dy reaches the held state
+ * unchanged.  Lengths are not clamped: L_b >= T is a full sequence, L_b <= 0
+ * an empty one.  The forward and the backward of one record take the same
+ * lengths. */
 
 /* Forward pass for training ("前向传播公式").
  *   x [T,B,I], W [4H,H+I]: required (x may be NULL only if T*B*I == 0)
  *   b [4H], h0 [B,H], c0 [B,H]: optional, NULL = zero
+ *   seq_length [B] int32: optional (see above; 4-byte aligned)
  *   y [T,B,H], hT [B,H], cT [B,H]: outputs (y may be NULL only if T*B == 0)
  *   workspace: receives the forward record for lstm_bwd. */
 int lstm_fwd_train(const lstm_shape* shape, const void* x, const void* W, const void* b,
-                   const void* h0, const void* c0, void* y, void* hT, void* cT,
+                   const void* h0, const void* c0, const void* seq_length, void* y, void* hT, void* cT,
                    void* workspace, size_t workspace_bytes, void* stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph
@@ -190,17 +220,18 @@ int lstm_fwd_train(const lstm_shape* shape, const void* x, const void* W, const 
  * caller's to inspect). */
 #define LSTM_SCRATCH_BYTES (64u << 20)
 int lstm_fwd_train_scratch(const lstm_shape* shape, const void* x, const void* W, const void* b,
-                           const void* h0, const void* c0, void* y, void* hT, void* cT, void* stream);
+                           const void* h0, const void* c0, const void* seq_length, void* y, void* hT,
+                           void* cT, void* stream);
 
 /* Backpropagation through time ("反向传播算法" steps 1-6).
  *   dy [T,B,H]: required; dhT, dcT [B,H]: optional, NULL = zero
- *   x, W, h0, c0, y: the same tensors the forward saw (h0 NULL = zero;
- *   c0 NULL = zero); the forward record in `workspace`
+ *   x, W, h0, c0, seq_length, y: the same tensors the forward saw (h0 NULL =
+ *   zero; c0 NULL = zero); the forward record in `workspace`
  *   dx [T,B,I], dW [4H,H+I], dh0 [B,H], dc0 [B,H]: outputs
  *   db [4H]: output, optional (NULL = not computed). */
 int lstm_bwd(const lstm_shape* shape, const void* dy, const void* dhT, const void* dcT,
-             const void* x, const void* W, const void* h0, const void* c0, const void* y,
-             void* workspace, size_t workspace_bytes,
+             const void* x, const void* W, const void* h0, const void* c0, const void* seq_length,
+             const void* y, void* workspace, size_t workspace_bytes,
              void* dx, void* dW, void* db, void* dh0, void* dc0, void* stream);
 
 /* Waits for `stream`, then reports (and clears) a time-out that a
@@ -219,7 +250,8 @@ int lstm_check_workspace(void* workspace, size_t workspace_bytes, void* stream);
  * call's stream, and the elapsed time is added to the total of its kind:
  *   0 input projection   1 forward recurrence   2 backward recurrence
  *   3 dW product (with its split-K sum and the final db sum)   4 dx product
- *   5 (not used)   6 state copies of the T = 0 / B = 0 cases
+ *   5 direction copies (LSTM_BIDIRECTIONAL: y joined, dy split)
+ *   6 state copies of the T = 0 / B = 0 cases
  * lstm_timing_enable(1) also resets the totals.  lstm_timing_read() waits for
  * the recorded events and returns the total milliseconds and the launch
  * count of one kind.  Not thread-safe; timing adds a few microseconds per

@@ -236,6 +236,17 @@ struct EpiStore {  // plain row-major output of the storage type
   __device__ __forceinline__ void store4(int64_t m, int64_t n, f32x4_t v) const { store_row4(out + m * ld + n, v); }
 };
 template <typename T>
+struct EpiAdd {  // out = storage(prev + v): the second of two products summed in fp32
+  T* out; const float* prev; int64_t ld;
+  __device__ __forceinline__ void operator()(int64_t m, int64_t n, float v) const {
+    out[m * ld + n] = Elem<T>::from_f(prev[m * ld + n] + v);
+  }
+  __device__ __forceinline__ f32x4_t col4(int64_t) const { return f32x4_t{0.f, 0.f, 0.f, 0.f}; }
+  __device__ __forceinline__ void store4(int64_t m, int64_t n, f32x4_t v) const {
+    store_row4(out + m * ld + n, v + *(const f32x4_t*)(prev + m * ld + n));
+  }
+};
+template <typename T>
 struct EpiDW {  // dW rows back in gate-block order
   T* dW; int64_t H, N; int ijfo;
   __device__ __forceinline__ void operator()(int64_t m, int64_t n, float v) const {
@@ -1126,18 +1137,26 @@ static hipError_t inproj_t(const Plan& p, const void* x, const void* W, const vo
   return run_gemm<T, KRowsX<T>, false, KRowsWx<T>, false, EpiP>(p, p.TB, p.G4, p.I, a, bw, e, part, zero, zero_bytes, s);
 }
 
-template <typename T>
-static hipError_t dx_t(const Plan& p, const void* dG, const void* W, void* dx, float* part, void* zero,
-                       size_t zero_bytes, hipStream_t s) {
+template <typename T, class Epi>
+static hipError_t dx_epi(const Plan& p, const void* dG, const void* W, const Epi& e, float* part, void* zero,
+                         size_t zero_bytes, hipStream_t s) {
   constexpr int VEC = 16 / sizeof(T);
   KRowsX<T> a{(const T*)dG, p.G4, p.TB, p.G4, aligned16(dG) && p.G4 % VEC == 0};
   MNRowsWx<T> bw{(const T*)W, p.H, p.Z, p.I, p.G4, aligned16(W) && p.Z % VEC == 0 && p.H % VEC == 0, p.ijfo};
-  EpiStore<T> e{(T*)dx, p.I};
   if (p.G4 % LdsCfg<T>::kKStage == 0 && lds_depth_ok<T>(p.G4) && p.I >= VEC && a.vec_ok && bw.vec_ok && p.TB > 0 &&
       small_buf(p.TB * p.G4, p.esize) && small_buf(p.G4 * p.Z, p.esize))
     return run_gemm_lds<T, 0, 1>(p, p.TB, p.I, p.G4, a, bw, e, part, zero, zero_bytes, s);
-  return run_gemm<T, KRowsX<T>, false, MNRowsWx<T>, true, EpiStore<T>>(p, p.TB, p.I, p.G4, a, bw, e, part, zero,
-                                                                       zero_bytes, s);
+  return run_gemm<T, KRowsX<T>, false, MNRowsWx<T>, true, Epi>(p, p.TB, p.I, p.G4, a, bw, e, part, zero,
+                                                               zero_bytes, s);
+}
+
+// dx in the storage type; or its fp32 sums into acc_out; or acc_in plus them
+template <typename T>
+static hipError_t dx_t(const Plan& p, const void* dG, const void* W, void* dx, float* part, void* zero,
+                       size_t zero_bytes, hipStream_t s, float* acc_out, const float* acc_in) {
+  if (acc_out) return dx_epi<T>(p, dG, W, EpiStore<float>{acc_out, p.I}, part, zero, zero_bytes, s);
+  if (acc_in) return dx_epi<T>(p, dG, W, EpiAdd<T>{(T*)dx, acc_in, p.I}, part, zero, zero_bytes, s);
+  return dx_epi<T>(p, dG, W, EpiStore<T>{(T*)dx, p.I}, part, zero, zero_bytes, s);
 }
 
 template <typename T>
@@ -1169,10 +1188,10 @@ hipError_t launch_gemm_inproj(const Plan& p, const void* x, const void* W, const
   return inproj_t<float>(p, x, W, b, P, part, zero, zero_bytes, s);
 }
 hipError_t launch_gemm_dx(const Plan& p, const void* dG, const void* W, void* dx, float* part, void* zero,
-                          size_t zero_bytes, hipStream_t s) {
-  if (p.dtype == 1) return dx_t<bf16_t>(p, dG, W, dx, part, zero, zero_bytes, s);
-  if (p.dtype == 2) return dx_t<f16_t>(p, dG, W, dx, part, zero, zero_bytes, s);
-  return dx_t<float>(p, dG, W, dx, part, zero, zero_bytes, s);
+                          size_t zero_bytes, hipStream_t s, float* acc_out, const float* acc_in) {
+  if (p.dtype == 1) return dx_t<bf16_t>(p, dG, W, dx, part, zero, zero_bytes, s, acc_out, acc_in);
+  if (p.dtype == 2) return dx_t<f16_t>(p, dG, W, dx, part, zero, zero_bytes, s, acc_out, acc_in);
+  return dx_t<float>(p, dG, W, dx, part, zero, zero_bytes, s, acc_out, acc_in);
 }
 hipError_t launch_gemm_dw(const Plan& p, const void* dG, const void* x, const void* h0, const void* y, void* dW,
                           float* part, void* zero, size_t zero_bytes, const float* DBP, void* db, hipStream_t s) {
@@ -1210,6 +1229,45 @@ hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint32_t*)p, n);
   return hipGetLastError();
+}
+
+// Two directions side by side: row r of `a` and of `b` (rb bytes each) into
+// row r of `out` (2*rb bytes), or back (split).  16-byte pieces when the
+// rows and pointers allow, else 2-byte ones (every element is 2 or 4 bytes).
+template <typename U>
+__global__ void __launch_bounds__(256) dirs_kernel(const U* a, const U* b, U* out, int64_t rows, int64_t ru, int split) {
+  const int64_t n = rows * ru;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / ru, c = i - r * ru;
+    if (split) {
+      ((U*)a)[i] = out[r * 2 * ru + c];
+      ((U*)b)[i] = out[r * 2 * ru + ru + c];
+    } else {
+      out[r * 2 * ru + c] = a[i];
+      out[r * 2 * ru + ru + c] = b[i];
+    }
+  }
+}
+static hipError_t launch_dirs(const void* a, const void* b, void* out, int64_t rows, int64_t rb, int split,
+                              hipStream_t s) {
+  if (rows <= 0 || rb <= 0) return hipSuccess;
+  const bool v16 = rb % 16 == 0 && ((uintptr_t)a | (uintptr_t)b | (uintptr_t)out) % 16 == 0;
+  const int64_t ru = v16 ? rb / 16 : rb / 2, n = rows * ru;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (v16)
+    hipLaunchKernelGGL(dirs_kernel<u32x4_t>, dim3((unsigned)blocks), dim3(256), 0, s, (const u32x4_t*)a,
+                       (const u32x4_t*)b, (u32x4_t*)out, rows, ru, split);
+  else
+    hipLaunchKernelGGL(dirs_kernel<uint16_t>, dim3((unsigned)blocks), dim3(256), 0, s, (const uint16_t*)a,
+                       (const uint16_t*)b, (uint16_t*)out, rows, ru, split);
+  return hipGetLastError();
+}
+hipError_t launch_join_dirs(const void* y0, const void* y1, void* y, int64_t rows, int64_t row_bytes, hipStream_t s) {
+  return launch_dirs(y0, y1, y, rows, row_bytes, 0, s);
+}
+hipError_t launch_split_dirs(const void* dy, void* dy0, void* dy1, int64_t rows, int64_t row_bytes, hipStream_t s) {
+  return launch_dirs(dy0, dy1, const_cast<void*>(dy), rows, row_bytes, 1, s);
 }
 
 // dst = src (n elements of esize bytes), or dst = 0 when src is NULL

@@ -53,6 +53,14 @@ struct Plan {
   int rev;          // 1: the reverse direction (steps from t = T-1 down to 0)
   int ijfo;         // 1: W, b, dW, db in the gate order i, g, f, o (gate_block)
   int two_bias;     // 1: b and db are [2][4H] (b_ih, b_hh)
+  // bidirectional layer: two direction blocks of dir_bytes each, holding
+  // the one-direction layout above plus that direction's y and dy
+  // ([T][B][H] at off_ydir, off_dydir inside the block), then the fp32 dx
+  // sums [TB][I] at off_dxacc; concurrent: both recurrences in one launch
+  // (the plan laid out for half the compute units each), else one after the
+  // other
+  int bidir, concurrent;
+  size_t dir_bytes, off_ydir, off_dydir, off_dxacc;
   int cus;          // compute units of the device
   int max_splits;   // largest split-K factor of the three products
   size_t off_gp;    // fp32 split-K partials of the products
@@ -66,7 +74,8 @@ constexpr int kWaves = 4;
 constexpr int kRecThreads = 64 * kWaves;
 
 // Fill the plan for a shape; returns 0 or an LSTM_ERR_* code.
-int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p);
+// cap_div: the recurrences' grid may take cus / cap_div compute units.
+int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p, int cap_div = 1);
 
 // The plan runs the VALU forward (fp32 batch groups of 4 rows).
 bool fwd_vec_ok(const Plan& p);
@@ -80,9 +89,11 @@ hipError_t launch_copy_state(const void* src, void* dst, size_t n, int esize, hi
 // P[tb][4j+g] = sum_k x[tb][k] W[gH+j][H+k] + b[gH+j]   (fp32 out)
 hipError_t launch_gemm_inproj(const Plan& p, const void* x, const void* W, const void* b, float* P, float* part,
                               void* zero, size_t zero_bytes, hipStream_t s);
-// dx[tb][i] = sum_n dG[tb][n] W[row(n)][H+i]
+// dx[tb][i] = sum_n dG[tb][n] W[row(n)][H+i]; with acc_out the fp32 sums go
+// there instead of dx, with acc_in they are added to it before the rounding
+// to dx (the two directions of a bidirectional layer)
 hipError_t launch_gemm_dx(const Plan& p, const void* dG, const void* W, void* dx, float* part, void* zero,
-                          size_t zero_bytes, hipStream_t s);
+                          size_t zero_bytes, hipStream_t s, float* acc_out = nullptr, const float* acc_in = nullptr);
 // dW[row(m)][n] = sum_tb dG[tb][m] Z[tb][n],  Z = [h_{t-1} | x_t]
 // The dW launch also writes db[row(n)] = sum_bg DBP[bg][n] (in bg order) when
 // db is not null.
@@ -93,12 +104,26 @@ size_t gemm_partial_bytes(const Plan& p, int cus);
 // 16-byte aligned operands assumed)
 int inproj_tiles_per_wg(const Plan& p);
 
+// One launch of both directions of a bidirectional layer: the second half
+// of the grid runs the reverse direction on tensors at these byte offsets
+// from the first direction's (workspace, W, [2][B][H] states).
+struct Bidir {
+  int64_t ws, w, st;
+};
+
+// The persistent recurrences; len: [B] sequence lengths or null; bd: null,
+// or both directions in one launch of twice the plan's grid.
 hipError_t launch_fwd_recurrent(const Plan& p, const float* P, const void* W, const void* h0,
                                 const void* c0, void* y, void* hT, void* cT, void* Gs, float* Cs,
-                                uint64_t* HX, uint32_t* err, uint64_t* stamps, hipStream_t s);
+                                uint64_t* HX, uint32_t* err, uint64_t* stamps, const int32_t* len,
+                                const Bidir* bd, hipStream_t s);
 hipError_t launch_bwd_recurrent(const Plan& p, const void* W, const void* c0, const void* dy,
                                 const void* dhT, const void* dcT, const void* Gs, const float* Cs,
                                 void* dG, uint64_t* PX, float* DBP, void* dh0, void* dc0, uint32_t* err,
-                                uint64_t* stamps, hipStream_t s);
+                                uint64_t* stamps, const int32_t* len, const Bidir* bd, hipStream_t s);
+// The two directions' [rows][H] outputs side by side into [rows][2H]
+// (join), or [rows][2H] cotangents back into two [rows][H] (split).
+hipError_t launch_join_dirs(const void* y0, const void* y1, void* y, int64_t rows, int64_t row_bytes, hipStream_t s);
+hipError_t launch_split_dirs(const void* dy, void* dy0, void* dy1, int64_t rows, int64_t row_bytes, hipStream_t s);
 
 }  // namespace lstm

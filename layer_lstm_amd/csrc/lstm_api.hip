@@ -30,7 +30,7 @@ static int device_cus(int* cus) {
   return LSTM_OK;
 }
 
-int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
+int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p, int cap_div) {
   if (T < 0 || B < 0 || I < 0 || H <= 0) return LSTM_ERR_DIMS;
   if (dtype != LSTM_F32 && dtype != LSTM_BF16 && dtype != LSTM_F16) return LSTM_ERR_DTYPE;
   if (H > 2048 || I > 65536 || T > ((int64_t)1 << 30)) return LSTM_ERR_UNSUPPORTED;
@@ -74,7 +74,7 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p) {
           if (NW == 8 && e == 4) continue;
           const int64_t nBG = B > 0 ? (B + NB - 1) / NB : 1;
           const int64_t nJG = (H + NJ - 1) / NJ;
-          if (nBG * nJG > cus) continue;
+          if (nBG * nJG > cus / cap_div) continue;
           if (pass == 0 && !(p->nxcd > 1 && nBG % p->nxcd == 0)) continue;
           const int NBr = NB < 16 ? 16 : NB;
           // forward: NJ/4 M-tiles of 16 interleaved gate rows in groups of
@@ -283,6 +283,36 @@ static void flush_timing() {
   g_pending.clear();
 }
 
+constexpr int kKnownFlags = LSTM_REVERSE | LSTM_GATES_IJFO | LSTM_TWO_BIAS | LSTM_BIDIRECTIONAL;
+
+// The plan of a shape with its flags: the one-direction plan, and for a
+// bidirectional layer the two direction blocks, the recurrences of both in
+// one launch when each fits half the compute units, else one after the
+// other on all of them.
+static int plan_for(const lstm_shape* shape, Plan* p) {
+  if ((shape->flags & ~kKnownFlags) != 0) return LSTM_ERR_DTYPE;
+  const bool bidir = (shape->flags & LSTM_BIDIRECTIONAL) != 0;
+  if (bidir && (shape->flags & LSTM_REVERSE)) return LSTM_ERR_DTYPE;
+  int rc = make_plan(shape->T, shape->B, shape->I, shape->H, shape->dtype, p, bidir ? 2 : 1);
+  const bool conc = bidir && rc == LSTM_OK;
+  if (bidir && !conc && rc == LSTM_ERR_UNSUPPORTED) rc = make_plan(shape->T, shape->B, shape->I, shape->H, shape->dtype, p, 1);
+  if (rc != LSTM_OK) return rc;
+  p->rev = (shape->flags & LSTM_REVERSE) ? 1 : 0;
+  p->ijfo = (shape->flags & LSTM_GATES_IJFO) ? 1 : 0;
+  p->two_bias = (shape->flags & LSTM_TWO_BIAS) ? 1 : 0;
+  p->bidir = bidir ? 1 : 0;
+  p->concurrent = conc ? 1 : 0;
+  if (bidir) {
+    const size_t yb = align256((size_t)p->TB * p->H * p->esize);
+    p->off_ydir = p->total;
+    p->off_dydir = p->off_ydir + yb;
+    p->dir_bytes = p->off_dydir + yb;
+    p->off_dxacc = 2 * p->dir_bytes;
+    p->total = p->off_dxacc + align256((size_t)p->TB * p->I * 4);
+  }
+  return LSTM_OK;
+}
+
 }  // namespace lstm
 
 using namespace lstm;
@@ -296,7 +326,7 @@ const char* lstm_status_string(int status) {
     case LSTM_OK: return "ok";
     case LSTM_ERR_NULL: return "a required pointer is NULL";
     case LSTM_ERR_DIMS: return "invalid dimensions (T, B, I < 0 or H <= 0)";
-    case LSTM_ERR_DTYPE: return "unsupported dtype";
+    case LSTM_ERR_DTYPE: return "unsupported dtype, unknown flag or invalid flag combination";
     case LSTM_ERR_ALIGN: return "misaligned pointer";
     case LSTM_ERR_WORKSPACE: return "workspace too small";
     case LSTM_ERR_UNSUPPORTED: return "shape outside the supported envelope";
@@ -311,9 +341,8 @@ const char* lstm_status_string(int status) {
 
 int lstm_query(const lstm_shape* shape, size_t* workspace_bytes) {
   if (!shape || !workspace_bytes) return LSTM_ERR_NULL;
-  if ((shape->flags & ~(LSTM_REVERSE | LSTM_GATES_IJFO | LSTM_TWO_BIAS)) != 0) return LSTM_ERR_DTYPE;
   Plan p;
-  const int rc = make_plan(shape->T, shape->B, shape->I, shape->H, shape->dtype, &p);
+  const int rc = plan_for(shape, &p);
   if (rc != LSTM_OK) return rc;
   *workspace_bytes = p.total;
   return LSTM_OK;
@@ -321,9 +350,8 @@ int lstm_query(const lstm_shape* shape, size_t* workspace_bytes) {
 
 int lstm_query_plan(const lstm_shape* shape, lstm_plan_info* info) {
   if (!shape || !info) return LSTM_ERR_NULL;
-  if ((shape->flags & ~(LSTM_REVERSE | LSTM_GATES_IJFO | LSTM_TWO_BIAS)) != 0) return LSTM_ERR_DTYPE;
   Plan p;
-  const int rc = make_plan(shape->T, shape->B, shape->I, shape->H, shape->dtype, &p);
+  const int rc = plan_for(shape, &p);
   if (rc != LSTM_OK) return rc;
   memset(info, 0, sizeof(*info));
   info->rows_per_group = p.NB;
@@ -336,6 +364,7 @@ int lstm_query_plan(const lstm_shape* shape, lstm_plan_info* info) {
   info->fwd_valu = fwd_vec_ok(p) ? 1 : 0;
   info->bwd_valu = p.bwd_valu ? 1 : 0;
   info->inproj_tiles_per_wg = inproj_tiles_per_wg(p);
+  info->directions_concurrent = p.bidir && p.concurrent ? 1 : 0;
   return LSTM_OK;
 }
 
@@ -374,55 +403,75 @@ static int scratch_for_device(void** ptr) {
 extern "C" {
 
 int lstm_fwd_train(const lstm_shape* shape, const void* x, const void* W, const void* b, const void* h0,
-                   const void* c0, void* y, void* hT, void* cT, void* workspace, size_t workspace_bytes,
-                   void* stream) {
+                   const void* c0, const void* seq_length, void* y, void* hT, void* cT, void* workspace,
+                   size_t workspace_bytes, void* stream) {
   if (!shape) return LSTM_ERR_NULL;
-  if ((shape->flags & ~(LSTM_REVERSE | LSTM_GATES_IJFO | LSTM_TWO_BIAS)) != 0) return LSTM_ERR_DTYPE;
   Plan p;
-  int rc = make_plan(shape->T, shape->B, shape->I, shape->H, shape->dtype, &p);
+  int rc = plan_for(shape, &p);
   if (rc != LSTM_OK) return rc;
-  p.rev = (shape->flags & LSTM_REVERSE) ? 1 : 0;
-  p.ijfo = (shape->flags & LSTM_GATES_IJFO) ? 1 : 0;
-  p.two_bias = (shape->flags & LSTM_TWO_BIAS) ? 1 : 0;
   const int e = p.esize;
   if (!W || !workspace) return LSTM_ERR_NULL;
   if (p.TB * p.I > 0 && !x) return LSTM_ERR_NULL;
   if (p.TB > 0 && !y) return LSTM_ERR_NULL;
   if (p.B > 0 && (!hT || !cT)) return LSTM_ERR_NULL;
   if (misaligned(x, e) || misaligned(W, e) || misaligned(b, e) || misaligned(h0, e) || misaligned(c0, e) ||
-      misaligned(y, e) || misaligned(hT, e) || misaligned(cT, e) || ((uintptr_t)workspace & 255u))
+      misaligned(y, e) || misaligned(hT, e) || misaligned(cT, e) || misaligned(seq_length, 4) ||
+      ((uintptr_t)workspace & 255u))
     return LSTM_ERR_ALIGN;
   if (workspace_bytes < p.total) return LSTM_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   hipError_t err = hipSuccess;
+  const int nd = p.bidir ? 2 : 1;
 
   if (p.B == 0) return LSTM_OK;
   if (p.T == 0) {
     Timed tm(6, s);
-    err = launch_copy_state(h0, hT, (size_t)(p.B * p.H), e, s);
-    if (err == hipSuccess) err = launch_copy_state(c0, cT, (size_t)(p.B * p.H), e, s);
+    err = launch_copy_state(h0, hT, (size_t)(nd * p.B * p.H), e, s);
+    if (err == hipSuccess) err = launch_copy_state(c0, cT, (size_t)(nd * p.B * p.H), e, s);
     return status_of(err);
   }
+  // per direction: W, b and the [B][H] states at these byte strides, the
+  // workspace block at dir_bytes
+  const int64_t wst = p.G4 * p.Z * e, bst = (p.two_bias ? 2 : 1) * p.G4 * e, sst = p.B * p.H * e;
+  auto at = [](const void* q, int64_t off) -> const char* { return q ? (const char*)q + off : nullptr; };
+  auto wsd = [&](int d) { return ws + (size_t)d * p.dir_bytes; };
+  auto ydir = [&](int d) -> void* { return p.bidir ? wsd(d) + p.off_ydir : y; };
   // the input projection's launch also clears the error word and both
-  // step-exchange buffers (tags 0) for the recurrences that follow
-  float* P = (float*)(ws + p.off_P);
-  {
+  // step-exchange buffers (tags 0) of its direction for the recurrences
+  for (int d = 0; d < nd && err == hipSuccess; ++d) {
     Timed tm(0, s);
-    err = launch_gemm_inproj(p, x, W, b, P, (float*)(ws + p.off_gp), ws + p.off_ctrl,
-                             p.off_PX + p.bytes_PX - p.off_ctrl, s);
+    err = launch_gemm_inproj(p, x, at(W, d * wst), at(b, d * bst), (float*)(wsd(d) + p.off_P),
+                             (float*)(wsd(d) + p.off_gp), wsd(d) + p.off_ctrl, p.off_PX + p.bytes_PX - p.off_ctrl, s);
   }
-  if (err == hipSuccess) {
+  const int32_t* len = (const int32_t*)seq_length;
+  uint32_t* errw = (uint32_t*)(ws + p.off_ctrl);  // one error word for both directions
+  if (err == hipSuccess && (!p.bidir || p.concurrent)) {
     Timed tm(1, s);
-    err = launch_fwd_recurrent(p, P, W, h0, c0, y, hT, cT, ws + p.off_G, (float*)(ws + p.off_C),
-                               (uint64_t*)(ws + p.off_HX), (uint32_t*)(ws + p.off_ctrl),
-                               stamps_fit(p) ? g_stamps_fwd : nullptr, s);
+    const Bidir bd{(int64_t)p.dir_bytes, wst, sst};
+    err = launch_fwd_recurrent(p, (const float*)(ws + p.off_P), W, h0, c0, ydir(0), hT, cT, ws + p.off_G,
+                               (float*)(ws + p.off_C), (uint64_t*)(ws + p.off_HX), errw,
+                               stamps_fit(p) ? g_stamps_fwd : nullptr, len, p.bidir ? &bd : nullptr, s);
+  } else {
+    for (int d = 0; d < nd && err == hipSuccess; ++d) {
+      Timed tm(1, s);
+      Plan pd = p;
+      pd.rev = d;
+      err = launch_fwd_recurrent(pd, (const float*)(wsd(d) + p.off_P), at(W, d * wst), at(h0, d * sst),
+                                 at(c0, d * sst), ydir(d), (char*)hT + d * sst, (char*)cT + d * sst,
+                                 wsd(d) + p.off_G, (float*)(wsd(d) + p.off_C), (uint64_t*)(wsd(d) + p.off_HX), errw,
+                                 d == 0 && stamps_fit(p) ? g_stamps_fwd : nullptr, len, nullptr, s);
+    }
+  }
+  if (err == hipSuccess && p.bidir) {
+    Timed tm(5, s);
+    err = launch_join_dirs(ydir(0), ydir(1), y, p.TB, p.H * e, s);
   }
   return status_of(err);
 }
 
 int lstm_fwd_train_scratch(const lstm_shape* shape, const void* x, const void* W, const void* b, const void* h0,
-                           const void* c0, void* y, void* hT, void* cT, void* stream) {
+                           const void* c0, const void* seq_length, void* y, void* hT, void* cT, void* stream) {
   if (!shape) return LSTM_ERR_NULL;
   size_t need = 0;
   const int rc = lstm_query(shape, &need);
@@ -431,20 +480,16 @@ int lstm_fwd_train_scratch(const lstm_shape* shape, const void* x, const void* W
   void* ws = nullptr;
   const int rs = scratch_for_device(&ws);
   if (rs != LSTM_OK) return rs;
-  return lstm_fwd_train(shape, x, W, b, h0, c0, y, hT, cT, ws, kScratchBytes, stream);
+  return lstm_fwd_train(shape, x, W, b, h0, c0, seq_length, y, hT, cT, ws, kScratchBytes, stream);
 }
 
 int lstm_bwd(const lstm_shape* shape, const void* dy, const void* dhT, const void* dcT, const void* x,
-             const void* W, const void* h0, const void* c0, const void* y, void* workspace, size_t workspace_bytes,
-             void* dx, void* dW, void* db, void* dh0, void* dc0, void* stream) {
+             const void* W, const void* h0, const void* c0, const void* seq_length, const void* y, void* workspace,
+             size_t workspace_bytes, void* dx, void* dW, void* db, void* dh0, void* dc0, void* stream) {
   if (!shape) return LSTM_ERR_NULL;
-  if ((shape->flags & ~(LSTM_REVERSE | LSTM_GATES_IJFO | LSTM_TWO_BIAS)) != 0) return LSTM_ERR_DTYPE;
   Plan p;
-  int rc = make_plan(shape->T, shape->B, shape->I, shape->H, shape->dtype, &p);
+  int rc = plan_for(shape, &p);
   if (rc != LSTM_OK) return rc;
-  p.rev = (shape->flags & LSTM_REVERSE) ? 1 : 0;
-  p.ijfo = (shape->flags & LSTM_GATES_IJFO) ? 1 : 0;
-  p.two_bias = (shape->flags & LSTM_TWO_BIAS) ? 1 : 0;
   const int e = p.esize;
   if (!W || !dW || !workspace) return LSTM_ERR_NULL;
   if (p.TB > 0 && (!dy || !y)) return LSTM_ERR_NULL;
@@ -452,41 +497,78 @@ int lstm_bwd(const lstm_shape* shape, const void* dy, const void* dhT, const voi
   if (p.B > 0 && (!dh0 || !dc0)) return LSTM_ERR_NULL;
   if (misaligned(dy, e) || misaligned(dhT, e) || misaligned(dcT, e) || misaligned(x, e) || misaligned(W, e) ||
       misaligned(h0, e) || misaligned(c0, e) || misaligned(y, e) || misaligned(dx, e) || misaligned(dW, e) ||
-      misaligned(db, e) || misaligned(dh0, e) || misaligned(dc0, e) || ((uintptr_t)workspace & 255u))
+      misaligned(db, e) || misaligned(dh0, e) || misaligned(dc0, e) || misaligned(seq_length, 4) ||
+      ((uintptr_t)workspace & 255u))
     return LSTM_ERR_ALIGN;
   if (workspace_bytes < p.total) return LSTM_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   hipError_t err = hipSuccess;
+  const int nd = p.bidir ? 2 : 1;
+  const int64_t wst = p.G4 * p.Z * e, bst = (p.two_bias ? 2 : 1) * p.G4 * e, sst = p.B * p.H * e;
 
   if (p.T == 0 || p.B == 0) {
     Timed tm(6, s);
-    err = launch_fill_zero(dW, (size_t)(p.G4 * p.Z) * e, s);
+    err = launch_fill_zero(dW, (size_t)(nd * wst), s);
     // db is [2][4H] with two biases: both halves are outputs
-    if (err == hipSuccess && db) err = launch_fill_zero(db, (size_t)(p.two_bias ? 2 : 1) * p.G4 * e, s);
-    if (err == hipSuccess && p.B > 0) err = launch_copy_state(dhT, dh0, (size_t)(p.B * p.H), e, s);
-    if (err == hipSuccess && p.B > 0) err = launch_copy_state(dcT, dc0, (size_t)(p.B * p.H), e, s);
+    if (err == hipSuccess && db) err = launch_fill_zero(db, (size_t)(nd * bst), s);
+    if (err == hipSuccess && p.B > 0) err = launch_copy_state(dhT, dh0, (size_t)(nd * p.B * p.H), e, s);
+    if (err == hipSuccess && p.B > 0) err = launch_copy_state(dcT, dc0, (size_t)(nd * p.B * p.H), e, s);
     return status_of(err);
+  }
+  auto at = [](const void* q, int64_t off) -> const char* { return q ? (const char*)q + off : nullptr; };
+  auto wsd = [&](int d) { return ws + (size_t)d * p.dir_bytes; };
+  auto ydir = [&](int d) -> const void* { return p.bidir ? wsd(d) + p.off_ydir : y; };
+  auto dydir = [&](int d) -> const void* { return p.bidir ? wsd(d) + p.off_dydir : dy; };
+  if (p.bidir) {
+    Timed tm(5, s);
+    err = launch_split_dirs(dy, wsd(0) + p.off_dydir, wsd(1) + p.off_dydir, p.TB, p.H * e, s);
   }
   // The backward exchange buffer starts cleared: the forward clears it, and
   // every backward clears it again once its recurrence is done (in the dW
-  // launch), so that a repeated backward finds it clean too.
-  void* dG = ws + p.off_P;  // the input projection is dead after the forward
-  {
+  // launch), so that a repeated backward finds it clean too.  The gate
+  // deltas go where the input projection was (dead after the forward).
+  const int32_t* len = (const int32_t*)seq_length;
+  uint32_t* errw = (uint32_t*)(ws + p.off_ctrl);
+  if (err == hipSuccess && (!p.bidir || p.concurrent)) {
     Timed tm(2, s);
-    err = launch_bwd_recurrent(p, W, c0, dy, dhT, dcT, ws + p.off_G, (const float*)(ws + p.off_C), dG,
-                               (uint64_t*)(ws + p.off_PX), db ? (float*)(ws + p.off_dbp) : nullptr, dh0, dc0,
-                               (uint32_t*)(ws + p.off_ctrl),
-                               stamps_fit(p) ? g_stamps_bwd : nullptr, s);
+    const Bidir bd{(int64_t)p.dir_bytes, wst, sst};
+    err = launch_bwd_recurrent(p, W, c0, dydir(0), dhT, dcT, ws + p.off_G, (const float*)(ws + p.off_C),
+                               ws + p.off_P, (uint64_t*)(ws + p.off_PX), db ? (float*)(ws + p.off_dbp) : nullptr,
+                               dh0, dc0, errw, stamps_fit(p) ? g_stamps_bwd : nullptr, len, p.bidir ? &bd : nullptr,
+                               s);
+  } else {
+    for (int d = 0; d < nd && err == hipSuccess; ++d) {
+      Timed tm(2, s);
+      Plan pd = p;
+      pd.rev = d;
+      err = launch_bwd_recurrent(pd, at(W, d * wst), at(c0, d * sst), dydir(d), at(dhT, d * sst), at(dcT, d * sst),
+                                 wsd(d) + p.off_G, (const float*)(wsd(d) + p.off_C), wsd(d) + p.off_P,
+                                 (uint64_t*)(wsd(d) + p.off_PX), db ? (float*)(wsd(d) + p.off_dbp) : nullptr,
+                                 (char*)dh0 + d * sst, (char*)dc0 + d * sst, errw,
+                                 d == 0 && stamps_fit(p) ? g_stamps_bwd : nullptr, len, nullptr, s);
+    }
   }
-  if (err == hipSuccess) {
+  for (int d = 0; d < nd && err == hipSuccess; ++d) {
     Timed tm(3, s);
-    err = launch_gemm_dw(p, dG, x, h0, y, dW, (float*)(ws + p.off_gp), ws + p.off_PX, p.bytes_PX,
-                         (const float*)(ws + p.off_dbp), db, s);
+    Plan pd = p;
+    pd.rev = p.bidir ? d : p.rev;
+    err = launch_gemm_dw(pd, wsd(d) + p.off_P, x, at(h0, d * sst), ydir(d), (char*)dW + d * wst,
+                         (float*)(wsd(d) + p.off_gp), wsd(d) + p.off_PX, p.bytes_PX,
+                         (const float*)(wsd(d) + p.off_dbp), db ? (char*)db + d * bst : nullptr, s);
   }
   if (err == hipSuccess && p.I > 0) {
     Timed tm(4, s);
-    err = launch_gemm_dx(p, dG, W, dx, (float*)(ws + p.off_gp), nullptr, 0, s);
+    if (!p.bidir) {
+      err = launch_gemm_dx(p, ws + p.off_P, W, dx, (float*)(ws + p.off_gp), nullptr, 0, s);
+    } else {
+      // x feeds both directions: dx = the sum of their two products, in fp32
+      float* acc = (float*)(ws + p.off_dxacc);
+      err = launch_gemm_dx(p, wsd(0) + p.off_P, W, dx, (float*)(wsd(0) + p.off_gp), nullptr, 0, s, acc, nullptr);
+      if (err == hipSuccess)
+        err = launch_gemm_dx(p, wsd(1) + p.off_P, at(W, wst), dx, (float*)(wsd(1) + p.off_gp), nullptr, 0, s, nullptr,
+                             acc);
+    }
   }
   return status_of(err);
 }

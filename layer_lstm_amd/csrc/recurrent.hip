@@ -54,7 +54,7 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, fq = lane >> 4;
   int bg, jg;
-  take_role(a.nBG, a.nJG, a.nxcd, a.local, bg, jg);
+  take_role(direction_of(a), a.nBG, a.nJG, a.nxcd, a.local, bg, jg);
   const bool local = a.local != 0;
   const int b0 = bg * a.NB, j0 = jg * a.NJ;
   const int MT = a.NJ / 4;                   // M-tiles (16 interleaved gate rows = 4 units)
@@ -157,9 +157,15 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
       dst[nt] = __builtin_bit_cast(
           f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, eok[nt] ? 16 * eidx[nt] : (int)stepP, 0, 0));
   };
-  T hq[NBT];
+  T hq[NBT];        // h of this lane's elements: h0, then the state after each step
   float cq[NBT];
   u32x4_t gq[NBT];  // activated gates of the step, packed (E == 2: two words)
+  int lenb[NBT];    // sequence length of each element's batch row
+#pragma unroll
+  for (int nt = 0; nt < NBT; ++nt) {
+    hq[nt] = (a.h0 && eok[nt]) ? ((const T*)a.h0)[eidx[nt]] : T(0);
+    lenb[nt] = eok[nt] ? len_of(a.len, b0 + 16 * nt + fr, a.T) : a.T;
+  }
   auto store_record = [&](int tt) {
     const __amdgpu_buffer_rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(
         (void*)((T*)a.y + mem_t(tt, a.T, a.rev) * stepY), 0, (int)(stepY * E), 0x00020000);
@@ -464,8 +470,12 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
         }
         const f32x4_t z = mine[nt] + pv;
         const float ig = sigmoidf(z[0]), fg = sigmoidf(z[1]), gg = tanh_f(z[2]), og = sigmoidf(z[3]);
-        const float c = fg * cst[nt] + ig * gg;
-        const float h = og * tanh_f(c);
+        float c = fg * cst[nt] + ig * gg;
+        float h = og * tanh_f(c);
+        if (mem_t(t, a.T, a.rev) >= lenb[nt]) {  // past the sequence's end: the state is held
+          c = cst[nt];
+          h = Elem<T>::to_f(hq[nt]);
+        }
         cst[nt] = c;
         cq[nt] = c;
         hq[nt] = Elem<T>::from_f(h);
@@ -521,13 +531,13 @@ template <typename T, int NBT, int C, int NW, int MW>
 static hipError_t fwd_dispatch_mw(const Plan& p, FwdArgs& a, hipStream_t s) {
   const int nt = 64 * NW;
   switch (p.fwd_nkbw) {
-    case 1: return coop_launch(fwd_rec_kernel<T, NBT, 1, C, NW, MW>, p.grid, p.lds_fwd, &a, s, nt);
-    case 2: return coop_launch(fwd_rec_kernel<T, NBT, 2, C, NW, MW>, p.grid, p.lds_fwd, &a, s, nt);
-    case 4: return coop_launch(fwd_rec_kernel<T, NBT, 4, C, NW, MW>, p.grid, p.lds_fwd, &a, s, nt);
-    case 8: return coop_launch(fwd_rec_kernel<T, NBT, 8, C, NW, MW>, p.grid, p.lds_fwd, &a, s, nt);
-    case 16: return coop_launch(fwd_rec_kernel<T, NBT, 16, C, NW, MW>, p.grid, p.lds_fwd, &a, s, nt);
+    case 1: return coop_launch(fwd_rec_kernel<T, NBT, 1, C, NW, MW>, launch_grid(p, a), p.lds_fwd, &a, s, nt);
+    case 2: return coop_launch(fwd_rec_kernel<T, NBT, 2, C, NW, MW>, launch_grid(p, a), p.lds_fwd, &a, s, nt);
+    case 4: return coop_launch(fwd_rec_kernel<T, NBT, 4, C, NW, MW>, launch_grid(p, a), p.lds_fwd, &a, s, nt);
+    case 8: return coop_launch(fwd_rec_kernel<T, NBT, 8, C, NW, MW>, launch_grid(p, a), p.lds_fwd, &a, s, nt);
+    case 16: return coop_launch(fwd_rec_kernel<T, NBT, 16, C, NW, MW>, launch_grid(p, a), p.lds_fwd, &a, s, nt);
     case 32:
-      if constexpr (MW == 1) return coop_launch(fwd_rec_kernel<T, NBT, 32, C, NW, MW>, p.grid, p.lds_fwd, &a, s, nt);
+      if constexpr (MW == 1) return coop_launch(fwd_rec_kernel<T, NBT, 32, C, NW, MW>, launch_grid(p, a), p.lds_fwd, &a, s, nt);
       break;
   }
   return hipErrorInvalidValue;
@@ -555,11 +565,12 @@ static hipError_t fwd_dispatch(const Plan& p, FwdArgs& a, hipStream_t s) {
 
 hipError_t launch_fwd_recurrent(const Plan& p, const float* P, const void* W, const void* h0, const void* c0,
                                 void* y, void* hT, void* cT, void* Gs, float* Cs, uint64_t* HX, uint32_t* err,
-                                uint64_t* stamps, hipStream_t s) {
+                                uint64_t* stamps, const int32_t* len, const Bidir* bd, hipStream_t s) {
   char* hd = (char*)HX;  // the packed ring and its flags share the tagged-word region
   FwdArgs a{P, W, h0, c0, y, hT, cT, Gs, Cs, HX, hd, (uint32_t*)(hd + p.off_hflags), (uint32_t)p.off_hflags, err,
             stamps, (int)p.T, (int)p.B, (int)p.H, (int)p.Z, p.NB, p.NJ,
-            p.nJG, p.Hp, p.Bp, p.esize == 2 ? (p.Hp / 2) : p.Hp, p.nBG, p.nxcd, p.xcd_local, p.rev, p.ijfo};
+            p.nJG, p.Hp, p.Bp, p.esize == 2 ? (p.Hp / 2) : p.Hp, p.nBG, p.nxcd, p.xcd_local, p.rev, p.ijfo,
+            len, bd ? p.grid : 0, bd ? bd->ws : 0, bd ? bd->w : 0, bd ? bd->st : 0};
   if (fwd_vec_ok(p)) return launch_fwd_vec(p, a, s);
   const int nbt = p.NB < 16 ? 1 : p.NB / 16;
   if (p.dtype == 1) {
@@ -580,11 +591,13 @@ hipError_t launch_fwd_recurrent(const Plan& p, const float* P, const void* W, co
 
 hipError_t launch_bwd_recurrent(const Plan& p, const void* W, const void* c0, const void* dy, const void* dhT,
                                 const void* dcT, const void* Gs, const float* Cs, void* dG, uint64_t* PX, float* DBP,
-                                void* dh0, void* dc0, uint32_t* err, uint64_t* stamps, hipStream_t s) {
+                                void* dh0, void* dc0, uint32_t* err, uint64_t* stamps, const int32_t* len,
+                                const Bidir* bd, hipStream_t s) {
   char* gd = (char*)PX;  // the gate-delta ring and its flags share the tagged-word region
   BwdArgs a{W, c0, dy, dhT, dcT, Gs, Cs, dG, PX, gd, (uint32_t*)(gd + p.off_pflags), (uint32_t)p.off_pflags,
             DBP, dh0, dc0, err, stamps, (int)p.T, (int)p.B, (int)p.H, (int)p.Z,
-            p.NB, p.NJ, p.nJG, p.Hp, p.Bp, p.nBG, p.nxcd, p.xcd_local, p.rev, p.ijfo};
+            p.NB, p.NJ, p.nJG, p.Hp, p.Bp, p.nBG, p.nxcd, p.xcd_local, p.rev, p.ijfo,
+            len, bd ? p.grid : 0, bd ? bd->ws : 0, bd ? bd->w : 0, bd ? bd->st : 0};
   if (p.bwd_valu) return launch_bwd_vec(p, a, s);
   return launch_bwd_col(p, a, s);
 }

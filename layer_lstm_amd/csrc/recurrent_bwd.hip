@@ -64,7 +64,7 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, fq = lane >> 4;
   int bg, jg;
-  take_role(a.nBG, a.nJG, a.nxcd, a.local, bg, jg);
+  take_role(direction_of(a), a.nBG, a.nJG, a.nxcd, a.local, bg, jg);
   const bool local = a.local != 0;
   const int b0 = bg * a.NB, j0 = jg * a.NJ;
   const int lgNJ = 31 - __builtin_clz(a.NJ);
@@ -134,11 +134,17 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
   auto elem_u = [&](int s) { return j0 + ((tid + NTH * s) & (a.NJ - 1)); };
   auto c_off = [&](int s) { return (uint32_t)elem_b(s) * (uint32_t)a.H + (uint32_t)elem_u(s); };
   float dcc[EPTM], dhc[EPTM];
+  // pass: dh of a step past the sequence's end, which reaches the held
+  // state unchanged (added to the next carry); lens: the row's length
+  float pass[EPTM];
+  int lens[EPTM];
   bool own[EPTM];
 #pragma unroll
   for (int s = 0; s < EPTM; ++s) {
     const int e = tid + NTH * s;
     own[s] = e < nel && elem_b(s) < a.B && elem_u(s) < a.H;
+    pass[s] = 0.f;
+    lens[s] = own[s] ? len_of(a.len, elem_b(s), a.T) : a.T;
     dcc[s] = (own[s] && a.dcT) ? ldf<T>(a.dcT, c_off(s)) : 0.f;
     dhc[s] = (own[s] && a.dhT) ? ldf<T>(a.dhT, c_off(s)) : 0.f;
     if (e < nel) *(f32x4_t*)(dba + 4 * e) = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -279,7 +285,7 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
           float v = 0.f;
 #pragma unroll
           for (int w2 = 0; w2 < NW; ++w2) v += red[(w2 * NBr + bl) * NJS + jj];
-          dhc[s] = v;
+          dhc[s] = v + pass[s];
         }
       }
     } else {
@@ -309,11 +315,16 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
       if (t == 0) cprev = (own[s] && a.c0) ? ldf<T>(a.c0, c_off(s)) : 0.f;
       const float tc = tanh_f(c);
       const float dh = Elem<T>::to_f(pdy[s]) + dhc[s];
+      // past the sequence's end the step held the state: no gate deltas,
+      // the cell carry unchanged, dh passed on to the next carry
+      const bool live = mem_t(t, a.T, a.rev) < lens[s];
+      const float m = live ? 1.f : 0.f;
       const float dc = dh * go * (1.f - tc * tc) + dcc[s];
-      const float d_o = dh * tc * go * (1.f - go);
-      const float d_g = dc * gi * (1.f - gg * gg);
-      const float d_i = dc * gg * gi * (1.f - gi);
-      const float d_f = dc * cprev * gf * (1.f - gf);
+      const float d_o = m * (dh * tc * go * (1.f - go));
+      const float d_g = m * (dc * gi * (1.f - gg * gg));
+      const float d_i = m * (dc * gg * gi * (1.f - gi));
+      const float d_f = m * (dc * cprev * gf * (1.f - gf));
+      pass[s] = live ? 0.f : dh;
       T dq[4] = {Elem<T>::from_f(d_i), Elem<T>::from_f(d_f), Elem<T>::from_f(d_g), Elem<T>::from_f(d_o)};
       if constexpr (E == 4) {
         const u32x4_t v = __builtin_bit_cast(u32x4_t, dq);
@@ -330,7 +341,7 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
           else
             *(uint64_t*)dst = __builtin_bit_cast(uint64_t, dq);
         }
-        dcc[s] = dc * gf;
+        dcc[s] = live ? dc * gf : dcc[s];
         *(f32x4_t*)(dba + 4 * (tid + NTH * s)) += f32x4_t{d_i, d_f, d_g, d_o};
         // gate rows 4u..4u+3 of row bl: chunk kc, bytes [o, o + 4E) of it
         const uint32_t bl = (uint32_t)(elem_b(s) - b0), ob = 4u * E * (uint32_t)elem_u(s);
@@ -399,13 +410,13 @@ template <typename T, int NBT, int MT, int NW, bool DEF>
 static hipError_t bwd_col_nkb(const Plan& p, BwdArgs& a, hipStream_t s) {
   const int nt = 64 * NW;
   switch (p.bwd_nkb) {
-    case 1: return coop_launch(bwd_col_kernel<T, NBT, MT, 1, NW, DEF>, p.grid, p.lds_bwd, &a, s, nt);
-    case 2: return coop_launch(bwd_col_kernel<T, NBT, MT, 2, NW, DEF>, p.grid, p.lds_bwd, &a, s, nt);
-    case 4: return coop_launch(bwd_col_kernel<T, NBT, MT, 4, NW, DEF>, p.grid, p.lds_bwd, &a, s, nt);
-    case 8: return coop_launch(bwd_col_kernel<T, NBT, MT, 8, NW, DEF>, p.grid, p.lds_bwd, &a, s, nt);
-    case 16: return coop_launch(bwd_col_kernel<T, NBT, MT, 16, NW, DEF>, p.grid, p.lds_bwd, &a, s, nt);
+    case 1: return coop_launch(bwd_col_kernel<T, NBT, MT, 1, NW, DEF>, launch_grid(p, a), p.lds_bwd, &a, s, nt);
+    case 2: return coop_launch(bwd_col_kernel<T, NBT, MT, 2, NW, DEF>, launch_grid(p, a), p.lds_bwd, &a, s, nt);
+    case 4: return coop_launch(bwd_col_kernel<T, NBT, MT, 4, NW, DEF>, launch_grid(p, a), p.lds_bwd, &a, s, nt);
+    case 8: return coop_launch(bwd_col_kernel<T, NBT, MT, 8, NW, DEF>, launch_grid(p, a), p.lds_bwd, &a, s, nt);
+    case 16: return coop_launch(bwd_col_kernel<T, NBT, MT, 16, NW, DEF>, launch_grid(p, a), p.lds_bwd, &a, s, nt);
     case 32:
-      if constexpr (MT == 1) return coop_launch(bwd_col_kernel<T, NBT, MT, 32, NW, DEF>, p.grid, p.lds_bwd, &a, s, nt);
+      if constexpr (MT == 1) return coop_launch(bwd_col_kernel<T, NBT, MT, 32, NW, DEF>, launch_grid(p, a), p.lds_bwd, &a, s, nt);
       break;
   }
   return hipErrorInvalidValue;

@@ -28,6 +28,13 @@ struct FwdArgs {
   int nBG, nxcd, local;
   int rev;          // 1: the reverse direction (steps run from t = T-1 down to 0)
   int ijfo;         // gate-block order of W (gate_block)
+  const int32_t* len;  // [B] sequence lengths (the seq_length mask in its per-row form) or null
+  // bidirectional launches (grid1 > 0): work-groups [grid1, 2*grid1) run
+  // the reverse direction on the second direction's tensors, at these byte
+  // offsets from the first's: inside the workspace (P, y, record, exchange),
+  // in W, and in the [2][B][H] states
+  int grid1;
+  int64_t bo_ws, bo_w, bo_st;
 };
 
 struct BwdArgs {
@@ -52,7 +59,72 @@ struct BwdArgs {
   int nBG, nxcd, local;
   int rev;          // 1: the reverse direction (the forward ran from t = T-1 down to 0)
   int ijfo;         // gate-block order of W (gate_block)
+  const int32_t* len;  // [B] sequence lengths or null (see FwdArgs)
+  int grid1;           // bidirectional launches, as in FwdArgs
+  int64_t bo_ws, bo_w, bo_st;
 };
+
+template <typename P>
+__device__ __forceinline__ P* shift_ptr(P* p, int64_t bytes) {
+  return p ? (P*)((char*)const_cast<void*>((const void*)p) + bytes) : p;
+}
+
+// Work-group index within its direction of time.  In a bidirectional
+// launch the second half of the grid takes the reverse direction: its
+// arguments are moved to the second direction's tensors (and its phase
+// stamps are off).
+__device__ __forceinline__ int direction_of(FwdArgs& a) {
+  int i = blockIdx.x;
+  if (a.grid1 > 0 && i >= a.grid1) {
+    i -= a.grid1;
+    a.rev = 1;
+    a.stamps = nullptr;
+    a.P = shift_ptr(a.P, a.bo_ws);
+    a.y = shift_ptr(a.y, a.bo_ws);
+    a.Gs = shift_ptr(a.Gs, a.bo_ws);
+    a.Cs = shift_ptr(a.Cs, a.bo_ws);
+    a.HX = shift_ptr(a.HX, a.bo_ws);
+    a.HD = shift_ptr(a.HD, a.bo_ws);
+    a.HF = shift_ptr(a.HF, a.bo_ws);
+    a.W = shift_ptr(a.W, a.bo_w);
+    a.h0 = shift_ptr(a.h0, a.bo_st);
+    a.c0 = shift_ptr(a.c0, a.bo_st);
+    a.hT = shift_ptr(a.hT, a.bo_st);
+    a.cT = shift_ptr(a.cT, a.bo_st);
+  }
+  return i;
+}
+__device__ __forceinline__ int direction_of(BwdArgs& a) {
+  int i = blockIdx.x;
+  if (a.grid1 > 0 && i >= a.grid1) {
+    i -= a.grid1;
+    a.rev = 1;
+    a.stamps = nullptr;
+    a.dy = shift_ptr(a.dy, a.bo_ws);
+    a.Gs = shift_ptr(a.Gs, a.bo_ws);
+    a.Cs = shift_ptr(a.Cs, a.bo_ws);
+    a.dG = shift_ptr(a.dG, a.bo_ws);
+    a.PX = shift_ptr(a.PX, a.bo_ws);
+    a.GD = shift_ptr(a.GD, a.bo_ws);
+    a.GF = shift_ptr(a.GF, a.bo_ws);
+    a.DBP = shift_ptr(a.DBP, a.bo_ws);
+    a.W = shift_ptr(a.W, a.bo_w);
+    a.c0 = shift_ptr(a.c0, a.bo_st);
+    a.dhT = shift_ptr(a.dhT, a.bo_st);
+    a.dcT = shift_ptr(a.dcT, a.bo_st);
+    a.dh0 = shift_ptr(a.dh0, a.bo_st);
+    a.dc0 = shift_ptr(a.dc0, a.bo_st);
+  }
+  return i;
+}
+
+// Work-groups of a recurrent launch: both directions' in a bidirectional one.
+template <class A>
+inline int launch_grid(const Plan& p, const A& a) { return a.grid1 > 0 ? 2 * p.grid : p.grid; }
+
+// Length of sequence b (T when there are no lengths): steps at times
+// t >= len_of(b) lie past its end.
+__device__ __forceinline__ int len_of(const int32_t* len, int b, int T) { return len ? len[b] : T; }
 
 // Time index in memory of processing step s (s = 0 is the step that reads
 // the initial state): s itself, or T-1-s in the reverse direction.  Loops,
@@ -73,17 +145,18 @@ __device__ __forceinline__ bool err_set(uint32_t* err) {
   return __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u;
 }
 
-// Role of this work-group: (batch group, unit group).  In the XCD-local
+// Role of work-group i of a direction: (batch group, unit group).  In the XCD-local
 // layout, XCD x holds batch groups [x*nBG/nxcd, (x+1)*nBG/nxcd) whole.  The
 // device deals the work-groups of a dispatch to its XCDs round robin from a
 // starting XCD that varies between dispatches, so work-group i runs on XCD
 // (s + i) % nxcd and i / nxcd numbers the work-groups of one XCD without
-// repeats; the XCD itself is read from the hardware.  (Were the dealing
+// repeats; the XCD itself is read from the hardware.  (The second direction
+// of a bidirectional launch starts at grid index grid1, a multiple of nxcd in
+// this layout, so the same holds for its own indices.)  (Were the dealing
 // ever different, two work-groups could take one role -- they would compute
 // and write the same values -- and another role would stay empty, which
 // the bounded waits report as a time-out; results are never mixed.)
-__device__ __forceinline__ void take_role(int nBG, int nJG, int nxcd, int local, int& bg, int& jg) {
-  const int i = blockIdx.x;
+__device__ __forceinline__ void take_role(int i, int nBG, int nJG, int nxcd, int local, int& bg, int& jg) {
   if (!local) {
     bg = i / nJG;
     jg = i % nJG;

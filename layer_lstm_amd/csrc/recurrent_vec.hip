@@ -64,7 +64,7 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_vec_kernel(FwdArgs a) {
   // would run for every wave)
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   int bg, jg;
-  take_role(a.nBG, a.nJG, a.nxcd, a.local, bg, jg);
+  take_role(direction_of(a), a.nBG, a.nJG, a.nxcd, a.local, bg, jg);
   const bool local = a.local != 0;
   const int b0 = bg * a.NB, j0 = jg * a.NJ;  // NB == 4
   const int c = lane & 31, ulb = 2 * w + (lane >> 5);
@@ -94,13 +94,15 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_vec_kernel(FwdArgs a) {
   const int bme_l = c >> 3;
   const bool ew = (c & 7) == 0 && bme_l < NBv;
   const int bme = b0 + bme_l;
-  float cst[U2];
+  float cst[U2], hst[U2];  // state of this lane's elements
   f32x4_t pf[U2];
 #pragma unroll
   for (int q = 0; q < U2; ++q) {
     const int u = j0 + ulb + 8 * q;
     cst[q] = (ew && a.c0 && u < a.H) ? ((const float*)a.c0)[(int64_t)bme * a.H + u] : 0.f;
+    hst[q] = (ew && a.h0 && u < a.H) ? ((const float*)a.h0)[(int64_t)bme * a.H + u] : 0.f;
   }
+  const int lenb = ew ? len_of(a.len, bme, a.T) : a.T;  // length of this lane's batch row
   auto load_p = [&](int tt) {
 #pragma unroll
     for (int q = 0; q < U2; ++q) {
@@ -228,9 +230,14 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_vec_kernel(FwdArgs a) {
         if (u < a.H) {
           const f32x4_t zz = z[q] + pf[q];
           const float ig = sigmoidf(zz[0]), fg = sigmoidf(zz[1]), gg = tanh_f(zz[2]), og = sigmoidf(zz[3]);
-          const float cn = fg * cst[q] + ig * gg;
-          const float h = og * tanh_f(cn);
+          float cn = fg * cst[q] + ig * gg;
+          float h = og * tanh_f(cn);
+          if (mem_t(t, a.T, a.rev) >= lenb) {  // past the sequence's end: the state is held
+            cn = cst[q];
+            h = hst[q];
+          }
           cst[q] = cn;
+          hst[q] = h;
           xstore(dst + (int64_t)bme * a.HW + u, h, (uint32_t)(t + 1), local);
           const int64_t o = (int64_t)mem_t(t, a.T, a.rev) * a.B + bme;
           ((float*)a.y)[o * a.H + u] = h;
@@ -270,7 +277,7 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_vec_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
   int bg, jg;
-  take_role(a.nBG, a.nJG, a.nxcd, a.local, bg, jg);
+  take_role(direction_of(a), a.nBG, a.nJG, a.nxcd, a.local, bg, jg);
   const bool local = a.local != 0;
   const int b0 = bg * a.NB, j0 = jg * a.NJ;
   const int nel = a.NB * a.NJ;               // (batch row, unit) elements: 32 or 64
@@ -313,6 +320,9 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_vec_kernel(BwdArgs a) {
   const bool own = e < nel && bown < a.B && uown < a.H;
   float dcc = (own && a.dcT) ? ((const float*)a.dcT)[(int64_t)bown * a.H + uown] : 0.f;
   float dhc = (own && a.dhT) ? ((const float*)a.dhT)[(int64_t)bown * a.H + uown] : 0.f;
+  // dh of a step past the sequence's end reaches the held state unchanged
+  float pass = 0.f;
+  const int lenb = own ? len_of(a.len, bown, a.T) : a.T;
 
   // elementwise operands of a step (activated gates, c_t, c_{t-1}, dy_t),
   // prefetched one step ahead
@@ -366,7 +376,7 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_vec_kernel(BwdArgs a) {
       if (e < nel) {
         float v = 0.f;
         for (int q = 0; q < TPE; ++q) v += sums[tid + q * nel];
-        dhc = v;
+        dhc = v + pass;
       }
       __syncthreads();
     }
@@ -382,12 +392,15 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_vec_kernel(BwdArgs a) {
         const float gi = pg[0], gf = pg[1], gg = pg[2], go = pg[3];
         const float tc = tanh_f(pc);
         const float dh = pdy + dhc;
+        const bool live = mem_t(t, a.T, a.rev) < lenb;
+        const float m = live ? 1.f : 0.f;
         const float dc = dh * go * (1.f - tc * tc) + dcc;
-        const float d_o = dh * tc * go * (1.f - go);
-        const float d_g = dc * gi * (1.f - gg * gg);
-        const float d_i = dc * gg * gi * (1.f - gi);
-        const float d_f = dc * pcp * gf * (1.f - gf);
-        dcc = dc * gf;
+        const float d_o = m * (dh * tc * go * (1.f - go));
+        const float d_g = m * (dc * gi * (1.f - gg * gg));
+        const float d_i = m * (dc * gg * gi * (1.f - gi));
+        const float d_f = m * (dc * pcp * gf * (1.f - gf));
+        dcc = live ? dc * gf : dcc;
+        pass = live ? 0.f : dh;
         dq = f32x4_t{d_i, d_f, d_g, d_o};
         *(f32x4_t*)(dba + 4 * e) += dq;
         *(f32x4_t*)((float*)a.dG + o * G4 + 4 * (int64_t)uown) = dq;
@@ -496,10 +509,10 @@ static hipError_t fwd_vec_l(const Plan& p, FwdArgs& a, hipStream_t s) {
   const int L = vec_chunk(p);
   const size_t lds = (size_t)4 * 32 * (L + 4) * sizeof(float);
   switch (L) {
-    case 4: return coop_launch(fwd_vec_kernel<4, U2, C>, p.grid, lds, &a, s);
-    case 8: return coop_launch(fwd_vec_kernel<8, U2, C>, p.grid, lds, &a, s);
+    case 4: return coop_launch(fwd_vec_kernel<4, U2, C>, launch_grid(p, a), lds, &a, s);
+    case 8: return coop_launch(fwd_vec_kernel<8, U2, C>, launch_grid(p, a), lds, &a, s);
     case 16:
-      if constexpr (U2 == 1) return coop_launch(fwd_vec_kernel<16, U2, C>, p.grid, lds, &a, s);
+      if constexpr (U2 == 1) return coop_launch(fwd_vec_kernel<16, U2, C>, launch_grid(p, a), lds, &a, s);
       break;
   }
   return hipErrorInvalidValue;
@@ -519,12 +532,12 @@ hipError_t launch_bwd_vec(const Plan& p, BwdArgs& a, hipStream_t s) {
   const int vnct = p.Hp <= kRecThreads ? 1 : p.Hp / kRecThreads;
   const bool wide = p.words_per_thread > 4;
   if (p.NJ == 8) {
-    if (vnct == 1) return coop_launch(wide ? bwd_vec_kernel<1, 32, 16> : bwd_vec_kernel<1, 32, 4>, p.grid, p.lds_bwd, &a, s);
-    if (vnct == 2) return coop_launch(wide ? bwd_vec_kernel<2, 32, 16> : bwd_vec_kernel<2, 32, 4>, p.grid, p.lds_bwd, &a, s);
-    if (vnct == 4) return coop_launch(wide ? bwd_vec_kernel<4, 32, 16> : bwd_vec_kernel<4, 32, 4>, p.grid, p.lds_bwd, &a, s);
+    if (vnct == 1) return coop_launch(wide ? bwd_vec_kernel<1, 32, 16> : bwd_vec_kernel<1, 32, 4>, launch_grid(p, a), p.lds_bwd, &a, s);
+    if (vnct == 2) return coop_launch(wide ? bwd_vec_kernel<2, 32, 16> : bwd_vec_kernel<2, 32, 4>, launch_grid(p, a), p.lds_bwd, &a, s);
+    if (vnct == 4) return coop_launch(wide ? bwd_vec_kernel<4, 32, 16> : bwd_vec_kernel<4, 32, 4>, launch_grid(p, a), p.lds_bwd, &a, s);
   }
   if (p.NJ == 16 && vnct == 1)
-    return coop_launch(wide ? bwd_vec_kernel<1, 64, 16> : bwd_vec_kernel<1, 64, 4>, p.grid, p.lds_bwd, &a, s);
+    return coop_launch(wide ? bwd_vec_kernel<1, 64, 16> : bwd_vec_kernel<1, 64, 4>, launch_grid(p, a), p.lds_bwd, &a, s);
   return hipErrorInvalidValue;
 }
 

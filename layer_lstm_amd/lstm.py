@@ -21,10 +21,11 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 # --- constants restated from include/lstm.h ---------------------------------
-ABI_VERSION = 2
+ABI_VERSION = 3
 REVERSE = 1  # lstm_shape.flags: the reverse direction of time
 GATES_IJFO = 2  # lstm_shape.flags: W/b/dW/db row blocks in the gate order i, g, f, o
 TWO_BIAS = 4  # lstm_shape.flags: b and db are [2][4H] (b_ih, b_hh)
+BIDIRECTIONAL = 8  # lstm_shape.flags: both directions of time, outputs side by side
 GATE_I, GATE_F, GATE_G, GATE_O = 0, 1, 2, 3
 F32, BF16, F16 = 0, 1, 2
 OK = 0
@@ -36,7 +37,7 @@ EXPORTS = ("lstm_abi_version", "lstm_status_string", "lstm_query", "lstm_query_p
            "lstm_fwd_train_scratch", "lstm_bwd", "lstm_check_workspace", "lstm_timing_enable", "lstm_timing_read", "lstm_stamps_set")
 STAMP_WGS, STAMP_POINTS = 8, 6
 KERNEL_KINDS = ("input_projection", "forward_recurrence", "backward_recurrence", "dW_product",
-                "dx_product", "unused", "state_copy")
+                "dx_product", "direction_copy", "state_copy")
 
 
 class Shape(ctypes.Structure):
@@ -47,8 +48,8 @@ class Shape(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("rows_per_group", "units_per_group", "groups", "units_groups",
                                                "grid", "waves", "xcd_local", "fwd_valu", "bwd_valu",
-                                               "inproj_tiles_per_wg")] + \
-               [("reserved", ctypes.c_int32 * 6)]
+                                               "inproj_tiles_per_wg", "directions_concurrent")] + \
+               [("reserved", ctypes.c_int32 * 5)]
 
 
 _P = ctypes.c_void_p
@@ -60,11 +61,11 @@ _lib.lstm_query.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(ctypes.c_size_
 _lib.lstm_query_plan.restype = ctypes.c_int
 _lib.lstm_query_plan.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(PlanInfo)]
 _lib.lstm_fwd_train.restype = ctypes.c_int
-_lib.lstm_fwd_train.argtypes = [ctypes.POINTER(Shape)] + [_P] * 8 + [_P, ctypes.c_size_t, _P]
+_lib.lstm_fwd_train.argtypes = [ctypes.POINTER(Shape)] + [_P] * 9 + [_P, ctypes.c_size_t, _P]
 _lib.lstm_fwd_train_scratch.restype = ctypes.c_int
-_lib.lstm_fwd_train_scratch.argtypes = [ctypes.POINTER(Shape)] + [_P] * 8 + [_P]
+_lib.lstm_fwd_train_scratch.argtypes = [ctypes.POINTER(Shape)] + [_P] * 9 + [_P]
 _lib.lstm_bwd.restype = ctypes.c_int
-_lib.lstm_bwd.argtypes = [ctypes.POINTER(Shape)] + [_P] * 8 + [_P, ctypes.c_size_t] + [_P] * 5 + [_P]
+_lib.lstm_bwd.argtypes = [ctypes.POINTER(Shape)] + [_P] * 9 + [_P, ctypes.c_size_t] + [_P] * 5 + [_P]
 _lib.lstm_check_workspace.restype = ctypes.c_int
 _lib.lstm_check_workspace.argtypes = [_P, ctypes.c_size_t, _P]
 _lib.lstm_timing_enable.restype = ctypes.c_int
@@ -98,10 +99,11 @@ def torch_dtype(dtype: int):
     return {F32: torch.float32, BF16: torch.bfloat16, F16: torch.float16}[dtype]
 
 
-def make_shape(T, B, I, H, dtype, reverse=False, gate_order="ifjo", two_bias=False) -> Shape:
+def make_shape(T, B, I, H, dtype, reverse=False, gate_order="ifjo", two_bias=False, bidirectional=False) -> Shape:
     if gate_order not in ("ifjo", "ijfo"):
         raise ValueError(f"gate_order {gate_order!r}: 'ifjo' or 'ijfo'")
-    flags = (REVERSE if reverse else 0) | (GATES_IJFO if gate_order == "ijfo" else 0) | (TWO_BIAS if two_bias else 0)
+    flags = (REVERSE if reverse else 0) | (GATES_IJFO if gate_order == "ijfo" else 0) | \
+        (TWO_BIAS if two_bias else 0) | (BIDIRECTIONAL if bidirectional else 0)
     return Shape(int(T), int(B), int(I), int(H), int(dtype), flags)
 
 
@@ -136,36 +138,39 @@ def _stream(stream):
     return stream.cuda_stream
 
 
-def fwd_train(shape, x, W, b, h0, c0, y, hT, cT, workspace, ws_bytes=None, stream=None, check=True):
-    """lstm_fwd_train on torch tensors (None = NULL).  Returns the status."""
+def fwd_train(shape, x, W, b, h0, c0, y, hT, cT, workspace, ws_bytes=None, stream=None, check=True,
+              seq_length=None):
+    """lstm_fwd_train on torch tensors (None = NULL; seq_length: int32 [B]
+    device tensor of sequence lengths).  Returns the status."""
     if ws_bytes is None:
         ws_bytes = workspace.numel() * workspace.element_size()
     rc = _lib.lstm_fwd_train(ctypes.byref(shape), _ptr(x), _ptr(W), _ptr(b), _ptr(h0), _ptr(c0),
-                             _ptr(y), _ptr(hT), _ptr(cT), _ptr(workspace), ws_bytes, _stream(stream))
+                             _ptr(seq_length), _ptr(y), _ptr(hT), _ptr(cT), _ptr(workspace), ws_bytes,
+                             _stream(stream))
     if check and rc != OK:
         raise LstmError(rc, "lstm_fwd_train")
     return rc
 
 
-def fwd_train_scratch(shape, x, W, b, h0, c0, y, hT, cT, stream=None, check=True):
+def fwd_train_scratch(shape, x, W, b, h0, c0, y, hT, cT, stream=None, check=True, seq_length=None):
     """lstm_fwd_train_scratch on torch tensors (None = NULL): the forward
     pass with the library's own device array as the workspace.  Returns the
     status."""
     rc = _lib.lstm_fwd_train_scratch(ctypes.byref(shape), _ptr(x), _ptr(W), _ptr(b), _ptr(h0), _ptr(c0),
-                                     _ptr(y), _ptr(hT), _ptr(cT), _stream(stream))
+                                     _ptr(seq_length), _ptr(y), _ptr(hT), _ptr(cT), _stream(stream))
     if check and rc != OK:
         raise LstmError(rc, "lstm_fwd_train_scratch")
     return rc
 
 
 def bwd(shape, dy, dhT, dcT, x, W, h0, c0, y, workspace, dx, dW, db, dh0, dc0, ws_bytes=None,
-        stream=None, check=True):
+        stream=None, check=True, seq_length=None):
     """lstm_bwd on torch tensors (None = NULL).  Returns the status."""
     if ws_bytes is None:
         ws_bytes = workspace.numel() * workspace.element_size()
     rc = _lib.lstm_bwd(ctypes.byref(shape), _ptr(dy), _ptr(dhT), _ptr(dcT), _ptr(x), _ptr(W),
-                       _ptr(h0), _ptr(c0), _ptr(y), _ptr(workspace), ws_bytes, _ptr(dx), _ptr(dW),
-                       _ptr(db), _ptr(dh0), _ptr(dc0), _stream(stream))
+                       _ptr(h0), _ptr(c0), _ptr(seq_length), _ptr(y), _ptr(workspace), ws_bytes, _ptr(dx),
+                       _ptr(dW), _ptr(db), _ptr(dh0), _ptr(dc0), _stream(stream))
     if check and rc != OK:
         raise LstmError(rc, "lstm_bwd")
     return rc
@@ -208,30 +213,32 @@ class Lstm:
     device.  ``forward``/``backward`` take device tensors and return device
     tensors; nothing is synchronised."""
 
-    def __init__(self, T, B, I, H, dtype=F32, device="cuda", reverse=False, gate_order="ifjo", two_bias=False):
-        self.shape = make_shape(T, B, I, H, dtype, reverse, gate_order, two_bias)
+    def __init__(self, T, B, I, H, dtype=F32, device="cuda", reverse=False, gate_order="ifjo", two_bias=False,
+                 bidirectional=False):
+        self.shape = make_shape(T, B, I, H, dtype, reverse, gate_order, two_bias, bidirectional)
         self.T, self.B, self.I, self.H, self.dtype = T, B, I, H, dtype
         self.tdtype = torch_dtype(dtype)
         self.ws_bytes = query(self.shape)
         self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
         dev, td = device, self.tdtype
-        self.y = torch.empty((T, B, H), dtype=td, device=dev)
-        self.hT = torch.empty((B, H), dtype=td, device=dev)
-        self.cT = torch.empty((B, H), dtype=td, device=dev)
+        nd = (2,) if bidirectional else ()
+        self.y = torch.empty((T, B, 2 * H if bidirectional else H), dtype=td, device=dev)
+        self.hT = torch.empty(nd + (B, H), dtype=td, device=dev)
+        self.cT = torch.empty(nd + (B, H), dtype=td, device=dev)
         self.dx = torch.empty((T, B, I), dtype=td, device=dev)
-        self.dW = torch.empty((4 * H, H + I), dtype=td, device=dev)
-        self.db = torch.empty((2, 4 * H) if two_bias else (4 * H,), dtype=td, device=dev)
-        self.dh0 = torch.empty((B, H), dtype=td, device=dev)
-        self.dc0 = torch.empty((B, H), dtype=td, device=dev)
+        self.dW = torch.empty(nd + (4 * H, H + I), dtype=td, device=dev)
+        self.db = torch.empty(nd + ((2, 4 * H) if two_bias else (4 * H,)), dtype=td, device=dev)
+        self.dh0 = torch.empty(nd + (B, H), dtype=td, device=dev)
+        self.dc0 = torch.empty(nd + (B, H), dtype=td, device=dev)
 
-    def forward(self, x, W, b=None, h0=None, c0=None, stream=None):
+    def forward(self, x, W, b=None, h0=None, c0=None, stream=None, seq_length=None):
         fwd_train(self.shape, x, W, b, h0, c0, self.y, self.hT, self.cT, self.workspace,
-                  self.ws_bytes, stream)
+                  self.ws_bytes, stream, seq_length=seq_length)
         return self.y, self.hT, self.cT
 
-    def backward(self, dy, dhT, dcT, x, W, h0=None, c0=None, want_db=True, stream=None):
+    def backward(self, dy, dhT, dcT, x, W, h0=None, c0=None, want_db=True, stream=None, seq_length=None):
         bwd(self.shape, dy, dhT, dcT, x, W, h0, c0, self.y, self.workspace, self.dx, self.dW,
-            self.db if want_db else None, self.dh0, self.dc0, self.ws_bytes, stream)
+            self.db if want_db else None, self.dh0, self.dc0, self.ws_bytes, stream, seq_length=seq_length)
         return self.dx, self.dW, self.db, self.dh0, self.dc0
 
     def check(self, stream=None):

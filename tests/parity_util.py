@@ -39,13 +39,17 @@ def run_gpu(inp, lstm, torch, want_db=True, stream=None, poison=False):
     T, B, I, H, dt = inp["T"], inp["B"], inp["I"], inp["H"], inp["dtype"]
     code = {"f32": lstm.F32, "bf16": lstm.BF16, "f16": lstm.F16}[dt]
     m = lstm.Lstm(T, B, I, H, code, reverse=bool(inp.get("reverse", False)),
-                  gate_order=inp.get("gate_order", "ifjo"), two_bias=bool(inp.get("two_bias", False)))
+                  gate_order=inp.get("gate_order", "ifjo"), two_bias=bool(inp.get("two_bias", False)),
+                  bidirectional=bool(inp.get("bidirectional", False)))
     if poison:
         for k in OUTPUTS:
             getattr(m, k).fill_(float("nan"))
     d = {k: to_dev(inp.get(k), dt, torch) for k in ("x", "W", "b", "h0", "c0", "dy", "dhT", "dcT")}
-    m.forward(d["x"], d["W"], d["b"], d["h0"], d["c0"], stream=stream)
-    m.backward(d["dy"], d["dhT"], d["dcT"], d["x"], d["W"], d["h0"], d["c0"], want_db=want_db, stream=stream)
+    lens = inp.get("lengths")
+    d["len"] = None if lens is None else torch.tensor(np.asarray(lens), dtype=torch.int32, device="cuda")
+    m.forward(d["x"], d["W"], d["b"], d["h0"], d["c0"], stream=stream, seq_length=d["len"])
+    m.backward(d["dy"], d["dhT"], d["dcT"], d["x"], d["W"], d["h0"], d["c0"], want_db=want_db, stream=stream,
+               seq_length=d["len"])
     m.check(stream)
     torch.cuda.synchronize()
     out = dict(y=to_host(m.y), hT=to_host(m.hT), cT=to_host(m.cT), dx=to_host(m.dx), dW=to_host(m.dW),
@@ -83,19 +87,14 @@ def row_errors(got, ref, row_dims):
     return np.where(den > 0, err / np.where(den > 0, den, 1.0), err)
 
 
-# rows of each output: (t, b) rows of y and dx, batch rows of the [B, H]
-# states, gate rows of dW, single values of db
-ROW_DIMS = dict(y=2, dx=2, hT=1, cT=1, dh0=1, dc0=1, dW=1, db=0)
-
-
 def compare_rows(out, ref, tol, keys=OUTPUTS):
     """Worst per-row error of each output (row_errors) and the outputs over
-    `tol`."""
+    `tol`.  Rows: (t, b) rows of y and dx, batch rows of the [B, H] states,
+    gate rows of dW (per direction where there are two), single values of
+    db."""
     worst = {}
     for k in keys:
-        rd = ROW_DIMS[k]
-        if k == "db" and np.ndim(ref[k]) == 2:  # two biases: [2][4H]
-            rd = 0
+        rd = 0 if k == "db" else np.ndim(ref[k]) - 1
         r = row_errors(out[k], ref[k], rd)
         worst[k] = float(r.max()) if r.size else 0.0
     bad = {k: v for k, v in worst.items() if not (v <= tol)}

@@ -47,6 +47,7 @@ def test_constants_match_header(lstm):
     assert header_enum("LSTM_REVERSE") == lstm.REVERSE
     assert header_enum("LSTM_GATES_IJFO") == lstm.GATES_IJFO
     assert header_enum("LSTM_TWO_BIAS") == lstm.TWO_BIAS
+    assert header_enum("LSTM_BIDIRECTIONAL") == lstm.BIDIRECTIONAL
     for code, name in lstm.STATUS.items():
         if code != 0:
             assert header_enum("LSTM_" + name) == code
@@ -91,11 +92,11 @@ def test_query_rejects_bad_dtype_and_nulls(lstm):
     assert lstm.lib().lstm_query_plan(ctypes.byref(lstm.make_shape(2, -1, 2, 2, 0)), ctypes.byref(info)) == -2
     assert info.grid == 0  # untouched on error
     s = lstm.make_shape(2, 2, 2, 2, 0)
-    s.flags = 8  # an unknown flag
+    s.flags = 16  # an unknown flag
     assert lstm.lib().lstm_query(ctypes.byref(s), ctypes.byref(n)) == -3
     assert lstm.lib().lstm_query_plan(ctypes.byref(s), ctypes.byref(info)) == -3
-    assert lstm.lib().lstm_fwd_train(None, *([None] * 9), 0, None) == -1
-    assert lstm.lib().lstm_bwd(None, *([None] * 9), 0, *([None] * 6)) == -1
+    assert lstm.lib().lstm_fwd_train(None, *([None] * 10), 0, None) == -1
+    assert lstm.lib().lstm_bwd(None, *([None] * 10), 0, *([None] * 6)) == -1
 
 
 def test_scratch_entry_point_host_checks(lstm):
@@ -105,4 +106,10 @@ def test_scratch_entry_point_host_checks(lstm):
     m = re.search(r"#define\s+LSTM_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", src)
     assert m and int(m.group(1)) << int(m.group(2)) == lstm.SCRATCH_BYTES
     assert header_enum("LSTM_ERR_SCRATCH") == -11
-    assert lstm.lib().lstm_fwd_train_scratch(None, *([None] * 8), None) == -1
+    assert lstm.lib().lstm_fwd_train_scratch(None, *([None] * 9), None) == -1
+
+
+def test_reverse_and_bidirectional_flags_exclude_each_other(lstm):
+    n = ctypes.c_size_t(0)
+    s = lstm.make_shape(2, 2, 2, 2, 0, reverse=True, bidirectional=True)
+    assert lstm.lib().lstm_query(ctypes.byref(s), ctypes.byref(n)) == -3

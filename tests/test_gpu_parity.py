@@ -663,3 +663,145 @@ def test_f16_workload_every_group(lstm, name, progress):
     for k, v in out.items():
         assert np.all(np.isfinite(v)), k
     check_every_group(lstm, inp, out, m, d, progress)
+
+
+# ---------------------------------------------------------------------------
+# The bidirectional layer (LSTM_BIDIRECTIONAL: the num_directions = 2 layout
+# of the PyTorch recurrent-layer page) and sequence lengths (the seq_length
+# mask of the operator page's parameter table, per-sequence form), against
+# the oracle's composition of its forward and reverse passes and its masked
+# blend.
+
+def contracting(H):
+    """ALL with W, b ~ U(+-1/sqrt(H)), the workloads' range.  ALL's 0.3 at
+    H = 1024 makes the recurrence chaotic (a gain of about 0.3*sqrt(H/3) per
+    step), so that over a hundred steps the rounding of the stored values
+    grows into errors of whole percent on both sides alike; long sequences at
+    large H take this range instead."""
+    k = 1.0 / np.sqrt(H)
+    return dict(ALL, W=("u", k), b=("u", k))
+
+
+def bidir_gpu_inputs(dt, T, B, I, H, seed, dist=ALL):
+    if dist is None:
+        dist = contracting(H)
+    a = synth.make_inputs(T, B, I, H, dt, seed=seed, dist=dist)
+    c = synth.make_inputs(T, B, I, H, dt, seed=seed + 1000, dist=dist)
+    inp = dict(a, bidirectional=True, dy=np.concatenate([a["dy"], c["dy"]], axis=2))
+    for k in ("W", "b", "h0", "c0", "dhT", "dcT"):
+        inp[k] = None if a[k] is None else np.stack([a[k], c[k]])
+    return inp
+
+
+# fp32 VALU recurrences (4-row groups), the fp32 MFMA forward, 16-bit MFMA
+# recurrences with and without the forward's direct-to-LDS path and the
+# XCD-local layout; the T=64 B=32 I=256 H=256 and T=128 B=64 I=512 H=1024
+# workload shapes; a ragged one.
+@pytest.mark.parametrize("dt,T,B,I,H", [
+    ("f32", 8, 4, 16, 32),
+    ("f32", 64, 32, 256, 256),
+    ("f32", 3, 100, 16, 256),
+    ("bf16", 4, 19, 40, 72),
+    ("bf16", 3, 60, 32, 512),
+    ("f16", 5, 40, 64, 1024),
+    ("bf16", 128, 64, 512, 1024),
+])
+def test_bidirectional(lstm, dt, T, B, I, H):
+    inp = bidir_gpu_inputs(dt, T, B, I, H, seed=101, dist=ALL if T * H <= 8192 else None)
+    code = {"f32": lstm.F32, "bf16": lstm.BF16, "f16": lstm.F16}[dt]
+    p = lstm.query_plan(lstm.make_shape(T, B, I, H, code, bidirectional=True))
+    say(f"case: bidirectional {dt} T={T} B={B} I={I} H={H}, plan {p}")
+    full_check(inp, lstm)
+
+
+def test_bidirectional_all_flags(lstm):
+    """Both directions with the "ijfo" gate order and two biases."""
+    inp = bidir_gpu_inputs("bf16", 3, 60, 32, 512, seed=103)
+    rng = np.random.default_rng(104)
+    inp["b"] = np.stack([inp["b"], synth.round_to_storage(rng.uniform(-0.3, 0.3, (2, 2048)), "bf16")], axis=1)
+    inp.update(two_bias=True, gate_order="ijfo")
+    say("case: bidirectional, ijfo, two biases")
+    full_check(inp, lstm)
+
+
+def test_bidirectional_is_two_directions_gpu(lstm):
+    """On the GPU the bidirectional layer gives what the forward direction
+    and the reverse direction give as two one-direction calls, within the
+    tolerance (dx: their sum).  Not bit for bit: the concurrent launch lays
+    each direction out for half the compute units, so its sums over units
+    and gate rows group differently."""
+    dt, T, B, I, H = "bf16", 3, 60, 32, 512
+    inp = bidir_gpu_inputs(dt, T, B, I, H, seed=105)
+    both, _, _ = run_gpu(inp, lstm, torch)
+    outs = []
+    for dd in range(2):
+        one = dict(inp, bidirectional=False, reverse=bool(dd), W=inp["W"][dd], b=inp["b"][dd],
+                   dy=inp["dy"][:, :, dd * H:(dd + 1) * H].copy())
+        for k in ("h0", "c0", "dhT", "dcT"):
+            one[k] = inp[k][dd]
+        outs.append(run_gpu(one, lstm, torch)[0])
+    assert rel_l2(both["y"], np.concatenate([outs[0]["y"], outs[1]["y"]], axis=2)) <= TOL[dt]
+    for k in ("hT", "cT", "dW", "db", "dh0", "dc0"):
+        assert rel_l2(both[k], np.stack([outs[0][k], outs[1][k]])) <= TOL[dt], k
+    assert rel_l2(both["dx"], outs[0]["dx"] + outs[1]["dx"]) <= TOL[dt]
+
+
+LENGTHS_DIST = dict(ALL)
+
+
+def ragged_lengths(T, B, seed):
+    """Lengths covering the edges: full (T), longer than T, empty (0),
+    negative, one step, and the rest spread over [1, T]."""
+    rng = np.random.default_rng(seed)
+    L = rng.integers(1, T + 1, size=B)
+    edges = [T, T + 3, 0, -2, 1]
+    L[:min(B, len(edges))] = edges[:min(B, len(edges))]
+    return L.astype(np.int32)
+
+
+@pytest.mark.parametrize("dt,T,B,I,H,rev", [
+    ("f32", 8, 4, 16, 32, False),
+    ("f32", 8, 4, 16, 32, True),
+    ("f32", 64, 32, 256, 256, False),
+    ("f32", 3, 100, 16, 256, True),
+    ("bf16", 6, 19, 40, 72, False),
+    ("bf16", 5, 60, 32, 512, True),
+    ("f16", 7, 40, 64, 1024, False),
+])
+def test_sequence_lengths(lstm, dt, T, B, I, H, rev):
+    inp = synth.make_inputs(T, B, I, H, dt, seed=107, dist=ALL)
+    inp.update(lengths=ragged_lengths(T, B, 108), reverse=rev)
+    say(f"case: lengths {dt} T={T} B={B} I={I} H={H} reverse={rev} lengths[:8]={inp['lengths'][:8]}")
+    full_check(inp, lstm)
+
+
+def test_sequence_lengths_bidirectional(lstm):
+    inp = bidir_gpu_inputs("bf16", 6, 60, 32, 512, seed=109)
+    inp["lengths"] = ragged_lengths(6, 60, 110)
+    say("case: lengths, bidirectional")
+    full_check(inp, lstm)
+
+
+def test_sequence_lengths_full_size(lstm, progress):
+    """T=128 B=64 I=512 H=1024 (bf16) at full size with ragged lengths,
+    every output against the oracle on the whole batch."""
+    name = "bf16_T128_B64_I512_H1024"
+    inp = synth.workload_inputs(name)
+    inp["lengths"] = ragged_lengths(inp["T"], inp["B"], 111)
+    progress(f"case: lengths at full size {name}")
+    out, _, _ = run_gpu(inp, lstm, torch, poison=True)
+    ref = oracle.fwd_bwd(inp)
+    errs, bad = compare(out, ref, "bf16")
+    worst, bad_rows = compare_rows(out, ref, ROW_TOL["bf16"])
+    progress("  rel-L2: " + str({k: f"{v:.2e}" for k, v in errs.items()}))
+    progress("  worst row: " + str({k: f"{v:.2e}" for k, v in worst.items()}))
+    assert not bad and not bad_rows, (bad, bad_rows)
+
+
+def test_full_lengths_are_the_plain_path_gpu(lstm):
+    """Every length >= T gives the same bits as no lengths at all."""
+    inp = synth.make_inputs(5, 60, 32, 512, "bf16", seed=113, dist=ALL)
+    a, _, _ = run_gpu(inp, lstm, torch)
+    b, _, _ = run_gpu(dict(inp, lengths=np.full(60, 5, np.int32)), lstm, torch)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
