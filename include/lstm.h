@@ -88,7 +88,10 @@ enum {
   LSTM_ERR_LAUNCH = -8,      /* a HIP launch failed */
   LSTM_ERR_TIMEOUT = -9,     /* a per-step wait of the recurrent kernels hit its time bound */
   LSTM_ERR_DEVICE = -10,     /* the current device is not gfx950 or could not be queried */
-  LSTM_ERR_SCRATCH = -11     /* lstm_fwd_train_scratch: the shape needs more than LSTM_SCRATCH_BYTES */
+  LSTM_ERR_SCRATCH = -11,    /* lstm_fwd_train_scratch: the shape needs more than LSTM_SCRATCH_BYTES */
+  LSTM_ERR_PLACEMENT = -12   /* lstm_check_workspace: two work-groups of a recurrent launch took one
+                                role (the device dealt them to its XCDs otherwise than the XCD-local
+                                layout assumes); later calls on this device use the spread layout */
 };
 
 /* Direction of time (SingleLayerLstmGrad, 参数说明: the direction attribute,
@@ -235,8 +238,11 @@ int lstm_bwd(const lstm_shape* shape, const void* dy, const void* dhT, const voi
              void* dx, void* dW, void* db, void* dh0, void* dc0, void* stream);
 
 /* Waits for `stream`, then reports (and clears) a time-out that a
- * recurrent kernel recorded in `workspace`: LSTM_ERR_TIMEOUT, else LSTM_OK
- * (or LSTM_ERR_LAUNCH if the stream itself reports an error).  The time-out
+ * recurrent kernel recorded in `workspace`: LSTM_ERR_PLACEMENT when a launch
+ * found two of its work-groups in one role (it then also timed out; later
+ * plans on this device use the spread layout, see lstm_query_plan's
+ * xcd_local), else LSTM_ERR_TIMEOUT, else LSTM_OK (or LSTM_ERR_LAUNCH if the
+ * stream itself reports an error).  The time-out
  * mark is set by the kernels themselves (a per-step wait that exceeded its
  * bound, e.g. because other work held the device's compute units for
  * seconds, or the device did not deal work-groups to its XCDs round robin
@@ -270,6 +276,22 @@ int lstm_timing_read(int kind, double* total_ms, int64_t* launches);
  * [work-group][step in execution order][point].  NULL disables.  Returns
  * LSTM_ERR_WORKSPACE if the buffer is too small for T. */
 int lstm_stamps_set(void* device_buffer, size_t bytes, int64_t T);
+
+/* Test hooks, for the tests of the failure paths (host-side settings that
+ * later calls copy into their launches; every kernel still exits normally):
+ *   LSTM_DEBUG_FAIL_STEP, value s >= 0: at step s (in execution order) of
+ *     every recurrent launch, work-group 0 records a time-out as if its wait
+ *     had run past its bound; value < 0 turns this off;
+ *   LSTM_DEBUG_MISPLACE, value 1: in the XCD-local layout, work-group 0 takes
+ *     the role of the neighbouring XCD, as a device that dealt the
+ *     work-groups differently would make it (two claimants of one role, one
+ *     role empty: the launch times out and reports LSTM_ERR_PLACEMENT);
+ *     0 turns this off;
+ *   LSTM_DEBUG_XCD_LOCAL, value 1: allow the XCD-local layout on the current
+ *     device again after LSTM_ERR_PLACEMENT (0: forbid it).
+ * Returns LSTM_OK, or LSTM_ERR_DIMS for an unknown `what`.  Not thread-safe. */
+enum { LSTM_DEBUG_FAIL_STEP = 1, LSTM_DEBUG_MISPLACE = 2, LSTM_DEBUG_XCD_LOCAL = 3 };
+int lstm_debug_inject(int what, int64_t value);
 
 #ifdef __cplusplus
 } /* extern "C" */

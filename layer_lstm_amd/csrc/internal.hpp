@@ -10,6 +10,10 @@ namespace lstm {
 // Bit of the error word (first 4 bytes of the workspace) that a recurrent
 // kernel sets when one of its per-step waits hits the time bound.
 constexpr uint32_t kErrTimeout = 1u;
+// Bit set (with kErrTimeout) when two work-groups of a launch took one role:
+// the device did not deal the work-groups to its XCDs as the XCD-local
+// layout assumes (one role then stays empty and its readers time out).
+constexpr uint32_t kErrPlacement = 2u;
 
 // Phase stamps of the recurrent kernels (see lstm_stamps_set in lstm.h).
 constexpr int kStampWGs = 8, kPhases = 6;
@@ -50,6 +54,14 @@ struct Plan {
   // region (h ring, gate-delta ring), step flags at these byte offsets
   // inside it
   size_t off_hflags, off_pflags;
+  // role claims of the persistent launches (one word per work-group role,
+  // cleared with their exchange region): at these byte offsets inside HX
+  // (forward) and PX (backward)
+  size_t off_hclaim, off_pclaim;
+  // test hooks (lstm_debug_inject): the step at which work-group 0 acts as
+  // if its wait had timed out (-1: never), and work-group 0 reading the
+  // wrong XCD in the XCD-local layout
+  int fail_step, misplace;
   int rev;          // 1: the reverse direction (steps from t = T-1 down to 0)
   int ijfo;         // 1: W, b, dW, db in the gate order i, g, f, o (gate_block)
   int two_bias;     // 1: b and db are [2][4H] (b_ih, b_hh)

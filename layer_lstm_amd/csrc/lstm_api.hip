@@ -2,6 +2,7 @@
 // argument checks, the work partition and workspace layout, and the launch
 // sequence of each pass.  No device memory is allocated here.
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 #include <string.h>
 
 #include <mutex>
@@ -14,9 +15,18 @@ namespace lstm {
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-static int device_cus(int* cus) {
+// Test hooks (lstm_debug_inject), copied into every plan.
+static int g_fail_step = -1, g_misplace = 0;
+// Devices on which a launch found two work-groups in one role (the XCD
+// dealing differs from what the XCD-local layout assumes): their plans use
+// the spread layout from then on.
+constexpr int kMaxDevices = 64;
+static bool g_spread_only[kMaxDevices];
+
+static int device_cus(int* cus, int* devp = nullptr) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return LSTM_ERR_DEVICE;
+  if (devp) *devp = dev;
   static int cached_dev = -1, cached_cus = 0, cached_ok = 0;
   if (dev != cached_dev) {
     hipDeviceProp_t prop;
@@ -36,9 +46,10 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p, in
   if (H > 2048 || I > 65536 || T > ((int64_t)1 << 30)) return LSTM_ERR_UNSUPPORTED;
   if (T > 0 && B > 0 && T * B > ((int64_t)1 << 31) / (4 * H)) return LSTM_ERR_UNSUPPORTED;
   if (B * H >= ((int64_t)1 << 27)) return LSTM_ERR_UNSUPPORTED;  // per-step buffer offsets fit 31 bits
-  int cus = 0;
-  const int dev = device_cus(&cus);
+  int cus = 0, devno = 0;
+  const int dev = device_cus(&cus, &devno);
   if (dev != LSTM_OK) return dev;
+  const bool spread_only = devno >= 0 && devno < kMaxDevices && g_spread_only[devno];
 
   memset(p, 0, sizeof(*p));
   p->T = T; p->B = B; p->I = I; p->H = H; p->dtype = dtype;
@@ -75,7 +86,7 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p, in
           const int64_t nBG = B > 0 ? (B + NB - 1) / NB : 1;
           const int64_t nJG = (H + NJ - 1) / NJ;
           if (nBG * nJG > cus / cap_div) continue;
-          if (pass == 0 && !(p->nxcd > 1 && nBG % p->nxcd == 0)) continue;
+          if (pass == 0 && (spread_only || !(p->nxcd > 1 && nBG % p->nxcd == 0))) continue;
           const int NBr = NB < 16 ? 16 : NB;
           // forward: NJ/4 M-tiles of 16 interleaved gate rows in groups of
           // MW, the waves of a group splitting k; two tiles per wave when k
@@ -138,7 +149,9 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p, in
   if (2 * ring_rows * 4 * Hp * e >= ((int64_t)1 << 30)) return LSTM_ERR_UNSUPPORTED;
 
   p->max_splits = 8;
-  p->xcd_local = p->nxcd > 1 && p->nBG % p->nxcd == 0;
+  p->xcd_local = !spread_only && p->nxcd > 1 && p->nBG % p->nxcd == 0;
+  p->fail_step = g_fail_step;
+  p->misplace = g_misplace;
 
   const size_t HW = e == 2 ? (size_t)p->Hp / 2 : (size_t)p->Hp;
   // HX: tagged words [2][Bp][HW] (VALU forward), or packed h [2][Bp][Hp] +
@@ -151,6 +164,11 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p, in
   size_t hx = p->off_hflags + nflag, px = p->off_pflags + nflag;
   if (fwd_vec_ok(*p) && hx < 2 * (size_t)p->Bp * HW * 8) hx = 2 * (size_t)p->Bp * HW * 8;
   if (p->bwd_valu && px < 2 * (size_t)p->nJG * p->Hp * p->Bp * 8) px = 2 * (size_t)p->nJG * p->Hp * p->Bp * 8;
+  // the role claims follow, one word per work-group
+  p->off_hclaim = align256(hx);
+  p->off_pclaim = align256(px);
+  hx = p->off_hclaim + (size_t)p->grid * 4;
+  px = p->off_pclaim + (size_t)p->grid * 4;
   size_t off = 0;
   p->off_ctrl = off; off += 256;
   p->off_HX = off; p->bytes_HX = align256(hx); off += p->bytes_HX;
@@ -166,7 +184,6 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p, in
 
 // ---- order of the persistent launches (recurrent_common.hpp) ----
 namespace {
-constexpr int kMaxDevices = 64;
 std::mutex g_persist_mu;
 hipEvent_t g_persist_ev[kMaxDevices];
 hipStream_t g_persist_stream[kMaxDevices];
@@ -335,6 +352,8 @@ const char* lstm_status_string(int status) {
     case LSTM_ERR_TIMEOUT: return "a recurrent step wait timed out";
     case LSTM_ERR_DEVICE: return "current device is not gfx950";
     case LSTM_ERR_SCRATCH: return "shape needs more workspace than the library's scratch array holds";
+    case LSTM_ERR_PLACEMENT:
+      return "work-groups were not dealt to the XCDs as the layout assumed; later calls use the spread layout";
     default: return "unknown status";
   }
 }
@@ -580,9 +599,14 @@ int lstm_check_workspace(void* workspace, size_t workspace_bytes, void* stream) 
   if (hipStreamSynchronize(s) != hipSuccess) return LSTM_ERR_LAUNCH;
   uint32_t word = 0;
   if (hipMemcpy(&word, workspace, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess) return LSTM_ERR_LAUNCH;
-  if (word & kErrTimeout) {
+  if (word & (kErrTimeout | kErrPlacement)) {
     const uint32_t zero = 0;
     if (hipMemcpy(workspace, &zero, sizeof(zero), hipMemcpyHostToDevice) != hipSuccess) return LSTM_ERR_LAUNCH;
+    if (word & kErrPlacement) {
+      int dev = 0;
+      if (hipGetDevice(&dev) == hipSuccess && dev >= 0 && dev < kMaxDevices) g_spread_only[dev] = true;
+      return LSTM_ERR_PLACEMENT;
+    }
     return LSTM_ERR_TIMEOUT;
   }
   return LSTM_OK;
@@ -597,6 +621,25 @@ int lstm_timing_enable(int on) {
       g_launches[k] = 0;
     }
   return LSTM_OK;
+}
+
+int lstm_debug_inject(int what, int64_t value) {
+  switch (what) {
+    case LSTM_DEBUG_FAIL_STEP:
+      g_fail_step = value < 0 || value > INT32_MAX ? -1 : (int)value;
+      return LSTM_OK;
+    case LSTM_DEBUG_MISPLACE:
+      g_misplace = value != 0;
+      return LSTM_OK;
+    case LSTM_DEBUG_XCD_LOCAL: {
+      int dev = 0;
+      if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return LSTM_ERR_DEVICE;
+      g_spread_only[dev] = value == 0;
+      return LSTM_OK;
+    }
+    default:
+      return LSTM_ERR_DIMS;
+  }
 }
 
 int lstm_stamps_set(void* device_buffer, size_t bytes, int64_t T) {

@@ -53,8 +53,10 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
   // a divergent branch would run for every wave)
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, fq = lane >> 4;
+  const int wgi = direction_of(a);
   int bg, jg;
-  take_role(direction_of(a), a.nBG, a.nJG, a.nxcd, a.local, bg, jg);
+  take_role(wgi, a.nBG, a.nJG, a.nxcd, a.local, a.misplace, bg, jg);
+  claim_role(a.claims, bg * a.nJG + jg, a.err);
   const bool local = a.local != 0;
   const int b0 = bg * a.NB, j0 = jg * a.NJ;
   const int MT = a.NJ / 4;                   // M-tiles (16 interleaved gate rows = 4 units)
@@ -291,6 +293,7 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
 
   for (int t = 0; t < a.T; ++t) {
     stamp(a.stamps, a.T, t, 0);
+    inject_failure(a.fail_step, t, wgi, a.err, dead);
     // wait until every work-group of the batch group has published h_{t-1}
     if (t > 0 && tid < a.nJG) wait_flag(a.HF + bg * a.nJG + tid, (uint32_t)t, a.err, dead);
     __syncthreads();  // flags seen; the previous step's readers of Hl are done
@@ -570,6 +573,7 @@ hipError_t launch_fwd_recurrent(const Plan& p, const float* P, const void* W, co
   FwdArgs a{P, W, h0, c0, y, hT, cT, Gs, Cs, HX, hd, (uint32_t*)(hd + p.off_hflags), (uint32_t)p.off_hflags, err,
             stamps, (int)p.T, (int)p.B, (int)p.H, (int)p.Z, p.NB, p.NJ,
             p.nJG, p.Hp, p.Bp, p.esize == 2 ? (p.Hp / 2) : p.Hp, p.nBG, p.nxcd, p.xcd_local, p.rev, p.ijfo,
+            (uint32_t*)(hd + p.off_hclaim), p.fail_step, p.misplace,
             len, bd ? p.grid : 0, bd ? bd->ws : 0, bd ? bd->w : 0, bd ? bd->st : 0};
   if (fwd_vec_ok(p)) return launch_fwd_vec(p, a, s);
   const int nbt = p.NB < 16 ? 1 : p.NB / 16;
@@ -597,6 +601,7 @@ hipError_t launch_bwd_recurrent(const Plan& p, const void* W, const void* c0, co
   BwdArgs a{W, c0, dy, dhT, dcT, Gs, Cs, dG, PX, gd, (uint32_t*)(gd + p.off_pflags), (uint32_t)p.off_pflags,
             DBP, dh0, dc0, err, stamps, (int)p.T, (int)p.B, (int)p.H, (int)p.Z,
             p.NB, p.NJ, p.nJG, p.Hp, p.Bp, p.nBG, p.nxcd, p.xcd_local, p.rev, p.ijfo,
+            (uint32_t*)(gd + p.off_pclaim), p.fail_step, p.misplace,
             len, bd ? p.grid : 0, bd ? bd->ws : 0, bd ? bd->w : 0, bd ? bd->st : 0};
   if (p.bwd_valu) return launch_bwd_vec(p, a, s);
   return launch_bwd_col(p, a, s);

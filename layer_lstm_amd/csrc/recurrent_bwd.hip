@@ -63,8 +63,10 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
   // would run for every wave)
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, fq = lane >> 4;
+  const int wgi = direction_of(a);
   int bg, jg;
-  take_role(direction_of(a), a.nBG, a.nJG, a.nxcd, a.local, bg, jg);
+  take_role(wgi, a.nBG, a.nJG, a.nxcd, a.local, a.misplace, bg, jg);
+  claim_role(a.claims, bg * a.nJG + jg, a.err);
   const bool local = a.local != 0;
   const int b0 = bg * a.NB, j0 = jg * a.NJ;
   const int lgNJ = 31 - __builtin_clz(a.NJ);
@@ -223,6 +225,7 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
   for (int t = a.T - 1; t >= -1; --t) {
     const int step = a.T - 1 - (t < 0 ? 0 : t);
     if (t >= 0) stamp(a.stamps, a.T, step, 0);
+    if (t >= 0) inject_failure(a.fail_step, step, wgi, a.err, dead);
     if (t < a.T - 1) {
       // 1. dh_carry = W_h^T dG_{t+1} for this group's units, complete
       if (tid < a.nJG) wait_flag(a.GF + bg * a.nJG + tid, (uint32_t)(a.T - t - 1), a.err, dead);

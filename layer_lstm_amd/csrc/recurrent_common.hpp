@@ -28,6 +28,8 @@ struct FwdArgs {
   int nBG, nxcd, local;
   int rev;          // 1: the reverse direction (steps run from t = T-1 down to 0)
   int ijfo;         // gate-block order of W (gate_block)
+  uint32_t* claims;    // [grid] role claims (cleared before the launch) or null
+  int fail_step, misplace;  // test hooks (Plan)
   const int32_t* len;  // [B] sequence lengths (the seq_length mask in its per-row form) or null
   // bidirectional launches (grid1 > 0): work-groups [grid1, 2*grid1) run
   // the reverse direction on the second direction's tensors, at these byte
@@ -59,6 +61,8 @@ struct BwdArgs {
   int nBG, nxcd, local;
   int rev;          // 1: the reverse direction (the forward ran from t = T-1 down to 0)
   int ijfo;         // gate-block order of W (gate_block)
+  uint32_t* claims;    // [grid] role claims or null (see FwdArgs)
+  int fail_step, misplace;
   const int32_t* len;  // [B] sequence lengths or null (see FwdArgs)
   int grid1;           // bidirectional launches, as in FwdArgs
   int64_t bo_ws, bo_w, bo_st;
@@ -86,6 +90,7 @@ __device__ __forceinline__ int direction_of(FwdArgs& a) {
     a.HX = shift_ptr(a.HX, a.bo_ws);
     a.HD = shift_ptr(a.HD, a.bo_ws);
     a.HF = shift_ptr(a.HF, a.bo_ws);
+    a.claims = shift_ptr(a.claims, a.bo_ws);
     a.W = shift_ptr(a.W, a.bo_w);
     a.h0 = shift_ptr(a.h0, a.bo_st);
     a.c0 = shift_ptr(a.c0, a.bo_st);
@@ -107,6 +112,7 @@ __device__ __forceinline__ int direction_of(BwdArgs& a) {
     a.PX = shift_ptr(a.PX, a.bo_ws);
     a.GD = shift_ptr(a.GD, a.bo_ws);
     a.GF = shift_ptr(a.GF, a.bo_ws);
+    a.claims = shift_ptr(a.claims, a.bo_ws);
     a.DBP = shift_ptr(a.DBP, a.bo_ws);
     a.W = shift_ptr(a.W, a.bo_w);
     a.c0 = shift_ptr(a.c0, a.bo_st);
@@ -156,15 +162,37 @@ __device__ __forceinline__ bool err_set(uint32_t* err) {
 // ever different, two work-groups could take one role -- they would compute
 // and write the same values -- and another role would stay empty, which
 // the bounded waits report as a time-out; results are never mixed.)
-__device__ __forceinline__ void take_role(int i, int nBG, int nJG, int nxcd, int local, int& bg, int& jg) {
+// (misplace: a test hook -- work-group 0 takes the role its neighbouring XCD
+// would give it, as a device that dealt differently would.)
+__device__ __forceinline__ void take_role(int i, int nBG, int nJG, int nxcd, int local, int misplace, int& bg,
+                                          int& jg) {
   if (!local) {
     bg = i / nJG;
     jg = i % nJG;
     return;
   }
-  const int x = (int)(xcc_id() % (uint32_t)nxcd), k = i / nxcd;
+  const uint32_t shift = (misplace && i == 0) ? 1u : 0u;
+  const int x = (int)((xcc_id() + shift) % (uint32_t)nxcd), k = i / nxcd;
   bg = x * (nBG / nxcd) + k / nJG;
   jg = k % nJG;
+}
+
+// Claim role (bg, jg): a second claimant of one role means the layout's
+// assumption about the dealing failed -- recorded as a time-out with the
+// placement bit (the host then stops using the XCD-local layout).
+__device__ __forceinline__ void claim_role(uint32_t* claims, int role, uint32_t* err) {
+  if (claims && threadIdx.x == 0 && atomicAdd(claims + role, 1u) != 0u) atomicOr(err, kErrTimeout | kErrPlacement);
+}
+
+// Test hook (lstm_debug_inject): at step `fail_step` (in execution order),
+// thread 0 of work-group 0 of each direction acts as if its wait had timed
+// out -- the error word is set and its later waits return at once -- so
+// that the time-out path runs with every kernel still exiting normally.
+__device__ __forceinline__ void inject_failure(int fail_step, int step, int wg, uint32_t* err, bool& dead) {
+  if (fail_step == step && wg == 0 && threadIdx.x == 0) {
+    atomicOr(err, kErrTimeout);
+    dead = true;
+  }
 }
 
 // Tagged-word reads, in two halves so that independent loads can be issued

@@ -63,8 +63,10 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_vec_kernel(FwdArgs a) {
   // branches on it are scalar branches: an s_waitcnt under a divergent branch
   // would run for every wave)
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wgi = direction_of(a);
   int bg, jg;
-  take_role(direction_of(a), a.nBG, a.nJG, a.nxcd, a.local, bg, jg);
+  take_role(wgi, a.nBG, a.nJG, a.nxcd, a.local, a.misplace, bg, jg);
+  claim_role(a.claims, bg * a.nJG + jg, a.err);
   const bool local = a.local != 0;
   const int b0 = bg * a.NB, j0 = jg * a.NJ;  // NB == 4
   const int c = lane & 31, ulb = 2 * w + (lane >> 5);
@@ -120,6 +122,7 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_vec_kernel(FwdArgs a) {
 
   for (int t = 0; t < a.T; ++t) {
     stamp(a.stamps, a.T, t, 0);
+    inject_failure(a.fail_step, t, wgi, a.err, dead);
     const uint64_t* src = a.HX + ((int64_t)((t - 1) & 1) * a.Bp + b0) * a.HW;
     uint32_t off[C];
     uint32_t live = 0;
@@ -276,8 +279,10 @@ template <int VNCT, int VR, int C>
 __global__ void __launch_bounds__(kRecThreads, 1) bwd_vec_kernel(BwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
+  const int wgi = direction_of(a);
   int bg, jg;
-  take_role(direction_of(a), a.nBG, a.nJG, a.nxcd, a.local, bg, jg);
+  take_role(wgi, a.nBG, a.nJG, a.nxcd, a.local, a.misplace, bg, jg);
+  claim_role(a.claims, bg * a.nJG + jg, a.err);
   const bool local = a.local != 0;
   const int b0 = bg * a.NB, j0 = jg * a.NJ;
   const int nel = a.NB * a.NJ;               // (batch row, unit) elements: 32 or 64
@@ -348,6 +353,7 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_vec_kernel(BwdArgs a) {
   for (int t = a.T - 1; t >= -1; --t) {
     const int step = a.T - 1 - (t < 0 ? 0 : t);
     if (t >= 0) stamp(a.stamps, a.T, step, 0);
+    if (t >= 0) inject_failure(a.fail_step, step, wgi, a.err, dead);
     // 1. gather dh_carry: sum over work-groups of the partials produced at
     //    step t+1.  Word idx = jg' * nel + e (e = jj * NB + bl): a thread
     //    always meets the same element, in increasing jg' order, and the TPE

@@ -31,10 +31,12 @@ F32, BF16, F16 = 0, 1, 2
 OK = 0
 STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_DIMS", -3: "ERR_DTYPE", -4: "ERR_ALIGN",
           -5: "ERR_WORKSPACE", -6: "ERR_UNSUPPORTED", -7: "ERR_COOP", -8: "ERR_LAUNCH",
-          -9: "ERR_TIMEOUT", -10: "ERR_DEVICE", -11: "ERR_SCRATCH"}
+          -9: "ERR_TIMEOUT", -10: "ERR_DEVICE", -11: "ERR_SCRATCH", -12: "ERR_PLACEMENT"}
+DEBUG_FAIL_STEP, DEBUG_MISPLACE, DEBUG_XCD_LOCAL = 1, 2, 3  # lstm_debug_inject
 SCRATCH_BYTES = 64 << 20  # LSTM_SCRATCH_BYTES
 EXPORTS = ("lstm_abi_version", "lstm_status_string", "lstm_query", "lstm_query_plan", "lstm_fwd_train",
-           "lstm_fwd_train_scratch", "lstm_bwd", "lstm_check_workspace", "lstm_timing_enable", "lstm_timing_read", "lstm_stamps_set")
+           "lstm_fwd_train_scratch", "lstm_bwd", "lstm_check_workspace", "lstm_timing_enable", "lstm_timing_read",
+           "lstm_stamps_set", "lstm_debug_inject")
 STAMP_WGS, STAMP_POINTS = 8, 6
 KERNEL_KINDS = ("input_projection", "forward_recurrence", "backward_recurrence", "dW_product",
                 "dx_product", "direction_copy", "state_copy")
@@ -72,6 +74,8 @@ _lib.lstm_timing_enable.restype = ctypes.c_int
 _lib.lstm_timing_enable.argtypes = [ctypes.c_int]
 _lib.lstm_timing_read.restype = ctypes.c_int
 _lib.lstm_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+_lib.lstm_debug_inject.restype = ctypes.c_int
+_lib.lstm_debug_inject.argtypes = [ctypes.c_int, ctypes.c_int64]
 _lib.lstm_stamps_set.restype = ctypes.c_int
 _lib.lstm_stamps_set.argtypes = [_P, ctypes.c_size_t, ctypes.c_int64]
 
@@ -195,6 +199,13 @@ def timing_read() -> dict:
             raise LstmError(rc, "lstm_timing_read")
         out[name] = (ms.value, n.value)
     return out
+
+
+def debug_inject(what: int, value: int) -> None:
+    """lstm_debug_inject: the test hooks of the failure paths."""
+    rc = _lib.lstm_debug_inject(int(what), int(value))
+    if rc != OK:
+        raise LstmError(rc, "lstm_debug_inject")
 
 
 def stamps_set(buf, T) -> None:

@@ -113,3 +113,15 @@ def test_reverse_and_bidirectional_flags_exclude_each_other(lstm):
     n = ctypes.c_size_t(0)
     s = lstm.make_shape(2, 2, 2, 2, 0, reverse=True, bidirectional=True)
     assert lstm.lib().lstm_query(ctypes.byref(s), ctypes.byref(n)) == -3
+
+
+def test_debug_inject_host_checks(lstm):
+    """The test hooks: an unknown kind is refused; the step hook is a host
+    setting (no device needed) and is turned off again."""
+    assert lstm.lib().lstm_debug_inject(99, 0) == -2
+    assert lstm.lib().lstm_debug_inject(lstm.DEBUG_FAIL_STEP, 3) == 0
+    assert lstm.lib().lstm_debug_inject(lstm.DEBUG_FAIL_STEP, -1) == 0
+    assert header_enum("LSTM_ERR_PLACEMENT") == -12
+    assert header_enum("LSTM_DEBUG_FAIL_STEP") == lstm.DEBUG_FAIL_STEP
+    assert header_enum("LSTM_DEBUG_MISPLACE") == lstm.DEBUG_MISPLACE
+    assert header_enum("LSTM_DEBUG_XCD_LOCAL") == lstm.DEBUG_XCD_LOCAL

@@ -1,0 +1,93 @@
+"""Failure paths of the persistent recurrences, forced from the host
+(lstm_debug_inject) so that every kernel still exits normally:
+
+ * a time-out recorded at a chosen step (as if a per-step wait had run past
+   its bound) is reported by lstm_check_workspace as LSTM_ERR_TIMEOUT, is
+   sticky until it is reported, and the next call on the same workspace is
+   correct again;
+ * a work-group that takes the role of another XCD's (as on a device that
+   dealt work-groups to its XCDs otherwise than the XCD-local layout
+   assumes) is detected by the role claims and reported as
+   LSTM_ERR_PLACEMENT; later plans use the spread layout, and calls are
+   correct.
+"""
+import numpy as np
+import pytest
+
+from layer_lstm_amd import synth
+from oracle import oracle
+from parity_util import compare, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+ALL = dict(W=("u", 0.3), b=("u", 0.3), x=("n", 1.0), h0=("n", 0.5), c0=("n", 0.5), dy=("n", 1.0),
+           dhT=("n", 1.0), dcT=("n", 1.0))
+
+
+@pytest.fixture(scope="module")
+def lstm():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from layer_lstm_amd import lstm as mod
+    yield mod
+    mod.debug_inject(mod.DEBUG_FAIL_STEP, -1)
+    mod.debug_inject(mod.DEBUG_MISPLACE, 0)
+    mod.debug_inject(mod.DEBUG_XCD_LOCAL, 1)
+
+
+def run(lstm, inp, m=None):
+    dt = inp["dtype"]
+    code = {"f32": lstm.F32, "bf16": lstm.BF16, "f16": lstm.F16}[dt]
+    if m is None:
+        m = lstm.Lstm(inp["T"], inp["B"], inp["I"], inp["H"], code)
+    d = {k: to_dev(inp.get(k), dt, torch) for k in ("x", "W", "b", "h0", "c0", "dy", "dhT", "dcT")}
+    m.forward(d["x"], d["W"], d["b"], d["h0"], d["c0"])
+    m.backward(d["dy"], d["dhT"], d["dcT"], d["x"], d["W"], d["h0"], d["c0"])
+    rc = lstm.check_workspace(m.workspace)
+    out = {k: to_host(getattr(m, k)) for k in ("y", "hT", "cT", "dx", "dW", "db", "dh0", "dc0")}
+    return rc, out, m
+
+
+# the VALU recurrences (fp32, 4-row groups) and the MFMA ones (bf16)
+@pytest.mark.parametrize("dt,T,B,I,H", [("f32", 12, 32, 64, 256), ("bf16", 12, 60, 32, 512)])
+def test_forced_timeout_is_reported_and_recovers(lstm, dt, T, B, I, H):
+    inp = synth.make_inputs(T, B, I, H, dt, seed=121, dist=ALL)
+    print(f"case: forced time-out {dt} T={T} B={B} I={I} H={H}", flush=True)
+    try:
+        lstm.debug_inject(lstm.DEBUG_FAIL_STEP, 5)
+        rc, _, m = run(lstm, inp)
+    finally:
+        lstm.debug_inject(lstm.DEBUG_FAIL_STEP, -1)
+    assert rc == -9, rc
+    # reported once, then cleared
+    assert lstm.check_workspace(m.workspace) == 0
+    rc, out, _ = run(lstm, inp, m)
+    assert rc == 0, rc
+    errs, bad = compare(out, oracle.fwd_bwd(inp), dt)
+    assert not bad, bad
+
+
+def test_misplaced_work_group_is_detected_and_spread_layout_taken(lstm):
+    dt, T, B, I, H = "bf16", 6, 60, 32, 512
+    shape = lstm.make_shape(T, B, I, H, lstm.BF16)
+    if not lstm.query_plan(shape)["xcd_local"]:
+        pytest.skip("this shape is not laid out XCD-local on this device")
+    inp = synth.make_inputs(T, B, I, H, dt, seed=123, dist=ALL)
+    print("case: misplaced work-group", flush=True)
+    try:
+        lstm.debug_inject(lstm.DEBUG_MISPLACE, 1)
+        rc, _, _ = run(lstm, inp)
+        lstm.debug_inject(lstm.DEBUG_MISPLACE, 0)
+        assert rc == -12, rc
+        # later plans on this device avoid the XCD-local layout, and are right
+        assert lstm.query_plan(shape)["xcd_local"] == 0
+        rc, out, _ = run(lstm, inp)
+        assert rc == 0, rc
+        errs, bad = compare(out, oracle.fwd_bwd(inp), dt)
+        assert not bad, bad
+    finally:
+        lstm.debug_inject(lstm.DEBUG_MISPLACE, 0)
+        lstm.debug_inject(lstm.DEBUG_XCD_LOCAL, 1)
+    assert lstm.query_plan(shape)["xcd_local"] == 1
