@@ -277,6 +277,20 @@ int lstm_timing_read(int kind, double* total_ms, int64_t* launches);
  * LSTM_ERR_WORKSPACE if the buffer is too small for T. */
 int lstm_stamps_set(void* device_buffer, size_t bytes, int64_t T);
 
+/* The floor under a recurrence step, for measurement: runs the forward
+ * recurrence's per-step exchange alone -- the step flags of the batch group,
+ * the copy of the group's h rows from the exchange ring into LDS, this
+ * work-group's stores into the next ring slot and its flag -- for T steps,
+ * in the layout lstm_fwd_train() uses for `shape` (layout 0), or that
+ * layout with its batch groups spread over the XCDs (layout 1: device-
+ * coherent stores, every exchange through memory), without the product or
+ * the gate math.  `workspace` (lstm_query() bytes) is overwritten.  Waits
+ * for the stream; sets *us_per_step to the launch's time / T.  Returns
+ * LSTM_OK, an error of lstm_query(), LSTM_ERR_DIMS (T or B < 1, or another
+ * layout), or LSTM_ERR_TIMEOUT. */
+int lstm_probe_exchange(const lstm_shape* shape, int layout, void* workspace, size_t workspace_bytes,
+                        double* us_per_step, void* stream);
+
 /* Test hooks, for the tests of the failure paths (host-side settings that
  * later calls copy into their launches; every kernel still exits normally):
  *   LSTM_DEBUG_FAIL_STEP, value s >= 0: at step s (in execution order) of

@@ -133,6 +133,9 @@ hipError_t launch_bwd_recurrent(const Plan& p, const void* W, const void* c0, co
                                 const void* dhT, const void* dcT, const void* Gs, const float* Cs,
                                 void* dG, uint64_t* PX, float* DBP, void* dh0, void* dc0, uint32_t* err,
                                 uint64_t* stamps, const int32_t* len, const Bidir* bd, hipStream_t s);
+// The forward recurrence's exchange alone (exchange_probe.hip): flags, ring
+// copy, ring stores, no arithmetic; HX must start cleared.
+hipError_t launch_exchange_probe(const Plan& p, void* HX, uint32_t* err, hipStream_t s);
 // The two directions' [rows][H] outputs side by side into [rows][2H]
 // (join), or [rows][2H] cotangents back into two [rows][H] (split).
 hipError_t launch_join_dirs(const void* y0, const void* y1, void* y, int64_t rows, int64_t row_bytes, hipStream_t s);

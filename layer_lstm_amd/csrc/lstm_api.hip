@@ -623,6 +623,38 @@ int lstm_timing_enable(int on) {
   return LSTM_OK;
 }
 
+int lstm_probe_exchange(const lstm_shape* shape, int layout, void* workspace, size_t workspace_bytes,
+                        double* us_per_step, void* stream) {
+  if (!shape || !workspace || !us_per_step) return LSTM_ERR_NULL;
+  if (layout != 0 && layout != 1) return LSTM_ERR_DIMS;
+  Plan p;
+  const int rc = plan_for(shape, &p);
+  if (rc != LSTM_OK) return rc;
+  if (p.T < 1 || p.B < 1) return LSTM_ERR_DIMS;
+  if (((uintptr_t)workspace & 255u)) return LSTM_ERR_ALIGN;
+  if (workspace_bytes < p.total) return LSTM_ERR_WORKSPACE;
+  if (layout == 1) p.xcd_local = 0;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return LSTM_ERR_LAUNCH;
+  }
+  hipError_t err = launch_fill_zero(ws + p.off_ctrl, p.off_PX + p.bytes_PX - p.off_ctrl, s);
+  if (err == hipSuccess) err = hipEventRecord(e0, s);
+  if (err == hipSuccess) err = launch_exchange_probe(p, ws + p.off_HX, (uint32_t*)(ws + p.off_ctrl), s);
+  if (err == hipSuccess) err = hipEventRecord(e1, s);
+  if (err == hipSuccess) err = hipEventSynchronize(e1);
+  float ms = 0.f;
+  if (err == hipSuccess) err = hipEventElapsedTime(&ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (err != hipSuccess) return status_of(err);
+  *us_per_step = (double)ms * 1e3 / (double)p.T;
+  return lstm_check_workspace(workspace, workspace_bytes, stream);
+}
+
 int lstm_debug_inject(int what, int64_t value) {
   switch (what) {
     case LSTM_DEBUG_FAIL_STEP:

@@ -36,7 +36,7 @@ DEBUG_FAIL_STEP, DEBUG_MISPLACE, DEBUG_XCD_LOCAL = 1, 2, 3  # lstm_debug_inject
 SCRATCH_BYTES = 64 << 20  # LSTM_SCRATCH_BYTES
 EXPORTS = ("lstm_abi_version", "lstm_status_string", "lstm_query", "lstm_query_plan", "lstm_fwd_train",
            "lstm_fwd_train_scratch", "lstm_bwd", "lstm_check_workspace", "lstm_timing_enable", "lstm_timing_read",
-           "lstm_stamps_set", "lstm_debug_inject")
+           "lstm_stamps_set", "lstm_probe_exchange", "lstm_debug_inject")
 STAMP_WGS, STAMP_POINTS = 8, 6
 KERNEL_KINDS = ("input_projection", "forward_recurrence", "backward_recurrence", "dW_product",
                 "dx_product", "direction_copy", "state_copy")
@@ -74,6 +74,9 @@ _lib.lstm_timing_enable.restype = ctypes.c_int
 _lib.lstm_timing_enable.argtypes = [ctypes.c_int]
 _lib.lstm_timing_read.restype = ctypes.c_int
 _lib.lstm_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+_lib.lstm_probe_exchange.restype = ctypes.c_int
+_lib.lstm_probe_exchange.argtypes = [ctypes.POINTER(Shape), ctypes.c_int, _P, ctypes.c_size_t,
+                                     ctypes.POINTER(ctypes.c_double), _P]
 _lib.lstm_debug_inject.restype = ctypes.c_int
 _lib.lstm_debug_inject.argtypes = [ctypes.c_int, ctypes.c_int64]
 _lib.lstm_stamps_set.restype = ctypes.c_int
@@ -199,6 +202,18 @@ def timing_read() -> dict:
             raise LstmError(rc, "lstm_timing_read")
         out[name] = (ms.value, n.value)
     return out
+
+
+def probe_exchange(shape: Shape, workspace, layout: int = 0, stream=None) -> float:
+    """lstm_probe_exchange: microseconds per step of the forward
+    recurrence's exchange alone (layout 0: the plan's own; 1: spread over
+    the XCDs)."""
+    us = ctypes.c_double(0)
+    rc = _lib.lstm_probe_exchange(ctypes.byref(shape), int(layout), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), ctypes.byref(us), _stream(stream))
+    if rc != OK:
+        raise LstmError(rc, "lstm_probe_exchange")
+    return us.value
 
 
 def debug_inject(what: int, value: int) -> None:

@@ -91,3 +91,16 @@ def test_misplaced_work_group_is_detected_and_spread_layout_taken(lstm):
         lstm.debug_inject(lstm.DEBUG_MISPLACE, 0)
         lstm.debug_inject(lstm.DEBUG_XCD_LOCAL, 1)
     assert lstm.query_plan(shape)["xcd_local"] == 1
+
+
+def test_exchange_probe_runs_in_both_layouts(lstm):
+    """lstm_probe_exchange (the forward's exchange alone) completes without a
+    time-out in the workload layouts and spread, and a step of it costs less
+    than a step of the real forward recurrence."""
+    for name in ("f32_T64_B32_I256_H256", "bf16_T256_B256_I1024_H1024"):
+        w = synth.WORKLOADS[name]
+        code = lstm.F32 if w.dtype == "f32" else lstm.BF16
+        m = lstm.Lstm(w.T, w.B, w.I, w.H, code)
+        us = [lstm.probe_exchange(m.shape, m.workspace, layout) for layout in (0, 1)]
+        print(name, "floor us/step", us, flush=True)
+        assert all(0 < u < 50 for u in us)
