@@ -183,6 +183,8 @@ def fwd_bwd(inp: dict) -> dict:
     two_bias (b and db [2][4H]), mask ([T,B,H], the seq_length mask matrix)
     or lengths ([B], turned into that mask by length_mask), and
     bidirectional (see below)."""
+    if inp.get("layers"):
+        return stacked_fwd_bwd(inp)
     if inp.get("bidirectional"):
         # Two directions of one layer: direction 0 runs forward in time and
         # direction 1 in reverse, each with its own W, b and initial state
@@ -232,4 +234,45 @@ def fwd_bwd(inp: dict) -> dict:
              inp.get("dhT"), inp.get("dcT"), reverse=rev, mask=mask)
     out = {k: fw[k] for k in ("y", "hT", "cT")}
     out.update(bw)
+    return out
+
+
+def stacked_fwd_bwd(inp: dict) -> dict:
+    """A stack of inp["layers"] = L one-direction layers (the MXNet page's
+    "Stack Multiple RNN Cells": the output sequence of a layer is the input
+    sequence of the next, each layer with its own initial state; the CMU
+    10-414 page's LSTM module with num_layers: h0, c0 and h_n, c_n of shape
+    [num_layers, B, H], the output the last layer's).
+
+    W is the list of the L weight matrices (layer 0 [4H, H+I], the others
+    [4H, 2H]), b the list of the L biases or None; h0, c0, dhT, dcT are
+    [L][B][H] or None; x [T,B,I]; dy [T,B,H] is the cotangent of the last
+    layer's output.  The backward runs the layers from the last to the
+    first; the input gradient of layer l is the output cotangent of layer
+    l - 1 (only the last layer's output is the stack's output).  Returns y
+    (the last layer's), hT, cT, dh0, dc0 as [L][B][H], dx, and dW, db as
+    lists of the L layers' gradients."""
+    L = int(inp["layers"])
+    x = inp["x"]
+    layer_in, fws, subs = x, [], []
+    for ll in range(L):
+        sub = dict(inp, layers=None, x=layer_in, W=inp["W"][ll], b=None if inp.get("b") is None else inp["b"][ll])
+        for k in ("h0", "c0", "dhT", "dcT"):
+            sub[k] = None if inp.get(k) is None else inp[k][ll]
+        fw = fwd(sub["x"], sub["W"], sub["b"], sub["h0"], sub["c0"])
+        fws.append(fw)
+        subs.append(sub)
+        layer_in = fw["y"]
+    out = {"y": fws[-1]["y"], "hT": np.stack([f["hT"] for f in fws]), "cT": np.stack([f["cT"] for f in fws])}
+    dy = inp["dy"]
+    bws = [None] * L
+    for ll in range(L - 1, -1, -1):
+        sub = subs[ll]
+        bws[ll] = bwd(sub["x"], sub["W"], sub["h0"], sub["c0"], fws[ll], dy, sub["dhT"], sub["dcT"])
+        dy = bws[ll]["dx"]
+    out["dx"] = bws[0]["dx"]
+    out["dW"] = [b["dW"] for b in bws]
+    out["db"] = np.stack([b["db"] for b in bws])
+    out["dh0"] = np.stack([b["dh0"] for b in bws])
+    out["dc0"] = np.stack([b["dc0"] for b in bws])
     return out

@@ -566,3 +566,97 @@ def test_masked_bidirectional_against_torch_packed_sequence():
     np.testing.assert_allclose(out["y"] * valid[:, :, None], ref["y"], rtol=1e-11, atol=1e-13)
     for k in ("hT", "cT", "dx", "dh0", "dc0", "dW", "db"):
         np.testing.assert_allclose(out[k], ref[k], rtol=1e-11, atol=1e-13, err_msg=k)
+
+
+# ---------------------------------------------------------------------------
+# Stacked layers (the MXNet page's "Stack Multiple RNN Cells"; the CMU page's
+# LSTM module with num_layers)
+
+def stacked_inputs(L, T, B, I, H, seed):
+    """Inputs of an L-layer stack: layer 0 sees x [T,B,I], the others the
+    layer below's output (input size H)."""
+    first = full_inputs(T, B, I, H, seed=seed)
+    inp = dict(first, layers=L, W=[first["W"]], b=[first["b"]])
+    for k in ("h0", "c0", "dhT", "dcT"):
+        inp[k] = [first[k]]
+    for ll in range(1, L):
+        nxt = full_inputs(T, B, H, H, seed=seed + 100 * ll)
+        inp["W"].append(nxt["W"])
+        inp["b"].append(nxt["b"])
+        for k in ("h0", "c0", "dhT", "dcT"):
+            inp[k].append(nxt[k])
+    inp["b"] = np.stack(inp["b"])
+    for k in ("h0", "c0", "dhT", "dcT"):
+        inp[k] = np.stack(inp[k])
+    return inp
+
+
+def test_fd_stacked():
+    """Finite differences of the stack's loss (the last layer's outputs, and
+    every layer's final state) with respect to x, every layer's W, b, h0,
+    c0: the input gradient of a layer is the output cotangent of the layer
+    below."""
+    inp = stacked_inputs(3, 3, 2, 2, 2, seed=131)
+    g = oracle.fwd_bwd(inp)
+    params = [("x", None), ("b", None), ("h0", None), ("c0", None)] + [("W", ll) for ll in range(3)]
+    for p, ll in params:
+        base = inp[p] if ll is None else inp[p][ll]
+        grad = g[GRAD_OF[p]] if ll is None else g["dW"][ll]
+        flat, gflat = base.reshape(-1), np.asarray(grad).reshape(-1)
+        for idx in range(flat.size):
+            th = flat[idx]
+            eps = 1e-6 * max(1.0, abs(th))
+            flat[idx] = th + eps
+            lp = outputs_loss(inp, oracle.fwd_bwd(inp))
+            flat[idx] = th - eps
+            lm = outputs_loss(inp, oracle.fwd_bwd(inp))
+            flat[idx] = th
+            fd = (lp - lm) / (2 * eps)
+            assert abs(fd - gflat[idx]) <= 1e-7 * (1.0 + abs(gflat[idx])), (p, ll, idx, fd, gflat[idx])
+
+
+def test_stacked_against_torch_nn_lstm_fp64():
+    """A 3-layer stack against torch.nn.LSTM(num_layers=3) in fp64: every
+    output and every layer's gradients (bias_hh zero)."""
+    torch = pytest.importorskip("torch")
+    L, T, B, I, H = 3, 5, 3, 4, 6
+    inp = stacked_inputs(L, T, B, I, H, seed=133)
+    m = torch.nn.LSTM(I, H, num_layers=L, bias=True, batch_first=False).double()
+    with torch.no_grad():
+        for ll in range(L):
+            getattr(m, f"weight_hh_l{ll}").copy_(torch.from_numpy(inp["W"][ll][:, :H]))
+            getattr(m, f"weight_ih_l{ll}").copy_(torch.from_numpy(inp["W"][ll][:, H:]))
+            getattr(m, f"bias_ih_l{ll}").copy_(torch.from_numpy(inp["b"][ll]))
+            getattr(m, f"bias_hh_l{ll}").zero_()
+    x = torch.from_numpy(inp["x"]).requires_grad_(True)
+    h0 = torch.from_numpy(inp["h0"]).clone().requires_grad_(True)
+    c0 = torch.from_numpy(inp["c0"]).clone().requires_grad_(True)
+    y, (hn, cn) = m(x, (h0, c0))
+    loss_t = (y * torch.from_numpy(inp["dy"])).sum() + (hn * torch.from_numpy(inp["dhT"])).sum() \
+        + (cn * torch.from_numpy(inp["dcT"])).sum()
+    loss_t.backward()
+    out = oracle.fwd_bwd(inp)
+    ref = dict(y=y.detach().numpy(), hT=hn.detach().numpy(), cT=cn.detach().numpy(), dx=x.grad.numpy(),
+               dh0=h0.grad.numpy(), dc0=c0.grad.numpy(),
+               db=np.stack([getattr(m, f"bias_ih_l{ll}").grad.numpy() for ll in range(L)]))
+    for k, v in ref.items():
+        np.testing.assert_allclose(out[k], v, rtol=1e-11, atol=1e-13, err_msg=k)
+    for ll in range(L):
+        dW = np.concatenate([getattr(m, f"weight_hh_l{ll}").grad.numpy(), getattr(m, f"weight_ih_l{ll}").grad.numpy()],
+                            axis=1)
+        np.testing.assert_allclose(out["dW"][ll], dW, rtol=1e-11, atol=1e-13, err_msg=f"dW[{ll}]")
+
+
+def test_one_layer_stack_is_the_layer():
+    """A stack of one layer is the one-layer oracle bit for bit."""
+    inp = stacked_inputs(1, 4, 3, 5, 6, seed=135)
+    a = oracle.fwd_bwd(inp)
+    plain = dict(inp, layers=None, W=inp["W"][0], b=inp["b"][0])
+    for k in ("h0", "c0", "dhT", "dcT"):
+        plain[k] = inp[k][0]
+    b = oracle.fwd_bwd(plain)
+    for k in ("y", "dx"):
+        np.testing.assert_array_equal(a[k], b[k])
+    for k in ("hT", "cT", "db", "dh0", "dc0"):
+        np.testing.assert_array_equal(a[k][0], b[k])
+    np.testing.assert_array_equal(a["dW"][0], b["dW"])
