@@ -116,23 +116,51 @@ size_t gemm_partial_bytes(const Plan& p, int cus);
 // 16-byte aligned operands assumed)
 int inproj_tiles_per_wg(const Plan& p);
 
-// One launch of both directions of a bidirectional layer: the second half
-// of the grid runs the reverse direction on tensors at these byte offsets
-// from the first direction's (workspace, W, [2][B][H] states).
-struct Bidir {
-  int64_t ws, w, st;
+// One recurrence of a persistent launch and its tensors.  A launch runs up
+// to four (the two directions of a bidirectional layer, or the layers of a
+// stack's wave), each on grid work-groups of the plan's layout.
+struct FwdSlot {
+  const float* P;   // [T][B][4H] fp32 input projection of the slot's steps
+  const void* W;    // the layer's [4H][Z] weights (W_h = the first H columns)
+  int64_t Z;        // W's row length: H plus the layer's input size
+  const void* h0;   // [B][H] or null
+  const void* c0;   // [B][H] or null
+  const float* c0f; // [B][H] fp32 initial cell state in place of c0, or null
+  void* y;          // [T][B][H]
+  void* hT;         // [B][H]
+  void* cT;         // [B][H]
+  void* Gs;         // [T][B][4H] activated gates (record)
+  float* Cs;        // [T][B][H] cell states (record)
+  uint64_t* HX;     // the slot's exchange region (cleared before the launch)
+  int T, rev;       // steps of the launch; direction of time
+};
+struct BwdSlot {
+  const void* W;
+  int64_t Z;
+  const void* c0;       // [B][H] or null: c_{-1} of the first step
+  const float* cprevf;  // fp32 c_{-1} of the first step in place of c0, or null
+  const void* dy;       // [T][B][H]
+  const void* dhT;      // [B][H] or null
+  const void* dcT;      // [B][H] or null
+  const void* Gs;
+  const float* Cs;
+  void* dG;             // [T][B][4H] gate deltas (record)
+  uint64_t* PX;         // the slot's exchange region (cleared before the launch)
+  float* DBP;           // [nBG][4H] db partials of the slot's steps, or null
+  void* dh0;
+  void* dc0;
+  float* carry;         // [2][B][H] fp32 carries (dh, dc) or null
+  int carry_in, carry_out;  // read the carries instead of dhT/dcT; write them instead of dh0/dc0
+  int T, rev;
 };
 
-// The persistent recurrences; len: [B] sequence lengths or null; bd: null,
-// or both directions in one launch of twice the plan's grid.
-hipError_t launch_fwd_recurrent(const Plan& p, const float* P, const void* W, const void* h0,
-                                const void* c0, void* y, void* hT, void* cT, void* Gs, float* Cs,
-                                uint64_t* HX, uint32_t* err, uint64_t* stamps, const int32_t* len,
-                                const Bidir* bd, hipStream_t s);
-hipError_t launch_bwd_recurrent(const Plan& p, const void* W, const void* c0, const void* dy,
-                                const void* dhT, const void* dcT, const void* Gs, const float* Cs,
-                                void* dG, uint64_t* PX, float* DBP, void* dh0, void* dc0, uint32_t* err,
-                                uint64_t* stamps, const int32_t* len, const Bidir* bd, hipStream_t s);
+// The persistent recurrences of `nslots` slots in one launch of nslots x
+// grid work-groups (every slot on the plan's layout); len: [B] sequence
+// lengths or null; err: the error word every slot reports to.
+hipError_t launch_fwd_recurrent(const Plan& p, const FwdSlot* slots, int nslots, uint32_t* err, uint64_t* stamps,
+                                const int32_t* len, hipStream_t s);
+hipError_t launch_bwd_recurrent(const Plan& p, const BwdSlot* slots, int nslots, uint32_t* err, uint64_t* stamps,
+                                const int32_t* len, hipStream_t s);
 // The forward recurrence's exchange alone (exchange_probe.hip): flags, ring
 // copy, ring stores, no arithmetic; HX must start cleared.
 hipError_t launch_exchange_probe(const Plan& p, void* HX, uint32_t* err, hipStream_t s);

@@ -465,21 +465,19 @@ int lstm_fwd_train(const lstm_shape* shape, const void* x, const void* W, const 
   }
   const int32_t* len = (const int32_t*)seq_length;
   uint32_t* errw = (uint32_t*)(ws + p.off_ctrl);  // one error word for both directions
+  FwdSlot sl[2];
+  for (int d = 0; d < nd; ++d)
+    sl[d] = FwdSlot{(const float*)(wsd(d) + p.off_P), at(W, d * wst), p.Z, at(h0, d * sst), at(c0, d * sst), nullptr,
+                    ydir(d), (char*)hT + d * sst, (char*)cT + d * sst, wsd(d) + p.off_G, (float*)(wsd(d) + p.off_C),
+                    (uint64_t*)(wsd(d) + p.off_HX), (int)p.T, p.bidir ? d : p.rev};
+  uint64_t* stamps = stamps_fit(p) ? g_stamps_fwd : nullptr;
   if (err == hipSuccess && (!p.bidir || p.concurrent)) {
     Timed tm(1, s);
-    const Bidir bd{(int64_t)p.dir_bytes, wst, sst};
-    err = launch_fwd_recurrent(p, (const float*)(ws + p.off_P), W, h0, c0, ydir(0), hT, cT, ws + p.off_G,
-                               (float*)(ws + p.off_C), (uint64_t*)(ws + p.off_HX), errw,
-                               stamps_fit(p) ? g_stamps_fwd : nullptr, len, p.bidir ? &bd : nullptr, s);
+    err = launch_fwd_recurrent(p, sl, nd, errw, stamps, len, s);
   } else {
     for (int d = 0; d < nd && err == hipSuccess; ++d) {
       Timed tm(1, s);
-      Plan pd = p;
-      pd.rev = d;
-      err = launch_fwd_recurrent(pd, (const float*)(wsd(d) + p.off_P), at(W, d * wst), at(h0, d * sst),
-                                 at(c0, d * sst), ydir(d), (char*)hT + d * sst, (char*)cT + d * sst,
-                                 wsd(d) + p.off_G, (float*)(wsd(d) + p.off_C), (uint64_t*)(wsd(d) + p.off_HX), errw,
-                                 d == 0 && stamps_fit(p) ? g_stamps_fwd : nullptr, len, nullptr, s);
+      err = launch_fwd_recurrent(p, &sl[d], 1, errw, d == 0 ? stamps : nullptr, len, s);
     }
   }
   if (err == hipSuccess && p.bidir) {
@@ -549,23 +547,20 @@ int lstm_bwd(const lstm_shape* shape, const void* dy, const void* dhT, const voi
   // deltas go where the input projection was (dead after the forward).
   const int32_t* len = (const int32_t*)seq_length;
   uint32_t* errw = (uint32_t*)(ws + p.off_ctrl);
+  BwdSlot sl[2];
+  for (int d = 0; d < nd; ++d)
+    sl[d] = BwdSlot{at(W, d * wst), p.Z, at(c0, d * sst), nullptr, dydir(d), at(dhT, d * sst), at(dcT, d * sst),
+                    wsd(d) + p.off_G, (const float*)(wsd(d) + p.off_C), wsd(d) + p.off_P,
+                    (uint64_t*)(wsd(d) + p.off_PX), db ? (float*)(wsd(d) + p.off_dbp) : nullptr,
+                    (char*)dh0 + d * sst, (char*)dc0 + d * sst, nullptr, 0, 0, (int)p.T, p.bidir ? d : p.rev};
+  uint64_t* stamps = stamps_fit(p) ? g_stamps_bwd : nullptr;
   if (err == hipSuccess && (!p.bidir || p.concurrent)) {
     Timed tm(2, s);
-    const Bidir bd{(int64_t)p.dir_bytes, wst, sst};
-    err = launch_bwd_recurrent(p, W, c0, dydir(0), dhT, dcT, ws + p.off_G, (const float*)(ws + p.off_C),
-                               ws + p.off_P, (uint64_t*)(ws + p.off_PX), db ? (float*)(ws + p.off_dbp) : nullptr,
-                               dh0, dc0, errw, stamps_fit(p) ? g_stamps_bwd : nullptr, len, p.bidir ? &bd : nullptr,
-                               s);
+    err = launch_bwd_recurrent(p, sl, nd, errw, stamps, len, s);
   } else {
     for (int d = 0; d < nd && err == hipSuccess; ++d) {
       Timed tm(2, s);
-      Plan pd = p;
-      pd.rev = d;
-      err = launch_bwd_recurrent(pd, at(W, d * wst), at(c0, d * sst), dydir(d), at(dhT, d * sst), at(dcT, d * sst),
-                                 wsd(d) + p.off_G, (const float*)(wsd(d) + p.off_C), wsd(d) + p.off_P,
-                                 (uint64_t*)(wsd(d) + p.off_PX), db ? (float*)(wsd(d) + p.off_dbp) : nullptr,
-                                 (char*)dh0 + d * sst, (char*)dc0 + d * sst, errw,
-                                 d == 0 && stamps_fit(p) ? g_stamps_bwd : nullptr, len, nullptr, s);
+      err = launch_bwd_recurrent(p, &sl[d], 1, errw, d == 0 ? stamps : nullptr, len, s);
     }
   }
   for (int d = 0; d < nd && err == hipSuccess; ++d) {

@@ -44,7 +44,7 @@ namespace lstm {
 
 // ---------------------------------------------------------------------------
 template <typename T, int NBT, int NKBW, int C, int NW, int MW>
-__global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
+__global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(Launch<FwdArgs> L) {
   constexpr int NTH = 64 * NW;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   constexpr int E = sizeof(T);
@@ -53,7 +53,8 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
   // a divergent branch would run for every wave)
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, fq = lane >> 4;
-  const int wgi = direction_of(a);
+  FwdArgs a;
+  const int wgi = slot_select(L, a);
   int bg, jg;
   take_role(wgi, a.nBG, a.nJG, a.nxcd, a.local, a.misplace, bg, jg);
   claim_role(a.claims, bg * a.nJG + jg, a.err);
@@ -120,7 +121,8 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
 #pragma unroll
   for (int nt = 0; nt < NBT; ++nt) {
     const int b = b0 + 16 * nt + fr;
-    cst[nt] = (a.c0 && u < a.H && 16 * nt + fr < NBv) ? ldf<T>(a.c0, (int64_t)b * a.H + u) : 0.f;
+    const bool ok = u < a.H && 16 * nt + fr < NBv;
+    cst[nt] = !ok ? 0.f : a.c0f ? a.c0f[(int64_t)b * a.H + u] : a.c0 ? ldf<T>(a.c0, (int64_t)b * a.H + u) : 0.f;
   }
   // packed h ring: row b of slot s at byte ((s * Bp + b) * Hp) * E; the chunks
   // covering [0, H) of the group's valid rows are read each step
@@ -531,7 +533,7 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(FwdArgs a) {
 
 // ---------------------------------------------------------------------------
 template <typename T, int NBT, int C, int NW, int MW>
-static hipError_t fwd_dispatch_mw(const Plan& p, FwdArgs& a, hipStream_t s) {
+static hipError_t fwd_dispatch_mw(const Plan& p, Launch<FwdArgs>& a, hipStream_t s) {
   const int nt = 64 * NW;
   switch (p.fwd_nkbw) {
     case 1: return coop_launch(fwd_rec_kernel<T, NBT, 1, C, NW, MW>, launch_grid(p, a), p.lds_fwd, &a, s, nt);
@@ -547,7 +549,7 @@ static hipError_t fwd_dispatch_mw(const Plan& p, FwdArgs& a, hipStream_t s) {
 }
 
 template <typename T, int NBT, int C, int NW>
-static hipError_t fwd_dispatch_c(const Plan& p, FwdArgs& a, hipStream_t s) {
+static hipError_t fwd_dispatch_c(const Plan& p, Launch<FwdArgs>& a, hipStream_t s) {
   if (p.fwd_mw == 2) return fwd_dispatch_mw<T, NBT, C, NW, 2>(p, a, s);
   if (p.fwd_mw == 1) return fwd_dispatch_mw<T, NBT, C, NW, 1>(p, a, s);
   return hipErrorInvalidValue;
@@ -558,7 +560,7 @@ static hipError_t fwd_dispatch_c(const Plan& p, FwdArgs& a, hipStream_t s) {
 // registers, 4 chunks in flight per thread and round.  8-wave work-groups
 // have 16-bit storage only.
 template <typename T, int NBT>
-static hipError_t fwd_dispatch(const Plan& p, FwdArgs& a, hipStream_t s) {
+static hipError_t fwd_dispatch(const Plan& p, Launch<FwdArgs>& a, hipStream_t s) {
   const bool dma = p.fwd_dma != 0;
   if constexpr (sizeof(T) == 2)
     if (p.waves == 8) return dma ? fwd_dispatch_c<T, NBT, 0, 8>(p, a, s) : fwd_dispatch_c<T, NBT, 4, 8>(p, a, s);
@@ -566,15 +568,21 @@ static hipError_t fwd_dispatch(const Plan& p, FwdArgs& a, hipStream_t s) {
   return dma ? fwd_dispatch_c<T, NBT, 0, kWaves>(p, a, s) : fwd_dispatch_c<T, NBT, 4, kWaves>(p, a, s);
 }
 
-hipError_t launch_fwd_recurrent(const Plan& p, const float* P, const void* W, const void* h0, const void* c0,
-                                void* y, void* hT, void* cT, void* Gs, float* Cs, uint64_t* HX, uint32_t* err,
-                                uint64_t* stamps, const int32_t* len, const Bidir* bd, hipStream_t s) {
-  char* hd = (char*)HX;  // the packed ring and its flags share the tagged-word region
-  FwdArgs a{P, W, h0, c0, y, hT, cT, Gs, Cs, HX, hd, (uint32_t*)(hd + p.off_hflags), (uint32_t)p.off_hflags, err,
-            stamps, (int)p.T, (int)p.B, (int)p.H, (int)p.Z, p.NB, p.NJ,
-            p.nJG, p.Hp, p.Bp, p.esize == 2 ? (p.Hp / 2) : p.Hp, p.nBG, p.nxcd, p.xcd_local, p.rev, p.ijfo,
-            (uint32_t*)(hd + p.off_hclaim), p.fail_step, p.misplace,
-            len, bd ? p.grid : 0, bd ? bd->ws : 0, bd ? bd->w : 0, bd ? bd->st : 0};
+hipError_t launch_fwd_recurrent(const Plan& p, const FwdSlot* slots, int nslots, uint32_t* err, uint64_t* stamps,
+                                const int32_t* len, hipStream_t s) {
+  if (nslots < 1 || nslots > kMaxSlots) return hipErrorInvalidValue;
+  Launch<FwdArgs> a{};
+  for (int k = 0; k < kMaxSlots; ++k) {
+    const FwdSlot& q = slots[k < nslots ? k : 0];
+    char* hd = (char*)q.HX;  // the packed ring and its flags share the tagged-word region
+    a.s[k] = FwdArgs{q.P, q.W, q.h0, q.c0, q.y, q.hT, q.cT, q.Gs, q.Cs, q.HX, hd,
+                     (uint32_t*)(hd + p.off_hflags), (uint32_t)p.off_hflags, err, k == 0 ? stamps : nullptr, q.T,
+                     (int)p.B, (int)p.H, (int)q.Z, p.NB, p.NJ, p.nJG, p.Hp, p.Bp,
+                     p.esize == 2 ? (p.Hp / 2) : p.Hp, p.nBG, p.nxcd, p.xcd_local, q.rev, p.ijfo,
+                     (uint32_t*)(hd + p.off_hclaim), p.fail_step, p.misplace, len, q.c0f};
+  }
+  a.nslots = nslots;
+  a.grid1 = p.grid;
   if (fwd_vec_ok(p)) return launch_fwd_vec(p, a, s);
   const int nbt = p.NB < 16 ? 1 : p.NB / 16;
   if (p.dtype == 1) {
@@ -593,16 +601,21 @@ hipError_t launch_fwd_recurrent(const Plan& p, const float* P, const void* W, co
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_recurrent(const Plan& p, const void* W, const void* c0, const void* dy, const void* dhT,
-                                const void* dcT, const void* Gs, const float* Cs, void* dG, uint64_t* PX, float* DBP,
-                                void* dh0, void* dc0, uint32_t* err, uint64_t* stamps, const int32_t* len,
-                                const Bidir* bd, hipStream_t s) {
-  char* gd = (char*)PX;  // the gate-delta ring and its flags share the tagged-word region
-  BwdArgs a{W, c0, dy, dhT, dcT, Gs, Cs, dG, PX, gd, (uint32_t*)(gd + p.off_pflags), (uint32_t)p.off_pflags,
-            DBP, dh0, dc0, err, stamps, (int)p.T, (int)p.B, (int)p.H, (int)p.Z,
-            p.NB, p.NJ, p.nJG, p.Hp, p.Bp, p.nBG, p.nxcd, p.xcd_local, p.rev, p.ijfo,
-            (uint32_t*)(gd + p.off_pclaim), p.fail_step, p.misplace,
-            len, bd ? p.grid : 0, bd ? bd->ws : 0, bd ? bd->w : 0, bd ? bd->st : 0};
+hipError_t launch_bwd_recurrent(const Plan& p, const BwdSlot* slots, int nslots, uint32_t* err, uint64_t* stamps,
+                                const int32_t* len, hipStream_t s) {
+  if (nslots < 1 || nslots > kMaxSlots) return hipErrorInvalidValue;
+  Launch<BwdArgs> a{};
+  for (int k = 0; k < kMaxSlots; ++k) {
+    const BwdSlot& q = slots[k < nslots ? k : 0];
+    char* gd = (char*)q.PX;  // the gate-delta ring and its flags share the tagged-word region
+    a.s[k] = BwdArgs{q.W, q.c0, q.dy, q.dhT, q.dcT, q.Gs, q.Cs, q.dG, q.PX, gd,
+                     (uint32_t*)(gd + p.off_pflags), (uint32_t)p.off_pflags, q.DBP, q.dh0, q.dc0, err,
+                     k == 0 ? stamps : nullptr, q.T, (int)p.B, (int)p.H, (int)q.Z, p.NB, p.NJ, p.nJG, p.Hp, p.Bp,
+                     p.nBG, p.nxcd, p.xcd_local, q.rev, p.ijfo, (uint32_t*)(gd + p.off_pclaim), p.fail_step,
+                     p.misplace, len, q.cprevf, q.carry, q.carry_in, q.carry_out};
+  }
+  a.nslots = nslots;
+  a.grid1 = p.grid;
   if (p.bwd_valu) return launch_bwd_vec(p, a, s);
   return launch_bwd_col(p, a, s);
 }

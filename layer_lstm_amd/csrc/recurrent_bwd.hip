@@ -45,7 +45,7 @@ namespace lstm {
 // per thread at most.  DEF selects where the step's other memory traffic
 // goes (see below).
 template <typename T, int NBT, int MT, int NKB, int NW, bool DEF>
-__global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(Launch<BwdArgs> L) {
   constexpr int NTH = 64 * NW;
   constexpr int E = sizeof(T);
   constexpr int KB = Mfma<T>::kBlock;
@@ -63,7 +63,8 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
   // would run for every wave)
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int fr = lane & 15, fq = lane >> 4;
-  const int wgi = direction_of(a);
+  BwdArgs a;
+  const int wgi = slot_select(L, a);
   int bg, jg;
   take_role(wgi, a.nBG, a.nJG, a.nxcd, a.local, a.misplace, bg, jg);
   claim_role(a.claims, bg * a.nJG + jg, a.err);
@@ -147,8 +148,9 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
     own[s] = e < nel && elem_b(s) < a.B && elem_u(s) < a.H;
     pass[s] = 0.f;
     lens[s] = own[s] ? len_of(a.len, elem_b(s), a.T) : a.T;
-    dcc[s] = (own[s] && a.dcT) ? ldf<T>(a.dcT, c_off(s)) : 0.f;
-    dhc[s] = (own[s] && a.dhT) ? ldf<T>(a.dhT, c_off(s)) : 0.f;
+    const int64_t BH = (int64_t)a.B * a.H;
+    dcc[s] = !own[s] ? 0.f : a.carry_in ? a.carry[BH + c_off(s)] : a.dcT ? ldf<T>(a.dcT, c_off(s)) : 0.f;
+    dhc[s] = !own[s] ? 0.f : a.carry_in ? a.carry[c_off(s)] : a.dhT ? ldf<T>(a.dhT, c_off(s)) : 0.f;
     if (e < nel) *(f32x4_t*)(dba + 4 * e) = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
@@ -315,7 +317,8 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
         gi = f_of_bits16<T>(gw[0]); gf = f_of_bits16<T>(gw[0] >> 16);
         gg = f_of_bits16<T>(gw[1]); go = f_of_bits16<T>(gw[1] >> 16);
       }
-      if (t == 0) cprev = (own[s] && a.c0) ? ldf<T>(a.c0, c_off(s)) : 0.f;
+      if (t == 0)
+        cprev = !own[s] ? 0.f : a.cprevf ? a.cprevf[c_off(s)] : a.c0 ? ldf<T>(a.c0, c_off(s)) : 0.f;
       const float tc = tanh_f(c);
       const float dh = Elem<T>::to_f(pdy[s]) + dhc[s];
       // past the sequence's end the step held the state: no gate deltas,
@@ -398,10 +401,13 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
     }
   }
 
-  // dh0 / dc0
+  // dh0 / dc0, or the fp32 carries of a stack's chunk
 #pragma unroll
   for (int s = 0; s < EPTM; ++s) {
-    if (own[s]) {
+    if (own[s] && a.carry_out) {
+      a.carry[c_off(s)] = dhc[s];
+      a.carry[(int64_t)a.B * a.H + c_off(s)] = dcc[s];
+    } else if (own[s]) {
       ((T*)a.dh0)[c_off(s)] = Elem<T>::from_f(dhc[s]);
       ((T*)a.dc0)[c_off(s)] = Elem<T>::from_f(dcc[s]);
     }
@@ -410,7 +416,7 @@ __global__ void __launch_bounds__(64 * NW, 1) bwd_col_kernel(BwdArgs a) {
 
 // ---------------------------------------------------------------------------
 template <typename T, int NBT, int MT, int NW, bool DEF>
-static hipError_t bwd_col_nkb(const Plan& p, BwdArgs& a, hipStream_t s) {
+static hipError_t bwd_col_nkb(const Plan& p, Launch<BwdArgs>& a, hipStream_t s) {
   const int nt = 64 * NW;
   switch (p.bwd_nkb) {
     case 1: return coop_launch(bwd_col_kernel<T, NBT, MT, 1, NW, DEF>, launch_grid(p, a), p.lds_bwd, &a, s, nt);
@@ -426,7 +432,7 @@ static hipError_t bwd_col_nkb(const Plan& p, BwdArgs& a, hipStream_t s) {
 }
 
 template <typename T, int NW, bool DEF>
-static hipError_t bwd_col_nw(const Plan& p, BwdArgs& a, hipStream_t s) {
+static hipError_t bwd_col_nw(const Plan& p, Launch<BwdArgs>& a, hipStream_t s) {
   const int nbt = p.NB < 16 ? 1 : p.NB / 16;
   if (p.bwd_mt == 1) {
     if (nbt == 1) return bwd_col_nkb<T, 1, 1, NW, DEF>(p, a, s);
@@ -441,11 +447,11 @@ static hipError_t bwd_col_nw(const Plan& p, BwdArgs& a, hipStream_t s) {
 }
 
 template <typename T, int NW>
-static hipError_t bwd_col_def(const Plan& p, BwdArgs& a, hipStream_t s) {
+static hipError_t bwd_col_def(const Plan& p, Launch<BwdArgs>& a, hipStream_t s) {
   return p.xcd_local ? bwd_col_nw<T, NW, true>(p, a, s) : bwd_col_nw<T, NW, false>(p, a, s);
 }
 
-hipError_t launch_bwd_col(const Plan& p, BwdArgs& a, hipStream_t s) {
+hipError_t launch_bwd_col(const Plan& p, Launch<BwdArgs>& a, hipStream_t s) {
   if (p.NB * p.NJ > 1024) return hipErrorInvalidValue;
   if (p.dtype == 1) return p.waves == 8 ? bwd_col_def<bf16_t, 8>(p, a, s) : bwd_col_def<bf16_t, kWaves>(p, a, s);
   if (p.dtype == 2) return p.waves == 8 ? bwd_col_def<f16_t, 8>(p, a, s) : bwd_col_def<f16_t, kWaves>(p, a, s);

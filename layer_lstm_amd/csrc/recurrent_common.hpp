@@ -31,12 +31,8 @@ struct FwdArgs {
   uint32_t* claims;    // [grid] role claims (cleared before the launch) or null
   int fail_step, misplace;  // test hooks (Plan)
   const int32_t* len;  // [B] sequence lengths (the seq_length mask in its per-row form) or null
-  // bidirectional launches (grid1 > 0): work-groups [grid1, 2*grid1) run
-  // the reverse direction on the second direction's tensors, at these byte
-  // offsets from the first's: inside the workspace (P, y, record, exchange),
-  // in W, and in the [2][B][H] states
-  int grid1;
-  int64_t bo_ws, bo_w, bo_st;
+  const float* c0f;    // [B][H] fp32 initial cell state in place of c0 (a stack's chunk continuing the
+                       // previous one from its fp32 record), or null
 };
 
 struct BwdArgs {
@@ -64,69 +60,43 @@ struct BwdArgs {
   uint32_t* claims;    // [grid] role claims or null (see FwdArgs)
   int fail_step, misplace;
   const int32_t* len;  // [B] sequence lengths or null (see FwdArgs)
-  int grid1;           // bidirectional launches, as in FwdArgs
-  int64_t bo_ws, bo_w, bo_st;
+  // a stack's chunk of steps: c_{t-1} of its first step from the fp32 record
+  // (cprevf, in place of c0), and the carries in fp32 (carry: [2][B][H], dh
+  // then dc) read at the start in place of dhT/dcT (carry_in) and written
+  // at the end in place of dh0/dc0 (carry_out); each element's carries are
+  // read and written by the one thread that owns it
+  const float* cprevf;
+  float* carry;
+  int carry_in, carry_out;
 };
 
-template <typename P>
-__device__ __forceinline__ P* shift_ptr(P* p, int64_t bytes) {
-  return p ? (P*)((char*)const_cast<void*>((const void*)p) + bytes) : p;
-}
-
-// Work-group index within its direction of time.  In a bidirectional
-// launch the second half of the grid takes the reverse direction: its
-// arguments are moved to the second direction's tensors (and its phase
-// stamps are off).
-__device__ __forceinline__ int direction_of(FwdArgs& a) {
-  int i = blockIdx.x;
-  if (a.grid1 > 0 && i >= a.grid1) {
-    i -= a.grid1;
-    a.rev = 1;
-    a.stamps = nullptr;
-    a.P = shift_ptr(a.P, a.bo_ws);
-    a.y = shift_ptr(a.y, a.bo_ws);
-    a.Gs = shift_ptr(a.Gs, a.bo_ws);
-    a.Cs = shift_ptr(a.Cs, a.bo_ws);
-    a.HX = shift_ptr(a.HX, a.bo_ws);
-    a.HD = shift_ptr(a.HD, a.bo_ws);
-    a.HF = shift_ptr(a.HF, a.bo_ws);
-    a.claims = shift_ptr(a.claims, a.bo_ws);
-    a.W = shift_ptr(a.W, a.bo_w);
-    a.h0 = shift_ptr(a.h0, a.bo_st);
-    a.c0 = shift_ptr(a.c0, a.bo_st);
-    a.hT = shift_ptr(a.hT, a.bo_st);
-    a.cT = shift_ptr(a.cT, a.bo_st);
-  }
-  return i;
-}
-__device__ __forceinline__ int direction_of(BwdArgs& a) {
-  int i = blockIdx.x;
-  if (a.grid1 > 0 && i >= a.grid1) {
-    i -= a.grid1;
-    a.rev = 1;
-    a.stamps = nullptr;
-    a.dy = shift_ptr(a.dy, a.bo_ws);
-    a.Gs = shift_ptr(a.Gs, a.bo_ws);
-    a.Cs = shift_ptr(a.Cs, a.bo_ws);
-    a.dG = shift_ptr(a.dG, a.bo_ws);
-    a.PX = shift_ptr(a.PX, a.bo_ws);
-    a.GD = shift_ptr(a.GD, a.bo_ws);
-    a.GF = shift_ptr(a.GF, a.bo_ws);
-    a.claims = shift_ptr(a.claims, a.bo_ws);
-    a.DBP = shift_ptr(a.DBP, a.bo_ws);
-    a.W = shift_ptr(a.W, a.bo_w);
-    a.c0 = shift_ptr(a.c0, a.bo_st);
-    a.dhT = shift_ptr(a.dhT, a.bo_st);
-    a.dcT = shift_ptr(a.dcT, a.bo_st);
-    a.dh0 = shift_ptr(a.dh0, a.bo_st);
-    a.dc0 = shift_ptr(a.dc0, a.bo_st);
-  }
-  return i;
-}
-
-// Work-groups of a recurrent launch: both directions' in a bidirectional one.
+// Several recurrences in one persistent launch (the two directions of a
+// bidirectional layer, the layers of a stack's wave): slot k takes
+// work-groups [k*grid1, (k+1)*grid1) and its own arguments.
+constexpr int kMaxSlots = 4;
 template <class A>
-inline int launch_grid(const Plan& p, const A& a) { return a.grid1 > 0 ? 2 * p.grid : p.grid; }
+struct Launch {
+  A s[kMaxSlots];
+  int nslots;
+  int grid1;  // work-groups per slot
+};
+
+// This work-group's slot arguments (a uniform choice among the kernel's
+// arguments) and its index within the slot.
+template <class A>
+__device__ __forceinline__ int slot_select(const Launch<A>& L, A& a) {
+  const int k = L.nslots > 1 ? (int)blockIdx.x / L.grid1 : 0;
+  a = L.s[0];
+#pragma unroll
+  for (int j = 1; j < kMaxSlots; ++j)
+    if (k == j) a = L.s[j];
+  if (k > 0) a.stamps = nullptr;  // phase stamps come from the first slot only
+  return (int)blockIdx.x - k * L.grid1;
+}
+
+// Work-groups of a recurrent launch: every slot's.
+template <class A>
+inline int launch_grid(const Plan& p, const Launch<A>& L) { return (L.nslots > 1 ? L.nslots : 1) * p.grid; }
 
 // Length of sequence b (T when there are no lengths): steps at times
 // t >= len_of(b) lie past its end.
@@ -156,8 +126,8 @@ __device__ __forceinline__ bool err_set(uint32_t* err) {
 // device deals the work-groups of a dispatch to its XCDs round robin from a
 // starting XCD that varies between dispatches, so work-group i runs on XCD
 // (s + i) % nxcd and i / nxcd numbers the work-groups of one XCD without
-// repeats; the XCD itself is read from the hardware.  (The second direction
-// of a bidirectional launch starts at grid index grid1, a multiple of nxcd in
+// repeats; the XCD itself is read from the hardware.  (Slot k of a launch
+// of several recurrences starts at grid index k*grid1, a multiple of nxcd in
 // this layout, so the same holds for its own indices.)  (Were the dealing
 // ever different, two work-groups could take one role -- they would compute
 // and write the same values -- and another role would stay empty, which
@@ -381,9 +351,9 @@ __device__ __forceinline__ float quad_dpp(float v) {
 }
 
 // VALU recurrences for fp32 batch groups of 4 rows (recurrent_vec.hip)
-hipError_t launch_fwd_vec(const Plan& p, FwdArgs& a, hipStream_t s);
-hipError_t launch_bwd_vec(const Plan& p, BwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_vec(const Plan& p, Launch<FwdArgs>& a, hipStream_t s);
+hipError_t launch_bwd_vec(const Plan& p, Launch<BwdArgs>& a, hipStream_t s);
 // MFMA backward, column partition (recurrent_bwd.hip)
-hipError_t launch_bwd_col(const Plan& p, BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_col(const Plan& p, Launch<BwdArgs>& a, hipStream_t s);
 
 }  // namespace lstm

@@ -54,7 +54,7 @@ __device__ __forceinline__ float rs16_f32(float lo, float hi) {
 }
 
 template <int L, int U2, int C>
-__global__ void __launch_bounds__(kRecThreads, 1) fwd_vec_kernel(FwdArgs a) {
+__global__ void __launch_bounds__(kRecThreads, 1) fwd_vec_kernel(Launch<FwdArgs> LA) {
   extern __shared__ __attribute__((aligned(16))) float hl[];
   constexpr int CS = L + 4;    // chunk stride (floats)
   constexpr int RS = 32 * CS;  // row stride
@@ -63,7 +63,8 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_vec_kernel(FwdArgs a) {
   // branches on it are scalar branches: an s_waitcnt under a divergent branch
   // would run for every wave)
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wgi = direction_of(a);
+  FwdArgs a;
+  const int wgi = slot_select(LA, a);
   int bg, jg;
   take_role(wgi, a.nBG, a.nJG, a.nxcd, a.local, a.misplace, bg, jg);
   claim_role(a.claims, bg * a.nJG + jg, a.err);
@@ -101,7 +102,10 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_vec_kernel(FwdArgs a) {
 #pragma unroll
   for (int q = 0; q < U2; ++q) {
     const int u = j0 + ulb + 8 * q;
-    cst[q] = (ew && a.c0 && u < a.H) ? ((const float*)a.c0)[(int64_t)bme * a.H + u] : 0.f;
+    cst[q] = !(ew && u < a.H) ? 0.f
+             : a.c0f           ? a.c0f[(int64_t)bme * a.H + u]
+             : a.c0            ? ((const float*)a.c0)[(int64_t)bme * a.H + u]
+                               : 0.f;
     hst[q] = (ew && a.h0 && u < a.H) ? ((const float*)a.h0)[(int64_t)bme * a.H + u] : 0.f;
   }
   const int lenb = ew ? len_of(a.len, bme, a.T) : a.T;  // length of this lane's batch row
@@ -276,10 +280,11 @@ __global__ void __launch_bounds__(kRecThreads, 1) fwd_vec_kernel(FwdArgs a) {
 // reduce-scatter across the quad (DPP) leaves lane p with the four
 // batch-row sums of column 256*i + 4*qd + p, stored as 32 contiguous bytes.
 template <int VNCT, int VR, int C>
-__global__ void __launch_bounds__(kRecThreads, 1) bwd_vec_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(kRecThreads, 1) bwd_vec_kernel(Launch<BwdArgs> L) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int tid = threadIdx.x;
-  const int wgi = direction_of(a);
+  BwdArgs a;
+  const int wgi = slot_select(L, a);
   int bg, jg;
   take_role(wgi, a.nBG, a.nJG, a.nxcd, a.local, a.misplace, bg, jg);
   claim_role(a.claims, bg * a.nJG + jg, a.err);
@@ -323,8 +328,11 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_vec_kernel(BwdArgs a) {
   const int bl0 = e & (a.NB - 1), jj0 = e >> lgNB;
   const int bown = b0 + bl0, uown = j0 + jj0;
   const bool own = e < nel && bown < a.B && uown < a.H;
-  float dcc = (own && a.dcT) ? ((const float*)a.dcT)[(int64_t)bown * a.H + uown] : 0.f;
-  float dhc = (own && a.dhT) ? ((const float*)a.dhT)[(int64_t)bown * a.H + uown] : 0.f;
+  const int64_t BH = (int64_t)a.B * a.H;
+  float dcc = !own ? 0.f : a.carry_in ? a.carry[BH + (int64_t)bown * a.H + uown]
+                   : a.dcT ? ((const float*)a.dcT)[(int64_t)bown * a.H + uown] : 0.f;
+  float dhc = !own ? 0.f : a.carry_in ? a.carry[(int64_t)bown * a.H + uown]
+                   : a.dhT ? ((const float*)a.dhT)[(int64_t)bown * a.H + uown] : 0.f;
   // dh of a step past the sequence's end reaches the held state unchanged
   float pass = 0.f;
   const int lenb = own ? len_of(a.len, bown, a.T) : a.T;
@@ -344,7 +352,7 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_vec_kernel(BwdArgs a) {
       pg[0] = gv[0]; pg[1] = gv[1]; pg[2] = gv[2]; pg[3] = gv[3];
       pc = a.Cs[oC + c_off];
       pcp = tt > 0 ? a.Cs[(int64_t)mem_t(tt - 1, a.T, a.rev) * stepC + c_off]
-                   : (a.c0 ? ((const float*)a.c0)[c_off] : 0.f);
+                   : a.cprevf ? a.cprevf[c_off] : (a.c0 ? ((const float*)a.c0)[c_off] : 0.f);
       pdy = ((const float*)a.dy)[oC + c_off];
     }
   };
@@ -493,7 +501,10 @@ __global__ void __launch_bounds__(kRecThreads, 1) bwd_vec_kernel(BwdArgs a) {
       if (j0 + jj < a.H) a.DBP[(int64_t)bg * G4 + 4 * (j0 + jj) + g] = v;
     }
   }
-  if (own) {
+  if (own && a.carry_out) {
+    a.carry[c_off] = dhc;
+    a.carry[BH + c_off] = dcc;
+  } else if (own) {
     ((float*)a.dh0)[c_off] = dhc;
     ((float*)a.dc0)[c_off] = dcc;
   }
@@ -511,7 +522,7 @@ bool fwd_vec_ok(const Plan& p) {
 }
 
 template <int U2, int C>
-static hipError_t fwd_vec_l(const Plan& p, FwdArgs& a, hipStream_t s) {
+static hipError_t fwd_vec_l(const Plan& p, Launch<FwdArgs>& a, hipStream_t s) {
   const int L = vec_chunk(p);
   const size_t lds = (size_t)4 * 32 * (L + 4) * sizeof(float);
   switch (L) {
@@ -524,7 +535,7 @@ static hipError_t fwd_vec_l(const Plan& p, FwdArgs& a, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_fwd_vec(const Plan& p, FwdArgs& a, hipStream_t s) {
+hipError_t launch_fwd_vec(const Plan& p, Launch<FwdArgs>& a, hipStream_t s) {
   // exchange words a thread reads per step: 4*Hp/256 (at most 16)
   const bool wide = p.words_per_thread > 4;
   if (p.NJ == 8) return wide ? fwd_vec_l<1, 16>(p, a, s) : fwd_vec_l<1, 4>(p, a, s);
@@ -534,7 +545,7 @@ hipError_t launch_fwd_vec(const Plan& p, FwdArgs& a, hipStream_t s) {
 // Backward: VNCT = Hp/256 column groups per thread (at least 1), VR = 4*NJ
 // rows; the make_plan conditions (NJ = 8 with VNCT <= 4, or NJ = 16 with
 // VNCT = 1) keep the resident VNCT*4*VR/4 floats per lane at most 128.
-hipError_t launch_bwd_vec(const Plan& p, BwdArgs& a, hipStream_t s) {
+hipError_t launch_bwd_vec(const Plan& p, Launch<BwdArgs>& a, hipStream_t s) {
   const int vnct = p.Hp <= kRecThreads ? 1 : p.Hp / kRecThreads;
   const bool wide = p.words_per_thread > 4;
   if (p.NJ == 8) {
