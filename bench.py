@@ -47,23 +47,32 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_work(w, kind, plan=None):
-    """Algorithmic work of one launch: (amount, unit, bound).  A recurrence
-    whose product runs on the vector ALUs (plan from lstm_query_plan) is
-    bound by "alu" arithmetic, else by the matrix cores."""
+def step_work(w, kind, layers=1, directions=1):
+    """Algorithmic FLOPs of one step's launches of `kind` (all of them:
+    every layer of a stack, both directions of a bidirectional layer)."""
     T, B, I, H = w.T, w.B, w.I, w.H
     TB = T * B
-    if kind == "input_projection":
-        return 2.0 * TB * 4 * H * I, "flop", "mfma"
+    ins = I + (layers - 1) * H  # the layers' input sizes, summed
+    if kind in ("input_projection", "dx_product"):
+        return directions * 2.0 * TB * 4 * H * ins
+    if kind in ("forward_recurrence", "backward_recurrence"):
+        return directions * layers * 2.0 * TB * 4 * H * H
+    if kind == "dW_product":
+        return directions * 2.0 * TB * 4 * H * (layers * H + ins)
+    return 0.0
+
+
+def kernel_work(w, kind, plan=None, launches_per_step=1.0, layers=1, directions=1):
+    """Algorithmic work of one launch of `kind`: (amount, unit, bound) --
+    the step's work over its launches.  A recurrence whose product runs on
+    the vector ALUs (plan from lstm_query_plan) is bound by "alu"
+    arithmetic, else by the matrix cores."""
+    work = step_work(w, kind, layers, directions) / max(launches_per_step, 1e-9)
     if kind in ("forward_recurrence", "backward_recurrence"):
         key = "fwd_valu" if kind == "forward_recurrence" else "bwd_valu"
-        # a bidirectional layer's concurrent launch runs both directions
-        nd = 2 if plan and plan.get("directions_concurrent") else 1
-        return nd * 2.0 * TB * 4 * H * H, "flop", "alu" if plan and plan[key] else "mfma"
-    if kind == "dW_product":
-        return 2.0 * TB * 4 * H * (H + I), "flop", "mfma"
-    if kind == "dx_product":
-        return 2.0 * TB * 4 * H * I, "flop", "mfma"
+        return work, "flop", "alu" if plan and plan[key] else "mfma"
+    if kind in ("input_projection", "dW_product", "dx_product"):
+        return work, "flop", "mfma"
     return 0.0, "byte", "hbm"
 
 
@@ -154,6 +163,11 @@ def main():
     ap.add_argument("--two-bias", action="store_true", help="two bias vectors (b_ih, b_hh)")
     ap.add_argument("--bidirectional", action="store_true",
                     help="both directions of time (the second direction's tensors seeded with seed 1)")
+    ap.add_argument("--layers", type=int, default=1,
+                    help="a stack of this many layers (lstm_stack_*: the wavefront schedule), layers >= 1 of input "
+                         "size H seeded with seeds 1, 2, ...")
+    ap.add_argument("--chunks", type=int, default=0, help="chunks of time of the stack's wavefront (0: default; "
+                                                          "1: the layers one after the other)")
     ap.add_argument("--lengths", default="none", choices=("none", "ragged"),
                     help="sequence lengths: none, or ragged (seeded, uniform over 1..T)")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB",
@@ -194,12 +208,34 @@ def main():
 
     d = {k: put(inp[k]) for k in ("x", "W", "b", "h0", "c0", "dy", "dhT", "dcT")}
     lens = None if inp.get("lengths") is None else torch.from_numpy(inp["lengths"]).to(dev)
-    m = lstm.Lstm(w.T, w.B, w.I, w.H, code, reverse=args.reverse, gate_order=args.gate_order, two_bias=args.two_bias,
-                  bidirectional=args.bidirectional)
+    if args.layers > 1:
+        # a stack: layer 0 on the workload's inputs, layers l >= 1 (input size
+        # H) on inputs seeded with seed l; W back to back, b and the states
+        # with a leading layer axis
+        Ws, bs, st = [inp["W"]], [inp["b"]], {k: [inp[k]] for k in ("h0", "c0", "dhT", "dcT")}
+        for ll in range(1, args.layers):
+            o = synth.make_inputs(w.T, w.B, w.H, w.H, w.dtype, seed=ll, dist=w.dist)
+            Ws.append(o["W"])
+            bs.append(o["b"])
+            for k in st:
+                st[k].append(o[k])
+        d["W"] = put(np.concatenate([a.reshape(-1) for a in Ws]))
+        d["b"] = put(np.stack(bs))
+        for k in st:
+            d[k] = None if st[k][0] is None else put(np.stack(st[k]))
+        m = lstm.Stack(w.T, w.B, w.I, w.H, args.layers, code, chunks=args.chunks, gate_order=args.gate_order,
+                       two_bias=args.two_bias)
 
-    def step():
-        m.forward(d["x"], d["W"], d["b"], d["h0"], d["c0"], seq_length=lens)
-        m.backward(d["dy"], d["dhT"], d["dcT"], d["x"], d["W"], d["h0"], d["c0"], seq_length=lens)
+        def step():
+            m.forward(d["x"], d["W"], d["b"], d["h0"], d["c0"])
+            m.backward(d["dy"], d["dhT"], d["dcT"], d["x"], d["W"], d["h0"], d["c0"])
+    else:
+        m = lstm.Lstm(w.T, w.B, w.I, w.H, code, reverse=args.reverse, gate_order=args.gate_order,
+                      two_bias=args.two_bias, bidirectional=args.bidirectional)
+
+        def step():
+            m.forward(d["x"], d["W"], d["b"], d["h0"], d["c0"], seq_length=lens)
+            m.backward(d["dy"], d["dhT"], d["dcT"], d["x"], d["W"], d["h0"], d["c0"], seq_length=lens)
 
     log(f"workload {w.name}{' (reverse)' if args.reverse else ''}: warmup {args.warmup}, steps {args.steps}")
     for _ in range(args.warmup):
@@ -242,7 +278,8 @@ def main():
     tot, n = kt[dom]
     avg_s = tot / n / 1e3
     plan = lstm.query_plan(lstm.make_shape(w.T, w.B, w.I, w.H, code, bidirectional=args.bidirectional))
-    work, unit, bound = kernel_work(w, dom, plan)
+    nd = 2 if args.bidirectional else 1
+    work, unit, bound = kernel_work(w, dom, plan, n / args.steps, args.layers, nd)
     if unit == "flop":
         achieved = work / avg_s / 1e12
         peak, runit = (VALU_TFLOPS if bound == "alu" else PEAK_TFLOPS[w.dtype]), "TFLOP/s"
@@ -253,7 +290,7 @@ def main():
                 "frac": round(achieved / peak, 5),
                 # (the counter runs are of the forward direction, default gate order, one bias)
                 "traffic": None if (args.reverse or args.gate_order != "ifjo" or args.two_bias or
-                                    args.bidirectional or args.lengths != "none")
+                                    args.bidirectional or args.lengths != "none" or args.layers > 1)
                 else traffic_for(w.name, dom),
                 "kernel": dom, "avg_launch_us": round(avg_s * 1e6, 2)}
 
@@ -264,13 +301,15 @@ def main():
     for kind in ("input_projection", "dW_product", "dx_product"):
         tot_k, n_k = kt.get(kind, (0.0, 0))
         if n_k:
-            fl = kernel_work(w, kind, plan)[0]
+            fl = kernel_work(w, kind, plan, n_k / args.steps, args.layers, nd)[0]
             gemm_frac[kind] = {"us": round(tot_k / n_k * 1e3, 2),
                                "frac": round(fl / (tot_k / n_k / 1e3) / 1e12 / PEAK_TFLOPS[w.dtype], 4)}
     rec_us = {k: round(kt[k][0] / kt[k][1] * 1e3, 2) for k in ("forward_recurrence", "backward_recurrence")
               if kt.get(k, (0, 0))[1]}
 
     flops = w.flops * (2 if args.bidirectional else 1)
+    if args.layers > 1:  # layers >= 1 take input size H
+        flops += (args.layers - 1) * 24.0 * w.T * w.B * w.H * 2 * w.H
     value = w.B / (ms / 1e3)
     eff_tflops = flops / (ms / 1e3) / 1e12
     out = {
@@ -282,6 +321,7 @@ def main():
                    "direction": "reverse" if args.reverse else "forward", "gate_order": args.gate_order,
                    "biases": 2 if args.two_bias else 1,
                    "bidirectional": args.bidirectional, "lengths": args.lengths,
+                   "layers": args.layers, "chunks": args.chunks,
                    "parallelism": "single GPU"},
         "effective_tflops": round(eff_tflops, 3),
         "fraction_of_peak": round(eff_tflops / PEAK_TFLOPS[w.dtype], 5),
@@ -291,7 +331,7 @@ def main():
         "recurrence_plan": plan,
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.layers == 1:
         log("timing the CPU oracle ...")
         out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget, args.reverse, args.gate_order, args.two_bias,
                                            args.bidirectional)

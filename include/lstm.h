@@ -277,6 +277,37 @@ int lstm_timing_read(int kind, double* total_ms, int64_t* launches);
  * LSTM_ERR_WORKSPACE if the buffer is too small for T. */
 int lstm_stamps_set(void* device_buffer, size_t bytes, int64_t T);
 
+/* Stacked layers (the "Stack Multiple RNN Cells" of the MXNet LSTM page;
+ * num_layers of the CMU 10-414 page's LSTM module): `layers` = L one-
+ * direction layers, layer l + 1 taking layer l's output sequence as its
+ * input; only the last layer's output is the stack's.  shape gives T, B, I
+ * (layer 0's input size; the others' is H), H, the dtype, and flags 0 or
+ * LSTM_GATES_IJFO / LSTM_TWO_BIAS (others: LSTM_ERR_DTYPE); 1 <= L <= 8.
+ *   W, dW   the layers' weights back to back: layer 0 [4H][H+I], then layers
+ *           1..L-1 [4H][2H] (columns [W_h | W_x] as above)
+ *   b, db   [L][4H] (or [L][2][4H] with two biases); b may be NULL
+ *   h0, c0, hT, cT, dhT, dcT, dh0, dc0   [L][B][H] (layer-major)
+ *   x, dx   [T][B][I]      y, dy   [T][B][H] (the last layer's output)
+ * Schedule (a wavefront): time is cut into `chunks` chunks (0: a default of
+ * up to 8); in wave w layer l runs chunk w - l, so layer l + 1's steps of
+ * chunk k run beside layer l's steps of chunk k + 1 -- in one persistent
+ * launch per wave, each layer on its share of the compute units, when the
+ * recurrences have a layout for cus / L and L <= 4 (*concurrent = 1), else
+ * one after the other.  The backward runs the waves from the last chunk of
+ * the last layer down.  Results equal the layers run one after the other
+ * (the state crosses chunk borders in fp32 as within a chunk).  Workspace,
+ * errors, streams and ownership as for the one-layer calls; the forward and
+ * the backward of one record take the same layers and chunks. */
+int lstm_stack_query(const lstm_shape* shape, int64_t layers, int64_t chunks, size_t* workspace_bytes,
+                     int32_t* concurrent);
+int lstm_stack_fwd_train(const lstm_shape* shape, int64_t layers, int64_t chunks, const void* x, const void* W,
+                         const void* b, const void* h0, const void* c0, void* y, void* hT, void* cT,
+                         void* workspace, size_t workspace_bytes, void* stream);
+int lstm_stack_bwd(const lstm_shape* shape, int64_t layers, int64_t chunks, const void* dy, const void* dhT,
+                   const void* dcT, const void* x, const void* W, const void* h0, const void* c0, const void* y,
+                   void* workspace, size_t workspace_bytes, void* dx, void* dW, void* db, void* dh0, void* dc0,
+                   void* stream);
+
 /* The floor under a recurrence step, for measurement: runs the forward
  * recurrence's per-step exchange alone -- the step flags of the batch group,
  * the copy of the group's h rows from the exchange ring into LDS, this

@@ -17,7 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblstm.so")
-SOURCES = ["lstm_api.hip", "gemm.hip", "recurrent.hip", "recurrent_vec.hip", "recurrent_bwd.hip", "exchange_probe.hip"]
+SOURCES = ["lstm_api.hip", "gemm.hip", "recurrent.hip", "recurrent_vec.hip", "recurrent_bwd.hip", "exchange_probe.hip",
+           "stack_api.hip"]
 ARCH = "gfx950"
 
 

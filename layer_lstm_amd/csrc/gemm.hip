@@ -1168,7 +1168,7 @@ static hipError_t dw_t(const Plan& p, const void* dG, const void* x, const void*
                 aligned16(x) && aligned16(y) && (h0 == nullptr || aligned16(h0)) && p.H % VEC == 0 && p.I % VEC == 0,
                 p.rev != 0};
   EpiDW<T> e{(T*)dW, p.H, p.Z, p.ijfo};
-  const DbDuty dd{DBP, db, p.nBG, p.G4, p.H, p.dtype, p.ijfo, p.two_bias};
+  const DbDuty dd{DBP, db, p.dbp_rows > 0 ? p.dbp_rows : p.nBG, p.G4, p.H, p.dtype, p.ijfo, p.two_bias};
   if (p.TB % LdsCfg<T>::kKStage == 0 && lds_depth_ok<T>(p.TB) && p.Z >= VEC && a.vec_ok && bz.vec_ok &&
       small_buf(p.TB * p.G4, p.esize) && small_buf(p.TB * p.Z, p.esize))
     return run_gemm_lds<T, 1, 1>(p, p.G4, p.Z, p.TB, a, bz, e, part, zero, zero_bytes, s, dd);

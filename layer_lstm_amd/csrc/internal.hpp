@@ -73,9 +73,25 @@ struct Plan {
   // other
   int bidir, concurrent;
   size_t dir_bytes, off_ydir, off_dydir, off_dxacc;
+  // rows of db partials the dW launch sums ([rows][4H]; 0: nBG, one set of
+  // steps)
+  int dbp_rows;
   int cus;          // compute units of the device
   int max_splits;   // largest split-K factor of the three products
   size_t off_gp;    // fp32 split-K partials of the products
+};
+
+// Brackets the launches made during its lifetime with two events on the
+// stream when per-kernel timing is on (lstm_timing_enable), adding their
+// elapsed time to the total of `kind`.
+struct Timed {
+  int kind;
+  hipStream_t s;
+  hipEvent_t a = nullptr;
+  Timed(int k, hipStream_t st);
+  ~Timed();
+  Timed(const Timed&) = delete;
+  Timed& operator=(const Timed&) = delete;
 };
 
 // LDS through which the MFMA recurrences gather their W_h slices at start.

@@ -259,28 +259,22 @@ static hipEvent_t take_event() {
   return e;
 }
 
-// Brackets the launches made during its lifetime with two events.
-struct Timed {
-  int kind;
-  hipStream_t s;
-  hipEvent_t a = nullptr;
-  Timed(int k, hipStream_t st) : kind(k), s(st) {
-    if (g_timing_on && (a = take_event()) != nullptr && hipEventRecord(a, s) != hipSuccess) {
-      g_pool.push_back(a);
-      a = nullptr;
-    }
+Timed::Timed(int k, hipStream_t st) : kind(k), s(st) {
+  if (g_timing_on && (a = take_event()) != nullptr && hipEventRecord(a, s) != hipSuccess) {
+    g_pool.push_back(a);
+    a = nullptr;
   }
-  ~Timed() {
-    if (!a) return;
-    hipEvent_t b = take_event();
-    if (b && hipEventRecord(b, s) == hipSuccess) {
-      g_pending.push_back({kind, a, b});
-    } else {
-      g_pool.push_back(a);
-      if (b) g_pool.push_back(b);
-    }
+}
+Timed::~Timed() {
+  if (!a) return;
+  hipEvent_t b = take_event();
+  if (b && hipEventRecord(b, s) == hipSuccess) {
+    g_pending.push_back({kind, a, b});
+  } else {
+    g_pool.push_back(a);
+    if (b) g_pool.push_back(b);
   }
-};
+}
 
 // the stamp buffer holds [2 passes][kStampWGs][T][kPhases] clock values
 static bool stamps_fit(const Plan& p) {

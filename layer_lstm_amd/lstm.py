@@ -36,7 +36,8 @@ DEBUG_FAIL_STEP, DEBUG_MISPLACE, DEBUG_XCD_LOCAL = 1, 2, 3  # lstm_debug_inject
 SCRATCH_BYTES = 64 << 20  # LSTM_SCRATCH_BYTES
 EXPORTS = ("lstm_abi_version", "lstm_status_string", "lstm_query", "lstm_query_plan", "lstm_fwd_train",
            "lstm_fwd_train_scratch", "lstm_bwd", "lstm_check_workspace", "lstm_timing_enable", "lstm_timing_read",
-           "lstm_stamps_set", "lstm_probe_exchange", "lstm_debug_inject")
+           "lstm_stamps_set", "lstm_probe_exchange", "lstm_debug_inject", "lstm_stack_query",
+           "lstm_stack_fwd_train", "lstm_stack_bwd")
 STAMP_WGS, STAMP_POINTS = 8, 6
 KERNEL_KINDS = ("input_projection", "forward_recurrence", "backward_recurrence", "dW_product",
                 "dx_product", "direction_copy", "state_copy")
@@ -77,6 +78,15 @@ _lib.lstm_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
 _lib.lstm_probe_exchange.restype = ctypes.c_int
 _lib.lstm_probe_exchange.argtypes = [ctypes.POINTER(Shape), ctypes.c_int, _P, ctypes.c_size_t,
                                      ctypes.POINTER(ctypes.c_double), _P]
+_lib.lstm_stack_query.restype = ctypes.c_int
+_lib.lstm_stack_query.argtypes = [ctypes.POINTER(Shape), ctypes.c_int64, ctypes.c_int64,
+                                  ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_int32)]
+_lib.lstm_stack_fwd_train.restype = ctypes.c_int
+_lib.lstm_stack_fwd_train.argtypes = [ctypes.POINTER(Shape), ctypes.c_int64, ctypes.c_int64] + [_P] * 8 + \
+    [_P, ctypes.c_size_t, _P]
+_lib.lstm_stack_bwd.restype = ctypes.c_int
+_lib.lstm_stack_bwd.argtypes = [ctypes.POINTER(Shape), ctypes.c_int64, ctypes.c_int64] + [_P] * 8 + \
+    [_P, ctypes.c_size_t] + [_P] * 5 + [_P]
 _lib.lstm_debug_inject.restype = ctypes.c_int
 _lib.lstm_debug_inject.argtypes = [ctypes.c_int, ctypes.c_int64]
 _lib.lstm_stamps_set.restype = ctypes.c_int
@@ -265,6 +275,62 @@ class Lstm:
     def backward(self, dy, dhT, dcT, x, W, h0=None, c0=None, want_db=True, stream=None, seq_length=None):
         bwd(self.shape, dy, dhT, dcT, x, W, h0, c0, self.y, self.workspace, self.dx, self.dW,
             self.db if want_db else None, self.dh0, self.dc0, self.ws_bytes, stream, seq_length=seq_length)
+        return self.dx, self.dW, self.db, self.dh0, self.dc0
+
+    def check(self, stream=None):
+        rc = check_workspace(self.workspace, stream)
+        if rc != OK:
+            raise LstmError(rc, "lstm_check_workspace")
+
+
+def stack_query(shape: Shape, layers: int, chunks: int = 0):
+    """lstm_stack_query: (workspace bytes, 1 if a wave's recurrences share
+    one launch)."""
+    n, conc = ctypes.c_size_t(0), ctypes.c_int32(0)
+    rc = _lib.lstm_stack_query(ctypes.byref(shape), int(layers), int(chunks), ctypes.byref(n), ctypes.byref(conc))
+    if rc != OK:
+        raise LstmError(rc, "lstm_stack_query")
+    return n.value, conc.value
+
+
+class Stack:
+    """An L-layer stack (lstm_stack_*) of one problem shape with its
+    workspace and output buffers on the current device.  W is the layers'
+    weights back to back (layer 0 [4H][H+I], the others [4H][2H]); b, h0, c0,
+    dhT, dcT have a leading layer axis."""
+
+    def __init__(self, T, B, I, H, layers, dtype=F32, chunks=0, device="cuda", gate_order="ifjo", two_bias=False):
+        self.shape = make_shape(T, B, I, H, dtype, False, gate_order, two_bias)
+        self.T, self.B, self.I, self.H, self.L, self.chunks = T, B, I, H, layers, chunks
+        self.tdtype = torch_dtype(dtype)
+        self.ws_bytes, self.concurrent = stack_query(self.shape, layers, chunks)
+        self.workspace = torch.empty(self.ws_bytes, dtype=torch.uint8, device=device)
+        dev, td, L = device, self.tdtype, layers
+        self.w_elems = 4 * H * (H + I) + (L - 1) * 4 * H * 2 * H
+        self.y = torch.empty((T, B, H), dtype=td, device=dev)
+        self.hT = torch.empty((L, B, H), dtype=td, device=dev)
+        self.cT = torch.empty((L, B, H), dtype=td, device=dev)
+        self.dx = torch.empty((T, B, I), dtype=td, device=dev)
+        self.dW = torch.empty((self.w_elems,), dtype=td, device=dev)
+        self.db = torch.empty((L, 2, 4 * H) if two_bias else (L, 4 * H), dtype=td, device=dev)
+        self.dh0 = torch.empty((L, B, H), dtype=td, device=dev)
+        self.dc0 = torch.empty((L, B, H), dtype=td, device=dev)
+
+    def forward(self, x, W, b=None, h0=None, c0=None, stream=None):
+        rc = _lib.lstm_stack_fwd_train(ctypes.byref(self.shape), self.L, self.chunks, _ptr(x), _ptr(W), _ptr(b),
+                                       _ptr(h0), _ptr(c0), _ptr(self.y), _ptr(self.hT), _ptr(self.cT),
+                                       _ptr(self.workspace), self.ws_bytes, _stream(stream))
+        if rc != OK:
+            raise LstmError(rc, "lstm_stack_fwd_train")
+        return self.y, self.hT, self.cT
+
+    def backward(self, dy, dhT, dcT, x, W, h0=None, c0=None, want_db=True, stream=None):
+        rc = _lib.lstm_stack_bwd(ctypes.byref(self.shape), self.L, self.chunks, _ptr(dy), _ptr(dhT), _ptr(dcT),
+                                 _ptr(x), _ptr(W), _ptr(h0), _ptr(c0), _ptr(self.y), _ptr(self.workspace),
+                                 self.ws_bytes, _ptr(self.dx), _ptr(self.dW), _ptr(self.db if want_db else None),
+                                 _ptr(self.dh0), _ptr(self.dc0), _stream(stream))
+        if rc != OK:
+            raise LstmError(rc, "lstm_stack_bwd")
         return self.dx, self.dW, self.db, self.dh0, self.dc0
 
     def check(self, stream=None):

@@ -125,3 +125,16 @@ def test_debug_inject_host_checks(lstm):
     assert header_enum("LSTM_DEBUG_FAIL_STEP") == lstm.DEBUG_FAIL_STEP
     assert header_enum("LSTM_DEBUG_MISPLACE") == lstm.DEBUG_MISPLACE
     assert header_enum("LSTM_DEBUG_XCD_LOCAL") == lstm.DEBUG_XCD_LOCAL
+
+
+def test_stack_query_host_checks(lstm):
+    """lstm_stack_query refuses a bad layer count, an unknown or unsupported
+    flag, and NULLs before any device work."""
+    n, c = ctypes.c_size_t(5), ctypes.c_int32(0)
+    s = lstm.make_shape(4, 2, 3, 8, 0)
+    assert lstm.lib().lstm_stack_query(None, 2, 0, ctypes.byref(n), ctypes.byref(c)) == -1
+    assert lstm.lib().lstm_stack_query(ctypes.byref(s), 0, 0, ctypes.byref(n), ctypes.byref(c)) == -2
+    assert lstm.lib().lstm_stack_query(ctypes.byref(s), 9, 0, ctypes.byref(n), ctypes.byref(c)) == -2
+    r = lstm.make_shape(4, 2, 3, 8, 0, reverse=True)
+    assert lstm.lib().lstm_stack_query(ctypes.byref(r), 2, 0, ctypes.byref(n), ctypes.byref(c)) == -3
+    assert n.value == 5
