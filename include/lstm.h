@@ -288,13 +288,15 @@ int lstm_stamps_set(void* device_buffer, size_t bytes, int64_t T);
  *   b, db   [L][4H] (or [L][2][4H] with two biases); b may be NULL
  *   h0, c0, hT, cT, dhT, dcT, dh0, dc0   [L][B][H] (layer-major)
  *   x, dx   [T][B][I]      y, dy   [T][B][H] (the last layer's output)
- * Schedule (a wavefront): time is cut into `chunks` chunks (0: a default of
- * up to 8); in wave w layer l runs chunk w - l, so layer l + 1's steps of
+ * Schedule (a wavefront): time is cut into `chunks` chunks (0: chunks of at
+ * least 128 steps, at most 8 of them; chunks > T: T); in wave w layer l runs chunk w - l, so layer l + 1's steps of
  * chunk k run beside layer l's steps of chunk k + 1 -- in one persistent
- * launch per wave, each layer on its share of the compute units, when the
- * recurrences have a layout for cus / L and L <= 4 (*concurrent = 1), else
- * one after the other.  The backward runs the waves from the last chunk of
- * the last layer down.  Results equal the layers run one after the other
+ * launch per wave, each of its n layers on cus / n compute units, when the
+ * recurrences have such a layout (n <= 4; *concurrent = the most layers one
+ * launch runs, 1: one after the other).  A wave of one layer gives it the
+ * whole device; chunks = 1 runs the layers one after the other.  Layer 0's
+ * input projection and input gradient run once over all T.  The backward
+ * runs the waves from the last chunk of the last layer down.  Results equal the layers run one after the other
  * (the state crosses chunk borders in fp32 as within a chunk).  Workspace,
  * errors, streams and ownership as for the one-layer calls; the forward and
  * the backward of one record take the same layers and chunks. */

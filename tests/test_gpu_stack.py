@@ -111,9 +111,10 @@ def check(inp, out, tol=None):
 @pytest.mark.parametrize("dt,L,T,B,I,H,chunks", [
     ("f32", 2, 8, 4, 16, 32, 1),      # one chunk: the layers one after the other
     ("f32", 2, 8, 4, 16, 32, 3),      # chunks of 3, 3, 2 steps
-    ("f32", 3, 20, 32, 64, 256, 0),   # the VALU recurrences, default chunks
+    ("f32", 2, 300, 4, 16, 32, 0),    # default chunks: two of 150 steps
+    ("f32", 3, 20, 32, 64, 256, 5),   # the VALU recurrences; waves of 1, 2, 3 layers
     ("bf16", 2, 12, 60, 32, 512, 4),  # MFMA recurrences, XCD-local
-    ("bf16", 4, 9, 19, 40, 72, 0),    # four layers in one launch
+    ("bf16", 4, 9, 19, 40, 72, 5),    # four layers in one launch
     ("f16", 2, 10, 40, 64, 1024, 5),
     ("bf16", 3, 7, 5, 0, 48, 7),      # no input features, one step per chunk
 ])
@@ -154,11 +155,11 @@ def test_wavefront_equals_layer_by_layer(lstm):
 
 
 def test_stacked_workload_size(lstm):
-    """Two layers at T=128 B=64 I=512 H=1024 (bf16), the default chunks,
-    against the oracle on the whole batch."""
+    """Two layers at T=128 B=64 I=512 H=1024 (bf16) in four chunks, against
+    the oracle on the whole batch."""
     w = synth.WORKLOADS["bf16_T128_B64_I512_H1024"]
     inp = stacked_inputs(2, w.T, w.B, w.I, w.H, "bf16", seed=0, dist=w.dist)
-    nb, conc = lstm.stack_query(lstm.make_shape(w.T, w.B, w.I, w.H, lstm.BF16), 2, 0)
+    nb, conc = lstm.stack_query(lstm.make_shape(w.T, w.B, w.I, w.H, lstm.BF16), 2, 4)
     print(f"case: stack of 2 at {w.name}, concurrent={conc}", flush=True)
-    out, _ = run_stack(lstm, inp, 0)
+    out, _ = run_stack(lstm, inp, 4)
     check(inp, out)
