@@ -569,7 +569,9 @@ struct Dma<T, MNRowsZ<T>, true> {  // Z[tb] = [h_prev(t)[b] | x[tb]]
   // reverse direction) for the others, and x
   __amdgpu_buffer_rsrc_t rh, ry, rx;
   uint32_t vh[2], vx[2];
-  bool seg;  // this lane's columns lie in the h part
+  bool seg[2];  // load j's columns lie in the h part (the swizzle moves a
+                // lane's column chunk between its k-rows, across the h / x
+                // border where H is not a multiple of 16 chunks)
   int64_t hlo, hhi, hb, ib;
   __device__ __forceinline__ Dma(const MNRowsZ<T>& op, int64_t r0, int w, int lane) {
     constexpr int64_t E = sizeof(T);
@@ -582,11 +584,11 @@ struct Dma<T, MNRowsZ<T>, true> {  // Z[tb] = [h_prev(t)[b] | x[tb]]
     ry = op.rev ? rsrc_of((const char*)op.y + op.B * hb, (op.K - op.B) * hb)
                 : rsrc_of((const char*)op.y - op.B * hb, op.K * hb);
     rx = rsrc_of(op.x, op.K * ib);
-    seg = mn_r<T>(r0, op.R, mn_kr(w, 0, lane), lane) < op.H;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int kr = mn_kr(w, j, lane);
       const int64_t rj = mn_r<T>(r0, op.R, kr, lane);
+      seg[j] = rj < op.H;
       vh[j] = (uint32_t)(kr * hb + rj * E);
       vx[j] = (uint32_t)(kr * ib + (rj - op.H) * E);
     }
@@ -598,7 +600,7 @@ struct Dma<T, MNRowsZ<T>, true> {  // Z[tb] = [h_prev(t)[b] | x[tb]]
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const uint32_t dst = lds + (4 * w + 2 * j) * 512;
-      if (!seg) {
+      if (!seg[j]) {
         dma16(rx, dst, vx[j], (uint32_t)(k0 * ib));
         asm volatile("; z: x part" ::: "memory");
       } else if (k0 + mn_kr(w, j, lane) >= hlo && k0 + mn_kr(w, j, lane) < hhi) {

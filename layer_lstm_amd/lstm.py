@@ -284,8 +284,8 @@ class Lstm:
 
 
 def stack_query(shape: Shape, layers: int, chunks: int = 0):
-    """lstm_stack_query: (workspace bytes, 1 if a wave's recurrences share
-    one launch)."""
+    """lstm_stack_query: (workspace bytes, the most layers whose
+    recurrences share one launch; 1: one after the other)."""
     n, conc = ctypes.c_size_t(0), ctypes.c_int32(0)
     rc = _lib.lstm_stack_query(ctypes.byref(shape), int(layers), int(chunks), ctypes.byref(n), ctypes.byref(conc))
     if rc != OK:

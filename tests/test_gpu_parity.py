@@ -119,6 +119,9 @@ ALL = dict(W=("u", 0.3), b=("u", 0.3), x=("n", 1.0), h0=("n", 0.5), c0=("n", 0.5
     ("f32", 6, 3, 0, 8),        # no input features
     ("f32", 4, 40, 130, 200),   # several batch groups
     ("bf16", 4, 19, 40, 72),
+    ("bf16", 8, 32, 40, 72),    # dW through the LDS path, the h / x border inside a swizzle group
+    ("bf16", 4, 64, 64, 96),
+    ("f32", 32, 32, 40, 72),    # the same for fp32 (T*B >= 1024)
     ("bf16", 3, 5, 7, 33),      # odd hidden size
     ("bf16", 2, 33, 24, 130),
     # rows of whole kilobytes (the forward's direct-to-LDS path, P and the
