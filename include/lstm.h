@@ -177,7 +177,11 @@ typedef struct {
                                   16-byte aligned x and W assumed) */
   int32_t directions_concurrent; /* LSTM_BIDIRECTIONAL: 1 when both recurrences
                                     run in one launch (grid above is per direction) */
-  int32_t reserved[5];
+  int32_t fwd_tagged;      /* 1: the forward recurrence exchanges h as tagged
+                              words (two values and the step in 8 bytes,
+                              polled in place) instead of a packed ring and
+                              step flags (spread layout, 16-bit storage) */
+  int32_t reserved[4];
 } lstm_plan_info;
 int lstm_query_plan(const lstm_shape* shape, lstm_plan_info* info);
 

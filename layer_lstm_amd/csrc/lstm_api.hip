@@ -163,6 +163,14 @@ int make_plan(int64_t T, int64_t B, int64_t I, int64_t H, int dtype, Plan* p, in
   const size_t nflag = align256((size_t)p->nBG * p->nJG * 4);
   size_t hx = p->off_hflags + nflag, px = p->off_pflags + nflag;
   if (fwd_vec_ok(*p) && hx < 2 * (size_t)p->Bp * HW * 8) hx = 2 * (size_t)p->Bp * HW * 8;
+  // Spread layout, 16-bit storage: the MFMA forward exchanges h as tagged
+  // words (two values and the step in 8 bytes) read straight from the ring,
+  // which saves the wait for the stores and the flag's round trip through
+  // memory on every step; its 8-wave form with one 16-row batch tile reads a
+  // group's words in one round of at most 16 per thread.
+  p->fwd_tag = !p->xcd_local && e == 2 && p->fwd_dma && p->waves == 8 && p->NB <= 16 &&
+               (size_t)p->NB * HW <= 16 * 512;
+  if (p->fwd_tag && hx < 2 * (size_t)p->Bp * HW * 8) hx = 2 * (size_t)p->Bp * HW * 8;
   if (p->bwd_valu && px < 2 * (size_t)p->nJG * p->Hp * p->Bp * 8) px = 2 * (size_t)p->nJG * p->Hp * p->Bp * 8;
   // the role claims follow, one word per work-group
   p->off_hclaim = align256(hx);
@@ -378,6 +386,7 @@ int lstm_query_plan(const lstm_shape* shape, lstm_plan_info* info) {
   info->bwd_valu = p.bwd_valu ? 1 : 0;
   info->inproj_tiles_per_wg = inproj_tiles_per_wg(p);
   info->directions_concurrent = p.bidir && p.concurrent ? 1 : 0;
+  info->fwd_tagged = p.fwd_tag ? 1 : 0;
   return LSTM_OK;
 }
 

@@ -43,7 +43,7 @@
 namespace lstm {
 
 // ---------------------------------------------------------------------------
-template <typename T, int NBT, int NKBW, int C, int NW, int MW>
+template <typename T, int NBT, int NKBW, int C, int NW, int MW, bool TG>
 __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(Launch<FwdArgs> L) {
   constexpr int NTH = 64 * NW;
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -199,6 +199,20 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(Launch<FwdArgs> L) 
   // publish, which waits for every operation of every wave.  The owners read
   // P_t from LDS and stage the step's record there.
   constexpr bool SPLIT = C == 0;
+  // Tagged-word exchange (spread layout): h_t of the group travels as 8-byte
+  // words of two values and the step (t + 1) in the HX region [2][Bp][HW],
+  // stored after the step without a wait or a flag; a reader polls the words
+  // of h_{t-1} until each carries tag t (one round of CW words per thread)
+  // and copies their values into Hl.  Two slots suffice: a work-group that
+  // rewrites a slot at step t + 2 has read every group member's h_{t+1},
+  // which each wrote only after reading the slot's h_t.
+  static_assert(!TG || (SPLIT && E == 2 && NW == 8 && NBT == 1), "the tagged exchange's instances");
+  constexpr bool TAGOK = TG;
+  constexpr int CW = 16;
+  constexpr bool tagm = TG;
+  const int lgHW = 31 - __builtin_clz(a.HW);
+  const int HWv = (a.H + 1) / 2;  // words of a row that carry data
+  const __amdgpu_buffer_rsrc_t hx_rsrc = make_rsrc(a.HX, (uint32_t)(2 * a.Bp * a.HW * 8));
   const uint32_t hl_lds = (uint32_t)(uintptr_t)(lds_void_t*)smem;  // LDS address of Hl
   const int lgNJ = 31 - __builtin_clz(a.NJ);
   const int nbj = a.NB * a.NJ;                            // 16-byte P chunks (4 gates) per step
@@ -297,7 +311,7 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(Launch<FwdArgs> L) 
     stamp(a.stamps, a.T, t, 0);
     inject_failure(a.fail_step, t, wgi, a.err, dead);
     // wait until every work-group of the batch group has published h_{t-1}
-    if (t > 0 && tid < a.nJG) wait_flag(a.HF + bg * a.nJG + tid, (uint32_t)t, a.err, dead);
+    if (t > 0 && !tagm && tid < a.nJG) wait_flag(a.HF + bg * a.nJG + tid, (uint32_t)t, a.err, dead);
     __syncthreads();  // flags seen; the previous step's readers of Hl are done
     stamp(a.stamps, a.T, t, 1);
     // h_{t-1} -> LDS, then the deferred operations
@@ -313,17 +327,77 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(Launch<FwdArgs> L) 
     } else {
       const uint32_t slot0 = (uint32_t)(((t - 1) & 1) * a.Bp + b0) * (uint32_t)rowB;
       if constexpr (C == 0) {
-        // direct-to-LDS: wave-load j moves chunks [64j, 64j + 64) -- 1 KB of
-        // one row, as every row holds a multiple of 64 chunks here (device-
-        // coherent loads, issued as inline asm and waited for explicitly:
-        // the compiler's own waits for the builtin form measured slower
-        // where the ring is read across XCDs)
-        for (int j = w; j * 64 < nchunk; j += NW) {
-          const int bl = (64 * j) / cpr, cc = 64 * j - bl * cpr;
-          lds_dma16_at<true>(hd_rsrc, hl_lds + (uint32_t)(bl * strideH + cc * 16),
-                             slot0 + (uint32_t)(bl * rowB + lane * 16), (uint32_t)(cc * 16));
+        bool tagged = false;
+        if constexpr (TAGOK) {
+          if (tagm) {
+            // word q = bl * HW + w of the group's rows in slot (t - 1) & 1,
+            // q = tid + NTH * c; 8-byte device-coherent loads, re-polled
+            // until each carries tag t (bounded as every other wait)
+            // P_{t+1} and the previous step's record first: they drain
+            // while the words of the other work-groups arrive (issued after
+            // the product's start, they would also hold up any wait for a
+            // spilled operand there)
+            if (t + 1 < a.T) dma_p(t + 1);
+            store_rec(t - 1);
+            const uint32_t sbase = (uint32_t)((((t - 1) & 1) * a.Bp + b0) * a.HW) * 8u;
+            const int nq = NBv << lgHW;
+            uint64_t wv[CW];
+            uint32_t pend = 0;
+#pragma unroll
+            for (int c = 0; c < CW; ++c) {
+              const int q = tid + NTH * c;
+              const bool ok = q < nq && (q & (a.HW - 1)) < HWv;
+              pend |= (ok ? 1u : 0u) << c;
+              wv[c] = ok ? __builtin_bit_cast(uint64_t, __builtin_amdgcn_raw_buffer_load_b64(hx_rsrc, 8 * q, sbase, 16))
+                         : 0ull;
+            }
+            if (!dead) {
+              uint64_t w0 = 0;
+              uint32_t rounds = 0;
+              while (true) {
+                uint32_t miss = 0;
+#pragma unroll
+                for (int c = 0; c < CW; ++c)
+                  if (((pend >> c) & 1u) && (uint32_t)(wv[c] >> 32) != (uint32_t)t) miss |= 1u << c;
+                if (!miss) break;
+                if (w0 == 0) {
+                  w0 = now_ticks();
+                } else if ((++rounds & 15u) == 0 && (now_ticks() - w0 > kWaitTicks || err_set(a.err))) {
+                  atomicOr(a.err, kErrTimeout);
+                  dead = true;
+                  break;
+                }
+#pragma unroll
+                for (int c = 0; c < CW; ++c)
+                  if ((miss >> c) & 1u)
+                    wv[c] = __builtin_bit_cast(
+                        uint64_t, __builtin_amdgcn_raw_buffer_load_b64(hx_rsrc, 8 * (tid + NTH * c), sbase, 16));
+              }
+            }
+            wait_vmem();
+#pragma unroll
+            for (int c = 0; c < CW; ++c)
+              if ((pend >> c) & 1u) {
+                const int q = tid + NTH * c, bl = q >> lgHW, wd = q & (a.HW - 1);
+                *(uint32_t*)(Hl + bl * strideH + wd * 4) = (uint32_t)wv[c];
+              }
+            __builtin_amdgcn_s_waitcnt(kLgkm0);
+            tagged = true;
+          }
         }
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        if (!tagged) {
+          // direct-to-LDS: wave-load j moves chunks [64j, 64j + 64) -- 1 KB
+          // of one row, as every row holds a multiple of 64 chunks here
+          // (device-coherent loads, issued as inline asm and waited for
+          // explicitly: the compiler's own waits for the builtin form
+          // measured slower where the ring is read across XCDs)
+          for (int j = w; j * 64 < nchunk; j += NW) {
+            const int bl = (64 * j) / cpr, cc = 64 * j - bl * cpr;
+            lds_dma16_at<true>(hd_rsrc, hl_lds + (uint32_t)(bl * strideH + cc * 16),
+                               slot0 + (uint32_t)(bl * rowB + lane * 16), (uint32_t)(cc * 16));
+          }
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        }
       } else {
         for (int q0 = 0; q0 < nchunk; q0 += NTH * C) {
           u32x4_t v[C];
@@ -356,8 +430,10 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(Launch<FwdArgs> L) 
     }
     stamp(a.stamps, a.T, t, 2);
     if constexpr (SPLIT) {
-      if (t + 1 < a.T) dma_p(t + 1);
-      if (t > 0) store_rec(t - 1);
+      if (!tagm || t == 0) {  // (the tagged exchange issues them before its ring read)
+        if (t + 1 < a.T) dma_p(t + 1);
+        if (t > 0) store_rec(t - 1);
+      }
     }
 
     // MFMA: part[mi][nt] = W_h[rows of M-tile mg*MW + mi, k part] .
@@ -491,7 +567,7 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(Launch<FwdArgs> L) 
           const uint64_t g64 = __builtin_bit_cast(uint64_t, g4);
           gq[nt] = u32x4_t{(uint32_t)g64, (uint32_t)(g64 >> 32), 0u, 0u};
         }
-        if (valid) store_elem<T>(dst + (int64_t)b * a.Hp + u, hq[nt], local);
+        if (valid && !tagm) store_elem<T>(dst + (int64_t)b * a.Hp + u, hq[nt], local);
         if constexpr (SPLIT) {
           const int bl = 16 * nt + fr, ul = u - j0;
           if (bl < a.NB) {
@@ -509,7 +585,25 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(Launch<FwdArgs> L) 
     }
     wait_vmem();
     __syncthreads();
-    if (tid == 0) store_flag(a.HF + bg * a.nJG + jg, (uint32_t)(t + 1), local);
+    if (tagm) {
+      if constexpr (TAGOK) {
+        // h_t of this work-group's units from the staging area: word i of
+        // row bl holds units j0 + 2i and j0 + 2i + 1 (0 past H)
+        const int npair = a.NJ / 2, lgp = 31 - __builtin_clz(npair);
+        uint64_t* slot = a.HX + ((int64_t)(t & 1) * a.Bp + b0) * a.HW + (j0 >> 1);
+        for (int q = tid; q < NBv * npair; q += NTH) {
+          const int bl = q >> lgp, i = q & (npair - 1), u0 = j0 + 2 * i;
+          if (u0 < a.H) {
+            const uint16_t v0 = *(const uint16_t*)(hS + bl * hSr + 2 * i * E);
+            const uint16_t v1 = u0 + 1 < a.H ? *(const uint16_t*)(hS + bl * hSr + (2 * i + 1) * E) : (uint16_t)0;
+            xstore_word(slot + (int64_t)bl * a.HW + i,
+                        ((uint64_t)(uint32_t)(t + 1) << 32) | ((uint64_t)v1 << 16) | (uint64_t)v0, false);
+          }
+        }
+      }
+    } else if (tid == 0) {
+      store_flag(a.HF + bg * a.nJG + jg, (uint32_t)(t + 1), local);
+    }
     stamp(a.stamps, a.T, t, 5);
   }
   // the last step's record and the final states
@@ -532,26 +626,27 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(Launch<FwdArgs> L) 
 }
 
 // ---------------------------------------------------------------------------
-template <typename T, int NBT, int C, int NW, int MW>
+template <typename T, int NBT, int C, int NW, int MW, bool TG>
 static hipError_t fwd_dispatch_mw(const Plan& p, Launch<FwdArgs>& a, hipStream_t s) {
   const int nt = 64 * NW;
   switch (p.fwd_nkbw) {
-    case 1: return coop_launch(fwd_rec_kernel<T, NBT, 1, C, NW, MW>, launch_grid(p, a), p.lds_fwd, &a, s, nt);
-    case 2: return coop_launch(fwd_rec_kernel<T, NBT, 2, C, NW, MW>, launch_grid(p, a), p.lds_fwd, &a, s, nt);
-    case 4: return coop_launch(fwd_rec_kernel<T, NBT, 4, C, NW, MW>, launch_grid(p, a), p.lds_fwd, &a, s, nt);
-    case 8: return coop_launch(fwd_rec_kernel<T, NBT, 8, C, NW, MW>, launch_grid(p, a), p.lds_fwd, &a, s, nt);
-    case 16: return coop_launch(fwd_rec_kernel<T, NBT, 16, C, NW, MW>, launch_grid(p, a), p.lds_fwd, &a, s, nt);
+    case 1: return coop_launch(fwd_rec_kernel<T, NBT, 1, C, NW, MW, TG>, launch_grid(p, a), p.lds_fwd, &a, s, nt);
+    case 2: return coop_launch(fwd_rec_kernel<T, NBT, 2, C, NW, MW, TG>, launch_grid(p, a), p.lds_fwd, &a, s, nt);
+    case 4: return coop_launch(fwd_rec_kernel<T, NBT, 4, C, NW, MW, TG>, launch_grid(p, a), p.lds_fwd, &a, s, nt);
+    case 8: return coop_launch(fwd_rec_kernel<T, NBT, 8, C, NW, MW, TG>, launch_grid(p, a), p.lds_fwd, &a, s, nt);
+    case 16: return coop_launch(fwd_rec_kernel<T, NBT, 16, C, NW, MW, TG>, launch_grid(p, a), p.lds_fwd, &a, s, nt);
     case 32:
-      if constexpr (MW == 1) return coop_launch(fwd_rec_kernel<T, NBT, 32, C, NW, MW>, launch_grid(p, a), p.lds_fwd, &a, s, nt);
+      if constexpr (MW == 1)
+        return coop_launch(fwd_rec_kernel<T, NBT, 32, C, NW, MW, TG>, launch_grid(p, a), p.lds_fwd, &a, s, nt);
       break;
   }
   return hipErrorInvalidValue;
 }
 
-template <typename T, int NBT, int C, int NW>
+template <typename T, int NBT, int C, int NW, bool TG = false>
 static hipError_t fwd_dispatch_c(const Plan& p, Launch<FwdArgs>& a, hipStream_t s) {
-  if (p.fwd_mw == 2) return fwd_dispatch_mw<T, NBT, C, NW, 2>(p, a, s);
-  if (p.fwd_mw == 1) return fwd_dispatch_mw<T, NBT, C, NW, 1>(p, a, s);
+  if (p.fwd_mw == 2) return fwd_dispatch_mw<T, NBT, C, NW, 2, TG>(p, a, s);
+  if (p.fwd_mw == 1) return fwd_dispatch_mw<T, NBT, C, NW, 1, TG>(p, a, s);
   return hipErrorInvalidValue;
 }
 
@@ -562,6 +657,9 @@ static hipError_t fwd_dispatch_c(const Plan& p, Launch<FwdArgs>& a, hipStream_t 
 template <typename T, int NBT>
 static hipError_t fwd_dispatch(const Plan& p, Launch<FwdArgs>& a, hipStream_t s) {
   const bool dma = p.fwd_dma != 0;
+  if constexpr (sizeof(T) == 2 && NBT == 1)
+    if (p.fwd_tag && dma && p.waves == 8) return fwd_dispatch_c<T, NBT, 0, 8, true>(p, a, s);
+  if (p.fwd_tag) return hipErrorInvalidValue;
   if constexpr (sizeof(T) == 2)
     if (p.waves == 8) return dma ? fwd_dispatch_c<T, NBT, 0, 8>(p, a, s) : fwd_dispatch_c<T, NBT, 4, 8>(p, a, s);
   if (p.waves != kWaves) return hipErrorInvalidValue;

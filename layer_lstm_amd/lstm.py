@@ -51,8 +51,8 @@ class Shape(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in ("rows_per_group", "units_per_group", "groups", "units_groups",
                                                "grid", "waves", "xcd_local", "fwd_valu", "bwd_valu",
-                                               "inproj_tiles_per_wg", "directions_concurrent")] + \
-               [("reserved", ctypes.c_int32 * 5)]
+                                               "inproj_tiles_per_wg", "directions_concurrent", "fwd_tagged")] + \
+               [("reserved", ctypes.c_int32 * 4)]
 
 
 _P = ctypes.c_void_p

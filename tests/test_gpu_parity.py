@@ -75,12 +75,15 @@ def full_check(inp, lstm, tol=None):
 # (rows per group, units per group, waves, XCD-local, forward VALU, backward
 # VALU), and the input projection's output tiles per work-group (> 1: the
 # persistent form; 256 x 256 bf16 tiles, 32-deep stages)
+# (rows, units, waves, XCD-local, VALU forward, VALU backward), input
+# projection tiles per work-group, tagged forward exchange (the spread
+# layout's 16-bit form)
 PLANS = {
-    "f32_T8_B4_I16_H32": ((4, 8, 4, 0, 1, 1), 1),
-    "f32_T64_B32_I256_H256": ((4, 8, 4, 1, 1, 1), 1),
-    "bf16_T128_B64_I512_H1024": ((8, 32, 8, 1, 0, 0), 2),     # 32 x 16 tiles
-    "bf16_T512_B16_I1024_H2048": ((8, 16, 8, 0, 0, 0), 4),    # 32 x 32 tiles
-    "bf16_T256_B256_I1024_H1024": ((32, 32, 8, 1, 0, 0), 16), # 256 x 16 tiles
+    "f32_T8_B4_I16_H32": ((4, 8, 4, 0, 1, 1), 1, 0),
+    "f32_T64_B32_I256_H256": ((4, 8, 4, 1, 1, 1), 1, 0),
+    "bf16_T128_B64_I512_H1024": ((8, 32, 8, 1, 0, 0), 2, 0),     # 32 x 16 tiles
+    "bf16_T512_B16_I1024_H2048": ((8, 16, 8, 0, 0, 0), 4, 1),    # 32 x 32 tiles
+    "bf16_T256_B256_I1024_H1024": ((32, 32, 8, 1, 0, 0), 16, 0), # 256 x 16 tiles
 }
 
 
@@ -95,6 +98,7 @@ def test_workload_plans(lstm, name):
     got = (p["rows_per_group"], p["units_per_group"], p["waves"], p["xcd_local"], p["fwd_valu"], p["bwd_valu"])
     assert got == PLANS[name][0]
     assert p["inproj_tiles_per_wg"] == PLANS[name][1]
+    assert p["fwd_tagged"] == PLANS[name][2]
     assert p["grid"] == p["groups"] * p["units_groups"] <= 256
 
 
@@ -808,3 +812,26 @@ def test_full_lengths_are_the_plain_path_gpu(lstm):
     b, _, _ = run_gpu(dict(inp, lengths=np.full(60, 5, np.int32)), lstm, torch)
     for k in a:
         assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("dt,T,B,I,H,rev,lengths", [
+    ("bf16", 6, 16, 64, 2048, False, False),   # the T=512 B=16 layout, short
+    ("bf16", 5, 13, 40, 2048, False, False),   # a last batch group that is not full
+    ("f16", 5, 16, 32, 2048, True, False),     # fp16, reverse direction
+    ("bf16", 7, 16, 24, 2048, False, True),    # sequence lengths (held states travel as words too)
+    ("bf16", 9, 9, 16, 1536, True, True),      # H not a power of two, both
+])
+def test_tagged_exchange(lstm, dt, T, B, I, H, rev, lengths):
+    """The forward recurrence's tagged-word exchange (spread layout, 16-bit
+    storage): h_t as words of two values and the step, polled in place."""
+    code = {"bf16": lstm.BF16, "f16": lstm.F16}[dt]
+    p = lstm.query_plan(lstm.make_shape(T, B, I, H, code, reverse=rev))
+    if torch.cuda.get_device_properties(0).multi_processor_count != 256:
+        pytest.skip("layouts are stated for 256 CUs")
+    assert p["fwd_tagged"] == 1, p
+    inp = synth.make_inputs(T, B, I, H, dt, seed=131, dist=contracting(H))
+    inp["reverse"] = rev
+    if lengths:
+        inp["lengths"] = ragged_lengths(T, B, 132)
+    say(f"case: tagged exchange {dt} T={T} B={B} I={I} H={H} reverse={rev} lengths={lengths} plan={p}")
+    full_check(inp, lstm)
