@@ -833,9 +833,10 @@ __device__ __forceinline__ float lane_xor8(float v) {
 // are in flight while the previous tile ends and writes its outputs.  Four
 // ring slots, the stages per tile a multiple of four: every tile starts in
 // slot 0 and its loop is unrolled over the ring.  splits == 1; a second
-// slab of work-groups (blockIdx.z == 1) only clears `zero`.  The tiles of an XCD (work-groups i mod nxcd) are one contiguous
-// range of the row-major tile order, walked together, each work-group taking
-// every (work-groups per XCD)-th.
+// slab of work-groups (blockIdx.z == 1) only clears `zero`.  The tiles of an
+// XCD (work-groups i mod nxcd) are one contiguous range of the tile order,
+// walked together, each work-group taking every (work-groups per XCD)-th;
+// within the range the order runs over blocks of 4 x 8 tiles (tm, tn below).
 template <typename T, class AOp, class BOp, class Epi>
 __global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_multi_kernel(GemmArgs<AOp, BOp, Epi> g) {
   constexpr int TILE = LdsCfg<T>::kTile, KST = LdsCfg<T>::kKStage;
@@ -852,21 +853,36 @@ __global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_multi_kernel(
   }
   const int wm = w / WGN, wn = w % WGN, fr = lane & 15, fq = lane >> 4;
   const int i = blockIdx.x, per_xcd = g.tiles_x * g.tiles_y / g.nxcd;
+  // Tile t of an XCD's range in blocks of 4 row-tiles x 8 column-tiles (the
+  // 32 tiles its work-groups run at once: 6 MB of operands at 256 x 256 x
+  // 1024 against 10 MB for 2 whole tile rows), where the range holds whole
+  // blocks; else row-major.
+  const bool blk48 = per_xcd % g.tiles_x == 0 && (per_xcd / g.tiles_x) % 4 == 0 && g.tiles_x % 8 == 0;
+  auto tm = [&](int t) -> int {
+    if (!blk48) return t / g.tiles_x;
+    const int r = t % per_xcd, bq = r >> 5, e = r & 31;
+    return (t - r) / g.tiles_x + (bq / (g.tiles_x >> 3)) * 4 + (e >> 3);
+  };
+  auto tn = [&](int t) -> int {
+    if (!blk48) return t % g.tiles_x;
+    const int r = t % per_xcd, bq = r >> 5, e = r & 31;
+    return (bq % (g.tiles_x >> 3)) * 8 + (e & 7);
+  };
   const int tstep = (int)gridDim.x / g.nxcd;
   const int tile0 = (i % g.nxcd) * per_xcd + i / g.nxcd;
   const int nk = (int)(g.K / KST);  // stages per tile
   const int S = nk * g.per_wg;      // stages of the stream
 
   int it = tile0, ik = 0;  // tile and stage of the next load
-  Dma<T, AOp, false> da(g.a, (int64_t)(it / g.tiles_x) * TILE, w, lane);
-  Dma<T, BOp, false> db(g.b, (int64_t)(it % g.tiles_x) * TILE, w, lane);
+  Dma<T, AOp, false> da(g.a, (int64_t)tm(it) * TILE, w, lane);
+  Dma<T, BOp, false> db(g.b, (int64_t)tn(it) * TILE, w, lane);
   const uint32_t rl0 = (uint32_t)(uintptr_t)(lds_void_t*)ring;
   auto issue_next = [&](uint32_t st) {
     if (ik == nk) {
       ik = 0;
       it += tstep;
-      da = Dma<T, AOp, false>(g.a, (int64_t)(it / g.tiles_x) * TILE, w, lane);
-      db = Dma<T, BOp, false>(g.b, (int64_t)(it % g.tiles_x) * TILE, w, lane);
+      da = Dma<T, AOp, false>(g.a, (int64_t)tm(it) * TILE, w, lane);
+      db = Dma<T, BOp, false>(g.b, (int64_t)tn(it) * TILE, w, lane);
     }
     const int64_t k0 = (int64_t)(ik++) * KST;
     da.issue(st, k0, w, lane);
@@ -880,7 +896,7 @@ __global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_multi_kernel(
     for (int a = 0; a < WM; ++a)
 #pragma unroll
       for (int j = 0; j < WN; ++j) acc[a][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int64_t n0 = (int64_t)(t % g.tiles_x) * TILE;
+    const int64_t n0 = (int64_t)tn(t) * TILE;
 #pragma unroll
     for (int j = 0; j < WN; ++j) {
       const int64_t n = n0 + wn * 16 * WN + j * 16 + 4 * fq;
@@ -912,7 +928,7 @@ __global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_multi_kernel(
     }
   };
   auto epilogue = [&](int t) {
-    const int64_t m0 = (int64_t)(t / g.tiles_x) * TILE, n0 = (int64_t)(t % g.tiles_x) * TILE;
+    const int64_t m0 = (int64_t)tm(t) * TILE, n0 = (int64_t)tn(t) * TILE;
     const bool hi = fr >= 8;
 #pragma unroll
     for (int a = 0; a < WM; ++a)
