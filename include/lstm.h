@@ -89,9 +89,11 @@ enum {
   LSTM_ERR_TIMEOUT = -9,     /* a per-step wait of the recurrent kernels hit its time bound */
   LSTM_ERR_DEVICE = -10,     /* the current device is not gfx950 or could not be queried */
   LSTM_ERR_SCRATCH = -11,    /* lstm_fwd_train_scratch: the shape needs more than LSTM_SCRATCH_BYTES */
-  LSTM_ERR_PLACEMENT = -12   /* lstm_check_workspace: two work-groups of a recurrent launch took one
+  LSTM_ERR_PLACEMENT = -12,  /* lstm_check_workspace: two work-groups of a recurrent launch took one
                                 role (the device dealt them to its XCDs otherwise than the XCD-local
                                 layout assumes); later calls on this device use the spread layout */
+  LSTM_ERR_STATE = -13       /* lstm_check_workspace: the workspace's status word holds bits no call
+                                writes (a workspace that no forward pass has filled) */
 };
 
 /* Direction of time (SingleLayerLstmGrad, 参数说明: the direction attribute,
@@ -252,7 +254,10 @@ int lstm_bwd(const lstm_shape* shape, const void* dy, const void* dhT, const voi
  * seconds, or the device did not deal work-groups to its XCDs round robin
  * as the XCD-local layout relies on); it stays set, and the outputs of later calls on the workspace are
  * undefined, until lstm_fwd_train() runs again on it.  After any error,
- * run lstm_fwd_train() before the next lstm_bwd() on the same workspace. */
+ * run lstm_fwd_train() before the next lstm_bwd() on the same workspace.
+ * Every lstm_fwd_train() (T = 0 and B = 0 included) defines the status word;
+ * a word with bits no call writes (a workspace no forward pass has filled)
+ * gives LSTM_ERR_STATE and changes no layout choice. */
 int lstm_check_workspace(void* workspace, size_t workspace_bytes, void* stream);
 
 /* Per-kernel timing, for measurement.  While enabled (on != 0), every
@@ -321,8 +326,9 @@ int lstm_stack_bwd(const lstm_shape* shape, int64_t layers, int64_t chunks, cons
  * in the layout lstm_fwd_train() uses for `shape` (layout 0), or that
  * layout with its batch groups spread over the XCDs (layout 1: device-
  * coherent stores, every exchange through memory), without the product or
- * the gate math.  `workspace` (lstm_query() bytes) is overwritten.  Waits
- * for the stream; sets *us_per_step to the launch's time / T.  Returns
+ * the gate math.  `workspace` (lstm_query() bytes) is overwritten.  Runs the
+ * probe once untimed, then once between two events; waits for the stream
+ * and sets *us_per_step to the timed launch's time / T.  Returns
  * LSTM_OK, an error of lstm_query(), LSTM_ERR_DIMS (T or B < 1, or another
  * layout), or LSTM_ERR_TIMEOUT. */
 int lstm_probe_exchange(const lstm_shape* shape, int layout, void* workspace, size_t workspace_bytes,

@@ -193,11 +193,12 @@ int lstm_stack_fwd_train(const lstm_shape* shape, int64_t layers, int64_t chunks
   hipStream_t s = (hipStream_t)stream;
   char* ws = (char*)workspace;
   hipError_t err = hipSuccess;
-  if (B == 0) return LSTM_OK;
   const int64_t sst = B * H * e;
-  if (T == 0) {
-    err = launch_copy_state(h0, hT, (size_t)(L * B * H), e, s);
-    if (err == hipSuccess) err = launch_copy_state(c0, cT, (size_t)(L * B * H), e, s);
+  if (B == 0 || T == 0) {
+    // no recurrence runs: the status word is cleared here (see lstm_fwd_train)
+    err = launch_fill_zero(ws, 4, s);
+    if (err == hipSuccess && B > 0) err = launch_copy_state(h0, hT, (size_t)(L * B * H), e, s);
+    if (err == hipSuccess && B > 0) err = launch_copy_state(c0, cT, (size_t)(L * B * H), e, s);
     return status_from(err);
   }
   auto wof = [&](int l) -> const char* {

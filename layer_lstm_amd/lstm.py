@@ -31,7 +31,8 @@ F32, BF16, F16 = 0, 1, 2
 OK = 0
 STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_DIMS", -3: "ERR_DTYPE", -4: "ERR_ALIGN",
           -5: "ERR_WORKSPACE", -6: "ERR_UNSUPPORTED", -7: "ERR_COOP", -8: "ERR_LAUNCH",
-          -9: "ERR_TIMEOUT", -10: "ERR_DEVICE", -11: "ERR_SCRATCH", -12: "ERR_PLACEMENT"}
+          -9: "ERR_TIMEOUT", -10: "ERR_DEVICE", -11: "ERR_SCRATCH", -12: "ERR_PLACEMENT",
+          -13: "ERR_STATE"}
 DEBUG_FAIL_STEP, DEBUG_MISPLACE, DEBUG_XCD_LOCAL = 1, 2, 3  # lstm_debug_inject
 SCRATCH_BYTES = 64 << 20  # LSTM_SCRATCH_BYTES
 EXPORTS = ("lstm_abi_version", "lstm_status_string", "lstm_query", "lstm_query_plan", "lstm_fwd_train",

@@ -122,6 +122,7 @@ def test_debug_inject_host_checks(lstm):
     assert lstm.lib().lstm_debug_inject(lstm.DEBUG_FAIL_STEP, 3) == 0
     assert lstm.lib().lstm_debug_inject(lstm.DEBUG_FAIL_STEP, -1) == 0
     assert header_enum("LSTM_ERR_PLACEMENT") == -12
+    assert header_enum("LSTM_ERR_STATE") == -13
     assert header_enum("LSTM_DEBUG_FAIL_STEP") == lstm.DEBUG_FAIL_STEP
     assert header_enum("LSTM_DEBUG_MISPLACE") == lstm.DEBUG_MISPLACE
     assert header_enum("LSTM_DEBUG_XCD_LOCAL") == lstm.DEBUG_XCD_LOCAL

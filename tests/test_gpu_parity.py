@@ -38,7 +38,7 @@ import pytest
 
 from layer_lstm_amd import synth
 from oracle import oracle
-from parity_util import TOL, compare, compare_rows, rel_l2, run_gpu, to_dev, to_host
+from parity_util import ROW_TOL, TOL, compare, compare_rows, rel_l2, run_gpu, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -219,12 +219,6 @@ FULL_CHUNK = {
 }
 LARGEST = "bf16_T256_B256_I1024_H1024"
 FULL_PARITY = os.environ.get("LSTM_FULL_PARITY") == "1"
-# Bound of the per-row check (row_errors), five times the whole-tensor
-# tolerance: a row is a small sample (a db value sums T*B terms, a dW row
-# H+I columns), so its rounding error spreads wider than the whole tensor's
-# (bf16 rows reach 2-4e-2 where the tensors sit at 5e-3), while a corrupted,
-# stale or unwritten row is off by about its own size (a ratio near 1).
-ROW_TOL = {"f32": 5e-5, "bf16": 1e-1, "f16": 1.25e-2}
 
 
 def rows_of(inp, rows):

@@ -104,3 +104,32 @@ def test_exchange_probe_runs_in_both_layouts(lstm):
         us = [lstm.probe_exchange(m.shape, m.workspace, layout) for layout in (0, 1)]
         print(name, "floor us/step", us, flush=True)
         assert all(0 < u < 50 for u in us)
+
+
+def test_status_word_of_empty_calls_and_unfilled_workspaces(lstm):
+    """A forward with T = 0 or B = 0 (no recurrence runs) still defines the
+    workspace's status word, so checking it after such a call reports OK
+    whatever the memory held before; a word holding bits no call writes (a
+    workspace no forward pass has filled) reports ERR_STATE and leaves the
+    layout choice alone.  (A stale word used to read as a placement error
+    and switch the device to the spread layout.)"""
+    probe = lstm.make_shape(6, 60, 32, 512, lstm.BF16)
+    local = lstm.query_plan(probe)["xcd_local"]
+    for T, B in ((0, 4), (3, 0)):
+        m = lstm.Lstm(T, B, 8, 16, lstm.F32)
+        m.workspace.fill_(0xFF)
+        x = torch.zeros((T, B, 8), device="cuda")
+        W = torch.zeros((64, 24), device="cuda")
+        h0 = torch.zeros((B, 16), device="cuda")
+        m.forward(x, W, None, h0, h0)
+        m.check()  # raises on anything but OK
+    m = lstm.Lstm(3, 4, 8, 16, lstm.F32)
+    m.workspace.fill_(0xFF)
+    torch.cuda.synchronize()
+    assert lstm.check_workspace(m.workspace) == -13
+    assert lstm.query_plan(probe)["xcd_local"] == local
+    stack = lstm.Stack(0, 4, 8, 16, 2, lstm.F32)
+    stack.workspace.fill_(0xFF)
+    h = torch.zeros((2, 4, 16), device="cuda")
+    stack.forward(torch.zeros((0, 4, 8), device="cuda"), torch.zeros(stack.w_elems, device="cuda"), None, h, h)
+    stack.check()

@@ -10,7 +10,7 @@ import pytest
 
 from layer_lstm_amd import synth
 from oracle import oracle
-from parity_util import TOL, compare, compare_rows, rel_l2, to_dev, to_host
+from parity_util import ROW_TOL, TOL, compare, compare_rows, rel_l2, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -18,7 +18,6 @@ torch = pytest.importorskip("torch")
 
 ALL = dict(W=("u", 0.3), b=("u", 0.3), x=("n", 1.0), h0=("n", 0.5), c0=("n", 0.5), dy=("n", 1.0),
            dhT=("n", 1.0), dcT=("n", 1.0))
-ROW_TOL = {"f32": 5e-5, "bf16": 1e-1, "f16": 1.25e-2}
 
 
 @pytest.fixture(scope="module")
