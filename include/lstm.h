@@ -151,9 +151,13 @@ int lstm_abi_version(void);
 const char* lstm_status_string(int status);
 
 /* Workspace size in bytes for `shape` on the current device.
- * Envelope: H <= 1024 (fp32) or 2048 (16-bit storage), I <= 65536, T*B <= 2^31/4H,
- * T <= 2^30.  Returns LSTM_OK and sets
- * *workspace_bytes, or an error code (workspace_bytes untouched). */
+ * Envelope: I <= 65536, T*B <= 2^31/4H, T <= 2^30, and a layout of the
+ * persistent recurrences for B and H (their work-groups hold W_h in
+ * registers, one per CU).  On a 256-CU MI355X: fp32 up to H = 512 (B up to
+ * 256 at H = 512, more below), H = 640..1024 for B <= 8; 16-bit storage up to
+ * H = 1024 (B up to 256 at H = 1024, more below), H up to 2048 for B <= 32
+ * (64 at some sizes).  Outside it: LSTM_ERR_UNSUPPORTED.  Returns LSTM_OK and
+ * sets *workspace_bytes, or an error code (workspace_bytes untouched). */
 int lstm_query(const lstm_shape* shape, size_t* workspace_bytes);
 
 /* How the persistent recurrences are laid out for `shape` on the current
