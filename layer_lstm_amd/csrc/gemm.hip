@@ -842,7 +842,9 @@ __global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_multi_kernel(
   constexpr int TILE = LdsCfg<T>::kTile, KST = LdsCfg<T>::kKStage;
   constexpr int STAGE = lds_stage_bytes<T>();
   constexpr int NS = 4;
+  constexpr int kColTable = 8192;  // column terms held in LDS (floats): N <= 8192
   __shared__ __attribute__((aligned(16))) char ring[NS * STAGE];
+  __shared__ __attribute__((aligned(16))) float coltab[kColTable];
   constexpr int WGN = LdsCfg<T>::kWaves / 2;  // waves along n (2 along m)
   constexpr int WM = TILE / 2 / 16, WN = TILE / WGN / 16;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -850,6 +852,16 @@ __global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_multi_kernel(
     const int64_t nt = (int64_t)gridDim.x * LdsCfg<T>::kThreads;
     for (int64_t i = (int64_t)blockIdx.x * LdsCfg<T>::kThreads + tid; i < g.zero_words; i += nt) g.zero[i] = 0u;
     return;
+  }
+  // The column terms (the bias) of every output column go into LDS once,
+  // before the stream of loads starts, when the columns come in fours and
+  // fit: a tile then reads its terms from LDS, and no global load of them
+  // sits between one tile's P stores and the next tile's stages.
+  const bool ctab = (g.N & 3) == 0 && g.N <= kColTable;
+  if (ctab) {
+    for (int64_t n = 4 * (int64_t)tid; n < g.N; n += 4 * (int64_t)LdsCfg<T>::kThreads)
+      *(f32x4_t*)(coltab + n) = g.epi.col4(n);
+    __syncthreads();
   }
   const int wm = w / WGN, wn = w % WGN, fr = lane & 15, fq = lane >> 4;
   const int i = blockIdx.x, per_xcd = g.tiles_x * g.tiles_y / g.nxcd;
@@ -897,15 +909,23 @@ __global__ void __launch_bounds__(LdsCfg<T>::kThreads, 1) gemm_lds_multi_kernel(
 #pragma unroll
       for (int j = 0; j < WN; ++j) acc[a][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int64_t n0 = (int64_t)tn(t) * TILE;
+    if (ctab) {
 #pragma unroll
-    for (int j = 0; j < WN; ++j) {
-      const int64_t n = n0 + wn * 16 * WN + j * 16 + 4 * fq;
-      colt[j] = ((g.N & 3) == 0 && n + 3 < g.N) ? g.epi.col4(n) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < WN; ++j) {
+        const int64_t n = n0 + wn * 16 * WN + j * 16 + 4 * fq;
+        colt[j] = n + 3 < g.N ? *(const f32x4_t*)(coltab + n) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < WN; ++j) {
+        const int64_t n = n0 + wn * 16 * WN + j * 16 + 4 * fq;
+        colt[j] = ((g.N & 3) == 0 && n + 3 < g.N) ? g.epi.col4(n) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      // an explicit wait for these loads (and everything before them), so
+      // that the compiler places none of its own in the epilogue inside the
+      // stream, where it would also wait for the next tile's ring loads
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     }
-    // an explicit wait for these loads (and everything before them), so that
-    // the compiler places none of its own in the epilogue inside the stream,
-    // where it would also wait for the next tile's ring loads
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   };
   // Output blocks are written in pairs of 16 x 16 blocks (j0, j1 = j0 + 1):
   // lanes of rows 0-7 keep their j0 values and take the j1 values of the
