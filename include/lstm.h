@@ -338,6 +338,32 @@ int lstm_stack_bwd(const lstm_shape* shape, int64_t layers, int64_t chunks, cons
 int lstm_probe_exchange(const lstm_shape* shape, int layout, void* workspace, size_t workspace_bytes,
                         double* us_per_step, void* stream);
 
+/* The parts of a stage of the pipelined bf16 products, for measurement:
+ * runs one work-group of 8 waves (512 threads; two waves per SIMD, as the
+ * products run) on every compute unit, each wave issuing `iters` iterations
+ * of 32 v_mfma_f32_16x16x32_bf16 on operands in registers, plus the parts
+ * of a product stage that `parts` (LSTM_PROBE_* bits) selects:
+ *   LSTM_PROBE_READS        12 KB of fragment reads per wave from LDS,
+ *                           before the iteration's products;
+ *   LSTM_PROBE_READS_AHEAD  the same reads for the next iteration, issued
+ *                           before this one's products (not with READS);
+ *   LSTM_PROBE_BARRIER      one work-group barrier per iteration;
+ *   LSTM_PROBE_DMA          four 1 KB direct-to-LDS loads per wave and
+ *                           iteration from a 64 KB buffer, three iterations
+ *                           in flight.
+ * It computes nothing of the LSTM.  `scratch` is device memory of at least
+ * LSTM_PROBE_SCRATCH_BYTES, 256-byte aligned, overwritten.  Runs the probe
+ * once untimed, then once between two events; waits for the stream and sets
+ * *frac_of_peak to the MFMA FLOPs / time / the dense bf16 peak (2516.6
+ * TFLOP/s for 256 compute units, scaled to the device's count).  Returns
+ * LSTM_OK, LSTM_ERR_NULL, LSTM_ERR_DIMS (unknown bits, both read orders, or
+ * iters outside [1, 2^24]), LSTM_ERR_ALIGN, LSTM_ERR_WORKSPACE (scratch too
+ * small), LSTM_ERR_DEVICE or LSTM_ERR_LAUNCH. */
+enum { LSTM_PROBE_READS = 1, LSTM_PROBE_READS_AHEAD = 2, LSTM_PROBE_BARRIER = 4, LSTM_PROBE_DMA = 8 };
+#define LSTM_PROBE_SCRATCH_BYTES ((size_t)1 << 20)
+int lstm_probe_mfma_stage(int parts, int64_t iters, void* scratch, size_t scratch_bytes, double* frac_of_peak,
+                          void* stream);
+
 /* Test hooks, for the tests of the failure paths (host-side settings that
  * later calls copy into their launches; every kernel still exits normally):
  *   LSTM_DEBUG_FAIL_STEP, value s >= 0: at step s (in execution order) of

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblstm.so")
 SOURCES = ["lstm_api.hip", "gemm.hip", "recurrent.hip", "recurrent_vec.hip", "recurrent_bwd.hip", "exchange_probe.hip",
-           "stack_api.hip"]
+           "stack_api.hip", "mfma_probe.hip"]
 ARCH = "gfx950"
 
 

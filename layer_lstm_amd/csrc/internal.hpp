@@ -181,6 +181,12 @@ hipError_t launch_bwd_recurrent(const Plan& p, const BwdSlot* slots, int nslots,
 // The forward recurrence's exchange alone (exchange_probe.hip): flags, ring
 // copy, ring stores, no arithmetic; HX must start cleared.
 hipError_t launch_exchange_probe(const Plan& p, void* HX, uint32_t* err, hipStream_t s);
+// The parts of a stage of the pipelined bf16 products (mfma_probe.hip):
+// `parts` of the kProbe* bits (LSTM_PROBE_* of lstm.h), at most one of the
+// two read orders; grid work-groups of 512 threads; src: 64 KB, sink: grid
+// x 512 floats.
+constexpr int kProbeReads = 1, kProbeReadsAhead = 2, kProbeBarrier = 4, kProbeDma = 8;
+hipError_t launch_mfma_probe(int parts, int grid, const uint32_t* src, float* sink, int iters, hipStream_t s);
 // The two directions' [rows][H] outputs side by side into [rows][2H]
 // (join), or [rows][2H] cotangents back into two [rows][H] (split).
 hipError_t launch_join_dirs(const void* y0, const void* y1, void* y, int64_t rows, int64_t row_bytes, hipStream_t s);

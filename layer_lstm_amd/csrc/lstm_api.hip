@@ -664,6 +664,47 @@ int lstm_probe_exchange(const lstm_shape* shape, int layout, void* workspace, si
   return lstm_check_workspace(workspace, workspace_bytes, stream);
 }
 
+int lstm_probe_mfma_stage(int parts, int64_t iters, void* scratch, size_t scratch_bytes, double* frac_of_peak,
+                          void* stream) {
+  if (!scratch || !frac_of_peak) return LSTM_ERR_NULL;
+  if (parts < 0 || parts > 15 || ((parts & LSTM_PROBE_READS) && (parts & LSTM_PROBE_READS_AHEAD)) || iters < 1 ||
+      iters > (1 << 24))
+    return LSTM_ERR_DIMS;
+  if (((uintptr_t)scratch & 255u)) return LSTM_ERR_ALIGN;
+  if (scratch_bytes < LSTM_PROBE_SCRATCH_BYTES) return LSTM_ERR_WORKSPACE;
+  int cus = 0;
+  const int dev = device_cus(&cus);
+  if (dev != LSTM_OK) return dev;
+  if ((size_t)64 * 1024 + (size_t)cus * 512 * 4 > LSTM_PROBE_SCRATCH_BYTES) return LSTM_ERR_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  const uint32_t* src = (const uint32_t*)scratch;
+  float* sink = (float*)((char*)scratch + 64 * 1024);
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+    if (e0) (void)hipEventDestroy(e0);
+    return LSTM_ERR_LAUNCH;
+  }
+  // an untimed run first (the kernel's code object is loaded then)
+  hipError_t err = launch_fill_zero(scratch, 64 * 1024, s);
+  if (err == hipSuccess) err = launch_mfma_probe(parts, cus, src, sink, 16, s);
+  if (err == hipSuccess) err = hipEventRecord(e0, s);
+  if (err == hipSuccess) err = launch_mfma_probe(parts, cus, src, sink, (int)iters, s);
+  if (err == hipSuccess) err = hipEventRecord(e1, s);
+  if (err == hipSuccess) err = hipEventSynchronize(e1);
+  float ms = 0.f;
+  if (err == hipSuccess) err = hipEventElapsedTime(&ms, e0, e1);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (err != hipSuccess) return status_of(err);
+  if (ms <= 0.f) return LSTM_ERR_LAUNCH;
+  // 8 waves x 32 MFMAs of 16 x 16 x 32 (16384 FLOP) per work-group and
+  // iteration, against the dense bf16 peak of this device's compute units
+  // (2516.6 TFLOP/s for 256 of them)
+  const double flops = (double)cus * 8 * 32 * 16384.0 * (double)iters;
+  *frac_of_peak = flops / ((double)ms * 1e-3) / (2516.6e12 * (double)cus / 256.0);
+  return LSTM_OK;
+}
+
 int lstm_debug_inject(int what, int64_t value) {
   switch (what) {
     case LSTM_DEBUG_FAIL_STEP:

@@ -34,10 +34,12 @@ STATUS = {0: "OK", -1: "ERR_NULL", -2: "ERR_DIMS", -3: "ERR_DTYPE", -4: "ERR_ALI
           -9: "ERR_TIMEOUT", -10: "ERR_DEVICE", -11: "ERR_SCRATCH", -12: "ERR_PLACEMENT",
           -13: "ERR_STATE"}
 DEBUG_FAIL_STEP, DEBUG_MISPLACE, DEBUG_XCD_LOCAL = 1, 2, 3  # lstm_debug_inject
+PROBE_READS, PROBE_READS_AHEAD, PROBE_BARRIER, PROBE_DMA = 1, 2, 4, 8  # lstm_probe_mfma_stage
+PROBE_SCRATCH_BYTES = 1 << 20  # LSTM_PROBE_SCRATCH_BYTES
 SCRATCH_BYTES = 64 << 20  # LSTM_SCRATCH_BYTES
 EXPORTS = ("lstm_abi_version", "lstm_status_string", "lstm_query", "lstm_query_plan", "lstm_fwd_train",
            "lstm_fwd_train_scratch", "lstm_bwd", "lstm_check_workspace", "lstm_timing_enable", "lstm_timing_read",
-           "lstm_stamps_set", "lstm_probe_exchange", "lstm_debug_inject", "lstm_stack_query",
+           "lstm_stamps_set", "lstm_probe_exchange", "lstm_probe_mfma_stage", "lstm_debug_inject", "lstm_stack_query",
            "lstm_stack_fwd_train", "lstm_stack_bwd")
 STAMP_WGS, STAMP_POINTS = 8, 6
 KERNEL_KINDS = ("input_projection", "forward_recurrence", "backward_recurrence", "dW_product",
@@ -79,6 +81,9 @@ _lib.lstm_timing_read.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_double),
 _lib.lstm_probe_exchange.restype = ctypes.c_int
 _lib.lstm_probe_exchange.argtypes = [ctypes.POINTER(Shape), ctypes.c_int, _P, ctypes.c_size_t,
                                      ctypes.POINTER(ctypes.c_double), _P]
+_lib.lstm_probe_mfma_stage.restype = ctypes.c_int
+_lib.lstm_probe_mfma_stage.argtypes = [ctypes.c_int, ctypes.c_int64, _P, ctypes.c_size_t,
+                                       ctypes.POINTER(ctypes.c_double), _P]
 _lib.lstm_stack_query.restype = ctypes.c_int
 _lib.lstm_stack_query.argtypes = [ctypes.POINTER(Shape), ctypes.c_int64, ctypes.c_int64,
                                   ctypes.POINTER(ctypes.c_size_t), ctypes.POINTER(ctypes.c_int32)]
@@ -225,6 +230,18 @@ def probe_exchange(shape: Shape, workspace, layout: int = 0, stream=None) -> flo
     if rc != OK:
         raise LstmError(rc, "lstm_probe_exchange")
     return us.value
+
+
+def probe_mfma_stage(parts: int, scratch, iters: int = 4000, stream=None) -> float:
+    """lstm_probe_mfma_stage: fraction of the bf16 dense peak of 32 MFMAs
+    per wave and iteration with the stage parts `parts` (PROBE_* bits);
+    scratch: device memory of at least PROBE_SCRATCH_BYTES."""
+    frac = ctypes.c_double(0)
+    rc = _lib.lstm_probe_mfma_stage(int(parts), int(iters), _ptr(scratch), scratch.numel() * scratch.element_size(),
+                                    ctypes.byref(frac), _stream(stream))
+    if rc != OK:
+        raise LstmError(rc, "lstm_probe_mfma_stage")
+    return frac.value
 
 
 def debug_inject(what: int, value: int) -> None:

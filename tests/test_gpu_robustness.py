@@ -106,6 +106,24 @@ def test_exchange_probe_runs_in_both_layouts(lstm):
         assert all(0 < u < 50 for u in us)
 
 
+def test_mfma_stage_probe(lstm):
+    """lstm_probe_mfma_stage runs every combination of a product stage's
+    parts and reports a fraction of the bf16 peak in (0, 1.1]; it rejects
+    both read orders at once and a scratch buffer that is too small."""
+    scratch = torch.empty(lstm.PROBE_SCRATCH_BYTES, dtype=torch.uint8, device="cuda")
+    fr = {}
+    for parts in (0, 1, 2, 4, 8, 5, 6, 9, 10, 12, 13, 14):
+        fr[parts] = lstm.probe_mfma_stage(parts, scratch, 200)
+    print("stage probe fractions", {k: round(v, 3) for k, v in fr.items()}, flush=True)
+    assert all(0.0 < v <= 1.1 for v in fr.values())
+    with pytest.raises(lstm.LstmError) as e:
+        lstm.probe_mfma_stage(lstm.PROBE_READS | lstm.PROBE_READS_AHEAD, scratch, 10)
+    assert e.value.code == -2
+    with pytest.raises(lstm.LstmError) as e:
+        lstm.probe_mfma_stage(0, scratch[: lstm.PROBE_SCRATCH_BYTES // 2], 10)
+    assert e.value.code == -5
+
+
 def test_status_word_of_empty_calls_and_unfilled_workspaces(lstm):
     """A forward with T = 0 or B = 0 (no recurrence runs) still defines the
     workspace's status word, so checking it after such a call reports OK
