@@ -191,13 +191,15 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(Launch<FwdArgs> L) 
     }
   };
   // Direct-to-LDS path: the ring-read phase moves h_{t-1} alone, and every
-  // wave waits for its part of it.  Right after, when the product (bound by
-  // LDS reads) leaves the memory path idle, the waves start P_{t+1} into one
-  // of two LDS buffers and write the previous step's record (y, activated
-  // gates, c) from an LDS staging area as whole 16-byte pieces of its rows;
-  // these drain during the product and the gate math and are complete at the
-  // publish, which waits for every operation of every wave.  The owners read
-  // P_t from LDS and stage the step's record there.
+  // wave waits for its part of it.  After the product, the waves start
+  // P_{t+1} into one of two LDS buffers and write the previous step's record
+  // (y, activated gates, c) from an LDS staging area as whole 16-byte pieces
+  // of its rows; these drain during the k-part reduction and the gate math
+  // and are complete at the publish, which waits for every operation of
+  // every wave.  (Issued before the product, their LDS writes and staging
+  // reads slowed the product's LDS reads: the forward on T=256 B=256 H=1024
+  // went from 1204-1211 to 1154-1160 us with them after it.)  The owners
+  // read P_t from LDS and stage the step's record there.
   constexpr bool SPLIT = C == 0;
   // Tagged-word exchange (spread layout): h_t of the group travels as 8-byte
   // words of two values and the step (t + 1) in the HX region [2][Bp][HW],
@@ -429,12 +431,6 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(Launch<FwdArgs> L) 
       __builtin_amdgcn_s_barrier();
     }
     stamp(a.stamps, a.T, t, 2);
-    if constexpr (SPLIT) {
-      if (!tagm || t == 0) {  // (the tagged exchange issues them before its ring read)
-        if (t + 1 < a.T) dma_p(t + 1);
-        if (t > 0) store_rec(t - 1);
-      }
-    }
 
     // MFMA: part[mi][nt] = W_h[rows of M-tile mg*MW + mi, k part] .
     // h_{t-1}[tile nt]^T, with CH independent accumulator chains per tile
@@ -495,6 +491,14 @@ __global__ void __launch_bounds__(64 * NW, 1) fwd_rec_kernel(Launch<FwdArgs> L) 
         for (int ch = 1; ch < CH; ++ch) acc[mi][nt] += part[mi][nt][ch];
       }
     stamp(a.stamps, a.T, t, 3);
+    // P_{t+1} and the record of step t - 1 (their staging reads come before
+    // the barrier below, the staging writes of this step after it)
+    if constexpr (SPLIT) {
+      if (!tagm || t == 0) {  // (the tagged exchange issues them before its ring read)
+        if (t + 1 < a.T) dma_p(t + 1);
+        if (t > 0) store_rec(t - 1);
+      }
+    }
     // k-part reduction: partial tiles go to their owners through LDS; slot
     // (M-tile m, kk) holds the part of the kk-th non-owner wave of m's group
     f32x4_t mine[NBT];
