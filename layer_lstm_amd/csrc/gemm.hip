@@ -1091,8 +1091,15 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 // operands of the pipelined path are addressed through buffer descriptors
 static bool small_buf(int64_t elems, int esize) { return elems * esize < ((int64_t)1 << 31); }
 
-// Pipelined path (gemm_lds_kernel): K is split (powers of two) while the
-// tiles do not cover the CUs and every split keeps at least 8 stages.
+// Pipelined path (gemm_lds_kernel): K is split in a power of two that
+// keeps at least 8 stages per split, chosen by the cost of the launch in
+// stage rounds -- waves of work-groups over the CUs times stages per
+// work-group, plus the fp32 partials each split writes and the sum reads
+// (M x N x 8 bytes; a stage round of all CUs moves about 3.4 MB at the
+// HBM rate with 16-bit operands, 6.8 MB with fp32) -- a split taken only
+// when it saves a tenth.  (Splitting until the tiles cover the CUs would
+// add a second, partial wave of work-groups: 96 tiles of dW on 256 CUs in
+// four splits are 1.5 waves, in two splits 0.75.)
 // fp32 products take it only for deep K (>= 1024): with a short K the
 // 64 x 64 tiles of gemm_kernel cover the CUs without a split-K pass.
 template <typename T>
@@ -1102,8 +1109,15 @@ static GemmShape choose_shape_lds(int64_t M, int64_t N, int64_t K, int cus, int 
   constexpr int TILE = LdsCfg<T>::kTile;
   const int64_t tiles = ((M + TILE - 1) / TILE) * ((N + TILE - 1) / TILE);
   const int64_t ktiles = K / LdsCfg<T>::kKStage;
+  const double round_bytes = sizeof(T) == 2 ? 3.4e6 : 6.8e6;
+  auto cost = [&](int s) {
+    const int64_t c = cus > 0 ? cus : 1;
+    const double rounds = (double)((tiles * s + c - 1) / c), stages = (double)((ktiles + s - 1) / s);
+    return rounds * stages + (s > 1 ? (double)s * (double)M * (double)N * 8.0 / round_bytes : 0.0);
+  };
   GemmShape gs{TILE, 1};
-  while (gs.splits < max_splits && tiles * gs.splits < cus && ktiles / (gs.splits * 2) >= 8) gs.splits *= 2;
+  for (int s = 2; s <= max_splits && ktiles / s >= 8; s *= 2)
+    if (cost(s) < 0.9 * cost(gs.splits)) gs.splits = s;
   return gs;
 }
 
